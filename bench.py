@@ -1,0 +1,230 @@
+"""HSTU layer forward benchmark on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload stack8_long]
+
+A step is one pass of the whole hot path over one batch of the workload: for
+the default `stack8_long` (8 HSTU layers, 8 jagged sequences of 4096..8192
+tokens, d=1024, 8 heads x 128/128, bf16) that is 8 hstu_layer_fwd calls
+(input LayerNorm, projection GEMM + SiLU, work list, fused pointwise
+attention, fused LayerNorm/gate/output GEMM + residual per layer).  Inputs are
+resident in HBM before timing starts.  Prints one JSON line.
+
+Besides the step time, the attention kernel — the dominant kernel — is timed
+on its own through hstu_attn_fwd with HIP events recorded on the stream it is
+launched on, and its algorithmic FLOPs per launch (2 (dqk + dv) H per
+attended (query, key) pair) give the roofline fraction against the dense bf16
+MFMA peak.  The CPU oracle is timed on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# MI355X published peaks
+PEAK_BF16_TFLOPS = 2516.6       # dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
+PEAK_FP32_MFMA_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+METRIC = "HSTU layer fwd tokens/sec (jagged bf16); attention TFLOP/s vs MFMA peak"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic_{workload}.json")
+ATTN_SOURCES = ["attn.hip", "common.h", "kernels.h"]
+
+
+def attn_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ATTN_SOURCES:
+        with open(os.path.join(ROOT, "hstu_sequential_transducer_layer_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def attended_pairs(lengths, ncand) -> int:
+    """Unmasked (query, key) pairs: causal history plus candidates that see the
+    history and themselves."""
+    tot = 0
+    for b, L in enumerate(lengths):
+        m = 0 if ncand is None else int(ncand[b])
+        n = int(L) - m
+        tot += n * (n + 1) // 2 + m * n + m
+    return tot
+
+
+def load_traffic(workload: str):
+    p = TRAFFIC_FILE.format(workload=workload)
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        rec = json.load(f)
+    if rec.get("attn_source_hash") != attn_source_hash():
+        return None          # counters were taken on a different kernel
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, budget_s: float = 20.0):
+    """The oracle as it stands, on a bounded sample: one layer over whole
+    sequences (shortest first) until the budget is spent; reported in the
+    metric's unit (tokens through all layers of the step per second)."""
+    from oracle import hstu_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    order = np.argsort(w.lengths())
+    done_rows, t_used, seqs = 0, 0.0, []
+    for b in order:
+        if t_used > budget_s * 0.5 and seqs:
+            break
+        sub = w.sub_batch([int(b)])
+        t0 = time.perf_counter()
+        O.layer_forward(sub.x, sub.offsets, sub.timestamps, sub.num_candidates, sub.layers[0],
+                        w.dims)
+        t_used += time.perf_counter() - t0
+        done_rows += sub.T
+        seqs.append(int(b))
+        if t_used > budget_s:
+            break
+    n_layers = len(w.layers)
+    value = done_rows / t_used / n_layers
+    return {"value": value, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"float64 NumPy oracle, layer 1 of {n_layers} over sequence(s) {seqs} "
+                      f"({done_rows} tokens) in {t_used:.1f} s; value = tokens / time / "
+                      f"{n_layers} layers"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="stack8_long")
+    ap.add_argument("--attn-reps", type=int, default=20)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the HSTU layer "
+              "forward here is a single-GPU path; sequences are independent, so a multi-GPU "
+              "deployment shards the jagged batch by sequence with no collectives.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from hstu_sequential_transducer_layer_amd import _lib, layer, synth
+
+    _lib.load()   # fails loudly if the HIP library is missing
+    w = synth.make_workload(args.workload)
+    dev = layer.to_device(w)
+    stack = layer.HSTUStack(w.dims, dev["layers"])
+    x, off, ts, nc = dev["x"], dev["offsets"], dev["timestamps"], dev["num_candidates"]
+    T, B = w.T, w.B
+    out = torch.empty_like(x)
+
+    for _ in range(args.warmup):
+        stack.forward(x, off, ts, nc, out=out)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(args.steps):
+        stack.forward(x, off, ts, nc, out=out)
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+
+    # Attention kernel alone, one layer's launch, events on the launch stream.
+    desc = stack.desc
+    acts = _lib.proj_fwd(desc, x, dev["layers"][0])
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        _lib.attn_fwd(desc, off, ts, nc, dev["layers"][0], acts)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.attn_reps)]
+    for a, b in ev:
+        a.record(stream)
+        _lib.attn_fwd(desc, off, ts, nc, dev["layers"][0], acts)
+        b.record(stream)
+    torch.cuda.synchronize()
+    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    # the other two stages of one layer, for context
+    def timed(fn, reps=10):
+        fn()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record(stream)
+        for _ in range(reps):
+            fn()
+        e.record(stream)
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / reps
+    proj_ms = timed(lambda: _lib.proj_fwd(desc, x, dev["layers"][0], acts))
+    out_ms = timed(lambda: _lib.out_fwd(desc, x, dev["layers"][0], acts, out=out))
+
+    pairs = attended_pairs(w.lengths(), w.num_candidates)
+    dm, H, dqk, dv = w.dims.d_model, w.dims.num_heads, w.dims.dqk, w.dims.dv
+    attn_flop = 2.0 * (dqk + dv) * H * pairs
+    attn_tflops = attn_flop / (attn_ms * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dims.dtype == "bf16" else PEAK_FP32_MFMA_TFLOPS
+    tokens_per_s = T / (ms_step * 1e-3)
+    e = 2 if w.dims.dtype == "bf16" else 4
+    proj_flop = 2.0 * T * dm * w.dims.n1
+    out_bytes = T * (H * dv * e * 2 + 2 * dm * e + H * 8) + H * dv * dm * e
+
+    rec = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dims.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{args.workload}: {synth.WORKLOADS[args.workload].description}",
+            "global_batch": B,
+            "tokens": T,
+            "layers": len(w.layers),
+            "seq_len": f"{int(w.lengths().min())}..{int(w.lengths().max())}",
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "kernel": "attn_kernel (fused pointwise attention, one layer)",
+            "bound": "mfma",
+            "achieved": attn_tflops,
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": attn_tflops / peak,
+            "traffic": load_traffic(args.workload),
+            "launch_ms": attn_ms,
+            "flop_per_launch": attn_flop,
+            "pairs_per_launch": pairs,
+        },
+        "stages_ms_per_layer": {
+            "proj (ln_in + f1 GEMM + SiLU)": proj_ms,
+            "attn (work list + attention)": attn_ms,
+            "out (LN gate + f2 GEMM + residual)": out_ms,
+            "proj_tflops": proj_flop / (proj_ms * 1e-3) / 1e12,
+            "out_gbs_algorithmic": out_bytes / (out_ms * 1e-3) / 1e9,
+        },
+        "layer_tokens_per_s": T * len(w.layers) / (ms_step * 1e-3),
+    }
+    if not args.no_cpu:
+        rec["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

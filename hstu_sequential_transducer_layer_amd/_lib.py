@@ -1,0 +1,236 @@
+"""ctypes binding of libhstu (include/hstu.h) — argument marshalling only.
+
+Every step of the layer runs in the HIP kernels of libhstu.so; this module
+turns torch device tensors into pointers, allocates caller-owned buffers
+(workspace, outputs) with torch, and passes torch's current HIP stream.  There
+is no fallback: if the library is missing, every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libhstu.so")
+
+HSTU_OK, HSTU_ERR_INVALID_ARG, HSTU_ERR_UNSUPPORTED, HSTU_ERR_WORKSPACE, HSTU_ERR_DEVICE = range(5)
+HSTU_F32, HSTU_BF16 = 0, 1
+HSTU_INPUT_NORM, HSTU_RESIDUAL, HSTU_CAND_SHARED_POS, HSTU_VALIDATE = 1, 2, 4, 8
+
+EXPORTS = [
+    "hstu_workspace_size", "hstu_layer_fwd", "hstu_proj_workspace_size", "hstu_proj_fwd",
+    "hstu_attn_workspace_size", "hstu_attn_fwd", "hstu_out_fwd", "hstu_debug_indices",
+    "hstu_status_str", "hstu_last_error",
+]
+
+
+class HstuDesc(ctypes.Structure):
+    _fields_ = [("d_model", ctypes.c_int32), ("num_heads", ctypes.c_int32),
+                ("dqk", ctypes.c_int32), ("dv", ctypes.c_int32),
+                ("pos_buckets", ctypes.c_int32), ("time_buckets", ctypes.c_int32),
+                ("time_sub_bits", ctypes.c_int32), ("dtype", ctypes.c_int),
+                ("flags", ctypes.c_uint32), ("ln_eps", ctypes.c_float),
+                ("norm_len", ctypes.c_int32)]
+
+
+class HstuWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("w1", "b1", "w2", "b2", "ln_in_g", "ln_in_b", "ln_av_g", "ln_av_b")]
+
+
+class HstuBiasTables(ctypes.Structure):
+    _fields_ = [("pos", ctypes.c_void_p), ("time", ctypes.c_void_p),
+                ("pos_head_stride", ctypes.c_int32), ("time_head_stride", ctypes.c_int32)]
+
+
+class HstuActivations(ctypes.Structure):
+    _fields_ = [("u", ctypes.c_void_p), ("v", ctypes.c_void_p), ("q", ctypes.c_void_p),
+                ("k", ctypes.c_void_p), ("av", ctypes.c_void_p), ("av_stats", ctypes.c_void_p)]
+
+
+class HstuError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"hstu status {status}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libhstu.so (built by build_lib.py); raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run "
+                           "`python -m hstu_sequential_transducer_layer_amd.build_lib`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, sz, i32, i64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int64
+    P = ctypes.POINTER
+    lib.hstu_workspace_size.argtypes = [P(HstuDesc), i64, i32]
+    lib.hstu_workspace_size.restype = sz
+    lib.hstu_proj_workspace_size.argtypes = [P(HstuDesc), i64]
+    lib.hstu_proj_workspace_size.restype = sz
+    lib.hstu_attn_workspace_size.argtypes = [P(HstuDesc), i64, i32]
+    lib.hstu_attn_workspace_size.restype = sz
+    lib.hstu_layer_fwd.argtypes = [P(HstuDesc), vp, vp, i32, i64, vp, vp, P(HstuWeights),
+                                   P(HstuBiasTables), vp, vp, sz, vp]
+    lib.hstu_proj_fwd.argtypes = [P(HstuDesc), vp, i64, P(HstuWeights), P(HstuActivations),
+                                  vp, sz, vp]
+    lib.hstu_attn_fwd.argtypes = [P(HstuDesc), vp, i32, i64, vp, vp, P(HstuBiasTables),
+                                  P(HstuActivations), vp, sz, vp]
+    lib.hstu_out_fwd.argtypes = [P(HstuDesc), vp, i64, P(HstuWeights), P(HstuActivations),
+                                 vp, vp, vp]
+    lib.hstu_debug_indices.argtypes = [P(HstuDesc), vp, i32, i64, vp, vp, vp, i64, vp, vp]
+    for f in ("hstu_layer_fwd", "hstu_proj_fwd", "hstu_attn_fwd", "hstu_out_fwd",
+              "hstu_debug_indices"):
+        getattr(lib, f).restype = ctypes.c_int
+    lib.hstu_status_str.argtypes = [ctypes.c_int]
+    lib.hstu_status_str.restype = ctypes.c_char_p
+    lib.hstu_last_error.argtypes = []
+    lib.hstu_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != HSTU_OK:
+        raise HstuError(status, load().hstu_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def make_desc(dims, flags_extra: int = 0) -> HstuDesc:
+    """HstuDesc from any object with the LayerDims attributes."""
+    flags = flags_extra
+    if dims.input_norm:
+        flags |= HSTU_INPUT_NORM
+    if dims.residual:
+        flags |= HSTU_RESIDUAL
+    if dims.cand_shared_pos:
+        flags |= HSTU_CAND_SHARED_POS
+    return HstuDesc(dims.d_model, dims.num_heads, dims.dqk, dims.dv, dims.pos_buckets,
+                    dims.time_buckets, dims.time_sub_bits,
+                    HSTU_BF16 if dims.dtype == "bf16" else HSTU_F32, flags,
+                    float(dims.ln_eps), int(dims.norm_len))
+
+
+def torch_dtype(desc: HstuDesc) -> torch.dtype:
+    return torch.bfloat16 if desc.dtype == HSTU_BF16 else torch.float32
+
+
+def make_weights(prm: Dict[str, torch.Tensor]) -> HstuWeights:
+    return HstuWeights(*[_ptr(prm.get(n)) for n in
+                         ("w1", "b1", "w2", "b2", "ln_in_g", "ln_in_b", "ln_av_g", "ln_av_b")])
+
+
+def make_tables(prm: Dict[str, torch.Tensor]) -> HstuBiasTables:
+    pos, tim = prm["pos_table"], prm["time_table"]
+    return HstuBiasTables(_ptr(pos), _ptr(tim),
+                          pos.shape[-1] if pos.dim() == 2 else 0,
+                          tim.shape[-1] if tim.dim() == 2 else 0)
+
+
+def workspace_size(desc: HstuDesc, T: int, B: int) -> int:
+    return int(load().hstu_workspace_size(ctypes.byref(desc), T, B))
+
+
+def alloc_workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def layer_fwd(desc: HstuDesc, x: torch.Tensor, seq_offsets: torch.Tensor,
+              timestamps: torch.Tensor, num_candidates: Optional[torch.Tensor],
+              prm: Dict[str, torch.Tensor], out: Optional[torch.Tensor] = None,
+              workspace: Optional[torch.Tensor] = None, weights: Optional[HstuWeights] = None,
+              tables: Optional[HstuBiasTables] = None) -> torch.Tensor:
+    """hstu_layer_fwd on torch's current stream; returns `out` ([T, d])."""
+    lib = load()
+    T, B = x.shape[0], seq_offsets.shape[0] - 1
+    if out is None:
+        out = torch.empty_like(x)
+    need = workspace_size(desc, T, B)
+    if workspace is None or workspace.numel() < need:
+        workspace = alloc_workspace(need, x.device)
+    w = weights if weights is not None else make_weights(prm)
+    t = tables if tables is not None else make_tables(prm)
+    _check(lib.hstu_layer_fwd(ctypes.byref(desc), _ptr(x), _ptr(seq_offsets), B, T,
+                              _ptr(timestamps), _ptr(num_candidates), ctypes.byref(w),
+                              ctypes.byref(t), _ptr(out), _ptr(workspace), workspace.numel(),
+                              _stream()))
+    return out
+
+
+def alloc_activations(desc: HstuDesc, T: int, device) -> Dict[str, torch.Tensor]:
+    dt = torch_dtype(desc)
+    H, dqk, dv = desc.num_heads, desc.dqk, desc.dv
+    return {
+        "u": torch.empty(T, H * dv, dtype=dt, device=device),
+        "v": torch.empty(H, T, dv, dtype=dt, device=device),
+        "q": torch.empty(H, T, dqk, dtype=dt, device=device),
+        "k": torch.empty(H, T, dqk, dtype=dt, device=device),
+        "av": torch.empty(T, H * dv, dtype=dt, device=device),
+        "av_stats": torch.empty(T, H, 2, dtype=torch.float32, device=device),
+    }
+
+
+def _acts(a: Dict[str, torch.Tensor]) -> HstuActivations:
+    return HstuActivations(*[_ptr(a.get(n)) for n in ("u", "v", "q", "k", "av", "av_stats")])
+
+
+def proj_fwd(desc: HstuDesc, x: torch.Tensor, prm: Dict[str, torch.Tensor],
+             acts: Optional[Dict[str, torch.Tensor]] = None) -> Dict[str, torch.Tensor]:
+    lib = load()
+    T = x.shape[0]
+    acts = acts or alloc_activations(desc, T, x.device)
+    need = int(lib.hstu_proj_workspace_size(ctypes.byref(desc), T))
+    ws = alloc_workspace(need, x.device)
+    a, w = _acts(acts), make_weights(prm)
+    _check(lib.hstu_proj_fwd(ctypes.byref(desc), _ptr(x), T, ctypes.byref(w), ctypes.byref(a),
+                             _ptr(ws), ws.numel(), _stream()))
+    return acts
+
+
+def attn_fwd(desc: HstuDesc, seq_offsets, timestamps, num_candidates, prm, acts):
+    lib = load()
+    T, B = acts["u"].shape[0], seq_offsets.shape[0] - 1
+    need = int(lib.hstu_attn_workspace_size(ctypes.byref(desc), T, B))
+    ws = alloc_workspace(need, acts["u"].device)
+    a, t = _acts(acts), make_tables(prm)
+    _check(lib.hstu_attn_fwd(ctypes.byref(desc), _ptr(seq_offsets), B, T, _ptr(timestamps),
+                             _ptr(num_candidates), ctypes.byref(t), ctypes.byref(a), _ptr(ws),
+                             ws.numel(), _stream()))
+    return acts
+
+
+def out_fwd(desc: HstuDesc, x, prm, acts, out=None, want_z: bool = False):
+    lib = load()
+    T = acts["u"].shape[0]
+    if out is None:
+        out = torch.empty(T, desc.d_model, dtype=torch_dtype(desc), device=acts["u"].device)
+    z = torch.empty_like(acts["u"]) if want_z else None
+    a, w = _acts(acts), make_weights(prm)
+    _check(lib.hstu_out_fwd(ctypes.byref(desc), _ptr(x), T, ctypes.byref(w), ctypes.byref(a),
+                            _ptr(out), _ptr(z), _stream()))
+    return out, z
+
+
+def debug_indices(desc: HstuDesc, seq_offsets, timestamps, num_candidates, pairs: torch.Tensor):
+    lib = load()
+    T, B = timestamps.shape[0], seq_offsets.shape[0] - 1
+    n = pairs.shape[0]
+    out = torch.empty(n, 6, dtype=torch.int64, device=pairs.device)
+    _check(lib.hstu_debug_indices(ctypes.byref(desc), _ptr(seq_offsets), B, T, _ptr(timestamps),
+                                  _ptr(num_candidates), _ptr(pairs), n, _ptr(out), _stream()))
+    return out

@@ -1,0 +1,376 @@
+// C ABI of libhstu (declarations and the layer's definition in include/hstu.h).
+// Host side only: argument validation, workspace carve-up and the launch
+// sequence  ln_in -> proj -> build_tiles -> attn -> out  on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+#include "hstu.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+hstu_status fail(hstu_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+hstu_status ok() {
+  g_err.clear();
+  return HSTU_OK;
+}
+
+size_t esize(hstu_dtype dt) { return dt == HSTU_BF16 ? 2 : 4; }
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+hstu_status check_desc(const hstu_desc* d) {
+  if (!d) return fail(HSTU_ERR_INVALID_ARG, "desc is NULL");
+  if (d->dtype != HSTU_F32 && d->dtype != HSTU_BF16)
+    return fail(HSTU_ERR_UNSUPPORTED, "unknown dtype %d", (int)d->dtype);
+  if (d->flags & ~(uint32_t)(HSTU_INPUT_NORM | HSTU_RESIDUAL | HSTU_CAND_SHARED_POS | HSTU_VALIDATE))
+    return fail(HSTU_ERR_INVALID_ARG, "unknown flag bits 0x%x", d->flags);
+  if (d->d_model < 32 || d->d_model > 8192 || d->d_model % 32 != 0)
+    return fail(HSTU_ERR_UNSUPPORTED, "d_model %d: must be a multiple of 32 in [32, 8192]", d->d_model);
+  if (d->num_heads < 1 || d->num_heads > 64)
+    return fail(HSTU_ERR_UNSUPPORTED, "num_heads %d: must be in [1, 64]", d->num_heads);
+  auto okdim = [](int v) { return v == 32 || v == 64 || v == 128; };
+  if (!okdim(d->dqk) || !okdim(d->dv))
+    return fail(HSTU_ERR_UNSUPPORTED, "dqk %d / dv %d: each must be 32, 64 or 128", d->dqk, d->dv);
+  if (d->dtype == HSTU_F32 && (d->dqk > 64 || d->dv > 64))
+    return fail(HSTU_ERR_UNSUPPORTED, "fp32 layers support dqk, dv <= 64");
+  if (d->pos_buckets < 1 || d->pos_buckets > 2047 || d->pos_buckets % 2 == 0)
+    return fail(HSTU_ERR_INVALID_ARG, "pos_buckets %d: must be odd in [1, 2047]", d->pos_buckets);
+  if (d->time_buckets < 1 || d->time_buckets > 2048)
+    return fail(HSTU_ERR_INVALID_ARG, "time_buckets %d: must be in [1, 2048]", d->time_buckets);
+  if (d->time_sub_bits < 0 || d->time_sub_bits > 4)
+    return fail(HSTU_ERR_INVALID_ARG, "time_sub_bits %d: must be in [0, 4]", d->time_sub_bits);
+  if (!(d->ln_eps > 0.f) || !std::isfinite(d->ln_eps))
+    return fail(HSTU_ERR_INVALID_ARG, "ln_eps must be positive and finite");
+  if (d->norm_len < 0) return fail(HSTU_ERR_INVALID_ARG, "norm_len %d < 0", d->norm_len);
+  return HSTU_OK;
+}
+
+hstu_status check_sizes(int64_t T, int32_t B) {
+  if (T < 0) return fail(HSTU_ERR_INVALID_ARG, "total_tokens %lld < 0", (long long)T);
+  if (T > INT32_MAX - 1024) return fail(HSTU_ERR_UNSUPPORTED, "total_tokens %lld too large", (long long)T);
+  if (B < 0) return fail(HSTU_ERR_INVALID_ARG, "batch %d < 0", B);
+  if (T > 0 && B == 0) return fail(HSTU_ERR_INVALID_ARG, "total_tokens > 0 with batch 0");
+  return HSTU_OK;
+}
+
+#define HSTU_REQ(ptr, al, name)                                                         \
+  do {                                                                                  \
+    if (!(ptr)) return fail(HSTU_ERR_INVALID_ARG, "%s is NULL", name);                  \
+    if (!aligned((ptr), (al))) return fail(HSTU_ERR_INVALID_ARG, "%s is not %d-byte aligned", name, (int)(al)); \
+  } while (0)
+
+hstu_status check_meta(const int64_t* off, int32_t B, const int64_t* ts, const int32_t* ncand) {
+  HSTU_REQ(off, 8, "seq_offsets");
+  HSTU_REQ(ts, 8, "timestamps");
+  if (ncand && !aligned(ncand, 4)) return fail(HSTU_ERR_INVALID_ARG, "num_candidates is not 4-byte aligned");
+  (void)B;
+  return HSTU_OK;
+}
+
+hstu_status check_tables(const hstu_desc* d, const hstu_bias_tables* t) {
+  if (!t) return fail(HSTU_ERR_INVALID_ARG, "tables is NULL");
+  HSTU_REQ(t->pos, esize(d->dtype), "tables->pos");
+  HSTU_REQ(t->time, esize(d->dtype), "tables->time");
+  if (t->pos_head_stride < 0 || t->time_head_stride < 0)
+    return fail(HSTU_ERR_INVALID_ARG, "negative table head stride");
+  if (t->pos_head_stride != 0 && t->pos_head_stride < d->pos_buckets)
+    return fail(HSTU_ERR_INVALID_ARG, "pos_head_stride %d < pos_buckets %d", t->pos_head_stride, d->pos_buckets);
+  if (t->time_head_stride != 0 && t->time_head_stride < d->time_buckets)
+    return fail(HSTU_ERR_INVALID_ARG, "time_head_stride %d < time_buckets %d", t->time_head_stride, d->time_buckets);
+  return HSTU_OK;
+}
+
+hstu_status check_proj_weights(const hstu_desc* d, const hstu_weights* w) {
+  if (!w) return fail(HSTU_ERR_INVALID_ARG, "weights is NULL");
+  HSTU_REQ(w->w1, 16, "weights->w1");
+  HSTU_REQ(w->b1, esize(d->dtype), "weights->b1");
+  if (d->flags & HSTU_INPUT_NORM) {
+    HSTU_REQ(w->ln_in_g, 16, "weights->ln_in_g");
+    HSTU_REQ(w->ln_in_b, 16, "weights->ln_in_b");
+  }
+  return HSTU_OK;
+}
+
+hstu_status check_out_weights(const hstu_desc* d, const hstu_weights* w) {
+  if (!w) return fail(HSTU_ERR_INVALID_ARG, "weights is NULL");
+  HSTU_REQ(w->w2, 16, "weights->w2");
+  HSTU_REQ(w->b2, esize(d->dtype), "weights->b2");
+  HSTU_REQ(w->ln_av_g, 16, "weights->ln_av_g");
+  HSTU_REQ(w->ln_av_b, 16, "weights->ln_av_b");
+  return HSTU_OK;
+}
+
+hstu_status check_acts(const hstu_activations* a, bool proj, bool attn) {
+  if (!a) return fail(HSTU_ERR_INVALID_ARG, "acts is NULL");
+  HSTU_REQ(a->u, 16, "acts->u");
+  if (proj || attn) {
+    HSTU_REQ(a->v, 16, "acts->v");
+    HSTU_REQ(a->q, 16, "acts->q");
+    HSTU_REQ(a->k, 16, "acts->k");
+  }
+  if (!proj) {
+    HSTU_REQ(a->av, 16, "acts->av");
+    HSTU_REQ(a->av_stats, 8, "acts->av_stats");
+  }
+  return HSTU_OK;
+}
+
+// Workspace carve-up shared by the size query and the layer call.
+struct Layout {
+  size_t xn, u, v, q, k, av, stats, tiles, count, total;
+};
+
+Layout layout(const hstu_desc* d, int64_t T, int32_t B) {
+  const size_t e = esize(d->dtype);
+  const size_t H = d->num_heads, hdv = H * d->dv, hdq = H * d->dqk;
+  Layout L{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o += align256(bytes);
+    return at;
+  };
+  L.xn = take((d->flags & HSTU_INPUT_NORM) ? (size_t)T * d->d_model * e : 0);
+  L.u = take((size_t)T * hdv * e);
+  L.v = take((size_t)T * hdv * e);
+  L.q = take((size_t)T * hdq * e);
+  L.k = take((size_t)T * hdq * e);
+  L.av = take((size_t)T * hdv * e);
+  L.stats = take((size_t)T * H * 2 * sizeof(float));
+  L.tiles = take((size_t)hstu::attn_max_tiles(T, B) * sizeof(int2));
+  L.count = take(sizeof(int32_t));
+  L.total = o;
+  return L;
+}
+
+size_t attn_ws(int64_t T, int32_t B) {
+  return align256((size_t)hstu::attn_max_tiles(T, B) * sizeof(int2)) + align256(sizeof(int32_t));
+}
+
+hstu_status device(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(HSTU_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+  return HSTU_OK;
+}
+
+hstu_status validate_metadata(const int64_t* off, int32_t B, int64_t T, const int32_t* ncand,
+                              hipStream_t s) {
+  std::vector<int64_t> h_off((size_t)B + 1);
+  std::vector<int32_t> h_nc(ncand ? (size_t)B : 0);
+  hstu_status st = device(hipMemcpyAsync(h_off.data(), off, h_off.size() * 8, hipMemcpyDeviceToHost, s),
+                          "copy seq_offsets");
+  if (st != HSTU_OK) return st;
+  if (ncand && B > 0) {
+    st = device(hipMemcpyAsync(h_nc.data(), ncand, h_nc.size() * 4, hipMemcpyDeviceToHost, s),
+                "copy num_candidates");
+    if (st != HSTU_OK) return st;
+  }
+  st = device(hipStreamSynchronize(s), "synchronise for validation");
+  if (st != HSTU_OK) return st;
+  if (h_off[0] != 0) return fail(HSTU_ERR_INVALID_ARG, "seq_offsets[0] = %lld, expected 0", (long long)h_off[0]);
+  if (h_off[B] != T)
+    return fail(HSTU_ERR_INVALID_ARG, "seq_offsets[B] = %lld, expected total_tokens %lld",
+                (long long)h_off[B], (long long)T);
+  for (int32_t b = 0; b < B; ++b) {
+    const int64_t L = h_off[b + 1] - h_off[b];
+    if (L < 0) return fail(HSTU_ERR_INVALID_ARG, "seq_offsets decreases at %d", b);
+    if (ncand && (h_nc[b] < 0 || h_nc[b] > L))
+      return fail(HSTU_ERR_INVALID_ARG, "num_candidates[%d] = %d outside [0, %lld]", b, h_nc[b], (long long)L);
+  }
+  return HSTU_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* hstu_status_str(hstu_status s) {
+  switch (s) {
+    case HSTU_OK: return "ok";
+    case HSTU_ERR_INVALID_ARG: return "invalid argument";
+    case HSTU_ERR_UNSUPPORTED: return "unsupported configuration";
+    case HSTU_ERR_WORKSPACE: return "workspace too small";
+    case HSTU_ERR_DEVICE: return "device error";
+  }
+  return "unknown status";
+}
+
+const char* hstu_last_error(void) { return g_err.c_str(); }
+
+size_t hstu_workspace_size(const hstu_desc* desc, int64_t T, int32_t B) {
+  if (check_desc(desc) != HSTU_OK || check_sizes(T, B) != HSTU_OK) return 0;
+  return layout(desc, T, B).total;
+}
+
+size_t hstu_proj_workspace_size(const hstu_desc* desc, int64_t T) {
+  if (check_desc(desc) != HSTU_OK || check_sizes(T, 1) != HSTU_OK) return 0;
+  if (!(desc->flags & HSTU_INPUT_NORM)) return 0;
+  return align256((size_t)T * desc->d_model * esize(desc->dtype));
+}
+
+size_t hstu_attn_workspace_size(const hstu_desc* desc, int64_t T, int32_t B) {
+  if (check_desc(desc) != HSTU_OK || check_sizes(T, B) != HSTU_OK) return 0;
+  return attn_ws(T, B);
+}
+
+static hstu_status run_proj(const hstu_desc* d, const void* x, int64_t T, const hstu_weights* w,
+                            const hstu_activations* a, void* xn, hipStream_t s) {
+  const void* src = x;
+  if (d->flags & HSTU_INPUT_NORM) {
+    hstu_status st = device(hstu::launch_ln_in(d->dtype, x, w->ln_in_g, w->ln_in_b, xn, T,
+                                               d->d_model, d->ln_eps, s), "ln_in launch");
+    if (st != HSTU_OK) return st;
+    src = xn;
+  }
+  return device(hstu::launch_proj(*d, src, T, w->w1, w->b1, a->u, a->v, a->q, a->k, s), "proj launch");
+}
+
+static hstu_status run_attn(const hstu_desc* d, const int64_t* off, int32_t B, int64_t T,
+                            const int64_t* ts, const int32_t* nc, const hstu_bias_tables* t,
+                            const hstu_activations* a, int2* tiles, int32_t* count, hipStream_t s) {
+  hstu_status st = device(hstu::launch_build_tiles(off, nc, B, T, tiles, count, s), "tile list launch");
+  if (st != HSTU_OK) return st;
+  return device(hstu::launch_attn(*d, off, nc, B, T, ts, *t, a->q, a->k, a->v, a->av, a->av_stats,
+                                  tiles, count, s), "attention launch");
+}
+
+hstu_status hstu_proj_fwd(const hstu_desc* desc, const void* x, int64_t T, const hstu_weights* w,
+                          const hstu_activations* acts, void* ws, size_t ws_bytes,
+                          hstu_stream_t stream) {
+  hstu_status st;
+  if ((st = check_desc(desc)) != HSTU_OK) return st;
+  if ((st = check_sizes(T, 1)) != HSTU_OK) return st;
+  if (T == 0) return ok();
+  HSTU_REQ(x, 16, "x");
+  if ((st = check_proj_weights(desc, w)) != HSTU_OK) return st;
+  if ((st = check_acts(acts, true, false)) != HSTU_OK) return st;
+  const size_t need = hstu_proj_workspace_size(desc, T);
+  if (need > 0 && (!ws || ws_bytes < need || !aligned(ws, 256)))
+    return fail(HSTU_ERR_WORKSPACE, "workspace: need %zu bytes (256-aligned), got %zu", need, ws_bytes);
+  if ((st = run_proj(desc, x, T, w, acts, ws, (hipStream_t)stream)) != HSTU_OK) return st;
+  return ok();
+}
+
+hstu_status hstu_attn_fwd(const hstu_desc* desc, const int64_t* off, int32_t B, int64_t T,
+                          const int64_t* ts, const int32_t* nc, const hstu_bias_tables* tables,
+                          const hstu_activations* acts, void* ws, size_t ws_bytes,
+                          hstu_stream_t stream) {
+  hstu_status st;
+  if ((st = check_desc(desc)) != HSTU_OK) return st;
+  if ((st = check_sizes(T, B)) != HSTU_OK) return st;
+  if (T == 0) return ok();
+  if ((st = check_meta(off, B, ts, nc)) != HSTU_OK) return st;
+  if ((st = check_tables(desc, tables)) != HSTU_OK) return st;
+  if ((st = check_acts(acts, false, true)) != HSTU_OK) return st;
+  const size_t need = attn_ws(T, B);
+  if (!ws || ws_bytes < need || !aligned(ws, 256))
+    return fail(HSTU_ERR_WORKSPACE, "workspace: need %zu bytes (256-aligned), got %zu", need, ws_bytes);
+  hipStream_t s = (hipStream_t)stream;
+  if (desc->flags & HSTU_VALIDATE)
+    if ((st = validate_metadata(off, B, T, nc, s)) != HSTU_OK) return st;
+  char* base = (char*)ws;
+  int2* tiles = (int2*)base;
+  int32_t* count = (int32_t*)(base + align256((size_t)hstu::attn_max_tiles(T, B) * sizeof(int2)));
+  if ((st = run_attn(desc, off, B, T, ts, nc, tables, acts, tiles, count, s)) != HSTU_OK) return st;
+  return ok();
+}
+
+hstu_status hstu_out_fwd(const hstu_desc* desc, const void* x, int64_t T, const hstu_weights* w,
+                         const hstu_activations* acts, void* out, void* z_out, hstu_stream_t stream) {
+  hstu_status st;
+  if ((st = check_desc(desc)) != HSTU_OK) return st;
+  if ((st = check_sizes(T, 1)) != HSTU_OK) return st;
+  if (T == 0) return ok();
+  if (desc->flags & HSTU_RESIDUAL) HSTU_REQ(x, 16, "x");
+  HSTU_REQ(out, 16, "out");
+  if (z_out && !aligned(z_out, 16)) return fail(HSTU_ERR_INVALID_ARG, "z_out is not 16-byte aligned");
+  if ((st = check_out_weights(desc, w)) != HSTU_OK) return st;
+  if ((st = check_acts(acts, false, false)) != HSTU_OK) return st;
+  st = device(hstu::launch_out(*desc, x, T, *w, acts->u, acts->av, acts->av_stats, out, z_out,
+                               (hipStream_t)stream), "out launch");
+  if (st != HSTU_OK) return st;
+  return ok();
+}
+
+hstu_status hstu_layer_fwd(const hstu_desc* desc, const void* x, const int64_t* off, int32_t B,
+                           int64_t T, const int64_t* ts, const int32_t* nc, const hstu_weights* w,
+                           const hstu_bias_tables* tables, void* out, void* ws, size_t ws_bytes,
+                           hstu_stream_t stream) {
+  hstu_status st;
+  if ((st = check_desc(desc)) != HSTU_OK) return st;
+  if ((st = check_sizes(T, B)) != HSTU_OK) return st;
+  if (T == 0) return ok();
+  HSTU_REQ(x, 16, "x");
+  HSTU_REQ(out, 16, "out");
+  if ((st = check_meta(off, B, ts, nc)) != HSTU_OK) return st;
+  if ((st = check_proj_weights(desc, w)) != HSTU_OK) return st;
+  if ((st = check_out_weights(desc, w)) != HSTU_OK) return st;
+  if ((st = check_tables(desc, tables)) != HSTU_OK) return st;
+  const Layout L = layout(desc, T, B);
+  if (!ws || ws_bytes < L.total || !aligned(ws, 256))
+    return fail(HSTU_ERR_WORKSPACE, "workspace: need %zu bytes (256-aligned), got %zu", L.total, ws_bytes);
+  hipStream_t s = (hipStream_t)stream;
+  if (desc->flags & HSTU_VALIDATE)
+    if ((st = validate_metadata(off, B, T, nc, s)) != HSTU_OK) return st;
+  char* base = (char*)ws;
+  hstu_activations a;
+  a.u = base + L.u;
+  a.v = base + L.v;
+  a.q = base + L.q;
+  a.k = base + L.k;
+  a.av = base + L.av;
+  a.av_stats = (float*)(base + L.stats);
+  if ((st = run_proj(desc, x, T, w, &a, base + L.xn, s)) != HSTU_OK) return st;
+  if ((st = run_attn(desc, off, B, T, ts, nc, tables, &a, (int2*)(base + L.tiles),
+                     (int32_t*)(base + L.count), s)) != HSTU_OK)
+    return st;
+  st = device(hstu::launch_out(*desc, x, T, *w, a.u, a.av, a.av_stats, out, nullptr, s), "out launch");
+  if (st != HSTU_OK) return st;
+  return ok();
+}
+
+hstu_status hstu_debug_indices(const hstu_desc* desc, const int64_t* off, int32_t B, int64_t T,
+                               const int64_t* ts, const int32_t* nc, const int64_t* pairs,
+                               int64_t n, int64_t* out, hstu_stream_t stream) {
+  hstu_status st;
+  if ((st = check_desc(desc)) != HSTU_OK) return st;
+  if ((st = check_sizes(T, B)) != HSTU_OK) return st;
+  if (n < 0) return fail(HSTU_ERR_INVALID_ARG, "n_pairs %lld < 0", (long long)n);
+  if (n == 0) return ok();
+  if ((st = check_meta(off, B, ts, nc)) != HSTU_OK) return st;
+  HSTU_REQ(pairs, 8, "pairs");
+  HSTU_REQ(out, 8, "out");
+  hipStream_t s = (hipStream_t)stream;
+  if (desc->flags & HSTU_VALIDATE) {
+    if ((st = validate_metadata(off, B, T, nc, s)) != HSTU_OK) return st;
+    std::vector<int64_t> hp((size_t)n * 2);
+    if ((st = device(hipMemcpyAsync(hp.data(), pairs, hp.size() * 8, hipMemcpyDeviceToHost, s),
+                     "copy pairs")) != HSTU_OK)
+      return st;
+    if ((st = device(hipStreamSynchronize(s), "synchronise")) != HSTU_OK) return st;
+    for (size_t i = 0; i < hp.size(); ++i)
+      if (hp[i] < 0 || hp[i] >= T) return fail(HSTU_ERR_INVALID_ARG, "pair row %lld outside [0, T)", (long long)hp[i]);
+  }
+  st = device(hstu::launch_debug_indices(*desc, off, nc, B, T, ts, pairs, n, out, s), "debug launch");
+  if (st != HSTU_OK) return st;
+  return ok();
+}
+
+}  // extern "C"

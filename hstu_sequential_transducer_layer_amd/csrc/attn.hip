@@ -1,0 +1,336 @@
+// Stage 2: pointwise aggregated attention over jagged sequences.
+//
+//   AV_i^h = (1/N_b) sum_j M_ij SiLU(q_i.k_j + pos[h][bp(i,j)] + time[h][bt(i,j)]) v_j
+//
+// Sources: page "4.4 Scaling Recommendation Models", section "Generative
+// Recommenders and HSTU" (second layer equation; SiLU applied to each score on
+// its own with a constant normaliser such as the sequence length; bias on
+// position and time difference; candidates appended to the history that see
+// the history but not one another) and section "Code" (per-head bias added to
+// q.k, lower-triangular mask keeping the diagonal, division by n, no softmax
+// and no 1/sqrt(d)); page "HSTU: The First Exploration of the Scaling Law",
+// 7.1.4 Innovations 1-2 and 7.1.5 M-FALCON layer 1.
+//
+// Work item: (sequence b, 128-row query tile, head h), one workgroup of four
+// waves, each wave owning 32 query rows.  The key range is streamed in 64-key
+// blocks through LDS: the history keys up to the tile's last row, then (for
+// candidate rows) the block(s) holding the candidates' own diagonal.  Nothing
+// is renormalised across blocks — pointwise weights just add — so there is no
+// running max or rescaling, and blocks no row of a wave can attend are skipped.
+//
+// Per key block, per wave:
+//   S^T[key, query] = K_blk . Q^T        MFMA, A = K rows from LDS, B = Q in registers
+//   P = mask * SiLU(S^T + biases)        registers (lane = query, 16 keys)
+//   O^T[dv, query] += V^T_blk . P^T      MFMA, A = V^T from LDS, B = P straight
+//                                        from the S^T accumulators
+// The S^T accumulator of lane l holds keys 8*(r/4) + 4*(l/32) + (r%4); those
+// eight keys per k16 step are used as that MFMA's k-order for both operands,
+// so P never leaves registers.  V is transposed into LDS while staged.
+//
+// Output: AV minus its per-(row, head) mean over dv, in the layer dtype, plus
+// fp32 (mean, sum of squared deviations) per (row, head) for the LayerNorm.
+#include "common.h"
+#include "kernels.h"
+
+namespace hstu {
+
+template <typename T, int DQK, int DV>
+struct AttnCfg {
+  static constexpr int BM = kAttnBM, BN = kAttnBN, NW = BM / 32;
+  static constexpr int NT = NW * kWave;
+  static constexpr int V = Elem<T>::kVec;
+  static constexpr int LDK = DQK + 16 / (int)sizeof(T);  // K rows: +16 bytes
+  static constexpr int LDV = BN + 4;                     // V^T rows: +4 elements
+};
+
+struct AttnArgs {
+  const int64_t* off;
+  const int32_t* ncand;
+  const int64_t* ts;
+  const void* pos_tab;
+  const void* time_tab;
+  const void* q;
+  const void* k;
+  const void* v;
+  void* av;
+  float* stats;
+  const int2* tiles;
+  const int32_t* tiles_count;
+  int64_t T;
+  int H, P, NB, sbits, pos_stride, time_stride, norm_len, shared_pos;
+};
+
+template <typename T>
+__device__ __forceinline__ void store_pair(T* dst, T a, T b);
+template <>
+__device__ __forceinline__ void store_pair<bf16>(bf16* dst, bf16 a, bf16 b) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 v = {a, b};
+  *reinterpret_cast<bf16x2*>(dst) = v;
+}
+template <>
+__device__ __forceinline__ void store_pair<float>(float* dst, float a, float b) {
+  *reinterpret_cast<float2*>(dst) = make_float2(a, b);
+}
+
+// Eight V^T values for one MFMA k16 step: keys base+0..3 and base+8..11.
+template <typename T>
+__device__ __forceinline__ typename Elem<T>::Frag vt_frag(const T* p);
+template <>
+__device__ __forceinline__ bf16x8 vt_frag<bf16>(const bf16* p) {
+  bf16x4 lo = *reinterpret_cast<const bf16x4*>(p);
+  bf16x4 hi = *reinterpret_cast<const bf16x4*>(p + 8);
+  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+template <>
+__device__ __forceinline__ f32x8 vt_frag<float>(const float* p) {
+  f32x4 lo = *reinterpret_cast<const f32x4*>(p);
+  f32x4 hi = *reinterpret_cast<const f32x4*>(p + 8);
+  return f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+template <typename T>
+__device__ __forceinline__ typename Elem<T>::Frag to_frag(const float* p);
+template <>
+__device__ __forceinline__ bf16x8 to_frag<bf16>(const float* p) {
+  bf16x8 f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f[e] = (bf16)p[e];
+  return f;
+}
+template <>
+__device__ __forceinline__ f32x8 to_frag<float>(const float* p) {
+  f32x8 f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f[e] = p[e];
+  return f;
+}
+
+template <typename T, int DQK, int DV>
+__global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
+  typedef AttnCfg<T, DQK, DV> C;
+  static_assert(C::NT == 256, "launch bounds assume 4 waves");
+  typedef typename Elem<T>::Frag Frag;
+  __shared__ __attribute__((aligned(16))) T Ks[C::BN * C::LDK];
+  __shared__ __attribute__((aligned(16))) T Vts[DV * C::LDV];
+  __shared__ int64_t ts_s[C::BN];
+  extern __shared__ float tabs[];  // [P] position table then [NB] time table, head h
+  float* pos_s = tabs;
+  float* time_s = tabs + a.P;
+
+  const int H = a.H;
+  const int h = blockIdx.x % H;
+  const int item = blockIdx.x / H;
+  if (item >= *a.tiles_count) return;
+  const int2 tl = a.tiles[item];
+  const SeqInfo si = seq_info(a.off, a.ncand, tl.x, a.T);
+  const int L = si.len, nh = si.nhist;
+  const int64_t s0 = si.start;
+  const int i0 = tl.y * C::BM;
+  const int iend = min(i0 + C::BM, L);
+  const float inv_n = 1.0f / (float)(a.norm_len > 0 ? a.norm_len : L);
+  const int R = (a.P - 1) / 2;
+  const bool shared = a.shared_pos != 0;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, half = lane >> 5;
+
+  // Bias tables of head h, as fp32, into LDS.
+  for (int i = tid; i < a.P; i += C::NT)
+    pos_s[i] = to_f32(reinterpret_cast<const T*>(a.pos_tab)[(int64_t)h * a.pos_stride + i]);
+  for (int i = tid; i < a.NB; i += C::NT)
+    time_s[i] = to_f32(reinterpret_cast<const T*>(a.time_tab)[(int64_t)h * a.time_stride + i]);
+
+  // This lane's query row and its operand fragments.
+  const int r0 = i0 + 32 * w;
+  const int rlast = min(r0 + 31, iend - 1);
+  const int iq = r0 + l32;
+  const bool qvalid = iq < iend;
+  const T* qbase = reinterpret_cast<const T*>(a.q) + ((int64_t)h * a.T + s0 + iq) * DQK;
+  Frag qf[DQK / 16];
+#pragma unroll
+  for (int c = 0; c < DQK / 16; ++c) {
+    if (qvalid) {
+      qf[c] = *reinterpret_cast<const Frag*>(qbase + 16 * c + 8 * half);
+    } else {
+      qf[c] = Frag{};
+    }
+  }
+  const int64_t ts_q = qvalid ? a.ts[s0 + iq] : 0;
+  const int p_q = position(iq, nh, shared);
+
+  f32x16 o[DV / 32];
+#pragma unroll
+  for (int n = 0; n < DV / 32; ++n) o[n] = f32x16{};
+
+  // Key blocks: history [0, min(iend, nh)), then the candidates' own rows.
+  const int a_end = min(iend, nh);
+  const int nblk_a = (a_end + C::BN - 1) / C::BN;
+  const int b_lo = max(i0, nh), b_hi = iend;
+  const int jb0 = max(nblk_a * C::BN, (b_lo / C::BN) * C::BN);
+  const int nblk_b = (b_lo < b_hi && jb0 < b_hi) ? (b_hi - jb0 + C::BN - 1) / C::BN : 0;
+  const int nblk = nblk_a + nblk_b;
+
+  const T* kg = reinterpret_cast<const T*>(a.k) + ((int64_t)h * a.T + s0) * DQK;
+  const T* vg = reinterpret_cast<const T*>(a.v) + ((int64_t)h * a.T + s0) * DV;
+
+  for (int blk = 0; blk < nblk; ++blk) {
+    const int j0 = blk < nblk_a ? blk * C::BN : jb0 + (blk - nblk_a) * C::BN;
+    __syncthreads();  // previous block's LDS reads are done (and tables written)
+    // Stage K rows [j0, j0 + BN) and V^T, zero beyond the sequence.
+    constexpr int KCH = C::BN * DQK / C::V;
+    for (int idx = tid; idx < KCH; idx += C::NT) {
+      const int jl = idx / (DQK / C::V), cc = (idx % (DQK / C::V)) * C::V;
+      const int j = j0 + jl;
+      uint4 val = j < L ? ld16(kg + (int64_t)j * DQK + cc) : make_uint4(0, 0, 0, 0);
+      st16(Ks + jl * C::LDK + cc, val);
+    }
+    constexpr int VCH = (C::BN / 2) * (DV / C::V);
+    for (int idx = tid; idx < VCH; idx += C::NT) {
+      const int kp = idx % (C::BN / 2), cc = (idx / (C::BN / 2)) * C::V;
+      const int j = j0 + 2 * kp;
+      uint4 v0 = j < L ? ld16(vg + (int64_t)j * DV + cc) : make_uint4(0, 0, 0, 0);
+      uint4 v1 = j + 1 < L ? ld16(vg + (int64_t)(j + 1) * DV + cc) : make_uint4(0, 0, 0, 0);
+      const T* e0 = reinterpret_cast<const T*>(&v0);
+      const T* e1 = reinterpret_cast<const T*>(&v1);
+#pragma unroll
+      for (int e = 0; e < C::V; ++e) store_pair<T>(Vts + (cc + e) * C::LDV + 2 * kp, e0[e], e1[e]);
+    }
+    if (tid < C::BN) ts_s[tid] = (j0 + tid < L) ? a.ts[s0 + j0 + tid] : 0;
+    __syncthreads();
+
+    // Can any row of this wave attend to any key of the block?
+    if (r0 >= iend) continue;
+    const bool any_hist = j0 < nh && j0 <= rlast;
+    const bool any_self = max(max(r0, nh), j0) <= min(rlast, j0 + C::BN - 1);
+    if (!any_hist && !any_self) continue;
+    const bool full = (j0 + C::BN - 1 <= r0) && (j0 + C::BN <= nh);
+
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      f32x16 s = f32x16{};
+#pragma unroll
+      for (int c = 0; c < DQK / 16; ++c) {
+        const Frag kf = *reinterpret_cast<const Frag*>(Ks + (kh * 32 + l32) * C::LDK + 16 * c + 8 * half);
+        s = mma_k16(kf, qf[c], s);
+      }
+      float p[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int jl = kh * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
+        const int j = j0 + jl;
+        const int bp = pos_bucket(p_q, position(j, nh, shared), R);
+        const int bt = time_bucket(wrap_sub(ts_q, ts_s[jl]), a.NB, a.sbits);
+        float val = silu(s[r] + pos_s[bp] + time_s[bt]);
+        if (!full && !attends(iq, j, nh)) val = 0.f;
+        p[r] = val;
+      }
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        const Frag pf = to_frag<T>(p + 8 * c2);
+#pragma unroll
+        for (int n = 0; n < DV / 32; ++n) {
+          const Frag vf = vt_frag<T>(Vts + (n * 32 + l32) * C::LDV + kh * 32 + 16 * c2 + 4 * half);
+          o[n] = mma_k16(vf, pf, o[n]);
+        }
+      }
+    }
+  }
+
+  // Epilogue: scale by 1/N_b, per-(row, head) mean and M2 over dv, centred AV.
+  if (r0 >= iend) return;
+  float sum = 0.f;
+#pragma unroll
+  for (int n = 0; n < DV / 32; ++n)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      o[n][r] *= inv_n;
+      sum += o[n][r];
+    }
+  sum += __shfl_xor(sum, 32, kWave);
+  const float mean = sum / (float)DV;
+  float m2 = 0.f;
+#pragma unroll
+  for (int n = 0; n < DV / 32; ++n)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float dlt = o[n][r] - mean;
+      m2 += dlt * dlt;
+    }
+  m2 += __shfl_xor(m2, 32, kWave);
+  if (!qvalid) return;
+  const int64_t row = s0 + iq;
+  T* dst = reinterpret_cast<T*>(a.av) + row * (int64_t)(H * DV) + h * DV;
+#pragma unroll
+  for (int n = 0; n < DV / 32; ++n)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      // rows 8g + 4*half + 0..3 of this 32-wide dv tile are consecutive
+      T* p = dst + n * 32 + 8 * g + 4 * half;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) p[e] = from_f32<T>(o[n][4 * g + e] - mean);
+    }
+  if (half == 0) {
+    a.stats[(row * H + h) * 2] = mean;
+    a.stats[(row * H + h) * 2 + 1] = m2;
+  }
+}
+
+template <typename T, int DQK, int DV>
+static hipError_t launch_t(const AttnArgs& a, int64_t grid, hipStream_t s) {
+  const size_t shmem = (size_t)(a.P + a.NB) * sizeof(float);
+  hipLaunchKernelGGL((attn_kernel<T, DQK, DV>), dim3((unsigned)grid), dim3(AttnCfg<T, DQK, DV>::NT),
+                     shmem, s, a);
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_dims(const AttnArgs& a, int dqk, int dv, int64_t grid, hipStream_t s) {
+#define HSTU_ATTN_CASE(Q, V_) \
+  if (dqk == Q && dv == V_) return launch_t<T, Q, V_>(a, grid, s);
+  HSTU_ATTN_CASE(32, 32)
+  HSTU_ATTN_CASE(32, 64)
+  HSTU_ATTN_CASE(32, 128)
+  HSTU_ATTN_CASE(64, 32)
+  HSTU_ATTN_CASE(64, 64)
+  HSTU_ATTN_CASE(64, 128)
+  HSTU_ATTN_CASE(128, 32)
+  HSTU_ATTN_CASE(128, 64)
+  HSTU_ATTN_CASE(128, 128)
+#undef HSTU_ATTN_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_attn(const hstu_desc& d, const int64_t* off, const int32_t* ncand, int32_t B,
+                       int64_t T, const int64_t* ts, const hstu_bias_tables& tab, const void* q,
+                       const void* k, const void* v, void* av, float* stats, const int2* tiles,
+                       const int32_t* tiles_count, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  AttnArgs a;
+  a.off = off;
+  a.ncand = ncand;
+  a.ts = ts;
+  a.pos_tab = tab.pos;
+  a.time_tab = tab.time;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.av = av;
+  a.stats = stats;
+  a.tiles = tiles;
+  a.tiles_count = tiles_count;
+  a.T = T;
+  a.H = d.num_heads;
+  a.P = d.pos_buckets;
+  a.NB = d.time_buckets;
+  a.sbits = d.time_sub_bits;
+  a.pos_stride = tab.pos_head_stride;
+  a.time_stride = tab.time_head_stride;
+  a.norm_len = d.norm_len;
+  a.shared_pos = (d.flags & HSTU_CAND_SHARED_POS) ? 1 : 0;
+  const int64_t grid = attn_max_tiles(T, B) * d.num_heads;
+  if (d.dtype == HSTU_BF16) return launch_dims<bf16>(a, d.dqk, d.dv, grid, s);
+  return launch_dims<float>(a, d.dqk, d.dv, grid, s);
+}
+
+}  // namespace hstu

@@ -1,0 +1,152 @@
+// Device-side building blocks shared by the HSTU kernels (gfx950 / CDNA4).
+//
+// MFMA convention used everywhere: one "k16 step" of a 32x32 output tile.
+//   A operand  lane l holds row (l % 32) and the eight k-values 8*(l/32) .. +7
+//   B operand  lane l holds column (l % 32) and the same eight k-values
+//   C (f32x16) lane l holds column (l % 32), rows 8*(r/4) + 4*(l/32) + (r%4)
+// For bf16 that is one v_mfma_f32_32x32x16_bf16.  For fp32 it is eight
+// v_mfma_f32_32x32x2_f32, the e-th contracting k-value e of each lane half; the
+// output layout is identical, so every kernel is written once for both types.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hstu {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+template <typename T>
+struct Elem;
+template <>
+struct Elem<bf16> {
+  typedef bf16x8 Frag;                 // one k16 step of an MFMA operand
+  static constexpr int kVec = 8;       // elements per 16-byte vector
+};
+template <>
+struct Elem<float> {
+  typedef f32x8 Frag;
+  static constexpr int kVec = 4;
+};
+
+__device__ __forceinline__ float to_f32(bf16 v) { return (float)v; }
+__device__ __forceinline__ float to_f32(float v) { return v; }
+template <typename T>
+__device__ __forceinline__ T from_f32(float v);
+template <>
+__device__ __forceinline__ bf16 from_f32<bf16>(float v) { return (bf16)v; }
+template <>
+__device__ __forceinline__ float from_f32<float>(float v) { return v; }
+
+__device__ __forceinline__ f32x16 mma_k16(const bf16x8& a, const bf16x8& b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mma_k16(const f32x8& a, const f32x8& b, f32x16 c) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], b[e], c, 0, 0, 0);
+  return c;
+}
+
+// 16-byte vector load/store of kVec elements.
+template <typename T>
+__device__ __forceinline__ uint4 ld16(const T* p) { return *reinterpret_cast<const uint4*>(p); }
+template <typename T>
+__device__ __forceinline__ void st16(T* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
+
+__device__ __forceinline__ void unpack(const uint4& v, float (&o)[8], bf16) {
+  const bf16* e = reinterpret_cast<const bf16*>(&v);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = (float)e[i];
+}
+__device__ __forceinline__ void unpack(const uint4& v, float (&o)[4], float) {
+  const float* e = reinterpret_cast<const float*>(&v);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = e[i];
+}
+__device__ __forceinline__ uint4 pack(const float (&o)[8], bf16) {
+  uint4 v;
+  bf16* e = reinterpret_cast<bf16*>(&v);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) e[i] = (bf16)o[i];
+  return v;
+}
+__device__ __forceinline__ uint4 pack(const float (&o)[4], float) {
+  uint4 v;
+  float* e = reinterpret_cast<float*>(&v);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) e[i] = o[i];
+  return v;
+}
+
+// SiLU(z) = z * sigmoid(z) = z / (1 + 2^(-z*log2(e))).  For z < -88 the power
+// overflows to +inf and the quotient is -0, the correct limit; no NaN arises.
+__device__ __forceinline__ float silu(float z) {
+  float e = __builtin_amdgcn_exp2f(z * -1.4426950408889634f);
+  return z * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// ---------------------------------------------------------------- indexing
+// Jagged metadata, clamped so that malformed offsets or candidate counts can
+// never address rows outside [0, T).
+struct SeqInfo {
+  int64_t start;  // first flat row
+  int32_t len;    // L_b
+  int32_t nhist;  // n_b = L_b - m_b
+};
+
+__device__ __forceinline__ SeqInfo seq_info(const int64_t* off, const int32_t* ncand, int b,
+                                            int64_t T) {
+  int64_t s0 = off[b], s1 = off[b + 1];
+  s0 = s0 < 0 ? 0 : (s0 > T ? T : s0);
+  s1 = s1 < s0 ? s0 : (s1 > T ? T : s1);
+  SeqInfo si;
+  si.start = s0;
+  si.len = (int32_t)(s1 - s0);
+  int32_t m = ncand ? ncand[b] : 0;
+  m = m < 0 ? 0 : (m > si.len ? si.len : m);
+  si.nhist = si.len - m;
+  return si;
+}
+
+// Log-bucketed time difference: 0 for dt <= 0, else 1 + (k << s) + the s bits
+// right below the leading one of dt, k = floor(log2 dt), capped at nb - 1.
+__device__ __forceinline__ int time_bucket(int64_t dt, int nb, int s) {
+  if (dt <= 0) return 0;
+  int k = 63 - __clzll((unsigned long long)dt);
+  int64_t below = (k >= s) ? (dt >> (k - s)) : (dt << (s - k));
+  int b = 1 + (k << s) + (int)(below & ((1 << s) - 1));
+  return b < nb - 1 ? b : nb - 1;
+}
+
+__device__ __forceinline__ int64_t wrap_sub(int64_t a, int64_t b) {
+  return (int64_t)((uint64_t)a - (uint64_t)b);
+}
+
+__device__ __forceinline__ int pos_bucket(int pi, int pj, int R) {
+  int d = pi - pj;
+  d = d < -R ? -R : (d > R ? R : d);
+  return d + R;
+}
+
+__device__ __forceinline__ int position(int i, int nhist, bool shared) {
+  return shared ? (i < nhist ? i : nhist) : i;
+}
+
+__device__ __forceinline__ bool attends(int i, int j, int nhist) {
+  return j <= i && (j < nhist || j == i);
+}
+
+}  // namespace hstu

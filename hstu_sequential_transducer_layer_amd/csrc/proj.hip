@@ -1,0 +1,101 @@
+// Stage 1: U, V, Q, K = Split(SiLU(f1(x~))) — page "4.4 Scaling
+// Recommendation Models", section "Generative Recommenders and HSTU" (first
+// layer equation) and section "Code" (f1 then SiLU, chunked u | v | q | k,
+// head h owning contiguous columns of each chunk).
+//
+// One MFMA GEMM over all packed rows of the jagged batch (the rows of a jagged
+// batch are just tokens here), with +b1 and SiLU in the epilogue, and the
+// result scattered straight into the layouts the attention kernel streams:
+//   U [T, H*dv] row-major, V [H, T, dv], Q [H, T, dqk], K [H, T, dqk].
+#include "common.h"
+#include "gemm.h"
+#include "kernels.h"
+
+namespace hstu {
+
+template <typename T>
+struct RowLoader {
+  const T* __restrict__ a;
+  int64_t row0, M;
+  int K;
+  __device__ __forceinline__ uint4 operator()(int k0, int r, int kc) const {
+    const int64_t row = row0 + r;
+    const int k = k0 + kc;
+    return (row < M && k < K) ? ld16(a + row * K + k) : make_uint4(0, 0, 0, 0);
+  }
+};
+
+template <typename T>
+__global__ __launch_bounds__(256, 2) void proj_kernel(const T* __restrict__ xn, const T* __restrict__ w1,
+                                                      const T* __restrict__ b1, T* __restrict__ u,
+                                                      T* __restrict__ v, T* __restrict__ q,
+                                                      T* __restrict__ k, int64_t M, int N, int K,
+                                                      int H, int dqk, int dv) {
+  typedef GemmTile<T> G;
+  __shared__ __attribute__((aligned(16))) T As[G::BM * G::LDK];
+  __shared__ __attribute__((aligned(16))) T Bs[G::BN * G::LDK];
+  const int nrow = (int)((M + G::BM - 1) / G::BM), ncol = (N + G::BN - 1) / G::BN;
+  int tr, tc;
+  map_tile(blockIdx.x, nrow, ncol, tr, tc);
+  const int64_t row0 = (int64_t)tr * G::BM;
+  const int col0 = tc * G::BN;
+  RowLoader<T> al{xn, row0, M, K};
+  f32x16 acc[2][2];
+  gemm_mainloop<T>(al, w1, col0, N, K, As, Bs, acc);
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
+  const int HDV = H * dv, HDQ = H * dqk;
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int cb = col0 + wn * 64 + nt * 32;  // first column of this 32-wide tile
+    if (cb >= N) continue;
+    const int col = cb + (lane & 31);
+    const float bias = to_f32(b1[col]);
+    // Destination of this tile's columns: all 32 lie in one chunk and one head.
+    T* base;
+    int64_t rstride;
+    if (cb < HDV) {
+      base = u + col;
+      rstride = HDV;
+    } else if (cb < 2 * HDV) {
+      const int c = cb - HDV, h = c / dv;
+      base = v + (int64_t)h * M * dv + (c % dv) + (lane & 31);
+      rstride = dv;
+    } else if (cb < 2 * HDV + HDQ) {
+      const int c = cb - 2 * HDV, h = c / dqk;
+      base = q + (int64_t)h * M * dqk + (c % dqk) + (lane & 31);
+      rstride = dqk;
+    } else {
+      const int c = cb - 2 * HDV - HDQ, h = c / dqk;
+      base = k + (int64_t)h * M * dqk + (c % dqk) + (lane & 31);
+      rstride = dqk;
+    }
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = row0 + acc_row(wm, mt, lane, r);
+        if (row < M) base[row * rstride] = from_f32<T>(silu(acc[mt][nt][r] + bias));
+      }
+    }
+  }
+}
+
+hipError_t launch_proj(const hstu_desc& d, const void* xn, int64_t T, const void* w1,
+                       const void* b1, void* u, void* v, void* q, void* k, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const int N = 2 * d.num_heads * (d.dqk + d.dv), K = d.d_model;
+  const int64_t nrow = (T + 127) / 128, ncol = (N + 127) / 128;
+  dim3 grid((unsigned)(nrow * ncol)), block(256);
+  if (d.dtype == HSTU_BF16)
+    hipLaunchKernelGGL(proj_kernel<bf16>, grid, block, 0, s, (const bf16*)xn, (const bf16*)w1,
+                       (const bf16*)b1, (bf16*)u, (bf16*)v, (bf16*)q, (bf16*)k, T, N, K,
+                       d.num_heads, d.dqk, d.dv);
+  else
+    hipLaunchKernelGGL(proj_kernel<float>, grid, block, 0, s, (const float*)xn, (const float*)w1,
+                       (const float*)b1, (float*)u, (float*)v, (float*)q, (float*)k, T, N, K,
+                       d.num_heads, d.dqk, d.dv);
+  return hipGetLastError();
+}
+
+}  // namespace hstu

@@ -1,0 +1,197 @@
+/*
+ * hstu.h — C ABI of libhstu: the HSTU layer forward over jagged sequences on
+ * AMD MI355X (gfx950).
+ *
+ * What is computed (sources cited by page title and section):
+ *   [SRM] "4.4 Scaling Recommendation Models", section "Generative
+ *         Recommenders and HSTU" — the layer's three equations:
+ *           U, V, Q, K = Split(SiLU(f1(X)))
+ *           AV         = SiLU(Q K^T + rab^{p,t}) V      (pointwise, no softmax)
+ *           Y          = f2(Norm(AV) * U)
+ *         the bullets under them (SiLU weights with a constant normaliser such
+ *         as the sequence length; bias from position and time difference), the
+ *         "Efficiency tricks" paragraph (variable-length sequences; candidates
+ *         appended to the history see the history but not one another), and
+ *         section "Code" (LayerNorm before f1, u|v|q|k chunk order, lower
+ *         triangular mask with the diagonal, division by n, LayerNorm over the
+ *         merged heads, gate by u, f2, residual add).
+ *   [FRC] "HSTU: The First Exploration of the Scaling Law", 7.1.4 Innovations
+ *         1-2 (LayerNorm(AV) * U; bias on p_i - p_j and t_i - t_j) and 7.1.5
+ *         M-FALCON layer 1 (batched candidates under a mask).
+ *
+ * Per sequence b with L_b tokens whose last m_b are candidates
+ * (n_b = L_b - m_b history tokens), local query i, key j:
+ *   x~      = LayerNorm_in(x)                   if HSTU_INPUT_NORM, else x
+ *   u|v|q|k = SiLU(x~ W1^T + b1)                split in that order; head h owns
+ *                                               columns h*dh .. h*dh+dh-1 of a block
+ *   M_ij    = (j <= i) && (j < n_b || j == i)
+ *   p(i)    = min(i, n_b) if HSTU_CAND_SHARED_POS else i
+ *   bp      = clamp(p(i) - p(j), -R, R) + R,     R = (pos_buckets - 1) / 2
+ *   dt      = ts[i] - ts[j]  (int64 seconds, two's-complement wrap)
+ *   bt      = dt <= 0 ? 0 : min(NB - 1, 1 + (k << s) + sub),  k = floor(log2 dt),
+ *             sub = the s = time_sub_bits bits right below dt's leading one
+ *   AV_i^h  = (1/N_b) sum_j M_ij SiLU(q_i^h . k_j^h + pos[h][bp] + time[h][bt]) v_j^h
+ *             N_b = L_b, or norm_len when norm_len > 0 (no 1/sqrt(d) scale)
+ *   Z       = LayerNorm_av(concat_h AV^h) * u   (over H*dv, biased variance)
+ *   Y       = Z W2^T + b2 (+ x if HSTU_RESIDUAL)
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers owned by the caller; the library keeps
+ *     none after returning and allocates no device memory (scratch comes from
+ *     the caller's workspace).
+ *   - Work is enqueued on `stream` and runs asynchronously.  The returned status
+ *     covers host-side validation and launch errors only; faults inside kernels
+ *     surface at the caller's next synchronisation.
+ *   - Errors: a non-HSTU_OK status leaves every output untouched (validation
+ *     happens before any launch); hstu_last_error() returns a thread-local
+ *     message describing the last failure on the calling thread.
+ *   - Thread-safe and stateless: concurrent calls on different streams with
+ *     disjoint outputs and workspaces are independent.
+ *   - Floating tensors (x, out, weights, LayerNorm parameters, bias tables) all
+ *     have the layer dtype; offsets and timestamps are int64, candidate counts
+ *     int32.  Floating tensors must be 16-byte aligned, int64 arrays 8-byte,
+ *     int32 arrays 4-byte.
+ *   - Device-side robustness: offsets are clamped to [0, T] and made
+ *     non-decreasing, candidate counts to [0, L_b], so malformed metadata
+ *     cannot cause out-of-bounds accesses (the result is then unspecified).
+ *     HSTU_VALIDATE checks them exactly instead (it synchronises the stream).
+ */
+#ifndef HSTU_H_
+#define HSTU_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* hstu_stream_t; /* a hipStream_t; NULL = default stream */
+
+typedef enum {
+  HSTU_OK = 0,
+  HSTU_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size, bad metadata */
+  HSTU_ERR_UNSUPPORTED = 2, /* a dimension or dtype this build has no kernel for */
+  HSTU_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
+  HSTU_ERR_DEVICE = 4       /* a HIP launch or copy returned an error */
+} hstu_status;
+
+typedef enum { HSTU_F32 = 0, HSTU_BF16 = 1 } hstu_dtype;
+
+enum {
+  HSTU_INPUT_NORM = 1u << 0,      /* LayerNorm on x before f1 ([SRM] "Code")        */
+  HSTU_RESIDUAL = 1u << 1,        /* Y += x ([SRM] "Code")                           */
+  HSTU_CAND_SHARED_POS = 1u << 2, /* candidates all take position n_b (M-FALCON)     */
+  HSTU_VALIDATE = 1u << 3         /* copy metadata to the host, check, synchronise   */
+};
+
+typedef struct {
+  int32_t d_model;       /* model width d; multiple of 32, 32..8192            */
+  int32_t num_heads;     /* H; 1..64                                           */
+  int32_t dqk;           /* query/key width per head: 32, 64 or 128            */
+  int32_t dv;            /* value width per head: 32, 64 or 128                */
+  int32_t pos_buckets;   /* P, odd, 1..2047; R = (P-1)/2                        */
+  int32_t time_buckets;  /* NB, 1..2048                                         */
+  int32_t time_sub_bits; /* s, 0..4                                             */
+  hstu_dtype dtype;      /* arithmetic/storage type of every floating tensor    */
+  uint32_t flags;        /* HSTU_* bits                                         */
+  float ln_eps;          /* LayerNorm epsilon (> 0), e.g. 1e-5                  */
+  int32_t norm_len;      /* 0: divide by L_b; > 0: divide by this constant      */
+} hstu_desc;
+
+/* Layer parameters, nn.Linear layouts (row n of W is output feature n).      */
+typedef struct {
+  const void* w1;      /* [2H(dqk+dv), d]: rows U | V | Q | K, heads contiguous */
+  const void* b1;      /* [2H(dqk+dv)]                                          */
+  const void* w2;      /* [d, H*dv]                                             */
+  const void* b2;      /* [d]                                                   */
+  const void* ln_in_g; /* [d]    gain of the input LayerNorm (HSTU_INPUT_NORM)  */
+  const void* ln_in_b; /* [d]    offset of the input LayerNorm                  */
+  const void* ln_av_g; /* [H*dv] gain of the LayerNorm over the merged heads    */
+  const void* ln_av_b; /* [H*dv] offset                                         */
+} hstu_weights;
+
+/* Relative-attention-bias tables.  Entry (h, idx) is at ptr[h*stride + idx];
+ * a head stride of 0 shares one table across heads.                          */
+typedef struct {
+  const void* pos;   /* >= [P]  position-difference table                      */
+  const void* time;  /* >= [NB] log-bucketed time-difference table             */
+  int32_t pos_head_stride;
+  int32_t time_head_stride;
+} hstu_bias_tables;
+
+/* Intermediate activations, the hand-off between the three stages.          */
+typedef struct {
+  void* u;         /* [T, H*dv]  gate                                          */
+  void* v;         /* [H, T, dv] values, head-major                            */
+  void* q;         /* [H, T, dqk]                                              */
+  void* k;         /* [H, T, dqk]                                              */
+  void* av;        /* [T, H*dv]  AV^h minus its mean over dv (per row, head)   */
+  float* av_stats; /* [T, H, 2]  fp32 mean over dv and sum of squared
+                      deviations over dv of AV^h, per (row, head)             */
+} hstu_activations;
+
+/* Bytes of workspace hstu_layer_fwd needs for T tokens in B sequences.       */
+size_t hstu_workspace_size(const hstu_desc* desc, int64_t total_tokens, int32_t batch);
+
+/* The layer forward ([SRM] three equations, "Code" sketch; [FRC] 7.1.4-7.1.5).
+ *   x               [T, d]   input rows, sequences packed back to back
+ *   seq_offsets     [B+1]    int64; sequence b owns rows off[b] .. off[b+1]-1,
+ *                            off[0] = 0, off[B] = T; empty sequences allowed
+ *   timestamps      [T]      int64 seconds
+ *   num_candidates  [B]      int32 trailing candidate tokens per sequence, or
+ *                            NULL for none (pure causal)
+ *   out             [T, d]   may alias x
+ *   workspace       >= hstu_workspace_size(desc, T, B) bytes, 256-aligned
+ * Returns HSTU_OK after enqueuing all kernels on `stream`.                    */
+hstu_status hstu_layer_fwd(const hstu_desc* desc, const void* x, const int64_t* seq_offsets,
+                           int32_t batch, int64_t total_tokens, const int64_t* timestamps,
+                           const int32_t* num_candidates, const hstu_weights* weights,
+                           const hstu_bias_tables* tables, void* out, void* workspace,
+                           size_t workspace_bytes, hstu_stream_t stream);
+
+/* Stage 1 ([SRM] first equation and the "Code" LayerNorm before f1): input
+ * LayerNorm, f1, SiLU, split into acts->u, v, q, k.  Needs
+ * hstu_proj_workspace_size() bytes of workspace (the normalised x).          */
+size_t hstu_proj_workspace_size(const hstu_desc* desc, int64_t total_tokens);
+hstu_status hstu_proj_fwd(const hstu_desc* desc, const void* x, int64_t total_tokens,
+                          const hstu_weights* weights, const hstu_activations* acts,
+                          void* workspace, size_t workspace_bytes, hstu_stream_t stream);
+
+/* Stage 2 ([SRM] second equation and bullets; [FRC] 7.1.4 Innovations 1-2,
+ * 7.1.5 candidate mask): reads acts->q, k, v; writes acts->av and
+ * acts->av_stats.  Needs hstu_attn_workspace_size() bytes (the work list).    */
+size_t hstu_attn_workspace_size(const hstu_desc* desc, int64_t total_tokens, int32_t batch);
+hstu_status hstu_attn_fwd(const hstu_desc* desc, const int64_t* seq_offsets, int32_t batch,
+                          int64_t total_tokens, const int64_t* timestamps,
+                          const int32_t* num_candidates, const hstu_bias_tables* tables,
+                          const hstu_activations* acts, void* workspace, size_t workspace_bytes,
+                          hstu_stream_t stream);
+
+/* Stage 3 ([SRM] third equation, "Code" LayerNorm over merged heads, gate,
+ * f2, residual; [FRC] 7.1.4 LayerNorm(AV) * U): reads acts->u, av, av_stats
+ * (and x for the residual); writes out [T, d].  If z_out is not NULL the
+ * gated normalised tensor Z [T, H*dv] is also written (for inspection).      */
+hstu_status hstu_out_fwd(const hstu_desc* desc, const void* x, int64_t total_tokens,
+                         const hstu_weights* weights, const hstu_activations* acts, void* out,
+                         void* z_out, hstu_stream_t stream);
+
+/* Integer indexing used by stage 2, for inspection: for each flat pair
+ * (query row, key row) in pairs[n_pairs][2] (int64, device) writes
+ * out[n][0..5] = {b, i, j, bp, bt, mask} (int64, device) with the definitions
+ * above; pairs whose key lies outside the query's sequence get b = -1 and
+ * zeros.  Out-of-range rows are an HSTU_ERR_INVALID_ARG only under
+ * HSTU_VALIDATE; otherwise they yield b = -1.                                */
+hstu_status hstu_debug_indices(const hstu_desc* desc, const int64_t* seq_offsets, int32_t batch,
+                               int64_t total_tokens, const int64_t* timestamps,
+                               const int32_t* num_candidates, const int64_t* pairs,
+                               int64_t n_pairs, int64_t* out, hstu_stream_t stream);
+
+const char* hstu_status_str(hstu_status status);
+const char* hstu_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HSTU_H_ */

@@ -217,20 +217,42 @@ def layer_forward(x, offsets, timestamps, num_candidates, prm, cfg, rows=None):
     u, v, q, k = project(x, prm, cfg)
     sel = np.arange(T, dtype=I64) if rows is None else np.asarray(rows, I64)
     av = attention(q, k, v, offsets, timestamps, num_candidates, prm, cfg, rows=sel)
-    ln_av = layer_norm(av, prm["ln_av_g"], prm["ln_av_b"], cfg.ln_eps)
-    z = ln_av * u[sel]
+    out = gate_and_project(av, u[sel], x[sel], prm, cfg)
+    return {"u": u, "v": v, "q": q, "k": k, "av": av, "ln_av": out["ln_av"], "z": out["z"],
+            "y": out["y"], "rows": sel}
+
+
+def gate_and_project(av, u, x, prm, cfg):
+    """Steps 4-5: Z = LayerNorm(AV) * U over the merged heads, Y = Z W2^T + b2
+    (+ x when cfg.residual).  Rows of av, u and x correspond one to one."""
+    ln_av = layer_norm(_f64(av), prm["ln_av_g"], prm["ln_av_b"], cfg.ln_eps)
+    z = ln_av * _f64(u)
     y = z @ _f64(prm["w2"]).T + _f64(prm["b2"])
     if cfg.residual:
-        y = y + x[sel]
-    return {"u": u, "v": v, "q": q, "k": k, "av": av, "ln_av": ln_av, "z": z,
-            "y": y, "rows": sel}
+        y = y + _f64(x)
+    return {"ln_av": ln_av, "z": z, "y": y}
 
 
-def stack_forward(x, offsets, timestamps, num_candidates, layers, cfg):
-    """Layers applied in order, each to the previous output (all rows)."""
+def round_to_bf16(a: np.ndarray) -> np.ndarray:
+    """Nearest bf16 value (ties to even) of each float64 element, as float64,
+    rounding the float64 value directly (8 significant bits)."""
+    a = np.asarray(a, np.float64)
+    m, e = np.frexp(a)                 # a = m * 2^e, 0.5 <= |m| < 1
+    # bf16 keeps 8 significant bits: scale m to [128, 256) and round half to even
+    return np.ldexp(np.round(m * 256.0), e - 8)
+
+
+def stack_forward(x, offsets, timestamps, num_candidates, layers, cfg, io_dtype=None):
+    """Layers applied in order, each to the previous output (all rows).
+
+    io_dtype="bf16": each layer's output is rounded to bf16 before it becomes
+    the next layer's input, as in a stack whose layer inputs and outputs are
+    bf16 tensors; every layer's arithmetic stays float64."""
     h = _f64(x)
     for prm in layers:
         h = layer_forward(h, offsets, timestamps, num_candidates, prm, cfg)["y"]
+        if io_dtype == "bf16":
+            h = round_to_bf16(h)
     return h
 
 

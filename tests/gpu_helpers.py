@@ -1,0 +1,84 @@
+"""Shared helpers of the GPU parity tests: run the HIP stages through the C ABI,
+collect their taps as float64 NumPy arrays, and compare with the oracle."""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+from hstu_sequential_transducer_layer_amd import _lib, layer, synth
+
+FP32_TOL = 1e-4   # every tap: max |y - ref| / max(|ref|, rms(ref))
+BF16_TOL = 2e-2   # output y: max |y - ref| / rms(ref) (unit scale);
+                  # intermediate taps: max |y - ref| / max(|ref|, rms(ref)), since
+                  # storing a tap in bf16 alone costs up to 2^-9 |ref| per element
+
+
+def say(msg: str) -> None:
+    print(f"[gpu] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def gpu_taps(w: "synth.Workload", layer_idx: int = 0, x=None, flags_extra: int = 0,
+             want_z: bool = True):
+    """Run proj -> attn -> out through the stage entry points; returns numpy taps
+    u [T,H*dv], v/q/k [T,H,dh], av [T,H*dv] (centred value + head mean),
+    z [T,H*dv], y [T,d], plus the hstu_layer_fwd output y_layer."""
+    dev = layer.to_device(w)
+    desc = _lib.make_desc(w.dims, flags_extra)
+    prm = dev["layers"][layer_idx]
+    xin = dev["x"] if x is None else x
+    acts = _lib.proj_fwd(desc, xin, prm)
+    _lib.attn_fwd(desc, dev["offsets"], dev["timestamps"], dev["num_candidates"], prm, acts)
+    y, z = _lib.out_fwd(desc, xin, prm, acts, want_z=want_z)
+    y_layer = _lib.layer_fwd(desc, xin, dev["offsets"], dev["timestamps"],
+                             dev["num_candidates"], prm)
+    torch.cuda.synchronize()
+    f = lambda t: t.float().cpu().numpy().astype(np.float64)
+    H, dv = w.dims.num_heads, w.dims.dv
+    T = w.T
+    st = f(acts["av_stats"])                                   # [T, H, 2]
+    av = f(acts["av"]).reshape(T, H, dv) + st[:, :, :1]
+    return {
+        "u": f(acts["u"]),
+        "v": f(acts["v"]).transpose(1, 0, 2),
+        "q": f(acts["q"]).transpose(1, 0, 2),
+        "k": f(acts["k"]).transpose(1, 0, 2),
+        "av": av.reshape(T, H * dv),
+        "av_m2": st[:, :, 1],
+        "z": f(z) if z is not None else None,
+        "y": f(y),
+        "y_layer": f(y_layer),
+        "y_layer_raw": y_layer,
+        "y_raw": y,
+    }
+
+
+def err_bf16(got, ref) -> float:
+    ref = np.asarray(ref, np.float64)
+    rms = float(np.sqrt(np.mean(ref ** 2))) if ref.size else 1.0
+    if ref.size == 0:
+        return 0.0
+    return float(np.max(np.abs(np.asarray(got, np.float64) - ref)) / max(rms, 1e-30))
+
+
+def err_fp32(got, ref) -> float:
+    ref = np.asarray(ref, np.float64)
+    if ref.size == 0:
+        return 0.0
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    den = np.maximum(np.abs(ref), max(rms, 1e-30))
+    return float(np.max(np.abs(np.asarray(got, np.float64) - ref) / den))
+
+
+def check(name: str, got, ref, dtype: str, unit: bool = False) -> float:
+    """unit=True: the unit-scale criterion (bf16 outputs); else element-relative
+    with an rms floor."""
+    e = err_bf16(got, ref) if (unit and dtype == "bf16") else err_fp32(got, ref)
+    tol = FP32_TOL if dtype == "fp32" else BF16_TOL
+    say(f"  {name}: err {e:.3e} (tol {tol:.0e})")
+    assert np.all(np.isfinite(got)), f"{name}: non-finite values"
+    assert e <= tol, f"{name}: error {e:.3e} > {tol:.0e}"
+    return e

@@ -143,6 +143,13 @@ def test_silu_and_layernorm_against_torch():
     np.testing.assert_allclose(O.layer_norm(c, g, b, 1e-5), np.broadcast_to(b, (3, 40)), atol=0)
 
 
+def test_round_to_bf16_matches_torch():
+    a = np.random.default_rng(5).normal(0, 50, 200000).astype(np.float32)
+    a = np.concatenate([a, np.float32([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 0.0, 1e30])])
+    want = torch.from_numpy(a).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(O.round_to_bf16(a.astype(np.float64)), want)
+
+
 def _zero_qk(prm, dims):
     H, dqk, dv = dims.num_heads, dims.dqk, dims.dv
     prm = dict(prm)
