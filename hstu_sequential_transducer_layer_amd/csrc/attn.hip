@@ -106,6 +106,45 @@ __device__ __forceinline__ f32x8 to_frag<float>(const float* p) {
   return f;
 }
 
+// Scores -> pointwise weights for one 32-key half held by this lane (query
+// iq, keys jb + 8*(r/4) + (r%4) of the block).  MODE = tmode*4 + pos*2 + mask:
+//   tmode 0: the row's time bias is one value (c_lo)
+//   tmode 1: two values, c_hi for keys whose offset from the block's earliest
+//            timestamp is <= thr, else c_lo
+//   tmode 2: the log time bucket computed per pair
+//   pos:  relative-position bias per pair (else folded into c_lo/c_hi/cadd)
+//   mask: causal/candidate mask per pair (else every pair is attended)
+template <int MODE>
+__device__ __forceinline__ void elems(const f32x16& s, float (&p)[16], int jb, int j0, int iq, int nh,
+                                      int p_q, int R, bool shared, int64_t ts_q, int NB, int sbits,
+                                      float c_lo, float c_hi, float cadd, int32_t thr,
+                                      const float* pos_s, const float* time_s, const int64_t* ts_s,
+                                      const int32_t* rel_s) {
+  constexpr int TM = MODE >> 2;
+  constexpr bool POS = (MODE >> 1) & 1, MASK = MODE & 1;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int jl0 = jb + 8 * g;
+    int32_t rel[4];
+    if (TM == 1) {
+      const int4 rv = *reinterpret_cast<const int4*>(rel_s + jl0);
+      rel[0] = rv.x; rel[1] = rv.y; rel[2] = rv.z; rel[3] = rv.w;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 4 * g + e, jl = jl0 + e, j = j0 + jl;
+      float b;
+      if (TM == 0) b = c_lo;
+      else if (TM == 1) b = rel[e] <= thr ? c_hi : c_lo;
+      else b = time_s[time_bucket(wrap_sub(ts_q, ts_s[jl]), NB, sbits)] + cadd;
+      if (POS) b += pos_s[pos_bucket(p_q, position(j, nh, shared), R)];
+      float v = silu(s[r] + b);
+      if (MASK) v = attends(iq, j, nh) ? v : 0.f;
+      p[r] = v;
+    }
+  }
+}
+
 template <typename T, int DQK, int DV>
 __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
   typedef AttnCfg<T, DQK, DV> C;
@@ -114,6 +153,9 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) T Ks[C::BN * C::LDK];
   __shared__ __attribute__((aligned(16))) T Vts[DV * C::LDV];
   __shared__ int64_t ts_s[C::BN];
+  __shared__ __attribute__((aligned(16))) int32_t rel_s[C::BN];
+  __shared__ int64_t blk_ts[2];
+  __shared__ int32_t blk_flags[1];
   extern __shared__ float tabs[];  // [P] position table then [NB] time table, head h
   float* pos_s = tabs;
   float* time_s = tabs + a.P;
@@ -170,70 +212,156 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
   const int jb0 = max(nblk_a * C::BN, (b_lo / C::BN) * C::BN);
   const int nblk_b = (b_lo < b_hi && jb0 < b_hi) ? (b_hi - jb0 + C::BN - 1) / C::BN : 0;
   const int nblk = nblk_a + nblk_b;
+  auto block_start = [&](int blk) { return blk < nblk_a ? blk * C::BN : jb0 + (blk - nblk_a) * C::BN; };
 
   const T* kg = reinterpret_cast<const T*>(a.k) + ((int64_t)h * a.T + s0) * DQK;
   const T* vg = reinterpret_cast<const T*>(a.v) + ((int64_t)h * a.T + s0) * DV;
 
-  for (int blk = 0; blk < nblk; ++blk) {
-    const int j0 = blk < nblk_a ? blk * C::BN : jb0 + (blk - nblk_a) * C::BN;
-    __syncthreads();  // previous block's LDS reads are done (and tables written)
-    // Stage K rows [j0, j0 + BN) and V^T, zero beyond the sequence.
-    constexpr int KCH = C::BN * DQK / C::V;
-    for (int idx = tid; idx < KCH; idx += C::NT) {
+  // Register staging of one key block: K rows, V rows (two keys per item,
+  // transposed on the way into LDS) and, in wave 0, one key timestamp per
+  // lane.  Two workgroups share a CU, so one's loads overlap the other's MFMAs.
+  constexpr int KTOT = C::BN * DQK / C::V;                 // 16-byte K chunks per block
+  constexpr int VTOT = (C::BN / 2) * (DV / C::V);          // key-pair V items per block
+  constexpr int KCH = (KTOT + C::NT - 1) / C::NT, VCH = (VTOT + C::NT - 1) / C::NT;
+  uint4 rk[KCH], rv0[VCH], rv1[VCH];
+  int64_t rts = 0;
+  auto gload = [&](int j0) {
+#pragma unroll
+    for (int c = 0; c < KCH; ++c) {
+      const int idx = tid + c * C::NT;
       const int jl = idx / (DQK / C::V), cc = (idx % (DQK / C::V)) * C::V;
       const int j = j0 + jl;
-      uint4 val = j < L ? ld16(kg + (int64_t)j * DQK + cc) : make_uint4(0, 0, 0, 0);
-      st16(Ks + jl * C::LDK + cc, val);
+      rk[c] = (idx < KTOT && j < L) ? ld16(kg + (int64_t)j * DQK + cc) : make_uint4(0, 0, 0, 0);
     }
-    constexpr int VCH = (C::BN / 2) * (DV / C::V);
-    for (int idx = tid; idx < VCH; idx += C::NT) {
+#pragma unroll
+    for (int c = 0; c < VCH; ++c) {
+      const int idx = tid + c * C::NT;
       const int kp = idx % (C::BN / 2), cc = (idx / (C::BN / 2)) * C::V;
       const int j = j0 + 2 * kp;
-      uint4 v0 = j < L ? ld16(vg + (int64_t)j * DV + cc) : make_uint4(0, 0, 0, 0);
-      uint4 v1 = j + 1 < L ? ld16(vg + (int64_t)(j + 1) * DV + cc) : make_uint4(0, 0, 0, 0);
-      const T* e0 = reinterpret_cast<const T*>(&v0);
-      const T* e1 = reinterpret_cast<const T*>(&v1);
+      const bool in = idx < VTOT;
+      rv0[c] = (in && j < L) ? ld16(vg + (int64_t)j * DV + cc) : make_uint4(0, 0, 0, 0);
+      rv1[c] = (in && j + 1 < L) ? ld16(vg + (int64_t)(j + 1) * DV + cc) : make_uint4(0, 0, 0, 0);
+    }
+    if (w == 0) rts = (j0 + lane < L) ? a.ts[s0 + j0 + lane] : 0;
+  };
+  auto sstore = [&](int j0) {
+#pragma unroll
+    for (int c = 0; c < KCH; ++c) {
+      const int idx = tid + c * C::NT;
+      const int jl = idx / (DQK / C::V), cc = (idx % (DQK / C::V)) * C::V;
+      if (idx < KTOT) st16(Ks + jl * C::LDK + cc, rk[c]);
+    }
+#pragma unroll
+    for (int c = 0; c < VCH; ++c) {
+      const int idx = tid + c * C::NT;
+      if (idx >= VTOT) continue;
+      const int kp = idx % (C::BN / 2), cc = (idx / (C::BN / 2)) * C::V;
+      const T* e0 = reinterpret_cast<const T*>(&rv0[c]);
+      const T* e1 = reinterpret_cast<const T*>(&rv1[c]);
 #pragma unroll
       for (int e = 0; e < C::V; ++e) store_pair<T>(Vts + (cc + e) * C::LDV + 2 * kp, e0[e], e1[e]);
     }
-    if (tid < C::BN) ts_s[tid] = (j0 + tid < L) ? a.ts[s0 + j0 + tid] : 0;
-    __syncthreads();
+    if (w == 0) {
+      // Key timestamps, their min/max over the block's real keys, and their
+      // offsets from the minimum as int32 when the block spans < 2^31 s.
+      const bool valid = j0 + lane < L;
+      int64_t mn = valid ? rts : INT64_MAX, mx = valid ? rts : INT64_MIN;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        const int64_t omn = __shfl_xor(mn, o, kWave), omx = __shfl_xor(mx, o, kWave);
+        mn = omn < mn ? omn : mn;
+        mx = omx > mx ? omx : mx;
+      }
+      int64_t span;
+      const bool span_ok = !__builtin_sub_overflow(mx, mn, &span) && span <= INT32_MAX;
+      ts_s[lane] = rts;
+      rel_s[lane] = (valid && span_ok) ? (int32_t)(rts - mn) : INT32_MAX;
+      if (lane == 0) {
+        blk_ts[0] = mn;
+        blk_ts[1] = mx;
+        blk_flags[0] = span_ok ? 1 : 0;
+      }
+    }
+  };
+
+  const int pmin_q = position(r0, nh, shared);
+  if (nblk > 0) {
+    gload(block_start(0));
+    sstore(block_start(0));
+  }
+  __syncthreads();  // tables and the first key block are in LDS
+  const float cpos_far = pos_s[2 * R];  // bias of every pair at distance >= R
+
+  for (int blk = 0; blk < nblk; ++blk) {
+    const int j0 = block_start(blk);
 
     // Can any row of this wave attend to any key of the block?
-    if (r0 >= iend) continue;
     const bool any_hist = j0 < nh && j0 <= rlast;
     const bool any_self = max(max(r0, nh), j0) <= min(rlast, j0 + C::BN - 1);
-    if (!any_hist && !any_self) continue;
-    const bool full = (j0 + C::BN - 1 <= r0) && (j0 + C::BN <= nh);
+    if (r0 < iend && (any_hist || any_self)) {
+      const bool full = (j0 + C::BN - 1 <= r0) && (j0 + C::BN <= nh);
+      const int pmax_k = position(min(j0 + C::BN - 1, L - 1), nh, shared);
+      const bool pos_far = pmin_q - pmax_k >= R;  // clamped position bias is constant
+
+      // Per query row: the block's time differences lie in [lo, hi]; the
+      // bucket is monotone in dt, so one bucket, or two split by a threshold
+      // on the key's time offset, covers the whole row.
+      const int64_t tmin = blk_ts[0], tmax = blk_ts[1];
+      const bool span_ok = blk_flags[0] != 0;
+      int64_t lo, hi;
+      const bool novf = !__builtin_sub_overflow(ts_q, tmax, &lo) &&
+                        !__builtin_sub_overflow(ts_q, tmin, &hi);
+      const int bt_lo = time_bucket(lo, a.NB, a.sbits), bt_hi = time_bucket(hi, a.NB, a.sbits);
+      const bool one = novf && bt_lo == bt_hi;
+      const bool two = novf && span_ok && bt_hi == bt_lo + 1;
+      int tmode = 2;
+      if (__all(one || !qvalid)) tmode = 0;
+      else if (__all(one || two || !qvalid)) tmode = 1;
+      const float cadd = pos_far ? cpos_far : 0.f;
+      const float c_lo = time_s[bt_lo] + cadd, c_hi = time_s[bt_hi] + cadd;
+      int32_t thr = 0;
+      if (tmode == 1 && bt_hi > 0) {
+        const int64_t t = hi - bucket_floor(bt_hi, a.sbits);
+        thr = t > INT32_MAX ? INT32_MAX : (int32_t)t;
+      }
+      const int mode = __builtin_amdgcn_readfirstlane(tmode * 4 + (pos_far ? 0 : 2) + (full ? 0 : 1));
 
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-      f32x16 s = f32x16{};
+      for (int kh = 0; kh < 2; ++kh) {
+        f32x16 sc = f32x16{};
 #pragma unroll
-      for (int c = 0; c < DQK / 16; ++c) {
-        const Frag kf = *reinterpret_cast<const Frag*>(Ks + (kh * 32 + l32) * C::LDK + 16 * c + 8 * half);
-        s = mma_k16(kf, qf[c], s);
-      }
-      float p[16];
+        for (int c = 0; c < DQK / 16; ++c) {
+          const Frag kf = *reinterpret_cast<const Frag*>(Ks + (kh * 32 + l32) * C::LDK + 16 * c + 8 * half);
+          sc = mma_k16(kf, qf[c], sc);
+        }
+        float p[16];
+        const int jb = kh * 32 + half * 4;  // key offset of r = 0 for this lane
+        switch (mode) {
+#define HSTU_ELEMS(M) \
+  case M: elems<M>(sc, p, jb, j0, iq, nh, p_q, R, shared, ts_q, a.NB, a.sbits, c_lo, c_hi, cadd, thr, \
+                   pos_s, time_s, ts_s, rel_s); break;
+          HSTU_ELEMS(0) HSTU_ELEMS(1) HSTU_ELEMS(2) HSTU_ELEMS(3)
+          HSTU_ELEMS(4) HSTU_ELEMS(5) HSTU_ELEMS(6) HSTU_ELEMS(7)
+          HSTU_ELEMS(8) HSTU_ELEMS(9) HSTU_ELEMS(10) HSTU_ELEMS(11)
+#undef HSTU_ELEMS
+          default: break;
+        }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int jl = kh * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
-        const int j = j0 + jl;
-        const int bp = pos_bucket(p_q, position(j, nh, shared), R);
-        const int bt = time_bucket(wrap_sub(ts_q, ts_s[jl]), a.NB, a.sbits);
-        float val = silu(s[r] + pos_s[bp] + time_s[bt]);
-        if (!full && !attends(iq, j, nh)) val = 0.f;
-        p[r] = val;
-      }
+        for (int c2 = 0; c2 < 2; ++c2) {
+          const Frag pf = to_frag<T>(p + 8 * c2);
 #pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) {
-        const Frag pf = to_frag<T>(p + 8 * c2);
-#pragma unroll
-        for (int n = 0; n < DV / 32; ++n) {
-          const Frag vf = vt_frag<T>(Vts + (n * 32 + l32) * C::LDV + kh * 32 + 16 * c2 + 4 * half);
-          o[n] = mma_k16(vf, pf, o[n]);
+          for (int n = 0; n < DV / 32; ++n) {
+            const Frag vf = vt_frag<T>(Vts + (n * 32 + l32) * C::LDV + kh * 32 + 16 * c2 + 4 * half);
+            o[n] = mma_k16(vf, pf, o[n]);
+          }
         }
       }
+    }
+    __syncthreads();  // every wave is done reading this block
+    if (blk + 1 < nblk) {
+      gload(block_start(blk + 1));
+      sstore(block_start(blk + 1));
+      __syncthreads();
     }
   }
 

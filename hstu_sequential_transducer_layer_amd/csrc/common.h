@@ -131,6 +131,18 @@ __device__ __forceinline__ int time_bucket(int64_t dt, int nb, int s) {
   return b < nb - 1 ? b : nb - 1;
 }
 
+// Smallest dt >= 1 whose time bucket is >= b, for a bucket b >= 1 that some
+// dt in int64 reaches.  With c = b - 1 = (k << s) + sub: for k >= s every
+// sub-bucket exists and starts at 2^k + sub * 2^(k-s); for k < s the bits
+// below dt's leading one are zero-extended, so only sub-buckets whose low
+// s - k bits are zero exist and the answer rounds sub up to the next one.
+__device__ __forceinline__ int64_t bucket_floor(int b, int s) {
+  const int c = b - 1, k = c >> s, sub = c & ((1 << s) - 1);
+  if (k >= s) return ((int64_t)1 << k) | ((int64_t)sub << (k - s));
+  const int sh = s - k;
+  return ((int64_t)1 << k) + (((int64_t)sub + (1 << sh) - 1) >> sh);
+}
+
 __device__ __forceinline__ int64_t wrap_sub(int64_t a, int64_t b) {
   return (int64_t)((uint64_t)a - (uint64_t)b);
 }
