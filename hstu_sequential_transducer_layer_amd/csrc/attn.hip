@@ -38,10 +38,22 @@ template <typename T, int DQK, int DV>
 struct AttnCfg {
   static constexpr int BM = kAttnBM, BN = kAttnBN, NW = BM / 32;
   static constexpr int NT = NW * kWave;
-  static constexpr int V = Elem<T>::kVec;
-  static constexpr int LDK = DQK + 16 / (int)sizeof(T);  // K rows: +16 bytes
-  static constexpr int LDV = BN + 4;                     // V^T rows: +4 elements
+  static constexpr int V = Elem<T>::kVec;                  // elements per 16-byte chunk
+  static constexpr int KCPR = DQK / V, VCPR = DV / V;      // chunks per K / V row
+  static constexpr int KCH = BN * KCPR, VCH = BN * VCPR;   // chunks per block
+  static_assert(KCH % NT == 0 && VCH % NT == 0, "block chunks must split evenly over waves");
 };
+
+// LDS tiles are written by direct global->LDS loads, 16 bytes per lane in
+// lane order, so rows cannot be padded; instead chunk c of row r is stored at
+// chunk c ^ swz(r).  K rows are read 16 bytes per lane down 8 consecutive rows
+// (xor with r & 7); V rows are read 8 bytes per lane from 4 consecutive rows
+// and two adjacent chunks (xor with 2 * (r & 3)).  Both keep one wave's reads
+// of a 128-byte bank window on distinct banks.
+template <int CPR>
+__device__ __forceinline__ int k_swz(int r) { return r & (CPR - 1) & 7; }
+template <int CPR>
+__device__ __forceinline__ int v_swz(int r) { return (2 * (r & 3)) & (CPR - 1); }
 
 struct AttnArgs {
   const int64_t* off;
@@ -61,32 +73,87 @@ struct AttnArgs {
 };
 
 template <typename T>
-__device__ __forceinline__ void store_pair(T* dst, T a, T b);
-template <>
-__device__ __forceinline__ void store_pair<bf16>(bf16* dst, bf16 a, bf16 b) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  bf16x2 v = {a, b};
-  *reinterpret_cast<bf16x2*>(dst) = v;
-}
-template <>
-__device__ __forceinline__ void store_pair<float>(float* dst, float a, float b) {
-  *reinterpret_cast<float2*>(dst) = make_float2(a, b);
+struct LdsPtr {
+  typedef __attribute__((address_space(3))) T type;
+};
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glb_void;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// Asynchronous copy of one key block of a [rows, D] head-major tensor into a
+// swizzled LDS tile: every wave issues NCH/NW 16-byte-per-lane direct loads.
+// Rows past the sequence read its last row instead (finite values that the
+// mask turns into zero weight).
+template <typename T, int D, int NW, int CPR, bool IS_K>
+__device__ __forceinline__ void async_tile(const T* __restrict__ g, int j0, int L, T* lds, int w, int lane) {
+  constexpr int V = Elem<T>::kVec;
+  constexpr int NCH = 64 * CPR;  // BN = 64 rows
+  constexpr int PER = NCH / (NW * 64);
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int slot0 = (w * PER + i) * 64;
+    const int slot = slot0 + lane;
+    const int r = slot / CPR, pc = slot % CPR;
+    const int lc = pc ^ (IS_K ? k_swz<CPR>(r) : v_swz<CPR>(r));
+    const int j = min(j0 + r, L - 1);
+    __builtin_amdgcn_global_load_lds((glb_void*)(g + (int64_t)j * D + lc * V),
+                                     (lds_void*)(lds + slot0 * V), 16, 0, 0);
+  }
 }
 
-// Eight V^T values for one MFMA k16 step: keys base+0..3 and base+8..11.
-template <typename T>
-__device__ __forceinline__ typename Elem<T>::Frag vt_frag(const T* p);
-template <>
-__device__ __forceinline__ bf16x8 vt_frag<bf16>(const bf16* p) {
-  bf16x4 lo = *reinterpret_cast<const bf16x4*>(p);
-  bf16x4 hi = *reinterpret_cast<const bf16x4*>(p + 8);
-  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+// A operand of S^T (K rows): row `r`, 8 elements starting at element `e0`.
+template <typename T, int D>
+__device__ __forceinline__ typename Elem<T>::Frag k_frag(const T* lds, int r, int e0) {
+  constexpr int V = Elem<T>::kVec, CPR = D / V;
+  typedef typename Elem<T>::Frag Frag;
+  if constexpr (V == 8) {
+    return *reinterpret_cast<const Frag*>(lds + r * D + ((e0 / V) ^ k_swz<CPR>(r)) * V);
+  } else {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(lds + r * D + ((e0 / V) ^ k_swz<CPR>(r)) * V);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(lds + r * D + ((e0 / V + 1) ^ k_swz<CPR>(r)) * V);
+    return Frag{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  }
 }
-template <>
-__device__ __forceinline__ f32x8 vt_frag<float>(const float* p) {
-  f32x4 lo = *reinterpret_cast<const f32x4*>(p);
-  f32x4 hi = *reinterpret_cast<const f32x4*>(p + 8);
-  return f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+
+// A operand of O^T (V^T): for this lane's value column n = 32*nt + (lane%32)
+// the eight keys kb + 4*(lane/32) + {0,1,2,3} and kb + 8 + 4*(lane/32) + {0..3}.
+// bf16: two transposing LDS reads; each 16-lane group of a ds_read_b64_tr_b16
+// returns, to lane l, element l%4 of the 4-element pieces addressed by lanes
+// l/4, 4+l/4, 8+l/4, 12+l/4; so source lane a of the group addresses row
+// k0 + a/4, columns D + 4*(a%4) .. +3.
+template <typename T, int DV>
+__device__ __forceinline__ typename Elem<T>::Frag v_frag(const T* lds, int kb, int nt, int lane) {
+  constexpr int V = Elem<T>::kVec, CPR = DV / V;
+  if constexpr (V == 8) {
+    const int a = lane & 15;
+    const int row = kb + 4 * (lane >> 5) + (a >> 2);
+    const int col = 32 * nt + 16 * ((lane >> 4) & 1) + 4 * (a & 3);
+    const int c = col / V, off = col % V;
+    const v4i16 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4i16*)(lds + row * DV + (c ^ v_swz<CPR>(row)) * V + off));
+    const v4i16 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4i16*)(lds + (row + 8) * DV + (c ^ v_swz<CPR>(row + 8)) * V + off));
+    bf16x8 f;
+    const bf16* p0 = reinterpret_cast<const bf16*>(&x0);
+    const bf16* p1 = reinterpret_cast<const bf16*>(&x1);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f[e] = p0[e];
+      f[4 + e] = p1[e];
+    }
+    return f;
+  } else {
+    const int n = 32 * nt + (lane & 31), k0 = kb + 4 * (lane >> 5);
+    const int c = n / V, off = n % V;
+    f32x8 f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int row = k0 + (e >> 2) * 8 + (e & 3);
+      f[e] = lds[row * DV + (c ^ v_swz<CPR>(row)) * V + off];
+    }
+    return f;
+  }
 }
 
 template <typename T>
@@ -106,6 +173,19 @@ __device__ __forceinline__ f32x8 to_frag<float>(const float* p) {
   return f;
 }
 
+// Per-(wave, key block) inputs of the score -> weight step.
+struct ElemCtx {
+  int j0, iq, nh, p_q, R, NB, sbits;
+  bool shared;
+  int64_t ts_q;
+  float c_lo, c_hi, cadd;
+  int32_t thr;
+  const float* pos_s;
+  const float* time_s;
+  const int64_t* ts_s;
+  const int32_t* rel_s;
+};
+
 // Scores -> pointwise weights for one 32-key half held by this lane (query
 // iq, keys jb + 8*(r/4) + (r%4) of the block).  MODE = tmode*4 + pos*2 + mask:
 //   tmode 0: the row's time bias is one value (c_lo)
@@ -115,11 +195,7 @@ __device__ __forceinline__ f32x8 to_frag<float>(const float* p) {
 //   pos:  relative-position bias per pair (else folded into c_lo/c_hi/cadd)
 //   mask: causal/candidate mask per pair (else every pair is attended)
 template <int MODE>
-__device__ __forceinline__ void elems(const f32x16& s, float (&p)[16], int jb, int j0, int iq, int nh,
-                                      int p_q, int R, bool shared, int64_t ts_q, int NB, int sbits,
-                                      float c_lo, float c_hi, float cadd, int32_t thr,
-                                      const float* pos_s, const float* time_s, const int64_t* ts_s,
-                                      const int32_t* rel_s) {
+__device__ __forceinline__ void elems(const f32x16& s, float (&p)[16], int jb, const ElemCtx& x) {
   constexpr int TM = MODE >> 2;
   constexpr bool POS = (MODE >> 1) & 1, MASK = MODE & 1;
 #pragma unroll
@@ -127,19 +203,19 @@ __device__ __forceinline__ void elems(const f32x16& s, float (&p)[16], int jb, i
     const int jl0 = jb + 8 * g;
     int32_t rel[4];
     if (TM == 1) {
-      const int4 rv = *reinterpret_cast<const int4*>(rel_s + jl0);
+      const int4 rv = *reinterpret_cast<const int4*>(x.rel_s + jl0);
       rel[0] = rv.x; rel[1] = rv.y; rel[2] = rv.z; rel[3] = rv.w;
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int r = 4 * g + e, jl = jl0 + e, j = j0 + jl;
+      const int r = 4 * g + e, jl = jl0 + e, j = x.j0 + jl;
       float b;
-      if (TM == 0) b = c_lo;
-      else if (TM == 1) b = rel[e] <= thr ? c_hi : c_lo;
-      else b = time_s[time_bucket(wrap_sub(ts_q, ts_s[jl]), NB, sbits)] + cadd;
-      if (POS) b += pos_s[pos_bucket(p_q, position(j, nh, shared), R)];
+      if (TM == 0) b = x.c_lo;
+      else if (TM == 1) b = rel[e] <= x.thr ? x.c_hi : x.c_lo;
+      else b = x.time_s[time_bucket(wrap_sub(x.ts_q, x.ts_s[jl]), x.NB, x.sbits)] + x.cadd;
+      if (POS) b += x.pos_s[pos_bucket(x.p_q, position(j, x.nh, x.shared), x.R)];
       float v = silu(s[r] + b);
-      if (MASK) v = attends(iq, j, nh) ? v : 0.f;
+      if (MASK) v = attends(x.iq, j, x.nh) ? v : 0.f;
       p[r] = v;
     }
   }
@@ -150,12 +226,15 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
   typedef AttnCfg<T, DQK, DV> C;
   static_assert(C::NT == 256, "launch bounds assume 4 waves");
   typedef typename Elem<T>::Frag Frag;
-  __shared__ __attribute__((aligned(16))) T Ks[C::BN * C::LDK];
-  __shared__ __attribute__((aligned(16))) T Vts[DV * C::LDV];
-  __shared__ int64_t ts_s[C::BN];
-  __shared__ __attribute__((aligned(16))) int32_t rel_s[C::BN];
-  __shared__ int64_t blk_ts[2];
-  __shared__ int32_t blk_flags[1];
+  // Two key-block buffers (even / odd blocks), filled asynchronously.
+  __shared__ __attribute__((aligned(16))) T Ks0[C::BN * DQK];
+  __shared__ __attribute__((aligned(16))) T Ks1[C::BN * DQK];
+  __shared__ __attribute__((aligned(16))) T Vs0[C::BN * DV];
+  __shared__ __attribute__((aligned(16))) T Vs1[C::BN * DV];
+  __shared__ int64_t ts_s[2][C::BN];
+  __shared__ __attribute__((aligned(16))) int32_t rel_s[2][C::BN];
+  __shared__ int64_t blk_ts[2][2];
+  __shared__ int32_t blk_flags[2];
   extern __shared__ float tabs[];  // [P] position table then [NB] time table, head h
   float* pos_s = tabs;
   float* time_s = tabs + a.P;
@@ -177,11 +256,53 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, half = lane >> 5;
 
+  // Key blocks: history [0, min(iend, nh)), then the candidates' own rows.
+  const int a_end = min(iend, nh);
+  const int nblk_a = (a_end + C::BN - 1) / C::BN;
+  const int b_lo = max(i0, nh), b_hi = iend;
+  const int jb0 = max(nblk_a * C::BN, (b_lo / C::BN) * C::BN);
+  const int nblk_b = (b_lo < b_hi && jb0 < b_hi) ? (b_hi - jb0 + C::BN - 1) / C::BN : 0;
+  const int nblk = nblk_a + nblk_b;
+  auto block_start = [&](int blk) __attribute__((always_inline)) { return blk < nblk_a ? blk * C::BN : jb0 + (blk - nblk_a) * C::BN; };
+
+  const T* kg = reinterpret_cast<const T*>(a.k) + ((int64_t)h * a.T + s0) * DQK;
+  const T* vg = reinterpret_cast<const T*>(a.v) + ((int64_t)h * a.T + s0) * DV;
+
+  // Issue the first block's copies before anything else.
+  if (nblk > 0) {
+    async_tile<T, DQK, C::NW, C::KCPR, true>(kg, block_start(0), L, Ks0, w, lane);
+    async_tile<T, DV, C::NW, C::VCPR, false>(vg, block_start(0), L, Vs0, w, lane);
+  }
+
+  // Key timestamps of a block (wave 0): their min/max over the block's real
+  // keys, and offsets from the minimum as int32 when the block spans < 2^31 s.
+  auto stage_ts = [&](int j0, int buf, int64_t t) __attribute__((always_inline)) {
+    const bool valid = j0 + lane < L;
+    int64_t mn = valid ? t : INT64_MAX, mx = valid ? t : INT64_MIN;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const int64_t omn = __shfl_xor(mn, o, kWave), omx = __shfl_xor(mx, o, kWave);
+      mn = omn < mn ? omn : mn;
+      mx = omx > mx ? omx : mx;
+    }
+    int64_t span;
+    const bool span_ok = !__builtin_sub_overflow(mx, mn, &span) && span <= INT32_MAX;
+    ts_s[buf][lane] = t;
+    rel_s[buf][lane] = (valid && span_ok) ? (int32_t)(t - mn) : INT32_MAX;
+    if (lane == 0) {
+      blk_ts[buf][0] = mn;
+      blk_ts[buf][1] = mx;
+      blk_flags[buf] = span_ok ? 1 : 0;
+    }
+  };
+  auto load_ts = [&](int j0) __attribute__((always_inline)) -> int64_t { return (j0 + lane < L) ? a.ts[s0 + j0 + lane] : 0; };
+
   // Bias tables of head h, as fp32, into LDS.
   for (int i = tid; i < a.P; i += C::NT)
     pos_s[i] = to_f32(reinterpret_cast<const T*>(a.pos_tab)[(int64_t)h * a.pos_stride + i]);
   for (int i = tid; i < a.NB; i += C::NT)
     time_s[i] = to_f32(reinterpret_cast<const T*>(a.time_tab)[(int64_t)h * a.time_stride + i]);
+  if (w == 0 && nblk > 0) stage_ts(block_start(0), 0, load_ts(block_start(0)));
 
   // This lane's query row and its operand fragments.
   const int r0 = i0 + 32 * w;
@@ -200,169 +321,102 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
   }
   const int64_t ts_q = qvalid ? a.ts[s0 + iq] : 0;
   const int p_q = position(iq, nh, shared);
+  const int pmin_q = position(r0, nh, shared);
 
   f32x16 o[DV / 32];
 #pragma unroll
   for (int n = 0; n < DV / 32; ++n) o[n] = f32x16{};
 
-  // Key blocks: history [0, min(iend, nh)), then the candidates' own rows.
-  const int a_end = min(iend, nh);
-  const int nblk_a = (a_end + C::BN - 1) / C::BN;
-  const int b_lo = max(i0, nh), b_hi = iend;
-  const int jb0 = max(nblk_a * C::BN, (b_lo / C::BN) * C::BN);
-  const int nblk_b = (b_lo < b_hi && jb0 < b_hi) ? (b_hi - jb0 + C::BN - 1) / C::BN : 0;
-  const int nblk = nblk_a + nblk_b;
-  auto block_start = [&](int blk) { return blk < nblk_a ? blk * C::BN : jb0 + (blk - nblk_a) * C::BN; };
-
-  const T* kg = reinterpret_cast<const T*>(a.k) + ((int64_t)h * a.T + s0) * DQK;
-  const T* vg = reinterpret_cast<const T*>(a.v) + ((int64_t)h * a.T + s0) * DV;
-
-  // Register staging of one key block: K rows, V rows (two keys per item,
-  // transposed on the way into LDS) and, in wave 0, one key timestamp per
-  // lane.  Two workgroups share a CU, so one's loads overlap the other's MFMAs.
-  constexpr int KTOT = C::BN * DQK / C::V;                 // 16-byte K chunks per block
-  constexpr int VTOT = (C::BN / 2) * (DV / C::V);          // key-pair V items per block
-  constexpr int KCH = (KTOT + C::NT - 1) / C::NT, VCH = (VTOT + C::NT - 1) / C::NT;
-  uint4 rk[KCH], rv0[VCH], rv1[VCH];
-  int64_t rts = 0;
-  auto gload = [&](int j0) {
-#pragma unroll
-    for (int c = 0; c < KCH; ++c) {
-      const int idx = tid + c * C::NT;
-      const int jl = idx / (DQK / C::V), cc = (idx % (DQK / C::V)) * C::V;
-      const int j = j0 + jl;
-      rk[c] = (idx < KTOT && j < L) ? ld16(kg + (int64_t)j * DQK + cc) : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int c = 0; c < VCH; ++c) {
-      const int idx = tid + c * C::NT;
-      const int kp = idx % (C::BN / 2), cc = (idx / (C::BN / 2)) * C::V;
-      const int j = j0 + 2 * kp;
-      const bool in = idx < VTOT;
-      rv0[c] = (in && j < L) ? ld16(vg + (int64_t)j * DV + cc) : make_uint4(0, 0, 0, 0);
-      rv1[c] = (in && j + 1 < L) ? ld16(vg + (int64_t)(j + 1) * DV + cc) : make_uint4(0, 0, 0, 0);
-    }
-    if (w == 0) rts = (j0 + lane < L) ? a.ts[s0 + j0 + lane] : 0;
-  };
-  auto sstore = [&](int j0) {
-#pragma unroll
-    for (int c = 0; c < KCH; ++c) {
-      const int idx = tid + c * C::NT;
-      const int jl = idx / (DQK / C::V), cc = (idx % (DQK / C::V)) * C::V;
-      if (idx < KTOT) st16(Ks + jl * C::LDK + cc, rk[c]);
-    }
-#pragma unroll
-    for (int c = 0; c < VCH; ++c) {
-      const int idx = tid + c * C::NT;
-      if (idx >= VTOT) continue;
-      const int kp = idx % (C::BN / 2), cc = (idx / (C::BN / 2)) * C::V;
-      const T* e0 = reinterpret_cast<const T*>(&rv0[c]);
-      const T* e1 = reinterpret_cast<const T*>(&rv1[c]);
-#pragma unroll
-      for (int e = 0; e < C::V; ++e) store_pair<T>(Vts + (cc + e) * C::LDV + 2 * kp, e0[e], e1[e]);
-    }
-    if (w == 0) {
-      // Key timestamps, their min/max over the block's real keys, and their
-      // offsets from the minimum as int32 when the block spans < 2^31 s.
-      const bool valid = j0 + lane < L;
-      int64_t mn = valid ? rts : INT64_MAX, mx = valid ? rts : INT64_MIN;
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        const int64_t omn = __shfl_xor(mn, o, kWave), omx = __shfl_xor(mx, o, kWave);
-        mn = omn < mn ? omn : mn;
-        mx = omx > mx ? omx : mx;
-      }
-      int64_t span;
-      const bool span_ok = !__builtin_sub_overflow(mx, mn, &span) && span <= INT32_MAX;
-      ts_s[lane] = rts;
-      rel_s[lane] = (valid && span_ok) ? (int32_t)(rts - mn) : INT32_MAX;
-      if (lane == 0) {
-        blk_ts[0] = mn;
-        blk_ts[1] = mx;
-        blk_flags[0] = span_ok ? 1 : 0;
-      }
-    }
-  };
-
-  const int pmin_q = position(r0, nh, shared);
-  if (nblk > 0) {
-    gload(block_start(0));
-    sstore(block_start(0));
-  }
-  __syncthreads();  // tables and the first key block are in LDS
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of block 0 have landed
+  __syncthreads();                // ... and every other wave's, plus tables
   const float cpos_far = pos_s[2 * R];  // bias of every pair at distance >= R
 
-  for (int blk = 0; blk < nblk; ++blk) {
+  // One block of work out of buffer `buf`.
+  auto consume = [&](int blk, int buf, const T* Kb, const T* Vb) __attribute__((always_inline)) {
     const int j0 = block_start(blk);
-
-    // Can any row of this wave attend to any key of the block?
     const bool any_hist = j0 < nh && j0 <= rlast;
     const bool any_self = max(max(r0, nh), j0) <= min(rlast, j0 + C::BN - 1);
-    if (r0 < iend && (any_hist || any_self)) {
-      const bool full = (j0 + C::BN - 1 <= r0) && (j0 + C::BN <= nh);
-      const int pmax_k = position(min(j0 + C::BN - 1, L - 1), nh, shared);
-      const bool pos_far = pmin_q - pmax_k >= R;  // clamped position bias is constant
+    if (r0 >= iend || !(any_hist || any_self)) return;
+    const bool full = (j0 + C::BN - 1 <= r0) && (j0 + C::BN <= nh);
+    const int pmax_k = position(min(j0 + C::BN - 1, L - 1), nh, shared);
+    const bool pos_far = pmin_q - pmax_k >= R;  // clamped position bias is constant
 
-      // Per query row: the block's time differences lie in [lo, hi]; the
-      // bucket is monotone in dt, so one bucket, or two split by a threshold
-      // on the key's time offset, covers the whole row.
-      const int64_t tmin = blk_ts[0], tmax = blk_ts[1];
-      const bool span_ok = blk_flags[0] != 0;
-      int64_t lo, hi;
-      const bool novf = !__builtin_sub_overflow(ts_q, tmax, &lo) &&
-                        !__builtin_sub_overflow(ts_q, tmin, &hi);
-      const int bt_lo = time_bucket(lo, a.NB, a.sbits), bt_hi = time_bucket(hi, a.NB, a.sbits);
-      const bool one = novf && bt_lo == bt_hi;
-      const bool two = novf && span_ok && bt_hi == bt_lo + 1;
-      int tmode = 2;
-      if (__all(one || !qvalid)) tmode = 0;
-      else if (__all(one || two || !qvalid)) tmode = 1;
-      const float cadd = pos_far ? cpos_far : 0.f;
-      const float c_lo = time_s[bt_lo] + cadd, c_hi = time_s[bt_hi] + cadd;
-      int32_t thr = 0;
-      if (tmode == 1 && bt_hi > 0) {
-        const int64_t t = hi - bucket_floor(bt_hi, a.sbits);
-        thr = t > INT32_MAX ? INT32_MAX : (int32_t)t;
-      }
-      const int mode = __builtin_amdgcn_readfirstlane(tmode * 4 + (pos_far ? 0 : 2) + (full ? 0 : 1));
-
+    // Per query row: the block's time differences lie in [lo, hi]; the
+    // bucket is monotone in dt, so one bucket, or two split by a threshold
+    // on the key's time offset, covers the whole row.
+    const int64_t tmin = blk_ts[buf][0], tmax = blk_ts[buf][1];
+    const bool span_ok = blk_flags[buf] != 0;
+    int64_t lo, hi;
+    const bool novf = !__builtin_sub_overflow(ts_q, tmax, &lo) && !__builtin_sub_overflow(ts_q, tmin, &hi);
+    const int bt_lo = time_bucket(lo, a.NB, a.sbits), bt_hi = time_bucket(hi, a.NB, a.sbits);
+    const bool one = novf && bt_lo == bt_hi;
+    const bool two = novf && span_ok && bt_hi == bt_lo + 1;
+    int tmode = 2;
+    if (__all(one || !qvalid)) tmode = 0;
+    else if (__all(one || two || !qvalid)) tmode = 1;
+    const float cadd = pos_far ? cpos_far : 0.f;
+    const float c_lo = time_s[bt_lo] + cadd, c_hi = time_s[bt_hi] + cadd;
+    int32_t thr = 0;
+    if (tmode == 1 && bt_hi > 0) {
+      const int64_t t = hi - bucket_floor(bt_hi, a.sbits);
+      thr = t > INT32_MAX ? INT32_MAX : (int32_t)t;
+    }
+    const int mode = __builtin_amdgcn_readfirstlane(tmode * 4 + (pos_far ? 0 : 2) + (full ? 0 : 1));
+    const ElemCtx x{j0, iq, nh, p_q, R, a.NB, a.sbits, shared, ts_q, c_lo, c_hi, cadd, thr,
+                    pos_s, time_s, ts_s[buf], rel_s[buf]};
 #pragma unroll
-      for (int kh = 0; kh < 2; ++kh) {
-        f32x16 sc = f32x16{};
+    for (int kh = 0; kh < 2; ++kh) {
+      f32x16 sc = f32x16{};
 #pragma unroll
-        for (int c = 0; c < DQK / 16; ++c) {
-          const Frag kf = *reinterpret_cast<const Frag*>(Ks + (kh * 32 + l32) * C::LDK + 16 * c + 8 * half);
-          sc = mma_k16(kf, qf[c], sc);
-        }
-        float p[16];
-        const int jb = kh * 32 + half * 4;  // key offset of r = 0 for this lane
-        switch (mode) {
+      for (int c = 0; c < DQK / 16; ++c)
+        sc = mma_k16(k_frag<T, DQK>(Kb, kh * 32 + l32, 16 * c + 8 * half), qf[c], sc);
+      float p[16];
+      const int jb = kh * 32 + half * 4;  // key offset of r = 0 for this lane
+      switch (mode) {
 #define HSTU_ELEMS(M) \
-  case M: elems<M>(sc, p, jb, j0, iq, nh, p_q, R, shared, ts_q, a.NB, a.sbits, c_lo, c_hi, cadd, thr, \
-                   pos_s, time_s, ts_s, rel_s); break;
-          HSTU_ELEMS(0) HSTU_ELEMS(1) HSTU_ELEMS(2) HSTU_ELEMS(3)
-          HSTU_ELEMS(4) HSTU_ELEMS(5) HSTU_ELEMS(6) HSTU_ELEMS(7)
-          HSTU_ELEMS(8) HSTU_ELEMS(9) HSTU_ELEMS(10) HSTU_ELEMS(11)
+  case M: elems<M>(sc, p, jb, x); break;
+        HSTU_ELEMS(0) HSTU_ELEMS(1) HSTU_ELEMS(2) HSTU_ELEMS(3)
+        HSTU_ELEMS(4) HSTU_ELEMS(5) HSTU_ELEMS(6) HSTU_ELEMS(7)
+        HSTU_ELEMS(8) HSTU_ELEMS(9) HSTU_ELEMS(10) HSTU_ELEMS(11)
 #undef HSTU_ELEMS
-          default: break;
-        }
+        default: break;
+      }
 #pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2) {
-          const Frag pf = to_frag<T>(p + 8 * c2);
+      for (int c2 = 0; c2 < 2; ++c2) {
+        const Frag pf = to_frag<T>(p + 8 * c2);
 #pragma unroll
-          for (int n = 0; n < DV / 32; ++n) {
-            const Frag vf = vt_frag<T>(Vts + (n * 32 + l32) * C::LDV + kh * 32 + 16 * c2 + 4 * half);
-            o[n] = mma_k16(vf, pf, o[n]);
-          }
-        }
+        for (int n = 0; n < DV / 32; ++n)
+          o[n] = mma_k16(v_frag<T, DV>(Vb, kh * 32 + 16 * c2, n, lane), pf, o[n]);
       }
     }
-    __syncthreads();  // every wave is done reading this block
+  };
+
+  // Block loop, two blocks per trip so each buffer is a distinct LDS object
+  // (the compiler then needs no wait on the in-flight copy before reading the
+  // other buffer): the copies of block b+1 run while block b is consumed; one
+  // barrier per block.
+  for (int blk = 0; blk < nblk; blk += 2) {
+    int64_t tnext = 0;
     if (blk + 1 < nblk) {
-      gload(block_start(blk + 1));
-      sstore(block_start(blk + 1));
-      __syncthreads();
+      async_tile<T, DQK, C::NW, C::KCPR, true>(kg, block_start(blk + 1), L, Ks1, w, lane);
+      async_tile<T, DV, C::NW, C::VCPR, false>(vg, block_start(blk + 1), L, Vs1, w, lane);
+      if (w == 0) tnext = load_ts(block_start(blk + 1));
     }
+    consume(blk, 0, Ks0, Vs0);
+    if (blk + 1 >= nblk) break;
+    if (w == 0) stage_ts(block_start(blk + 1), 1, tnext);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (blk + 2 < nblk) {
+      async_tile<T, DQK, C::NW, C::KCPR, true>(kg, block_start(blk + 2), L, Ks0, w, lane);
+      async_tile<T, DV, C::NW, C::VCPR, false>(vg, block_start(blk + 2), L, Vs0, w, lane);
+      if (w == 0) tnext = load_ts(block_start(blk + 2));
+    }
+    consume(blk + 1, 1, Ks1, Vs1);
+    if (blk + 2 >= nblk) break;
+    if (w == 0) stage_ts(block_start(blk + 2), 0, tnext);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
   }
 
   // Epilogue: scale by 1/N_b, per-(row, head) mean and M2 over dv, centred AV.
@@ -429,6 +483,15 @@ static hipError_t launch_dims(const AttnArgs& a, int dqk, int dv, int64_t grid, 
   return hipErrorInvalidValue;
 }
 
+// fp32 layers: head widths up to 64 (the API rejects wider ones for fp32).
+static hipError_t launch_dims_f32(const AttnArgs& a, int dqk, int dv, int64_t grid, hipStream_t s) {
+  if (dqk == 32 && dv == 32) return launch_t<float, 32, 32>(a, grid, s);
+  if (dqk == 32 && dv == 64) return launch_t<float, 32, 64>(a, grid, s);
+  if (dqk == 64 && dv == 32) return launch_t<float, 64, 32>(a, grid, s);
+  if (dqk == 64 && dv == 64) return launch_t<float, 64, 64>(a, grid, s);
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_attn(const hstu_desc& d, const int64_t* off, const int32_t* ncand, int32_t B,
                        int64_t T, const int64_t* ts, const hstu_bias_tables& tab, const void* q,
                        const void* k, const void* v, void* av, float* stats, const int2* tiles,
@@ -458,7 +521,7 @@ hipError_t launch_attn(const hstu_desc& d, const int64_t* off, const int32_t* nc
   a.shared_pos = (d.flags & HSTU_CAND_SHARED_POS) ? 1 : 0;
   const int64_t grid = attn_max_tiles(T, B) * d.num_heads;
   if (d.dtype == HSTU_BF16) return launch_dims<bf16>(a, d.dqk, d.dv, grid, s);
-  return launch_dims<float>(a, d.dqk, d.dv, grid, s);
+  return launch_dims_f32(a, d.dqk, d.dv, grid, s);
 }
 
 }  // namespace hstu
