@@ -6,14 +6,17 @@ A step is one pass of the whole hot path over one batch of the workload: for
 the default `stack8_long` (8 HSTU layers, 8 jagged sequences of 4096..8192
 tokens, d=1024, 8 heads x 128/128, bf16) that is 8 hstu_layer_fwd calls
 (input LayerNorm, projection GEMM + SiLU, work list, fused pointwise
-attention, fused LayerNorm/gate/output GEMM + residual per layer).  Inputs are
+attention, LayerNorm/gate kernel, output GEMM + residual per layer).  Inputs are
 resident in HBM before timing starts.  Prints one JSON line.
 
 Besides the step time, the attention kernel — the dominant kernel — is timed
 on its own through hstu_attn_fwd with HIP events recorded on the stream it is
 launched on, and its algorithmic FLOPs per launch (2 (dqk + dv) H per
 attended (query, key) pair) give the roofline fraction against the dense bf16
-MFMA peak.  The CPU oracle is timed on a bounded sample of the same workload.
+MFMA peak.  The LayerNorm/gate kernel is timed the same way through
+hstu_gate_fwd against the HBM peak (its algorithmic bytes: AV and U read and
+Z written once, plus the per-head statistics).  The CPU oracle is timed on a
+bounded sample of the same workload.
 """
 
 from __future__ import annotations
@@ -167,7 +170,9 @@ def main():
         torch.cuda.synchronize()
         return s.elapsed_time(e) / reps
     proj_ms = timed(lambda: _lib.proj_fwd(desc, x, dev["layers"][0], acts))
-    out_ms = timed(lambda: _lib.out_fwd(desc, x, dev["layers"][0], acts, out=out))
+    zbuf = torch.empty_like(acts["u"])
+    gate_ms = timed(lambda: _lib.gate_fwd(desc, dev["layers"][0], acts, z=zbuf), reps=20)
+    out_ms = timed(lambda: _lib.out_fwd(desc, x, dev["layers"][0], acts, out=out, z=zbuf))
 
     pairs = attended_pairs(w.lengths(), w.num_candidates)
     dm, H, dqk, dv = w.dims.d_model, w.dims.num_heads, w.dims.dqk, w.dims.dv
@@ -177,7 +182,11 @@ def main():
     tokens_per_s = T / (ms_step * 1e-3)
     e = 2 if w.dims.dtype == "bf16" else 4
     proj_flop = 2.0 * T * dm * w.dims.n1
-    out_bytes = T * (H * dv * e * 2 + 2 * dm * e + H * 8) + H * dv * dm * e
+    # gate kernel, algorithmic bytes: per row AV and U read, Z written (H*dv
+    # elements each) and the H (mean, M2) fp32 partials read; plus gamma, beta.
+    gate_bytes = T * (3 * H * dv * e + 8 * H) + 2 * H * dv * e
+    gate_gbs = gate_bytes / (gate_ms * 1e-3) / 1e9
+    f2_flop = 2.0 * T * H * dv * dm
 
     rec = {
         "metric": METRIC,
@@ -212,12 +221,22 @@ def main():
             "flop_per_launch": attn_flop,
             "pairs_per_launch": pairs,
         },
+        "gate_roofline": {
+            "kernel": "gate_kernel (LayerNorm over H*dv, times U; one layer)",
+            "bound": "hbm",
+            "achieved": gate_gbs,
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": gate_gbs / PEAK_HBM_GBS,
+            "launch_ms": gate_ms,
+            "bytes_per_launch": gate_bytes,
+        },
         "stages_ms_per_layer": {
             "proj (ln_in + f1 GEMM + SiLU)": proj_ms,
             "attn (work list + attention)": attn_ms,
-            "out (LN gate + f2 GEMM + residual)": out_ms,
+            "out (gate + f2 GEMM + residual)": out_ms,
             "proj_tflops": proj_flop / (proj_ms * 1e-3) / 1e12,
-            "out_gbs_algorithmic": out_bytes / (out_ms * 1e-3) / 1e9,
+            "f2_tflops_excl_gate": f2_flop / (max(out_ms - gate_ms, 1e-6) * 1e-3) / 1e12,
         },
         "layer_tokens_per_s": T * len(w.layers) / (ms_step * 1e-3),
     }

@@ -23,7 +23,8 @@ HSTU_INPUT_NORM, HSTU_RESIDUAL, HSTU_CAND_SHARED_POS, HSTU_VALIDATE = 1, 2, 4, 8
 
 EXPORTS = [
     "hstu_workspace_size", "hstu_layer_fwd", "hstu_proj_workspace_size", "hstu_proj_fwd",
-    "hstu_attn_workspace_size", "hstu_attn_fwd", "hstu_out_fwd", "hstu_debug_indices",
+    "hstu_attn_workspace_size", "hstu_attn_fwd", "hstu_gate_fwd", "hstu_out_fwd",
+    "hstu_debug_indices",
     "hstu_status_str", "hstu_last_error",
 ]
 
@@ -86,8 +87,9 @@ def load() -> ctypes.CDLL:
                                   P(HstuActivations), vp, sz, vp]
     lib.hstu_out_fwd.argtypes = [P(HstuDesc), vp, i64, P(HstuWeights), P(HstuActivations),
                                  vp, vp, vp]
+    lib.hstu_gate_fwd.argtypes = [P(HstuDesc), i64, P(HstuWeights), P(HstuActivations), vp, vp]
     lib.hstu_debug_indices.argtypes = [P(HstuDesc), vp, i32, i64, vp, vp, vp, i64, vp, vp]
-    for f in ("hstu_layer_fwd", "hstu_proj_fwd", "hstu_attn_fwd", "hstu_out_fwd",
+    for f in ("hstu_layer_fwd", "hstu_proj_fwd", "hstu_attn_fwd", "hstu_gate_fwd", "hstu_out_fwd",
               "hstu_debug_indices"):
         getattr(lib, f).restype = ctypes.c_int
     lib.hstu_status_str.argtypes = [ctypes.c_int]
@@ -214,12 +216,25 @@ def attn_fwd(desc: HstuDesc, seq_offsets, timestamps, num_candidates, prm, acts)
     return acts
 
 
-def out_fwd(desc: HstuDesc, x, prm, acts, out=None, want_z: bool = False):
+def gate_fwd(desc: HstuDesc, prm, acts, z=None):
+    """Stage 3a (Z = LayerNorm(AV) * U); returns z, allocating it when not given."""
+    lib = load()
+    T = acts["u"].shape[0]
+    if z is None:
+        z = torch.empty_like(acts["u"])
+    a, w = _acts(acts), make_weights(prm)
+    _check(lib.hstu_gate_fwd(ctypes.byref(desc), T, ctypes.byref(w), ctypes.byref(a), _ptr(z), _stream()))
+    return z
+
+
+def out_fwd(desc: HstuDesc, x, prm, acts, out=None, z=None):
+    """Stage 3; returns (out, z), allocating either when not given."""
     lib = load()
     T = acts["u"].shape[0]
     if out is None:
         out = torch.empty(T, desc.d_model, dtype=torch_dtype(desc), device=acts["u"].device)
-    z = torch.empty_like(acts["u"]) if want_z else None
+    if z is None:
+        z = torch.empty_like(acts["u"])
     a, w = _acts(acts), make_weights(prm)
     _check(lib.hstu_out_fwd(ctypes.byref(desc), _ptr(x), T, ctypes.byref(w), ctypes.byref(a),
                             _ptr(out), _ptr(z), _stream()))

@@ -292,20 +292,37 @@ hstu_status hstu_attn_fwd(const hstu_desc* desc, const int64_t* off, int32_t B, 
   return ok();
 }
 
+hstu_status hstu_gate_fwd(const hstu_desc* desc, int64_t T, const hstu_weights* w,
+                          const hstu_activations* acts, void* z, hstu_stream_t stream) {
+  hstu_status st;
+  if ((st = check_desc(desc)) != HSTU_OK) return st;
+  if ((st = check_sizes(T, 1)) != HSTU_OK) return st;
+  if (T == 0) return ok();
+  HSTU_REQ(z, 16, "z");
+  if ((st = check_out_weights(desc, w)) != HSTU_OK) return st;
+  if ((st = check_acts(acts, false, false)) != HSTU_OK) return st;
+  st = device(hstu::launch_gate(*desc, T, *w, acts->u, acts->av, acts->av_stats, z, (hipStream_t)stream),
+              "gate launch");
+  if (st != HSTU_OK) return st;
+  return ok();
+}
+
 hstu_status hstu_out_fwd(const hstu_desc* desc, const void* x, int64_t T, const hstu_weights* w,
-                         const hstu_activations* acts, void* out, void* z_out, hstu_stream_t stream) {
+                         const hstu_activations* acts, void* out, void* z, hstu_stream_t stream) {
   hstu_status st;
   if ((st = check_desc(desc)) != HSTU_OK) return st;
   if ((st = check_sizes(T, 1)) != HSTU_OK) return st;
   if (T == 0) return ok();
   if (desc->flags & HSTU_RESIDUAL) HSTU_REQ(x, 16, "x");
   HSTU_REQ(out, 16, "out");
-  if (z_out && !aligned(z_out, 16)) return fail(HSTU_ERR_INVALID_ARG, "z_out is not 16-byte aligned");
+  HSTU_REQ(z, 16, "z");
   if ((st = check_out_weights(desc, w)) != HSTU_OK) return st;
   if ((st = check_acts(acts, false, false)) != HSTU_OK) return st;
-  st = device(hstu::launch_out(*desc, x, T, *w, acts->u, acts->av, acts->av_stats, out, z_out,
-                               (hipStream_t)stream), "out launch");
-  if (st != HSTU_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if ((st = device(hstu::launch_gate(*desc, T, *w, acts->u, acts->av, acts->av_stats, z, s), "gate launch")) !=
+      HSTU_OK)
+    return st;
+  if ((st = device(hstu::launch_f2(*desc, x, T, *w, z, out, s), "f2 launch")) != HSTU_OK) return st;
   return ok();
 }
 
@@ -341,8 +358,11 @@ hstu_status hstu_layer_fwd(const hstu_desc* desc, const void* x, const int64_t* 
   if ((st = run_attn(desc, off, B, T, ts, nc, tables, &a, (int2*)(base + L.tiles),
                      (int32_t*)(base + L.count), s)) != HSTU_OK)
     return st;
-  st = device(hstu::launch_out(*desc, x, T, *w, a.u, a.av, a.av_stats, out, nullptr, s), "out launch");
-  if (st != HSTU_OK) return st;
+  // Z takes the V region: V [H, T, dv] has Z's size and is dead after stage 2.
+  void* z = base + L.v;
+  if ((st = device(hstu::launch_gate(*desc, T, *w, a.u, a.av, a.av_stats, z, s), "gate launch")) != HSTU_OK)
+    return st;
+  if ((st = device(hstu::launch_f2(*desc, x, T, *w, z, out, s), "f2 launch")) != HSTU_OK) return st;
   return ok();
 }
 

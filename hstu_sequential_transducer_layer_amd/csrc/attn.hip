@@ -46,14 +46,19 @@ struct AttnCfg {
 
 // LDS tiles are written by direct global->LDS loads, 16 bytes per lane in
 // lane order, so rows cannot be padded; instead chunk c of row r is stored at
-// chunk c ^ swz(r).  K rows are read 16 bytes per lane down 8 consecutive rows
-// (xor with r & 7); V rows are read 8 bytes per lane from 4 consecutive rows
-// and two adjacent chunks (xor with 2 * (r & 3)).  Both keep one wave's reads
-// of a 128-byte bank window on distinct banks.
+// chunk c ^ swz(r).  The LDS has 64 four-byte banks (16 chunk slots of 16
+// bytes per 256-byte line).  K rows (CPR chunks) are read 16 bytes per lane
+// down 16 consecutive rows: k_swz spreads those rows over all 16 slots.  V
+// rows are read through the transposing 8-byte read, 4 consecutive rows x 4
+// consecutive chunks per 32 lanes: v_swz spreads those 16 pieces likewise.
 template <int CPR>
-__device__ __forceinline__ int k_swz(int r) { return r & (CPR - 1) & 7; }
+__device__ __forceinline__ int k_swz(int r) {
+  return CPR >= 16 ? (r & 15) & (CPR - 1) : ((r / (16 / CPR)) & (CPR - 1));
+}
 template <int CPR>
-__device__ __forceinline__ int v_swz(int r) { return (2 * (r & 3)) & (CPR - 1); }
+__device__ __forceinline__ int v_swz(int r) {
+  return CPR >= 16 ? 4 * (r & 3) : (CPR == 8 ? 4 * ((r >> 1) & 1) : 0);
+}
 
 struct AttnArgs {
   const int64_t* off;
@@ -178,7 +183,7 @@ struct ElemCtx {
   int j0, iq, nh, p_q, R, NB, sbits;
   bool shared;
   int64_t ts_q;
-  float c_lo, c_hi, cadd;
+  float c_lo, c_hi;
   int32_t thr;
   const float* pos_s;
   const float* time_s;
@@ -187,35 +192,36 @@ struct ElemCtx {
 };
 
 // Scores -> pointwise weights for one 32-key half held by this lane (query
-// iq, keys jb + 8*(r/4) + (r%4) of the block).  MODE = tmode*4 + pos*2 + mask:
-//   tmode 0: the row's time bias is one value (c_lo)
-//   tmode 1: two values, c_hi for keys whose offset from the block's earliest
-//            timestamp is <= thr, else c_lo
-//   tmode 2: the log time bucket computed per pair
-//   pos:  relative-position bias per pair (else folded into c_lo/c_hi/cadd)
-//   mask: causal/candidate mask per pair (else every pair is attended)
+// iq, keys jb + 8*(r/4) + (r%4) of the block).  Every variant is branch-free.
+//   MODE 0: every pair attended, one bias per row (c_lo: time bucket and
+//           position bias both constant over the block).
+//   MODE 1: every pair attended, bias c_hi for keys whose offset from the
+//           block's earliest timestamp is <= thr, else c_lo.
+//   MODE 2: log time bucket, relative-position bucket and mask per pair.
 template <int MODE>
 __device__ __forceinline__ void elems(const f32x16& s, float (&p)[16], int jb, const ElemCtx& x) {
-  constexpr int TM = MODE >> 2;
-  constexpr bool POS = (MODE >> 1) & 1, MASK = MODE & 1;
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     const int jl0 = jb + 8 * g;
     int32_t rel[4];
-    if (TM == 1) {
+    if (MODE == 1) {
       const int4 rv = *reinterpret_cast<const int4*>(x.rel_s + jl0);
       rel[0] = rv.x; rel[1] = rv.y; rel[2] = rv.z; rel[3] = rv.w;
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int r = 4 * g + e, jl = jl0 + e, j = x.j0 + jl;
-      float b;
-      if (TM == 0) b = x.c_lo;
-      else if (TM == 1) b = rel[e] <= x.thr ? x.c_hi : x.c_lo;
-      else b = x.time_s[time_bucket(wrap_sub(x.ts_q, x.ts_s[jl]), x.NB, x.sbits)] + x.cadd;
-      if (POS) b += x.pos_s[pos_bucket(x.p_q, position(j, x.nh, x.shared), x.R)];
-      float v = silu(s[r] + b);
-      if (MASK) v = attends(x.iq, j, x.nh) ? v : 0.f;
+      float v;
+      if (MODE == 0) {
+        v = silu(s[r] + x.c_lo);
+      } else if (MODE == 1) {
+        v = silu(s[r] + (rel[e] <= x.thr ? x.c_hi : x.c_lo));
+      } else {
+        const float b = x.time_s[time_bucket(wrap_sub(x.ts_q, x.ts_s[jl]), x.NB, x.sbits)] +
+                        x.pos_s[pos_bucket(x.p_q, position(j, x.nh, x.shared), x.R)];
+        v = silu(s[r] + b);
+        v = attends(x.iq, j, x.nh) ? v : 0.f;
+      }
       p[r] = v;
     }
   }
@@ -253,7 +259,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
   const int R = (a.P - 1) / 2;
   const bool shared = a.shared_pos != 0;
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
   const int l32 = lane & 31, half = lane >> 5;
 
   // Key blocks: history [0, min(iend, nh)), then the candidates' own rows.
@@ -351,42 +357,42 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
     const int bt_lo = time_bucket(lo, a.NB, a.sbits), bt_hi = time_bucket(hi, a.NB, a.sbits);
     const bool one = novf && bt_lo == bt_hi;
     const bool two = novf && span_ok && bt_hi == bt_lo + 1;
-    int tmode = 2;
-    if (__all(one || !qvalid)) tmode = 0;
-    else if (__all(one || two || !qvalid)) tmode = 1;
-    const float cadd = pos_far ? cpos_far : 0.f;
-    const float c_lo = time_s[bt_lo] + cadd, c_hi = time_s[bt_hi] + cadd;
-    int32_t thr = 0;
-    if (tmode == 1 && bt_hi > 0) {
-      const int64_t t = hi - bucket_floor(bt_hi, a.sbits);
-      thr = t > INT32_MAX ? INT32_MAX : (int32_t)t;
-    }
-    const int mode = __builtin_amdgcn_readfirstlane(tmode * 4 + (pos_far ? 0 : 2) + (full ? 0 : 1));
-    const ElemCtx x{j0, iq, nh, p_q, R, a.NB, a.sbits, shared, ts_q, c_lo, c_hi, cadd, thr,
+    // FAST: no mask, constant position bias, and per row at most two time
+    // buckets (decided for the whole wave).
+    const bool fast = full && pos_far && __all(one || two || !qvalid);
+    const float c_lo = time_s[bt_lo] + cpos_far, c_hi = time_s[bt_hi] + cpos_far;
+    // one bucket: thr = INT32_MAX, every key takes c_hi == c_lo (selects only)
+    const int64_t tt = hi - bucket_floor(bt_hi > 0 ? bt_hi : 1, a.sbits);
+    const int32_t thr = (one || bt_hi == 0 || tt > INT32_MAX) ? INT32_MAX : (int32_t)tt;
+    const int mode = __builtin_amdgcn_readfirstlane(!fast ? 2 : (__all(one || !qvalid) ? 0 : 1));
+    const ElemCtx x{j0, iq, nh, p_q, R, a.NB, a.sbits, shared, ts_q, c_lo, c_hi, thr,
                     pos_s, time_s, ts_s[buf], rel_s[buf]};
+    // Per 32-key half: S^T (K fragments straight from LDS), then this half's
+    // V fragments are read while its weights are computed, then P.V.
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
       f32x16 sc = f32x16{};
 #pragma unroll
       for (int c = 0; c < DQK / 16; ++c)
         sc = mma_k16(k_frag<T, DQK>(Kb, kh * 32 + l32, 16 * c + 8 * half), qf[c], sc);
+      Frag vf[2][DV / 32];
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+        for (int n = 0; n < DV / 32; ++n) vf[c2][n] = v_frag<T, DV>(Vb, kh * 32 + 16 * c2, n, lane);
       float p[16];
       const int jb = kh * 32 + half * 4;  // key offset of r = 0 for this lane
-      switch (mode) {
-#define HSTU_ELEMS(M) \
-  case M: elems<M>(sc, p, jb, x); break;
-        HSTU_ELEMS(0) HSTU_ELEMS(1) HSTU_ELEMS(2) HSTU_ELEMS(3)
-        HSTU_ELEMS(4) HSTU_ELEMS(5) HSTU_ELEMS(6) HSTU_ELEMS(7)
-        HSTU_ELEMS(8) HSTU_ELEMS(9) HSTU_ELEMS(10) HSTU_ELEMS(11)
-#undef HSTU_ELEMS
-        default: break;
-      }
+      if (mode == 0)
+        elems<0>(sc, p, jb, x);
+      else if (mode == 1)
+        elems<1>(sc, p, jb, x);
+      else
+        elems<2>(sc, p, jb, x);
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2) {
         const Frag pf = to_frag<T>(p + 8 * c2);
 #pragma unroll
-        for (int n = 0; n < DV / 32; ++n)
-          o[n] = mma_k16(v_frag<T, DV>(Vb, kh * 32 + 16 * c2, n, lane), pf, o[n]);
+        for (int n = 0; n < DV / 32; ++n) o[n] = mma_k16(vf[c2][n], pf, o[n]);
       }
     }
   };

@@ -23,6 +23,12 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 
+// Index of the calling wave within its workgroup, as a wave-uniform (scalar)
+// value: the compiler cannot infer that threadIdx.x / 64 is uniform, and
+// branches on values derived from it would otherwise be compiled as divergent
+// (every wave issuing every side under an exec mask).
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
 template <typename T>
 struct Elem;
 template <>
@@ -123,12 +129,14 @@ __device__ __forceinline__ SeqInfo seq_info(const int64_t* off, const int32_t* n
 
 // Log-bucketed time difference: 0 for dt <= 0, else 1 + (k << s) + the s bits
 // right below the leading one of dt, k = floor(log2 dt), capped at nb - 1.
+// Written with selects only (no per-lane branch), so that callers inside
+// wave-uniform branches keep those branches.
 __device__ __forceinline__ int time_bucket(int64_t dt, int nb, int s) {
-  if (dt <= 0) return 0;
-  int k = 63 - __clzll((unsigned long long)dt);
-  int64_t below = (k >= s) ? (dt >> (k - s)) : (dt << (s - k));
+  const int k = 63 - __clzll((unsigned long long)(dt | 1));
+  const int64_t below = (k >= s) ? (dt >> (k - s)) : (dt << (s - k));
   int b = 1 + (k << s) + (int)(below & ((1 << s) - 1));
-  return b < nb - 1 ? b : nb - 1;
+  b = b < nb - 1 ? b : nb - 1;
+  return dt > 0 ? b : 0;
 }
 
 // Smallest dt >= 1 whose time bucket is >= b, for a bucket b >= 1 that some

@@ -46,6 +46,19 @@ __device__ __forceinline__ void map_tile(int bid, int nrow, int ncol, int& tr, i
   tc = in / rows;
 }
 
+// A operand = plain rows of a [M, K] matrix.
+template <typename T>
+struct RowLoader {
+  const T* __restrict__ a;
+  int64_t row0, M;
+  int K;
+  __device__ __forceinline__ uint4 operator()(int k0, int r, int kc) const {
+    const int64_t row = row0 + r;
+    const int k = k0 + kc;
+    return (row < M && k < K) ? ld16(a + row * K + k) : make_uint4(0, 0, 0, 0);
+  }
+};
+
 template <typename T>
 __device__ __forceinline__ typename Elem<T>::Frag lds_frag(const T* p) {
   return *reinterpret_cast<const typename Elem<T>::Frag*>(p);
@@ -58,7 +71,7 @@ template <typename T, class ALoad>
 __device__ __forceinline__ void gemm_mainloop(ALoad& aload, const T* __restrict__ b, int64_t col0,
                                               int N, int K, T* As, T* Bs, f32x16 (&acc)[2][2]) {
   typedef GemmTile<T> G;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
   const int wm = w >> 1, wn = w & 1;
   uint4 ra[G::NCH], rb[G::NCH];
   auto gload = [&](int k0) {

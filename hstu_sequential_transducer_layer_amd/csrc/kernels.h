@@ -34,10 +34,11 @@ hipError_t launch_attn(const hstu_desc& d, const int64_t* off, const int32_t* nc
                        const void* k, const void* v, void* av, float* stats, const int2* tiles,
                        const int32_t* tiles_count, hipStream_t s);
 
-// --- out.hip: out = (LN_av(av) * u) W2^T + b2 (+ x).
-hipError_t launch_out(const hstu_desc& d, const void* x, int64_t T, const hstu_weights& w,
-                      const void* u, const void* av, const float* stats, void* out, void* z_out,
-                      hipStream_t s);
+// --- out.hip: z = LN_av(av) * u, then out = z W2^T + b2 (+ x).
+hipError_t launch_gate(const hstu_desc& d, int64_t T, const hstu_weights& w, const void* u,
+                       const void* av, const float* stats, void* z, hipStream_t s);
+hipError_t launch_f2(const hstu_desc& d, const void* x, int64_t T, const hstu_weights& w,
+                     const void* z, void* out, hipStream_t s);
 
 // --- debug.hip
 hipError_t launch_debug_indices(const hstu_desc& d, const int64_t* off, const int32_t* ncand,

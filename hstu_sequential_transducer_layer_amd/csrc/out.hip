@@ -4,97 +4,80 @@
 // the merged heads, multiply by u, f2, residual add); page "HSTU: The First
 // Exploration of the Scaling Law", 7.1.4 Innovation 1 (LayerNorm(AV) * U).
 //
-// One fused kernel: the A operand of the f2 GEMM is produced on the fly from
-// the per-head-centred AV, the fp32 per-(row, head) statistics written by the
-// attention kernel, the LayerNorm affine and U; bias and residual are added in
-// the epilogue.  Row statistics are merged from the H head partials with the
-// parallel-variance formula: mean = avg_h mean_h,
-// M2 = sum_h M2_h + dv * sum_h (mean_h - mean)^2, so no bf16-rounded value ever
-// enters a variance.
+// Two kernels:
+//  * gate: Z = (LayerNorm(AV) * g + b) * U, one wave per row, reading the
+//    per-head-centred AV, the fp32 per-(row, head) statistics written by the
+//    attention kernel and U once each (HBM-bound).  Row statistics are merged
+//    from the H head partials with the parallel-variance formula:
+//    mean = avg_h mean_h, M2 = sum_h M2_h + dv * sum_h (mean_h - mean)^2, so no
+//    bf16-rounded value ever enters a variance.
+//  * f2: the MFMA GEMM Z W2^T with + b2 and the residual in its epilogue.
+// Producing Z inside the GEMM's operand load instead would redo the gate once
+// per output-column tile (d_model / 256 times) and hold its inputs in
+// registers next to the accumulators; writing Z once and reading it back costs
+// one extra pass over T x H*dv elements.
 #include "common.h"
 #include "gemm.h"
+#include "gemm2.h"
 #include "kernels.h"
 
 namespace hstu {
 
+// One wave per row; K = H * dv columns, head h owning [h*dv, (h+1)*dv).
 template <typename T>
-struct GateLoader {
-  const T* __restrict__ av;
-  const T* __restrict__ u;
-  const T* __restrict__ g;
-  const T* __restrict__ be;
-  T* __restrict__ z_out;  // optional copy of the produced operand
-  const float* __restrict__ stats;  // [M, H, 2] per-head mean, M2
-  const float* s_mean;    // [BM] LDS: mean of the merged row
-  const float* s_rstd;    // [BM] LDS: 1 / sqrt(var + eps)
-  int64_t row0, M;
-  int K, H, dv;
-  __device__ __forceinline__ uint4 operator()(int k0, int r, int kc) const {
-    constexpr int V = Elem<T>::kVec;
-    const int64_t row = row0 + r;
-    const int k = k0 + kc;
-    if (row >= M || k >= K) return make_uint4(0, 0, 0, 0);
-    float a[V], uu[V], gg[V], bb[V], z[V];
-    unpack(ld16(av + row * K + k), a, T());
-    unpack(ld16(u + row * K + k), uu, T());
-    unpack(ld16(g + k), gg, T());
-    unpack(ld16(be + k), bb, T());
-    const float rs = s_rstd[r], sh = stats[(row * H + k / dv) * 2] - s_mean[r];
+__global__ __launch_bounds__(256) void gate_kernel(const T* __restrict__ av, const T* __restrict__ u,
+                                                   const float* __restrict__ stats,
+                                                   const T* __restrict__ g, const T* __restrict__ be,
+                                                   T* __restrict__ z, int64_t M, int H, int dv,
+                                                   float eps) {
+  constexpr int V = Elem<T>::kVec;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + wave_id();
+  if (row >= M) return;  // whole wave leaves together
+  const int K = H * dv;
+  // lane h < H holds head h's partials
+  const float2 st = lane < H ? reinterpret_cast<const float2*>(stats)[row * H + lane] : make_float2(0.f, 0.f);
+  const float mean = wave_sum(st.x) / (float)H;
+  const float dm = st.x - mean;
+  const float m2 = wave_sum(lane < H ? st.y + (float)dv * dm * dm : 0.f);
+  const float rstd = rsqrtf(m2 / (float)K + eps);
+  const T* ar = av + row * K;
+  const T* ur = u + row * K;
+  T* zr = z + row * K;
+#pragma unroll 2
+  for (int c = lane * V; c < K; c += kWave * V) {
+    float a[V], uu[V], gg[V], bb[V], o[V];
+    unpack(ld16(ar + c), a, T());
+    unpack(ld16(ur + c), uu, T());
+    unpack(ld16(g + c), gg, T());
+    unpack(ld16(be + c), bb, T());
+    const float sh = __shfl(dm, c / dv, kWave);  // mean_h - mean of this chunk's head
 #pragma unroll
-    for (int e = 0; e < V; ++e) z[e] = ((a[e] + sh) * rs * gg[e] + bb[e]) * uu[e];
-    uint4 out = pack(z, T());
-    if (z_out) st16(z_out + row * K + k, out);
-    return out;
+    for (int e = 0; e < V; ++e) o[e] = ((a[e] + sh) * rstd * gg[e] + bb[e]) * uu[e];
+    st16(zr + c, pack(o, T()));
   }
-};
+}
 
-// `out` may alias `x`: each output element is read (residual) and written by
-// the same thread, and nothing else in the kernel reads x.
+// f2 for any dtype / width: 128 x 128 tiles.  `out` may alias `x`: each output
+// element is read (residual) and written by the same thread, and nothing else
+// in the kernel reads x.
 template <typename T>
-__global__ __launch_bounds__(256, 2) void out_kernel(const T* x, const T* __restrict__ w2,
-                                                     const T* __restrict__ b2, const T* __restrict__ g,
-                                                     const T* __restrict__ be, const T* __restrict__ u,
-                                                     const T* __restrict__ av,
-                                                     const float* __restrict__ stats,
-                                                     T* out, T* __restrict__ z_out,
-                                                     int64_t M, int N, int H, int dv, float eps,
-                                                     int residual) {
+__global__ __launch_bounds__(256, 2) void f2_kernel(const T* x, const T* __restrict__ zin,
+                                                    const T* __restrict__ w2, const T* __restrict__ b2,
+                                                    T* out, int64_t M, int N, int K, int residual) {
   typedef GemmTile<T> G;
   __shared__ __attribute__((aligned(16))) T As[G::BM * G::LDK];
   __shared__ __attribute__((aligned(16))) T Bs[G::BN * G::LDK];
-  __shared__ float s_mean[G::BM], s_rstd[G::BM];
-  const int K = H * dv;
   const int nrow = (int)((M + G::BM - 1) / G::BM), ncol = (N + G::BN - 1) / G::BN;
   int tr, tc;
   map_tile(blockIdx.x, nrow, ncol, tr, tc);
   const int64_t row0 = (int64_t)tr * G::BM;
   const int col0 = tc * G::BN;
-
-  // Row statistics of the merged heads.
-  for (int r = threadIdx.x; r < G::BM; r += 256) {
-    const int64_t row = row0 + r;
-    float mean = 0.f, rstd = 0.f;
-    if (row < M) {
-      const float* st = stats + row * H * 2;
-      for (int h = 0; h < H; ++h) mean += st[2 * h];
-      mean /= (float)H;
-      float m2 = 0.f;
-      for (int h = 0; h < H; ++h) {
-        const float dm = st[2 * h] - mean;
-        m2 += st[2 * h + 1] + (float)dv * dm * dm;
-      }
-      rstd = rsqrtf(m2 / (float)K + eps);
-    }
-    s_mean[r] = mean;
-    s_rstd[r] = rstd;
-  }
-  __syncthreads();
-
-  GateLoader<T> al{av, u, g, be, tc == 0 ? z_out : nullptr, stats, s_mean, s_rstd, row0, M, K, H, dv};
+  RowLoader<T> al{zin, row0, M, K};
   f32x16 acc[2][2];
   gemm_mainloop<T>(al, w2, col0, N, K, As, Bs, acc);
 
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
+  const int lane = threadIdx.x & 63, w = wave_id(), wm = w >> 1, wn = w & 1;
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     const int col = col0 + wn * 64 + nt * 32 + (lane & 31);
@@ -115,24 +98,82 @@ __global__ __launch_bounds__(256, 2) void out_kernel(const T* x, const T* __rest
   }
 }
 
-hipError_t launch_out(const hstu_desc& d, const void* x, int64_t T, const hstu_weights& w,
-                      const void* u, const void* av, const float* stats, void* out, void* z_out,
-                      hipStream_t s) {
+// f2 for bf16 with K a multiple of 64: 256 x 256 tiles, both operands copied
+// straight into LDS.  Same aliasing rule as f2_kernel.
+__global__ __launch_bounds__(512, 2) void f2_big_kernel(const bf16* x, const bf16* __restrict__ zin,
+                                                        const bf16* __restrict__ w2,
+                                                        const bf16* __restrict__ b2, bf16* out, int64_t M,
+                                                        int N, int K, int residual) {
+  __shared__ __attribute__((aligned(16))) bf16 As0[G2::STAGE];
+  __shared__ __attribute__((aligned(16))) bf16 As1[G2::STAGE];
+  __shared__ __attribute__((aligned(16))) bf16 Bs0[G2::STAGE];
+  __shared__ __attribute__((aligned(16))) bf16 Bs1[G2::STAGE];
+  const int nrow = (int)((M + G2::BM - 1) / G2::BM), ncol = (N + G2::BN - 1) / G2::BN;
+  int tr, tc;
+  map_tile(blockIdx.x, nrow, ncol, tr, tc);
+  const int64_t row0 = (int64_t)tr * G2::BM;
+  const int col0 = tc * G2::BN;
+  const int lane = threadIdx.x & 63, w = wave_id(), wm = w >> 1, wn = w & 1;
+  G2RowsA ap;
+  ap.c.init(zin, row0, M, K, w, lane);
+  ap.w = w;
+  G2Copy bc;
+  bc.init(w2, col0, N, K, w, lane);
+  f32x16 acc[2][4];
+  g2_mainloop<true>(ap, bc, K, As0, As1, Bs0, Bs1, acc);
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    const int col = col0 + wn * 128 + nt * 32 + (lane & 31);
+    if (col >= N) continue;
+    const float bias = (float)b2[col];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = row0 + g2_row(wm, mt, lane, r);
+        if (row < M) {
+          float y = acc[mt][nt][r] + bias;
+          if (residual) y += (float)x[row * N + col];
+          out[row * N + col] = (bf16)y;
+        }
+      }
+  }
+}
+
+hipError_t launch_gate(const hstu_desc& d, int64_t T, const hstu_weights& w, const void* u,
+                       const void* av, const float* stats, void* z, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  const int N = d.d_model;
+  const dim3 grid((unsigned)((T + 3) / 4)), block(256);
+  if (d.dtype == HSTU_BF16)
+    hipLaunchKernelGGL(gate_kernel<bf16>, grid, block, 0, s, (const bf16*)av, (const bf16*)u, stats,
+                       (const bf16*)w.ln_av_g, (const bf16*)w.ln_av_b, (bf16*)z, T, d.num_heads, d.dv,
+                       d.ln_eps);
+  else
+    hipLaunchKernelGGL(gate_kernel<float>, grid, block, 0, s, (const float*)av, (const float*)u, stats,
+                       (const float*)w.ln_av_g, (const float*)w.ln_av_b, (float*)z, T, d.num_heads,
+                       d.dv, d.ln_eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_f2(const hstu_desc& d, const void* x, int64_t T, const hstu_weights& w,
+                     const void* z, void* out, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const int N = d.d_model, K = d.num_heads * d.dv;
+  const int res = (d.flags & HSTU_RESIDUAL) ? 1 : 0;
+  if (d.dtype == HSTU_BF16 && K % G2::BK == 0) {
+    const int64_t nr = (T + G2::BM - 1) / G2::BM, nc = (N + G2::BN - 1) / G2::BN;
+    hipLaunchKernelGGL(f2_big_kernel, dim3((unsigned)(nr * nc)), dim3(G2::NT), 0, s, (const bf16*)x,
+                       (const bf16*)z, (const bf16*)w.w2, (const bf16*)w.b2, (bf16*)out, T, N, K, res);
+    return hipGetLastError();
+  }
   const int64_t nrow = (T + 127) / 128, ncol = (N + 127) / 128;
   dim3 grid((unsigned)(nrow * ncol)), block(256);
-  const int res = (d.flags & HSTU_RESIDUAL) ? 1 : 0;
   if (d.dtype == HSTU_BF16)
-    hipLaunchKernelGGL(out_kernel<bf16>, grid, block, 0, s, (const bf16*)x, (const bf16*)w.w2,
-                       (const bf16*)w.b2, (const bf16*)w.ln_av_g, (const bf16*)w.ln_av_b,
-                       (const bf16*)u, (const bf16*)av, stats, (bf16*)out, (bf16*)z_out, T, N,
-                       d.num_heads, d.dv, d.ln_eps, res);
+    hipLaunchKernelGGL(f2_kernel<bf16>, grid, block, 0, s, (const bf16*)x, (const bf16*)z,
+                       (const bf16*)w.w2, (const bf16*)w.b2, (bf16*)out, T, N, K, res);
   else
-    hipLaunchKernelGGL(out_kernel<float>, grid, block, 0, s, (const float*)x, (const float*)w.w2,
-                       (const float*)w.b2, (const float*)w.ln_av_g, (const float*)w.ln_av_b,
-                       (const float*)u, (const float*)av, stats, (float*)out, (float*)z_out, T, N,
-                       d.num_heads, d.dv, d.ln_eps, res);
+    hipLaunchKernelGGL(f2_kernel<float>, grid, block, 0, s, (const float*)x, (const float*)z,
+                       (const float*)w.w2, (const float*)w.b2, (float*)out, T, N, K, res);
   return hipGetLastError();
 }
 

@@ -17,7 +17,7 @@ __global__ __launch_bounds__(256) void ln_in_kernel(const T* __restrict__ x, con
                                                     int64_t rows, int d, float eps) {
   constexpr int V = Elem<T>::kVec;
   const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t row = (int64_t)blockIdx.x * 4 + wave_id();
   if (row >= rows) return;  // whole wave leaves together
   const T* xr = x + row * d;
   T* yr = y + row * d;

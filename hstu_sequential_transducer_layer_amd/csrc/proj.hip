@@ -9,21 +9,10 @@
 //   U [T, H*dv] row-major, V [H, T, dv], Q [H, T, dqk], K [H, T, dqk].
 #include "common.h"
 #include "gemm.h"
+#include "gemm2.h"
 #include "kernels.h"
 
 namespace hstu {
-
-template <typename T>
-struct RowLoader {
-  const T* __restrict__ a;
-  int64_t row0, M;
-  int K;
-  __device__ __forceinline__ uint4 operator()(int k0, int r, int kc) const {
-    const int64_t row = row0 + r;
-    const int k = k0 + kc;
-    return (row < M && k < K) ? ld16(a + row * K + k) : make_uint4(0, 0, 0, 0);
-  }
-};
 
 template <typename T>
 __global__ __launch_bounds__(256, 2) void proj_kernel(const T* __restrict__ xn, const T* __restrict__ w1,
@@ -43,7 +32,7 @@ __global__ __launch_bounds__(256, 2) void proj_kernel(const T* __restrict__ xn, 
   f32x16 acc[2][2];
   gemm_mainloop<T>(al, w1, col0, N, K, As, Bs, acc);
 
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
+  const int lane = threadIdx.x & 63, w = wave_id(), wm = w >> 1, wn = w & 1;
   const int HDV = H * dv, HDQ = H * dqk;
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
@@ -81,10 +70,85 @@ __global__ __launch_bounds__(256, 2) void proj_kernel(const T* __restrict__ xn, 
   }
 }
 
+// Destination of output columns [cb, cb + 32): base pointer (already offset by
+// the lane's column) and row stride.  All 32 columns lie in one chunk of
+// U | V | Q | K and in one head, since every block and head width is a
+// multiple of 32.
+template <typename T>
+__device__ __forceinline__ T* proj_dst(int cb, int lane, T* u, T* v, T* q, T* k, int64_t M, int H,
+                                       int dqk, int dv, int64_t& rstride) {
+  const int HDV = H * dv, HDQ = H * dqk;
+  if (cb < HDV) {
+    rstride = HDV;
+    return u + cb + (lane & 31);
+  }
+  if (cb < 2 * HDV) {
+    const int c = cb - HDV, h = c / dv;
+    rstride = dv;
+    return v + (int64_t)h * M * dv + (c % dv) + (lane & 31);
+  }
+  if (cb < 2 * HDV + HDQ) {
+    const int c = cb - 2 * HDV, h = c / dqk;
+    rstride = dqk;
+    return q + (int64_t)h * M * dqk + (c % dqk) + (lane & 31);
+  }
+  const int c = cb - 2 * HDV - HDQ, h = c / dqk;
+  rstride = dqk;
+  return k + (int64_t)h * M * dqk + (c % dqk) + (lane & 31);
+}
+
+// Large-tile bf16 version (K a multiple of 64): 256 x 256 tiles, operands
+// copied straight into LDS.
+__global__ __launch_bounds__(512, 2) void proj2_kernel(const bf16* __restrict__ xn, const bf16* __restrict__ w1,
+                                                       const bf16* __restrict__ b1, bf16* __restrict__ u,
+                                                       bf16* __restrict__ v, bf16* __restrict__ q,
+                                                       bf16* __restrict__ k, int64_t M, int N, int K, int H,
+                                                       int dqk, int dv) {
+  __shared__ __attribute__((aligned(16))) bf16 As0[G2::STAGE];
+  __shared__ __attribute__((aligned(16))) bf16 As1[G2::STAGE];
+  __shared__ __attribute__((aligned(16))) bf16 Bs0[G2::STAGE];
+  __shared__ __attribute__((aligned(16))) bf16 Bs1[G2::STAGE];
+  const int nrow = (int)((M + G2::BM - 1) / G2::BM), ncol = (N + G2::BN - 1) / G2::BN;
+  int tr, tc;
+  map_tile(blockIdx.x, nrow, ncol, tr, tc);
+  const int64_t row0 = (int64_t)tr * G2::BM;
+  const int col0 = tc * G2::BN;
+  const int lane = threadIdx.x & 63, w = wave_id(), wm = w >> 1, wn = w & 1;
+  G2RowsA ap;
+  ap.c.init(xn, row0, M, K, w, lane);
+  ap.w = w;
+  G2Copy bc;
+  bc.init(w1, col0, N, K, w, lane);
+  f32x16 acc[2][4];
+  g2_mainloop<true>(ap, bc, K, As0, As1, Bs0, Bs1, acc);
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    const int cb = col0 + wn * 128 + nt * 32;
+    if (cb >= N) continue;
+    const float bias = (float)b1[cb + (lane & 31)];
+    int64_t rstride;
+    bf16* base = proj_dst(cb, lane, u, v, q, k, M, H, dqk, dv, rstride);
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = row0 + g2_row(wm, mt, lane, r);
+        if (row < M) base[row * rstride] = (bf16)silu(acc[mt][nt][r] + bias);
+      }
+  }
+}
+
 hipError_t launch_proj(const hstu_desc& d, const void* xn, int64_t T, const void* w1,
                        const void* b1, void* u, void* v, void* q, void* k, hipStream_t s) {
   if (T == 0) return hipSuccess;
   const int N = 2 * d.num_heads * (d.dqk + d.dv), K = d.d_model;
+  if (d.dtype == HSTU_BF16 && K % G2::BK == 0) {
+    const int64_t nr = (T + G2::BM - 1) / G2::BM, nc = (N + G2::BN - 1) / G2::BN;
+    hipLaunchKernelGGL(proj2_kernel, dim3((unsigned)(nr * nc)), dim3(G2::NT), 0, s, (const bf16*)xn,
+                       (const bf16*)w1, (const bf16*)b1, (bf16*)u, (bf16*)v, (bf16*)q, (bf16*)k, T, N,
+                       K, d.num_heads, d.dqk, d.dv);
+    return hipGetLastError();
+  }
   const int64_t nrow = (T + 127) / 128, ncol = (N + 127) / 128;
   dim3 grid((unsigned)(nrow * ncol)), block(256);
   if (d.dtype == HSTU_BF16)

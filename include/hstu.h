@@ -168,13 +168,24 @@ hstu_status hstu_attn_fwd(const hstu_desc* desc, const int64_t* seq_offsets, int
                           const hstu_activations* acts, void* workspace, size_t workspace_bytes,
                           hstu_stream_t stream);
 
+/* Stage 3a ([SRM] third equation, "Code" LayerNorm over the merged heads
+ * then multiplication by u; [FRC] 7.1.4 LayerNorm(AV) * U): reads acts->u,
+ * av, av_stats and weights->ln_av_g / ln_av_b; writes
+ * z = (LayerNorm(AV) * ln_av_g + ln_av_b) * U, [T, H*dv] in the layer dtype,
+ * row-major, caller-owned device memory, 16-byte aligned.                    */
+hstu_status hstu_gate_fwd(const hstu_desc* desc, int64_t total_tokens, const hstu_weights* weights,
+                          const hstu_activations* acts, void* z, hstu_stream_t stream);
+
 /* Stage 3 ([SRM] third equation, "Code" LayerNorm over merged heads, gate,
  * f2, residual; [FRC] 7.1.4 LayerNorm(AV) * U): reads acts->u, av, av_stats
- * (and x for the residual); writes out [T, d].  If z_out is not NULL the
- * gated normalised tensor Z [T, H*dv] is also written (for inspection).      */
+ * (and x for the residual); writes the gated normalised tensor
+ * z [T, H*dv] (layer dtype, row-major, caller-owned device memory, 16-byte
+ * aligned, required: it is the f2 GEMM's operand and stays readable
+ * afterwards) and out [T, d].  out may alias x; z must not overlap any other
+ * argument.                                                                  */
 hstu_status hstu_out_fwd(const hstu_desc* desc, const void* x, int64_t total_tokens,
                          const hstu_weights* weights, const hstu_activations* acts, void* out,
-                         void* z_out, hstu_stream_t stream);
+                         void* z, hstu_stream_t stream);
 
 /* Integer indexing used by stage 2, for inspection: for each flat pair
  * (query row, key row) in pairs[n_pairs][2] (int64, device) writes

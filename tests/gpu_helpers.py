@@ -21,8 +21,7 @@ def say(msg: str) -> None:
     sys.stdout.flush()
 
 
-def gpu_taps(w: "synth.Workload", layer_idx: int = 0, x=None, flags_extra: int = 0,
-             want_z: bool = True):
+def gpu_taps(w: "synth.Workload", layer_idx: int = 0, x=None, flags_extra: int = 0):
     """Run proj -> attn -> out through the stage entry points; returns numpy taps
     u [T,H*dv], v/q/k [T,H,dh], av [T,H*dv] (centred value + head mean),
     z [T,H*dv], y [T,d], plus the hstu_layer_fwd output y_layer."""
@@ -32,7 +31,7 @@ def gpu_taps(w: "synth.Workload", layer_idx: int = 0, x=None, flags_extra: int =
     xin = dev["x"] if x is None else x
     acts = _lib.proj_fwd(desc, xin, prm)
     _lib.attn_fwd(desc, dev["offsets"], dev["timestamps"], dev["num_candidates"], prm, acts)
-    y, z = _lib.out_fwd(desc, xin, prm, acts, want_z=want_z)
+    y, z = _lib.out_fwd(desc, xin, prm, acts)
     y_layer = _lib.layer_fwd(desc, xin, dev["offsets"], dev["timestamps"],
                              dev["num_candidates"], prm)
     torch.cuda.synchronize()

@@ -28,7 +28,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 10
+    assert len(names) == 11
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.EXPORTS)
@@ -126,6 +126,24 @@ def test_input_norm_weights_only_required_with_flag(lib):
     assert _call(lib, d, weights=w, T=0, B=1) == _lib.HSTU_OK
     d2 = _desc()
     assert _call(lib, d2, weights=w) == _lib.HSTU_ERR_INVALID_ARG
+
+
+def test_stage3_entry_points_check_arguments(lib):
+    d = _desc()
+    w = _lib.HstuWeights(*([FAKE] * 8))
+    a = _lib.HstuActivations(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    R = ctypes.byref
+    # z is required by both; NULL or misaligned is rejected before any launch
+    assert lib.hstu_gate_fwd(R(d), 100, R(w), R(a), None, None) == _lib.HSTU_ERR_INVALID_ARG
+    assert lib.hstu_gate_fwd(R(d), 100, R(w), R(a), FAKE + 8, None) == _lib.HSTU_ERR_INVALID_ARG
+    assert lib.hstu_out_fwd(R(d), FAKE, 100, R(w), R(a), FAKE, None, None) == _lib.HSTU_ERR_INVALID_ARG
+    assert lib.hstu_out_fwd(R(d), FAKE, 100, R(w), R(a), None, FAKE, None) == _lib.HSTU_ERR_INVALID_ARG
+    a_bad = _lib.HstuActivations(FAKE, FAKE, FAKE, FAKE, None, FAKE)    # no av
+    assert lib.hstu_gate_fwd(R(d), 100, R(w), R(a_bad), FAKE, None) == _lib.HSTU_ERR_INVALID_ARG
+    w_bad = _lib.HstuWeights(*([FAKE] * 6 + [None, FAKE]))             # no ln_av_g
+    assert lib.hstu_gate_fwd(R(d), 100, R(w_bad), R(a), FAKE, None) == _lib.HSTU_ERR_INVALID_ARG
+    assert lib.hstu_gate_fwd(R(d), -1, R(w), R(a), FAKE, None) == _lib.HSTU_ERR_INVALID_ARG
+    assert lib.hstu_gate_fwd(R(d), 0, R(w), R(a), FAKE, None) == _lib.HSTU_OK   # nothing to do
 
 
 def test_status_strings(lib):
