@@ -135,7 +135,7 @@ hstu_status check_acts(const hstu_activations* a, bool proj, bool attn) {
 
 // Workspace carve-up shared by the size query and the layer call.
 struct Layout {
-  size_t xn, u, v, q, k, av, stats, tiles, count, total;
+  size_t xn, u, v, q, k, av, stats, attn, total;
 };
 
 Layout layout(const hstu_desc* d, int64_t T, int32_t B) {
@@ -155,15 +155,12 @@ Layout layout(const hstu_desc* d, int64_t T, int32_t B) {
   L.k = take((size_t)T * hdq * e);
   L.av = take((size_t)T * hdv * e);
   L.stats = take((size_t)T * H * 2 * sizeof(float));
-  L.tiles = take((size_t)hstu::attn_max_tiles(T, B) * sizeof(int2));
-  L.count = take(sizeof(int32_t));
+  L.attn = take(hstu::attn_scratch_bytes(T, B));
   L.total = o;
   return L;
 }
 
-size_t attn_ws(int64_t T, int32_t B) {
-  return align256((size_t)hstu::attn_max_tiles(T, B) * sizeof(int2)) + align256(sizeof(int32_t));
-}
+size_t attn_ws(int64_t T, int32_t B) { return hstu::attn_scratch_bytes(T, B); }
 
 hstu_status device(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(HSTU_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
@@ -244,11 +241,12 @@ static hstu_status run_proj(const hstu_desc* d, const void* x, int64_t T, const 
 
 static hstu_status run_attn(const hstu_desc* d, const int64_t* off, int32_t B, int64_t T,
                             const int64_t* ts, const int32_t* nc, const hstu_bias_tables* t,
-                            const hstu_activations* a, int2* tiles, int32_t* count, hipStream_t s) {
-  hstu_status st = device(hstu::launch_build_tiles(off, nc, B, T, tiles, count, s), "tile list launch");
+                            const hstu_activations* a, void* scratch, hipStream_t s) {
+  const hstu::AttnScratch sc = hstu::attn_scratch(scratch, T, B);
+  hstu_status st = device(hstu::launch_attn_prep(off, nc, B, T, ts, sc, s), "attention prep launch");
   if (st != HSTU_OK) return st;
-  return device(hstu::launch_attn(*d, off, nc, B, T, ts, *t, a->q, a->k, a->v, a->av, a->av_stats,
-                                  tiles, count, s), "attention launch");
+  return device(hstu::launch_attn(*d, off, nc, B, T, ts, *t, a->q, a->k, a->v, a->av, a->av_stats, sc, s),
+                "attention launch");
 }
 
 hstu_status hstu_proj_fwd(const hstu_desc* desc, const void* x, int64_t T, const hstu_weights* w,
@@ -285,10 +283,7 @@ hstu_status hstu_attn_fwd(const hstu_desc* desc, const int64_t* off, int32_t B, 
   hipStream_t s = (hipStream_t)stream;
   if (desc->flags & HSTU_VALIDATE)
     if ((st = validate_metadata(off, B, T, nc, s)) != HSTU_OK) return st;
-  char* base = (char*)ws;
-  int2* tiles = (int2*)base;
-  int32_t* count = (int32_t*)(base + align256((size_t)hstu::attn_max_tiles(T, B) * sizeof(int2)));
-  if ((st = run_attn(desc, off, B, T, ts, nc, tables, acts, tiles, count, s)) != HSTU_OK) return st;
+  if ((st = run_attn(desc, off, B, T, ts, nc, tables, acts, ws, s)) != HSTU_OK) return st;
   return ok();
 }
 
@@ -355,8 +350,7 @@ hstu_status hstu_layer_fwd(const hstu_desc* desc, const void* x, const int64_t* 
   a.av = base + L.av;
   a.av_stats = (float*)(base + L.stats);
   if ((st = run_proj(desc, x, T, w, &a, base + L.xn, s)) != HSTU_OK) return st;
-  if ((st = run_attn(desc, off, B, T, ts, nc, tables, &a, (int2*)(base + L.tiles),
-                     (int32_t*)(base + L.count), s)) != HSTU_OK)
+  if ((st = run_attn(desc, off, B, T, ts, nc, tables, &a, base + L.attn, s)) != HSTU_OK)
     return st;
   // Z takes the V region: V [H, T, dv] has Z's size and is dead after stage 2.
   void* z = base + L.v;

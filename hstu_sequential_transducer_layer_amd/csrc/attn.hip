@@ -72,7 +72,9 @@ struct AttnArgs {
   void* av;
   float* stats;
   const int2* tiles;
-  const int32_t* tiles_count;
+  const int32_t* counts;   // [0]: work items
+  const int32_t* rel;      // per row: offset from its key block's earliest timestamp
+  const int64_t* tstat;    // per key block's first row: earliest, latest timestamp
   int64_t T;
   int H, P, NB, sbits, pos_stride, time_stride, norm_len, shared_pos;
 };
@@ -87,25 +89,43 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 // Asynchronous copy of one key block of a [rows, D] head-major tensor into a
-// swizzled LDS tile: every wave issues NCH/NW 16-byte-per-lane direct loads.
-// Rows past the sequence read its last row instead (finite values that the
-// mask turns into zero weight).
+// swizzled LDS tile: every wave issues PER 16-byte-per-lane direct loads.  The
+// per-lane element offsets (relative to the block's first row) are fixed and
+// computed once.  In a block that runs past the sequence's end, rows past it
+// read the sequence's last row instead (finite values that the mask turns into
+// zero weight), so no other sequence's data is read.
 template <typename T, int D, int NW, int CPR, bool IS_K>
-__device__ __forceinline__ void async_tile(const T* __restrict__ g, int j0, int L, T* lds, int w, int lane) {
-  constexpr int V = Elem<T>::kVec;
-  constexpr int NCH = 64 * CPR;  // BN = 64 rows
-  constexpr int PER = NCH / (NW * 64);
+struct TileCopy {
+  static constexpr int V = Elem<T>::kVec;
+  static constexpr int PER = 64 * CPR / (NW * 64);  // BN = 64 rows
+  static constexpr int LOG_D = D == 32 ? 5 : D == 64 ? 6 : 7;
+  static_assert(D == 32 || D == 64 || D == 128, "head width");
+  int off[PER];
+  __device__ __forceinline__ void init(int w, int lane) {
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int slot0 = (w * PER + i) * 64;
-    const int slot = slot0 + lane;
-    const int r = slot / CPR, pc = slot % CPR;
-    const int lc = pc ^ (IS_K ? k_swz<CPR>(r) : v_swz<CPR>(r));
-    const int j = min(j0 + r, L - 1);
-    __builtin_amdgcn_global_load_lds((glb_void*)(g + (int64_t)j * D + lc * V),
-                                     (lds_void*)(lds + slot0 * V), 16, 0, 0);
+    for (int i = 0; i < PER; ++i) {
+      const int slot = (w * PER + i) * 64 + lane;
+      const int r = slot / CPR, pc = slot % CPR;
+      off[i] = r * D + (pc ^ (IS_K ? k_swz<CPR>(r) : v_swz<CPR>(r))) * V;
+    }
   }
-}
+  // g: the block's first row; rows: rows of the sequence from there (>= 1).
+  __device__ __forceinline__ void issue(const T* __restrict__ g, int rows, T* lds, int w) const {
+    if (rows >= 64) {
+#pragma unroll
+      for (int i = 0; i < PER; ++i)
+        __builtin_amdgcn_global_load_lds((glb_void*)(g + off[i]), (lds_void*)(lds + (w * PER + i) * 64 * V), 16,
+                                         0, 0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int r = off[i] >> LOG_D, rr = min(r, rows - 1);
+        __builtin_amdgcn_global_load_lds((glb_void*)(g + off[i] + (rr - r) * D),
+                                         (lds_void*)(lds + (w * PER + i) * 64 * V), 16, 0, 0);
+      }
+    }
+  }
+};
 
 // A operand of S^T (K rows): row `r`, 8 elements starting at element `e0`.
 template <typename T, int D>
@@ -178,17 +198,39 @@ __device__ __forceinline__ f32x8 to_frag<float>(const float* p) {
   return f;
 }
 
+// Log time bucket of dt for |dt| < 2^24, where (float)dt is exact: its bits
+// hold the exponent floor(log2 dt) + 127 followed by the mantissa, so
+// bits >> (23 - s) = ((k + 127) << s) | (the s bits below the leading one).
+// dt <= 0 gives a value below 1 (the bits of a negative float are negative as
+// int32), which the clamp sends to bucket 0.  Equal to time_bucket there.
+__device__ __forceinline__ int time_bucket_small(int dt, int nb, int s) {
+  const int b = (__float_as_int((float)dt) >> (23 - s)) + 1 - (127 << s);
+  return min(max(b, 0), nb - 1);
+}
+
+// bucket_floor for buckets reached by dt < 2^24 (k < 24), in 32 bits and
+// with selects only.
+__device__ __forceinline__ int bucket_floor_small(int b, int s) {
+  const int c = b - 1, k = min(c >> s, 30), sub = c & ((1 << s) - 1);
+  const int sh = s - k;  // > 0 only when k < s (then sh <= s <= 4)
+  const int ge = (1 << k) | (sub << (k >= s ? k - s : 0));
+  const int lt = (1 << k) + ((sub + (1 << (sh > 0 ? sh : 0)) - 1) >> (sh > 0 ? sh : 0));
+  return k >= s ? ge : lt;
+}
+
 // Per-(wave, key block) inputs of the score -> weight step.
 struct ElemCtx {
-  int j0, iq, nh, p_q, R, NB, sbits;
+  int j0, iq, nh, p_q, R, NB, sbits, L;
   bool shared;
-  int64_t ts_q;
   float c_lo, c_hi;
-  int32_t thr;
+  int32_t thr;   // MODE 1: keys with offset <= thr take c_hi
+  int32_t hi32;  // MODE 2: t_i - (block's earliest timestamp)
+  int pq0, iq0;  // MODE 2: p(i) - j0 and i - j0
+  int64_t ts_q;
   const float* pos_s;
   const float* time_s;
-  const int64_t* ts_s;
   const int32_t* rel_s;
+  const int64_t* ts;  // MODE 3: the sequence's timestamps (global)
 };
 
 // Scores -> pointwise weights for one 32-key half held by this lane (query
@@ -197,14 +239,18 @@ struct ElemCtx {
 //           position bias both constant over the block).
 //   MODE 1: every pair attended, bias c_hi for keys whose offset from the
 //           block's earliest timestamp is <= thr, else c_lo.
-//   MODE 2: log time bucket, relative-position bucket and mask per pair.
+//   MODE 2: a block of history keys only: time bucket, relative-position
+//           bucket and causal mask per pair, with t_i - t_j = hi32 - offset_j
+//           in 32 bits (|dt| < 2^24 over the block) and position(j) = j.
+//   MODE 3: any block: the same from the 64-bit timestamps, with shared
+//           candidate positions and the candidate mask.
 template <int MODE>
 __device__ __forceinline__ void elems(const f32x16& s, float (&p)[16], int jb, const ElemCtx& x) {
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     const int jl0 = jb + 8 * g;
     int32_t rel[4];
-    if (MODE == 1) {
+    if (MODE == 1 || MODE == 2) {
       const int4 rv = *reinterpret_cast<const int4*>(x.rel_s + jl0);
       rel[0] = rv.x; rel[1] = rv.y; rel[2] = rv.z; rel[3] = rv.w;
     }
@@ -216,9 +262,14 @@ __device__ __forceinline__ void elems(const f32x16& s, float (&p)[16], int jb, c
         v = silu(s[r] + x.c_lo);
       } else if (MODE == 1) {
         v = silu(s[r] + (rel[e] <= x.thr ? x.c_hi : x.c_lo));
+      } else if (MODE == 2) {
+        const int bt = time_bucket_small((int)((uint32_t)x.hi32 - (uint32_t)rel[e]), x.NB, x.sbits);
+        const int d = min(max(x.pq0 - jl, -x.R), x.R);  // p(i) - p(j), clamped
+        v = silu(s[r] + (x.time_s[bt] + x.pos_s[x.R + d]));
+        v = jl <= x.iq0 ? v : 0.f;                     // j <= i
       } else {
-        const float b = x.time_s[time_bucket(wrap_sub(x.ts_q, x.ts_s[jl]), x.NB, x.sbits)] +
-                        x.pos_s[pos_bucket(x.p_q, position(j, x.nh, x.shared), x.R)];
+        const int bt = time_bucket(wrap_sub(x.ts_q, x.ts[min(j, x.L - 1)]), x.NB, x.sbits);
+        const float b = x.time_s[bt] + x.pos_s[pos_bucket(x.p_q, position(j, x.nh, x.shared), x.R)];
         v = silu(s[r] + b);
         v = attends(x.iq, j, x.nh) ? v : 0.f;
       }
@@ -237,10 +288,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) T Ks1[C::BN * DQK];
   __shared__ __attribute__((aligned(16))) T Vs0[C::BN * DV];
   __shared__ __attribute__((aligned(16))) T Vs1[C::BN * DV];
-  __shared__ int64_t ts_s[2][C::BN];
   __shared__ __attribute__((aligned(16))) int32_t rel_s[2][C::BN];
-  __shared__ int64_t blk_ts[2][2];
-  __shared__ int32_t blk_flags[2];
   extern __shared__ float tabs[];  // [P] position table then [NB] time table, head h
   float* pos_s = tabs;
   float* time_s = tabs + a.P;
@@ -248,7 +296,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
   const int H = a.H;
   const int h = blockIdx.x % H;
   const int item = blockIdx.x / H;
-  if (item >= *a.tiles_count) return;
+  if (item >= a.counts[0]) return;
   const int2 tl = a.tiles[item];
   const SeqInfo si = seq_info(a.off, a.ncand, tl.x, a.T);
   const int L = si.len, nh = si.nhist;
@@ -273,42 +321,33 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
 
   const T* kg = reinterpret_cast<const T*>(a.k) + ((int64_t)h * a.T + s0) * DQK;
   const T* vg = reinterpret_cast<const T*>(a.v) + ((int64_t)h * a.T + s0) * DV;
+  TileCopy<T, DQK, C::NW, C::KCPR, true> kcopy;
+  TileCopy<T, DV, C::NW, C::VCPR, false> vcopy;
+  kcopy.init(w, lane);
+  vcopy.init(w, lane);
+  // K, V and the keys' time offsets of block `blk` into buffer set (Kb, Vb, rb),
+  // and the block's earliest / latest timestamp into tb (read before the
+  // copies, so the wait that covers them covers it too).
+  auto issue = [&](int blk, T* Kb, T* Vb, int32_t* rb, longlong2& tb) __attribute__((always_inline)) {
+    const int j0 = block_start(blk);
+    tb = *reinterpret_cast<const longlong2*>(a.tstat + 2 * (s0 + j0));
+    kcopy.issue(kg + (int64_t)j0 * DQK, L - j0, Kb, w);
+    vcopy.issue(vg + (int64_t)j0 * DV, L - j0, Vb, w);
+    // the offsets array has kAttnBN rows of padding past T, so this never
+    // reads outside it; offsets of rows past the sequence are never used
+    if (w == 0)
+      __builtin_amdgcn_global_load_lds((glb_void*)(a.rel + s0 + j0 + lane), (lds_void*)rb, 4, 0, 0);
+  };
 
   // Issue the first block's copies before anything else.
-  if (nblk > 0) {
-    async_tile<T, DQK, C::NW, C::KCPR, true>(kg, block_start(0), L, Ks0, w, lane);
-    async_tile<T, DV, C::NW, C::VCPR, false>(vg, block_start(0), L, Vs0, w, lane);
-  }
-
-  // Key timestamps of a block (wave 0): their min/max over the block's real
-  // keys, and offsets from the minimum as int32 when the block spans < 2^31 s.
-  auto stage_ts = [&](int j0, int buf, int64_t t) __attribute__((always_inline)) {
-    const bool valid = j0 + lane < L;
-    int64_t mn = valid ? t : INT64_MAX, mx = valid ? t : INT64_MIN;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const int64_t omn = __shfl_xor(mn, o, kWave), omx = __shfl_xor(mx, o, kWave);
-      mn = omn < mn ? omn : mn;
-      mx = omx > mx ? omx : mx;
-    }
-    int64_t span;
-    const bool span_ok = !__builtin_sub_overflow(mx, mn, &span) && span <= INT32_MAX;
-    ts_s[buf][lane] = t;
-    rel_s[buf][lane] = (valid && span_ok) ? (int32_t)(t - mn) : INT32_MAX;
-    if (lane == 0) {
-      blk_ts[buf][0] = mn;
-      blk_ts[buf][1] = mx;
-      blk_flags[buf] = span_ok ? 1 : 0;
-    }
-  };
-  auto load_ts = [&](int j0) __attribute__((always_inline)) -> int64_t { return (j0 + lane < L) ? a.ts[s0 + j0 + lane] : 0; };
+  longlong2 tb0 = {0, 0}, tb1 = {0, 0};
+  if (nblk > 0) issue(0, Ks0, Vs0, rel_s[0], tb0);
 
   // Bias tables of head h, as fp32, into LDS.
   for (int i = tid; i < a.P; i += C::NT)
     pos_s[i] = to_f32(reinterpret_cast<const T*>(a.pos_tab)[(int64_t)h * a.pos_stride + i]);
   for (int i = tid; i < a.NB; i += C::NT)
     time_s[i] = to_f32(reinterpret_cast<const T*>(a.time_tab)[(int64_t)h * a.time_stride + i]);
-  if (w == 0 && nblk > 0) stage_ts(block_start(0), 0, load_ts(block_start(0)));
 
   // This lane's query row and its operand fragments.
   const int r0 = i0 + 32 * w;
@@ -337,8 +376,9 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
   __syncthreads();                // ... and every other wave's, plus tables
   const float cpos_far = pos_s[2 * R];  // bias of every pair at distance >= R
 
-  // One block of work out of buffer `buf`.
-  auto consume = [&](int blk, int buf, const T* Kb, const T* Vb) __attribute__((always_inline)) {
+  // One block of work out of buffer set (Kb, Vb, rb).
+  auto consume = [&](int blk, const T* Kb, const T* Vb, const int32_t* rb, int64_t tmin, int64_t tmax)
+                     __attribute__((always_inline)) {
     const int j0 = block_start(blk);
     const bool any_hist = j0 < nh && j0 <= rlast;
     const bool any_self = max(max(r0, nh), j0) <= min(rlast, j0 + C::BN - 1);
@@ -350,23 +390,35 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
     // Per query row: the block's time differences lie in [lo, hi]; the
     // bucket is monotone in dt, so one bucket, or two split by a threshold
     // on the key's time offset, covers the whole row.
-    const int64_t tmin = blk_ts[buf][0], tmax = blk_ts[buf][1];
-    const bool span_ok = blk_flags[buf] != 0;
+    int64_t span;
+    const bool span_ok = !__builtin_sub_overflow(tmax, tmin, &span) && span <= INT32_MAX;
     int64_t lo, hi;
     const bool novf = !__builtin_sub_overflow(ts_q, tmax, &lo) && !__builtin_sub_overflow(ts_q, tmin, &hi);
-    const int bt_lo = time_bucket(lo, a.NB, a.sbits), bt_hi = time_bucket(hi, a.NB, a.sbits);
+    const bool small = novf && hi < (1 << 24) && lo > -(1 << 24);
+    const bool all_small = __builtin_amdgcn_readfirstlane(__all(small || !qvalid) ? 1 : 0) != 0;
+    int bt_lo, bt_hi;
+    int32_t thr;
+    if (all_small) {
+      bt_lo = time_bucket_small((int)lo, a.NB, a.sbits);
+      bt_hi = time_bucket_small((int)hi, a.NB, a.sbits);
+      thr = (int)hi - bucket_floor_small(max(bt_hi, 1), a.sbits);
+    } else {
+      bt_lo = time_bucket(lo, a.NB, a.sbits);
+      bt_hi = time_bucket(hi, a.NB, a.sbits);
+      const int64_t tt = hi - bucket_floor(max(bt_hi, 1), a.sbits);
+      thr = tt > INT32_MAX ? INT32_MAX : (int32_t)tt;
+    }
     const bool one = novf && bt_lo == bt_hi;
     const bool two = novf && span_ok && bt_hi == bt_lo + 1;
-    // FAST: no mask, constant position bias, and per row at most two time
-    // buckets (decided for the whole wave).
+    // Fast modes: no mask, constant position bias, and per row at most two
+    // time buckets (decided for the whole wave).
     const bool fast = full && pos_far && __all(one || two || !qvalid);
     const float c_lo = time_s[bt_lo] + cpos_far, c_hi = time_s[bt_hi] + cpos_far;
-    // one bucket: thr = INT32_MAX, every key takes c_hi == c_lo (selects only)
-    const int64_t tt = hi - bucket_floor(bt_hi > 0 ? bt_hi : 1, a.sbits);
-    const int32_t thr = (one || bt_hi == 0 || tt > INT32_MAX) ? INT32_MAX : (int32_t)tt;
-    const int mode = __builtin_amdgcn_readfirstlane(!fast ? 2 : (__all(one || !qvalid) ? 0 : 1));
-    const ElemCtx x{j0, iq, nh, p_q, R, a.NB, a.sbits, shared, ts_q, c_lo, c_hi, thr,
-                    pos_s, time_s, ts_s[buf], rel_s[buf]};
+    const bool hist_only = j0 + C::BN <= nh;
+    const int mode = __builtin_amdgcn_readfirstlane(
+        !fast ? (all_small && hist_only ? 2 : 3) : (__all(one || !qvalid) ? 0 : 1));
+    const ElemCtx x{j0, iq, nh, p_q, R, a.NB, a.sbits, L, shared, c_lo, c_hi, thr, (int32_t)hi,
+                    p_q - j0, iq - j0, ts_q, pos_s, time_s, rb, a.ts + s0};
     // Per 32-key half: S^T (K fragments straight from LDS), then this half's
     // V fragments are read while its weights are computed, then P.V.
 #pragma unroll
@@ -386,8 +438,10 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
         elems<0>(sc, p, jb, x);
       else if (mode == 1)
         elems<1>(sc, p, jb, x);
-      else
+      else if (mode == 2)
         elems<2>(sc, p, jb, x);
+      else
+        elems<3>(sc, p, jb, x);
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2) {
         const Frag pf = to_frag<T>(p + 8 * c2);
@@ -401,28 +455,24 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
   // (the compiler then needs no wait on the in-flight copy before reading the
   // other buffer): the copies of block b+1 run while block b is consumed; one
   // barrier per block.
+  // The block timestamps move to scalar registers once their load has
+  // completed (after the wait that precedes each barrier).
+  int64_t tmin0 = uniform64(tb0.x), tmax0 = uniform64(tb0.y), tmin1 = 0, tmax1 = 0;
   for (int blk = 0; blk < nblk; blk += 2) {
-    int64_t tnext = 0;
-    if (blk + 1 < nblk) {
-      async_tile<T, DQK, C::NW, C::KCPR, true>(kg, block_start(blk + 1), L, Ks1, w, lane);
-      async_tile<T, DV, C::NW, C::VCPR, false>(vg, block_start(blk + 1), L, Vs1, w, lane);
-      if (w == 0) tnext = load_ts(block_start(blk + 1));
-    }
-    consume(blk, 0, Ks0, Vs0);
+    if (blk + 1 < nblk) issue(blk + 1, Ks1, Vs1, rel_s[1], tb1);
+    consume(blk, Ks0, Vs0, rel_s[0], tmin0, tmax0);
     if (blk + 1 >= nblk) break;
-    if (w == 0) stage_ts(block_start(blk + 1), 1, tnext);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (blk + 2 < nblk) {
-      async_tile<T, DQK, C::NW, C::KCPR, true>(kg, block_start(blk + 2), L, Ks0, w, lane);
-      async_tile<T, DV, C::NW, C::VCPR, false>(vg, block_start(blk + 2), L, Vs0, w, lane);
-      if (w == 0) tnext = load_ts(block_start(blk + 2));
-    }
-    consume(blk + 1, 1, Ks1, Vs1);
+    tmin1 = uniform64(tb1.x);
+    tmax1 = uniform64(tb1.y);
+    if (blk + 2 < nblk) issue(blk + 2, Ks0, Vs0, rel_s[0], tb0);
+    consume(blk + 1, Ks1, Vs1, rel_s[1], tmin1, tmax1);
     if (blk + 2 >= nblk) break;
-    if (w == 0) stage_ts(block_start(blk + 2), 0, tnext);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    tmin0 = uniform64(tb0.x);
+    tmax0 = uniform64(tb0.y);
   }
 
   // Epilogue: scale by 1/N_b, per-(row, head) mean and M2 over dv, centred AV.
@@ -500,8 +550,8 @@ static hipError_t launch_dims_f32(const AttnArgs& a, int dqk, int dv, int64_t gr
 
 hipError_t launch_attn(const hstu_desc& d, const int64_t* off, const int32_t* ncand, int32_t B,
                        int64_t T, const int64_t* ts, const hstu_bias_tables& tab, const void* q,
-                       const void* k, const void* v, void* av, float* stats, const int2* tiles,
-                       const int32_t* tiles_count, hipStream_t s) {
+                       const void* k, const void* v, void* av, float* stats, const AttnScratch& sc,
+                       hipStream_t s) {
   if (T == 0) return hipSuccess;
   AttnArgs a;
   a.off = off;
@@ -514,8 +564,10 @@ hipError_t launch_attn(const hstu_desc& d, const int64_t* off, const int32_t* nc
   a.v = v;
   a.av = av;
   a.stats = stats;
-  a.tiles = tiles;
-  a.tiles_count = tiles_count;
+  a.tiles = sc.tiles;
+  a.counts = sc.counts;
+  a.rel = sc.rel;
+  a.tstat = sc.tstat;
   a.T = T;
   a.H = d.num_heads;
   a.P = d.pos_buckets;

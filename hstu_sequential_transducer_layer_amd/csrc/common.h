@@ -29,6 +29,13 @@ constexpr int kWave = 64;
 // (every wave issuing every side under an exec mask).
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
+// A wave-uniform 64-bit value moved to scalar registers (both halves).
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 template <typename T>
 struct Elem;
 template <>
@@ -155,11 +162,7 @@ __device__ __forceinline__ int64_t wrap_sub(int64_t a, int64_t b) {
   return (int64_t)((uint64_t)a - (uint64_t)b);
 }
 
-__device__ __forceinline__ int pos_bucket(int pi, int pj, int R) {
-  int d = pi - pj;
-  d = d < -R ? -R : (d > R ? R : d);
-  return d + R;
-}
+__device__ __forceinline__ int pos_bucket(int pi, int pj, int R) { return min(max(pi - pj, -R), R) + R; }
 
 __device__ __forceinline__ int position(int i, int nhist, bool shared) {
   return shared ? (i < nhist ? i : nhist) : i;

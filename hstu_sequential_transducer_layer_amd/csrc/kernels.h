@@ -15,14 +15,53 @@ constexpr int kAttnBN = 64;
 
 // Upper bound on attention work items (q-tiles over all sequences).
 inline int64_t attn_max_tiles(int64_t T, int32_t B) { return (T + kAttnBM - 1) / kAttnBM + B; }
+// Upper bound on key blocks (64 keys from a sequence's start) over all sequences.
+inline int64_t attn_max_kblocks(int64_t T, int32_t B) { return (T + kAttnBN - 1) / kAttnBN + B; }
+
+// Device scratch of the attention stage, carved from one caller buffer.
+//   tiles   int2 {b, q-tile}, work list ordered by decreasing cost
+//   kblocks int2 {b, key block}, every key block once, any order
+//   counts  int32 [2]: number of tiles, number of key blocks
+//   rel     int32 [T + kAttnBN]: ts[row] - (earliest timestamp of its key block)
+//   tstat   int64 [T][2]: at each key block's first row, the block's
+//           earliest and latest timestamps (other rows unused)
+struct AttnScratch {
+  int2* tiles;
+  int2* kblocks;
+  int32_t* counts;
+  int32_t* rel;
+  int64_t* tstat;
+};
+
+inline size_t attn_align(size_t n) { return (n + 255) & ~(size_t)255; }
+
+inline size_t attn_scratch_bytes(int64_t T, int32_t B) {
+  return attn_align((size_t)attn_max_tiles(T, B) * 8) + attn_align((size_t)attn_max_kblocks(T, B) * 8) +
+         attn_align(2 * sizeof(int32_t)) + attn_align((size_t)(T + kAttnBN) * 4) + attn_align((size_t)T * 16);
+}
+
+inline AttnScratch attn_scratch(void* base, int64_t T, int32_t B) {
+  char* p = (char*)base;
+  AttnScratch a;
+  a.tiles = (int2*)p;
+  p += attn_align((size_t)attn_max_tiles(T, B) * 8);
+  a.kblocks = (int2*)p;
+  p += attn_align((size_t)attn_max_kblocks(T, B) * 8);
+  a.counts = (int32_t*)p;
+  p += attn_align(2 * sizeof(int32_t));
+  a.rel = (int32_t*)p;
+  p += attn_align((size_t)(T + kAttnBN) * 4);
+  a.tstat = (int64_t*)p;
+  return a;
+}
 
 // --- prep.hip
 hipError_t launch_ln_in(hstu_dtype dt, const void* x, const void* g, const void* b, void* y,
                         int64_t T, int d, float eps, hipStream_t s);
-// Builds the attention work list: int2 {b, q-tile} ordered by decreasing cost,
-// count stored at tiles_count.  One workgroup.
-hipError_t launch_build_tiles(const int64_t* off, const int32_t* ncand, int32_t B, int64_t T,
-                              int2* tiles, int32_t* tiles_count, hipStream_t s);
+// Attention preparation: the work list (one workgroup), then the per-key-block
+// time-stamp summary (tstat, rel) that the attention kernel reads per block.
+hipError_t launch_attn_prep(const int64_t* off, const int32_t* ncand, int32_t B, int64_t T,
+                            const int64_t* ts, const AttnScratch& sc, hipStream_t s);
 
 // --- proj.hip: u|v|q|k = SiLU(xn W1^T + b1), scattered to the stage layouts.
 hipError_t launch_proj(const hstu_desc& d, const void* xn, int64_t T, const void* w1,
@@ -31,8 +70,8 @@ hipError_t launch_proj(const hstu_desc& d, const void* xn, int64_t T, const void
 // --- attn.hip
 hipError_t launch_attn(const hstu_desc& d, const int64_t* off, const int32_t* ncand, int32_t B,
                        int64_t T, const int64_t* ts, const hstu_bias_tables& tab, const void* q,
-                       const void* k, const void* v, void* av, float* stats, const int2* tiles,
-                       const int32_t* tiles_count, hipStream_t s);
+                       const void* k, const void* v, void* av, float* stats, const AttnScratch& sc,
+                       hipStream_t s);
 
 // --- out.hip: z = LN_av(av) * u, then out = z W2^T + b2 (+ x).
 hipError_t launch_gate(const hstu_desc& d, int64_t T, const hstu_weights& w, const void* u,

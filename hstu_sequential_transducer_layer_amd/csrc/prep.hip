@@ -5,7 +5,11 @@
 //  * build_tiles: the attention work list for jagged batches — one item per
 //    (sequence, 128-row query tile), ordered by decreasing work so the longest
 //    items start first (the pages' "sparsity-aware kernels for variable-length
-//    sequences", "Efficiency tricks" paragraph of the same page).
+//    sequences", "Efficiency tricks" paragraph of the same page), plus the
+//    list of all 64-key blocks;
+//  * block_ts: per 64-key block, the earliest and latest timestamp and each
+//    key's offset from the earliest — head- and query-independent facts that
+//    every attention workgroup streaming the block would otherwise recompute.
 #include "common.h"
 #include "kernels.h"
 
@@ -77,11 +81,15 @@ __global__ __launch_bounds__(kTileThreads) void build_tiles_kernel(const int64_t
                                                                    int32_t B, int64_t T,
                                                                    int64_t max_tiles,
                                                                    int2* __restrict__ tiles,
+                                                                   int64_t max_kblocks,
+                                                                   int2* __restrict__ kblocks,
                                                                    int32_t* __restrict__ count) {
   __shared__ int hist[kCostBuckets];
   __shared__ int part[kTileThreads];
+  __shared__ int nkb;
   const int tid = threadIdx.x;
   for (int i = tid; i < kCostBuckets; i += kTileThreads) hist[i] = 0;
+  if (tid == 0) nkb = 0;
   __syncthreads();
   for (int b = tid; b < B; b += kTileThreads) {
     SeqInfo si = seq_info(off, ncand, b, T);
@@ -114,14 +122,59 @@ __global__ __launch_bounds__(kTileThreads) void build_tiles_kernel(const int64_t
       int pos = atomicAdd(&hist[tile_cost_bucket(si, qt)], 1);
       if (pos < max_tiles) tiles[pos] = make_int2(b, qt);
     }
+    const int nb = (si.len + kAttnBN - 1) / kAttnBN;
+    const int kpos = nb > 0 ? atomicAdd(&nkb, nb) : 0;
+    for (int kb = 0; kb < nb; ++kb)
+      if (kpos + kb < max_kblocks) kblocks[kpos + kb] = make_int2(b, kb);
   }
-  if (tid == 0) *count = (int32_t)min((int64_t)total, max_tiles);
+  __syncthreads();
+  if (tid == 0) {
+    count[0] = (int32_t)min((int64_t)total, max_tiles);
+    count[1] = (int32_t)min((int64_t)nkb, max_kblocks);
+  }
 }
 
-hipError_t launch_build_tiles(const int64_t* off, const int32_t* ncand, int32_t B, int64_t T,
-                              int2* tiles, int32_t* tiles_count, hipStream_t s) {
+// One wave per key block: min / max of its timestamps and each key's offset
+// from the min (meaningful when the block spans at most INT32_MAX; the
+// attention kernel checks that from tstat before using rel).
+__global__ __launch_bounds__(256) void block_ts_kernel(const int64_t* __restrict__ off,
+                                                       const int32_t* __restrict__ ncand, int64_t T,
+                                                       const int64_t* __restrict__ ts,
+                                                       const int2* __restrict__ kblocks,
+                                                       const int32_t* __restrict__ count,
+                                                       int32_t* __restrict__ rel,
+                                                       int64_t* __restrict__ tstat) {
+  const int lane = threadIdx.x & 63;
+  const int64_t id = (int64_t)blockIdx.x * 4 + wave_id();
+  if (id >= count[1]) return;  // whole wave leaves together
+  const int2 e = kblocks[id];
+  const SeqInfo si = seq_info(off, ncand, e.x, T);
+  const int j = e.y * kAttnBN + lane;
+  const bool valid = j < si.len;
+  const int64_t t = valid ? ts[si.start + j] : 0;
+  int64_t mn = valid ? t : INT64_MAX, mx = valid ? t : INT64_MIN;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const int64_t omn = __shfl_xor(mn, o, kWave), omx = __shfl_xor(mx, o, kWave);
+    mn = omn < mn ? omn : mn;
+    mx = omx > mx ? omx : mx;
+  }
+  if (valid) rel[si.start + j] = (int32_t)(uint32_t)((uint64_t)t - (uint64_t)mn);
+  if (lane == 0) {
+    tstat[2 * (si.start + e.y * kAttnBN)] = mn;
+    tstat[2 * (si.start + e.y * kAttnBN) + 1] = mx;
+  }
+}
+
+hipError_t launch_attn_prep(const int64_t* off, const int32_t* ncand, int32_t B, int64_t T,
+                            const int64_t* ts, const AttnScratch& sc, hipStream_t s) {
+  const int64_t max_kb = attn_max_kblocks(T, B);
   hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(kTileThreads), 0, s, off, ncand, B, T,
-                     attn_max_tiles(T, B), tiles, tiles_count);
+                     attn_max_tiles(T, B), sc.tiles, max_kb, sc.kblocks, sc.counts);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(block_ts_kernel, dim3((unsigned)((max_kb + 3) / 4)), dim3(256), 0, s, off, ncand, T, ts,
+                     sc.kblocks, sc.counts, sc.rel, sc.tstat);
   return hipGetLastError();
 }
 

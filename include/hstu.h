@@ -160,7 +160,8 @@ hstu_status hstu_proj_fwd(const hstu_desc* desc, const void* x, int64_t total_to
 
 /* Stage 2 ([SRM] second equation and bullets; [FRC] 7.1.4 Innovations 1-2,
  * 7.1.5 candidate mask): reads acts->q, k, v; writes acts->av and
- * acts->av_stats.  Needs hstu_attn_workspace_size() bytes (the work list).    */
+ * acts->av_stats.  Needs hstu_attn_workspace_size() bytes (the work list and
+ * a per-key-block summary of the timestamps), 256-aligned.                   */
 size_t hstu_attn_workspace_size(const hstu_desc* desc, int64_t total_tokens, int32_t batch);
 hstu_status hstu_attn_fwd(const hstu_desc* desc, const int64_t* seq_offsets, int32_t batch,
                           int64_t total_tokens, const int64_t* timestamps,

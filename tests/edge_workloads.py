@@ -1,0 +1,39 @@
+"""Seeded workloads shared by the GPU parity tests and the CPU checks of
+their sensitivity (inputs only: no layer arithmetic here)."""
+
+import numpy as np
+
+from hstu_sequential_transducer_layer_amd import synth
+
+
+def boundary_offsets():
+    """Time offsets whose pairwise differences hit every log-bucket edge:
+    2^k - 1, 2^k, 2^k + 1 and the half-octave edges 3 * 2^(k-1) +- 1, up to
+    2^26 (past 2^24, where the kernel's 32-bit bucket path hands over to the
+    64-bit one)."""
+    offs = {0}
+    for k in range(0, 27):
+        offs.update(2 ** k + d for d in (-1, 0, 1))
+        if k >= 1:
+            offs.update(3 * 2 ** (k - 1) + d for d in (-1, 0, 1))
+    return np.array(sorted(o for o in offs if o >= 0), np.int64)
+
+
+def bucket_edge_workload(sub_bits: int, pos_buckets: int):
+    """Three sequences over the boundary offsets (increasing, shuffled,
+    decreasing), fp32, with a time table of unit-scale distinct values so that
+    a pair put in a neighbouring bucket moves its weight by O(1)."""
+    offs = boundary_offsets()
+    n = len(offs)
+    rng = np.random.default_rng(11 + sub_bits)
+    dims = synth.LayerDims(64, 2, 32, 32, pos_buckets=pos_buckets, time_buckets=64 << sub_bits,
+                           time_sub_bits=sub_bits, dtype="fp32")
+    w = synth.make_workload("small_fp32", seed=5, lengths=[n, n, n], candidates=[0, 0, 0], dims=dims)
+    ts = w.timestamps.copy()
+    base = synth.EPOCH
+    ts[0:n] = base + offs
+    ts[n:2 * n] = base + rng.permutation(offs)
+    ts[2 * n:] = base + offs[::-1]
+    w.timestamps = ts
+    w.layers[0]["time_table"] = rng.normal(0.0, 1.0, w.layers[0]["time_table"].shape).astype(np.float32)
+    return w

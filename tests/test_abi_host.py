@@ -52,13 +52,16 @@ def test_workspace_size_matches_layout(lib):
     e, H, dv, dq, dm = 2, 8, 128, 128, 512
     a = lambda n: (n + 255) // 256 * 256
     tiles = (T + 127) // 128 + B
+    kblocks = (T + 63) // 64 + B
+    # work list, key-block list, two counters, per-row offsets (+64 pad), per-row stats pair
+    attn = a(tiles * 8) + a(kblocks * 8) + a(8) + a((T + 64) * 4) + a(T * 16)
     want = (a(T * dm * e) + a(T * H * dv * e) * 3 + a(T * H * dq * e) * 2 + a(T * H * 8)
-            + a(tiles * 8) + a(4))
+            + attn)
     assert _lib.workspace_size(d, T, B) == want
     d2 = _desc(flags=_lib.HSTU_RESIDUAL)     # no input LayerNorm buffer
     assert _lib.workspace_size(d2, T, B) == want - a(T * dm * e)
     assert _lib.workspace_size(_desc(dqk=48), T, B) == 0
-    assert lib.hstu_attn_workspace_size(ctypes.byref(d), T, B) == a(tiles * 8) + a(4)
+    assert lib.hstu_attn_workspace_size(ctypes.byref(d), T, B) == attn
     assert lib.hstu_proj_workspace_size(ctypes.byref(d), T) == a(T * dm * e)
 
 

@@ -18,6 +18,7 @@ import torch
 from hstu_sequential_transducer_layer_amd import _lib, layer, synth
 from oracle import hstu_oracle as O
 
+from edge_workloads import bucket_edge_workload
 from gpu_helpers import check, gpu_taps, say
 
 pytestmark = pytest.mark.gpu
@@ -191,6 +192,17 @@ def _edge_workload(kind, seed=0, **flags):
 def test_edge_cases(kind, flags):
     w = _edge_workload(kind, **flags)
     say(f"edge {kind} {flags}: lengths {w.lengths().tolist()}")
+    _compare_layer(w)
+
+
+@pytest.mark.parametrize("sub_bits,pos_buckets", [(0, 9), (1, 9), (2, 129)])
+def test_time_bucket_edges_fp32(sub_bits, pos_buckets):
+    """Every time-bucket edge (edge_workloads.bucket_edge_workload): fp32
+    parity (1e-4) pins the bucket of every pair, since a pair moved to a
+    neighbouring bucket changes y by far more (tests/test_oracle_pins.py,
+    test_bucket_edge_workload_detects_a_wrong_bucket)."""
+    w = bucket_edge_workload(sub_bits, pos_buckets)
+    say(f"bucket edges s={sub_bits} P={pos_buckets}: {w.T} tokens")
     _compare_layer(w)
 
 

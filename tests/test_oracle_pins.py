@@ -379,3 +379,34 @@ def test_planted_time_direction_is_caught(monkeypatch):
     real = O.wrap_sub_i64
     monkeypatch.setattr(O, "wrap_sub_i64", lambda a, b: real(b, a))
     assert not _brute_pin_holds()
+
+
+# The GPU test over every time-bucket edge (test_time_bucket_edges_fp32) is
+# only as strong as its workload: a kernel that put pairs at one kind of edge
+# into the neighbouring bucket must move y by far more than the fp32
+# tolerance there (1e-4).  Planted in the oracle here, on the CPU.
+def _edge_shift(kind):
+    def shifted(dt, nb, s, real=O.time_bucket):
+        out = real(dt, nb, s)
+        d = np.asarray(dt, np.int64)
+        if kind == "octave":        # dt = 2^k goes one bucket down
+            hit = (d > 1) & ((d & (d - 1)) == 0)
+        elif kind == "half_octave":  # dt = 3 * 2^(k-1), k >= 2
+            q = d // 3
+            hit = (d > 3) & (d % 3 == 0) & ((q & (q - 1)) == 0)
+        else:                       # "large": dt = 2^k + 1 beyond 2^24
+            hit = (d > (1 << 24)) & (((d - 1) & (d - 2)) == 0)
+        return np.where(hit, np.maximum(out - 1, 0), out)
+    return shifted
+
+
+@pytest.mark.parametrize("kind,sub_bits", [("octave", 0), ("half_octave", 1), ("large", 1)])
+def test_bucket_edge_workload_detects_a_wrong_bucket(kind, sub_bits, monkeypatch):
+    from edge_workloads import bucket_edge_workload
+    w = bucket_edge_workload(sub_bits, 9)
+    ref = O.layer_forward(w.x, w.offsets, w.timestamps, w.num_candidates, w.layers[0], w.dims)["y"]
+    monkeypatch.setattr(O, "time_bucket", _edge_shift(kind))
+    bad = O.layer_forward(w.x, w.offsets, w.timestamps, w.num_candidates, w.layers[0], w.dims)["y"]
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    err = float(np.max(np.abs(bad - ref) / np.maximum(np.abs(ref), rms)))
+    assert err > 1e-3, (kind, err)
