@@ -151,6 +151,52 @@ __device__ __forceinline__ void g2_mainloop(AProd& ap, const G2Copy& bc, int K, 
   if (ks < nk) g2_mma_step<PIPE>(As0, Bs0, acc, wm, wn, lane);  // odd step count: last stage is in buffer 0
 }
 
+// ---------------------------------------------------------------- epilogue
+// The 256 x 256 output tile is staged through LDS so that global loads and
+// stores move 16 bytes per lane along rows: 64-row quarter q of the tile lives
+// in operand stage q (32 KB each), row-major, with 16-byte chunk c of row r at
+// chunk c ^ g2_out_swz(r).  In the accumulator phase a wave touches 32
+// consecutive columns of rows R and R + 4 (2 bytes per lane); the swizzle puts
+// those two rows on different banks.  In the row phase, "slot" s = i * 512 +
+// tid (i = 0..15) is row s / 32, physical chunk s % 32 of the tile, so each
+// thread keeps one logical column chunk for all its rows.
+__device__ __forceinline__ int g2_out_swz(int r) { return ((r >> 2) & 1) << 2; }
+
+// Element offset of (row within quarter, column within tile).
+__device__ __forceinline__ int g2_out_off(int r, int col) {
+  return r * G2::BN + (((col >> 3) ^ g2_out_swz(r)) << 3) + (col & 7);
+}
+
+// Row within the quarter of accumulator element r of wave tile (wm, mt).
+__device__ __forceinline__ int g2_out_row(int mt, int lane, int r) {
+  return mt * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+}
+
+// Logical column chunk of this thread in the row phase.
+__device__ __forceinline__ int g2_out_chunk(int tid) { return (tid & 31) ^ g2_out_swz(tid >> 5); }
+
+// Row phase: copy rows [row0, row0 + 256) x columns [col0, col0 + 256) of a
+// [M, ld] bf16 matrix into the staged tile (direct global->LDS, 16 bytes per
+// lane).  Rows past M and column chunks past N read valid elements instead;
+// those tile entries are never stored.
+struct G2Quarters {
+  bf16 *q0, *q1, *q2, *q3;
+  __device__ __forceinline__ bf16* operator[](int i) const { return i == 0 ? q0 : i == 1 ? q1 : i == 2 ? q2 : q3; }
+};
+
+__device__ __forceinline__ void g2_out_load(const bf16* g, int64_t row0, int64_t M, int col0, int N, int ld,
+                                            const G2Quarters& qs, int tid, int w) {
+  const int col = col0 + 8 * g2_out_chunk(tid);
+  const int colc = col < N ? col : 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int R = (i * G2::NT + tid) >> 5;
+    const int64_t row = row0 + R < M ? row0 + R : M - 1;
+    __builtin_amdgcn_global_load_lds((g2_glb_void*)(g + row * ld + colc),
+                                     (g2_lds_void*)(qs[i >> 2] + ((i & 3) * G2::NT + w * 64) * 8), 16, 0, 0);
+  }
+}
+
 // A operand = plain rows of a [M, K] matrix, copied directly.
 struct G2RowsA {
   G2Copy c;

@@ -99,7 +99,7 @@ __global__ __launch_bounds__(256, 2) void f2_kernel(const T* x, const T* __restr
 }
 
 // f2 for bf16 with K a multiple of 64: 256 x 256 tiles, both operands copied
-// straight into LDS.  Same aliasing rule as f2_kernel.
+// straight into LDS.
 __global__ __launch_bounds__(512, 2) void f2_big_kernel(const bf16* x, const bf16* __restrict__ zin,
                                                         const bf16* __restrict__ w2,
                                                         const bf16* __restrict__ b2, bf16* out, int64_t M,
@@ -113,7 +113,7 @@ __global__ __launch_bounds__(512, 2) void f2_big_kernel(const bf16* x, const bf1
   map_tile(blockIdx.x, nrow, ncol, tr, tc);
   const int64_t row0 = (int64_t)tr * G2::BM;
   const int col0 = tc * G2::BN;
-  const int lane = threadIdx.x & 63, w = wave_id(), wm = w >> 1, wn = w & 1;
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), wm = w >> 1, wn = w & 1;
   G2RowsA ap;
   ap.c.init(zin, row0, M, K, w, lane);
   ap.w = w;
@@ -121,22 +121,42 @@ __global__ __launch_bounds__(512, 2) void f2_big_kernel(const bf16* x, const bf1
   bc.init(w2, col0, N, K, w, lane);
   f32x16 acc[2][4];
   g2_mainloop<true>(ap, bc, K, As0, As1, Bs0, Bs1, acc);
+
+  // Epilogue through LDS (the operand stages are free once every wave is
+  // past its last MFMA read): residual tile in, + acc + b2 in place, rows out.
+  // Every x element of the tile is read before any element of out is
+  // written, so out may alias x.
+  __syncthreads();
+  const G2Quarters qs{As0, As1, Bs0, Bs1};
+  if (residual) {
+    g2_out_load(x, row0, M, col0, N, N, qs, tid, w);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+  bf16* const yq = qs[wm];
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) {
-    const int col = col0 + wn * 128 + nt * 32 + (lane & 31);
-    if (col >= N) continue;
-    const float bias = (float)b2[col];
+    const int ct = wn * 128 + nt * 32 + (lane & 31);
+    const float bias = col0 + ct < N ? (float)b2[col0 + ct] : 0.f;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t row = row0 + g2_row(wm, mt, lane, r);
-        if (row < M) {
-          float y = acc[mt][nt][r] + bias;
-          if (residual) y += (float)x[row * N + col];
-          out[row * N + col] = (bf16)y;
-        }
+        bf16* p = yq + g2_out_off(g2_out_row(mt, lane, r), ct);
+        float y = acc[mt][nt][r] + bias;
+        if (residual) y += (float)*p;
+        *p = (bf16)y;
       }
+  }
+  __syncthreads();
+  const int col = col0 + 8 * g2_out_chunk(tid);
+  if (col < N) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int s = i * G2::NT + tid;
+      const int64_t row = row0 + (s >> 5);
+      if (row < M) st16(out + row * N + col, ld16(qs[i >> 2] + (s & (4 * G2::NT - 1)) * 8));
+    }
   }
 }
 

@@ -121,20 +121,34 @@ __global__ __launch_bounds__(512, 2) void proj2_kernel(const bf16* __restrict__ 
   bc.init(w1, col0, N, K, w, lane);
   f32x16 acc[2][4];
   g2_mainloop<true>(ap, bc, K, As0, As1, Bs0, Bs1, acc);
+
+  // Epilogue through LDS: SiLU(acc + b1) into the staged tile, then rows out
+  // with 16-byte stores (a 16-byte chunk never straddles a head or a chunk of
+  // U | V | Q | K).
+  __syncthreads();
+  const G2Quarters qs{As0, As1, Bs0, Bs1};
+  bf16* const yq = qs[wm];
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) {
-    const int cb = col0 + wn * 128 + nt * 32;
-    if (cb >= N) continue;
-    const float bias = (float)b1[cb + (lane & 31)];
-    int64_t rstride;
-    bf16* base = proj_dst(cb, lane, u, v, q, k, M, H, dqk, dv, rstride);
+    const int ct = wn * 128 + nt * 32 + (lane & 31);
+    const float bias = col0 + ct < N ? (float)b1[col0 + ct] : 0.f;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t row = row0 + g2_row(wm, mt, lane, r);
-        if (row < M) base[row * rstride] = (bf16)silu(acc[mt][nt][r] + bias);
-      }
+      for (int r = 0; r < 16; ++r)
+        yq[g2_out_off(g2_out_row(mt, lane, r), ct)] = (bf16)silu(acc[mt][nt][r] + bias);
+  }
+  __syncthreads();
+  const int col = col0 + 8 * g2_out_chunk(threadIdx.x);
+  if (col < N) {
+    int64_t rstride;
+    bf16* base = proj_dst(col & ~31, 0, u, v, q, k, M, H, dqk, dv, rstride) + (col & 31);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int s = i * G2::NT + threadIdx.x;
+      const int64_t row = row0 + (s >> 5);
+      if (row < M) st16(base + row * rstride, ld16(qs[i >> 2] + (s & (4 * G2::NT - 1)) * 8));
+    }
   }
 }
 
