@@ -243,7 +243,8 @@ static hstu_status run_attn(const hstu_desc* d, const int64_t* off, int32_t B, i
                             const int64_t* ts, const int32_t* nc, const hstu_bias_tables* t,
                             const hstu_activations* a, void* scratch, hipStream_t s) {
   const hstu::AttnScratch sc = hstu::attn_scratch(scratch, T, B);
-  hstu_status st = device(hstu::launch_attn_prep(off, nc, B, T, ts, sc, s), "attention prep launch");
+  hstu_status st = device(hstu::launch_attn_prep(off, nc, B, T, ts, hstu::kAttnBM, sc, s),
+                          "attention prep launch");
   if (st != HSTU_OK) return st;
   return device(hstu::launch_attn(*d, off, nc, B, T, ts, *t, a->q, a->k, a->v, a->av, a->av_stats, sc, s),
                 "attention launch");

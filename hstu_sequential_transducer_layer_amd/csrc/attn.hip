@@ -218,23 +218,27 @@ __device__ __forceinline__ int bucket_floor_small(int b, int s) {
   return k >= s ? ge : lt;
 }
 
-// Per-(wave, key block) inputs of the score -> weight step.
+// Per-(wave, key block) inputs of the score -> weight step.  Lane offsets are
+// folded into the per-lane fields, so the key index of accumulator entry r of
+// half kh is a compile-time constant c = 32 kh + 8 (r / 4) + r % 4 plus jq.
 struct ElemCtx {
-  int j0, iq, nh, p_q, R, NB, sbits, L;
+  int jq;        // j0 + 4 * (lane / 32): key index of c = 0
+  int iq, nh, p_q, R, NB, sbits, L;
   bool shared;
   float c_lo, c_hi;
   int32_t thr;   // MODE 1: keys with offset <= thr take c_hi
   int32_t hi32;  // MODE 2: t_i - (block's earliest timestamp)
-  int pq0, iq0;  // MODE 2: p(i) - j0 and i - j0
+  int pq0, iq0;  // MODE 2: p(i) - jq and i - jq
   int64_t ts_q;
   const float* pos_s;
   const float* time_s;
-  const int32_t* rel_s;
-  const int64_t* ts;  // MODE 3: the sequence's timestamps (global)
+  const int32_t* rel_s;  // the block's key offsets, from key jq
+  const int64_t* ts;     // MODE 3: the sequence's timestamps (global)
 };
 
-// Scores -> pointwise weights for one 32-key half held by this lane (query
-// iq, keys jb + 8*(r/4) + (r%4) of the block).  Every variant is branch-free.
+// Scores -> pointwise weights for one 32-key half (kb = 32 kh) held by this
+// lane: query iq, keys jq + kb + 8 (r / 4) + r % 4.  Every variant is
+// branch-free.
 //   MODE 0: every pair attended, one bias per row (c_lo: time bucket and
 //           position bias both constant over the block).
 //   MODE 1: every pair attended, bias c_hi for keys whose offset from the
@@ -245,18 +249,17 @@ struct ElemCtx {
 //   MODE 3: any block: the same from the 64-bit timestamps, with shared
 //           candidate positions and the candidate mask.
 template <int MODE>
-__device__ __forceinline__ void elems(const f32x16& s, float (&p)[16], int jb, const ElemCtx& x) {
+__device__ __forceinline__ void elems(const f32x16& s, float (&p)[16], int kb, const ElemCtx& x) {
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
-    const int jl0 = jb + 8 * g;
     int32_t rel[4];
     if (MODE == 1 || MODE == 2) {
-      const int4 rv = *reinterpret_cast<const int4*>(x.rel_s + jl0);
+      const int4 rv = *reinterpret_cast<const int4*>(x.rel_s + kb + 8 * g);
       rel[0] = rv.x; rel[1] = rv.y; rel[2] = rv.z; rel[3] = rv.w;
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int r = 4 * g + e, jl = jl0 + e, j = x.j0 + jl;
+      const int r = 4 * g + e, c = kb + 8 * g + e;
       float v;
       if (MODE == 0) {
         v = silu(s[r] + x.c_lo);
@@ -264,10 +267,11 @@ __device__ __forceinline__ void elems(const f32x16& s, float (&p)[16], int jb, c
         v = silu(s[r] + (rel[e] <= x.thr ? x.c_hi : x.c_lo));
       } else if (MODE == 2) {
         const int bt = time_bucket_small((int)((uint32_t)x.hi32 - (uint32_t)rel[e]), x.NB, x.sbits);
-        const int d = min(max(x.pq0 - jl, -x.R), x.R);  // p(i) - p(j), clamped
+        const int d = min(max(x.pq0 - c, -x.R), x.R);  // p(i) - p(j), clamped
         v = silu(s[r] + (x.time_s[bt] + x.pos_s[x.R + d]));
-        v = jl <= x.iq0 ? v : 0.f;                     // j <= i
+        v = c <= x.iq0 ? v : 0.f;                     // j <= i
       } else {
+        const int j = x.jq + c;
         const int bt = time_bucket(wrap_sub(x.ts_q, x.ts[min(j, x.L - 1)]), x.NB, x.sbits);
         const float b = x.time_s[bt] + x.pos_s[pos_bucket(x.p_q, position(j, x.nh, x.shared), x.R)];
         v = silu(s[r] + b);
@@ -278,8 +282,131 @@ __device__ __forceinline__ void elems(const f32x16& s, float (&p)[16], int jb, c
   }
 }
 
+// Facts about this lane's query row and its wave that the per-block
+// classification needs.
+struct QueryRow {
+  int r0, rlast, iq, p_q, pmin_q;  // wave's first / last row, this row, positions
+  bool qvalid;
+  int64_t ts_q;
+};
+
+// Per-(workgroup) constants of the classification.
+struct SeqCtx {
+  int L, nh, iend, R, NB, sbits;
+  bool shared;
+  float cpos_far;  // bias of every pair at relative distance >= R
+  const float* pos_s;
+  const float* time_s;
+  const int64_t* ts;  // the sequence's timestamps
+};
+
+// Whether any row of the wave attends a key of the block starting at j0.
+__device__ __forceinline__ bool block_active(int j0, const QueryRow& q, const SeqCtx& sq) {
+  const bool any_hist = j0 < sq.nh && j0 <= q.rlast;
+  const bool any_self = max(max(q.r0, sq.nh), j0) <= min(q.rlast, j0 + kAttnBN - 1);
+  return q.r0 < sq.iend && (any_hist || any_self);
+}
+
+// Weight mode of one (wave, key block) — wave-uniform — and the per-lane
+// context of the weight step.  Per query row the block's time differences lie
+// in [lo, hi]; the bucket is monotone in dt, so one bucket, or two split by a
+// threshold on the key's time offset, covers the whole row.
+__device__ __forceinline__ int classify_block(int j0, int64_t tmin, int64_t tmax, const QueryRow& q,
+                                              const SeqCtx& sq, const int32_t* rb, ElemCtx& x) {
+  const bool full = (j0 + kAttnBN - 1 <= q.r0) && (j0 + kAttnBN <= sq.nh);
+  const int pmax_k = position(min(j0 + kAttnBN - 1, sq.L - 1), sq.nh, sq.shared);
+  const bool pos_far = q.pmin_q - pmax_k >= sq.R;  // clamped position bias is constant
+  int64_t span;
+  const bool span_ok = !__builtin_sub_overflow(tmax, tmin, &span) && span <= INT32_MAX;
+  int64_t lo, hi;
+  const bool novf = !__builtin_sub_overflow(q.ts_q, tmax, &lo) && !__builtin_sub_overflow(q.ts_q, tmin, &hi);
+  const bool small = novf && hi < (1 << 24) && lo > -(1 << 24);
+  const bool all_small = __builtin_amdgcn_readfirstlane(__all(small || !q.qvalid) ? 1 : 0) != 0;
+  int bt_lo, bt_hi;
+  int32_t thr;
+  if (all_small) {
+    bt_lo = time_bucket_small((int)lo, sq.NB, sq.sbits);
+    bt_hi = time_bucket_small((int)hi, sq.NB, sq.sbits);
+    thr = (int)hi - bucket_floor_small(max(bt_hi, 1), sq.sbits);
+  } else {
+    bt_lo = time_bucket(lo, sq.NB, sq.sbits);
+    bt_hi = time_bucket(hi, sq.NB, sq.sbits);
+    const int64_t tt = hi - bucket_floor(max(bt_hi, 1), sq.sbits);
+    thr = tt > INT32_MAX ? INT32_MAX : (int32_t)tt;
+  }
+  const bool one = novf && bt_lo == bt_hi;
+  const bool two = novf && span_ok && bt_hi == bt_lo + 1;
+  // Fast modes: no mask, constant position bias, and per row at most two
+  // time buckets (decided for the whole wave).
+  const bool fast = full && pos_far && __all(one || two || !q.qvalid);
+  const float c_lo = sq.time_s[bt_lo] + sq.cpos_far, c_hi = sq.time_s[bt_hi] + sq.cpos_far;
+  const bool hist_only = j0 + kAttnBN <= sq.nh;
+  const int jq = j0 + 4 * (int)((threadIdx.x >> 5) & 1);
+  x = ElemCtx{jq, q.iq, sq.nh, q.p_q, sq.R, sq.NB, sq.sbits, sq.L, sq.shared, c_lo, c_hi, thr, (int32_t)hi,
+              q.p_q - jq, q.iq - jq, q.ts_q, sq.pos_s, sq.time_s, rb + (jq - j0), sq.ts};
+  return __builtin_amdgcn_readfirstlane(!fast ? (all_small && hist_only ? 2 : 3)
+                                              : (__all(one || !q.qvalid) ? 0 : 1));
+}
+
+// Weights of 32-key half kh in the wave's mode.
+__device__ __forceinline__ void half_weights(int mode, const f32x16& sc, float (&p)[16], int kh, const ElemCtx& x) {
+  if (mode == 0)
+    elems<0>(sc, p, 32 * kh, x);
+  else if (mode == 1)
+    elems<1>(sc, p, 32 * kh, x);
+  else if (mode == 2)
+    elems<2>(sc, p, 32 * kh, x);
+  else
+    elems<3>(sc, p, 32 * kh, x);
+}
+
+// Epilogue of one wave: scale by 1/N_b, per-(row, head) mean and M2 over dv,
+// centred AV in the layer dtype and the fp32 statistics.
+template <typename T, int DV>
+__device__ __forceinline__ void attn_store(f32x16 (&o)[DV / 32], float inv_n, bool qvalid, int64_t row, int h,
+                                           int H, void* av, float* stats, int half) {
+  float sum = 0.f;
+#pragma unroll
+  for (int n = 0; n < DV / 32; ++n)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      o[n][r] *= inv_n;
+      sum += o[n][r];
+    }
+  sum += __shfl_xor(sum, 32, kWave);
+  const float mean = sum / (float)DV;
+  float m2 = 0.f;
+#pragma unroll
+  for (int n = 0; n < DV / 32; ++n)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float dlt = o[n][r] - mean;
+      m2 += dlt * dlt;
+    }
+  m2 += __shfl_xor(m2, 32, kWave);
+  if (!qvalid) return;
+  T* dst = reinterpret_cast<T*>(av) + row * (int64_t)(H * DV) + h * DV;
+#pragma unroll
+  for (int n = 0; n < DV / 32; ++n)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      // rows 8g + 4*half + 0..3 of this 32-wide dv tile are consecutive
+      T* p = dst + n * 32 + 8 * g + 4 * half;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) p[e] = from_f32<T>(o[n][4 * g + e] - mean);
+    }
+  if (half == 0) {
+    stats[(row * H + h) * 2] = mean;
+    stats[(row * H + h) * 2 + 1] = m2;
+  }
+}
+
+// Workgroups per CU the register budget is sized for: three (at most 168
+// VGPRs per lane) when a q row plus a k row take at most 256 bytes, else two.
+constexpr int attn_min_blocks(int row_bytes) { return row_bytes <= 256 ? 3 : 2; }
+
 template <typename T, int DQK, int DV>
-__global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256, attn_min_blocks((DQK + DV) * (int)sizeof(T))) void attn_kernel(AttnArgs a) {
   typedef AttnCfg<T, DQK, DV> C;
   static_assert(C::NT == 256, "launch bounds assume 4 waves");
   typedef typename Elem<T>::Frag Frag;
@@ -377,48 +504,14 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
   const float cpos_far = pos_s[2 * R];  // bias of every pair at distance >= R
 
   // One block of work out of buffer set (Kb, Vb, rb).
+  const QueryRow qr{r0, rlast, iq, p_q, pmin_q, qvalid, ts_q};
+  const SeqCtx sq{L, nh, iend, R, a.NB, a.sbits, shared, cpos_far, pos_s, time_s, a.ts + s0};
   auto consume = [&](int blk, const T* Kb, const T* Vb, const int32_t* rb, int64_t tmin, int64_t tmax)
                      __attribute__((always_inline)) {
     const int j0 = block_start(blk);
-    const bool any_hist = j0 < nh && j0 <= rlast;
-    const bool any_self = max(max(r0, nh), j0) <= min(rlast, j0 + C::BN - 1);
-    if (r0 >= iend || !(any_hist || any_self)) return;
-    const bool full = (j0 + C::BN - 1 <= r0) && (j0 + C::BN <= nh);
-    const int pmax_k = position(min(j0 + C::BN - 1, L - 1), nh, shared);
-    const bool pos_far = pmin_q - pmax_k >= R;  // clamped position bias is constant
-
-    // Per query row: the block's time differences lie in [lo, hi]; the
-    // bucket is monotone in dt, so one bucket, or two split by a threshold
-    // on the key's time offset, covers the whole row.
-    int64_t span;
-    const bool span_ok = !__builtin_sub_overflow(tmax, tmin, &span) && span <= INT32_MAX;
-    int64_t lo, hi;
-    const bool novf = !__builtin_sub_overflow(ts_q, tmax, &lo) && !__builtin_sub_overflow(ts_q, tmin, &hi);
-    const bool small = novf && hi < (1 << 24) && lo > -(1 << 24);
-    const bool all_small = __builtin_amdgcn_readfirstlane(__all(small || !qvalid) ? 1 : 0) != 0;
-    int bt_lo, bt_hi;
-    int32_t thr;
-    if (all_small) {
-      bt_lo = time_bucket_small((int)lo, a.NB, a.sbits);
-      bt_hi = time_bucket_small((int)hi, a.NB, a.sbits);
-      thr = (int)hi - bucket_floor_small(max(bt_hi, 1), a.sbits);
-    } else {
-      bt_lo = time_bucket(lo, a.NB, a.sbits);
-      bt_hi = time_bucket(hi, a.NB, a.sbits);
-      const int64_t tt = hi - bucket_floor(max(bt_hi, 1), a.sbits);
-      thr = tt > INT32_MAX ? INT32_MAX : (int32_t)tt;
-    }
-    const bool one = novf && bt_lo == bt_hi;
-    const bool two = novf && span_ok && bt_hi == bt_lo + 1;
-    // Fast modes: no mask, constant position bias, and per row at most two
-    // time buckets (decided for the whole wave).
-    const bool fast = full && pos_far && __all(one || two || !qvalid);
-    const float c_lo = time_s[bt_lo] + cpos_far, c_hi = time_s[bt_hi] + cpos_far;
-    const bool hist_only = j0 + C::BN <= nh;
-    const int mode = __builtin_amdgcn_readfirstlane(
-        !fast ? (all_small && hist_only ? 2 : 3) : (__all(one || !qvalid) ? 0 : 1));
-    const ElemCtx x{j0, iq, nh, p_q, R, a.NB, a.sbits, L, shared, c_lo, c_hi, thr, (int32_t)hi,
-                    p_q - j0, iq - j0, ts_q, pos_s, time_s, rb, a.ts + s0};
+    if (!block_active(j0, qr, sq)) return;
+    ElemCtx x;
+    const int mode = classify_block(j0, tmin, tmax, qr, sq, rb, x);
     // Per 32-key half: S^T (K fragments straight from LDS), then this half's
     // V fragments are read while its weights are computed, then P.V.
 #pragma unroll
@@ -433,15 +526,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int n = 0; n < DV / 32; ++n) vf[c2][n] = v_frag<T, DV>(Vb, kh * 32 + 16 * c2, n, lane);
       float p[16];
-      const int jb = kh * 32 + half * 4;  // key offset of r = 0 for this lane
-      if (mode == 0)
-        elems<0>(sc, p, jb, x);
-      else if (mode == 1)
-        elems<1>(sc, p, jb, x);
-      else if (mode == 2)
-        elems<2>(sc, p, jb, x);
-      else
-        elems<3>(sc, p, jb, x);
+      half_weights(mode, sc, p, kh, x);
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2) {
         const Frag pf = to_frag<T>(p + 8 * c2);
@@ -475,43 +560,8 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
     tmax0 = uniform64(tb0.y);
   }
 
-  // Epilogue: scale by 1/N_b, per-(row, head) mean and M2 over dv, centred AV.
   if (r0 >= iend) return;
-  float sum = 0.f;
-#pragma unroll
-  for (int n = 0; n < DV / 32; ++n)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      o[n][r] *= inv_n;
-      sum += o[n][r];
-    }
-  sum += __shfl_xor(sum, 32, kWave);
-  const float mean = sum / (float)DV;
-  float m2 = 0.f;
-#pragma unroll
-  for (int n = 0; n < DV / 32; ++n)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float dlt = o[n][r] - mean;
-      m2 += dlt * dlt;
-    }
-  m2 += __shfl_xor(m2, 32, kWave);
-  if (!qvalid) return;
-  const int64_t row = s0 + iq;
-  T* dst = reinterpret_cast<T*>(a.av) + row * (int64_t)(H * DV) + h * DV;
-#pragma unroll
-  for (int n = 0; n < DV / 32; ++n)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      // rows 8g + 4*half + 0..3 of this 32-wide dv tile are consecutive
-      T* p = dst + n * 32 + 8 * g + 4 * half;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) p[e] = from_f32<T>(o[n][4 * g + e] - mean);
-    }
-  if (half == 0) {
-    a.stats[(row * H + h) * 2] = mean;
-    a.stats[(row * H + h) * 2 + 1] = m2;
-  }
+  attn_store<T, DV>(o, inv_n, qvalid, s0 + iq, h, H, a.av, a.stats, half);
 }
 
 template <typename T, int DQK, int DV>

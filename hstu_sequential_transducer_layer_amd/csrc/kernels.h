@@ -61,7 +61,7 @@ hipError_t launch_ln_in(hstu_dtype dt, const void* x, const void* g, const void*
 // Attention preparation: the work list (one workgroup), then the per-key-block
 // time-stamp summary (tstat, rel) that the attention kernel reads per block.
 hipError_t launch_attn_prep(const int64_t* off, const int32_t* ncand, int32_t B, int64_t T,
-                            const int64_t* ts, const AttnScratch& sc, hipStream_t s);
+                            const int64_t* ts, int bm, const AttnScratch& sc, hipStream_t s);
 
 // --- proj.hip: u|v|q|k = SiLU(xn W1^T + b1), scattered to the stage layouts.
 hipError_t launch_proj(const hstu_desc& d, const void* xn, int64_t T, const void* w1,

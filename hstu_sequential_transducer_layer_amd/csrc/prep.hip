@@ -69,16 +69,16 @@ constexpr int kTileThreads = 1024;
 
 // Keys a query tile touches: the history keys up to its last row, plus one
 // key block for the candidates' own diagonal.
-__device__ __forceinline__ int tile_cost_bucket(const SeqInfo& si, int qt) {
-  int i0 = qt * kAttnBM;
-  int iend = min(i0 + kAttnBM, si.len);
+__device__ __forceinline__ int tile_cost_bucket(const SeqInfo& si, int qt, int bm) {
+  int i0 = qt * bm;
+  int iend = min(i0 + bm, si.len);
   int cost = min(iend, si.nhist) + (iend > si.nhist ? kAttnBN : 0);
   return min(kCostBuckets - 1, cost >> 4);
 }
 
 __global__ __launch_bounds__(kTileThreads) void build_tiles_kernel(const int64_t* __restrict__ off,
                                                                    const int32_t* __restrict__ ncand,
-                                                                   int32_t B, int64_t T,
+                                                                   int32_t B, int64_t T, int bm,
                                                                    int64_t max_tiles,
                                                                    int2* __restrict__ tiles,
                                                                    int64_t max_kblocks,
@@ -93,8 +93,8 @@ __global__ __launch_bounds__(kTileThreads) void build_tiles_kernel(const int64_t
   __syncthreads();
   for (int b = tid; b < B; b += kTileThreads) {
     SeqInfo si = seq_info(off, ncand, b, T);
-    int nt = (si.len + kAttnBM - 1) / kAttnBM;
-    for (int qt = 0; qt < nt; ++qt) atomicAdd(&hist[tile_cost_bucket(si, qt)], 1);
+    int nt = (si.len + bm - 1) / bm;
+    for (int qt = 0; qt < nt; ++qt) atomicAdd(&hist[tile_cost_bucket(si, qt, bm)], 1);
   }
   __syncthreads();
   // Exclusive scan in decreasing-cost order: start[k] = sum of hist[k'] for k' > k.
@@ -117,9 +117,9 @@ __global__ __launch_bounds__(kTileThreads) void build_tiles_kernel(const int64_t
   __syncthreads();
   for (int b = tid; b < B; b += kTileThreads) {
     SeqInfo si = seq_info(off, ncand, b, T);
-    int nt = (si.len + kAttnBM - 1) / kAttnBM;
+    int nt = (si.len + bm - 1) / bm;
     for (int qt = 0; qt < nt; ++qt) {
-      int pos = atomicAdd(&hist[tile_cost_bucket(si, qt)], 1);
+      int pos = atomicAdd(&hist[tile_cost_bucket(si, qt, bm)], 1);
       if (pos < max_tiles) tiles[pos] = make_int2(b, qt);
     }
     const int nb = (si.len + kAttnBN - 1) / kAttnBN;
@@ -167,9 +167,9 @@ __global__ __launch_bounds__(256) void block_ts_kernel(const int64_t* __restrict
 }
 
 hipError_t launch_attn_prep(const int64_t* off, const int32_t* ncand, int32_t B, int64_t T,
-                            const int64_t* ts, const AttnScratch& sc, hipStream_t s) {
+                            const int64_t* ts, int bm, const AttnScratch& sc, hipStream_t s) {
   const int64_t max_kb = attn_max_kblocks(T, B);
-  hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(kTileThreads), 0, s, off, ncand, B, T,
+  hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(kTileThreads), 0, s, off, ncand, B, T, bm,
                      attn_max_tiles(T, B), sc.tiles, max_kb, sc.kblocks, sc.counts);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
