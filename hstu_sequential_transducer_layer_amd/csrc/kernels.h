@@ -22,6 +22,7 @@ inline int64_t attn_max_kblocks(int64_t T, int32_t B) { return (T + kAttnBN - 1)
 //   tiles   int2 {b, q-tile}, work list ordered by decreasing cost
 //   kblocks int2 {b, key block}, every key block once, any order
 //   counts  int32 [2]: number of tiles, number of key blocks
+//   tbase, kbase  int32 [B + 1]: first tile / key block of each sequence
 //   rel     int32 [T + kAttnBN]: ts[row] - (earliest timestamp of its key block)
 //   tstat   int64 [T][2]: at each key block's first row, the block's
 //           earliest and latest timestamps (other rows unused)
@@ -29,6 +30,8 @@ struct AttnScratch {
   int2* tiles;
   int2* kblocks;
   int32_t* counts;
+  int32_t* tbase;
+  int32_t* kbase;
   int32_t* rel;
   int64_t* tstat;
 };
@@ -37,7 +40,8 @@ inline size_t attn_align(size_t n) { return (n + 255) & ~(size_t)255; }
 
 inline size_t attn_scratch_bytes(int64_t T, int32_t B) {
   return attn_align((size_t)attn_max_tiles(T, B) * 8) + attn_align((size_t)attn_max_kblocks(T, B) * 8) +
-         attn_align(2 * sizeof(int32_t)) + attn_align((size_t)(T + kAttnBN) * 4) + attn_align((size_t)T * 16);
+         attn_align(2 * sizeof(int32_t)) + 2 * attn_align(((size_t)B + 1) * 4) +
+         attn_align((size_t)(T + kAttnBN) * 4) + attn_align((size_t)T * 16);
 }
 
 inline AttnScratch attn_scratch(void* base, int64_t T, int32_t B) {
@@ -49,6 +53,10 @@ inline AttnScratch attn_scratch(void* base, int64_t T, int32_t B) {
   p += attn_align((size_t)attn_max_kblocks(T, B) * 8);
   a.counts = (int32_t*)p;
   p += attn_align(2 * sizeof(int32_t));
+  a.tbase = (int32_t*)p;
+  p += attn_align(((size_t)B + 1) * 4);
+  a.kbase = (int32_t*)p;
+  p += attn_align(((size_t)B + 1) * 4);
   a.rel = (int32_t*)p;
   p += attn_align((size_t)(T + kAttnBN) * 4);
   a.tstat = (int64_t*)p;

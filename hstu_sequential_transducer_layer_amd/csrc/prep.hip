@@ -1,7 +1,7 @@
 // Preparation kernels:
 //  * ln_in: the LayerNorm applied to x before f1 (page "4.4 Scaling
 //    Recommendation Models", section "Code": norm_in ahead of f1), one wave per
-//    row, fp32 statistics, biased variance.
+//    row held in registers, fp32 statistics, biased variance.
 //  * build_tiles: the attention work list for jagged batches — one item per
 //    (sequence, 128-row query tile), ordered by decreasing work so the longest
 //    items start first (the pages' "sparsity-aware kernels for variable-length
@@ -15,7 +15,10 @@
 
 namespace hstu {
 
-template <typename T>
+// The row stays in registers between the statistics and the output: NC
+// 16-byte chunks per lane cover rows of up to NC * 64 * V elements, so x is
+// read from HBM once.
+template <typename T, int NC>
 __global__ __launch_bounds__(256) void ln_in_kernel(const T* __restrict__ x, const T* __restrict__ g,
                                                     const T* __restrict__ b, T* __restrict__ y,
                                                     int64_t rows, int d, float eps) {
@@ -25,42 +28,70 @@ __global__ __launch_bounds__(256) void ln_in_kernel(const T* __restrict__ x, con
   if (row >= rows) return;  // whole wave leaves together
   const T* xr = x + row * d;
   T* yr = y + row * d;
+  uint4 xv[NC];
   float f[V], gg[V], bb[V];
   float s = 0.f;
-  for (int c = lane * V; c < d; c += kWave * V) {
-    unpack(ld16(xr + c), f, T());
 #pragma unroll
-    for (int e = 0; e < V; ++e) s += f[e];
+  for (int k = 0; k < NC; ++k) {
+    const int c = (k * kWave + lane) * V;
+    if (c < d) {
+      xv[k] = ld16(xr + c);
+      unpack(xv[k], f, T());
+#pragma unroll
+      for (int e = 0; e < V; ++e) s += f[e];
+    }
   }
   const float mean = wave_sum(s) / (float)d;
   float q = 0.f;
-  for (int c = lane * V; c < d; c += kWave * V) {
-    unpack(ld16(xr + c), f, T());
 #pragma unroll
-    for (int e = 0; e < V; ++e) q += (f[e] - mean) * (f[e] - mean);
+  for (int k = 0; k < NC; ++k) {
+    if ((k * kWave + lane) * V < d) {
+      unpack(xv[k], f, T());
+#pragma unroll
+      for (int e = 0; e < V; ++e) q += (f[e] - mean) * (f[e] - mean);
+    }
   }
   const float rstd = rsqrtf(wave_sum(q) / (float)d + eps);
-  for (int c = lane * V; c < d; c += kWave * V) {
-    unpack(ld16(xr + c), f, T());
-    unpack(ld16(g + c), gg, T());
-    unpack(ld16(b + c), bb, T());
 #pragma unroll
-    for (int e = 0; e < V; ++e) f[e] = (f[e] - mean) * rstd * gg[e] + bb[e];
-    st16(yr + c, pack(f, T()));
+  for (int k = 0; k < NC; ++k) {
+    const int c = (k * kWave + lane) * V;
+    if (c < d) {
+      unpack(xv[k], f, T());
+      unpack(ld16(g + c), gg, T());
+      unpack(ld16(b + c), bb, T());
+#pragma unroll
+      for (int e = 0; e < V; ++e) f[e] = (f[e] - mean) * rstd * gg[e] + bb[e];
+      st16(yr + c, pack(f, T()));
+    }
   }
+}
+
+template <typename T>
+static hipError_t launch_ln_in_t(const void* x, const void* g, const void* b, void* y, int64_t T_,
+                                 int d, float eps, hipStream_t s) {
+  const dim3 grid((unsigned)((T_ + 3) / 4)), block(256);
+  const int per_lane = (d / Elem<T>::kVec + kWave - 1) / kWave;  // chunks per lane
+#define HSTU_LN_CASE(NC)                                                                           \
+  if (per_lane <= NC) {                                                                            \
+    hipLaunchKernelGGL((ln_in_kernel<T, NC>), grid, block, 0, s, (const T*)x, (const T*)g, (const T*)b, \
+                       (T*)y, T_, d, eps);                                                         \
+    return hipGetLastError();                                                                      \
+  }
+  HSTU_LN_CASE(1)
+  HSTU_LN_CASE(2)
+  HSTU_LN_CASE(4)
+  HSTU_LN_CASE(8)
+  HSTU_LN_CASE(16)
+  HSTU_LN_CASE(32)
+#undef HSTU_LN_CASE
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_ln_in(hstu_dtype dt, const void* x, const void* g, const void* b, void* y,
                         int64_t T, int d, float eps, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  dim3 grid((unsigned)((T + 3) / 4)), block(256);
-  if (dt == HSTU_BF16)
-    hipLaunchKernelGGL(ln_in_kernel<bf16>, grid, block, 0, s, (const bf16*)x, (const bf16*)g,
-                       (const bf16*)b, (bf16*)y, T, d, eps);
-  else
-    hipLaunchKernelGGL(ln_in_kernel<float>, grid, block, 0, s, (const float*)x, (const float*)g,
-                       (const float*)b, (float*)y, T, d, eps);
-  return hipGetLastError();
+  if (dt == HSTU_BF16) return launch_ln_in_t<bf16>(x, g, b, y, T, d, eps, s);
+  return launch_ln_in_t<float>(x, g, b, y, T, d, eps, s);
 }
 
 // ------------------------------------------------------------ work list
@@ -76,6 +107,41 @@ __device__ __forceinline__ int tile_cost_bucket(const SeqInfo& si, int qt, int b
   return min(kCostBuckets - 1, cost >> 4);
 }
 
+// Exclusive prefix sum of v over the workgroup's kTileThreads threads; the
+// sum of all v goes to total.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* part, int& total) {
+  const int tid = threadIdx.x;
+  part[tid] = v;
+  __syncthreads();
+  for (int o = 1; o < kTileThreads; o <<= 1) {
+    const int u = tid >= o ? part[tid - o] : 0;
+    __syncthreads();
+    part[tid] += u;
+    __syncthreads();
+  }
+  const int incl = part[tid];
+  total = part[kTileThreads - 1];
+  __syncthreads();
+  return incl - v;
+}
+
+// Largest b in [0, B) with base[b] <= g: the sequence whose items
+// [base[b], base[b + 1]) hold item g (empty sequences are skipped).
+__device__ __forceinline__ int owner(const int32_t* base, int B, int g) {
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (base[mid] <= g)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  return lo;
+}
+
+// One workgroup.  Items are spread over the threads through per-sequence
+// prefix sums (tbase, kbase: first tile / key block of each sequence), so the
+// work does not serialise on a few long sequences.
 __global__ __launch_bounds__(kTileThreads) void build_tiles_kernel(const int64_t* __restrict__ off,
                                                                    const int32_t* __restrict__ ncand,
                                                                    int32_t B, int64_t T, int bm,
@@ -83,54 +149,64 @@ __global__ __launch_bounds__(kTileThreads) void build_tiles_kernel(const int64_t
                                                                    int2* __restrict__ tiles,
                                                                    int64_t max_kblocks,
                                                                    int2* __restrict__ kblocks,
+                                                                   int32_t* __restrict__ tbase,
+                                                                   int32_t* __restrict__ kbase,
                                                                    int32_t* __restrict__ count) {
   __shared__ int hist[kCostBuckets];
   __shared__ int part[kTileThreads];
-  __shared__ int nkb;
   const int tid = threadIdx.x;
   for (int i = tid; i < kCostBuckets; i += kTileThreads) hist[i] = 0;
-  if (tid == 0) nkb = 0;
+
+  // Per-sequence item counts -> exclusive bases.
+  int run_t = 0, run_k = 0;
+  for (int b0 = 0; b0 < B; b0 += kTileThreads) {
+    const int b = b0 + tid;
+    int nt = 0, nk = 0;
+    if (b < B) {
+      const SeqInfo si = seq_info(off, ncand, b, T);
+      nt = (si.len + bm - 1) / bm;
+      nk = (si.len + kAttnBN - 1) / kAttnBN;
+    }
+    int tot_t, tot_k;
+    const int et = block_exclusive_scan(nt, part, tot_t);
+    const int ek = block_exclusive_scan(nk, part, tot_k);
+    if (b < B) {
+      tbase[b] = run_t + et;
+      kbase[b] = run_k + ek;
+    }
+    run_t += tot_t;
+    run_k += tot_k;
+  }
+  const int total = (int)min((int64_t)run_t, max_tiles), total_k = (int)min((int64_t)run_k, max_kblocks);
   __syncthreads();
-  for (int b = tid; b < B; b += kTileThreads) {
-    SeqInfo si = seq_info(off, ncand, b, T);
-    int nt = (si.len + bm - 1) / bm;
-    for (int qt = 0; qt < nt; ++qt) atomicAdd(&hist[tile_cost_bucket(si, qt, bm)], 1);
+
+  // Histogram of tile costs; the key-block list in sequence order.
+  for (int g = tid; g < total; g += kTileThreads) {
+    const int b = owner(tbase, B, g);
+    atomicAdd(&hist[tile_cost_bucket(seq_info(off, ncand, b, T), g - tbase[b], bm)], 1);
+  }
+  for (int g = tid; g < total_k; g += kTileThreads) {
+    const int b = owner(kbase, B, g);
+    kblocks[g] = make_int2(b, g - kbase[b]);
   }
   __syncthreads();
   // Exclusive scan in decreasing-cost order: start[k] = sum of hist[k'] for k' > k.
   // Thread t owns the two buckets 2047-2t and 2046-2t.
   const int hi = kCostBuckets - 1 - 2 * tid, lo = hi - 1;
   const int h_hi = hist[hi], h_lo = hist[lo];
-  part[tid] = h_hi + h_lo;
-  __syncthreads();
-  for (int o = 1; o < kTileThreads; o <<= 1) {
-    int v = tid >= o ? part[tid - o] : 0;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
-  }
-  const int before = part[tid] - (h_hi + h_lo);
-  const int total = part[kTileThreads - 1];
-  __syncthreads();
+  int dummy;
+  const int before = block_exclusive_scan(h_hi + h_lo, part, dummy);
   hist[hi] = before;
   hist[lo] = before + h_hi;
   __syncthreads();
-  for (int b = tid; b < B; b += kTileThreads) {
-    SeqInfo si = seq_info(off, ncand, b, T);
-    int nt = (si.len + bm - 1) / bm;
-    for (int qt = 0; qt < nt; ++qt) {
-      int pos = atomicAdd(&hist[tile_cost_bucket(si, qt, bm)], 1);
-      if (pos < max_tiles) tiles[pos] = make_int2(b, qt);
-    }
-    const int nb = (si.len + kAttnBN - 1) / kAttnBN;
-    const int kpos = nb > 0 ? atomicAdd(&nkb, nb) : 0;
-    for (int kb = 0; kb < nb; ++kb)
-      if (kpos + kb < max_kblocks) kblocks[kpos + kb] = make_int2(b, kb);
+  for (int g = tid; g < total; g += kTileThreads) {
+    const int b = owner(tbase, B, g), qt = g - tbase[b];
+    const int pos = atomicAdd(&hist[tile_cost_bucket(seq_info(off, ncand, b, T), qt, bm)], 1);
+    tiles[pos] = make_int2(b, qt);
   }
-  __syncthreads();
   if (tid == 0) {
-    count[0] = (int32_t)min((int64_t)total, max_tiles);
-    count[1] = (int32_t)min((int64_t)nkb, max_kblocks);
+    count[0] = total;
+    count[1] = total_k;
   }
 }
 
@@ -170,7 +246,7 @@ hipError_t launch_attn_prep(const int64_t* off, const int32_t* ncand, int32_t B,
                             const int64_t* ts, int bm, const AttnScratch& sc, hipStream_t s) {
   const int64_t max_kb = attn_max_kblocks(T, B);
   hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(kTileThreads), 0, s, off, ncand, B, T, bm,
-                     attn_max_tiles(T, B), sc.tiles, max_kb, sc.kblocks, sc.counts);
+                     attn_max_tiles(T, B), sc.tiles, max_kb, sc.kblocks, sc.tbase, sc.kbase, sc.counts);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(block_ts_kernel, dim3((unsigned)((max_kb + 3) / 4)), dim3(256), 0, s, off, ncand, T, ts,

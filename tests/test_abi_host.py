@@ -53,8 +53,9 @@ def test_workspace_size_matches_layout(lib):
     a = lambda n: (n + 255) // 256 * 256
     tiles = (T + 127) // 128 + B
     kblocks = (T + 63) // 64 + B
-    # work list, key-block list, two counters, per-row offsets (+64 pad), per-row stats pair
-    attn = a(tiles * 8) + a(kblocks * 8) + a(8) + a((T + 64) * 4) + a(T * 16)
+    # work list, key-block list, two counters, per-sequence tile / key-block bases,
+    # per-row offsets (+64 pad), per-row stats pair
+    attn = a(tiles * 8) + a(kblocks * 8) + a(8) + 2 * a((B + 1) * 4) + a((T + 64) * 4) + a(T * 16)
     want = (a(T * dm * e) + a(T * H * dv * e) * 3 + a(T * H * dq * e) * 2 + a(T * H * 8)
             + attn)
     assert _lib.workspace_size(d, T, B) == want
