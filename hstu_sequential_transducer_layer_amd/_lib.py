@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libhstu.so")
 HSTU_OK, HSTU_ERR_INVALID_ARG, HSTU_ERR_UNSUPPORTED, HSTU_ERR_WORKSPACE, HSTU_ERR_DEVICE = range(5)
 HSTU_F32, HSTU_BF16 = 0, 1
 HSTU_INPUT_NORM, HSTU_RESIDUAL, HSTU_CAND_SHARED_POS, HSTU_VALIDATE = 1, 2, 4, 8
+HSTU_REUSE_PLAN = 1 << 4
 
 EXPORTS = [
     "hstu_workspace_size", "hstu_layer_fwd", "hstu_proj_workspace_size", "hstu_proj_fwd",
@@ -204,11 +205,16 @@ def proj_fwd(desc: HstuDesc, x: torch.Tensor, prm: Dict[str, torch.Tensor],
     return acts
 
 
-def attn_fwd(desc: HstuDesc, seq_offsets, timestamps, num_candidates, prm, acts):
+def attn_workspace_size(desc: HstuDesc, T: int, B: int) -> int:
+    return int(load().hstu_attn_workspace_size(ctypes.byref(desc), T, B))
+
+
+def attn_fwd(desc: HstuDesc, seq_offsets, timestamps, num_candidates, prm, acts, workspace=None):
     lib = load()
     T, B = acts["u"].shape[0], seq_offsets.shape[0] - 1
-    need = int(lib.hstu_attn_workspace_size(ctypes.byref(desc), T, B))
-    ws = alloc_workspace(need, acts["u"].device)
+    need = attn_workspace_size(desc, T, B)
+    ws = workspace if workspace is not None and workspace.numel() >= need else \
+        alloc_workspace(need, acts["u"].device)
     a, t = _acts(acts), make_tables(prm)
     _check(lib.hstu_attn_fwd(ctypes.byref(desc), _ptr(seq_offsets), B, T, _ptr(timestamps),
                              _ptr(num_candidates), ctypes.byref(t), ctypes.byref(a), _ptr(ws),

@@ -40,7 +40,8 @@ hstu_status check_desc(const hstu_desc* d) {
   if (!d) return fail(HSTU_ERR_INVALID_ARG, "desc is NULL");
   if (d->dtype != HSTU_F32 && d->dtype != HSTU_BF16)
     return fail(HSTU_ERR_UNSUPPORTED, "unknown dtype %d", (int)d->dtype);
-  if (d->flags & ~(uint32_t)(HSTU_INPUT_NORM | HSTU_RESIDUAL | HSTU_CAND_SHARED_POS | HSTU_VALIDATE))
+  if (d->flags & ~(uint32_t)(HSTU_INPUT_NORM | HSTU_RESIDUAL | HSTU_CAND_SHARED_POS | HSTU_VALIDATE |
+                             HSTU_REUSE_PLAN))
     return fail(HSTU_ERR_INVALID_ARG, "unknown flag bits 0x%x", d->flags);
   if (d->d_model < 32 || d->d_model > 8192 || d->d_model % 32 != 0)
     return fail(HSTU_ERR_UNSUPPORTED, "d_model %d: must be a multiple of 32 in [32, 8192]", d->d_model);
@@ -243,9 +244,11 @@ static hstu_status run_attn(const hstu_desc* d, const int64_t* off, int32_t B, i
                             const int64_t* ts, const int32_t* nc, const hstu_bias_tables* t,
                             const hstu_activations* a, void* scratch, hipStream_t s) {
   const hstu::AttnScratch sc = hstu::attn_scratch(scratch, T, B);
-  hstu_status st = device(hstu::launch_attn_prep(off, nc, B, T, ts, hstu::kAttnBM, sc, s),
-                          "attention prep launch");
-  if (st != HSTU_OK) return st;
+  if (!(d->flags & HSTU_REUSE_PLAN)) {
+    const hstu_status st = device(hstu::launch_attn_prep(off, nc, B, T, ts, hstu::kAttnBM, sc, s),
+                                  "attention prep launch");
+    if (st != HSTU_OK) return st;
+  }
   return device(hstu::launch_attn(*d, off, nc, B, T, ts, *t, a->q, a->k, a->v, a->av, a->av_stats, sc, s),
                 "attention launch");
 }

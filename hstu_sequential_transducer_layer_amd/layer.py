@@ -2,7 +2,9 @@
 run one layer or a stack of layers through hstu_layer_fwd.
 
 The stack is a plain loop over hstu_layer_fwd calls (each layer's output is
-the next layer's input, residual inside the layer), sharing one workspace.
+the next layer's input, residual inside the layer), sharing one workspace;
+layers after the first pass HSTU_REUSE_PLAN, since the attention plan depends
+only on the batch metadata.
 """
 
 from __future__ import annotations
@@ -36,6 +38,8 @@ class HSTUStack:
 
     def __init__(self, dims, layers: List[Dict[str, torch.Tensor]], flags_extra: int = 0):
         self.desc = _lib.make_desc(dims, flags_extra)
+        # every layer after the first reuses the first layer's attention plan
+        self.desc_reuse = _lib.make_desc(dims, flags_extra | _lib.HSTU_REUSE_PLAN)
         self.layers = layers
         self._weights = [_lib.make_weights(p) for p in layers]
         self._tables = [_lib.make_tables(p) for p in layers]
@@ -57,7 +61,8 @@ class HSTUStack:
         for n, prm in enumerate(self.layers):
             last = n == len(self.layers) - 1
             dst = out if (last and out is not None) else self._bufs[n % 2]
-            _lib.layer_fwd(self.desc, h, offsets, timestamps, num_candidates, prm, out=dst,
-                           workspace=ws, weights=self._weights[n], tables=self._tables[n])
+            _lib.layer_fwd(self.desc if n == 0 else self.desc_reuse, h, offsets, timestamps,
+                           num_candidates, prm, out=dst, workspace=ws, weights=self._weights[n],
+                           tables=self._tables[n])
             h = dst
         return h

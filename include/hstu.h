@@ -82,8 +82,17 @@ enum {
   HSTU_INPUT_NORM = 1u << 0,      /* LayerNorm on x before f1 ([SRM] "Code")        */
   HSTU_RESIDUAL = 1u << 1,        /* Y += x ([SRM] "Code")                           */
   HSTU_CAND_SHARED_POS = 1u << 2, /* candidates all take position n_b (M-FALCON)     */
-  HSTU_VALIDATE = 1u << 3         /* copy metadata to the host, check, synchronise   */
+  HSTU_VALIDATE = 1u << 3,        /* copy metadata to the host, check, synchronise   */
+  HSTU_REUSE_PLAN = 1u << 4       /* attention plan already in the workspace (below) */
 };
+
+/* HSTU_REUSE_PLAN: the attention work list and the per-key-block timestamp
+ * summary in the workspace depend only on seq_offsets, num_candidates,
+ * timestamps, batch and total_tokens.  With this flag hstu_layer_fwd and
+ * hstu_attn_fwd skip rebuilding them: the caller asserts that an earlier call
+ * enqueued on the same stream, with the same workspace and the same metadata,
+ * built them (e.g. every layer after the first of a stack).  With other
+ * metadata the results are wrong but every access stays in bounds.          */
 
 typedef struct {
   int32_t d_model;       /* model width d; multiple of 32, 32..8192            */

@@ -323,6 +323,36 @@ def test_deterministic_bitwise():
     np.testing.assert_array_equal(_layer_y(w), _layer_y(w))
 
 
+def test_reused_plan_is_bitwise_identical():
+    """HSTU_REUSE_PLAN: a call that skips the attention plan gives the bits of a
+    call that builds it, when an earlier call on the same workspace built the
+    plan for the same metadata (here after an unrelated batch's plan was
+    overwritten by this batch's)."""
+    w = synth.make_workload("ranking_cand", batch=5, n_layers=2)
+    other = synth.make_workload("ranking_cand", seed=3, batch=7, n_layers=1)
+    dev, dev_o = layer.to_device(w), layer.to_device(other)
+    desc = _lib.make_desc(w.dims)
+    reuse = _lib.make_desc(w.dims, _lib.HSTU_REUSE_PLAN)
+    T, B = w.T, w.B
+    ws = _lib.alloc_workspace(max(_lib.workspace_size(desc, T, B),
+                                  _lib.workspace_size(desc, other.T, other.B)), "cuda")
+    args = (dev["offsets"], dev["timestamps"], dev["num_candidates"])
+    _lib.layer_fwd(desc, dev_o["x"], dev_o["offsets"], dev_o["timestamps"], dev_o["num_candidates"],
+                   dev_o["layers"][0], workspace=ws)
+    fresh = [_lib.layer_fwd(desc, dev["x"], *args, dev["layers"][n], workspace=ws).clone() for n in (0, 1)]
+    reused = _lib.layer_fwd(reuse, dev["x"], *args, dev["layers"][1], workspace=ws)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(reused.float().cpu().numpy(), fresh[1].float().cpu().numpy())
+    acts = _lib.proj_fwd(desc, dev["x"], dev["layers"][0])
+    a1 = {k: v.clone() for k, v in _lib.attn_fwd(desc, *args, dev["layers"][0], acts).items()}
+    ws_a = _lib.alloc_workspace(_lib.attn_workspace_size(desc, T, B), "cuda")
+    _lib.attn_fwd(desc, *args, dev["layers"][0], acts, workspace=ws_a)
+    _lib.attn_fwd(reuse, *args, dev["layers"][0], acts, workspace=ws_a)
+    torch.cuda.synchronize()
+    for k in ("av", "av_stats"):
+        np.testing.assert_array_equal(acts[k].float().cpu().numpy(), a1[k].float().cpu().numpy())
+
+
 def test_out_aliases_x():
     w = synth.make_workload("zipf_bf16", batch=6)
     dev = layer.to_device(w)
