@@ -114,6 +114,9 @@ def main():
     ap.add_argument("--attn-reps", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only copy a MIB-MiB device buffer 4 times (a plain copy kernel of "
+                         "known size, to scale profiler byte counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the HSTU layer "
@@ -124,6 +127,16 @@ def main():
 
     import torch
     from hstu_sequential_transducer_layer_amd import _lib, layer, synth
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "copies": 4}), flush=True)
+        return
 
     _lib.load()   # fails loudly if the HIP library is missing
     w = synth.make_workload(args.workload)
