@@ -25,7 +25,7 @@ HSTU_REUSE_PLAN = 1 << 4
 EXPORTS = [
     "hstu_workspace_size", "hstu_layer_fwd", "hstu_proj_workspace_size", "hstu_proj_fwd",
     "hstu_attn_workspace_size", "hstu_attn_fwd", "hstu_gate_fwd", "hstu_out_fwd",
-    "hstu_debug_indices",
+    "hstu_cand_workspace_size", "hstu_cand_fwd", "hstu_debug_indices",
     "hstu_status_str", "hstu_last_error",
 ]
 
@@ -89,9 +89,13 @@ def load() -> ctypes.CDLL:
     lib.hstu_out_fwd.argtypes = [P(HstuDesc), vp, i64, P(HstuWeights), P(HstuActivations),
                                  vp, vp, vp]
     lib.hstu_gate_fwd.argtypes = [P(HstuDesc), i64, P(HstuWeights), P(HstuActivations), vp, vp]
+    lib.hstu_cand_workspace_size.argtypes = [P(HstuDesc), i64, i64, i32]
+    lib.hstu_cand_workspace_size.restype = sz
+    lib.hstu_cand_fwd.argtypes = [P(HstuDesc), vp, vp, i32, i64, vp, vp, vp, i64, vp, vp, vp,
+                                  P(HstuWeights), P(HstuBiasTables), vp, vp, sz, vp]
     lib.hstu_debug_indices.argtypes = [P(HstuDesc), vp, i32, i64, vp, vp, vp, i64, vp, vp]
     for f in ("hstu_layer_fwd", "hstu_proj_fwd", "hstu_attn_fwd", "hstu_gate_fwd", "hstu_out_fwd",
-              "hstu_debug_indices"):
+              "hstu_cand_fwd", "hstu_debug_indices"):
         getattr(lib, f).restype = ctypes.c_int
     lib.hstu_status_str.argtypes = [ctypes.c_int]
     lib.hstu_status_str.restype = ctypes.c_char_p
@@ -245,6 +249,35 @@ def out_fwd(desc: HstuDesc, x, prm, acts, out=None, z=None):
     _check(lib.hstu_out_fwd(ctypes.byref(desc), _ptr(x), T, ctypes.byref(w), ctypes.byref(a),
                             _ptr(out), _ptr(z), _stream()))
     return out, z
+
+
+def cand_workspace_size(desc: HstuDesc, Tc: int, Th: int, B: int) -> int:
+    return int(load().hstu_cand_workspace_size(ctypes.byref(desc), Tc, Th, B))
+
+
+def cand_fwd(desc: HstuDesc, x_cand: torch.Tensor, cand_offsets: torch.Tensor,
+             cand_ts: torch.Tensor, num_candidates: torch.Tensor, hist_offsets: torch.Tensor,
+             hist_ts: torch.Tensor, hist_k: torch.Tensor, hist_v: torch.Tensor,
+             prm: Dict[str, torch.Tensor], out: Optional[torch.Tensor] = None,
+             workspace: Optional[torch.Tensor] = None, weights: Optional[HstuWeights] = None,
+             tables: Optional[HstuBiasTables] = None) -> torch.Tensor:
+    """hstu_cand_fwd on torch's current stream; returns `out` ([Tc, d])."""
+    lib = load()
+    Tc, B = x_cand.shape[0], cand_offsets.shape[0] - 1
+    Th = hist_ts.shape[0]
+    if out is None:
+        out = torch.empty_like(x_cand)
+    need = cand_workspace_size(desc, Tc, Th, B)
+    if workspace is None or workspace.numel() < need:
+        workspace = alloc_workspace(need, x_cand.device)
+    w = weights if weights is not None else make_weights(prm)
+    t = tables if tables is not None else make_tables(prm)
+    _check(lib.hstu_cand_fwd(ctypes.byref(desc), _ptr(x_cand), _ptr(cand_offsets), B, Tc,
+                             _ptr(cand_ts), _ptr(num_candidates), _ptr(hist_offsets), Th,
+                             _ptr(hist_ts), _ptr(hist_k), _ptr(hist_v), ctypes.byref(w),
+                             ctypes.byref(t), _ptr(out), _ptr(workspace), workspace.numel(),
+                             _stream()))
+    return out
 
 
 def debug_indices(desc: HstuDesc, seq_offsets, timestamps, num_candidates, pairs: torch.Tensor):

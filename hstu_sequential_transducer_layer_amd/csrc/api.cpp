@@ -139,7 +139,9 @@ struct Layout {
   size_t xn, u, v, q, k, av, stats, attn, total;
 };
 
-Layout layout(const hstu_desc* d, int64_t T, int32_t B) {
+// Tk: key rows of the attention pass (T in a layer pass, the cached history
+// rows in a candidate pass).
+Layout layout(const hstu_desc* d, int64_t T, int32_t B, int64_t Tk) {
   const size_t e = esize(d->dtype);
   const size_t H = d->num_heads, hdv = H * d->dv, hdq = H * d->dqk;
   Layout L{};
@@ -156,7 +158,7 @@ Layout layout(const hstu_desc* d, int64_t T, int32_t B) {
   L.k = take((size_t)T * hdq * e);
   L.av = take((size_t)T * hdv * e);
   L.stats = take((size_t)T * H * 2 * sizeof(float));
-  L.attn = take(hstu::attn_scratch_bytes(T, B));
+  L.attn = take(hstu::attn_scratch_bytes(T, Tk, B));
   L.total = o;
   return L;
 }
@@ -214,7 +216,7 @@ const char* hstu_last_error(void) { return g_err.c_str(); }
 
 size_t hstu_workspace_size(const hstu_desc* desc, int64_t T, int32_t B) {
   if (check_desc(desc) != HSTU_OK || check_sizes(T, B) != HSTU_OK) return 0;
-  return layout(desc, T, B).total;
+  return layout(desc, T, B, T).total;
 }
 
 size_t hstu_proj_workspace_size(const hstu_desc* desc, int64_t T) {
@@ -244,12 +246,12 @@ static hstu_status run_attn(const hstu_desc* d, const int64_t* off, int32_t B, i
                             const int64_t* ts, const int32_t* nc, const hstu_bias_tables* t,
                             const hstu_activations* a, void* scratch, hipStream_t s) {
   const hstu::AttnScratch sc = hstu::attn_scratch(scratch, T, B);
+  const hstu::AttnRows rows{off, nc, ts, T, off, ts, T, nullptr, B, false};
   if (!(d->flags & HSTU_REUSE_PLAN)) {
-    const hstu_status st = device(hstu::launch_attn_prep(off, nc, B, T, ts, hstu::kAttnBM, sc, s),
-                                  "attention prep launch");
+    const hstu_status st = device(hstu::launch_attn_prep(rows, hstu::kAttnBM, sc, s), "attention prep launch");
     if (st != HSTU_OK) return st;
   }
-  return device(hstu::launch_attn(*d, off, nc, B, T, ts, *t, a->q, a->k, a->v, a->av, a->av_stats, sc, s),
+  return device(hstu::launch_attn(*d, rows, *t, a->q, a->k, a->v, nullptr, nullptr, a->av, a->av_stats, sc, s),
                 "attention launch");
 }
 
@@ -339,7 +341,7 @@ hstu_status hstu_layer_fwd(const hstu_desc* desc, const void* x, const int64_t* 
   if ((st = check_proj_weights(desc, w)) != HSTU_OK) return st;
   if ((st = check_out_weights(desc, w)) != HSTU_OK) return st;
   if ((st = check_tables(desc, tables)) != HSTU_OK) return st;
-  const Layout L = layout(desc, T, B);
+  const Layout L = layout(desc, T, B, T);
   if (!ws || ws_bytes < L.total || !aligned(ws, 256))
     return fail(HSTU_ERR_WORKSPACE, "workspace: need %zu bytes (256-aligned), got %zu", L.total, ws_bytes);
   hipStream_t s = (hipStream_t)stream;
@@ -361,6 +363,69 @@ hstu_status hstu_layer_fwd(const hstu_desc* desc, const void* x, const int64_t* 
   if ((st = device(hstu::launch_gate(*desc, T, *w, a.u, a.av, a.av_stats, z, s), "gate launch")) != HSTU_OK)
     return st;
   if ((st = device(hstu::launch_f2(*desc, x, T, *w, z, out, s), "f2 launch")) != HSTU_OK) return st;
+  return ok();
+}
+
+size_t hstu_cand_workspace_size(const hstu_desc* desc, int64_t Tc, int64_t Th, int32_t B) {
+  if (check_desc(desc) != HSTU_OK || check_sizes(Tc, B) != HSTU_OK || check_sizes(Th, B) != HSTU_OK) return 0;
+  return layout(desc, Tc, B, Th).total;
+}
+
+hstu_status hstu_cand_fwd(const hstu_desc* desc, const void* x, const int64_t* coff, int32_t B, int64_t Tc,
+                          const int64_t* cts, const int32_t* mtotal, const int64_t* hoff, int64_t Th,
+                          const int64_t* hts, const void* hk, const void* hv, const hstu_weights* w,
+                          const hstu_bias_tables* tables, void* out, void* ws, size_t ws_bytes,
+                          hstu_stream_t stream) {
+  hstu_status st;
+  if ((st = check_desc(desc)) != HSTU_OK) return st;
+  if (!(desc->flags & HSTU_CAND_SHARED_POS))
+    return fail(HSTU_ERR_UNSUPPORTED, "the candidate pass needs HSTU_CAND_SHARED_POS");
+  if ((st = check_sizes(Tc, B)) != HSTU_OK) return st;
+  if ((st = check_sizes(Th, B)) != HSTU_OK) return st;
+  if (Tc == 0) return ok();
+  HSTU_REQ(x, 16, "x");
+  HSTU_REQ(out, 16, "out");
+  HSTU_REQ(mtotal, 4, "num_candidates");
+  if ((st = check_meta(coff, B, cts, nullptr)) != HSTU_OK) return st;
+  HSTU_REQ(hoff, 8, "hist_offsets");
+  if (Th > 0) {  // with no history rows the cache may be empty (NULL)
+    HSTU_REQ(hk, 16, "hist_k");
+    HSTU_REQ(hv, 16, "hist_v");
+    HSTU_REQ(hts, 8, "hist_ts");
+  }
+  if ((st = check_proj_weights(desc, w)) != HSTU_OK) return st;
+  if ((st = check_out_weights(desc, w)) != HSTU_OK) return st;
+  if ((st = check_tables(desc, tables)) != HSTU_OK) return st;
+  const Layout L = layout(desc, Tc, B, Th);
+  if (!ws || ws_bytes < L.total || !aligned(ws, 256))
+    return fail(HSTU_ERR_WORKSPACE, "workspace: need %zu bytes (256-aligned), got %zu", L.total, ws_bytes);
+  hipStream_t s = (hipStream_t)stream;
+  if (desc->flags & HSTU_VALIDATE) {
+    if ((st = validate_metadata(coff, B, Tc, nullptr, s)) != HSTU_OK) return st;
+    if ((st = validate_metadata(hoff, B, Th, nullptr, s)) != HSTU_OK) return st;
+  }
+  char* base = (char*)ws;
+  hstu_activations a;
+  a.u = base + L.u;
+  a.v = base + L.v;
+  a.q = base + L.q;
+  a.k = base + L.k;
+  a.av = base + L.av;
+  a.av_stats = (float*)(base + L.stats);
+  if ((st = run_proj(desc, x, Tc, w, &a, base + L.xn, s)) != HSTU_OK) return st;
+  const hstu::AttnScratch sc = hstu::attn_scratch(base + L.attn, Tc, Th, B);
+  const hstu::AttnRows rows{coff, nullptr, cts, Tc, hoff, hts, Th, mtotal, B, true};
+  if (!(desc->flags & HSTU_REUSE_PLAN))
+    if ((st = device(hstu::launch_attn_prep(rows, hstu::kAttnBM, sc, s), "attention prep launch")) != HSTU_OK)
+      return st;
+  if ((st = device(hstu::launch_attn(*desc, rows, *tables, a.q, hk, hv, a.k, a.v, a.av, a.av_stats, sc, s),
+                   "attention launch")) != HSTU_OK)
+    return st;
+  // Z takes the V region, dead once the attention (self terms included) has run.
+  void* z = base + L.v;
+  if ((st = device(hstu::launch_gate(*desc, Tc, *w, a.u, a.av, a.av_stats, z, s), "gate launch")) != HSTU_OK)
+    return st;
+  if ((st = device(hstu::launch_f2(*desc, x, Tc, *w, z, out, s), "f2 launch")) != HSTU_OK) return st;
   return ok();
 }
 

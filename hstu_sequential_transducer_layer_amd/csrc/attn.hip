@@ -61,21 +61,26 @@ __device__ __forceinline__ int v_swz(int r) {
 }
 
 struct AttnArgs {
-  const int64_t* off;
+  const int64_t* off;      // query rows of each sequence
   const int32_t* ncand;
-  const int64_t* ts;
+  const int64_t* ts;       // query rows' timestamps
+  const int64_t* koff;     // key rows of each sequence (= off unless cached)
+  const int64_t* kts;      // key rows' timestamps
+  const int32_t* mtotal;   // cached: each sequence's full candidate count
   const void* pos_tab;
   const void* time_tab;
   const void* q;
-  const void* k;
+  const void* k;           // key rows' K, V  [H, TK, d]
   const void* v;
+  const void* qk;          // cached: the query rows' own K, V [H, T, d]
+  const void* qv;
   void* av;
   float* stats;
   const int2* tiles;
   const int32_t* counts;   // [0]: work items
-  const int32_t* rel;      // per row: offset from its key block's earliest timestamp
+  const int32_t* rel;      // per key row: offset from its key block's earliest timestamp
   const int64_t* tstat;    // per key block's first row: earliest, latest timestamp
-  int64_t T;
+  int64_t T, TK;           // query rows, key rows
   int H, P, NB, sbits, pos_stride, time_stride, norm_len, shared_pos;
 };
 
@@ -292,7 +297,7 @@ struct QueryRow {
 
 // Per-(workgroup) constants of the classification.
 struct SeqCtx {
-  int L, nh, iend, R, NB, sbits;
+  int L, nh, R, NB, sbits;
   bool shared;
   float cpos_far;  // bias of every pair at relative distance >= R
   const float* pos_s;
@@ -300,11 +305,12 @@ struct SeqCtx {
   const int64_t* ts;  // the sequence's timestamps
 };
 
-// Whether any row of the wave attends a key of the block starting at j0.
+// Whether any row of the wave (which has rows) attends a key of the block
+// starting at j0.
 __device__ __forceinline__ bool block_active(int j0, const QueryRow& q, const SeqCtx& sq) {
   const bool any_hist = j0 < sq.nh && j0 <= q.rlast;
   const bool any_self = max(max(q.r0, sq.nh), j0) <= min(q.rlast, j0 + kAttnBN - 1);
-  return q.r0 < sq.iend && (any_hist || any_self);
+  return any_hist || any_self;
 }
 
 // Weight mode of one (wave, key block) — wave-uniform — and the per-lane
@@ -405,7 +411,10 @@ __device__ __forceinline__ void attn_store(f32x16 (&o)[DV / 32], float inv_n, bo
 // VGPRs per lane) when a q row plus a k row take at most 256 bytes, else two.
 constexpr int attn_min_blocks(int row_bytes) { return row_bytes <= 256 ? 3 : 2; }
 
-template <typename T, int DQK, int DV>
+// CACHED: the queries are candidates only, the keys a cached history of the
+// same sequences; every candidate attends the whole history and itself (the
+// self term is added in the epilogue), with the shared candidate position.
+template <typename T, int DQK, int DV, bool CACHED>
 __global__ __launch_bounds__(256, attn_min_blocks((DQK + DV) * (int)sizeof(T))) void attn_kernel(AttnArgs a) {
   typedef AttnCfg<T, DQK, DV> C;
   static_assert(C::NT == 256, "launch bounds assume 4 waves");
@@ -425,29 +434,33 @@ __global__ __launch_bounds__(256, attn_min_blocks((DQK + DV) * (int)sizeof(T))) 
   const int item = blockIdx.x / H;
   if (item >= a.counts[0]) return;
   const int2 tl = a.tiles[item];
-  const SeqInfo si = seq_info(a.off, a.ncand, tl.x, a.T);
-  const int L = si.len, nh = si.nhist;
-  const int64_t s0 = si.start;
+  const SeqInfo si = seq_info(a.off, a.ncand, tl.x, a.T);      // query rows
+  const SeqInfo ki = CACHED ? seq_info(a.koff, nullptr, tl.x, a.TK) : si;  // key rows
+  const int Lq = si.len;
+  const int L = ki.len, nh = CACHED ? ki.len : si.nhist;
+  const int64_t s0 = si.start, k0 = ki.start;
   const int i0 = tl.y * C::BM;
-  const int iend = min(i0 + C::BM, L);
-  const float inv_n = 1.0f / (float)(a.norm_len > 0 ? a.norm_len : L);
+  const int iend = min(i0 + C::BM, Lq);
+  const int N_b = CACHED ? L + max(a.mtotal[tl.x], Lq) : L;
+  const float inv_n = 1.0f / (float)(a.norm_len > 0 ? a.norm_len : N_b);
   const int R = (a.P - 1) / 2;
   const bool shared = a.shared_pos != 0;
 
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
   const int l32 = lane & 31, half = lane >> 5;
 
-  // Key blocks: history [0, min(iend, nh)), then the candidates' own rows.
-  const int a_end = min(iend, nh);
+  // Key blocks: history [0, min(iend, nh)), then the candidates' own rows; in a
+  // cached pass the whole history.
+  const int a_end = CACHED ? nh : min(iend, nh);
   const int nblk_a = (a_end + C::BN - 1) / C::BN;
   const int b_lo = max(i0, nh), b_hi = iend;
   const int jb0 = max(nblk_a * C::BN, (b_lo / C::BN) * C::BN);
-  const int nblk_b = (b_lo < b_hi && jb0 < b_hi) ? (b_hi - jb0 + C::BN - 1) / C::BN : 0;
+  const int nblk_b = (!CACHED && b_lo < b_hi && jb0 < b_hi) ? (b_hi - jb0 + C::BN - 1) / C::BN : 0;
   const int nblk = nblk_a + nblk_b;
   auto block_start = [&](int blk) __attribute__((always_inline)) { return blk < nblk_a ? blk * C::BN : jb0 + (blk - nblk_a) * C::BN; };
 
-  const T* kg = reinterpret_cast<const T*>(a.k) + ((int64_t)h * a.T + s0) * DQK;
-  const T* vg = reinterpret_cast<const T*>(a.v) + ((int64_t)h * a.T + s0) * DV;
+  const T* kg = reinterpret_cast<const T*>(a.k) + ((int64_t)h * a.TK + k0) * DQK;
+  const T* vg = reinterpret_cast<const T*>(a.v) + ((int64_t)h * a.TK + k0) * DV;
   TileCopy<T, DQK, C::NW, C::KCPR, true> kcopy;
   TileCopy<T, DV, C::NW, C::VCPR, false> vcopy;
   kcopy.init(w, lane);
@@ -457,13 +470,13 @@ __global__ __launch_bounds__(256, attn_min_blocks((DQK + DV) * (int)sizeof(T))) 
   // copies, so the wait that covers them covers it too).
   auto issue = [&](int blk, T* Kb, T* Vb, int32_t* rb, longlong2& tb) __attribute__((always_inline)) {
     const int j0 = block_start(blk);
-    tb = *reinterpret_cast<const longlong2*>(a.tstat + 2 * (s0 + j0));
+    tb = *reinterpret_cast<const longlong2*>(a.tstat + 2 * (k0 + j0));
     kcopy.issue(kg + (int64_t)j0 * DQK, L - j0, Kb, w);
     vcopy.issue(vg + (int64_t)j0 * DV, L - j0, Vb, w);
     // the offsets array has kAttnBN rows of padding past T, so this never
     // reads outside it; offsets of rows past the sequence are never used
     if (w == 0)
-      __builtin_amdgcn_global_load_lds((glb_void*)(a.rel + s0 + j0 + lane), (lds_void*)rb, 4, 0, 0);
+      __builtin_amdgcn_global_load_lds((glb_void*)(a.rel + k0 + j0 + lane), (lds_void*)rb, 4, 0, 0);
   };
 
   // Issue the first block's copies before anything else.
@@ -492,8 +505,11 @@ __global__ __launch_bounds__(256, attn_min_blocks((DQK + DV) * (int)sizeof(T))) 
     }
   }
   const int64_t ts_q = qvalid ? a.ts[s0 + iq] : 0;
-  const int p_q = position(iq, nh, shared);
-  const int pmin_q = position(r0, nh, shared);
+  // A cached pass places every candidate after the whole history at the
+  // shared position nh, and masks with row nh - 1 (all history, nothing past it).
+  const int p_q = CACHED ? nh : position(iq, nh, shared);
+  const int pmin_q = CACHED ? nh : position(r0, nh, shared);
+  const bool wave_rows = r0 < iend;
 
   f32x16 o[DV / 32];
 #pragma unroll
@@ -504,12 +520,13 @@ __global__ __launch_bounds__(256, attn_min_blocks((DQK + DV) * (int)sizeof(T))) 
   const float cpos_far = pos_s[2 * R];  // bias of every pair at distance >= R
 
   // One block of work out of buffer set (Kb, Vb, rb).
-  const QueryRow qr{r0, rlast, iq, p_q, pmin_q, qvalid, ts_q};
-  const SeqCtx sq{L, nh, iend, R, a.NB, a.sbits, shared, cpos_far, pos_s, time_s, a.ts + s0};
+  const QueryRow qr = CACHED ? QueryRow{nh - 1, nh - 1, nh - 1, p_q, pmin_q, qvalid, ts_q}
+                             : QueryRow{r0, rlast, iq, p_q, pmin_q, qvalid, ts_q};
+  const SeqCtx sq{L, nh, R, a.NB, a.sbits, shared, cpos_far, pos_s, time_s, a.kts + k0};
   auto consume = [&](int blk, const T* Kb, const T* Vb, const int32_t* rb, int64_t tmin, int64_t tmax)
                      __attribute__((always_inline)) {
     const int j0 = block_start(blk);
-    if (!block_active(j0, qr, sq)) return;
+    if (!wave_rows || !block_active(j0, qr, sq)) return;
     ElemCtx x;
     const int mode = classify_block(j0, tmin, tmax, qr, sq, rb, x);
     // Per 32-key half: S^T (K fragments straight from LDS), then this half's
@@ -561,21 +578,44 @@ __global__ __launch_bounds__(256, attn_min_blocks((DQK + DV) * (int)sizeof(T))) 
   }
 
   if (r0 >= iend) return;
+  if (CACHED && qvalid) {
+    // The candidate's own key: distance 0 (bucket R), time difference 0
+    // (bucket 0).  q.k over this lane's half of dqk, then across the halves.
+    const T* ks = reinterpret_cast<const T*>(a.qk) + ((int64_t)h * a.T + s0 + iq) * DQK;
+    float dot = 0.f;
+#pragma unroll
+    for (int c = 0; c < DQK / 16; ++c) {
+      const Frag kf = *reinterpret_cast<const Frag*>(ks + 16 * c + 8 * half);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dot += to_f32(qf[c][e]) * to_f32(kf[e]);
+    }
+    dot += __shfl_xor(dot, 32, kWave);
+    const float wself = silu(dot + pos_s[R] + time_s[0]);
+    const T* vs = reinterpret_cast<const T*>(a.qv) + ((int64_t)h * a.T + s0 + iq) * DV;
+#pragma unroll
+    for (int n = 0; n < DV / 32; ++n)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[n][r] += wself * to_f32(vs[32 * n + 8 * (r >> 2) + 4 * half + (r & 3)]);
+  }
   attn_store<T, DV>(o, inv_n, qvalid, s0 + iq, h, H, a.av, a.stats, half);
 }
 
 template <typename T, int DQK, int DV>
-static hipError_t launch_t(const AttnArgs& a, int64_t grid, hipStream_t s) {
+static hipError_t launch_t(const AttnArgs& a, bool cached, int64_t grid, hipStream_t s) {
   const size_t shmem = (size_t)(a.P + a.NB) * sizeof(float);
-  hipLaunchKernelGGL((attn_kernel<T, DQK, DV>), dim3((unsigned)grid), dim3(AttnCfg<T, DQK, DV>::NT),
-                     shmem, s, a);
+  if (cached)
+    hipLaunchKernelGGL((attn_kernel<T, DQK, DV, true>), dim3((unsigned)grid), dim3(AttnCfg<T, DQK, DV>::NT),
+                       shmem, s, a);
+  else
+    hipLaunchKernelGGL((attn_kernel<T, DQK, DV, false>), dim3((unsigned)grid), dim3(AttnCfg<T, DQK, DV>::NT),
+                       shmem, s, a);
   return hipGetLastError();
 }
 
 template <typename T>
-static hipError_t launch_dims(const AttnArgs& a, int dqk, int dv, int64_t grid, hipStream_t s) {
+static hipError_t launch_dims(const AttnArgs& a, bool cached, int dqk, int dv, int64_t grid, hipStream_t s) {
 #define HSTU_ATTN_CASE(Q, V_) \
-  if (dqk == Q && dv == V_) return launch_t<T, Q, V_>(a, grid, s);
+  if (dqk == Q && dv == V_) return launch_t<T, Q, V_>(a, cached, grid, s);
   HSTU_ATTN_CASE(32, 32)
   HSTU_ATTN_CASE(32, 64)
   HSTU_ATTN_CASE(32, 128)
@@ -590,35 +630,40 @@ static hipError_t launch_dims(const AttnArgs& a, int dqk, int dv, int64_t grid, 
 }
 
 // fp32 layers: head widths up to 64 (the API rejects wider ones for fp32).
-static hipError_t launch_dims_f32(const AttnArgs& a, int dqk, int dv, int64_t grid, hipStream_t s) {
-  if (dqk == 32 && dv == 32) return launch_t<float, 32, 32>(a, grid, s);
-  if (dqk == 32 && dv == 64) return launch_t<float, 32, 64>(a, grid, s);
-  if (dqk == 64 && dv == 32) return launch_t<float, 64, 32>(a, grid, s);
-  if (dqk == 64 && dv == 64) return launch_t<float, 64, 64>(a, grid, s);
+static hipError_t launch_dims_f32(const AttnArgs& a, bool cached, int dqk, int dv, int64_t grid, hipStream_t s) {
+  if (dqk == 32 && dv == 32) return launch_t<float, 32, 32>(a, cached, grid, s);
+  if (dqk == 32 && dv == 64) return launch_t<float, 32, 64>(a, cached, grid, s);
+  if (dqk == 64 && dv == 32) return launch_t<float, 64, 32>(a, cached, grid, s);
+  if (dqk == 64 && dv == 64) return launch_t<float, 64, 64>(a, cached, grid, s);
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_attn(const hstu_desc& d, const int64_t* off, const int32_t* ncand, int32_t B,
-                       int64_t T, const int64_t* ts, const hstu_bias_tables& tab, const void* q,
-                       const void* k, const void* v, void* av, float* stats, const AttnScratch& sc,
-                       hipStream_t s) {
-  if (T == 0) return hipSuccess;
+hipError_t launch_attn(const hstu_desc& d, const AttnRows& r, const hstu_bias_tables& tab, const void* q,
+                       const void* k, const void* v, const void* qk, const void* qv, void* av, float* stats,
+                       const AttnScratch& sc, hipStream_t s) {
+  if (r.Tq == 0) return hipSuccess;
   AttnArgs a;
-  a.off = off;
-  a.ncand = ncand;
-  a.ts = ts;
+  a.off = r.qoff;
+  a.ncand = r.ncand;
+  a.ts = r.qts;
+  a.koff = r.koff;
+  a.kts = r.kts;
+  a.mtotal = r.mtotal;
   a.pos_tab = tab.pos;
   a.time_tab = tab.time;
   a.q = q;
   a.k = k;
   a.v = v;
+  a.qk = qk;
+  a.qv = qv;
   a.av = av;
   a.stats = stats;
   a.tiles = sc.tiles;
   a.counts = sc.counts;
   a.rel = sc.rel;
   a.tstat = sc.tstat;
-  a.T = T;
+  a.T = r.Tq;
+  a.TK = r.Tk;
   a.H = d.num_heads;
   a.P = d.pos_buckets;
   a.NB = d.time_buckets;
@@ -627,9 +672,9 @@ hipError_t launch_attn(const hstu_desc& d, const int64_t* off, const int32_t* nc
   a.time_stride = tab.time_head_stride;
   a.norm_len = d.norm_len;
   a.shared_pos = (d.flags & HSTU_CAND_SHARED_POS) ? 1 : 0;
-  const int64_t grid = attn_max_tiles(T, B) * d.num_heads;
-  if (d.dtype == HSTU_BF16) return launch_dims<bf16>(a, d.dqk, d.dv, grid, s);
-  return launch_dims_f32(a, d.dqk, d.dv, grid, s);
+  const int64_t grid = attn_max_tiles(r.Tq, r.B) * d.num_heads;
+  if (d.dtype == HSTU_BF16) return launch_dims<bf16>(a, r.cached, d.dqk, d.dv, grid, s);
+  return launch_dims_f32(a, r.cached, d.dqk, d.dv, grid, s);
 }
 
 }  // namespace hstu

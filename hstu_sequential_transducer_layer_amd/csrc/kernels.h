@@ -18,13 +18,15 @@ inline int64_t attn_max_tiles(int64_t T, int32_t B) { return (T + kAttnBM - 1) /
 // Upper bound on key blocks (64 keys from a sequence's start) over all sequences.
 inline int64_t attn_max_kblocks(int64_t T, int32_t B) { return (T + kAttnBN - 1) / kAttnBN + B; }
 
-// Device scratch of the attention stage, carved from one caller buffer.
+// Device scratch of the attention stage, carved from one caller buffer.  Tq
+// counts query rows, Tk key rows (the same rows in a layer pass; the cached
+// history in a candidate pass).
 //   tiles   int2 {b, q-tile}, work list ordered by decreasing cost
 //   kblocks int2 {b, key block}, every key block once, any order
 //   counts  int32 [2]: number of tiles, number of key blocks
 //   tbase, kbase  int32 [B + 1]: first tile / key block of each sequence
-//   rel     int32 [T + kAttnBN]: ts[row] - (earliest timestamp of its key block)
-//   tstat   int64 [T][2]: at each key block's first row, the block's
+//   rel     int32 [Tk + kAttnBN]: ts[row] - (earliest timestamp of its key block)
+//   tstat   int64 [Tk][2]: at each key block's first row, the block's
 //           earliest and latest timestamps (other rows unused)
 struct AttnScratch {
   int2* tiles;
@@ -38,19 +40,20 @@ struct AttnScratch {
 
 inline size_t attn_align(size_t n) { return (n + 255) & ~(size_t)255; }
 
-inline size_t attn_scratch_bytes(int64_t T, int32_t B) {
-  return attn_align((size_t)attn_max_tiles(T, B) * 8) + attn_align((size_t)attn_max_kblocks(T, B) * 8) +
+inline size_t attn_scratch_bytes(int64_t Tq, int64_t Tk, int32_t B) {
+  return attn_align((size_t)attn_max_tiles(Tq, B) * 8) + attn_align((size_t)attn_max_kblocks(Tk, B) * 8) +
          attn_align(2 * sizeof(int32_t)) + 2 * attn_align(((size_t)B + 1) * 4) +
-         attn_align((size_t)(T + kAttnBN) * 4) + attn_align((size_t)T * 16);
+         attn_align((size_t)(Tk + kAttnBN) * 4) + attn_align((size_t)Tk * 16);
 }
+inline size_t attn_scratch_bytes(int64_t T, int32_t B) { return attn_scratch_bytes(T, T, B); }
 
-inline AttnScratch attn_scratch(void* base, int64_t T, int32_t B) {
+inline AttnScratch attn_scratch(void* base, int64_t Tq, int64_t Tk, int32_t B) {
   char* p = (char*)base;
   AttnScratch a;
   a.tiles = (int2*)p;
-  p += attn_align((size_t)attn_max_tiles(T, B) * 8);
+  p += attn_align((size_t)attn_max_tiles(Tq, B) * 8);
   a.kblocks = (int2*)p;
-  p += attn_align((size_t)attn_max_kblocks(T, B) * 8);
+  p += attn_align((size_t)attn_max_kblocks(Tk, B) * 8);
   a.counts = (int32_t*)p;
   p += attn_align(2 * sizeof(int32_t));
   a.tbase = (int32_t*)p;
@@ -58,28 +61,48 @@ inline AttnScratch attn_scratch(void* base, int64_t T, int32_t B) {
   a.kbase = (int32_t*)p;
   p += attn_align(((size_t)B + 1) * 4);
   a.rel = (int32_t*)p;
-  p += attn_align((size_t)(T + kAttnBN) * 4);
+  p += attn_align((size_t)(Tk + kAttnBN) * 4);
   a.tstat = (int64_t*)p;
   return a;
 }
+inline AttnScratch attn_scratch(void* base, int64_t T, int32_t B) { return attn_scratch(base, T, T, B); }
+
+// The rows an attention pass reads.  Query rows: sequence b is
+// [qoff[b], qoff[b + 1]) of the query-side tensors, its last ncand[b] rows
+// candidates.  Key rows: in a layer pass the same rows (koff = qoff, kts = the
+// query timestamps); in a cached candidate pass the queries are candidates
+// only and the keys are the history [koff[b], koff[b + 1]) of the cache,
+// mtotal[b] being the sequence's full candidate count (for N_b).
+struct AttnRows {
+  const int64_t* qoff;
+  const int32_t* ncand;
+  const int64_t* qts;
+  int64_t Tq;
+  const int64_t* koff;
+  const int64_t* kts;
+  int64_t Tk;
+  const int32_t* mtotal;  // cached pass only
+  int32_t B;
+  bool cached;
+};
 
 // --- prep.hip
 hipError_t launch_ln_in(hstu_dtype dt, const void* x, const void* g, const void* b, void* y,
                         int64_t T, int d, float eps, hipStream_t s);
 // Attention preparation: the work list (one workgroup), then the per-key-block
 // time-stamp summary (tstat, rel) that the attention kernel reads per block.
-hipError_t launch_attn_prep(const int64_t* off, const int32_t* ncand, int32_t B, int64_t T,
-                            const int64_t* ts, int bm, const AttnScratch& sc, hipStream_t s);
+hipError_t launch_attn_prep(const AttnRows& rows, int bm, const AttnScratch& sc, hipStream_t s);
 
 // --- proj.hip: u|v|q|k = SiLU(xn W1^T + b1), scattered to the stage layouts.
 hipError_t launch_proj(const hstu_desc& d, const void* xn, int64_t T, const void* w1,
                        const void* b1, void* u, void* v, void* q, void* k, hipStream_t s);
 
-// --- attn.hip
-hipError_t launch_attn(const hstu_desc& d, const int64_t* off, const int32_t* ncand, int32_t B,
-                       int64_t T, const int64_t* ts, const hstu_bias_tables& tab, const void* q,
-                       const void* k, const void* v, void* av, float* stats, const AttnScratch& sc,
-                       hipStream_t s);
+// --- attn.hip: av, stats of the query rows.  k, v: the key rows' tensors (in
+// a cached pass the history cache; q, qk, qv are then the candidates' own
+// tensors, qk / qv giving each candidate's self term).
+hipError_t launch_attn(const hstu_desc& d, const AttnRows& rows, const hstu_bias_tables& tab, const void* q,
+                       const void* k, const void* v, const void* qk, const void* qv, void* av, float* stats,
+                       const AttnScratch& sc, hipStream_t s);
 
 // --- out.hip: z = LN_av(av) * u, then out = z W2^T + b2 (+ x).
 hipError_t launch_gate(const hstu_desc& d, int64_t T, const hstu_weights& w, const void* u,

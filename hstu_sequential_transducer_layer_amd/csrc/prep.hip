@@ -99,11 +99,12 @@ constexpr int kCostBuckets = 2048;
 constexpr int kTileThreads = 1024;
 
 // Keys a query tile touches: the history keys up to its last row, plus one
-// key block for the candidates' own diagonal.
-__device__ __forceinline__ int tile_cost_bucket(const SeqInfo& si, int qt, int bm) {
+// key block for the candidates' own diagonal; in a cached pass (klen >= 0)
+// the whole cached history of the sequence.
+__device__ __forceinline__ int tile_cost_bucket(const SeqInfo& si, int qt, int bm, int klen) {
   int i0 = qt * bm;
   int iend = min(i0 + bm, si.len);
-  int cost = min(iend, si.nhist) + (iend > si.nhist ? kAttnBN : 0);
+  int cost = klen >= 0 ? klen : min(iend, si.nhist) + (iend > si.nhist ? kAttnBN : 0);
   return min(kCostBuckets - 1, cost >> 4);
 }
 
@@ -141,10 +142,14 @@ __device__ __forceinline__ int owner(const int32_t* base, int B, int g) {
 
 // One workgroup.  Items are spread over the threads through per-sequence
 // prefix sums (tbase, kbase: first tile / key block of each sequence), so the
-// work does not serialise on a few long sequences.
+// work does not serialise on a few long sequences.  Tiles cover the query
+// rows (off, ncand, T); key blocks cover the key rows (koff, Tk), which are
+// the same rows unless the pass reads a cached history.
 __global__ __launch_bounds__(kTileThreads) void build_tiles_kernel(const int64_t* __restrict__ off,
                                                                    const int32_t* __restrict__ ncand,
                                                                    int32_t B, int64_t T, int bm,
+                                                                   const int64_t* __restrict__ koff,
+                                                                   int64_t Tk, int cached,
                                                                    int64_t max_tiles,
                                                                    int2* __restrict__ tiles,
                                                                    int64_t max_kblocks,
@@ -156,6 +161,7 @@ __global__ __launch_bounds__(kTileThreads) void build_tiles_kernel(const int64_t
   __shared__ int part[kTileThreads];
   const int tid = threadIdx.x;
   for (int i = tid; i < kCostBuckets; i += kTileThreads) hist[i] = 0;
+  auto klen = [&](int b) { return cached ? seq_info(koff, nullptr, b, Tk).len : -1; };
 
   // Per-sequence item counts -> exclusive bases.
   int run_t = 0, run_k = 0;
@@ -165,7 +171,7 @@ __global__ __launch_bounds__(kTileThreads) void build_tiles_kernel(const int64_t
     if (b < B) {
       const SeqInfo si = seq_info(off, ncand, b, T);
       nt = (si.len + bm - 1) / bm;
-      nk = (si.len + kAttnBN - 1) / kAttnBN;
+      nk = ((cached ? klen(b) : si.len) + kAttnBN - 1) / kAttnBN;
     }
     int tot_t, tot_k;
     const int et = block_exclusive_scan(nt, part, tot_t);
@@ -183,7 +189,7 @@ __global__ __launch_bounds__(kTileThreads) void build_tiles_kernel(const int64_t
   // Histogram of tile costs; the key-block list in sequence order.
   for (int g = tid; g < total; g += kTileThreads) {
     const int b = owner(tbase, B, g);
-    atomicAdd(&hist[tile_cost_bucket(seq_info(off, ncand, b, T), g - tbase[b], bm)], 1);
+    atomicAdd(&hist[tile_cost_bucket(seq_info(off, ncand, b, T), g - tbase[b], bm, klen(b))], 1);
   }
   for (int g = tid; g < total_k; g += kTileThreads) {
     const int b = owner(kbase, B, g);
@@ -201,7 +207,7 @@ __global__ __launch_bounds__(kTileThreads) void build_tiles_kernel(const int64_t
   __syncthreads();
   for (int g = tid; g < total; g += kTileThreads) {
     const int b = owner(tbase, B, g), qt = g - tbase[b];
-    const int pos = atomicAdd(&hist[tile_cost_bucket(seq_info(off, ncand, b, T), qt, bm)], 1);
+    const int pos = atomicAdd(&hist[tile_cost_bucket(seq_info(off, ncand, b, T), qt, bm, klen(b))], 1);
     tiles[pos] = make_int2(b, qt);
   }
   if (tid == 0) {
@@ -242,15 +248,15 @@ __global__ __launch_bounds__(256) void block_ts_kernel(const int64_t* __restrict
   }
 }
 
-hipError_t launch_attn_prep(const int64_t* off, const int32_t* ncand, int32_t B, int64_t T,
-                            const int64_t* ts, int bm, const AttnScratch& sc, hipStream_t s) {
-  const int64_t max_kb = attn_max_kblocks(T, B);
-  hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(kTileThreads), 0, s, off, ncand, B, T, bm,
-                     attn_max_tiles(T, B), sc.tiles, max_kb, sc.kblocks, sc.tbase, sc.kbase, sc.counts);
+hipError_t launch_attn_prep(const AttnRows& r, int bm, const AttnScratch& sc, hipStream_t s) {
+  const int64_t max_kb = attn_max_kblocks(r.Tk, r.B);
+  hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(kTileThreads), 0, s, r.qoff, r.ncand, r.B, r.Tq, bm, r.koff,
+                     r.Tk, r.cached ? 1 : 0, attn_max_tiles(r.Tq, r.B), sc.tiles, max_kb, sc.kblocks, sc.tbase,
+                     sc.kbase, sc.counts);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(block_ts_kernel, dim3((unsigned)((max_kb + 3) / 4)), dim3(256), 0, s, off, ncand, T, ts,
-                     sc.kblocks, sc.counts, sc.rel, sc.tstat);
+  hipLaunchKernelGGL(block_ts_kernel, dim3((unsigned)((max_kb + 3) / 4)), dim3(256), 0, s, r.koff,
+                     (const int32_t*)nullptr, r.Tk, r.kts, sc.kblocks, sc.counts, sc.rel, sc.tstat);
   return hipGetLastError();
 }
 

@@ -66,3 +66,84 @@ class HSTUStack:
                            tables=self._tables[n])
             h = dst
         return h
+
+
+# ------------------------------------------------------------ cached ranking
+def split_history(offsets: np.ndarray, num_candidates: Optional[np.ndarray]):
+    """Host-side index arithmetic of a packed batch whose sequences end in
+    candidates: returns (history rows, history offsets, candidate rows,
+    candidate offsets, per-sequence candidate counts), all int64 NumPy."""
+    off = np.asarray(offsets, np.int64)
+    B = len(off) - 1
+    L = np.diff(off)
+    m = np.zeros(B, np.int64) if num_candidates is None else \
+        np.minimum(np.maximum(np.asarray(num_candidates, np.int64), 0), L)
+    n = L - m
+    hrows = np.concatenate([np.arange(off[b], off[b] + n[b]) for b in range(B)] + [np.zeros(0, np.int64)])
+    crows = np.concatenate([np.arange(off[b] + n[b], off[b + 1]) for b in range(B)] + [np.zeros(0, np.int64)])
+    hoff = np.concatenate([[0], np.cumsum(n)]).astype(np.int64)
+    coff = np.concatenate([[0], np.cumsum(m)]).astype(np.int64)
+    return hrows.astype(np.int64), hoff, crows.astype(np.int64), coff, m
+
+
+def candidate_microbatches(cand_offsets: np.ndarray, per_seq: int):
+    """Splits every sequence's candidates (rows cand_offsets[b] ..
+    cand_offsets[b+1]-1 of the packed candidates) into consecutive groups of at
+    most `per_seq`; yields (rows, offsets) per micro-batch, sequences with no
+    candidates left contributing empty ranges."""
+    coff = np.asarray(cand_offsets, np.int64)
+    m = np.diff(coff)
+    nmb = int((m.max() + per_seq - 1) // per_seq) if len(m) and m.max() > 0 else 0
+    for k in range(nmb):
+        lo = np.minimum(m, k * per_seq)
+        hi = np.minimum(m, (k + 1) * per_seq)
+        rows = np.concatenate([np.arange(coff[b] + lo[b], coff[b] + hi[b]) for b in range(len(m))])
+        yield rows.astype(np.int64), np.concatenate([[0], np.cumsum(hi - lo)]).astype(np.int64)
+
+
+class CachedRanker:
+    """Candidate scoring against a cached history for a stack of layers.
+
+    encode_history() runs the stack over the history rows alone through the
+    stage entry points and keeps every layer's K and V of those rows (history
+    rows never see candidates, so these are the K, V of the full batch's history
+    rows).  score() then pushes one micro-batch of candidates through every layer
+    with hstu_cand_fwd against that layer's cache.  Needs HSTU_CAND_SHARED_POS
+    (the dims' cand_shared_pos)."""
+
+    def __init__(self, dims, layers: List[Dict[str, torch.Tensor]], flags_extra: int = 0):
+        self.desc = _lib.make_desc(dims, flags_extra)
+        self.layers = layers
+        self._weights = [_lib.make_weights(p) for p in layers]
+        self._tables = [_lib.make_tables(p) for p in layers]
+        self.cache: List[Dict[str, torch.Tensor]] = []
+        self._ws: Optional[torch.Tensor] = None
+
+    def encode_history(self, x_hist, hist_offsets, hist_ts) -> torch.Tensor:
+        """Fills the per-layer K/V cache; returns the history's last-layer output."""
+        self.hist_offsets, self.hist_ts = hist_offsets, hist_ts
+        self.cache = []
+        h = x_hist
+        for prm in self.layers:
+            acts = _lib.proj_fwd(self.desc, h, prm)
+            _lib.attn_fwd(self.desc, hist_offsets, hist_ts, None, prm, acts)
+            h, _ = _lib.out_fwd(self.desc, h, prm, acts)
+            self.cache.append({"k": acts["k"], "v": acts["v"]})
+        return h
+
+    def score(self, x_cand, cand_offsets, cand_ts, num_candidates, out=None) -> torch.Tensor:
+        """The last layer's output rows of one candidate micro-batch;
+        num_candidates[b] counts the sequence's candidates over all micro-batches."""
+        Tc, B = x_cand.shape[0], cand_offsets.shape[0] - 1
+        need = _lib.cand_workspace_size(self.desc, Tc, self.hist_ts.shape[0], B)
+        if self._ws is None or self._ws.numel() < need or self._ws.device != x_cand.device:
+            self._ws = _lib.alloc_workspace(need, x_cand.device)
+        h = x_cand
+        for n, prm in enumerate(self.layers):
+            last = n == len(self.layers) - 1
+            dst = out if (last and out is not None) else torch.empty_like(x_cand)
+            _lib.cand_fwd(self.desc, h, cand_offsets, cand_ts, num_candidates, self.hist_offsets,
+                          self.hist_ts, self.cache[n]["k"], self.cache[n]["v"], prm, out=dst,
+                          workspace=self._ws, weights=self._weights[n], tables=self._tables[n])
+            h = dst
+        return h

@@ -197,6 +197,43 @@ hstu_status hstu_out_fwd(const hstu_desc* desc, const void* x, int64_t total_tok
                          const hstu_weights* weights, const hstu_activations* acts, void* out,
                          void* z, hstu_stream_t stream);
 
+/* Candidate pass against cached history ([FRC] 7.1.5 M-FALCON; [SRM]
+ * "Efficiency tricks": candidates see the history and themselves, not one
+ * another).  A candidate's output row depends only on its own row, the
+ * history's K and V and its metadata, so a caller scores m_b candidates in
+ * micro-batches: the history's K/V come once from hstu_proj_fwd over the
+ * history rows alone (acts->k, acts->v of that call), and each micro-batch
+ * runs stage 1 on its candidates only and stage 2 with queries = those
+ * candidates, keys = cached history + the candidate itself.  Each output row
+ * equals the candidate's row of hstu_layer_fwd over history + all m_b
+ * candidates (same weights, HSTU_CAND_SHARED_POS) up to rounding order.
+ *   x_cand         [Tc, d]   candidate rows of this micro-batch, packed per
+ *                            sequence (sequence b owns cand_offsets[b] ..
+ *                            cand_offsets[b+1]-1; empty allowed)
+ *   cand_offsets   [B+1]     int64, cand_offsets[0] = 0, [B] = Tc
+ *   cand_ts        [Tc]      int64 candidate timestamps
+ *   num_candidates [B]       int32 m_b: the sequence's candidates over ALL
+ *                            micro-batches (N_b = n_b + m_b; values below the
+ *                            micro-batch's own count are raised to it)
+ *   hist_offsets   [B+1]     int64 history rows of the cache, [B] = Th
+ *   hist_ts        [Th]      int64 history timestamps
+ *   hist_k         [H, Th, dqk], hist_v [H, Th, dv]: the cache, layer dtype
+ *                            (hist_k, hist_v, hist_ts may be NULL when Th = 0)
+ *   out            [Tc, d]   may alias x_cand
+ *   workspace      >= hstu_cand_workspace_size(desc, Tc, Th, B), 256-aligned
+ * Requires HSTU_CAND_SHARED_POS (a candidate's position is then n_b whatever
+ * micro-batch it is in); without it returns HSTU_ERR_UNSUPPORTED.
+ * HSTU_REUSE_PLAN applies as in hstu_layer_fwd (same micro-batch metadata).  */
+size_t hstu_cand_workspace_size(const hstu_desc* desc, int64_t cand_tokens, int64_t hist_tokens,
+                                int32_t batch);
+hstu_status hstu_cand_fwd(const hstu_desc* desc, const void* x_cand, const int64_t* cand_offsets,
+                          int32_t batch, int64_t cand_tokens, const int64_t* cand_ts,
+                          const int32_t* num_candidates, const int64_t* hist_offsets,
+                          int64_t hist_tokens, const int64_t* hist_ts, const void* hist_k,
+                          const void* hist_v, const hstu_weights* weights,
+                          const hstu_bias_tables* tables, void* out, void* workspace,
+                          size_t workspace_bytes, hstu_stream_t stream);
+
 /* Integer indexing used by stage 2, for inspection: for each flat pair
  * (query row, key row) in pairs[n_pairs][2] (int64, device) writes
  * out[n][0..5] = {b, i, j, bp, bt, mask} (int64, device) with the definitions

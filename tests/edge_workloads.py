@@ -1,6 +1,8 @@
 """Seeded workloads shared by the GPU parity tests and the CPU checks of
 their sensitivity (inputs only: no layer arithmetic here)."""
 
+import dataclasses
+
 import numpy as np
 
 from hstu_sequential_transducer_layer_amd import synth
@@ -36,4 +38,32 @@ def bucket_edge_workload(sub_bits: int, pos_buckets: int):
     ts[2 * n:] = base + offs[::-1]
     w.timestamps = ts
     w.layers[0]["time_table"] = rng.normal(0.0, 1.0, w.layers[0]["time_table"].shape).astype(np.float32)
+    return w
+
+
+EDGE_DIMS = {
+    "bf16": synth.LayerDims(64, 2, 32, 64, pos_buckets=9, time_buckets=16, dtype="bf16"),
+    "fp32": synth.LayerDims(64, 2, 32, 32, pos_buckets=9, time_buckets=16, dtype="fp32"),
+    "bf16_s1": synth.LayerDims(96, 3, 64, 32, pos_buckets=129, time_buckets=128,
+                               time_sub_bits=1, dtype="bf16"),
+}
+
+
+def edge_workload(kind, seed=0, **flags):
+    """Nine sequences: empty ones, one token, tile edges (127/128/129), all-
+    candidate ones, and in sequence 6 equal, decreasing and far-apart
+    timestamps; ``flags`` replace fields of EDGE_DIMS[kind]."""
+    lens = [0, 1, 127, 128, 129, 0, 200, 64, 3]
+    cands = [0, 1, 0, 5, 129, 0, 70, 64, 2]
+    dims = dataclasses.replace(EDGE_DIMS[kind], **flags)
+    hist = [L - m for L, m in zip(lens, cands)]
+    w = synth.make_workload("small_fp32", seed=seed, lengths=hist, candidates=cands, dims=dims,
+                            random_ln=True)
+    ts = w.timestamps.copy()
+    # equal, decreasing and far-apart timestamps inside sequence 6
+    s0 = int(w.offsets[6])
+    ts[s0 + 10:s0 + 20] = ts[s0 + 10]
+    ts[s0 + 30] = ts[s0 + 29] - 1000
+    ts[s0 + 40:] += 1 << 40
+    w.timestamps = ts
     return w

@@ -28,7 +28,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 11
+    assert len(names) == 13
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.EXPORTS)
@@ -154,3 +154,44 @@ def test_status_strings(lib):
     for s in range(5):
         assert lib.hstu_status_str(s).decode()
     assert lib.hstu_status_str(99).decode() == "unknown status"
+
+
+def test_cand_workspace_size_matches_layout(lib):
+    Tc, Th, B = 3000, 57291, 64
+    d = _desc()
+    e, H, dv, dq, dm = 2, 8, 128, 128, 512
+    a = lambda n: (n + 255) // 256 * 256
+    # query-side tiles over the candidates, key blocks / offsets / stats over the history
+    attn = (a(((Tc + 127) // 128 + B) * 8) + a(((Th + 63) // 64 + B) * 8) + a(8) + 2 * a((B + 1) * 4)
+            + a((Th + 64) * 4) + a(Th * 16))
+    want = (a(Tc * dm * e) + a(Tc * H * dv * e) * 3 + a(Tc * H * dq * e) * 2 + a(Tc * H * 8)
+            + attn)
+    assert _lib.cand_workspace_size(d, Tc, Th, B) == want
+    assert _lib.cand_workspace_size(d, Tc, -1, B) == 0
+
+
+def _cand(lib, desc, Tc=100, Th=1000, B=4, x=FAKE, coff=FAKE, cts=FAKE, m=FAKE, hoff=FAKE,
+          hts=FAKE, hk=FAKE, hv=FAKE, out=FAKE, ws=FAKE, ws_bytes=1 << 40):
+    w = _lib.HstuWeights(*([FAKE] * 8))
+    t = _lib.HstuBiasTables(FAKE, FAKE, 129, 64)
+    R = ctypes.byref
+    return lib.hstu_cand_fwd(R(desc), x, coff, B, Tc, cts, m, hoff, Th, hts, hk, hv, R(w), R(t),
+                             out, ws, ws_bytes, None)
+
+
+def test_cand_entry_point_checks_arguments(lib):
+    d = _desc()
+    no_shared = _desc(flags=_lib.HSTU_INPUT_NORM | _lib.HSTU_RESIDUAL)
+    assert _cand(lib, no_shared) == _lib.HSTU_ERR_UNSUPPORTED
+    assert "SHARED_POS" in lib.hstu_last_error().decode()
+    for kw in (dict(x=None), dict(out=None), dict(m=None), dict(m=FAKE + 2), dict(hk=None),
+               dict(hv=FAKE + 8), dict(coff=None), dict(hts=None), dict(cts=FAKE + 4),
+               dict(Th=-1), dict(Tc=-1), dict(B=0)):
+        assert _cand(lib, d, **kw) == _lib.HSTU_ERR_INVALID_ARG, kw
+    assert _cand(lib, d, ws=None) == _lib.HSTU_ERR_WORKSPACE
+    assert _cand(lib, d, ws_bytes=4096) == _lib.HSTU_ERR_WORKSPACE
+    assert _cand(lib, d, Tc=0, x=None, out=None) == _lib.HSTU_OK        # nothing to score
+    # no history: the cache pointers are not needed (the call then reaches the
+    # device only through a workspace check, which fails here)
+    assert _cand(lib, d, Th=0, hk=None, hv=None, hts=None, ws_bytes=4096) == _lib.HSTU_ERR_WORKSPACE
+    assert _cand(lib, d, hoff=None) == _lib.HSTU_ERR_INVALID_ARG

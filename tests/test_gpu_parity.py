@@ -18,7 +18,7 @@ import torch
 from hstu_sequential_transducer_layer_amd import _lib, layer, synth
 from oracle import hstu_oracle as O
 
-from edge_workloads import bucket_edge_workload
+from edge_workloads import EDGE_DIMS, bucket_edge_workload, edge_workload as _edge_workload
 from gpu_helpers import check, gpu_taps, say
 
 pytestmark = pytest.mark.gpu
@@ -157,31 +157,6 @@ def test_stack8_full_stack():
 
 
 # ---------------------------------------------------------------- edge cases
-EDGE_DIMS = {
-    "bf16": synth.LayerDims(64, 2, 32, 64, pos_buckets=9, time_buckets=16, dtype="bf16"),
-    "fp32": synth.LayerDims(64, 2, 32, 32, pos_buckets=9, time_buckets=16, dtype="fp32"),
-    "bf16_s1": synth.LayerDims(96, 3, 64, 32, pos_buckets=129, time_buckets=128,
-                               time_sub_bits=1, dtype="bf16"),
-}
-
-
-def _edge_workload(kind, seed=0, **flags):
-    lens = [0, 1, 127, 128, 129, 0, 200, 64, 3]
-    cands = [0, 1, 0, 5, 129, 0, 70, 64, 2]
-    dims = dataclasses.replace(EDGE_DIMS[kind], **flags)
-    hist = [L - m for L, m in zip(lens, cands)]
-    w = synth.make_workload("small_fp32", seed=seed, lengths=hist, candidates=cands, dims=dims,
-                            random_ln=True)
-    ts = w.timestamps.copy()
-    # equal, decreasing and far-apart timestamps inside sequence 6
-    s0 = int(w.offsets[6])
-    ts[s0 + 10:s0 + 20] = ts[s0 + 10]
-    ts[s0 + 30] = ts[s0 + 29] - 1000
-    ts[s0 + 40:] += 1 << 40
-    w.timestamps = ts
-    return w
-
-
 @pytest.mark.parametrize("kind", sorted(EDGE_DIMS))
 @pytest.mark.parametrize("flags", [
     {},
