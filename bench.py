@@ -105,6 +105,110 @@ def cpu_baseline(w, budget_s: float = 20.0):
                       f"{n_layers} layers"}
 
 
+def cand_inference(torch, _lib, layer, synth, per_seq: int = 128, reps: int = 20):
+    """Scoring every candidate of the ranking workload (B=16, history
+    U[512, 2048] + 512 candidates, d=512, 8 heads x 64/64, bf16) three ways:
+    one batched pass over history + all candidates; micro-batches of
+    `per_seq` candidates per sequence, each a full pass over history + those
+    candidates; and the same micro-batches against a history K/V cache
+    (history projected once, then hstu_cand_fwd per micro-batch).  Each way is
+    captured once into a HIP graph and replayed (the small per-micro-batch
+    kernels would otherwise time the host's launch rate); the eager times are
+    reported too."""
+    w = synth.make_workload("ranking_cand")
+    dev = layer.to_device(w)
+    D = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    hrows, hoff, crows, coff, m = layer.split_history(w.offsets, w.num_candidates)
+    x, ts = dev["x"], dev["timestamps"]
+    prm = dev["layers"][0]
+    desc = _lib.make_desc(w.dims)
+    wts, tab = _lib.make_weights(prm), _lib.make_tables(prm)
+    B = w.B
+    mbs = list(layer.candidate_microbatches(coff, per_seq))
+    # full passes: batched, and per micro-batch over history + its candidates
+    full_in = []
+    for rows, moff in mbs:
+        cnt = np.diff(moff)
+        sel = np.concatenate([np.r_[hrows[hoff[b]:hoff[b + 1]], crows[rows[moff[b]:moff[b + 1]]]]
+                              for b in range(B)])
+        off = np.concatenate([[0], np.cumsum(np.diff(hoff) + cnt)]).astype(np.int64)
+        full_in.append((x[D(sel)].contiguous(), D(off), ts[D(sel)].contiguous(), D(cnt.astype(np.int32))))
+    ws_full = _lib.alloc_workspace(_lib.workspace_size(desc, w.T, B), "cuda")
+    out_full = torch.empty_like(x)
+    outs_mb = [torch.empty_like(a[0]) for a in full_in]
+    # cached: history rows, then candidate micro-batches
+    xh, hoff_d, hts = x[D(hrows)].contiguous(), D(hoff), ts[D(hrows)].contiguous()
+    cand_in = [(x[D(crows[r])].contiguous(), D(o), ts[D(crows[r])].contiguous()) for r, o in mbs]
+    m_d = D(m.astype(np.int32))
+    acts_h = _lib.alloc_activations(desc, len(hrows), "cuda")
+    ws_proj = _lib.alloc_workspace(_lib.proj_workspace_size(desc, len(hrows)), "cuda")
+    Tc_max = max(len(r) for r, _ in mbs)
+    ws_c = _lib.alloc_workspace(_lib.cand_workspace_size(desc, Tc_max, len(hrows), B), "cuda")
+    outs_c = [torch.empty_like(a[0]) for a in cand_in]
+
+    def batched():
+        _lib.layer_fwd(desc, x, dev["offsets"], ts, dev["num_candidates"], prm, out=out_full,
+                       workspace=ws_full, weights=wts, tables=tab)
+
+    def microbatched():
+        for (xi, oi, ti, ni), yo in zip(full_in, outs_mb):
+            _lib.layer_fwd(desc, xi, oi, ti, ni, prm, out=yo, workspace=ws_full, weights=wts, tables=tab)
+
+    def encode():
+        _lib.proj_fwd(desc, xh, prm, acts_h, workspace=ws_proj, weights=wts)
+
+    def cached_mbs():
+        for (xc, oc, tc), yo in zip(cand_in, outs_c):
+            _lib.cand_fwd(desc, xc, oc, tc, m_d, hoff_d, hts, acts_h["k"], acts_h["v"], prm, out=yo,
+                          workspace=ws_c, weights=wts, tables=tab)
+
+    def cached():
+        encode()
+        cached_mbs()
+
+    def ev_time(fn):
+        fn()
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        st = torch.cuda.current_stream()
+        s.record(st)
+        for _ in range(reps):
+            fn()
+        e.record(st)
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / reps
+
+    def graph_time(fn):
+        fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        torch.cuda.synchronize()
+        return ev_time(g.replay)
+
+    res = {}
+    for name, fn in (("batched", batched), ("microbatched", microbatched), ("cached", cached),
+                     ("cache_encode", encode), ("cached_microbatches", cached_mbs)):
+        res[name] = {"graph_ms": graph_time(fn), "eager_ms": ev_time(fn)}
+    nmb = len(mbs)
+    ncand = int(m.sum())
+    per_unc = res["microbatched"]["graph_ms"] / nmb
+    per_c = res["cached_microbatches"]["graph_ms"] / nmb
+    return {
+        "workload": f"ranking_cand: {synth.WORKLOADS['ranking_cand'].description}; 1 layer",
+        "history_tokens": int(len(hrows)),
+        "candidates": ncand,
+        "micro_batch_per_seq": per_seq,
+        "micro_batches": nmb,
+        "ms": res,
+        "per_microbatch_ms": {"full_pass": per_unc, "cached": per_c},
+        "cache_speedup_per_microbatch": per_unc / per_c,
+        "candidates_per_s": {k: ncand / (res[k]["graph_ms"] * 1e-3)
+                             for k in ("batched", "microbatched", "cached")},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -113,6 +217,7 @@ def main():
     ap.add_argument("--workload", default="stack8_long")
     ap.add_argument("--attn-reps", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--no-cand", action="store_true", help="skip the cached-candidate measurement")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-MiB device buffer 4 times (a plain copy kernel of "
@@ -253,6 +358,8 @@ def main():
         },
         "layer_tokens_per_s": T * len(w.layers) / (ms_step * 1e-3),
     }
+    if not args.no_cand:
+        rec["cand_inference"] = cand_inference(torch, _lib, layer, synth)
     if not args.no_cpu:
         rec["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
     print(json.dumps(rec), flush=True)

@@ -196,14 +196,22 @@ def _acts(a: Dict[str, torch.Tensor]) -> HstuActivations:
     return HstuActivations(*[_ptr(a.get(n)) for n in ("u", "v", "q", "k", "av", "av_stats")])
 
 
+def proj_workspace_size(desc: HstuDesc, T: int) -> int:
+    return int(load().hstu_proj_workspace_size(ctypes.byref(desc), T))
+
+
 def proj_fwd(desc: HstuDesc, x: torch.Tensor, prm: Dict[str, torch.Tensor],
-             acts: Optional[Dict[str, torch.Tensor]] = None) -> Dict[str, torch.Tensor]:
+             acts: Optional[Dict[str, torch.Tensor]] = None,
+             workspace: Optional[torch.Tensor] = None,
+             weights: Optional[HstuWeights] = None) -> Dict[str, torch.Tensor]:
     lib = load()
     T = x.shape[0]
     acts = acts or alloc_activations(desc, T, x.device)
-    need = int(lib.hstu_proj_workspace_size(ctypes.byref(desc), T))
-    ws = alloc_workspace(need, x.device)
-    a, w = _acts(acts), make_weights(prm)
+    need = proj_workspace_size(desc, T)
+    ws = workspace if workspace is not None and workspace.numel() >= need else \
+        alloc_workspace(need, x.device)
+    a = _acts(acts)
+    w = weights if weights is not None else make_weights(prm)
     _check(lib.hstu_proj_fwd(ctypes.byref(desc), _ptr(x), T, ctypes.byref(w), ctypes.byref(a),
                              _ptr(ws), ws.numel(), _stream()))
     return acts

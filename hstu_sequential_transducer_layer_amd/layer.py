@@ -119,16 +119,20 @@ class CachedRanker:
         self.cache: List[Dict[str, torch.Tensor]] = []
         self._ws: Optional[torch.Tensor] = None
 
-    def encode_history(self, x_hist, hist_offsets, hist_ts) -> torch.Tensor:
-        """Fills the per-layer K/V cache; returns the history's last-layer output."""
+    def encode_history(self, x_hist, hist_offsets, hist_ts, need_output: bool = False):
+        """Fills the per-layer K/V cache.  The last layer's attention and output
+        stage only matter for the history's own output, returned when
+        need_output (else None)."""
         self.hist_offsets, self.hist_ts = hist_offsets, hist_ts
         self.cache = []
         h = x_hist
-        for prm in self.layers:
+        for n, prm in enumerate(self.layers):
             acts = _lib.proj_fwd(self.desc, h, prm)
+            self.cache.append({"k": acts["k"], "v": acts["v"]})
+            if n == len(self.layers) - 1 and not need_output:
+                return None
             _lib.attn_fwd(self.desc, hist_offsets, hist_ts, None, prm, acts)
             h, _ = _lib.out_fwd(self.desc, h, prm, acts)
-            self.cache.append({"k": acts["k"], "v": acts["v"]})
         return h
 
     def score(self, x_cand, cand_offsets, cand_ts, num_candidates, out=None) -> torch.Tensor:

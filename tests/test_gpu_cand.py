@@ -130,6 +130,59 @@ def test_cached_without_history():
     _check_against_full(w, per_seq=2)
 
 
+def test_graph_replay_matches_eager():
+    """The layer pass, the history projection and cached micro-batches captured
+    into one HIP graph: every replay (with eager work and synchronisations in
+    between) gives the eager bits."""
+    w = edge_workload("bf16", seed=6)
+    dev = layer.to_device(w)
+    prm = dev["layers"][0]
+    desc = _lib.make_desc(w.dims)
+    wts, tab = _lib.make_weights(prm), _lib.make_tables(prm)
+    hrows, hoff, crows, coff, m = layer.split_history(w.offsets, w.num_candidates)
+    x, ts = dev["x"], dev["timestamps"]
+    xh, hts, hoff_d = x[_dev(hrows)].contiguous(), ts[_dev(hrows)].contiguous(), _dev(hoff)
+    acts = _lib.alloc_activations(desc, len(hrows), "cuda")
+    ws_p = _lib.alloc_workspace(_lib.proj_workspace_size(desc, len(hrows)), "cuda")
+    ws_l = _lib.alloc_workspace(_lib.workspace_size(desc, w.T, w.B), "cuda")
+    mbs = list(layer.candidate_microbatches(coff, 40))
+    cin = [(x[_dev(crows[r])].contiguous(), _dev(o), ts[_dev(crows[r])].contiguous()) for r, o in mbs]
+    ws_c = _lib.alloc_workspace(max(_lib.cand_workspace_size(desc, len(r), len(hrows), w.B)
+                                    for r, _ in mbs), "cuda")
+    m_d = _dev(m.astype(np.int32))
+    y_l = torch.empty_like(x)
+    y_c = [torch.empty_like(c[0]) for c in cin]
+
+    def work():
+        _lib.layer_fwd(desc, x, dev["offsets"], ts, dev["num_candidates"], prm, out=y_l,
+                       workspace=ws_l, weights=wts, tables=tab)
+        _lib.proj_fwd(desc, xh, prm, acts, workspace=ws_p, weights=wts)
+        for (xc, oc, tc), yo in zip(cin, y_c):
+            _lib.cand_fwd(desc, xc, oc, tc, m_d, hoff_d, hts, acts["k"], acts["v"], prm, out=yo,
+                          workspace=ws_c, weights=wts, tables=tab)
+
+    def snap():
+        return [t.float().cpu().numpy() for t in [y_l] + y_c]
+
+    work()
+    torch.cuda.synchronize()
+    ref = snap()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        work()
+    torch.cuda.synchronize()
+    say(f"graph of 1 layer pass + history projection + {len(mbs)} cached micro-batches")
+    for rep in range(3):
+        for t in [y_l] + y_c:
+            t.fill_(float("nan"))
+        _lib.layer_fwd(desc, x, dev["offsets"], ts, None, prm)     # unrelated eager work
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(snap(), ref):
+            np.testing.assert_array_equal(a, b, err_msg=f"replay {rep}")
+
+
 def test_cached_pass_requires_shared_positions():
     w = edge_workload("bf16", cand_shared_pos=False)
     dev = layer.to_device(w)
