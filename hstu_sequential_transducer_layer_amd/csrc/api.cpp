@@ -136,12 +136,12 @@ hstu_status check_acts(const hstu_activations* a, bool proj, bool attn) {
 
 // Workspace carve-up shared by the size query and the layer call.
 struct Layout {
-  size_t xn, u, v, q, k, av, stats, attn, total;
+  size_t xn, u, v, q, k, av, stats, attn, part, total;
 };
 
 // Tk: key rows of the attention pass (T in a layer pass, the cached history
-// rows in a candidate pass).
-Layout layout(const hstu_desc* d, int64_t T, int32_t B, int64_t Tk) {
+// rows in a candidate pass, which also needs the per-chunk partial AV).
+Layout layout(const hstu_desc* d, int64_t T, int32_t B, int64_t Tk, bool cached) {
   const size_t e = esize(d->dtype);
   const size_t H = d->num_heads, hdv = H * d->dv, hdq = H * d->dqk;
   Layout L{};
@@ -158,7 +158,8 @@ Layout layout(const hstu_desc* d, int64_t T, int32_t B, int64_t Tk) {
   L.k = take((size_t)T * hdq * e);
   L.av = take((size_t)T * hdv * e);
   L.stats = take((size_t)T * H * 2 * sizeof(float));
-  L.attn = take(hstu::attn_scratch_bytes(T, Tk, B));
+  L.attn = take(hstu::attn_scratch_bytes(T, Tk, B, cached));
+  L.part = take(cached ? hstu::cand_partial_bytes(T, d->num_heads, d->dv) : 0);
   L.total = o;
   return L;
 }
@@ -216,7 +217,7 @@ const char* hstu_last_error(void) { return g_err.c_str(); }
 
 size_t hstu_workspace_size(const hstu_desc* desc, int64_t T, int32_t B) {
   if (check_desc(desc) != HSTU_OK || check_sizes(T, B) != HSTU_OK) return 0;
-  return layout(desc, T, B, T).total;
+  return layout(desc, T, B, T, false).total;
 }
 
 size_t hstu_proj_workspace_size(const hstu_desc* desc, int64_t T) {
@@ -341,7 +342,7 @@ hstu_status hstu_layer_fwd(const hstu_desc* desc, const void* x, const int64_t* 
   if ((st = check_proj_weights(desc, w)) != HSTU_OK) return st;
   if ((st = check_out_weights(desc, w)) != HSTU_OK) return st;
   if ((st = check_tables(desc, tables)) != HSTU_OK) return st;
-  const Layout L = layout(desc, T, B, T);
+  const Layout L = layout(desc, T, B, T, false);
   if (!ws || ws_bytes < L.total || !aligned(ws, 256))
     return fail(HSTU_ERR_WORKSPACE, "workspace: need %zu bytes (256-aligned), got %zu", L.total, ws_bytes);
   hipStream_t s = (hipStream_t)stream;
@@ -368,7 +369,7 @@ hstu_status hstu_layer_fwd(const hstu_desc* desc, const void* x, const int64_t* 
 
 size_t hstu_cand_workspace_size(const hstu_desc* desc, int64_t Tc, int64_t Th, int32_t B) {
   if (check_desc(desc) != HSTU_OK || check_sizes(Tc, B) != HSTU_OK || check_sizes(Th, B) != HSTU_OK) return 0;
-  return layout(desc, Tc, B, Th).total;
+  return layout(desc, Tc, B, Th, true).total;
 }
 
 hstu_status hstu_cand_fwd(const hstu_desc* desc, const void* x, const int64_t* coff, int32_t B, int64_t Tc,
@@ -396,7 +397,7 @@ hstu_status hstu_cand_fwd(const hstu_desc* desc, const void* x, const int64_t* c
   if ((st = check_proj_weights(desc, w)) != HSTU_OK) return st;
   if ((st = check_out_weights(desc, w)) != HSTU_OK) return st;
   if ((st = check_tables(desc, tables)) != HSTU_OK) return st;
-  const Layout L = layout(desc, Tc, B, Th);
+  const Layout L = layout(desc, Tc, B, Th, true);
   if (!ws || ws_bytes < L.total || !aligned(ws, 256))
     return fail(HSTU_ERR_WORKSPACE, "workspace: need %zu bytes (256-aligned), got %zu", L.total, ws_bytes);
   hipStream_t s = (hipStream_t)stream;
@@ -413,17 +414,19 @@ hstu_status hstu_cand_fwd(const hstu_desc* desc, const void* x, const int64_t* c
   a.av = base + L.av;
   a.av_stats = (float*)(base + L.stats);
   if ((st = run_proj(desc, x, Tc, w, &a, base + L.xn, s)) != HSTU_OK) return st;
-  const hstu::AttnScratch sc = hstu::attn_scratch(base + L.attn, Tc, Th, B);
+  const hstu::AttnScratch sc = hstu::attn_scratch(base + L.attn, Tc, Th, B, true);
   const hstu::AttnRows rows{coff, nullptr, cts, Tc, hoff, hts, Th, mtotal, B, true};
   if (!(desc->flags & HSTU_REUSE_PLAN))
     if ((st = device(hstu::launch_attn_prep(rows, hstu::kAttnBM, sc, s), "attention prep launch")) != HSTU_OK)
       return st;
-  if ((st = device(hstu::launch_attn(*desc, rows, *tables, a.q, hk, hv, a.k, a.v, a.av, a.av_stats, sc, s),
+  float* part = (float*)(base + L.part);
+  if ((st = device(hstu::launch_attn_cached(*desc, rows, *tables, a.q, hk, hv, a.k, a.v, part, sc, s),
                    "attention launch")) != HSTU_OK)
     return st;
   // Z takes the V region, dead once the attention (self terms included) has run.
   void* z = base + L.v;
-  if ((st = device(hstu::launch_gate(*desc, Tc, *w, a.u, a.av, a.av_stats, z, s), "gate launch")) != HSTU_OK)
+  if ((st = device(hstu::launch_cand_gate(*desc, coff, B, Tc, sc.nsplit, part, *w, a.u, z, s), "gate launch")) !=
+      HSTU_OK)
     return st;
   if ((st = device(hstu::launch_f2(*desc, x, Tc, *w, z, out, s), "f2 launch")) != HSTU_OK) return st;
   return ok();

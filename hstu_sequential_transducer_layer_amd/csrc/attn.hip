@@ -76,6 +76,8 @@ struct AttnArgs {
   const void* qv;
   void* av;
   float* stats;
+  float* part;             // cached: per-chunk partial AV [kCandMaxSplit][T][H * DV]
+  const int32_t* nsplit;   // cached: history chunks per sequence
   const int2* tiles;
   const int32_t* counts;   // [0]: work items
   const int32_t* rel;      // per key row: offset from its key block's earliest timestamp
@@ -439,7 +441,11 @@ __global__ __launch_bounds__(256, attn_min_blocks((DQK + DV) * (int)sizeof(T))) 
   const int Lq = si.len;
   const int L = ki.len, nh = CACHED ? ki.len : si.nhist;
   const int64_t s0 = si.start, k0 = ki.start;
-  const int i0 = tl.y * C::BM;
+  // cached: this item's history chunk (key blocks [clo, chi))
+  const int chunk = CACHED ? (tl.y >> 24) : 0;
+  int clo = 0, chi = 0;
+  if (CACHED) cand_chunk((nh + C::BN - 1) / C::BN, a.nsplit[tl.x], chunk, clo, chi);
+  const int i0 = (CACHED ? (tl.y & 0xFFFFFF) : tl.y) * C::BM;
   const int iend = min(i0 + C::BM, Lq);
   const int N_b = CACHED ? L + max(a.mtotal[tl.x], Lq) : L;
   const float inv_n = 1.0f / (float)(a.norm_len > 0 ? a.norm_len : N_b);
@@ -450,14 +456,16 @@ __global__ __launch_bounds__(256, attn_min_blocks((DQK + DV) * (int)sizeof(T))) 
   const int l32 = lane & 31, half = lane >> 5;
 
   // Key blocks: history [0, min(iend, nh)), then the candidates' own rows; in a
-  // cached pass the whole history.
+  // cached pass the history chunk's blocks.
   const int a_end = CACHED ? nh : min(iend, nh);
-  const int nblk_a = (a_end + C::BN - 1) / C::BN;
+  const int nblk_a = CACHED ? chi - clo : (a_end + C::BN - 1) / C::BN;
   const int b_lo = max(i0, nh), b_hi = iend;
   const int jb0 = max(nblk_a * C::BN, (b_lo / C::BN) * C::BN);
   const int nblk_b = (!CACHED && b_lo < b_hi && jb0 < b_hi) ? (b_hi - jb0 + C::BN - 1) / C::BN : 0;
   const int nblk = nblk_a + nblk_b;
-  auto block_start = [&](int blk) __attribute__((always_inline)) { return blk < nblk_a ? blk * C::BN : jb0 + (blk - nblk_a) * C::BN; };
+  auto block_start = [&](int blk) __attribute__((always_inline)) {
+    return CACHED ? (clo + blk) * C::BN : (blk < nblk_a ? blk * C::BN : jb0 + (blk - nblk_a) * C::BN);
+  };
 
   const T* kg = reinterpret_cast<const T*>(a.k) + ((int64_t)h * a.TK + k0) * DQK;
   const T* vg = reinterpret_cast<const T*>(a.v) + ((int64_t)h * a.TK + k0) * DV;
@@ -578,7 +586,7 @@ __global__ __launch_bounds__(256, attn_min_blocks((DQK + DV) * (int)sizeof(T))) 
   }
 
   if (r0 >= iend) return;
-  if (CACHED && qvalid) {
+  if (CACHED && qvalid && chunk == 0) {
     // The candidate's own key: distance 0 (bucket R), time difference 0
     // (bucket 0).  q.k over this lane's half of dqk, then across the halves.
     const T* ks = reinterpret_cast<const T*>(a.qk) + ((int64_t)h * a.T + s0 + iq) * DQK;
@@ -596,6 +604,19 @@ __global__ __launch_bounds__(256, attn_min_blocks((DQK + DV) * (int)sizeof(T))) 
     for (int n = 0; n < DV / 32; ++n)
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[n][r] += wself * to_f32(vs[32 * n + 8 * (r >> 2) + 4 * half + (r & 3)]);
+  }
+  if (CACHED) {
+    // this chunk's share, scaled; cand_gate_kernel sums the chunks
+    if (!qvalid) return;
+    float* dst = a.part + ((int64_t)chunk * a.T + s0 + iq) * (H * DV) + h * DV;
+#pragma unroll
+    for (int n = 0; n < DV / 32; ++n)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<float4*>(dst + n * 32 + 8 * g + 4 * half) =
+            make_float4(o[n][4 * g] * inv_n, o[n][4 * g + 1] * inv_n, o[n][4 * g + 2] * inv_n,
+                        o[n][4 * g + 3] * inv_n);
+    return;
   }
   attn_store<T, DV>(o, inv_n, qvalid, s0 + iq, h, H, a.av, a.stats, half);
 }
@@ -638,11 +659,13 @@ static hipError_t launch_dims_f32(const AttnArgs& a, bool cached, int dqk, int d
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_attn(const hstu_desc& d, const AttnRows& r, const hstu_bias_tables& tab, const void* q,
-                       const void* k, const void* v, const void* qk, const void* qv, void* av, float* stats,
-                       const AttnScratch& sc, hipStream_t s) {
+static hipError_t launch_attn_impl(const hstu_desc& d, const AttnRows& r, const hstu_bias_tables& tab,
+                                   const void* q, const void* k, const void* v, const void* qk, const void* qv,
+                                   float* part, void* av, float* stats, const AttnScratch& sc, hipStream_t s) {
   if (r.Tq == 0) return hipSuccess;
   AttnArgs a;
+  a.part = part;
+  a.nsplit = sc.nsplit;
   a.off = r.qoff;
   a.ncand = r.ncand;
   a.ts = r.qts;
@@ -672,9 +695,23 @@ hipError_t launch_attn(const hstu_desc& d, const AttnRows& r, const hstu_bias_ta
   a.time_stride = tab.time_head_stride;
   a.norm_len = d.norm_len;
   a.shared_pos = (d.flags & HSTU_CAND_SHARED_POS) ? 1 : 0;
-  const int64_t grid = attn_max_tiles(r.Tq, r.B) * d.num_heads;
+  const int64_t grid = attn_max_items(r.Tq, r.B, r.cached) * d.num_heads;
   if (d.dtype == HSTU_BF16) return launch_dims<bf16>(a, r.cached, d.dqk, d.dv, grid, s);
   return launch_dims_f32(a, r.cached, d.dqk, d.dv, grid, s);
+}
+
+hipError_t launch_attn(const hstu_desc& d, const AttnRows& r, const hstu_bias_tables& tab, const void* q,
+                       const void* k, const void* v, const void* qk, const void* qv, void* av, float* stats,
+                       const AttnScratch& sc, hipStream_t s) {
+  if (r.cached) return hipErrorInvalidValue;  // needs the partial buffer: launch_attn_cached
+  return launch_attn_impl(d, r, tab, q, k, v, qk, qv, nullptr, av, stats, sc, s);
+}
+
+hipError_t launch_attn_cached(const hstu_desc& d, const AttnRows& r, const hstu_bias_tables& tab,
+                              const void* q, const void* k, const void* v, const void* qk, const void* qv,
+                              float* part, const AttnScratch& sc, hipStream_t s) {
+  if (!r.cached) return hipErrorInvalidValue;
+  return launch_attn_impl(d, r, tab, q, k, v, qk, qv, part, nullptr, nullptr, sc, s);
 }
 
 }  // namespace hstu

@@ -20,6 +20,13 @@ namespace hstu {
 typedef __attribute__((address_space(3))) void g2_lds_void;
 typedef __attribute__((address_space(1))) void g2_glb_void;
 
+// Below this many 256 x 256 tiles a projection launch leaves most compute
+// units idle, and the 128 x 128 kernel (four times the tiles) finishes first
+// (measured on a 2048-row candidate micro-batch: 16 us against 21 us).  The
+// f2 GEMM keeps the large tiles at every size: its 128 x 128 kernel was
+// slower even there.
+constexpr int64_t kG2MinTiles = 128;
+
 struct G2 {
   static constexpr int BM = 256, BN = 256, BK = 64;
   static constexpr int NT = 512;            // threads

@@ -13,18 +13,43 @@ namespace hstu {
 constexpr int kAttnBM = 128;
 constexpr int kAttnBN = 64;
 
+// A cached candidate pass splits each sequence's history into
+// min(kCandMaxSplit, ceil(key blocks / kCandSplitBlocks)) chunks (at least one),
+// each its own work item, so that a micro-batch with few query tiles still
+// fills the chip.  The split depends only on the history length, so a row's
+// result does not depend on the micro-batch it is scored in.
+constexpr int kCandSplitBlocks = 4;
+constexpr int kCandMaxSplit = 8;
+
+__host__ __device__ inline int cand_nsplit(int hist_len) {
+  const int nb = (hist_len + kAttnBN - 1) / kAttnBN;
+  const int s = (nb + kCandSplitBlocks - 1) / kCandSplitBlocks;
+  return s < 1 ? 1 : (s > kCandMaxSplit ? kCandMaxSplit : s);
+}
+// Key blocks [lo, hi) of history chunk c out of ns over nblk blocks (balanced;
+// empty only when nblk = 0).
+__host__ __device__ inline void cand_chunk(int nblk, int ns, int c, int& lo, int& hi) {
+  lo = c * nblk / ns;
+  hi = (c + 1) * nblk / ns;
+}
+
 // Upper bound on attention work items (q-tiles over all sequences).
 inline int64_t attn_max_tiles(int64_t T, int32_t B) { return (T + kAttnBM - 1) / kAttnBM + B; }
+inline int64_t attn_max_items(int64_t Tq, int32_t B, bool cached) {
+  return attn_max_tiles(Tq, B) * (cached ? kCandMaxSplit : 1);
+}
 // Upper bound on key blocks (64 keys from a sequence's start) over all sequences.
 inline int64_t attn_max_kblocks(int64_t T, int32_t B) { return (T + kAttnBN - 1) / kAttnBN + B; }
 
 // Device scratch of the attention stage, carved from one caller buffer.  Tq
 // counts query rows, Tk key rows (the same rows in a layer pass; the cached
 // history in a candidate pass).
-//   tiles   int2 {b, q-tile}, work list ordered by decreasing cost
+//   tiles   int2 {b, q-tile}, work list ordered by decreasing cost; in a
+//           cached pass {b, q-tile | history chunk << 24}
 //   kblocks int2 {b, key block}, every key block once, any order
 //   counts  int32 [2]: number of tiles, number of key blocks
 //   tbase, kbase  int32 [B + 1]: first tile / key block of each sequence
+//   nsplit  int32 [B]: history chunks per sequence (cached pass; else 1)
 //   rel     int32 [Tk + kAttnBN]: ts[row] - (earliest timestamp of its key block)
 //   tstat   int64 [Tk][2]: at each key block's first row, the block's
 //           earliest and latest timestamps (other rows unused)
@@ -34,24 +59,25 @@ struct AttnScratch {
   int32_t* counts;
   int32_t* tbase;
   int32_t* kbase;
+  int32_t* nsplit;
   int32_t* rel;
   int64_t* tstat;
 };
 
 inline size_t attn_align(size_t n) { return (n + 255) & ~(size_t)255; }
 
-inline size_t attn_scratch_bytes(int64_t Tq, int64_t Tk, int32_t B) {
-  return attn_align((size_t)attn_max_tiles(Tq, B) * 8) + attn_align((size_t)attn_max_kblocks(Tk, B) * 8) +
-         attn_align(2 * sizeof(int32_t)) + 2 * attn_align(((size_t)B + 1) * 4) +
+inline size_t attn_scratch_bytes(int64_t Tq, int64_t Tk, int32_t B, bool cached) {
+  return attn_align((size_t)attn_max_items(Tq, B, cached) * 8) + attn_align((size_t)attn_max_kblocks(Tk, B) * 8) +
+         attn_align(2 * sizeof(int32_t)) + 3 * attn_align(((size_t)B + 1) * 4) +
          attn_align((size_t)(Tk + kAttnBN) * 4) + attn_align((size_t)Tk * 16);
 }
-inline size_t attn_scratch_bytes(int64_t T, int32_t B) { return attn_scratch_bytes(T, T, B); }
+inline size_t attn_scratch_bytes(int64_t T, int32_t B) { return attn_scratch_bytes(T, T, B, false); }
 
-inline AttnScratch attn_scratch(void* base, int64_t Tq, int64_t Tk, int32_t B) {
+inline AttnScratch attn_scratch(void* base, int64_t Tq, int64_t Tk, int32_t B, bool cached) {
   char* p = (char*)base;
   AttnScratch a;
   a.tiles = (int2*)p;
-  p += attn_align((size_t)attn_max_tiles(Tq, B) * 8);
+  p += attn_align((size_t)attn_max_items(Tq, B, cached) * 8);
   a.kblocks = (int2*)p;
   p += attn_align((size_t)attn_max_kblocks(Tk, B) * 8);
   a.counts = (int32_t*)p;
@@ -60,12 +86,20 @@ inline AttnScratch attn_scratch(void* base, int64_t Tq, int64_t Tk, int32_t B) {
   p += attn_align(((size_t)B + 1) * 4);
   a.kbase = (int32_t*)p;
   p += attn_align(((size_t)B + 1) * 4);
+  a.nsplit = (int32_t*)p;
+  p += attn_align(((size_t)B + 1) * 4);
   a.rel = (int32_t*)p;
   p += attn_align((size_t)(Tk + kAttnBN) * 4);
   a.tstat = (int64_t*)p;
   return a;
 }
-inline AttnScratch attn_scratch(void* base, int64_t T, int32_t B) { return attn_scratch(base, T, T, B); }
+inline AttnScratch attn_scratch(void* base, int64_t T, int32_t B) { return attn_scratch(base, T, T, B, false); }
+
+// Partial AV of a cached pass: [kCandMaxSplit][Tq][H * dv] fp32, chunk c of
+// row r at (c * Tq + r) * H * dv (only each sequence's nsplit chunks written).
+inline size_t cand_partial_bytes(int64_t Tq, int H, int dv) {
+  return attn_align((size_t)kCandMaxSplit * (size_t)Tq * (size_t)H * (size_t)dv * 4);
+}
 
 // The rows an attention pass reads.  Query rows: sequence b is
 // [qoff[b], qoff[b + 1]) of the query-side tensors, its last ncand[b] rows
@@ -103,12 +137,22 @@ hipError_t launch_proj(const hstu_desc& d, const void* xn, int64_t T, const void
 hipError_t launch_attn(const hstu_desc& d, const AttnRows& rows, const hstu_bias_tables& tab, const void* q,
                        const void* k, const void* v, const void* qk, const void* qv, void* av, float* stats,
                        const AttnScratch& sc, hipStream_t s);
+// Cached pass: the attention writes each history chunk's partial AV (scaled
+// by 1/N_b; the candidate's own term in chunk 0) to `part`.
+hipError_t launch_attn_cached(const hstu_desc& d, const AttnRows& rows, const hstu_bias_tables& tab,
+                              const void* q, const void* k, const void* v, const void* qk, const void* qv,
+                              float* part, const AttnScratch& sc, hipStream_t s);
 
 // --- out.hip: z = LN_av(av) * u, then out = z W2^T + b2 (+ x).
 hipError_t launch_gate(const hstu_desc& d, int64_t T, const hstu_weights& w, const void* u,
                        const void* av, const float* stats, void* z, hipStream_t s);
 hipError_t launch_f2(const hstu_desc& d, const void* x, int64_t T, const hstu_weights& w,
                      const void* z, void* out, hipStream_t s);
+// Cached pass: z = (LayerNorm(sum of the row's history chunks) * g + b) * u,
+// the chunks summed in chunk order (query rows qoff / B / Tq of the pass).
+hipError_t launch_cand_gate(const hstu_desc& d, const int64_t* qoff, int32_t B, int64_t Tq,
+                            const int32_t* nsplit, const float* part, const hstu_weights& w, const void* u,
+                            void* z, hipStream_t s);
 
 // --- debug.hip
 hipError_t launch_debug_indices(const hstu_desc& d, const int64_t* off, const int32_t* ncand,

@@ -58,6 +58,122 @@ __global__ __launch_bounds__(256) void gate_kernel(const T* __restrict__ av, con
   }
 }
 
+// The sequence holding `row`: the largest b in [0, B) whose (clamped) start
+// is <= row, found by the whole wave, 64 candidates per step.
+__device__ __forceinline__ int row_sequence(const int64_t* off, int B, int64_t T, int64_t row, int lane) {
+  int lo = 0, n = B;  // answer in [lo, lo + n)
+  while (n > 1) {
+    const int stride = (n + kWave - 1) / kWave;
+    const int64_t s = lane * stride < n ? off[lo + lane * stride] : T + 1;
+    const int cnt = __popcll(__ballot(min(max(s, (int64_t)0), T + 1) <= row));
+    const int pick = max(cnt, 1) - 1;
+    lo += pick * stride;
+    n = min(stride, n - pick * stride);
+  }
+  return lo;
+}
+
+// Cached candidate pass: one wave per row sums the row's fp32 history-chunk
+// partials of AV in chunk order (the scheduling of the attention work items
+// cannot change the result), then z = (LayerNorm(AV) * g + b) * u directly
+// from those fp32 values.  NC: 16-byte column groups per lane.
+template <typename T, int NC>
+__global__ __launch_bounds__(256) void cand_gate_kernel(const float* __restrict__ part,
+                                                        const int64_t* __restrict__ off, int32_t B, int64_t Tq,
+                                                        const int32_t* __restrict__ nsplit,
+                                                        const T* __restrict__ u, const T* __restrict__ g,
+                                                        const T* __restrict__ be, T* __restrict__ z, int K,
+                                                        float eps) {
+  constexpr int V = Elem<T>::kVec;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + wave_id();
+  if (row >= Tq) return;  // whole wave leaves together
+  const int b = row_sequence(off, B, Tq, row, lane);
+  const int ns = min(max(nsplit[b], 1), kCandMaxSplit);
+  float x[NC][V];
+#pragma unroll
+  for (int i = 0; i < NC; ++i)
+#pragma unroll
+    for (int e = 0; e < V; ++e) x[i][e] = 0.f;
+#pragma unroll
+  for (int c = 0; c < kCandMaxSplit; ++c) {
+    if (c >= ns) break;
+    const float* src = part + ((int64_t)c * Tq + row) * K;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int col = (lane + kWave * i) * V;
+      if (col < K) {
+#pragma unroll
+        for (int q4 = 0; q4 < V / 4; ++q4) {
+          const float4 v = *reinterpret_cast<const float4*>(src + col + 4 * q4);
+          x[i][4 * q4] += v.x;
+          x[i][4 * q4 + 1] += v.y;
+          x[i][4 * q4 + 2] += v.z;
+          x[i][4 * q4 + 3] += v.w;
+        }
+      }
+    }
+  }
+  float s1 = 0.f;
+#pragma unroll
+  for (int i = 0; i < NC; ++i)
+    if ((lane + kWave * i) * V < K)
+#pragma unroll
+      for (int e = 0; e < V; ++e) s1 += x[i][e];
+  const float mean = wave_sum(s1) / (float)K;
+  float s2 = 0.f;
+#pragma unroll
+  for (int i = 0; i < NC; ++i)
+    if ((lane + kWave * i) * V < K)
+#pragma unroll
+      for (int e = 0; e < V; ++e) s2 += (x[i][e] - mean) * (x[i][e] - mean);
+  const float rstd = rsqrtf(wave_sum(s2) / (float)K + eps);
+  const T* ur = u + row * K;
+  T* zr = z + row * K;
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int col = (lane + kWave * i) * V;
+    if (col >= K) continue;
+    float uu[V], gg[V], bb[V], o[V];
+    unpack(ld16(ur + col), uu, T());
+    unpack(ld16(g + col), gg, T());
+    unpack(ld16(be + col), bb, T());
+#pragma unroll
+    for (int e = 0; e < V; ++e) o[e] = ((x[i][e] - mean) * rstd * gg[e] + bb[e]) * uu[e];
+    st16(zr + col, pack(o, T()));
+  }
+}
+
+template <typename T>
+static hipError_t launch_cand_gate_t(const hstu_desc& d, const int64_t* qoff, int32_t B, int64_t Tq,
+                                     const int32_t* nsplit, const float* part, const hstu_weights& w,
+                                     const void* u, void* z, hipStream_t s) {
+  const int K = d.num_heads * d.dv;
+  const int groups = (K / Elem<T>::kVec + kWave - 1) / kWave;
+  const dim3 grid((unsigned)((Tq + 3) / 4)), block(256);
+#define HSTU_CG(NC_)                                                                                   \
+  if (groups <= NC_) {                                                                                 \
+    hipLaunchKernelGGL((cand_gate_kernel<T, NC_>), grid, block, 0, s, part, qoff, B, Tq, nsplit,        \
+                       (const T*)u, (const T*)w.ln_av_g, (const T*)w.ln_av_b, (T*)z, K, d.ln_eps);    \
+    return hipGetLastError();                                                                          \
+  }
+  HSTU_CG(1)
+  HSTU_CG(2)
+  HSTU_CG(4)
+  HSTU_CG(8)
+  HSTU_CG(16)
+#undef HSTU_CG
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_cand_gate(const hstu_desc& d, const int64_t* qoff, int32_t B, int64_t Tq,
+                            const int32_t* nsplit, const float* part, const hstu_weights& w, const void* u,
+                            void* z, hipStream_t s) {
+  if (Tq == 0) return hipSuccess;
+  if (d.dtype == HSTU_BF16) return launch_cand_gate_t<bf16>(d, qoff, B, Tq, nsplit, part, w, u, z, s);
+  return launch_cand_gate_t<float>(d, qoff, B, Tq, nsplit, part, w, u, z, s);
+}
+
 // f2 for any dtype / width: 128 x 128 tiles.  `out` may alias `x`: each output
 // element is read (residual) and written by the same thread, and nothing else
 // in the kernel reads x.

@@ -98,13 +98,20 @@ hipError_t launch_ln_in(hstu_dtype dt, const void* x, const void* g, const void*
 constexpr int kCostBuckets = 2048;
 constexpr int kTileThreads = 1024;
 
-// Keys a query tile touches: the history keys up to its last row, plus one
-// key block for the candidates' own diagonal; in a cached pass (klen >= 0)
-// the whole cached history of the sequence.
-__device__ __forceinline__ int tile_cost_bucket(const SeqInfo& si, int qt, int bm, int klen) {
+// Keys a work item touches: the history keys up to its tile's last row, plus
+// one key block for the candidates' own diagonal; in a cached pass (klen >= 0)
+// the key blocks of its history chunk.
+__device__ __forceinline__ int tile_cost_bucket(const SeqInfo& si, int qt, int bm, int klen, int ns, int c) {
   int i0 = qt * bm;
   int iend = min(i0 + bm, si.len);
-  int cost = klen >= 0 ? klen : min(iend, si.nhist) + (iend > si.nhist ? kAttnBN : 0);
+  int cost;
+  if (klen >= 0) {
+    int lo, hi;
+    cand_chunk((klen + kAttnBN - 1) / kAttnBN, ns, c, lo, hi);
+    cost = (hi - lo) * kAttnBN;
+  } else {
+    cost = min(iend, si.nhist) + (iend > si.nhist ? kAttnBN : 0);
+  }
   return min(kCostBuckets - 1, cost >> 4);
 }
 
@@ -156,12 +163,14 @@ __global__ __launch_bounds__(kTileThreads) void build_tiles_kernel(const int64_t
                                                                    int2* __restrict__ kblocks,
                                                                    int32_t* __restrict__ tbase,
                                                                    int32_t* __restrict__ kbase,
+                                                                   int32_t* __restrict__ nsplit,
                                                                    int32_t* __restrict__ count) {
   __shared__ int hist[kCostBuckets];
   __shared__ int part[kTileThreads];
   const int tid = threadIdx.x;
   for (int i = tid; i < kCostBuckets; i += kTileThreads) hist[i] = 0;
   auto klen = [&](int b) { return cached ? seq_info(koff, nullptr, b, Tk).len : -1; };
+  auto splits = [&](int b) { return cached ? cand_nsplit(klen(b)) : 1; };
 
   // Per-sequence item counts -> exclusive bases.
   int run_t = 0, run_k = 0;
@@ -170,8 +179,10 @@ __global__ __launch_bounds__(kTileThreads) void build_tiles_kernel(const int64_t
     int nt = 0, nk = 0;
     if (b < B) {
       const SeqInfo si = seq_info(off, ncand, b, T);
-      nt = (si.len + bm - 1) / bm;
+      const int ns = splits(b);
+      nt = (si.len + bm - 1) / bm * ns;
       nk = ((cached ? klen(b) : si.len) + kAttnBN - 1) / kAttnBN;
+      nsplit[b] = ns;
     }
     int tot_t, tot_k;
     const int et = block_exclusive_scan(nt, part, tot_t);
@@ -187,9 +198,10 @@ __global__ __launch_bounds__(kTileThreads) void build_tiles_kernel(const int64_t
   __syncthreads();
 
   // Histogram of tile costs; the key-block list in sequence order.
+  // item k of sequence b: query tile k / ns, history chunk k % ns
   for (int g = tid; g < total; g += kTileThreads) {
-    const int b = owner(tbase, B, g);
-    atomicAdd(&hist[tile_cost_bucket(seq_info(off, ncand, b, T), g - tbase[b], bm, klen(b))], 1);
+    const int b = owner(tbase, B, g), ns = splits(b), k = g - tbase[b];
+    atomicAdd(&hist[tile_cost_bucket(seq_info(off, ncand, b, T), k / ns, bm, klen(b), ns, k % ns)], 1);
   }
   for (int g = tid; g < total_k; g += kTileThreads) {
     const int b = owner(kbase, B, g);
@@ -206,9 +218,10 @@ __global__ __launch_bounds__(kTileThreads) void build_tiles_kernel(const int64_t
   hist[lo] = before + h_hi;
   __syncthreads();
   for (int g = tid; g < total; g += kTileThreads) {
-    const int b = owner(tbase, B, g), qt = g - tbase[b];
-    const int pos = atomicAdd(&hist[tile_cost_bucket(seq_info(off, ncand, b, T), qt, bm, klen(b))], 1);
-    tiles[pos] = make_int2(b, qt);
+    const int b = owner(tbase, B, g), ns = splits(b), k = g - tbase[b];
+    const int qt = k / ns, c = k % ns;
+    const int pos = atomicAdd(&hist[tile_cost_bucket(seq_info(off, ncand, b, T), qt, bm, klen(b), ns, c)], 1);
+    tiles[pos] = make_int2(b, qt | (c << 24));
   }
   if (tid == 0) {
     count[0] = total;
@@ -251,8 +264,8 @@ __global__ __launch_bounds__(256) void block_ts_kernel(const int64_t* __restrict
 hipError_t launch_attn_prep(const AttnRows& r, int bm, const AttnScratch& sc, hipStream_t s) {
   const int64_t max_kb = attn_max_kblocks(r.Tk, r.B);
   hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(kTileThreads), 0, s, r.qoff, r.ncand, r.B, r.Tq, bm, r.koff,
-                     r.Tk, r.cached ? 1 : 0, attn_max_tiles(r.Tq, r.B), sc.tiles, max_kb, sc.kblocks, sc.tbase,
-                     sc.kbase, sc.counts);
+                     r.Tk, r.cached ? 1 : 0, attn_max_items(r.Tq, r.B, r.cached), sc.tiles, max_kb, sc.kblocks,
+                     sc.tbase, sc.kbase, sc.nsplit, sc.counts);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(block_ts_kernel, dim3((unsigned)((max_kb + 3) / 4)), dim3(256), 0, s, r.koff,

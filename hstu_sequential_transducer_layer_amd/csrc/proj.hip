@@ -156,8 +156,10 @@ hipError_t launch_proj(const hstu_desc& d, const void* xn, int64_t T, const void
                        const void* b1, void* u, void* v, void* q, void* k, hipStream_t s) {
   if (T == 0) return hipSuccess;
   const int N = 2 * d.num_heads * (d.dqk + d.dv), K = d.d_model;
-  if (d.dtype == HSTU_BF16 && K % G2::BK == 0) {
-    const int64_t nr = (T + G2::BM - 1) / G2::BM, nc = (N + G2::BN - 1) / G2::BN;
+  const int64_t nr = (T + G2::BM - 1) / G2::BM, nc = (N + G2::BN - 1) / G2::BN;
+  // 256 x 256 tiles unless they would leave most compute units idle; a small
+  // problem (a candidate micro-batch) runs 4x as many 128 x 128 tiles instead
+  if (d.dtype == HSTU_BF16 && K % G2::BK == 0 && nr * nc >= kG2MinTiles) {
     hipLaunchKernelGGL(proj2_kernel, dim3((unsigned)(nr * nc)), dim3(G2::NT), 0, s, (const bf16*)xn,
                        (const bf16*)w1, (const bf16*)b1, (bf16*)u, (bf16*)v, (bf16*)q, (bf16*)k, T, N,
                        K, d.num_heads, d.dqk, d.dv);

@@ -220,7 +220,10 @@ hstu_status hstu_out_fwd(const hstu_desc* desc, const void* x, int64_t total_tok
  *   hist_k         [H, Th, dqk], hist_v [H, Th, dv]: the cache, layer dtype
  *                            (hist_k, hist_v, hist_ts may be NULL when Th = 0)
  *   out            [Tc, d]   may alias x_cand
- *   workspace      >= hstu_cand_workspace_size(desc, Tc, Th, B), 256-aligned
+ *   workspace      >= hstu_cand_workspace_size(desc, Tc, Th, B), 256-aligned;
+ *                            besides the stage buffers it holds the fp32
+ *                            partial AV of up to 8 history chunks per
+ *                            candidate row (32 * Tc * H * dv bytes)
  * Requires HSTU_CAND_SHARED_POS (a candidate's position is then n_b whatever
  * micro-batch it is in); without it returns HSTU_ERR_UNSUPPORTED.
  * HSTU_REUSE_PLAN applies as in hstu_layer_fwd (same micro-batch metadata).  */

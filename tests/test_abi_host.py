@@ -53,9 +53,9 @@ def test_workspace_size_matches_layout(lib):
     a = lambda n: (n + 255) // 256 * 256
     tiles = (T + 127) // 128 + B
     kblocks = (T + 63) // 64 + B
-    # work list, key-block list, two counters, per-sequence tile / key-block bases,
-    # per-row offsets (+64 pad), per-row stats pair
-    attn = a(tiles * 8) + a(kblocks * 8) + a(8) + 2 * a((B + 1) * 4) + a((T + 64) * 4) + a(T * 16)
+    # work list, key-block list, two counters, per-sequence tile / key-block bases
+    # and history split, per-row offsets (+64 pad), per-row stats pair
+    attn = a(tiles * 8) + a(kblocks * 8) + a(8) + 3 * a((B + 1) * 4) + a((T + 64) * 4) + a(T * 16)
     want = (a(T * dm * e) + a(T * H * dv * e) * 3 + a(T * H * dq * e) * 2 + a(T * H * 8)
             + attn)
     assert _lib.workspace_size(d, T, B) == want
@@ -161,11 +161,14 @@ def test_cand_workspace_size_matches_layout(lib):
     d = _desc()
     e, H, dv, dq, dm = 2, 8, 128, 128, 512
     a = lambda n: (n + 255) // 256 * 256
-    # query-side tiles over the candidates, key blocks / offsets / stats over the history
-    attn = (a(((Tc + 127) // 128 + B) * 8) + a(((Th + 63) // 64 + B) * 8) + a(8) + 2 * a((B + 1) * 4)
+    # work items (query tiles x up to 8 history chunks) over the candidates, key
+    # blocks / offsets / stats over the history, then the fp32 partial AV of up
+    # to 8 chunks per candidate row
+    attn = (a(((Tc + 127) // 128 + B) * 8 * 8) + a(((Th + 63) // 64 + B) * 8) + a(8) + 3 * a((B + 1) * 4)
             + a((Th + 64) * 4) + a(Th * 16))
+    part = a(8 * Tc * H * dv * 4)
     want = (a(Tc * dm * e) + a(Tc * H * dv * e) * 3 + a(Tc * H * dq * e) * 2 + a(Tc * H * 8)
-            + attn)
+            + attn + part)
     assert _lib.cand_workspace_size(d, Tc, Th, B) == want
     assert _lib.cand_workspace_size(d, Tc, -1, B) == 0
 

@@ -121,6 +121,16 @@ def test_cached_two_layer_stack_fp32():
     _check_against_full(w, per_seq=8, n_layers=2)
 
 
+def test_cached_long_history_fp32():
+    """Histories split into several chunks (2100 keys: 33 key blocks, the
+    8-chunk cap; 300 keys: 2 chunks; 5 keys: 1), summed by the reduction."""
+    dims = dataclasses.replace(synth.WORKLOADS["small_fp32"].dims, pos_buckets=129, time_buckets=64)
+    w = synth.make_workload("small_fp32", seed=12, lengths=[2100, 300, 5, 0], candidates=[3, 130, 2, 4],
+                            dims=dims, random_ln=True)
+    say(f"cached candidates, long histories (fp32), lengths {w.lengths().tolist()}")
+    _check_against_full(w, per_seq=64)
+
+
 def test_cached_without_history():
     """Sequences made only of candidates (an empty cache, Th = 0): each
     candidate sees itself alone."""
