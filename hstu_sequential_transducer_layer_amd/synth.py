@@ -62,6 +62,7 @@ class LayerDims:
     cand_shared_pos: bool = True    # candidates all sit at position n_b
     ln_eps: float = 1e-5
     norm_len: int = 0               # 0 => divide by the sequence length L_b
+    num_types: int = 0              # > 0: token-type bias table [H, types, types]
 
     @property
     def n1(self) -> int:
@@ -77,6 +78,7 @@ class Workload:
     timestamps: np.ndarray          # [T] int64
     num_candidates: Optional[np.ndarray]  # [B] int32 or None
     layers: List[Dict[str, np.ndarray]] = field(default_factory=list)
+    token_types: Optional[np.ndarray] = None  # [T] uint8 when dims.num_types > 0
 
     @property
     def T(self) -> int:
@@ -103,12 +105,16 @@ class Workload:
         nc = None
         if self.num_candidates is not None:
             nc = self.num_candidates[seqs].copy()
+        ty = None
+        if self.token_types is not None:
+            ty = np.concatenate([self.token_types[int(self.offsets[s]):int(self.offsets[s + 1])]
+                                 for s in seqs] + [np.zeros(0, np.uint8)])
         d = self.dims.d_model
         return Workload(self.name + "[sub]", self.dims,
                         np.concatenate(xs) if xs else np.zeros((0, d), np.float32),
                         off,
                         np.concatenate(ts) if ts else np.zeros((0,), np.int64),
-                        nc, self.layers)
+                        nc, self.layers, ty)
 
 
 @dataclass(frozen=True)
@@ -214,6 +220,9 @@ def draw_layer_params(rng, dims: LayerDims, random_ln: bool = False) -> Dict[str
         p["ln_in_b"] = np.zeros(d, np.float32)
         p["ln_av_g"] = np.ones(hdv, np.float32)
         p["ln_av_b"] = np.zeros(hdv, np.float32)
+    if dims.num_types > 0:   # drawn last, so untyped workloads keep their draws
+        nt = dims.num_types
+        p["type_table"] = _cast(rng.normal(0.0, sd, (H, nt, nt)), dims.dtype)
     return p
 
 
@@ -276,8 +285,20 @@ def make_workload(name: str, seed: int = 0, batch: Optional[int] = None,
     x = _cast(rng.normal(0.0, 1.0, (T, dims.d_model)), dims.dtype)
     # 6. parameters, layer by layer
     layers = [draw_layer_params(rng, dims, random_ln) for _ in range(L)]
+    # 7. token types: with two types, the history interleaves content (0) and
+    #    action (1) tokens and every candidate is content; other counts draw
+    #    uniformly (tests)
+    types = None
+    if dims.num_types > 0:
+        if dims.num_types == 2:
+            types = np.zeros(T, np.uint8)
+            for b in range(B):
+                nh = int(lens[b] - ncand[b]) if has_cand else int(lens[b])
+                types[off[b]:off[b] + nh] = np.arange(nh) % 2
+        else:
+            types = rng.integers(0, dims.num_types, T).astype(np.uint8)
     return Workload(name, dims, x, off, timestamps.astype(np.int64),
-                    ncand.astype(np.int32) if has_cand else None, layers)
+                    ncand.astype(np.int32) if has_cand else None, layers, types)
 
 
 def with_dims(w: Workload, **changes) -> Workload:

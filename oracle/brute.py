@@ -58,8 +58,10 @@ def _ln(row, g, b, eps):
     return [(row[c] - mu) * r * float(g[c]) + float(b[c]) for c in range(n)]
 
 
-def layer(x, offsets, timestamps, num_candidates, prm, cfg):
-    """Returns dict with av, z and y as nested Python lists (all rows)."""
+def layer(x, offsets, timestamps, num_candidates, prm, cfg, token_types=None):
+    """Returns dict with av, z and y as nested Python lists (all rows).  With
+    cfg.num_types > 0 the bias adds type_table[h][type of row t][type of key]."""
+    typed = getattr(cfg, "num_types", 0) > 0
     T = len(x)
     d = cfg.d_model
     H, dqk, dv = cfg.num_heads, cfg.dqk, cfg.dv
@@ -114,6 +116,8 @@ def layer(x, offsets, timestamps, num_candidates, prm, cfg):
                 for c in range(dqk):
                     sc += act[t][Q0 + h * dqk + c] * act[s0 + j][K0 + h * dqk + c]
                 sc += float(prm["pos_table"][h][bp]) + float(prm["time_table"][h][bt])
+                if typed:
+                    sc += float(prm["type_table"][h][int(token_types[t])][int(token_types[s0 + j])])
                 w = _sig_mul(sc) / N
                 for c in range(dv):
                     av[t][h * dv + c] += w * act[s0 + j][V0 + h * dv + c]

@@ -32,7 +32,11 @@ Readings where the pages are silent or disagree (each is a flag or parameter):
     complement int64; dt <= 0 -> 0; else with k = floor(log2 dt),
     bt = min(NB - 1, 1 + k * 2^s + (the s bits below dt's leading one));
   * mask M_ij = (j <= i) and (j < n_b or j == i): causal with the diagonal,
-    candidates see the history and themselves only.
+    candidates see the history and themselves only;
+  * token types ([FRC] 7.1.4 Innovation 2: the bias also depends on the two
+    tokens' types, content or action): when cfg.num_types > 0 the bias gains
+    the additive per-head term type_table[h, type_i, type_j] (query type
+    first), one more table next to the position and time tables.
 
 Pins (tests/): brute-force scalar loops (oracle/brute.py); an independent
 dense torch formulation of the [SRM] "Code" layer; closed forms (prefix sums,
@@ -101,6 +105,11 @@ def attend_mask(i: np.ndarray, j: np.ndarray, n_hist: int) -> np.ndarray:
     return (j <= i) & ((j < n_hist) | (j == i))
 
 
+def type_bias(table_h: np.ndarray, type_q: np.ndarray, type_k: np.ndarray) -> np.ndarray:
+    """Token-type term of one head: table_h[type of query, type of key]."""
+    return np.asarray(table_h, np.float64)[np.asarray(type_q, I64), np.asarray(type_k, I64)]
+
+
 def wrap_sub_i64(a, b):
     """a - b in two's-complement int64 (numpy array subtraction wraps)."""
     with np.errstate(over="ignore"):
@@ -153,13 +162,19 @@ def project(x, prm, cfg):
 
 
 def attention(q, k, v, offsets, timestamps, num_candidates, prm, cfg, rows=None,
-              row_chunk: int = 256):
+              row_chunk: int = 256, token_types=None):
     """Step 3: AV_i^h = (1/N_b) sum_{j: M_ij} SiLU(q_i.k_j + rab_ij^h) v_j^h.
 
     Returns AV [len(rows), H*dv] for the requested flat rows (all rows when
     ``rows`` is None).  Query rows are processed a chunk at a time only to
     bound memory; each row's sum is one matrix product over keys 0..i.
+    With cfg.num_types > 0, rab gains type_table[h, type_i, type_j]
+    (token_types: one type per flat row).
     """
+    typed = getattr(cfg, "num_types", 0) > 0
+    if typed:
+        ty_all = np.asarray(token_types, I64)
+        wy = _f64(prm["type_table"])
     T, H, dqk = q.shape
     dv = v.shape[2]
     off = np.asarray(offsets, I64)
@@ -198,12 +213,14 @@ def attention(q, k, v, offsets, timestamps, num_candidates, prm, cfg, rows=None,
                              cfg.time_buckets, cfg.time_sub_bits)
             for h in range(H):
                 S = q[s0 + ii, h] @ k[s0:s0 + kend, h].T + wp[h][bp] + wt[h][bt]
+                if typed:
+                    S = S + type_bias(wy[h], ty_all[s0 + ii][:, None], ty_all[s0 + jj][None, :])
                 A = np.where(M, silu(S), 0.0) / N
                 out[idx, h] = A @ v[s0:s0 + kend, h]
     return out.reshape(len(rows), H * dv)
 
 
-def layer_forward(x, offsets, timestamps, num_candidates, prm, cfg, rows=None):
+def layer_forward(x, offsets, timestamps, num_candidates, prm, cfg, rows=None, token_types=None):
     """One HSTU layer.  Returns a dict of taps:
 
     u, v, q, k   projections for all rows;
@@ -216,7 +233,8 @@ def layer_forward(x, offsets, timestamps, num_candidates, prm, cfg, rows=None):
     T = x.shape[0]
     u, v, q, k = project(x, prm, cfg)
     sel = np.arange(T, dtype=I64) if rows is None else np.asarray(rows, I64)
-    av = attention(q, k, v, offsets, timestamps, num_candidates, prm, cfg, rows=sel)
+    av = attention(q, k, v, offsets, timestamps, num_candidates, prm, cfg, rows=sel,
+                   token_types=token_types)
     out = gate_and_project(av, u[sel], x[sel], prm, cfg)
     return {"u": u, "v": v, "q": q, "k": k, "av": av, "ln_av": out["ln_av"], "z": out["z"],
             "y": out["y"], "rows": sel}
@@ -242,7 +260,8 @@ def round_to_bf16(a: np.ndarray) -> np.ndarray:
     return np.ldexp(np.round(m * 256.0), e - 8)
 
 
-def stack_forward(x, offsets, timestamps, num_candidates, layers, cfg, io_dtype=None):
+def stack_forward(x, offsets, timestamps, num_candidates, layers, cfg, io_dtype=None,
+                  token_types=None):
     """Layers applied in order, each to the previous output (all rows).
 
     io_dtype="bf16": each layer's output is rounded to bf16 before it becomes
@@ -250,7 +269,8 @@ def stack_forward(x, offsets, timestamps, num_candidates, layers, cfg, io_dtype=
     bf16 tensors; every layer's arithmetic stays float64."""
     h = _f64(x)
     for prm in layers:
-        h = layer_forward(h, offsets, timestamps, num_candidates, prm, cfg)["y"]
+        h = layer_forward(h, offsets, timestamps, num_candidates, prm, cfg,
+                          token_types=token_types)["y"]
         if io_dtype == "bf16":
             h = round_to_bf16(h)
     return h

@@ -410,3 +410,75 @@ def test_bucket_edge_workload_detects_a_wrong_bucket(kind, sub_bits, monkeypatch
     rms = float(np.sqrt(np.mean(ref ** 2)))
     err = float(np.max(np.abs(bad - ref) / np.maximum(np.abs(ref), rms)))
     assert err > 1e-3, (kind, err)
+
+
+# ------------------------------------------------------------- token types
+# Page "HSTU: The First Exploration of the Scaling Law", 7.1.4 Innovation 2:
+# the bias also depends on the query's and the key's token types.
+def _typed_case(n, seed=None):
+    rng = np.random.default_rng(seed if seed is not None else 777 + n)
+    nt = int(rng.choice([1, 2, 3, 5]))
+    dims = synth.LayerDims(8, int(rng.integers(1, 3)), 4, 4, pos_buckets=9, time_buckets=16,
+                           dtype="fp32", num_types=nt, cand_shared_pos=bool(rng.integers(0, 2)))
+    B = int(rng.integers(1, 4))
+    lens = [int(v) for v in rng.integers(1, 9, size=B)]
+    cands = [int(rng.integers(0, L + 1)) for L in lens]
+    w, prm = _tiny(900 + n, [L - m for L, m in zip(lens, cands)], cands, dims)
+    prm["type_table"] = prm["type_table"] * 8.0
+    w.token_types = rng.integers(0, nt, w.T).astype(np.uint8)
+    return w, prm, dims
+
+
+def _typed_brute_pin_holds(cases=range(10)):
+    for n in cases:
+        w, prm, dims = _typed_case(n)
+        ref = brute.layer(w.x, w.offsets, w.timestamps, w.num_candidates, prm, dims, w.token_types)
+        got = O.layer_forward(w.x, w.offsets, w.timestamps, w.num_candidates, prm, dims,
+                              token_types=w.token_types)
+        if not np.allclose(got["y"], np.array(ref["y"]).reshape(got["y"].shape), rtol=0, atol=1e-11):
+            return False
+    return True
+
+
+def test_typed_oracle_matches_brute():
+    assert _typed_brute_pin_holds(range(16))
+
+
+def test_zero_type_table_is_the_untyped_layer():
+    w, prm, dims = _typed_case(3, seed=5)
+    prm["type_table"] = np.zeros_like(prm["type_table"])
+    typed = O.layer_forward(w.x, w.offsets, w.timestamps, w.num_candidates, prm, dims,
+                            token_types=w.token_types)["y"]
+    plain = O.layer_forward(w.x, w.offsets, w.timestamps, w.num_candidates, prm,
+                            dataclasses.replace(dims, num_types=0))["y"]
+    np.testing.assert_array_equal(typed, plain)
+
+
+def test_one_type_equals_shifted_position_table():
+    # every token of type a: the type term is the constant table[h, a, a],
+    # the same as adding it to every entry of the position table
+    dims = synth.LayerDims(8, 2, 4, 4, pos_buckets=9, time_buckets=16, dtype="fp32", num_types=3)
+    w, prm = _tiny(41, [7, 3], [2, 0], dims)
+    prm["type_table"] = prm["type_table"] * 8.0
+    a = 2
+    w.token_types = np.full(w.T, a, np.uint8)
+    typed = O.layer_forward(w.x, w.offsets, w.timestamps, w.num_candidates, prm, dims,
+                            token_types=w.token_types)["y"]
+    shifted = dict(prm)
+    shifted["pos_table"] = prm["pos_table"] + prm["type_table"][:, a, a][:, None]
+    plain = O.layer_forward(w.x, w.offsets, w.timestamps, w.num_candidates, shifted,
+                            dataclasses.replace(dims, num_types=0))["y"]
+    np.testing.assert_allclose(typed, plain, rtol=0, atol=1e-12)
+
+
+def test_planted_type_transpose_is_caught(monkeypatch):
+    real = O.type_bias
+    monkeypatch.setattr(O, "type_bias", lambda t, a, b: real(t, b, a))
+    assert not _typed_brute_pin_holds()
+
+
+def test_interleaved_types_recipe():
+    dims = synth.LayerDims(64, 2, 32, 32, dtype="fp32", num_types=2)
+    w = synth.make_workload("small_fp32", lengths=[5, 0, 4], candidates=[2, 1, 0], dims=dims)
+    np.testing.assert_array_equal(w.token_types, [0, 1, 0, 1, 0, 0, 0, 0, 0, 1, 0, 1])
+    assert w.layers[0]["type_table"].shape == (2, 2, 2)
