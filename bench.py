@@ -22,6 +22,7 @@ bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -292,6 +293,17 @@ def main():
         e.record(stream)
         torch.cuda.synchronize()
         return s.elapsed_time(e) / reps
+    # The same launch with the token-type term: two types, the history
+    # interleaving content (0) and action (1) tokens, a random [H, 2, 2] table.
+    rng = np.random.default_rng(7)
+    types = np.concatenate([np.arange(L) % 2 for L in w.lengths()]).astype(np.uint8)
+    tdims = dataclasses.replace(w.dims, num_types=2)
+    tdesc = _lib.make_desc(tdims)
+    tprm = dict(dev["layers"][0])
+    tprm["type_table"] = torch.from_numpy(synth.round_bf16(
+        rng.normal(0.0, 0.02, (w.dims.num_heads, 2, 2)))).to(x.dtype).cuda()
+    ttypes = torch.from_numpy(types).cuda()
+    typed_ms = timed(lambda: _lib.attn_fwd(tdesc, off, ts, nc, tprm, acts, token_types=ttypes), reps=args.attn_reps)
     proj_ms = timed(lambda: _lib.proj_fwd(desc, x, dev["layers"][0], acts))
     zbuf = torch.empty_like(acts["u"])
     gate_ms = timed(lambda: _lib.gate_fwd(desc, dev["layers"][0], acts, z=zbuf), reps=20)
@@ -362,6 +374,13 @@ def main():
             "f2_tflops_excl_gate": f2_flop / (max(out_ms - gate_ms, 1e-6) * 1e-3) / 1e12,
         },
         "layer_tokens_per_s": T * len(w.layers) / (ms_step * 1e-3),
+        "type_bias": {
+            "what": "hstu_attn_fwd of layer 1 with a 2-type token-type term (interleaved content/action)",
+            "launch_ms": typed_ms,
+            "untyped_launch_ms": attn_ms,
+            "overhead": typed_ms / attn_ms - 1.0,
+            "tflops": attn_flop / (typed_ms * 1e-3) / 1e12,
+        },
     }
     if not args.no_cand:
         rec["cand_inference"] = cand_inference(torch, _lib, layer, synth)

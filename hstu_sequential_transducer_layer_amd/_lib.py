@@ -36,7 +36,7 @@ class HstuDesc(ctypes.Structure):
                 ("pos_buckets", ctypes.c_int32), ("time_buckets", ctypes.c_int32),
                 ("time_sub_bits", ctypes.c_int32), ("dtype", ctypes.c_int),
                 ("flags", ctypes.c_uint32), ("ln_eps", ctypes.c_float),
-                ("norm_len", ctypes.c_int32)]
+                ("norm_len", ctypes.c_int32), ("num_types", ctypes.c_int32)]
 
 
 class HstuWeights(ctypes.Structure):
@@ -46,7 +46,10 @@ class HstuWeights(ctypes.Structure):
 
 class HstuBiasTables(ctypes.Structure):
     _fields_ = [("pos", ctypes.c_void_p), ("time", ctypes.c_void_p),
-                ("pos_head_stride", ctypes.c_int32), ("time_head_stride", ctypes.c_int32)]
+                ("pos_head_stride", ctypes.c_int32), ("time_head_stride", ctypes.c_int32),
+                ("type", ctypes.c_void_p), ("type_head_stride", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("token_types", ctypes.c_void_p),
+                ("hist_types", ctypes.c_void_p)]
 
 
 class HstuActivations(ctypes.Structure):
@@ -130,7 +133,7 @@ def make_desc(dims, flags_extra: int = 0) -> HstuDesc:
     return HstuDesc(dims.d_model, dims.num_heads, dims.dqk, dims.dv, dims.pos_buckets,
                     dims.time_buckets, dims.time_sub_bits,
                     HSTU_BF16 if dims.dtype == "bf16" else HSTU_F32, flags,
-                    float(dims.ln_eps), int(dims.norm_len))
+                    float(dims.ln_eps), int(dims.norm_len), int(getattr(dims, "num_types", 0)))
 
 
 def torch_dtype(desc: HstuDesc) -> torch.dtype:
@@ -142,11 +145,19 @@ def make_weights(prm: Dict[str, torch.Tensor]) -> HstuWeights:
                          ("w1", "b1", "w2", "b2", "ln_in_g", "ln_in_b", "ln_av_g", "ln_av_b")])
 
 
-def make_tables(prm: Dict[str, torch.Tensor]) -> HstuBiasTables:
+def make_tables(prm: Dict[str, torch.Tensor], token_types: Optional[torch.Tensor] = None,
+                hist_types: Optional[torch.Tensor] = None) -> HstuBiasTables:
+    """Tables of one layer; the token-type fields are filled when the layer
+    has a "type_table" ([H, NT, NT], or [NT, NT] shared across heads)."""
     pos, tim = prm["pos_table"], prm["time_table"]
+    typ = prm.get("type_table")
+    tstride = 0
+    if typ is not None and typ.dim() == 3:
+        tstride = typ.shape[1] * typ.shape[2]
     return HstuBiasTables(_ptr(pos), _ptr(tim),
                           pos.shape[-1] if pos.dim() == 2 else 0,
-                          tim.shape[-1] if tim.dim() == 2 else 0)
+                          tim.shape[-1] if tim.dim() == 2 else 0,
+                          _ptr(typ), tstride, 0, _ptr(token_types), _ptr(hist_types))
 
 
 def workspace_size(desc: HstuDesc, T: int, B: int) -> int:
@@ -161,7 +172,8 @@ def layer_fwd(desc: HstuDesc, x: torch.Tensor, seq_offsets: torch.Tensor,
               timestamps: torch.Tensor, num_candidates: Optional[torch.Tensor],
               prm: Dict[str, torch.Tensor], out: Optional[torch.Tensor] = None,
               workspace: Optional[torch.Tensor] = None, weights: Optional[HstuWeights] = None,
-              tables: Optional[HstuBiasTables] = None) -> torch.Tensor:
+              tables: Optional[HstuBiasTables] = None,
+              token_types: Optional[torch.Tensor] = None) -> torch.Tensor:
     """hstu_layer_fwd on torch's current stream; returns `out` ([T, d])."""
     lib = load()
     T, B = x.shape[0], seq_offsets.shape[0] - 1
@@ -171,7 +183,7 @@ def layer_fwd(desc: HstuDesc, x: torch.Tensor, seq_offsets: torch.Tensor,
     if workspace is None or workspace.numel() < need:
         workspace = alloc_workspace(need, x.device)
     w = weights if weights is not None else make_weights(prm)
-    t = tables if tables is not None else make_tables(prm)
+    t = tables if tables is not None else make_tables(prm, token_types)
     _check(lib.hstu_layer_fwd(ctypes.byref(desc), _ptr(x), _ptr(seq_offsets), B, T,
                               _ptr(timestamps), _ptr(num_candidates), ctypes.byref(w),
                               ctypes.byref(t), _ptr(out), _ptr(workspace), workspace.numel(),
@@ -221,13 +233,14 @@ def attn_workspace_size(desc: HstuDesc, T: int, B: int) -> int:
     return int(load().hstu_attn_workspace_size(ctypes.byref(desc), T, B))
 
 
-def attn_fwd(desc: HstuDesc, seq_offsets, timestamps, num_candidates, prm, acts, workspace=None):
+def attn_fwd(desc: HstuDesc, seq_offsets, timestamps, num_candidates, prm, acts, workspace=None,
+             token_types=None):
     lib = load()
     T, B = acts["u"].shape[0], seq_offsets.shape[0] - 1
     need = attn_workspace_size(desc, T, B)
     ws = workspace if workspace is not None and workspace.numel() >= need else \
         alloc_workspace(need, acts["u"].device)
-    a, t = _acts(acts), make_tables(prm)
+    a, t = _acts(acts), make_tables(prm, token_types)
     _check(lib.hstu_attn_fwd(ctypes.byref(desc), _ptr(seq_offsets), B, T, _ptr(timestamps),
                              _ptr(num_candidates), ctypes.byref(t), ctypes.byref(a), _ptr(ws),
                              ws.numel(), _stream()))
@@ -268,7 +281,8 @@ def cand_fwd(desc: HstuDesc, x_cand: torch.Tensor, cand_offsets: torch.Tensor,
              hist_ts: torch.Tensor, hist_k: torch.Tensor, hist_v: torch.Tensor,
              prm: Dict[str, torch.Tensor], out: Optional[torch.Tensor] = None,
              workspace: Optional[torch.Tensor] = None, weights: Optional[HstuWeights] = None,
-             tables: Optional[HstuBiasTables] = None) -> torch.Tensor:
+             tables: Optional[HstuBiasTables] = None, cand_types: Optional[torch.Tensor] = None,
+             hist_types: Optional[torch.Tensor] = None) -> torch.Tensor:
     """hstu_cand_fwd on torch's current stream; returns `out` ([Tc, d])."""
     lib = load()
     Tc, B = x_cand.shape[0], cand_offsets.shape[0] - 1
@@ -279,7 +293,7 @@ def cand_fwd(desc: HstuDesc, x_cand: torch.Tensor, cand_offsets: torch.Tensor,
     if workspace is None or workspace.numel() < need:
         workspace = alloc_workspace(need, x_cand.device)
     w = weights if weights is not None else make_weights(prm)
-    t = tables if tables is not None else make_tables(prm)
+    t = tables if tables is not None else make_tables(prm, cand_types, hist_types)
     _check(lib.hstu_cand_fwd(ctypes.byref(desc), _ptr(x_cand), _ptr(cand_offsets), B, Tc,
                              _ptr(cand_ts), _ptr(num_candidates), _ptr(hist_offsets), Th,
                              _ptr(hist_ts), _ptr(hist_k), _ptr(hist_v), ctypes.byref(w),

@@ -61,6 +61,8 @@ hstu_status check_desc(const hstu_desc* d) {
   if (!(d->ln_eps > 0.f) || !std::isfinite(d->ln_eps))
     return fail(HSTU_ERR_INVALID_ARG, "ln_eps must be positive and finite");
   if (d->norm_len < 0) return fail(HSTU_ERR_INVALID_ARG, "norm_len %d < 0", d->norm_len);
+  if (d->num_types < 0 || d->num_types > 16)
+    return fail(HSTU_ERR_UNSUPPORTED, "num_types %d: must be in [0, 16]", d->num_types);
   return HSTU_OK;
 }
 
@@ -96,7 +98,21 @@ hstu_status check_tables(const hstu_desc* d, const hstu_bias_tables* t) {
     return fail(HSTU_ERR_INVALID_ARG, "pos_head_stride %d < pos_buckets %d", t->pos_head_stride, d->pos_buckets);
   if (t->time_head_stride != 0 && t->time_head_stride < d->time_buckets)
     return fail(HSTU_ERR_INVALID_ARG, "time_head_stride %d < time_buckets %d", t->time_head_stride, d->time_buckets);
+  if (d->num_types > 0) {
+    const int nt2 = d->num_types * d->num_types;
+    HSTU_REQ(t->type, esize(d->dtype), "tables->type");
+    if (t->token_types == nullptr) return fail(HSTU_ERR_INVALID_ARG, "tables->token_types is NULL");
+    if (t->type_head_stride < 0 || (t->type_head_stride != 0 && t->type_head_stride < nt2))
+      return fail(HSTU_ERR_INVALID_ARG, "type_head_stride %d: must be 0 or >= num_types^2 = %d",
+                  t->type_head_stride, nt2);
+    if (t->reserved != 0) return fail(HSTU_ERR_INVALID_ARG, "tables->reserved must be 0");
+  }
   return HSTU_OK;
+}
+
+hstu::AttnTypes layer_types(const hstu_desc* d, const hstu_bias_tables* t) {
+  if (d->num_types == 0) return hstu::AttnTypes{nullptr, nullptr, 0};
+  return hstu::AttnTypes{t->token_types, t->token_types, d->num_types};
 }
 
 hstu_status check_proj_weights(const hstu_desc* d, const hstu_weights* w) {
@@ -247,7 +263,7 @@ static hstu_status run_attn(const hstu_desc* d, const int64_t* off, int32_t B, i
                             const int64_t* ts, const int32_t* nc, const hstu_bias_tables* t,
                             const hstu_activations* a, void* scratch, hipStream_t s) {
   const hstu::AttnScratch sc = hstu::attn_scratch(scratch, T, B);
-  const hstu::AttnRows rows{off, nc, ts, T, off, ts, T, nullptr, B, false};
+  const hstu::AttnRows rows{off, nc, ts, T, off, ts, T, nullptr, B, false, layer_types(d, t)};
   if (!(d->flags & HSTU_REUSE_PLAN)) {
     const hstu_status st = device(hstu::launch_attn_prep(rows, hstu::kAttnBM, sc, s), "attention prep launch");
     if (st != HSTU_OK) return st;
@@ -393,6 +409,8 @@ hstu_status hstu_cand_fwd(const hstu_desc* desc, const void* x, const int64_t* c
     HSTU_REQ(hk, 16, "hist_k");
     HSTU_REQ(hv, 16, "hist_v");
     HSTU_REQ(hts, 8, "hist_ts");
+    if (desc->num_types > 0 && tables && !tables->hist_types)
+      return fail(HSTU_ERR_INVALID_ARG, "tables->hist_types is NULL");
   }
   if ((st = check_proj_weights(desc, w)) != HSTU_OK) return st;
   if ((st = check_out_weights(desc, w)) != HSTU_OK) return st;
@@ -415,7 +433,10 @@ hstu_status hstu_cand_fwd(const hstu_desc* desc, const void* x, const int64_t* c
   a.av_stats = (float*)(base + L.stats);
   if ((st = run_proj(desc, x, Tc, w, &a, base + L.xn, s)) != HSTU_OK) return st;
   const hstu::AttnScratch sc = hstu::attn_scratch(base + L.attn, Tc, Th, B, true);
-  const hstu::AttnRows rows{coff, nullptr, cts, Tc, hoff, hts, Th, mtotal, B, true};
+  const hstu::AttnTypes types = desc->num_types > 0
+                                    ? hstu::AttnTypes{tables->token_types, tables->hist_types, desc->num_types}
+                                    : hstu::AttnTypes{nullptr, nullptr, 0};
+  const hstu::AttnRows rows{coff, nullptr, cts, Tc, hoff, hts, Th, mtotal, B, true, types};
   if (!(desc->flags & HSTU_REUSE_PLAN))
     if ((st = device(hstu::launch_attn_prep(rows, hstu::kAttnBM, sc, s), "attention prep launch")) != HSTU_OK)
       return st;

@@ -78,6 +78,10 @@ struct AttnArgs {
   float* stats;
   float* part;             // cached: per-chunk partial AV [kCandMaxSplit][T][H * DV]
   const int32_t* nsplit;   // cached: history chunks per sequence
+  const uint8_t* qtypes;   // typed: query rows' token types
+  const int32_t* kty;      // typed: key rows' token types (int32, clamped)
+  const void* type_tab;    // typed: [NT][NT] per head
+  int NT, type_stride;
   const int2* tiles;
   const int32_t* counts;   // [0]: work items
   const int32_t* rel;      // per key row: offset from its key block's earliest timestamp
@@ -410,14 +414,20 @@ __device__ __forceinline__ void attn_store(f32x16 (&o)[DV / 32], float inv_n, bo
 }
 
 // Workgroups per CU the register budget is sized for: three (at most 168
-// VGPRs per lane) when a q row plus a k row take at most 256 bytes, else two.
+// VGPRs per lane) when a q row plus a k row take at most 256 bytes, else two
+// (the token-type step's operands count as 64 bytes more).
 constexpr int attn_min_blocks(int row_bytes) { return row_bytes <= 256 ? 3 : 2; }
 
 // CACHED: the queries are candidates only, the keys a cached history of the
 // same sequences; every candidate attends the whole history and itself (the
 // self term is added in the epilogue), with the shared candidate position.
-template <typename T, int DQK, int DV, bool CACHED>
-__global__ __launch_bounds__(256, attn_min_blocks((DQK + DV) * (int)sizeof(T))) void attn_kernel(AttnArgs a) {
+// TYPED: the bias gains the token-type term table[type_i][type_j], added by
+// one more k16 MFMA step per 32-key half: the keys' one-hot types times each
+// query row's table row (exact: one-hot entries, table values in the layer
+// dtype, fp32 accumulation).
+template <typename T, int DQK, int DV, bool CACHED, bool TYPED>
+__global__ __launch_bounds__(256, attn_min_blocks((DQK + DV) * (int)sizeof(T) + (TYPED ? 64 : 0))) void attn_kernel(
+    AttnArgs a) {
   typedef AttnCfg<T, DQK, DV> C;
   static_assert(C::NT == 256, "launch bounds assume 4 waves");
   typedef typename Elem<T>::Frag Frag;
@@ -427,9 +437,11 @@ __global__ __launch_bounds__(256, attn_min_blocks((DQK + DV) * (int)sizeof(T))) 
   __shared__ __attribute__((aligned(16))) T Vs0[C::BN * DV];
   __shared__ __attribute__((aligned(16))) T Vs1[C::BN * DV];
   __shared__ __attribute__((aligned(16))) int32_t rel_s[2][C::BN];
-  extern __shared__ float tabs[];  // [P] position table then [NB] time table, head h
+  __shared__ __attribute__((aligned(16))) int32_t kty_s[2][TYPED ? C::BN : 1];
+  extern __shared__ float tabs[];  // [P] position, [NB] time, [NT * NT] type table of head h
   float* pos_s = tabs;
   float* time_s = tabs + a.P;
+  float* type_s = tabs + a.P + a.NB;
 
   const int H = a.H;
   const int h = blockIdx.x % H;
@@ -476,26 +488,32 @@ __global__ __launch_bounds__(256, attn_min_blocks((DQK + DV) * (int)sizeof(T))) 
   // K, V and the keys' time offsets of block `blk` into buffer set (Kb, Vb, rb),
   // and the block's earliest / latest timestamp into tb (read before the
   // copies, so the wait that covers them covers it too).
-  auto issue = [&](int blk, T* Kb, T* Vb, int32_t* rb, longlong2& tb) __attribute__((always_inline)) {
+  auto issue = [&](int blk, T* Kb, T* Vb, int32_t* rb, int32_t* yb, longlong2& tb) __attribute__((always_inline)) {
     const int j0 = block_start(blk);
     tb = *reinterpret_cast<const longlong2*>(a.tstat + 2 * (k0 + j0));
     kcopy.issue(kg + (int64_t)j0 * DQK, L - j0, Kb, w);
     vcopy.issue(vg + (int64_t)j0 * DV, L - j0, Vb, w);
-    // the offsets array has kAttnBN rows of padding past T, so this never
-    // reads outside it; offsets of rows past the sequence are never used
+    // the offsets and types arrays have kAttnBN rows of padding past the key
+    // rows, so these never read outside them; entries of rows past the
+    // sequence are never used
     if (w == 0)
       __builtin_amdgcn_global_load_lds((glb_void*)(a.rel + k0 + j0 + lane), (lds_void*)rb, 4, 0, 0);
+    if (TYPED && w == 1)
+      __builtin_amdgcn_global_load_lds((glb_void*)(a.kty + k0 + j0 + lane), (lds_void*)yb, 4, 0, 0);
   };
 
   // Issue the first block's copies before anything else.
   longlong2 tb0 = {0, 0}, tb1 = {0, 0};
-  if (nblk > 0) issue(0, Ks0, Vs0, rel_s[0], tb0);
+  if (nblk > 0) issue(0, Ks0, Vs0, rel_s[0], kty_s[0], tb0);
 
   // Bias tables of head h, as fp32, into LDS.
   for (int i = tid; i < a.P; i += C::NT)
     pos_s[i] = to_f32(reinterpret_cast<const T*>(a.pos_tab)[(int64_t)h * a.pos_stride + i]);
   for (int i = tid; i < a.NB; i += C::NT)
     time_s[i] = to_f32(reinterpret_cast<const T*>(a.time_tab)[(int64_t)h * a.time_stride + i]);
+  if (TYPED)
+    for (int i = tid; i < a.NT * a.NT; i += C::NT)
+      type_s[i] = to_f32(reinterpret_cast<const T*>(a.type_tab)[(int64_t)h * a.type_stride + i]);
 
   // This lane's query row and its operand fragments.
   const int r0 = i0 + 32 * w;
@@ -526,13 +544,24 @@ __global__ __launch_bounds__(256, attn_min_blocks((DQK + DV) * (int)sizeof(T))) 
   __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of block 0 have landed
   __syncthreads();                // ... and every other wave's, plus tables
   const float cpos_far = pos_s[2 * R];  // bias of every pair at distance >= R
+  // typed: this lane's query row of the type table, as the B operand of the
+  // type step (k = key type 8 * half + e)
+  const int ty_q = TYPED && qvalid ? min((int)a.qtypes[s0 + iq], a.NT - 1) : 0;
+  Frag wrow{};
+  if (TYPED) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int c = 8 * half + e;
+      wrow[e] = from_f32<T>(c < a.NT ? type_s[ty_q * a.NT + c] : 0.f);
+    }
+  }
 
   // One block of work out of buffer set (Kb, Vb, rb).
   const QueryRow qr = CACHED ? QueryRow{nh - 1, nh - 1, nh - 1, p_q, pmin_q, qvalid, ts_q}
                              : QueryRow{r0, rlast, iq, p_q, pmin_q, qvalid, ts_q};
   const SeqCtx sq{L, nh, R, a.NB, a.sbits, shared, cpos_far, pos_s, time_s, a.kts + k0};
-  auto consume = [&](int blk, const T* Kb, const T* Vb, const int32_t* rb, int64_t tmin, int64_t tmax)
-                     __attribute__((always_inline)) {
+  auto consume = [&](int blk, const T* Kb, const T* Vb, const int32_t* rb, const int32_t* yb, int64_t tmin,
+                     int64_t tmax) __attribute__((always_inline)) {
     const int j0 = block_start(blk);
     if (!wave_rows || !block_active(j0, qr, sq)) return;
     ElemCtx x;
@@ -545,6 +574,15 @@ __global__ __launch_bounds__(256, attn_min_blocks((DQK + DV) * (int)sizeof(T))) 
 #pragma unroll
       for (int c = 0; c < DQK / 16; ++c)
         sc = mma_k16(k_frag<T, DQK>(Kb, kh * 32 + l32, 16 * c + 8 * half), qf[c], sc);
+      if (TYPED) {
+        // one-hot of key kh * 32 + l32's type over k = 8 * half + e (a type
+        // outside [0, 16), e.g. in a padding row, gives zeros)
+        const int kt = yb[kh * 32 + l32] - 8 * half;
+        Frag oh;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) oh[e] = from_f32<T>(kt == e ? 1.f : 0.f);
+        sc = mma_k16(oh, wrow, sc);
+      }
       Frag vf[2][DV / 32];
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2)
@@ -569,15 +607,15 @@ __global__ __launch_bounds__(256, attn_min_blocks((DQK + DV) * (int)sizeof(T))) 
   // completed (after the wait that precedes each barrier).
   int64_t tmin0 = uniform64(tb0.x), tmax0 = uniform64(tb0.y), tmin1 = 0, tmax1 = 0;
   for (int blk = 0; blk < nblk; blk += 2) {
-    if (blk + 1 < nblk) issue(blk + 1, Ks1, Vs1, rel_s[1], tb1);
-    consume(blk, Ks0, Vs0, rel_s[0], tmin0, tmax0);
+    if (blk + 1 < nblk) issue(blk + 1, Ks1, Vs1, rel_s[1], kty_s[1], tb1);
+    consume(blk, Ks0, Vs0, rel_s[0], kty_s[0], tmin0, tmax0);
     if (blk + 1 >= nblk) break;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     tmin1 = uniform64(tb1.x);
     tmax1 = uniform64(tb1.y);
-    if (blk + 2 < nblk) issue(blk + 2, Ks0, Vs0, rel_s[0], tb0);
-    consume(blk + 1, Ks1, Vs1, rel_s[1], tmin1, tmax1);
+    if (blk + 2 < nblk) issue(blk + 2, Ks0, Vs0, rel_s[0], kty_s[0], tb0);
+    consume(blk + 1, Ks1, Vs1, rel_s[1], kty_s[1], tmin1, tmax1);
     if (blk + 2 >= nblk) break;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -598,7 +636,7 @@ __global__ __launch_bounds__(256, attn_min_blocks((DQK + DV) * (int)sizeof(T))) 
       for (int e = 0; e < 8; ++e) dot += to_f32(qf[c][e]) * to_f32(kf[e]);
     }
     dot += __shfl_xor(dot, 32, kWave);
-    const float wself = silu(dot + pos_s[R] + time_s[0]);
+    const float wself = silu(dot + pos_s[R] + time_s[0] + (TYPED ? type_s[ty_q * a.NT + ty_q] : 0.f));
     const T* vs = reinterpret_cast<const T*>(a.qv) + ((int64_t)h * a.T + s0 + iq) * DV;
 #pragma unroll
     for (int n = 0; n < DV / 32; ++n)
@@ -623,13 +661,17 @@ __global__ __launch_bounds__(256, attn_min_blocks((DQK + DV) * (int)sizeof(T))) 
 
 template <typename T, int DQK, int DV>
 static hipError_t launch_t(const AttnArgs& a, bool cached, int64_t grid, hipStream_t s) {
-  const size_t shmem = (size_t)(a.P + a.NB) * sizeof(float);
-  if (cached)
-    hipLaunchKernelGGL((attn_kernel<T, DQK, DV, true>), dim3((unsigned)grid), dim3(AttnCfg<T, DQK, DV>::NT),
-                       shmem, s, a);
+  const bool typed = a.NT > 0;
+  const size_t shmem = (size_t)(a.P + a.NB + (typed ? a.NT * a.NT : 0)) * sizeof(float);
+  const dim3 g((unsigned)grid), b(AttnCfg<T, DQK, DV>::NT);
+  if (cached && typed)
+    hipLaunchKernelGGL((attn_kernel<T, DQK, DV, true, true>), g, b, shmem, s, a);
+  else if (cached)
+    hipLaunchKernelGGL((attn_kernel<T, DQK, DV, true, false>), g, b, shmem, s, a);
+  else if (typed)
+    hipLaunchKernelGGL((attn_kernel<T, DQK, DV, false, true>), g, b, shmem, s, a);
   else
-    hipLaunchKernelGGL((attn_kernel<T, DQK, DV, false>), dim3((unsigned)grid), dim3(AttnCfg<T, DQK, DV>::NT),
-                       shmem, s, a);
+    hipLaunchKernelGGL((attn_kernel<T, DQK, DV, false, false>), g, b, shmem, s, a);
   return hipGetLastError();
 }
 
@@ -666,6 +708,11 @@ static hipError_t launch_attn_impl(const hstu_desc& d, const AttnRows& r, const 
   AttnArgs a;
   a.part = part;
   a.nsplit = sc.nsplit;
+  a.NT = r.types.nt;
+  a.qtypes = r.types.q;
+  a.kty = sc.kty;
+  a.type_tab = tab.type;
+  a.type_stride = tab.type_head_stride;
   a.off = r.qoff;
   a.ncand = r.ncand;
   a.ts = r.qts;

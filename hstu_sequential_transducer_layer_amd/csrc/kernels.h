@@ -53,6 +53,7 @@ inline int64_t attn_max_kblocks(int64_t T, int32_t B) { return (T + kAttnBN - 1)
 //   rel     int32 [Tk + kAttnBN]: ts[row] - (earliest timestamp of its key block)
 //   tstat   int64 [Tk][2]: at each key block's first row, the block's
 //           earliest and latest timestamps (other rows unused)
+//   kty     int32 [Tk + kAttnBN]: key rows' token types (typed layers)
 struct AttnScratch {
   int2* tiles;
   int2* kblocks;
@@ -62,6 +63,7 @@ struct AttnScratch {
   int32_t* nsplit;
   int32_t* rel;
   int64_t* tstat;
+  int32_t* kty;
 };
 
 inline size_t attn_align(size_t n) { return (n + 255) & ~(size_t)255; }
@@ -69,7 +71,7 @@ inline size_t attn_align(size_t n) { return (n + 255) & ~(size_t)255; }
 inline size_t attn_scratch_bytes(int64_t Tq, int64_t Tk, int32_t B, bool cached) {
   return attn_align((size_t)attn_max_items(Tq, B, cached) * 8) + attn_align((size_t)attn_max_kblocks(Tk, B) * 8) +
          attn_align(2 * sizeof(int32_t)) + 3 * attn_align(((size_t)B + 1) * 4) +
-         attn_align((size_t)(Tk + kAttnBN) * 4) + attn_align((size_t)Tk * 16);
+         2 * attn_align((size_t)(Tk + kAttnBN) * 4) + attn_align((size_t)Tk * 16);
 }
 inline size_t attn_scratch_bytes(int64_t T, int32_t B) { return attn_scratch_bytes(T, T, B, false); }
 
@@ -91,6 +93,8 @@ inline AttnScratch attn_scratch(void* base, int64_t Tq, int64_t Tk, int32_t B, b
   a.rel = (int32_t*)p;
   p += attn_align((size_t)(Tk + kAttnBN) * 4);
   a.tstat = (int64_t*)p;
+  p += attn_align((size_t)Tk * 16);
+  a.kty = (int32_t*)p;
   return a;
 }
 inline AttnScratch attn_scratch(void* base, int64_t T, int32_t B) { return attn_scratch(base, T, T, B, false); }
@@ -100,6 +104,13 @@ inline AttnScratch attn_scratch(void* base, int64_t T, int32_t B) { return attn_
 inline size_t cand_partial_bytes(int64_t Tq, int H, int dv) {
   return attn_align((size_t)kCandMaxSplit * (size_t)Tq * (size_t)H * (size_t)dv * 4);
 }
+
+// Token types of a pass (num_types > 0): the query rows' and the key rows'.
+struct AttnTypes {
+  const uint8_t* q;
+  const uint8_t* k;
+  int nt;  // 0: no type term
+};
 
 // The rows an attention pass reads.  Query rows: sequence b is
 // [qoff[b], qoff[b + 1]) of the query-side tensors, its last ncand[b] rows
@@ -118,6 +129,7 @@ struct AttnRows {
   const int32_t* mtotal;  // cached pass only
   int32_t B;
   bool cached;
+  AttnTypes types;
 };
 
 // --- prep.hip

@@ -231,14 +231,17 @@ __global__ __launch_bounds__(kTileThreads) void build_tiles_kernel(const int64_t
 
 // One wave per key block: min / max of its timestamps and each key's offset
 // from the min (meaningful when the block spans at most INT32_MAX; the
-// attention kernel checks that from tstat before using rel).
+// attention kernel checks that from tstat before using rel); with token types
+// (nt > 0) each key's type, clamped to nt - 1, as int32.
 __global__ __launch_bounds__(256) void block_ts_kernel(const int64_t* __restrict__ off,
                                                        const int32_t* __restrict__ ncand, int64_t T,
                                                        const int64_t* __restrict__ ts,
                                                        const int2* __restrict__ kblocks,
                                                        const int32_t* __restrict__ count,
                                                        int32_t* __restrict__ rel,
-                                                       int64_t* __restrict__ tstat) {
+                                                       int64_t* __restrict__ tstat,
+                                                       const uint8_t* __restrict__ types, int nt,
+                                                       int32_t* __restrict__ kty) {
   const int lane = threadIdx.x & 63;
   const int64_t id = (int64_t)blockIdx.x * 4 + wave_id();
   if (id >= count[1]) return;  // whole wave leaves together
@@ -255,6 +258,7 @@ __global__ __launch_bounds__(256) void block_ts_kernel(const int64_t* __restrict
     mx = omx > mx ? omx : mx;
   }
   if (valid) rel[si.start + j] = (int32_t)(uint32_t)((uint64_t)t - (uint64_t)mn);
+  if (valid && nt > 0) kty[si.start + j] = min((int)types[si.start + j], nt - 1);
   if (lane == 0) {
     tstat[2 * (si.start + e.y * kAttnBN)] = mn;
     tstat[2 * (si.start + e.y * kAttnBN) + 1] = mx;
@@ -269,7 +273,8 @@ hipError_t launch_attn_prep(const AttnRows& r, int bm, const AttnScratch& sc, hi
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(block_ts_kernel, dim3((unsigned)((max_kb + 3) / 4)), dim3(256), 0, s, r.koff,
-                     (const int32_t*)nullptr, r.Tk, r.kts, sc.kblocks, sc.counts, sc.rel, sc.tstat);
+                     (const int32_t*)nullptr, r.Tk, r.kts, sc.kblocks, sc.counts, sc.rel, sc.tstat, r.types.k,
+                     r.types.nt, sc.kty);
   return hipGetLastError();
 }
 

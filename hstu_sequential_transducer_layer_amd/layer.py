@@ -28,6 +28,8 @@ def to_device(w, device="cuda") -> Dict[str, object]:
                            torch.from_numpy(np.ascontiguousarray(w.num_candidates)).to(device)),
         "layers": [{k: torch.from_numpy(np.ascontiguousarray(v)).to(device=device, dtype=dt)
                     for k, v in prm.items()} for prm in w.layers],
+        "token_types": (None if getattr(w, "token_types", None) is None else
+                        torch.from_numpy(np.ascontiguousarray(w.token_types)).to(device)),
     }
     return d
 
@@ -45,6 +47,7 @@ class HSTUStack:
         self._tables = [_lib.make_tables(p) for p in layers]
         self._ws: Optional[torch.Tensor] = None
         self._bufs: List[torch.Tensor] = []
+        self._types: Optional[torch.Tensor] = None
 
     def workspace(self, T: int, B: int, device) -> torch.Tensor:
         need = _lib.workspace_size(self.desc, T, B)
@@ -52,9 +55,14 @@ class HSTUStack:
             self._ws = _lib.alloc_workspace(need, device)
         return self._ws
 
-    def forward(self, x, offsets, timestamps, num_candidates=None, out=None) -> torch.Tensor:
+    def forward(self, x, offsets, timestamps, num_candidates=None, out=None,
+                token_types=None) -> torch.Tensor:
+        """token_types: [T] uint8 when the layers have a type table."""
         T, B = x.shape[0], offsets.shape[0] - 1
         ws = self.workspace(T, B, x.device)
+        if token_types is not self._types:
+            self._types = token_types
+            self._tables = [_lib.make_tables(p, token_types) for p in self.layers]
         if len(self._bufs) != 2 or self._bufs[0].shape != x.shape or self._bufs[0].dtype != x.dtype:
             self._bufs = [torch.empty_like(x), torch.empty_like(x)]
         h = x
@@ -119,11 +127,12 @@ class CachedRanker:
         self.cache: List[Dict[str, torch.Tensor]] = []
         self._ws: Optional[torch.Tensor] = None
 
-    def encode_history(self, x_hist, hist_offsets, hist_ts, need_output: bool = False):
+    def encode_history(self, x_hist, hist_offsets, hist_ts, need_output: bool = False,
+                       hist_types=None):
         """Fills the per-layer K/V cache.  The last layer's attention and output
         stage only matter for the history's own output, returned when
         need_output (else None)."""
-        self.hist_offsets, self.hist_ts = hist_offsets, hist_ts
+        self.hist_offsets, self.hist_ts, self.hist_types = hist_offsets, hist_ts, hist_types
         self.cache = []
         h = x_hist
         for n, prm in enumerate(self.layers):
@@ -131,11 +140,12 @@ class CachedRanker:
             self.cache.append({"k": acts["k"], "v": acts["v"]})
             if n == len(self.layers) - 1 and not need_output:
                 return None
-            _lib.attn_fwd(self.desc, hist_offsets, hist_ts, None, prm, acts)
+            _lib.attn_fwd(self.desc, hist_offsets, hist_ts, None, prm, acts, token_types=hist_types)
             h, _ = _lib.out_fwd(self.desc, h, prm, acts)
         return h
 
-    def score(self, x_cand, cand_offsets, cand_ts, num_candidates, out=None) -> torch.Tensor:
+    def score(self, x_cand, cand_offsets, cand_ts, num_candidates, out=None,
+              cand_types=None) -> torch.Tensor:
         """The last layer's output rows of one candidate micro-batch;
         num_candidates[b] counts the sequence's candidates over all micro-batches."""
         Tc, B = x_cand.shape[0], cand_offsets.shape[0] - 1
@@ -146,8 +156,10 @@ class CachedRanker:
         for n, prm in enumerate(self.layers):
             last = n == len(self.layers) - 1
             dst = out if (last and out is not None) else torch.empty_like(x_cand)
+            tables = self._tables[n] if cand_types is None else \
+                _lib.make_tables(prm, cand_types, self.hist_types)
             _lib.cand_fwd(self.desc, h, cand_offsets, cand_ts, num_candidates, self.hist_offsets,
                           self.hist_ts, self.cache[n]["k"], self.cache[n]["v"], prm, out=dst,
-                          workspace=self._ws, weights=self._weights[n], tables=self._tables[n])
+                          workspace=self._ws, weights=self._weights[n], tables=tables)
             h = dst
         return h

@@ -30,7 +30,8 @@
  *   dt      = ts[i] - ts[j]  (int64 seconds, two's-complement wrap)
  *   bt      = dt <= 0 ? 0 : min(NB - 1, 1 + (k << s) + sub),  k = floor(log2 dt),
  *             sub = the s = time_sub_bits bits right below dt's leading one
- *   AV_i^h  = (1/N_b) sum_j M_ij SiLU(q_i^h . k_j^h + pos[h][bp] + time[h][bt]) v_j^h
+ *   rab     = pos[h][bp] + time[h][bt] (+ type[h][ty(i)][ty(j)] if num_types > 0)
+ *   AV_i^h  = (1/N_b) sum_j M_ij SiLU(q_i^h . k_j^h + rab) v_j^h
  *             N_b = L_b, or norm_len when norm_len > 0 (no 1/sqrt(d) scale)
  *   Z       = LayerNorm_av(concat_h AV^h) * u   (over H*dv, biased variance)
  *   Y       = Z W2^T + b2 (+ x if HSTU_RESIDUAL)
@@ -106,6 +107,7 @@ typedef struct {
   uint32_t flags;        /* HSTU_* bits                                         */
   float ln_eps;          /* LayerNorm epsilon (> 0), e.g. 1e-5                  */
   int32_t norm_len;      /* 0: divide by L_b; > 0: divide by this constant      */
+  int32_t num_types;     /* 0: no token-type term; 1..16: token types (below)  */
 } hstu_desc;
 
 /* Layer parameters, nn.Linear layouts (row n of W is output feature n).      */
@@ -121,12 +123,25 @@ typedef struct {
 } hstu_weights;
 
 /* Relative-attention-bias tables.  Entry (h, idx) is at ptr[h*stride + idx];
- * a head stride of 0 shares one table across heads.                          */
+ * a head stride of 0 shares one table across heads.
+ *
+ * Token-type term ([FRC] 7.1.4 Innovation 2: the bias also depends on the
+ * two tokens' types, e.g. content and action tokens), used when
+ * desc->num_types = NT > 0: the bias gains type[h*type_head_stride + a*NT + b]
+ * for a query of type a and a key of type b.  token_types gives each row's
+ * type (uint8, values >= NT are taken as NT - 1); in hstu_cand_fwd it holds
+ * the candidates' types and hist_types the cached history rows' types.  All
+ * type fields are ignored when num_types = 0.                               */
 typedef struct {
   const void* pos;   /* >= [P]  position-difference table                      */
   const void* time;  /* >= [NB] log-bucketed time-difference table             */
   int32_t pos_head_stride;
   int32_t time_head_stride;
+  const void* type;  /* >= [NT * NT] token-type table (layer dtype)            */
+  int32_t type_head_stride;       /* 0, or >= NT * NT                          */
+  int32_t reserved;               /* must be 0                                 */
+  const uint8_t* token_types;     /* [T] (query rows)                          */
+  const uint8_t* hist_types;      /* [Th] hstu_cand_fwd only                   */
 } hstu_bias_tables;
 
 /* Intermediate activations, the hand-off between the three stages.          */

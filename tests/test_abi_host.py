@@ -55,7 +55,8 @@ def test_workspace_size_matches_layout(lib):
     kblocks = (T + 63) // 64 + B
     # work list, key-block list, two counters, per-sequence tile / key-block bases
     # and history split, per-row offsets (+64 pad), per-row stats pair
-    attn = a(tiles * 8) + a(kblocks * 8) + a(8) + 3 * a((B + 1) * 4) + a((T + 64) * 4) + a(T * 16)
+    attn = a(tiles * 8) + a(kblocks * 8) + a(8) + 3 * a((B + 1) * 4) + a((T + 64) * 4) + a(T * 16) \
+        + a((T + 64) * 4)   # key rows' token types
     want = (a(T * dm * e) + a(T * H * dv * e) * 3 + a(T * H * dq * e) * 2 + a(T * H * 8)
             + attn)
     assert _lib.workspace_size(d, T, B) == want
@@ -91,6 +92,8 @@ def _call(lib, desc, T=1000, B=4, x=FAKE, off=FAKE, ts=FAKE, nc=None, weights=No
     ("flags", 1 << 9, _lib.HSTU_ERR_INVALID_ARG),
     ("ln_eps", 0.0, _lib.HSTU_ERR_INVALID_ARG),
     ("norm_len", -1, _lib.HSTU_ERR_INVALID_ARG),
+    ("num_types", 17, _lib.HSTU_ERR_UNSUPPORTED),
+    ("num_types", -1, _lib.HSTU_ERR_UNSUPPORTED),
 ])
 def test_bad_descriptor(lib, field, value, status):
     assert _call(lib, _desc(**{field: value})) == status
@@ -165,7 +168,7 @@ def test_cand_workspace_size_matches_layout(lib):
     # blocks / offsets / stats over the history, then the fp32 partial AV of up
     # to 8 chunks per candidate row
     attn = (a(((Tc + 127) // 128 + B) * 8 * 8) + a(((Th + 63) // 64 + B) * 8) + a(8) + 3 * a((B + 1) * 4)
-            + a((Th + 64) * 4) + a(Th * 16))
+            + a((Th + 64) * 4) + a(Th * 16) + a((Th + 64) * 4))
     part = a(8 * Tc * H * dv * 4)
     want = (a(Tc * dm * e) + a(Tc * H * dv * e) * 3 + a(Tc * H * dq * e) * 2 + a(Tc * H * 8)
             + attn + part)
@@ -198,3 +201,20 @@ def test_cand_entry_point_checks_arguments(lib):
     # device only through a workspace check, which fails here)
     assert _cand(lib, d, Th=0, hk=None, hv=None, hts=None, ws_bytes=4096) == _lib.HSTU_ERR_WORKSPACE
     assert _cand(lib, d, hoff=None) == _lib.HSTU_ERR_INVALID_ARG
+
+
+def test_type_table_fields_checked(lib):
+    d = _desc(num_types=2)
+    T4 = lambda **kw: _lib.HstuBiasTables(**{**dict(pos=FAKE, time=FAKE, pos_head_stride=129,
+                                                    time_head_stride=64, type=FAKE, type_head_stride=4,
+                                                    reserved=0, token_types=FAKE, hist_types=FAKE), **kw})
+    assert _call(lib, d, tables=T4(), ws=None) == _lib.HSTU_ERR_WORKSPACE       # all type fields valid
+    assert _call(lib, d, tables=T4(type=None)) == _lib.HSTU_ERR_INVALID_ARG
+    assert _call(lib, d, tables=T4(type=FAKE + 1)) == _lib.HSTU_ERR_INVALID_ARG  # misaligned bf16
+    assert _call(lib, d, tables=T4(token_types=None)) == _lib.HSTU_ERR_INVALID_ARG
+    assert _call(lib, d, tables=T4(type_head_stride=3)) == _lib.HSTU_ERR_INVALID_ARG
+    assert _call(lib, d, tables=T4(type_head_stride=0), ws=None) == _lib.HSTU_ERR_WORKSPACE
+    assert _call(lib, d, tables=T4(reserved=1)) == _lib.HSTU_ERR_INVALID_ARG
+    # untyped layers ignore every type field
+    assert _call(lib, _desc(), tables=T4(type=None, token_types=None, reserved=5), ws=None) == \
+        _lib.HSTU_ERR_WORKSPACE
