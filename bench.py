@@ -210,6 +210,58 @@ def cand_inference(torch, _lib, layer, synth, per_seq: int = 128, reps: int = 20
     }
 
 
+def sl_repack(torch, _lib, reps: int = 20):
+    """Stochastic length on the training shape (B = 64 sequences of 4096
+    tokens, N = 4096, alpha = 1.6), then the re-pack of x (bf16, d = 512),
+    timestamps and token types: events around sample + gathers."""
+    B, L, d = 64, 4096, 512
+    g = torch.Generator(device="cuda").manual_seed(11)
+    off = torch.arange(0, (B + 1) * L, L, dtype=torch.int64, device="cuda")
+    u = torch.rand(B, generator=g, device="cuda")
+    keys = torch.randint(-(1 << 31), 1 << 31, (B * L,), generator=g, device="cuda", dtype=torch.int32)
+    x = torch.randn(B * L, d, generator=g, device="cuda").to(torch.bfloat16)
+    ts = torch.randint(0, 1 << 40, (B * L,), generator=g, device="cuda")
+    ty = torch.randint(0, 2, (B * L,), generator=g, device="cuda").to(torch.uint8)
+    new_off = torch.empty(B + 1, dtype=torch.int64, device="cuda")
+    rows = torch.empty(B * L, dtype=torch.int64, device="cuda")
+    xo, tso, tyo = torch.empty_like(x), torch.empty_like(ts), torch.empty_like(ty)
+    ws = _lib.alloc_workspace(int(_lib.load().hstu_sl_workspace_size(B)), "cuda")
+
+    def step():
+        _lib.sl_sample(off, u, keys, L, 1.6, out_offsets=new_off, out_rows=rows, workspace=ws)
+        cnt = new_off[-1:]
+        _lib.gather_rows(x, rows, cnt, out=xo)
+        _lib.gather_rows(ts, rows, cnt, out=tso)
+        _lib.gather_rows(ty, rows, cnt, out=tyo)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        st = torch.cuda.current_stream()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(st)
+        for _ in range(reps):
+            fn()
+        b.record(st)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    total_ms = timed(step)
+    sample_ms = timed(lambda: _lib.sl_sample(off, u, keys, L, 1.6, out_offsets=new_off, out_rows=rows,
+                                             workspace=ws))
+    kept = int(new_off[-1].item())
+    moved = kept * (2 * d * 2 + 2 * 8 + 2 * 1 + 3 * 8)   # rows read + written, and their index read thrice
+    return {
+        "workload": "64 x 4096 tokens, N = 4096, alpha = 1.6; re-pack x (bf16 x 512), timestamps, types",
+        "kept_tokens": kept,
+        "tokens": B * L,
+        "sample_ms": sample_ms,
+        "sample_and_repack_ms": total_ms,
+        "repack_gbs": moved / ((total_ms - sample_ms) * 1e-3) / 1e9,
+        "repack_hbm_frac": moved / ((total_ms - sample_ms) * 1e-3) / 1e9 / PEAK_HBM_GBS,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -384,6 +436,7 @@ def main():
     }
     if not args.no_cand:
         rec["cand_inference"] = cand_inference(torch, _lib, layer, synth)
+        rec["stochastic_length"] = sl_repack(torch, _lib)
     if not args.no_cpu:
         rec["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
     print(json.dumps(rec), flush=True)

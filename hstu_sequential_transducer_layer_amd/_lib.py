@@ -25,7 +25,8 @@ HSTU_REUSE_PLAN = 1 << 4
 EXPORTS = [
     "hstu_workspace_size", "hstu_layer_fwd", "hstu_proj_workspace_size", "hstu_proj_fwd",
     "hstu_attn_workspace_size", "hstu_attn_fwd", "hstu_gate_fwd", "hstu_out_fwd",
-    "hstu_cand_workspace_size", "hstu_cand_fwd", "hstu_debug_indices",
+    "hstu_cand_workspace_size", "hstu_cand_fwd", "hstu_sl_workspace_size", "hstu_sl_sample",
+    "hstu_gather_rows", "hstu_debug_indices",
     "hstu_status_str", "hstu_last_error",
 ]
 
@@ -96,9 +97,13 @@ def load() -> ctypes.CDLL:
     lib.hstu_cand_workspace_size.restype = sz
     lib.hstu_cand_fwd.argtypes = [P(HstuDesc), vp, vp, i32, i64, vp, vp, vp, i64, vp, vp, vp,
                                   P(HstuWeights), P(HstuBiasTables), vp, vp, sz, vp]
+    lib.hstu_sl_workspace_size.argtypes = [i32]
+    lib.hstu_sl_workspace_size.restype = sz
+    lib.hstu_sl_sample.argtypes = [vp, i32, i64, i32, ctypes.c_float, vp, vp, vp, vp, vp, sz, vp]
+    lib.hstu_gather_rows.argtypes = [vp, i64, i64, vp, vp, i64, vp, vp]
     lib.hstu_debug_indices.argtypes = [P(HstuDesc), vp, i32, i64, vp, vp, vp, i64, vp, vp]
     for f in ("hstu_layer_fwd", "hstu_proj_fwd", "hstu_attn_fwd", "hstu_gate_fwd", "hstu_out_fwd",
-              "hstu_cand_fwd", "hstu_debug_indices"):
+              "hstu_cand_fwd", "hstu_sl_sample", "hstu_gather_rows", "hstu_debug_indices"):
         getattr(lib, f).restype = ctypes.c_int
     lib.hstu_status_str.argtypes = [ctypes.c_int]
     lib.hstu_status_str.restype = ctypes.c_char_p
@@ -299,6 +304,42 @@ def cand_fwd(desc: HstuDesc, x_cand: torch.Tensor, cand_offsets: torch.Tensor,
                              _ptr(hist_ts), _ptr(hist_k), _ptr(hist_v), ctypes.byref(w),
                              ctypes.byref(t), _ptr(out), _ptr(workspace), workspace.numel(),
                              _stream()))
+    return out
+
+
+def sl_sample(seq_offsets: torch.Tensor, u: torch.Tensor, keys: torch.Tensor, max_len: int,
+              alpha: float, out_offsets: Optional[torch.Tensor] = None,
+              out_rows: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """hstu_sl_sample; returns (out_offsets [B+1], out_rows [T]) device tensors
+    (out_rows valid up to out_offsets[B])."""
+    lib = load()
+    B, T = seq_offsets.shape[0] - 1, keys.shape[0]
+    dev = seq_offsets.device
+    if out_offsets is None:
+        out_offsets = torch.empty(B + 1, dtype=torch.int64, device=dev)
+    if out_rows is None:
+        out_rows = torch.empty(max(T, 1), dtype=torch.int64, device=dev)
+    need = int(lib.hstu_sl_workspace_size(B))
+    if workspace is None or workspace.numel() < need:
+        workspace = alloc_workspace(need, dev)
+    _check(lib.hstu_sl_sample(_ptr(seq_offsets), B, T, int(max_len), float(alpha), _ptr(u), _ptr(keys),
+                              _ptr(out_offsets), _ptr(out_rows), _ptr(workspace), workspace.numel(),
+                              _stream()))
+    return out_offsets, out_rows
+
+
+def gather_rows(src: torch.Tensor, rows: torch.Tensor, num_rows: torch.Tensor,
+                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """hstu_gather_rows over src's first dimension; num_rows: a one-element
+    device tensor (e.g. out_offsets[-1:]).  out has src's shape (rows past
+    *num_rows untouched)."""
+    lib = load()
+    if out is None:
+        out = torch.empty_like(src)
+    n = src.shape[0]
+    row_bytes = src.element_size() * (src.numel() // max(n, 1))
+    _check(lib.hstu_gather_rows(_ptr(src), n, row_bytes, _ptr(rows), _ptr(num_rows), out.shape[0],
+                                _ptr(out), _stream()))
     return out
 
 

@@ -453,6 +453,49 @@ hstu_status hstu_cand_fwd(const hstu_desc* desc, const void* x, const int64_t* c
   return ok();
 }
 
+size_t hstu_sl_workspace_size(int32_t B) { return B < 0 ? 0 : align256(((size_t)B + 1) * sizeof(int32_t)); }
+
+hstu_status hstu_sl_sample(const int64_t* off, int32_t B, int64_t T, int32_t max_len, float alpha, const float* u,
+                           const uint32_t* keys, int64_t* out_off, int64_t* out_rows, void* ws, size_t ws_bytes,
+                           hstu_stream_t stream) {
+  hstu_status st;
+  if ((st = check_sizes(T, B)) != HSTU_OK) return st;
+  if (max_len < 1) return fail(HSTU_ERR_INVALID_ARG, "max_len %d < 1", max_len);
+  if (!(alpha > 0.f && alpha <= 2.f)) return fail(HSTU_ERR_INVALID_ARG, "alpha %g: must be in (0, 2]", (double)alpha);
+  HSTU_REQ(off, 8, "seq_offsets");
+  HSTU_REQ(out_off, 8, "out_offsets");
+  if (B > 0) HSTU_REQ(u, 4, "u");
+  if (T > 0) {
+    HSTU_REQ(keys, 4, "keys");
+    HSTU_REQ(out_rows, 8, "out_rows");
+  }
+  const size_t need = hstu_sl_workspace_size(B);
+  if (!ws || ws_bytes < need || !aligned(ws, 256))
+    return fail(HSTU_ERR_WORKSPACE, "workspace: need %zu bytes (256-aligned), got %zu", need, ws_bytes);
+  // thresholds in float64, as C pow gives them: N^(alpha/2), its floor, N^alpha
+  const double thr = std::pow((double)max_len, (double)alpha / 2.0);
+  const int64_t k = (int64_t)std::floor(thr);
+  const double na = std::pow((double)max_len, (double)alpha);
+  return device(hstu::launch_sl_sample(off, B, T, u, keys, thr, k, na, out_off, out_rows, (int32_t*)ws,
+                                       (hipStream_t)stream),
+                "stochastic-length launch");
+}
+
+hstu_status hstu_gather_rows(const void* src, int64_t src_rows, int64_t row_bytes, const int64_t* rows,
+                             const int64_t* num_rows, int64_t max_rows, void* dst, hstu_stream_t stream) {
+  if (src_rows < 0 || row_bytes < 0 || max_rows < 0)
+    return fail(HSTU_ERR_INVALID_ARG, "negative size (src_rows %lld, row_bytes %lld, max_rows %lld)",
+                (long long)src_rows, (long long)row_bytes, (long long)max_rows);
+  if (max_rows == 0 || row_bytes == 0) return ok();
+  if (src_rows == 0) return fail(HSTU_ERR_INVALID_ARG, "rows to gather from an empty source");
+  if (!src || !dst) return fail(HSTU_ERR_INVALID_ARG, "src or dst is NULL");
+  HSTU_REQ(rows, 8, "rows");
+  HSTU_REQ(num_rows, 8, "num_rows");
+  return device(hstu::launch_gather_rows(src, src_rows, row_bytes, rows, num_rows, max_rows, dst,
+                                         (hipStream_t)stream),
+                "gather launch");
+}
+
 hstu_status hstu_debug_indices(const hstu_desc* desc, const int64_t* off, int32_t B, int64_t T,
                                const int64_t* ts, const int32_t* nc, const int64_t* pairs,
                                int64_t n, int64_t* out, hstu_stream_t stream) {

@@ -166,6 +166,13 @@ hipError_t launch_cand_gate(const hstu_desc& d, const int64_t* qoff, int32_t B, 
                             const int32_t* nsplit, const float* part, const hstu_weights& w, const void* u,
                             void* z, hipStream_t s);
 
+// --- sl.hip: stochastic length (plan + selection) and the row gather.
+hipError_t launch_sl_sample(const int64_t* off, int32_t B, int64_t T, const float* u, const uint32_t* keys,
+                            double thr, int64_t k, double na, int64_t* new_off, int64_t* rows, int32_t* trunc,
+                            hipStream_t s);
+hipError_t launch_gather_rows(const void* src, int64_t src_rows, int64_t row_bytes, const int64_t* rows,
+                              const int64_t* count, int64_t max_rows, void* dst, hipStream_t s);
+
 // --- debug.hip
 hipError_t launch_debug_indices(const hstu_desc& d, const int64_t* off, const int32_t* ncand,
                                 int32_t B, int64_t T, const int64_t* ts, const int64_t* pairs,

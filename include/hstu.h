@@ -252,6 +252,36 @@ hstu_status hstu_cand_fwd(const hstu_desc* desc, const void* x_cand, const int64
                           const hstu_bias_tables* tables, void* out, void* workspace,
                           size_t workspace_bytes, hstu_stream_t stream);
 
+/* Stochastic length ([FRC] 7.1.5 "Stochastic Length"), the training-time
+ * input sampler: with N = max_len, a sequence of n > N^(alpha/2) tokens is,
+ * when u[b] < 1 - N^alpha / n^2 (float64), replaced by k = floor(N^(alpha/2))
+ * of its tokens: those with the k smallest (keys[row], row) pairs, kept in
+ * their original order; other sequences are kept whole.  alpha = 2 keeps
+ * every sequence of at most N tokens.  The random draws are the caller's:
+ *   u            [B]    float32 uniforms in [0, 1), one per sequence
+ *   keys         [T]    uint32, one per token (uniform keys give a uniform
+ *                       subset; the page's feature weighting is not modelled)
+ *   out_offsets  [B+1]  int64: the sampled batch's offsets (out_offsets[B] =
+ *                       the kept token count, on the device)
+ *   out_rows     [T]    int64: flat source row of every kept token, in order
+ *                       (entries past out_offsets[B] are left untouched)
+ *   workspace    >= hstu_sl_workspace_size(B) bytes, 256-aligned
+ * alpha must lie in (0, 2] and max_len >= 1.  Re-pack the per-token tensors
+ * with hstu_gather_rows (num_rows = out_offsets + B).                       */
+size_t hstu_sl_workspace_size(int32_t batch);
+hstu_status hstu_sl_sample(const int64_t* seq_offsets, int32_t batch, int64_t total_tokens, int32_t max_len,
+                           float alpha, const float* u, const uint32_t* keys, int64_t* out_offsets,
+                           int64_t* out_rows, void* workspace, size_t workspace_bytes,
+                           hstu_stream_t stream);
+
+/* Jagged re-packing: dst row r = src row rows[r] (row_bytes bytes each) for
+ * r < min(*num_rows, max_rows), where num_rows points to DEVICE memory (e.g.
+ * out_offsets + B of hstu_sl_sample), so no synchronisation is needed; rows
+ * outside [0, src_rows) are clamped into it.  16-, 8- or 4-byte words are
+ * used when src, dst and row_bytes allow.                                    */
+hstu_status hstu_gather_rows(const void* src, int64_t src_rows, int64_t row_bytes, const int64_t* rows,
+                             const int64_t* num_rows, int64_t max_rows, void* dst, hstu_stream_t stream);
+
 /* Integer indexing used by stage 2, for inspection: for each flat pair
  * (query row, key row) in pairs[n_pairs][2] (int64, device) writes
  * out[n][0..5] = {b, i, j, bp, bt, mask} (int64, device) with the definitions

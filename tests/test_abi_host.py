@@ -28,7 +28,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 13
+    assert len(names) == 16
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.EXPORTS)
@@ -218,3 +218,27 @@ def test_type_table_fields_checked(lib):
     # untyped layers ignore every type field
     assert _call(lib, _desc(), tables=T4(type=None, token_types=None, reserved=5), ws=None) == \
         _lib.HSTU_ERR_WORKSPACE
+
+
+def test_sl_entry_points_check_arguments(lib):
+    ws = lambda n: n
+    call = lambda **kw: lib.hstu_sl_sample(*[{**dict(off=FAKE, B=4, T=100, N=4096, a=1.6, u=FAKE, keys=FAKE,
+                                                     oo=FAKE, orows=FAKE, ws=FAKE, wb=1 << 20), **kw}[k]
+                                             for k in ("off", "B", "T", "N", "a", "u", "keys", "oo", "orows",
+                                                       "ws", "wb")], None)
+    assert lib.hstu_sl_workspace_size(4) == 256
+    assert call(a=0.0) == _lib.HSTU_ERR_INVALID_ARG
+    assert call(a=2.5) == _lib.HSTU_ERR_INVALID_ARG
+    assert call(N=0) == _lib.HSTU_ERR_INVALID_ARG
+    assert call(keys=None) == _lib.HSTU_ERR_INVALID_ARG
+    assert call(u=FAKE + 2) == _lib.HSTU_ERR_INVALID_ARG
+    assert call(orows=None) == _lib.HSTU_ERR_INVALID_ARG
+    assert call(ws=None) == _lib.HSTU_ERR_WORKSPACE
+    assert call(T=-1) == _lib.HSTU_ERR_INVALID_ARG
+    g = lambda **kw: lib.hstu_gather_rows(*[{**dict(src=FAKE, sr=10, rb=64, rows=FAKE, n=FAKE, mr=10, dst=FAKE),
+                                            **kw}[k] for k in ("src", "sr", "rb", "rows", "n", "mr", "dst")], None)
+    assert g(rows=None) == _lib.HSTU_ERR_INVALID_ARG
+    assert g(n=FAKE + 4) == _lib.HSTU_ERR_INVALID_ARG
+    assert g(sr=0) == _lib.HSTU_ERR_INVALID_ARG
+    assert g(rb=-8) == _lib.HSTU_ERR_INVALID_ARG
+    assert g(mr=0, src=None) == _lib.HSTU_OK                            # nothing to copy
