@@ -571,9 +571,15 @@ __global__ __launch_bounds__(256, attn_min_blocks((DQK + DV) * (int)sizeof(T) + 
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
       f32x16 sc = f32x16{};
+      // Raised wave priority while a wave issues its MFMA chains: the other
+      // wave on the SIMD (another workgroup's) then fills the matrix core's
+      // busy cycles with its weight arithmetic instead of delaying these
+      // issues (measured 1-2% faster).
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int c = 0; c < DQK / 16; ++c)
         sc = mma_k16(k_frag<T, DQK>(Kb, kh * 32 + l32, 16 * c + 8 * half), qf[c], sc);
+      __builtin_amdgcn_s_setprio(0);
       if (TYPED) {
         // one-hot of key kh * 32 + l32's type over k = 8 * half + e (a type
         // outside [0, 16), e.g. in a padding row, gives zeros)
@@ -590,12 +596,14 @@ __global__ __launch_bounds__(256, attn_min_blocks((DQK + DV) * (int)sizeof(T) + 
         for (int n = 0; n < DV / 32; ++n) vf[c2][n] = v_frag<T, DV>(Vb, kh * 32 + 16 * c2, n, lane);
       float p[16];
       half_weights(mode, sc, p, kh, x);
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2) {
         const Frag pf = to_frag<T>(p + 8 * c2);
 #pragma unroll
         for (int n = 0; n < DV / 32; ++n) o[n] = mma_k16(vf[c2][n], pf, o[n]);
       }
+      __builtin_amdgcn_s_setprio(0);
     }
   };
 
