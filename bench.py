@@ -356,6 +356,17 @@ def main():
         rng.normal(0.0, 0.02, (w.dims.num_heads, 2, 2)))).to(x.dtype).cuda()
     ttypes = torch.from_numpy(types).cuda()
     typed_ms = timed(lambda: _lib.attn_fwd(tdesc, off, ts, nc, tprm, acts, token_types=ttypes), reps=args.attn_reps)
+    # The layer backward (forward recompute + all gradients) of layer 1.
+    gdy = torch.randn(x.shape, generator=torch.Generator(device="cuda").manual_seed(5), device="cuda").to(x.dtype)
+    gdx = torch.empty_like(x)
+    gws = _lib.alloc_workspace(_lib.bwd_workspace_size(desc, T, B), "cuda")
+    gout = {}
+
+    def bwd():
+        nonlocal gout
+        _, gout = _lib.layer_bwd(desc, x, off, ts, nc, dev["layers"][0], gdy, dx=gdx,
+                                 grads=gout or None, workspace=gws)
+    bwd_ms = timed(bwd, reps=5)
     proj_ms = timed(lambda: _lib.proj_fwd(desc, x, dev["layers"][0], acts))
     zbuf = torch.empty_like(acts["u"])
     gate_ms = timed(lambda: _lib.gate_fwd(desc, dev["layers"][0], acts, z=zbuf), reps=20)
@@ -426,6 +437,12 @@ def main():
             "f2_tflops_excl_gate": f2_flop / (max(out_ms - gate_ms, 1e-6) * 1e-3) / 1e12,
         },
         "layer_tokens_per_s": T * len(w.layers) / (ms_step * 1e-3),
+        "backward": {
+            "what": "hstu_layer_bwd of layer 1: forward recompute, then dx and every parameter gradient",
+            "ms": bwd_ms,
+            "tokens_per_s": T / (bwd_ms * 1e-3),
+            "ratio_to_forward_layer": bwd_ms / (ms_step / len(w.layers)),
+        },
         "type_bias": {
             "what": "hstu_attn_fwd of layer 1 with a 2-type token-type term (interleaved content/action)",
             "launch_ms": typed_ms,

@@ -25,7 +25,8 @@ HSTU_REUSE_PLAN = 1 << 4
 EXPORTS = [
     "hstu_workspace_size", "hstu_layer_fwd", "hstu_proj_workspace_size", "hstu_proj_fwd",
     "hstu_attn_workspace_size", "hstu_attn_fwd", "hstu_gate_fwd", "hstu_out_fwd",
-    "hstu_cand_workspace_size", "hstu_cand_fwd", "hstu_sl_workspace_size", "hstu_sl_sample",
+    "hstu_cand_workspace_size", "hstu_cand_fwd", "hstu_bwd_workspace_size", "hstu_layer_bwd",
+    "hstu_sl_workspace_size", "hstu_sl_sample",
     "hstu_gather_rows", "hstu_debug_indices",
     "hstu_status_str", "hstu_last_error",
 ]
@@ -51,6 +52,13 @@ class HstuBiasTables(ctypes.Structure):
                 ("type", ctypes.c_void_p), ("type_head_stride", ctypes.c_int32),
                 ("reserved", ctypes.c_int32), ("token_types", ctypes.c_void_p),
                 ("hist_types", ctypes.c_void_p)]
+
+
+GRAD_FIELDS = ("w1", "b1", "w2", "b2", "ln_in_g", "ln_in_b", "ln_av_g", "ln_av_b", "pos", "time")
+
+
+class HstuGrads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in GRAD_FIELDS]
 
 
 class HstuActivations(ctypes.Structure):
@@ -97,13 +105,17 @@ def load() -> ctypes.CDLL:
     lib.hstu_cand_workspace_size.restype = sz
     lib.hstu_cand_fwd.argtypes = [P(HstuDesc), vp, vp, i32, i64, vp, vp, vp, i64, vp, vp, vp,
                                   P(HstuWeights), P(HstuBiasTables), vp, vp, sz, vp]
+    lib.hstu_bwd_workspace_size.argtypes = [P(HstuDesc), i64, i32]
+    lib.hstu_bwd_workspace_size.restype = sz
+    lib.hstu_layer_bwd.argtypes = [P(HstuDesc), vp, vp, i32, i64, vp, vp, P(HstuWeights), P(HstuBiasTables),
+                                   vp, vp, P(HstuGrads), vp, sz, vp]
     lib.hstu_sl_workspace_size.argtypes = [i32]
     lib.hstu_sl_workspace_size.restype = sz
     lib.hstu_sl_sample.argtypes = [vp, i32, i64, i32, ctypes.c_float, vp, vp, vp, vp, vp, sz, vp]
     lib.hstu_gather_rows.argtypes = [vp, i64, i64, vp, vp, i64, vp, vp]
     lib.hstu_debug_indices.argtypes = [P(HstuDesc), vp, i32, i64, vp, vp, vp, i64, vp, vp]
     for f in ("hstu_layer_fwd", "hstu_proj_fwd", "hstu_attn_fwd", "hstu_gate_fwd", "hstu_out_fwd",
-              "hstu_cand_fwd", "hstu_sl_sample", "hstu_gather_rows", "hstu_debug_indices"):
+              "hstu_cand_fwd", "hstu_layer_bwd", "hstu_sl_sample", "hstu_gather_rows", "hstu_debug_indices"):
         getattr(lib, f).restype = ctypes.c_int
     lib.hstu_status_str.argtypes = [ctypes.c_int]
     lib.hstu_status_str.restype = ctypes.c_char_p
@@ -305,6 +317,38 @@ def cand_fwd(desc: HstuDesc, x_cand: torch.Tensor, cand_offsets: torch.Tensor,
                              ctypes.byref(t), _ptr(out), _ptr(workspace), workspace.numel(),
                              _stream()))
     return out
+
+
+def bwd_workspace_size(desc: HstuDesc, T: int, B: int) -> int:
+    return int(load().hstu_bwd_workspace_size(ctypes.byref(desc), T, B))
+
+
+def layer_bwd(desc: HstuDesc, x: torch.Tensor, seq_offsets: torch.Tensor, timestamps: torch.Tensor,
+              num_candidates: Optional[torch.Tensor], prm: Dict[str, torch.Tensor], dy: torch.Tensor,
+              dx: Optional[torch.Tensor] = None, grads: Optional[Dict[str, torch.Tensor]] = None,
+              workspace: Optional[torch.Tensor] = None):
+    """hstu_layer_bwd; returns (dx, grads) with grads[name] fp32 shaped like
+    the parameter (pos/time like the tables)."""
+    lib = load()
+    T, B = x.shape[0], seq_offsets.shape[0] - 1
+    dev = x.device
+    if dx is None:
+        dx = torch.empty_like(x)
+    if grads is None:
+        shape = {"w1": prm["w1"].shape, "b1": prm["b1"].shape, "w2": prm["w2"].shape, "b2": prm["b2"].shape,
+                 "ln_in_g": prm["ln_in_g"].shape, "ln_in_b": prm["ln_in_b"].shape,
+                 "ln_av_g": prm["ln_av_g"].shape, "ln_av_b": prm["ln_av_b"].shape,
+                 "pos": prm["pos_table"].shape, "time": prm["time_table"].shape}
+        grads = {n: torch.empty(shape[n], dtype=torch.float32, device=dev) for n in GRAD_FIELDS}
+    need = bwd_workspace_size(desc, T, B)
+    if workspace is None or workspace.numel() < need:
+        workspace = alloc_workspace(need, dev)
+    g = HstuGrads(*[_ptr(grads[n]) for n in GRAD_FIELDS])
+    w, t = make_weights(prm), make_tables(prm)
+    _check(lib.hstu_layer_bwd(ctypes.byref(desc), _ptr(x), _ptr(seq_offsets), B, T, _ptr(timestamps),
+                              _ptr(num_candidates), ctypes.byref(w), ctypes.byref(t), _ptr(dy), _ptr(dx),
+                              ctypes.byref(g), _ptr(workspace), workspace.numel(), _stream()))
+    return dx, grads
 
 
 def sl_sample(seq_offsets: torch.Tensor, u: torch.Tensor, keys: torch.Tensor, max_len: int,

@@ -22,7 +22,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libhstu.so")
 INCLUDE = os.path.join(ROOT, "include")
 
-SOURCES = ["prep.hip", "proj.hip", "attn.hip", "out.hip", "sl.hip", "debug.hip", "api.cpp"]
+SOURCES = ["prep.hip", "proj.hip", "attn.hip", "attn_bwd.hip", "out.hip", "bwd.hip", "sl.hip", "debug.hip", "api.cpp"]
 
 ARCH = "gfx950"
 FLAGS = [

@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "hstu.h"
@@ -450,6 +451,172 @@ hstu_status hstu_cand_fwd(const hstu_desc* desc, const void* x, const int64_t* c
       HSTU_OK)
     return st;
   if ((st = device(hstu::launch_f2(*desc, x, Tc, *w, z, out, s), "f2 launch")) != HSTU_OK) return st;
+  return ok();
+}
+
+// Backward workspace: the forward's buffers, then the backward's.
+struct BwdLayout {
+  Layout f;
+  size_t z, dz, dact, dav, gterm_av, bterm_av, tab_part, pre, dpre_t, w2t, dyt, zt, w1t, dpret, xnt, dxn, gterm_in,
+      ctmp, wsplit, total;
+  int64_t Tp;
+};
+
+static BwdLayout bwd_layout(const hstu_desc* d, int64_t T, int32_t B) {
+  BwdLayout L{};
+  L.f = layout(d, T, B, T, false);
+  const size_t e = esize(d->dtype);
+  const int64_t K2 = (int64_t)d->num_heads * d->dv, N1 = 2 * (int64_t)d->num_heads * (d->dqk + d->dv);
+  const int64_t dm = d->d_model;
+  L.Tp = (T + 63) / 64 * 64;
+  size_t o = L.f.total;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o += align256(bytes);
+    return at;
+  };
+  L.z = take((size_t)T * K2 * e);
+  L.dz = take((size_t)T * K2 * 4);
+  L.dact = take((size_t)T * N1 * 4);
+  L.dav = take((size_t)T * K2 * e);
+  L.gterm_av = take((size_t)T * K2 * 4);
+  L.bterm_av = take((size_t)T * K2 * 4);
+  L.tab_part = take((size_t)hstu::attn_max_tiles(T, B) * d->num_heads * (d->pos_buckets + d->time_buckets) * 4);
+  L.pre = take((size_t)T * N1 * 4);
+  L.dpre_t = take((size_t)T * N1 * e);
+  L.w2t = take((size_t)K2 * dm * e);
+  L.dyt = take((size_t)dm * L.Tp * e);
+  L.zt = take((size_t)K2 * L.Tp * e);
+  L.w1t = take((size_t)dm * N1 * e);
+  L.dpret = take((size_t)N1 * L.Tp * e);
+  L.xnt = take((size_t)dm * L.Tp * e);
+  L.dxn = take((size_t)T * dm * 4);
+  L.gterm_in = take((size_t)T * dm * 4);
+  const int64_t cmax = N1 > dm ? (N1 > K2 ? N1 : K2) : (dm > K2 ? dm : K2);
+  L.ctmp = take(hstu::colsum_tmp_bytes(T, cmax));
+  L.wsplit = take((size_t)hstu::kGemmMaxSplit * (size_t)(N1 > K2 ? N1 : K2) * dm * 4);
+  L.total = o;
+  return L;
+}
+
+static hstu_status check_bwd_desc(const hstu_desc* d) {
+  hstu_status st;
+  if ((st = check_desc(d)) != HSTU_OK) return st;
+  if (d->num_types != 0) return fail(HSTU_ERR_UNSUPPORTED, "the backward pass has no token-type term yet");
+  if (d->dqk != d->dv) return fail(HSTU_ERR_UNSUPPORTED, "the backward pass needs dqk == dv");
+  if (d->pos_buckets + d->time_buckets > 2048)
+    return fail(HSTU_ERR_UNSUPPORTED, "the backward pass needs pos_buckets + time_buckets <= 2048");
+  return HSTU_OK;
+}
+
+size_t hstu_bwd_workspace_size(const hstu_desc* desc, int64_t T, int32_t B) {
+  if (check_bwd_desc(desc) != HSTU_OK || check_sizes(T, B) != HSTU_OK) return 0;
+  return bwd_layout(desc, T, B).total;
+}
+
+hstu_status hstu_layer_bwd(const hstu_desc* desc, const void* x, const int64_t* off, int32_t B, int64_t T,
+                           const int64_t* ts, const int32_t* nc, const hstu_weights* w,
+                           const hstu_bias_tables* tables, const void* dy, void* dx, const hstu_grads* g,
+                           void* ws, size_t ws_bytes, hstu_stream_t stream) {
+  hstu_status st;
+  if ((st = check_bwd_desc(desc)) != HSTU_OK) return st;
+  if ((st = check_sizes(T, B)) != HSTU_OK) return st;
+  if (!g) return fail(HSTU_ERR_INVALID_ARG, "grads is NULL");
+  const float* gp[] = {g->w1, g->b1, g->w2, g->b2, g->ln_in_g, g->ln_in_b, g->ln_av_g, g->ln_av_b, g->pos, g->time};
+  for (const float* p : gp)
+    if (!p || !aligned(p, 4)) return fail(HSTU_ERR_INVALID_ARG, "a gradient pointer is NULL or misaligned");
+  HSTU_REQ(x, 16, "x");
+  HSTU_REQ(dy, 16, "dy");
+  HSTU_REQ(dx, 16, "dx");
+  if ((st = check_meta(off, B, ts, nc)) != HSTU_OK) return st;
+  if ((st = check_proj_weights(desc, w)) != HSTU_OK) return st;
+  if ((st = check_out_weights(desc, w)) != HSTU_OK) return st;
+  if ((st = check_tables(desc, tables)) != HSTU_OK) return st;
+  const BwdLayout L = bwd_layout(desc, T, B);
+  if (!ws || ws_bytes < L.total || !aligned(ws, 256))
+    return fail(HSTU_ERR_WORKSPACE, "workspace: need %zu bytes (256-aligned), got %zu", L.total, ws_bytes);
+  hipStream_t s = (hipStream_t)stream;
+  if (desc->flags & HSTU_VALIDATE)
+    if ((st = validate_metadata(off, B, T, nc, s)) != HSTU_OK) return st;
+  const hstu_dtype dt = desc->dtype;
+  const int64_t K2 = (int64_t)desc->num_heads * desc->dv, N1 = 2 * (int64_t)desc->num_heads * (desc->dqk + desc->dv);
+  const int dm = desc->d_model;
+  char* base = (char*)ws;
+  auto F = [&](size_t o) { return (float*)(base + o); };
+  float* ctmp = F(L.ctmp);
+  auto colsum = [&](bool f32, const void* src, int64_t R, int64_t C, float* dst) {
+    return device(hstu::launch_colsum(dt, f32, src, R, C, ctmp, dst, s), "column-sum launch");
+  };
+  if (T == 0) {  // no tokens: every gradient is zero
+    if ((st = colsum(true, ctmp, 0, N1 * dm, g->w1)) != HSTU_OK) return st;
+    const std::pair<float*, int64_t> z[] = {{g->b1, N1}, {g->w2, dm * K2}, {g->b2, dm}, {g->ln_in_g, dm},
+                                            {g->ln_in_b, dm}, {g->ln_av_g, K2}, {g->ln_av_b, K2},
+                                            {g->pos, (int64_t)desc->num_heads * desc->pos_buckets},
+                                            {g->time, (int64_t)desc->num_heads * desc->time_buckets}};
+    for (const auto& p : z)
+      if ((st = colsum(true, ctmp, 0, p.second, p.first)) != HSTU_OK) return st;
+    return ok();
+  }
+  hstu_activations a;
+  a.u = base + L.f.u;
+  a.v = base + L.f.v;
+  a.q = base + L.f.q;
+  a.k = base + L.f.k;
+  a.av = base + L.f.av;
+  a.av_stats = F(L.f.stats);
+  const bool norm = (desc->flags & HSTU_INPUT_NORM) != 0;
+  const void* xn = norm ? (const void*)(base + L.f.xn) : x;
+  // forward recompute: U, V, Q, K; AV and its statistics (and the work list); Z
+  if ((st = run_proj(desc, x, T, w, &a, base + L.f.xn, s)) != HSTU_OK) return st;
+  if ((st = run_attn(desc, off, B, T, ts, nc, tables, &a, base + L.f.attn, s)) != HSTU_OK) return st;
+  void* z = base + L.z;
+  if ((st = device(hstu::launch_gate(*desc, T, *w, a.u, a.av, a.av_stats, z, s), "gate launch")) != HSTU_OK) return st;
+  // f2: dZ = dY W2, dW2 = dY^T Z, db2 = sum dY
+  if ((st = device(hstu::launch_transpose(dt, w->w2, dm, K2, dm, base + L.w2t, s), "transpose")) != HSTU_OK) return st;
+  if ((st = device(hstu::launch_gemm_nt_f32(dt, dy, base + L.w2t, F(L.dz), T, (int)K2, dm, nullptr, s), "gemm")) != HSTU_OK)
+    return st;
+  if ((st = device(hstu::launch_transpose(dt, dy, T, dm, L.Tp, base + L.dyt, s), "transpose")) != HSTU_OK) return st;
+  if ((st = device(hstu::launch_transpose(dt, z, T, K2, L.Tp, base + L.zt, s), "transpose")) != HSTU_OK) return st;
+  if ((st = device(hstu::launch_gemm_nt_f32(dt, base + L.dyt, base + L.zt, g->w2, dm, (int)K2, (int)L.Tp, F(L.wsplit), s), "gemm")) !=
+      HSTU_OK)
+    return st;
+  if ((st = colsum(false, dy, T, dm, g->b2)) != HSTU_OK) return st;
+  // gate and LayerNorm over the merged heads
+  float* dact = F(L.dact);
+  if ((st = device(hstu::launch_gate_bwd(*desc, T, *w, F(L.dz), a.u, a.av, a.av_stats, dact, base + L.dav,
+                                         F(L.gterm_av), F(L.bterm_av), s),
+                   "gate backward launch")) != HSTU_OK)
+    return st;
+  if ((st = colsum(true, F(L.gterm_av), T, K2, g->ln_av_g)) != HSTU_OK) return st;
+  if ((st = colsum(true, F(L.bterm_av), T, K2, g->ln_av_b)) != HSTU_OK) return st;
+  // attention: dV, dQ, dK into dact; the bias tables
+  const hstu::AttnScratch sc = hstu::attn_scratch(base + L.f.attn, T, B);
+  if ((st = device(hstu::launch_attn_bwd(*desc, off, nc, B, T, ts, *tables, a.q, a.k, a.v, base + L.dav, dact,
+                                         F(L.tab_part), g->pos, g->time, sc, s),
+                   "attention backward launch")) != HSTU_OK)
+    return st;
+  // f1 and SiLU: dpre = d(u|v|q|k) * SiLU'(x~ W1^T + b1); db1, dW1 = dpre^T x~, dx~ = dpre W1
+  if ((st = device(hstu::launch_gemm_nt_f32(dt, xn, w->w1, F(L.pre), T, (int)N1, dm, nullptr, s), "gemm")) != HSTU_OK) return st;
+  if ((st = device(hstu::launch_silu_bwd(dt, F(L.pre), w->b1, dact, T, (int)N1, dact, base + L.dpre_t, s),
+                   "silu backward launch")) != HSTU_OK)
+    return st;
+  if ((st = colsum(true, dact, T, N1, g->b1)) != HSTU_OK) return st;
+  if ((st = device(hstu::launch_transpose(dt, w->w1, N1, dm, N1, base + L.w1t, s), "transpose")) != HSTU_OK) return st;
+  if ((st = device(hstu::launch_gemm_nt_f32(dt, base + L.dpre_t, base + L.w1t, F(L.dxn), T, dm, (int)N1, nullptr, s), "gemm")) !=
+      HSTU_OK)
+    return st;
+  if ((st = device(hstu::launch_transpose(dt, base + L.dpre_t, T, N1, L.Tp, base + L.dpret, s), "transpose")) != HSTU_OK)
+    return st;
+  if ((st = device(hstu::launch_transpose(dt, xn, T, dm, L.Tp, base + L.xnt, s), "transpose")) != HSTU_OK) return st;
+  if ((st = device(hstu::launch_gemm_nt_f32(dt, base + L.dpret, base + L.xnt, g->w1, N1, dm, (int)L.Tp, F(L.wsplit), s), "gemm")) !=
+      HSTU_OK)
+    return st;
+  // input LayerNorm and the residual
+  if ((st = device(hstu::launch_ln_bwd(*desc, x, F(L.dxn), *w, dy, T, dx, F(L.gterm_in), s), "ln backward launch")) !=
+      HSTU_OK)
+    return st;
+  if ((st = colsum(true, F(L.gterm_in), norm ? T : 0, dm, g->ln_in_g)) != HSTU_OK) return st;
+  if ((st = colsum(true, F(L.dxn), norm ? T : 0, dm, g->ln_in_b)) != HSTU_OK) return st;
   return ok();
 }
 

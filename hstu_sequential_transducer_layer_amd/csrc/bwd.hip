@@ -1,0 +1,308 @@
+// The layer backward around the attention (row f2): the gradients of
+//   x~ = LayerNorm_in(x);  u|v|q|k = SiLU(x~ W1^T + b1);
+//   Z = (LayerNorm_av(AV) * g + b) * U;  Y = Z W2^T + b2 (+ x)
+// (page "4.4 Scaling Recommendation Models", "Generative Recommenders and
+// HSTU" first and third layer equations and the "Code" sketch; page "HSTU:
+// The First Exploration of the Scaling Law", 7.1.4 Innovation 1).
+// Kernels:
+//   transpose_kernel      [R, C] -> [C, Rp] in the layer dtype, columns past R zero
+//   gemm_nt_f32_kernel    C = A B^T with fp32 output (128 x 128 tiles, MFMA)
+//   colsum_kernel         column sums, in two deterministic stages
+//   gate_bwd_kernel       one wave per row: dU, dL/dAV, and the per-row terms
+//                         of the LayerNorm_av parameter gradients
+//   silu_bwd_kernel       dpre = d(u|v|q|k) * SiLU'(pre)
+//   ln_bwd_kernel         one wave per row: dx through LayerNorm_in (+ dY)
+#include "common.h"
+#include "gemm.h"
+#include "kernels.h"
+
+namespace hstu {
+
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ src, int64_t R, int64_t C, int64_t Rp,
+                                                        T* __restrict__ dst) {
+  __shared__ T tile[64][65];
+  const int64_t r0 = (int64_t)blockIdx.x * 64, c0 = (int64_t)blockIdx.y * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int i = ty; i < 64; i += 4) {
+    const int64_t r = r0 + i, c = c0 + tx;
+    tile[i][tx] = (r < R && c < C) ? src[r * C + c] : from_f32<T>(0.f);
+  }
+  __syncthreads();
+  for (int i = ty; i < 64; i += 4) {
+    const int64_t c = c0 + i, r = r0 + tx;
+    if (c < C && r < Rp) dst[c * Rp + r] = tile[tx][i];
+  }
+}
+
+// Split over K: workgroup (tile, s) multiplies columns [s kc, (s + 1) kc) and
+// writes its partial product to C + s M N (summed afterwards in s order).
+template <typename T>
+__global__ __launch_bounds__(256, 2) void gemm_nt_f32_kernel(const T* __restrict__ A, const T* __restrict__ Bm,
+                                                             float* __restrict__ C, int64_t M, int N, int K,
+                                                             int kc) {
+  typedef GemmTile<T> G;
+  __shared__ __attribute__((aligned(16))) T As[G::BM * G::LDK];
+  __shared__ __attribute__((aligned(16))) T Bs[G::BN * G::LDK];
+  const int nrow = (int)((M + G::BM - 1) / G::BM), ncol = (N + G::BN - 1) / G::BN;
+  const int tiles = nrow * ncol, split = blockIdx.x / tiles;
+  int tr, tc;
+  map_tile(blockIdx.x - split * tiles, nrow, ncol, tr, tc);
+  const int64_t row0 = (int64_t)tr * G::BM;
+  const int col0 = tc * G::BN;
+  const int k0 = split * kc, kn = min(kc, K - k0);
+  C += (int64_t)split * M * N;
+  RowLoader<T> al{A + k0, row0, M, kn, K};
+  f32x16 acc[2][2];
+  gemm_mainloop<T>(al, Bm + k0, col0, N, kn, As, Bs, acc, K);
+  const int lane = threadIdx.x & 63, w = wave_id(), wm = w >> 1, wn = w & 1;
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int col = col0 + wn * 64 + nt * 32 + (lane & 31);
+    if (col >= N) continue;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = row0 + acc_row(wm, mt, lane, r);
+        if (row < M) C[row * N + col] = acc[mt][nt][r];
+      }
+  }
+}
+
+// dst[chunk][c] = sum of src rows [chunk * rows_per, (chunk + 1) * rows_per), c < C.
+template <typename TIn>
+__global__ __launch_bounds__(256) void colsum_kernel(const TIn* __restrict__ src, int64_t R, int64_t C,
+                                                     int64_t rows_per, float* __restrict__ dst) {
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= C) return;
+  const int64_t r0 = (int64_t)blockIdx.y * rows_per, r1 = min(r0 + rows_per, R);
+  float s = 0.f;
+  for (int64_t r = r0; r < r1; ++r) s += to_f32(src[r * C + c]);
+  dst[blockIdx.y * C + c] = s;
+}
+
+// One wave per row.  Recomputes the LayerNorm of AV from the attention's
+// per-head statistics (the forward gate's merge), then
+//   n^ = (AV - mean) * rstd,  dn = dZ * U,  dn^ = dn * g
+//   dU = dZ * (n^ g + b),  dAV = rstd (dn^ - mean(dn^) - n^ mean(dn^ n^))
+// and the per-row terms dn * n^ and dn of dg and db.
+template <typename T>
+__global__ __launch_bounds__(256) void gate_bwd_kernel(const float* __restrict__ dz, const T* __restrict__ u,
+                                                       const T* __restrict__ av, const float* __restrict__ stats,
+                                                       const T* __restrict__ g, const T* __restrict__ be,
+                                                       int64_t M, int H, int dv, float eps, int64_t n1,
+                                                       float* __restrict__ du, T* __restrict__ dav,
+                                                       float* __restrict__ gterm, float* __restrict__ bterm) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + wave_id();
+  if (row >= M) return;
+  const int K = H * dv;
+  const float2 st = lane < H ? reinterpret_cast<const float2*>(stats)[row * H + lane] : make_float2(0.f, 0.f);
+  const float mean = wave_sum(st.x) / (float)H;
+  const float dm = st.x - mean;
+  const float m2 = wave_sum(lane < H ? st.y + (float)dv * dm * dm : 0.f);
+  const float rstd = rsqrtf(m2 / (float)K + eps);
+  const int64_t o = row * K;
+  float s1 = 0.f, s2 = 0.f;
+  for (int c = lane; c < K; c += kWave) {
+    const float nh = (to_f32(av[o + c]) + __shfl(dm, c / dv, kWave)) * rstd;
+    const float dnh = dz[o + c] * to_f32(u[o + c]) * to_f32(g[c]);
+    s1 += dnh;
+    s2 += dnh * nh;
+  }
+  const float m1 = wave_sum(s1) / (float)K, mm = wave_sum(s2) / (float)K;
+  for (int c = lane; c < K; c += kWave) {
+    const float nh = (to_f32(av[o + c]) + __shfl(dm, c / dv, kWave)) * rstd;
+    const float gg = to_f32(g[c]);
+    const float dn = dz[o + c] * to_f32(u[o + c]);
+    du[row * n1 + c] = dz[o + c] * (nh * gg + to_f32(be[c]));
+    dav[o + c] = from_f32<T>(rstd * (dn * gg - m1 - nh * mm));
+    gterm[o + c] = dn * nh;
+    bterm[o + c] = dn;
+  }
+}
+
+// dpre = dact * SiLU'(pre + b1), SiLU'(z) = s (1 + z (1 - s)), s = sigmoid(z);
+// written in fp32 and in the layer dtype.
+template <typename T>
+__global__ __launch_bounds__(256) void silu_bwd_kernel(const float* __restrict__ pre, const T* __restrict__ b1,
+                                                       const float* __restrict__ dact, int64_t total, int n1,
+                                                       float* __restrict__ dpre, T* __restrict__ dpre_t) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= total) return;
+  const float z = pre[i] + to_f32(b1[i % n1]);
+  const float s = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z * -1.4426950408889634f));
+  const float d = dact[i] * s * (1.0f + z * (1.0f - s));
+  dpre[i] = d;
+  dpre_t[i] = from_f32<T>(d);
+}
+
+// One wave per row.  With the input LayerNorm: x^ = (x - mean) rstd,
+// dx = rstd (dxn g - mean(dxn g) - x^ mean(dxn g x^)); else dx = dxn.  Plus dY
+// for the residual.  gterm = dxn * x^ (per-row term of the gain's gradient).
+template <typename T>
+__global__ __launch_bounds__(256) void ln_bwd_kernel(const T* __restrict__ x, const float* __restrict__ dxn,
+                                                     const T* __restrict__ g, const T* __restrict__ dy, int64_t M,
+                                                     int d, float eps, int norm, int residual, T* __restrict__ dx,
+                                                     float* __restrict__ gterm) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + wave_id();
+  if (row >= M) return;
+  const int64_t o = row * d;
+  float mean = 0.f, rstd = 1.f, m1 = 0.f, mm = 0.f;
+  if (norm) {
+    float s = 0.f;
+    for (int c = lane; c < d; c += kWave) s += to_f32(x[o + c]);
+    mean = wave_sum(s) / (float)d;
+    float v = 0.f;
+    for (int c = lane; c < d; c += kWave) {
+      const float t = to_f32(x[o + c]) - mean;
+      v += t * t;
+    }
+    rstd = rsqrtf(wave_sum(v) / (float)d + eps);
+    float s1 = 0.f, s2 = 0.f;
+    for (int c = lane; c < d; c += kWave) {
+      const float xh = (to_f32(x[o + c]) - mean) * rstd;
+      const float t = dxn[o + c] * to_f32(g[c]);
+      s1 += t;
+      s2 += t * xh;
+    }
+    m1 = wave_sum(s1) / (float)d;
+    mm = wave_sum(s2) / (float)d;
+  }
+  for (int c = lane; c < d; c += kWave) {
+    float r;
+    if (norm) {
+      const float xh = (to_f32(x[o + c]) - mean) * rstd;
+      r = rstd * (dxn[o + c] * to_f32(g[c]) - m1 - xh * mm);
+      gterm[o + c] = dxn[o + c] * xh;
+    } else {
+      r = dxn[o + c];
+    }
+    if (residual) r += to_f32(dy[o + c]);
+    dx[o + c] = from_f32<T>(r);
+  }
+}
+
+template <typename T>
+static hipError_t colsum_t(const T* src, int64_t R, int64_t C, float* tmp, float* dst, hipStream_t s) {
+  const int64_t rows_per = 256, chunks = (R + rows_per - 1) / rows_per;
+  if (R == 0) {  // zero sums: one chunk of no rows
+    hipLaunchKernelGGL(colsum_kernel<float>, dim3((unsigned)((C + 255) / 256), 1), dim3(256), 0, s,
+                       (const float*)tmp, (int64_t)0, C, (int64_t)1, dst);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(colsum_kernel<T>, dim3((unsigned)((C + 255) / 256), (unsigned)chunks), dim3(256), 0, s, src, R, C,
+                     rows_per, tmp);
+  hipLaunchKernelGGL(colsum_kernel<float>, dim3((unsigned)((C + 255) / 256), 1), dim3(256), 0, s, (const float*)tmp,
+                     chunks, C, chunks, dst);
+  return hipGetLastError();
+}
+
+size_t colsum_tmp_bytes(int64_t R, int64_t C) { return (size_t)((R + 255) / 256 + 1) * (size_t)C * sizeof(float); }
+
+hipError_t launch_colsum(hstu_dtype dt_in, bool in_f32, const void* src, int64_t R, int64_t C, float* tmp, float* dst,
+                         hipStream_t s) {
+  if (in_f32) return colsum_t<float>((const float*)src, R, C, tmp, dst, s);
+  if (dt_in == HSTU_BF16) return colsum_t<bf16>((const bf16*)src, R, C, tmp, dst, s);
+  return colsum_t<float>((const float*)src, R, C, tmp, dst, s);
+}
+
+hipError_t launch_transpose(hstu_dtype dt, const void* src, int64_t R, int64_t C, int64_t Rp, void* dst,
+                            hipStream_t s) {
+  if (R == 0 && Rp == 0) return hipSuccess;
+  const dim3 grid((unsigned)((Rp + 63) / 64), (unsigned)((C + 63) / 64)), block(256);
+  if (dt == HSTU_BF16)
+    hipLaunchKernelGGL(transpose_kernel<bf16>, grid, block, 0, s, (const bf16*)src, R, C, Rp, (bf16*)dst);
+  else
+    hipLaunchKernelGGL(transpose_kernel<float>, grid, block, 0, s, (const float*)src, R, C, Rp, (float*)dst);
+  return hipGetLastError();
+}
+
+// dst[i] = sum over s < S of part[s * n + i], in s order.
+__global__ __launch_bounds__(256) void split_sum_kernel(const float* __restrict__ part, int64_t n, int S,
+                                                        float* __restrict__ dst) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  float v = 0.f;
+  for (int s = 0; s < S; ++s) v += part[s * n + i];
+  dst[i] = v;
+}
+
+int gemm_splits(int64_t M, int N, int K) {
+  const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
+  int S = 1;
+  while (S < kGemmMaxSplit && tiles * S < 512 && (int64_t)K / (2 * S) >= 512) S *= 2;
+  return S;
+}
+
+hipError_t launch_gemm_nt_f32(hstu_dtype dt, const void* A, const void* Bm, float* C, int64_t M, int N, int K,
+                              float* split_buf, hipStream_t s) {
+  if (M == 0 || N == 0) return hipSuccess;
+  const int64_t nr = (M + 127) / 128, nc = (N + 127) / 128;
+  const int S = split_buf ? gemm_splits(M, N, K) : 1;
+  const int bk = dt == HSTU_BF16 ? 64 : 32;
+  const int kc = (int)((((int64_t)K + S - 1) / S + bk - 1) / bk * bk);
+  float* out = S > 1 ? split_buf : C;
+  const dim3 grid((unsigned)(nr * nc * ((K + kc - 1) / kc)));
+  if (dt == HSTU_BF16)
+    hipLaunchKernelGGL(gemm_nt_f32_kernel<bf16>, grid, dim3(256), 0, s, (const bf16*)A, (const bf16*)Bm, out, M, N, K,
+                       kc);
+  else
+    hipLaunchKernelGGL(gemm_nt_f32_kernel<float>, grid, dim3(256), 0, s, (const float*)A, (const float*)Bm, out, M,
+                       N, K, kc);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || S == 1) return e;
+  const int64_t n = M * (int64_t)N;
+  hipLaunchKernelGGL(split_sum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, (const float*)split_buf, n,
+                     (int)((K + kc - 1) / kc), C);
+  return hipGetLastError();
+}
+
+hipError_t launch_gate_bwd(const hstu_desc& d, int64_t T, const hstu_weights& w, const float* dz, const void* u,
+                           const void* av, const float* stats, float* du, void* dav, float* gterm, float* bterm,
+                           hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const int64_t n1 = 2 * (int64_t)d.num_heads * (d.dqk + d.dv);
+  const dim3 grid((unsigned)((T + 3) / 4)), block(256);
+  if (d.dtype == HSTU_BF16)
+    hipLaunchKernelGGL(gate_bwd_kernel<bf16>, grid, block, 0, s, dz, (const bf16*)u, (const bf16*)av, stats,
+                       (const bf16*)w.ln_av_g, (const bf16*)w.ln_av_b, T, d.num_heads, d.dv, d.ln_eps, n1, du,
+                       (bf16*)dav, gterm, bterm);
+  else
+    hipLaunchKernelGGL(gate_bwd_kernel<float>, grid, block, 0, s, dz, (const float*)u, (const float*)av, stats,
+                       (const float*)w.ln_av_g, (const float*)w.ln_av_b, T, d.num_heads, d.dv, d.ln_eps, n1, du,
+                       (float*)dav, gterm, bterm);
+  return hipGetLastError();
+}
+
+hipError_t launch_silu_bwd(hstu_dtype dt, const float* pre, const void* b1, const float* dact, int64_t T, int n1,
+                           float* dpre, void* dpre_t, hipStream_t s) {
+  const int64_t total = T * n1;
+  if (total == 0) return hipSuccess;
+  const dim3 grid((unsigned)((total + 255) / 256)), block(256);
+  if (dt == HSTU_BF16)
+    hipLaunchKernelGGL(silu_bwd_kernel<bf16>, grid, block, 0, s, pre, (const bf16*)b1, dact, total, n1, dpre,
+                       (bf16*)dpre_t);
+  else
+    hipLaunchKernelGGL(silu_bwd_kernel<float>, grid, block, 0, s, pre, (const float*)b1, dact, total, n1, dpre,
+                       (float*)dpre_t);
+  return hipGetLastError();
+}
+
+hipError_t launch_ln_bwd(const hstu_desc& d, const void* x, const float* dxn, const hstu_weights& w, const void* dy,
+                         int64_t T, void* dx, float* gterm, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const int norm = (d.flags & HSTU_INPUT_NORM) ? 1 : 0, res = (d.flags & HSTU_RESIDUAL) ? 1 : 0;
+  const dim3 grid((unsigned)((T + 3) / 4)), block(256);
+  if (d.dtype == HSTU_BF16)
+    hipLaunchKernelGGL(ln_bwd_kernel<bf16>, grid, block, 0, s, (const bf16*)x, dxn, (const bf16*)w.ln_in_g,
+                       (const bf16*)dy, T, d.d_model, d.ln_eps, norm, res, (bf16*)dx, gterm);
+  else
+    hipLaunchKernelGGL(ln_bwd_kernel<float>, grid, block, 0, s, (const float*)x, dxn, (const float*)w.ln_in_g,
+                       (const float*)dy, T, d.d_model, d.ln_eps, norm, res, (float*)dx, gterm);
+  return hipGetLastError();
+}
+
+}  // namespace hstu

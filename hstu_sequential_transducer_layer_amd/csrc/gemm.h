@@ -52,10 +52,11 @@ struct RowLoader {
   const T* __restrict__ a;
   int64_t row0, M;
   int K;
+  int64_t ld = 0;  // row stride when it is not K (a column slice of a wider matrix)
   __device__ __forceinline__ uint4 operator()(int k0, int r, int kc) const {
     const int64_t row = row0 + r;
     const int k = k0 + kc;
-    return (row < M && k < K) ? ld16(a + row * K + k) : make_uint4(0, 0, 0, 0);
+    return (row < M && k < K) ? ld16(a + row * (ld ? ld : (int64_t)K) + k) : make_uint4(0, 0, 0, 0);
   }
 };
 
@@ -69,8 +70,9 @@ __device__ __forceinline__ typename Elem<T>::Frag lds_frag(const T* p) {
 // from `b` [N, K].  acc[mt][nt] holds the wave's 2 x 2 MFMA tiles.
 template <typename T, class ALoad>
 __device__ __forceinline__ void gemm_mainloop(ALoad& aload, const T* __restrict__ b, int64_t col0,
-                                              int N, int K, T* As, T* Bs, f32x16 (&acc)[2][2]) {
+                                              int N, int K, T* As, T* Bs, f32x16 (&acc)[2][2], int64_t ldb = 0) {
   typedef GemmTile<T> G;
+  const int64_t bstride = ldb ? ldb : (int64_t)K;
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
   const int wm = w >> 1, wn = w & 1;
   uint4 ra[G::NCH], rb[G::NCH];
@@ -82,7 +84,7 @@ __device__ __forceinline__ void gemm_mainloop(ALoad& aload, const T* __restrict_
       ra[c] = aload(k0, r, kc);
       const int64_t n = col0 + r;
       const int k = k0 + kc;
-      rb[c] = (n < N && k < K) ? ld16(b + n * K + k) : make_uint4(0, 0, 0, 0);
+      rb[c] = (n < N && k < K) ? ld16(b + n * bstride + k) : make_uint4(0, 0, 0, 0);
     }
   };
   auto sstore = [&]() {

@@ -173,6 +173,33 @@ hipError_t launch_sl_sample(const int64_t* off, int32_t B, int64_t T, const floa
 hipError_t launch_gather_rows(const void* src, int64_t src_rows, int64_t row_bytes, const int64_t* rows,
                               const int64_t* count, int64_t max_rows, void* dst, hipStream_t s);
 
+// --- attn_bwd.hip: dq, dv, dk into dact (fp32 [T, N1], columns of the
+// u|v|q|k split) and the bias-table gradients (tab_part: [max items * H][P + NB]).
+hipError_t launch_attn_bwd(const hstu_desc& d, const int64_t* off, const int32_t* ncand, int32_t B, int64_t T,
+                           const int64_t* ts, const hstu_bias_tables& tab, const void* q, const void* k,
+                           const void* v, const void* dout, float* dact, float* tab_part, float* gpos,
+                           float* gtime, const AttnScratch& sc, hipStream_t s);
+
+// --- bwd.hip
+size_t colsum_tmp_bytes(int64_t R, int64_t C);
+hipError_t launch_colsum(hstu_dtype dt_in, bool in_f32, const void* src, int64_t R, int64_t C, float* tmp,
+                         float* dst, hipStream_t s);
+hipError_t launch_transpose(hstu_dtype dt, const void* src, int64_t R, int64_t C, int64_t Rp, void* dst,
+                            hipStream_t s);
+// C [M, N] fp32 = A [M, K] B [N, K]^T (K a multiple of 8).  With split_buf
+// (kGemmMaxSplit * M * N floats) a long K is split over up to kGemmMaxSplit
+// workgroups per tile when the tiles alone would not fill the chip.
+constexpr int kGemmMaxSplit = 8;
+hipError_t launch_gemm_nt_f32(hstu_dtype dt, const void* A, const void* Bm, float* C, int64_t M, int N, int K,
+                              float* split_buf, hipStream_t s);
+hipError_t launch_gate_bwd(const hstu_desc& d, int64_t T, const hstu_weights& w, const float* dz, const void* u,
+                           const void* av, const float* stats, float* du, void* dav, float* gterm, float* bterm,
+                           hipStream_t s);
+hipError_t launch_silu_bwd(hstu_dtype dt, const float* pre, const void* b1, const float* dact, int64_t T, int n1,
+                           float* dpre, void* dpre_t, hipStream_t s);
+hipError_t launch_ln_bwd(const hstu_desc& d, const void* x, const float* dxn, const hstu_weights& w, const void* dy,
+                         int64_t T, void* dx, float* gterm, hipStream_t s);
+
 // --- debug.hip
 hipError_t launch_debug_indices(const hstu_desc& d, const int64_t* off, const int32_t* ncand,
                                 int32_t B, int64_t T, const int64_t* ts, const int64_t* pairs,

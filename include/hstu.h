@@ -252,6 +252,41 @@ hstu_status hstu_cand_fwd(const hstu_desc* desc, const void* x_cand, const int64
                           const hstu_bias_tables* tables, void* out, void* workspace,
                           size_t workspace_bytes, hstu_stream_t stream);
 
+/* Gradients of one layer's parameters (fp32, overwritten), each laid out
+ * like its parameter: w1 [N1, d], b1 [N1], w2 [d, H*dv], b2 [d], the four
+ * LayerNorm vectors, pos [H][P] and time [H][NB] ([P] / [NB] when the table's
+ * head stride is 0: the heads' gradients summed).  A NULL pointer skips
+ * nothing: every field is required.                                          */
+typedef struct {
+  float* w1;
+  float* b1;
+  float* w2;
+  float* b2;
+  float* ln_in_g;  /* zeros without HSTU_INPUT_NORM */
+  float* ln_in_b;
+  float* ln_av_g;
+  float* ln_av_b;
+  float* pos;
+  float* time;
+} hstu_grads;
+
+/* The layer backward (training; [SRM] "Reported results" and [FRC] 7.1.5
+ * Stochastic Length train this layer): given dy = dL/dy [T, d] (layer
+ * dtype), writes dx = dL/dx [T, d] (layer dtype; may not alias dy or x) and
+ * every parameter gradient, for the layer defined above.  The forward
+ * activations are recomputed into the workspace (nothing is kept from a
+ * forward call).  Supported: dqk = dv in {32, 64, 128} for bf16, {32, 64} for
+ * fp32, num_types = 0, pos_buckets + time_buckets <= 2048; else
+ * HSTU_ERR_UNSUPPORTED.  Results are reproducible bit for bit.  Weight gradients come from
+ * GEMMs over the token dimension in the layer dtype with fp32 accumulation.
+ *   workspace >= hstu_bwd_workspace_size(desc, T, B) bytes, 256-aligned     */
+size_t hstu_bwd_workspace_size(const hstu_desc* desc, int64_t total_tokens, int32_t batch);
+hstu_status hstu_layer_bwd(const hstu_desc* desc, const void* x, const int64_t* seq_offsets, int32_t batch,
+                           int64_t total_tokens, const int64_t* timestamps, const int32_t* num_candidates,
+                           const hstu_weights* weights, const hstu_bias_tables* tables, const void* dy,
+                           void* dx, const hstu_grads* grads, void* workspace, size_t workspace_bytes,
+                           hstu_stream_t stream);
+
 /* Stochastic length ([FRC] 7.1.5 "Stochastic Length"), the training-time
  * input sampler: with N = max_len, a sequence of n > N^(alpha/2) tokens is,
  * when u[b] < 1 - N^alpha / n^2 (float64), replaced by k = floor(N^(alpha/2))

@@ -28,7 +28,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 16
+    assert len(names) == 18
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.EXPORTS)
@@ -242,3 +242,19 @@ def test_sl_entry_points_check_arguments(lib):
     assert g(sr=0) == _lib.HSTU_ERR_INVALID_ARG
     assert g(rb=-8) == _lib.HSTU_ERR_INVALID_ARG
     assert g(mr=0, src=None) == _lib.HSTU_OK                            # nothing to copy
+
+
+def test_bwd_entry_point_checks_arguments(lib):
+    R = ctypes.byref
+    gr = _lib.HstuGrads(*([FAKE] * 10))
+    w = _lib.HstuWeights(*([FAKE] * 8))
+    t = _lib.HstuBiasTables(FAKE, FAKE, 129, 64)
+    call = lambda d, gg=gr, dy=FAKE, ws=FAKE, wb=1 << 40: lib.hstu_layer_bwd(
+        R(d), FAKE, FAKE, 4, 1000, FAKE, None, R(w), R(t), dy, FAKE, R(gg), ws, wb, None)
+    assert call(_desc(dqk=64, dv=128)) == _lib.HSTU_ERR_UNSUPPORTED          # dqk != dv
+    assert call(_desc(num_types=2)) == _lib.HSTU_ERR_UNSUPPORTED
+    assert call(_desc(), dy=None) == _lib.HSTU_ERR_INVALID_ARG
+    assert call(_desc(), gg=_lib.HstuGrads(*([FAKE] * 9 + [None]))) == _lib.HSTU_ERR_INVALID_ARG
+    assert call(_desc(), ws=None) == _lib.HSTU_ERR_WORKSPACE
+    assert lib.hstu_bwd_workspace_size(R(_desc()), 1000, 4) > lib.hstu_workspace_size(R(_desc()), 1000, 4)
+    assert lib.hstu_bwd_workspace_size(R(_desc(dqk=64, dv=32)), 1000, 4) == 0
