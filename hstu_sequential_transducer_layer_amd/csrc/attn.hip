@@ -273,19 +273,19 @@ __device__ __forceinline__ void elems(const f32x16& s, float (&p)[16], int kb, c
       const int r = 4 * g + e, c = kb + 8 * g + e;
       float v;
       if (MODE == 0) {
-        v = silu(s[r] + x.c_lo);
+        v = silu_neglog2e(s[r], x.c_lo);
       } else if (MODE == 1) {
-        v = silu(s[r] + (rel[e] <= x.thr ? x.c_hi : x.c_lo));
+        v = silu_neglog2e(s[r], rel[e] <= x.thr ? x.c_hi : x.c_lo);
       } else if (MODE == 2) {
         const int bt = time_bucket_small((int)((uint32_t)x.hi32 - (uint32_t)rel[e]), x.NB, x.sbits);
         const int d = min(max(x.pq0 - c, -x.R), x.R);  // p(i) - p(j), clamped
-        v = silu(s[r] + (x.time_s[bt] + x.pos_s[x.R + d]));
+        v = silu_neglog2e(s[r], x.time_s[bt] + x.pos_s[x.R + d]);
         v = c <= x.iq0 ? v : 0.f;                     // j <= i
       } else {
         const int j = x.jq + c;
         const int bt = time_bucket(wrap_sub(x.ts_q, x.ts[min(j, x.L - 1)]), x.NB, x.sbits);
         const float b = x.time_s[bt] + x.pos_s[pos_bucket(x.p_q, position(j, x.nh, x.shared), x.R)];
-        v = silu(s[r] + b);
+        v = silu_neglog2e(s[r], b);
         v = attends(x.iq, j, x.nh) ? v : 0.f;
       }
       p[r] = v;
@@ -460,7 +460,8 @@ __global__ __launch_bounds__(256, attn_min_blocks((DQK + DV) * (int)sizeof(T) + 
   const int i0 = (CACHED ? (tl.y & 0xFFFFFF) : tl.y) * C::BM;
   const int iend = min(i0 + C::BM, Lq);
   const int N_b = CACHED ? L + max(a.mtotal[tl.x], Lq) : L;
-  const float inv_n = 1.0f / (float)(a.norm_len > 0 ? a.norm_len : N_b);
+  // weights come out scaled by -log2(e) (silu_neglog2e): undone with 1/N_b
+  const float inv_n = kNegLn2 / (float)(a.norm_len > 0 ? a.norm_len : N_b);
   const int R = (a.P - 1) / 2;
   const bool shared = a.shared_pos != 0;
 
@@ -506,11 +507,13 @@ __global__ __launch_bounds__(256, attn_min_blocks((DQK + DV) * (int)sizeof(T) + 
   longlong2 tb0 = {0, 0}, tb1 = {0, 0};
   if (nblk > 0) issue(0, Ks0, Vs0, rel_s[0], kty_s[0], tb0);
 
-  // Bias tables of head h, as fp32, into LDS.
+  // Bias tables of head h, as fp32 times -log2(e), into LDS (the weights take
+  // s * -log2(e) + bias in one fused multiply-add; the type table stays
+  // unscaled: its term is added to the score on the matrix cores).
   for (int i = tid; i < a.P; i += C::NT)
-    pos_s[i] = to_f32(reinterpret_cast<const T*>(a.pos_tab)[(int64_t)h * a.pos_stride + i]);
+    pos_s[i] = kNegLog2e * to_f32(reinterpret_cast<const T*>(a.pos_tab)[(int64_t)h * a.pos_stride + i]);
   for (int i = tid; i < a.NB; i += C::NT)
-    time_s[i] = to_f32(reinterpret_cast<const T*>(a.time_tab)[(int64_t)h * a.time_stride + i]);
+    time_s[i] = kNegLog2e * to_f32(reinterpret_cast<const T*>(a.time_tab)[(int64_t)h * a.time_stride + i]);
   if (TYPED)
     for (int i = tid; i < a.NT * a.NT; i += C::NT)
       type_s[i] = to_f32(reinterpret_cast<const T*>(a.type_tab)[(int64_t)h * a.type_stride + i]);
@@ -644,7 +647,7 @@ __global__ __launch_bounds__(256, attn_min_blocks((DQK + DV) * (int)sizeof(T) + 
       for (int e = 0; e < 8; ++e) dot += to_f32(qf[c][e]) * to_f32(kf[e]);
     }
     dot += __shfl_xor(dot, 32, kWave);
-    const float wself = silu(dot + pos_s[R] + time_s[0] + (TYPED ? type_s[ty_q * a.NT + ty_q] : 0.f));
+    const float wself = silu_neglog2e(dot + (TYPED ? type_s[ty_q * a.NT + ty_q] : 0.f), pos_s[R] + time_s[0]);
     const T* vs = reinterpret_cast<const T*>(a.qv) + ((int64_t)h * a.T + s0 + iq) * DV;
 #pragma unroll
     for (int n = 0; n < DV / 32; ++n)

@@ -76,14 +76,53 @@ __device__ __forceinline__ typename Elem<T>::Frag bwd_row_frag(const T* lds, int
   }
 }
 
-// A operand from tile columns: feature f of the eight rows
-// kb + 8 (e / 4) + 4 half + e % 4 (the k order of an accumulator-fed B operand).
+typedef short bwd_v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bwd_v4i16 bwd_lds_v4i16;
+
+// A operand from tile columns: feature f = 32 nt + lane % 32 of the eight rows
+// kb + 8 (e / 4) + 4 half + e % 4 (the k order of an accumulator-fed B
+// operand).  bf16: two transposing 8-byte LDS reads; within each 16-lane group
+// of a ds_read_b64_tr_b16, lane l receives element l % 4 of the 4-element
+// pieces addressed by lanes l / 4, 4 + l / 4, 8 + l / 4, 12 + l / 4, so lane a
+// of the group addresses row kb + 4 half + a / 4, columns 32 nt + 16 ((lane /
+// 16) % 2) + 4 (a % 4) .. + 3 (and the same 8 rows further).  fp32: element
+// by element.
 template <typename T, int D>
-__device__ __forceinline__ typename Elem<T>::Frag bwd_col_frag(const T* lds, int kb, int f, int half) {
+__device__ __forceinline__ typename Elem<T>::Frag bwd_col_frag(const T* lds, int kb, int nt, int lane) {
   typename Elem<T>::Frag x;
+  const int half = lane >> 5;
+  if constexpr (Elem<T>::kVec == 8) {
+    const int a = lane & 15;
+    const int row = kb + 4 * half + (a >> 2);
+    const int col = 32 * nt + 16 * ((lane >> 4) & 1) + 4 * (a & 3);
+    const bwd_v4i16 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((bwd_lds_v4i16*)(lds + row * BTile<T, D>::LD + col));
+    const bwd_v4i16 x1 =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((bwd_lds_v4i16*)(lds + (row + 8) * BTile<T, D>::LD + col));
+    const bf16* p0 = reinterpret_cast<const bf16*>(&x0);
+    const bf16* p1 = reinterpret_cast<const bf16*>(&x1);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) x[e] = lds[(kb + 8 * (e >> 2) + 4 * half + (e & 3)) * BTile<T, D>::LD + f];
+    for (int e = 0; e < 4; ++e) {
+      x[e] = p0[e];
+      x[4 + e] = p1[e];
+    }
+  } else {
+    const int f = 32 * nt + (lane & 31);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = lds[(kb + 8 * (e >> 2) + 4 * half + (e & 3)) * BTile<T, D>::LD + f];
+  }
   return x;
+}
+
+// Min and max of 64 int64 values held one per lane (wave 0 of a block copy).
+__device__ __forceinline__ void bwd_minmax64(int64_t v, int64_t& mn, int64_t& mx) {
+  mn = v;
+  mx = v;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const int64_t a = __shfl_xor(mn, o, kWave), b = __shfl_xor(mx, o, kWave);
+    mn = a < mn ? a : mn;
+    mx = b > mx ? b : mx;
+  }
 }
 
 template <typename T>
@@ -104,6 +143,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) T Ks[64 * BTile<T, DQK>::LD];
   __shared__ __attribute__((aligned(16))) T Vs[64 * BTile<T, DV>::LD];
   __shared__ int64_t tsk[64];
+  __shared__ int64_t kmm[2];  // the block's earliest and latest key timestamp
   // pos[P], time[NB], then one gradient histogram [P + NB] per wave (a
   // wave's updates land in program and lane order, so the sums are
   // reproducible; the four are added in wave order at the end)
@@ -177,9 +217,32 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
     __syncthreads();  // the previous block's reads are done
     bwd_copy<T, DQK>(kg + (int64_t)j0 * DQK, DQK, L - j0, Ks);
     bwd_copy<T, DV>(vg + (int64_t)j0 * DV, DV, L - j0, Vs);
-    if (tid < 64) tsk[tid] = a.ts[s0 + min(j0 + tid, L - 1)];
+    if (tid < 64) {
+      const int64_t t = a.ts[s0 + min(j0 + tid, L - 1)];
+      tsk[tid] = t;
+      int64_t mn, mx;
+      bwd_minmax64(t, mn, mx);
+      if (tid == 0) {
+        kmm[0] = mn;
+        kmm[1] = mx;
+      }
+    }
     __syncthreads();
     if (r0 >= iend) continue;
+    // A far block: every key a history key strictly before the wave's first
+    // row and at least R positions from it (position bucket 2R, no mask);
+    // with one time bucket per row over the block's time span, the bias is
+    // one value per row (wave-uniform test).
+    bool fast = j0 + 63 < L && j0 + 63 < nh && j0 + 63 < r0 && position(r0, nh, shared) - (j0 + 63) >= R;
+    int bt_row = 0;
+    float b_row = 0.f;
+    if (fast) {
+      const int lo = time_bucket(wrap_sub(ts_q, kmm[1]), NB, a.sbits);
+      const int hi = time_bucket(wrap_sub(ts_q, kmm[0]), NB, a.sbits);
+      fast = __all(lo == hi || !qvalid);
+      bt_row = lo;
+      b_row = pos_s[2 * R] + time_s[lo];
+    }
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
       f32x16 sc = f32x16{}, da = f32x16{};
@@ -188,6 +251,23 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int c = 0; c < DV / 16; ++c) da = mma_k16(bwd_row_frag<T, DV>(Vs, kh * 32 + l32, 16 * c + 8 * half), df[c], da);
       float ds[16];
+      if (fast) {
+        float sum = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float s = sc[r] + b_row;
+          const float sg = bwd_sigmoid(s);
+          ds[r] = qvalid ? da[r] * sg * (1.0f + s * (1.0f - sg)) * inv_n : 0.f;
+          sum += ds[r];
+        }
+        far_hi += sum;
+        if (bt_row != run_bt) {
+          if (run != 0.f) atomicAdd(&gtime[run_bt], run);
+          run_bt = bt_row;
+          run = 0.f;
+        }
+        run += sum;
+      } else
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int kl = kh * 32 + 8 * (r >> 2) + 4 * half + (r & 3), j = j0 + kl;
@@ -218,7 +298,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
         const Frag pf = bwd_frag<T>(ds + 8 * c2);
 #pragma unroll
         for (int n = 0; n < DQK / 32; ++n)
-          dq[n] = mma_k16(bwd_col_frag<T, DQK>(Ks, kh * 32 + 16 * c2, 32 * n + l32, half), pf, dq[n]);
+          dq[n] = mma_k16(bwd_col_frag<T, DQK>(Ks, kh * 32 + 16 * c2, n, lane), pf, dq[n]);
       }
     }
   }
@@ -248,6 +328,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) T Qs[64 * BTile<T, DQK>::LD];
   __shared__ __attribute__((aligned(16))) T Os[64 * BTile<T, DV>::LD];
   __shared__ int64_t tsq[64];
+  __shared__ int64_t qmm[2];  // the block's earliest and latest query timestamp
   extern __shared__ float tabs[];  // pos[P], time[NB]
   const int H = a.H, h = blockIdx.x % H, item = blockIdx.x / H;
   if (item >= a.counts[0]) return;
@@ -303,9 +384,30 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(BwdArgs a) {
     __syncthreads();
     bwd_copy<T, DQK>(qg + (int64_t)i0 * DQK, DQK, L - i0, Qs);
     bwd_copy<T, DV>(og + (int64_t)i0 * K2, K2, L - i0, Os);
-    if (tid < 64) tsq[tid] = a.ts[s0 + min(i0 + tid, L - 1)];
+    if (tid < 64) {
+      const int64_t t = a.ts[s0 + min(i0 + tid, L - 1)];
+      tsq[tid] = t;
+      int64_t mn, mx;
+      bwd_minmax64(t, mn, mx);
+      if (tid == 0) {
+        qmm[0] = mn;
+        qmm[1] = mx;
+      }
+    }
     __syncthreads();
     if (kr0 >= jend) continue;
+    // A far block (the dq kernel's test with queries and keys swapped): all
+    // the wave's keys history keys strictly before the block's first query
+    // and at least R positions from it; one time bucket per key.
+    const int k_last = min(kr0 + 31, jend - 1);
+    bool fast = i0 + 63 < L && k_last < nh && i0 > k_last && position(i0, nh, shared) - k_last >= R;
+    float b_key = 0.f;
+    if (fast) {
+      const int lo = time_bucket(wrap_sub(qmm[0], ts_k), NB, a.sbits);
+      const int hi = time_bucket(wrap_sub(qmm[1], ts_k), NB, a.sbits);
+      fast = __all(lo == hi || !kvalid);
+      b_key = pos_s[2 * R] + time_s[lo];
+    }
 #pragma unroll
     for (int qh = 0; qh < 2; ++qh) {
       f32x16 sc = f32x16{}, da = f32x16{};
@@ -316,6 +418,15 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(BwdArgs a) {
         for (int c = 0; c < DV / 16; ++c) da = mma_k16(bwd_row_frag<T, DV>(Os, qh * 32 + l32, 16 * c + 8 * half), vf[c], da);
       }
       float g[16];
+      if (fast) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float s = sc[r] + b_key;
+          const float sg = bwd_sigmoid(s);
+          const float val = DK ? da[r] * sg * (1.0f + s * (1.0f - sg)) * inv_n : s * sg * inv_n;
+          g[r] = kvalid ? val : 0.f;
+        }
+      } else
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int ql = qh * 32 + 8 * (r >> 2) + 4 * half + (r & 3), i = i0 + ql;
@@ -332,8 +443,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(BwdArgs a) {
         const Frag pf = bwd_frag<T>(g + 8 * c2);
 #pragma unroll
         for (int n = 0; n < DACC / 32; ++n) {
-          const Frag af = DK ? bwd_col_frag<T, DQK>(Qs, qh * 32 + 16 * c2, 32 * n + l32, half)
-                             : bwd_col_frag<T, DV>(Os, qh * 32 + 16 * c2, 32 * n + l32, half);
+          const Frag af = DK ? bwd_col_frag<T, DQK>(Qs, qh * 32 + 16 * c2, n, lane)
+                             : bwd_col_frag<T, DV>(Os, qh * 32 + 16 * c2, n, lane);
           acc[n] = mma_k16(af, pf, acc[n]);
         }
       }

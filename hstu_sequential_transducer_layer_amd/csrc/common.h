@@ -105,6 +105,16 @@ __device__ __forceinline__ float silu(float z) {
   return z * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
+// -log2(e) * SiLU(s + b), given bn = -log2(e) * b: z' = -log2(e) (s + b) in one
+// fused multiply-add, then z' / (1 + 2^z').  Callers fold the constant
+// -ln(2) = 1 / -log2(e) into a later scale.
+constexpr float kNegLog2e = -1.4426950408889634f;
+constexpr float kNegLn2 = -0.6931471805599453f;
+__device__ __forceinline__ float silu_neglog2e(float s, float bn) {
+  const float z = __builtin_fmaf(s, kNegLog2e, bn);
+  return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z));
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);

@@ -14,6 +14,11 @@ FP32_TOL = 1e-4   # every tap: max |y - ref| / max(|ref|, rms(ref))
 BF16_TOL = 2e-2   # output y: max |y - ref| / rms(ref) (unit scale);
                   # intermediate taps: max |y - ref| / max(|ref|, rms(ref)), since
                   # storing a tap in bf16 alone costs up to 2^-9 |ref| per element
+BF16_AV_TOL = 4e-2  # the attention tap av against the oracle fed the GPU's own
+                  # q, k, v: the kernel rounds each pointwise weight to bf16 for
+                  # the A.V product, and on the edge workloads that rounding
+                  # alone reaches 2.7e-2 on this metric (tests/test_bf16_rounding.py
+                  # computes it on the CPU); 1.5x that
 
 
 def say(msg: str) -> None:
@@ -72,11 +77,12 @@ def err_fp32(got, ref) -> float:
     return float(np.max(np.abs(np.asarray(got, np.float64) - ref) / den))
 
 
-def check(name: str, got, ref, dtype: str, unit: bool = False) -> float:
+def check(name: str, got, ref, dtype: str, unit: bool = False, tol: float = None) -> float:
     """unit=True: the unit-scale criterion (bf16 outputs); else element-relative
-    with an rms floor."""
+    with an rms floor.  tol overrides the dtype's default."""
     e = err_bf16(got, ref) if (unit and dtype == "bf16") else err_fp32(got, ref)
-    tol = FP32_TOL if dtype == "fp32" else BF16_TOL
+    if tol is None:
+        tol = FP32_TOL if dtype == "fp32" else BF16_TOL
     say(f"  {name}: err {e:.3e} (tol {tol:.0e})")
     assert np.all(np.isfinite(got)), f"{name}: non-finite values"
     assert e <= tol, f"{name}: error {e:.3e} > {tol:.0e}"

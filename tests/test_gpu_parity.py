@@ -3,7 +3,9 @@
 Tolerances: fp32 layers max |y - ref| / max(|ref|, rms(ref)) <= 1e-4 at every
 tap; bf16 layers max |y - ref| / rms(ref) <= 2e-2 on the unit-scale output y,
 and max |y - ref| / max(|ref|, rms(ref)) <= 2e-2 on the intermediate taps
-(u, v, q, k, av, z = LayerNorm(av) * u), which are stored in bf16.  Integer indexing is compared bitwise.  Full-size
+(u, v, q, k, z = LayerNorm(av) * u), which are stored in bf16, and <= 4e-2 on
+av (gpu_helpers.BF16_AV_TOL: the bf16 rounding of the pointwise weights
+alone reaches 2.7e-2 there).  Integer indexing is compared bitwise.  Full-size
 workloads run on the GPU in full; the oracle recomputes a stated subset of
 their sequences (sequences are independent, so those rows are exact
 references), and the invariants below hold at any size.
@@ -52,7 +54,8 @@ def _compare_layer(w, seqs=None, layer_idx=0):
         errs[t] = check(t, g[t][rows], ref[t], dt)
     av_iso = O.attention(g["q"][rows], g["k"][rows], g["v"][rows], sub.offsets, sub.timestamps,
                          sub.num_candidates, prm, w.dims)
-    errs["av"] = check("av (stage)", g["av"][rows], av_iso, dt)
+    from gpu_helpers import BF16_AV_TOL
+    errs["av"] = check("av (stage)", g["av"][rows], av_iso, dt, tol=BF16_AV_TOL if dt == "bf16" else None)
     out_iso = O.gate_and_project(g["av"][rows], g["u"][rows], sub.x, prm, w.dims)
     errs["z"] = check("z (stage)", g["z"][rows], out_iso["z"], dt)
     errs["y_stage"] = check("y (stage)", g["y"][rows], out_iso["y"], dt, unit=True)
