@@ -299,6 +299,8 @@ struct QueryRow {
   int r0, rlast, iq, p_q, pmin_q;  // wave's first / last row, this row, positions
   bool qvalid;
   int64_t ts_q;
+  int32_t rq;   // ts_q - t0 when every row of the wave is within 2^29 of t0 (narrow)
+  bool narrow;  // wave-uniform
 };
 
 // Per-(workgroup) constants of the classification.
@@ -309,6 +311,7 @@ struct SeqCtx {
   const float* pos_s;
   const float* time_s;
   const int64_t* ts;  // the sequence's timestamps
+  int64_t t0;         // reference time of the 32-bit classification: the first key's
 };
 
 // Whether any row of the wave (which has rows) attends a key of the block
@@ -323,41 +326,68 @@ __device__ __forceinline__ bool block_active(int j0, const QueryRow& q, const Se
 // context of the weight step.  Per query row the block's time differences lie
 // in [lo, hi]; the bucket is monotone in dt, so one bucket, or two split by a
 // threshold on the key's time offset, covers the whole row.
+//
+// When the block's and the wave's timestamps all lie within 2^29 of the
+// reference t0 (the usual case; a wave-uniform test on scalars), the row's
+// range comes from 32-bit differences of times relative to t0; otherwise from
+// overflow-checked 64-bit ones.  The mode-1 threshold and second bias are
+// only formed when mode 1 is chosen.
 __device__ __forceinline__ int classify_block(int j0, int64_t tmin, int64_t tmax, const QueryRow& q,
                                               const SeqCtx& sq, const int32_t* rb, ElemCtx& x) {
   const bool full = (j0 + kAttnBN - 1 <= q.r0) && (j0 + kAttnBN <= sq.nh);
   const int pmax_k = position(min(j0 + kAttnBN - 1, sq.L - 1), sq.nh, sq.shared);
   const bool pos_far = q.pmin_q - pmax_k >= sq.R;  // clamped position bias is constant
-  int64_t span;
-  const bool span_ok = !__builtin_sub_overflow(tmax, tmin, &span) && span <= INT32_MAX;
+  constexpr int64_t kNear = (int64_t)1 << 29;
+  int64_t dmin = 0, dmax = 0;
+  const bool narrow = q.narrow && !__builtin_sub_overflow(tmin, sq.t0, &dmin) &&
+                      !__builtin_sub_overflow(tmax, sq.t0, &dmax) && dmin > -kNear && dmin < kNear &&
+                      dmax > -kNear && dmax < kNear;
+  bool novf, span_ok;
   int64_t lo, hi;
-  const bool novf = !__builtin_sub_overflow(q.ts_q, tmax, &lo) && !__builtin_sub_overflow(q.ts_q, tmin, &hi);
+  if (narrow) {  // |t - t0| < 2^29 for every time involved: 32-bit differences are exact
+    novf = true;
+    span_ok = true;
+    lo = q.rq - (int32_t)dmax;
+    hi = q.rq - (int32_t)dmin;
+  } else {
+    int64_t span;
+    span_ok = !__builtin_sub_overflow(tmax, tmin, &span) && span <= INT32_MAX;
+    novf = !__builtin_sub_overflow(q.ts_q, tmax, &lo) && !__builtin_sub_overflow(q.ts_q, tmin, &hi);
+  }
   const bool small = novf && hi < (1 << 24) && lo > -(1 << 24);
   const bool all_small = __builtin_amdgcn_readfirstlane(__all(small || !q.qvalid) ? 1 : 0) != 0;
   int bt_lo, bt_hi;
-  int32_t thr;
   if (all_small) {
     bt_lo = time_bucket_small((int)lo, sq.NB, sq.sbits);
     bt_hi = time_bucket_small((int)hi, sq.NB, sq.sbits);
-    thr = (int)hi - bucket_floor_small(max(bt_hi, 1), sq.sbits);
   } else {
     bt_lo = time_bucket(lo, sq.NB, sq.sbits);
     bt_hi = time_bucket(hi, sq.NB, sq.sbits);
-    const int64_t tt = hi - bucket_floor(max(bt_hi, 1), sq.sbits);
-    thr = tt > INT32_MAX ? INT32_MAX : (int32_t)tt;
   }
   const bool one = novf && bt_lo == bt_hi;
   const bool two = novf && span_ok && bt_hi == bt_lo + 1;
   // Fast modes: no mask, constant position bias, and per row at most two
   // time buckets (decided for the whole wave).
   const bool fast = full && pos_far && __all(one || two || !q.qvalid);
-  const float c_lo = sq.time_s[bt_lo] + sq.cpos_far, c_hi = sq.time_s[bt_hi] + sq.cpos_far;
+  const float c_lo = sq.time_s[bt_lo] + sq.cpos_far;
   const bool hist_only = j0 + kAttnBN <= sq.nh;
   const int jq = j0 + 4 * (int)((threadIdx.x >> 5) & 1);
+  const int mode = __builtin_amdgcn_readfirstlane(!fast ? (all_small && hist_only ? 2 : 3)
+                                                         : (__all(one || !q.qvalid) ? 0 : 1));
+  float c_hi = c_lo;
+  int32_t thr = 0;
+  if (mode == 1) {
+    c_hi = sq.time_s[bt_hi] + sq.cpos_far;
+    if (all_small) {
+      thr = (int)hi - bucket_floor_small(max(bt_hi, 1), sq.sbits);
+    } else {
+      const int64_t tt = hi - bucket_floor(max(bt_hi, 1), sq.sbits);
+      thr = tt > INT32_MAX ? INT32_MAX : (int32_t)tt;
+    }
+  }
   x = ElemCtx{jq, q.iq, sq.nh, q.p_q, sq.R, sq.NB, sq.sbits, sq.L, sq.shared, c_lo, c_hi, thr, (int32_t)hi,
               q.p_q - jq, q.iq - jq, q.ts_q, sq.pos_s, sq.time_s, rb + (jq - j0), sq.ts};
-  return __builtin_amdgcn_readfirstlane(!fast ? (all_small && hist_only ? 2 : 3)
-                                              : (__all(one || !q.qvalid) ? 0 : 1));
+  return mode;
 }
 
 // Weights of 32-key half kh in the wave's mode.
@@ -560,9 +590,16 @@ __global__ __launch_bounds__(256, attn_min_blocks((DQK + DV) * (int)sizeof(T) + 
   }
 
   // One block of work out of buffer set (Kb, Vb, rb).
-  const QueryRow qr = CACHED ? QueryRow{nh - 1, nh - 1, nh - 1, p_q, pmin_q, qvalid, ts_q}
-                             : QueryRow{r0, rlast, iq, p_q, pmin_q, qvalid, ts_q};
-  const SeqCtx sq{L, nh, R, a.NB, a.sbits, shared, cpos_far, pos_s, time_s, a.kts + k0};
+  // reference time of the 32-bit classification: the first key row's
+  const int64_t t0 = L > 0 ? uniform64(a.kts[k0]) : 0;
+  constexpr int64_t kNear = (int64_t)1 << 29;
+  int64_t dq = 0;
+  const bool q_near = !qvalid || (!__builtin_sub_overflow(ts_q, t0, &dq) && dq > -kNear && dq < kNear);
+  const bool q_narrow = __builtin_amdgcn_readfirstlane(__all(q_near) ? 1 : 0) != 0;
+  const int32_t rq = qvalid && q_near ? (int32_t)dq : 0;
+  const QueryRow qr = CACHED ? QueryRow{nh - 1, nh - 1, nh - 1, p_q, pmin_q, qvalid, ts_q, rq, q_narrow}
+                             : QueryRow{r0, rlast, iq, p_q, pmin_q, qvalid, ts_q, rq, q_narrow};
+  const SeqCtx sq{L, nh, R, a.NB, a.sbits, shared, cpos_far, pos_s, time_s, a.kts + k0, t0};
   auto consume = [&](int blk, const T* Kb, const T* Vb, const int32_t* rb, const int32_t* yb, int64_t tmin,
                      int64_t tmax) __attribute__((always_inline)) {
     const int j0 = block_start(blk);
