@@ -26,6 +26,7 @@ EXPORTS = [
     "hstu_workspace_size", "hstu_layer_fwd", "hstu_proj_workspace_size", "hstu_proj_fwd",
     "hstu_attn_workspace_size", "hstu_attn_fwd", "hstu_gate_fwd", "hstu_out_fwd",
     "hstu_cand_workspace_size", "hstu_cand_fwd", "hstu_bwd_workspace_size", "hstu_layer_bwd",
+    "hstu_attn_bwd_workspace_size", "hstu_attn_bwd",
     "hstu_sl_workspace_size", "hstu_sl_sample",
     "hstu_gather_rows", "hstu_debug_indices",
     "hstu_status_str", "hstu_last_error",
@@ -109,13 +110,17 @@ def load() -> ctypes.CDLL:
     lib.hstu_bwd_workspace_size.restype = sz
     lib.hstu_layer_bwd.argtypes = [P(HstuDesc), vp, vp, i32, i64, vp, vp, P(HstuWeights), P(HstuBiasTables),
                                    vp, vp, P(HstuGrads), vp, sz, vp]
+    lib.hstu_attn_bwd_workspace_size.argtypes = [P(HstuDesc), i64, i32]
+    lib.hstu_attn_bwd_workspace_size.restype = sz
+    lib.hstu_attn_bwd.argtypes = [P(HstuDesc), vp, i32, i64, vp, vp, P(HstuBiasTables), P(HstuActivations),
+                                  vp, vp, vp, vp, vp, sz, vp]
     lib.hstu_sl_workspace_size.argtypes = [i32]
     lib.hstu_sl_workspace_size.restype = sz
     lib.hstu_sl_sample.argtypes = [vp, i32, i64, i32, ctypes.c_float, vp, vp, vp, vp, vp, sz, vp]
     lib.hstu_gather_rows.argtypes = [vp, i64, i64, vp, vp, i64, vp, vp]
     lib.hstu_debug_indices.argtypes = [P(HstuDesc), vp, i32, i64, vp, vp, vp, i64, vp, vp]
     for f in ("hstu_layer_fwd", "hstu_proj_fwd", "hstu_attn_fwd", "hstu_gate_fwd", "hstu_out_fwd",
-              "hstu_cand_fwd", "hstu_layer_bwd", "hstu_sl_sample", "hstu_gather_rows", "hstu_debug_indices"):
+              "hstu_cand_fwd", "hstu_layer_bwd", "hstu_attn_bwd", "hstu_sl_sample", "hstu_gather_rows", "hstu_debug_indices"):
         getattr(lib, f).restype = ctypes.c_int
     lib.hstu_status_str.argtypes = [ctypes.c_int]
     lib.hstu_status_str.restype = ctypes.c_char_p
@@ -349,6 +354,25 @@ def layer_bwd(desc: HstuDesc, x: torch.Tensor, seq_offsets: torch.Tensor, timest
                               _ptr(num_candidates), ctypes.byref(w), ctypes.byref(t), _ptr(dy), _ptr(dx),
                               ctypes.byref(g), _ptr(workspace), workspace.numel(), _stream()))
     return dx, grads
+
+
+def attn_bwd(desc: HstuDesc, seq_offsets, timestamps, num_candidates, prm, acts, dav: torch.Tensor):
+    """hstu_attn_bwd; returns (dqkv [T, N1] fp32 with the v, q, k column blocks
+    written, dpos, dtime)."""
+    lib = load()
+    T, B = dav.shape[0], seq_offsets.shape[0] - 1
+    dev = dav.device
+    n1 = 2 * desc.num_heads * (desc.dqk + desc.dv)
+    dqkv = torch.zeros(T, n1, dtype=torch.float32, device=dev)
+    dpos = torch.empty(prm["pos_table"].shape, dtype=torch.float32, device=dev)
+    dtime = torch.empty(prm["time_table"].shape, dtype=torch.float32, device=dev)
+    need = int(lib.hstu_attn_bwd_workspace_size(ctypes.byref(desc), T, B))
+    ws = alloc_workspace(need, dev)
+    a, t = _acts(acts), make_tables(prm)
+    _check(lib.hstu_attn_bwd(ctypes.byref(desc), _ptr(seq_offsets), B, T, _ptr(timestamps),
+                             _ptr(num_candidates), ctypes.byref(t), ctypes.byref(a), _ptr(dav), _ptr(dqkv),
+                             _ptr(dpos), _ptr(dtime), _ptr(ws), ws.numel(), _stream()))
+    return dqkv, dpos, dtime
 
 
 def sl_sample(seq_offsets: torch.Tensor, u: torch.Tensor, keys: torch.Tensor, max_len: int,

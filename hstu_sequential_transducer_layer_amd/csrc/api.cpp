@@ -620,6 +620,53 @@ hstu_status hstu_layer_bwd(const hstu_desc* desc, const void* x, const int64_t* 
   return ok();
 }
 
+static size_t attn_bwd_ws(const hstu_desc* d, int64_t T, int32_t B, size_t* part_off) {
+  const size_t a = align256(hstu::attn_scratch_bytes(T, B));
+  if (part_off) *part_off = a;
+  return a + align256((size_t)hstu::attn_max_tiles(T, B) * d->num_heads * (d->pos_buckets + d->time_buckets) * 4);
+}
+
+size_t hstu_attn_bwd_workspace_size(const hstu_desc* desc, int64_t T, int32_t B) {
+  if (check_bwd_desc(desc) != HSTU_OK || check_sizes(T, B) != HSTU_OK) return 0;
+  return attn_bwd_ws(desc, T, B, nullptr);
+}
+
+hstu_status hstu_attn_bwd(const hstu_desc* desc, const int64_t* off, int32_t B, int64_t T, const int64_t* ts,
+                          const int32_t* nc, const hstu_bias_tables* tables, const hstu_activations* acts,
+                          const void* dav, float* dqkv, float* dpos, float* dtime, void* ws, size_t ws_bytes,
+                          hstu_stream_t stream) {
+  hstu_status st;
+  if ((st = check_bwd_desc(desc)) != HSTU_OK) return st;
+  if ((st = check_sizes(T, B)) != HSTU_OK) return st;
+  if (T == 0) return ok();
+  if ((st = check_meta(off, B, ts, nc)) != HSTU_OK) return st;
+  if ((st = check_tables(desc, tables)) != HSTU_OK) return st;
+  if (!acts) return fail(HSTU_ERR_INVALID_ARG, "acts is NULL");
+  HSTU_REQ(acts->q, 16, "acts->q");
+  HSTU_REQ(acts->k, 16, "acts->k");
+  HSTU_REQ(acts->v, 16, "acts->v");
+  HSTU_REQ(dav, 16, "dav");
+  HSTU_REQ(dqkv, 16, "dqkv");
+  HSTU_REQ(dpos, 4, "dpos");
+  HSTU_REQ(dtime, 4, "dtime");
+  size_t part_off = 0;
+  const size_t need = attn_bwd_ws(desc, T, B, &part_off);
+  if (!ws || ws_bytes < need || !aligned(ws, 256))
+    return fail(HSTU_ERR_WORKSPACE, "workspace: need %zu bytes (256-aligned), got %zu", need, ws_bytes);
+  hipStream_t s = (hipStream_t)stream;
+  if (desc->flags & HSTU_VALIDATE)
+    if ((st = validate_metadata(off, B, T, nc, s)) != HSTU_OK) return st;
+  const hstu::AttnScratch sc = hstu::attn_scratch(ws, T, B);
+  if (!(desc->flags & HSTU_REUSE_PLAN)) {
+    const hstu::AttnRows rows{off, nc, ts, T, off, ts, T, nullptr, B, false, layer_types(desc, tables)};
+    if ((st = device(hstu::launch_attn_prep(rows, hstu::kAttnBM, sc, s), "attention prep launch")) != HSTU_OK)
+      return st;
+  }
+  return device(hstu::launch_attn_bwd(*desc, off, nc, B, T, ts, *tables, acts->q, acts->k, acts->v, dav, dqkv,
+                                      (float*)((char*)ws + part_off), dpos, dtime, sc, s),
+                "attention backward launch");
+}
+
 size_t hstu_sl_workspace_size(int32_t B) { return B < 0 ? 0 : align256(((size_t)B + 1) * sizeof(int32_t)); }
 
 hstu_status hstu_sl_sample(const int64_t* off, int32_t B, int64_t T, int32_t max_len, float alpha, const float* u,

@@ -287,6 +287,20 @@ hstu_status hstu_layer_bwd(const hstu_desc* desc, const void* x, const int64_t* 
                            void* dx, const hstu_grads* grads, void* workspace, size_t workspace_bytes,
                            hstu_stream_t stream);
 
+/* The attention stage of the backward alone ([SRM] second layer equation;
+ * the gradient of AV = sum_j a_ij v_j, a_ij = M_ij SiLU(S_ij) / N_b): reads
+ * acts->q, k, v and dav = dL/dAV [T, H*dv] (layer dtype, row-major), writes
+ * dqkv [T, N1] fp32 in the columns of the u|v|q|k split: dL/dv, dL/dq and
+ * dL/dk (the u block is left untouched), and the position / time table
+ * gradients (fp32, laid out like the tables' gradients in hstu_grads).
+ * Limits as hstu_layer_bwd; HSTU_REUSE_PLAN as in hstu_attn_fwd.
+ *   workspace >= hstu_attn_bwd_workspace_size(desc, T, B) bytes, 256-aligned */
+size_t hstu_attn_bwd_workspace_size(const hstu_desc* desc, int64_t total_tokens, int32_t batch);
+hstu_status hstu_attn_bwd(const hstu_desc* desc, const int64_t* seq_offsets, int32_t batch, int64_t total_tokens,
+                          const int64_t* timestamps, const int32_t* num_candidates, const hstu_bias_tables* tables,
+                          const hstu_activations* acts, const void* dav, float* dqkv, float* dpos, float* dtime,
+                          void* workspace, size_t workspace_bytes, hstu_stream_t stream);
+
 /* Stochastic length ([FRC] 7.1.5 "Stochastic Length"), the training-time
  * input sampler: with N = max_len, a sequence of n > N^(alpha/2) tokens is,
  * when u[b] < 1 - N^alpha / n^2 (float64), replaced by k = floor(N^(alpha/2))

@@ -41,17 +41,9 @@ def _indices(offsets, timestamps, num_candidates, cfg, b):
     return s0, s1, torch.from_numpy(M), torch.from_numpy(bp), torch.from_numpy(bt), N
 
 
-def forward(x, offsets, timestamps, num_candidates, prm, cfg):
-    """y [T, d] as a torch float64 graph; x and prm are torch float64 tensors."""
-    T = x.shape[0]
-    H, dqk, dv = cfg.num_heads, cfg.dqk, cfg.dv
-    xin = F.layer_norm(x, (x.shape[1],), prm["ln_in_g"], prm["ln_in_b"], cfg.ln_eps) if cfg.input_norm else x
-    act = F.silu(xin @ prm["w1"].T + prm["b1"])
-    c0, c1, c2 = H * dv, 2 * H * dv, 2 * H * dv + H * dqk
-    u = act[:, :c0]
-    v = act[:, c0:c1].reshape(T, H, dv)
-    q = act[:, c1:c2].reshape(T, H, dqk)
-    k = act[:, c2:].reshape(T, H, dqk)
+def attention(q, k, v, offsets, timestamps, num_candidates, prm, cfg):
+    """AV [T, H*dv] from q, k [T, H, dqk] and v [T, H, dv] (torch float64)."""
+    T, H, dv = v.shape
     B = len(offsets) - 1
     rows = []
     for b in range(B):
@@ -64,7 +56,34 @@ def forward(x, offsets, timestamps, num_candidates, prm, cfg):
             A = torch.where(M, F.silu(S), torch.zeros((), dtype=S.dtype)) / N
             heads.append(A @ v[s0:s1, h])
         rows.append(torch.cat(heads, dim=1))
-    av = torch.cat(rows, dim=0) if rows else torch.zeros(0, H * dv, dtype=x.dtype)
+    return torch.cat(rows, dim=0) if rows else torch.zeros(0, H * dv, dtype=v.dtype)
+
+
+def attention_grads(q, k, v, dav, offsets, timestamps, num_candidates, prm, cfg):
+    """float64 NumPy gradients of sum(AV * dav) with respect to q, k [T, H, dqk],
+    v [T, H, dv] and the position and time tables (the attention stage alone)."""
+    qt, kt, vt = (torch.tensor(np.asarray(a, np.float64), requires_grad=True) for a in (q, k, v))
+    pt = {n: torch.tensor(np.asarray(prm[n], np.float64), requires_grad=True) for n in ("pos_table", "time_table")}
+    av = attention(qt, kt, vt, offsets, timestamps, num_candidates, pt, cfg)
+    g = torch.autograd.grad((av * torch.from_numpy(np.asarray(dav, np.float64))).sum(),
+                            [qt, kt, vt, pt["pos_table"], pt["time_table"]], allow_unused=True)
+    names = ("q", "k", "v", "pos_table", "time_table")
+    refs = (qt, kt, vt, pt["pos_table"], pt["time_table"])
+    return {n: (np.zeros(r.shape) if x is None else x.numpy()) for n, x, r in zip(names, g, refs)}
+
+
+def forward(x, offsets, timestamps, num_candidates, prm, cfg):
+    """y [T, d] as a torch float64 graph; x and prm are torch float64 tensors."""
+    T = x.shape[0]
+    H, dqk, dv = cfg.num_heads, cfg.dqk, cfg.dv
+    xin = F.layer_norm(x, (x.shape[1],), prm["ln_in_g"], prm["ln_in_b"], cfg.ln_eps) if cfg.input_norm else x
+    act = F.silu(xin @ prm["w1"].T + prm["b1"])
+    c0, c1, c2 = H * dv, 2 * H * dv, 2 * H * dv + H * dqk
+    u = act[:, :c0]
+    v = act[:, c0:c1].reshape(T, H, dv)
+    q = act[:, c1:c2].reshape(T, H, dqk)
+    k = act[:, c2:].reshape(T, H, dqk)
+    av = attention(q, k, v, offsets, timestamps, num_candidates, prm, cfg)
     z = F.layer_norm(av, (H * dv,), prm["ln_av_g"], prm["ln_av_b"], cfg.ln_eps) * u
     y = z @ prm["w2"].T + prm["b2"]
     return y + x if cfg.residual else y

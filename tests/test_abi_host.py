@@ -28,7 +28,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 18
+    assert len(names) == 20
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.EXPORTS)
@@ -258,3 +258,16 @@ def test_bwd_entry_point_checks_arguments(lib):
     assert call(_desc(), ws=None) == _lib.HSTU_ERR_WORKSPACE
     assert lib.hstu_bwd_workspace_size(R(_desc()), 1000, 4) > lib.hstu_workspace_size(R(_desc()), 1000, 4)
     assert lib.hstu_bwd_workspace_size(R(_desc(dqk=64, dv=32)), 1000, 4) == 0
+
+
+def test_attn_bwd_entry_point_checks_arguments(lib):
+    R = ctypes.byref
+    a = _lib.HstuActivations(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    t = _lib.HstuBiasTables(FAKE, FAKE, 129, 64)
+    call = lambda d, dav=FAKE, acts=a, ws=FAKE: lib.hstu_attn_bwd(R(d), FAKE, 4, 1000, FAKE, None, R(t), R(acts),
+                                                                   dav, FAKE, FAKE, FAKE, ws, 1 << 40, None)
+    assert call(_desc(dqk=64, dv=128)) == _lib.HSTU_ERR_UNSUPPORTED
+    assert call(_desc(), dav=None) == _lib.HSTU_ERR_INVALID_ARG
+    assert call(_desc(), acts=_lib.HstuActivations(FAKE, FAKE, None, FAKE, FAKE, FAKE)) == _lib.HSTU_ERR_INVALID_ARG
+    assert call(_desc(), ws=None) == _lib.HSTU_ERR_WORKSPACE
+    assert lib.hstu_attn_bwd_workspace_size(R(_desc()), 1000, 4) >= lib.hstu_attn_workspace_size(R(_desc()), 1000, 4)

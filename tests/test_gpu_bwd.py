@@ -120,3 +120,76 @@ def test_bwd_deterministic_bitwise():
     b, _ = _gpu_bwd(w, dy)
     for k in a:
         np.testing.assert_array_equal(a[k], b[k], err_msg=k)
+
+
+def test_bwd_ranking_full_size():
+    """The ranking workload (bf16, B=16, history U[512, 2048] + 512 candidates,
+    d=512, 8 x 64/64) at full size: dx rows of the shortest sequence depend on
+    that sequence alone, so they are compared with the oracle run on it; the
+    parameter gradients of the same sequence run alone on the GPU (the kernels
+    at the full-size shape, one sequence) against the oracle's."""
+    w = synth.make_workload("ranking_cand", n_layers=1)
+    s = int(np.argmin(w.lengths()))
+    rng = np.random.default_rng(11)
+    dy = rng.normal(0, 1, (w.T, w.dims.d_model))
+    got, dy_used = _gpu_bwd(w, dy)
+    sub = w.sub_batch([s])
+    rows = np.arange(w.offsets[s], w.offsets[s + 1])
+    ref = G.layer_grads(sub.x, sub.offsets, sub.timestamps, sub.num_candidates, sub.layers[0], w.dims,
+                        dy_used[rows])
+    say(f"backward, ranking_cand full batch (T={w.T}); oracle on sequence {s} ({len(rows)} rows)")
+    e = err_bf16(got["x"][rows], ref["x"])
+    say(f"  dx (full batch, sequence {s}): err {e:.3e} (tol 5e-02)")
+    assert e <= 5e-2
+    got1, _ = _gpu_bwd(sub, dy_used[rows])
+    for k, rk in NAMES.items():
+        tol = 1e-1 if k in ("pos", "time") else 5e-2
+        e = err_bf16(got1[k], ref[rk])
+        say(f"  d{k} (sequence {s} alone): err {e:.3e} (tol {tol:.0e})")
+        assert e <= tol, k
+
+
+@pytest.mark.parametrize("case", ["edge_fp32", "edge_bf16_64", "zipf_bf16", "sl_128_bf16"])
+def test_attention_stage_backward(case):
+    """hstu_attn_bwd fed the GPU's own q, k, v and a bf16 dL/dAV, against the
+    float64 autograd of the attention alone fed the same values: the stage's
+    own arithmetic, element-relative (max |g - ref| / max(|ref|, rms(ref))).
+    fp32: 1e-3.  bf16: 5e-2 — the kernels round the pointwise weights (for dV)
+    and dS (for dQ, dK) to bf16 as MFMA operands, like the forward's weights;
+    rounding only the weights to bf16 inside the float64 oracle already moves
+    dV by 3.4e-2 on the bf16 edge case (a single-token sequence's key carries
+    a weight of order 1 while most gradients are small), and the forward's
+    attention tap has the same 4e-2-class bound."""
+    if case == "edge_fp32":
+        w = edge_workload("fp32", seed=3)
+    elif case == "edge_bf16_64":
+        w = synth.make_workload("small_fp32", seed=3, lengths=[0, 1, 127, 123, 0, 0, 130, 0, 1],
+                                candidates=[0, 1, 0, 5, 129, 0, 70, 64, 2], dims=BF16_64, random_ln=True)
+    elif case == "zipf_bf16":
+        w = synth.make_workload("zipf_bf16", batch=6)
+    else:
+        w = synth.make_workload("sl_train", batch=2, lengths=[700, 300], dims=synth.WORKLOADS["sl_train"].dims)
+    dev = layer.to_device(w)
+    desc = _lib.make_desc(w.dims)
+    prm = dev["layers"][0]
+    acts = _lib.proj_fwd(desc, dev["x"], prm)
+    H, dqk, dv = w.dims.num_heads, w.dims.dqk, w.dims.dv
+    g = torch.Generator(device="cuda").manual_seed(9)
+    dav = torch.randn(w.T, H * dv, generator=g, device="cuda").to(dev["x"].dtype)
+    dqkv, dpos, dtime = _lib.attn_bwd(desc, dev["offsets"], dev["timestamps"], dev["num_candidates"], prm, acts, dav)
+    torch.cuda.synchronize()
+    f = lambda t: t.float().cpu().numpy().astype(np.float64)
+    q, k, v = (f(acts[n]).transpose(1, 0, 2) for n in ("q", "k", "v"))
+    ref = G.attention_grads(q, k, v, f(dav), w.offsets, w.timestamps, w.num_candidates, w.layers[0], w.dims)
+    K2 = H * dv
+    D = f(dqkv)
+    got = {"v": D[:, K2:2 * K2].reshape(w.T, H, dv), "q": D[:, 2 * K2:2 * K2 + H * dqk].reshape(w.T, H, dqk),
+           "k": D[:, 2 * K2 + H * dqk:].reshape(w.T, H, dqk), "pos_table": f(dpos), "time_table": f(dtime)}
+    fp32 = w.dims.dtype == "fp32"
+    say(f"attention backward stage, {case}: T={w.T}")
+    for n in got:
+        e = err_fp32(got[n], ref[n])
+        tol = 1e-3 if fp32 else 5e-2
+        say(f"  d{n}: err {e:.3e} (tol {tol:.0e})")
+        assert e <= tol, n
+    assert np.all(D[:, :K2] == 0)   # the u block is not written

@@ -77,3 +77,34 @@ def test_unused_table_entries_get_zero_gradient():
     assert np.count_nonzero(g["pos_table"][:, np.arange(dims.pos_buckets) != R]) == 0
     assert np.count_nonzero(g["time_table"][:, 1:]) == 0
     assert np.count_nonzero(g["pos_table"][:, R]) == dims.num_heads
+
+
+def test_attention_stage_gradients_match_the_layer_chain():
+    # the attention stage's gradients are the layer's, seen through dL/dAV:
+    # pin by finite differences of sum(AV * dav) on a tiny case
+    w, prm, dims = _case(7, [6, 4], [2, 1])
+    rng = np.random.default_rng(7)
+    _, v, q, k = O.project(w.x, prm, dims)
+    dav = rng.normal(0, 1, (w.T, dims.num_heads * dims.dv))
+    g = G.attention_grads(q, k, v, dav, w.offsets, w.timestamps, w.num_candidates, prm, dims)
+
+    def loss(qq, kk, vv, pp):
+        av = O.attention(qq, kk, vv, w.offsets, w.timestamps, w.num_candidates, pp, dims)
+        return float(np.sum(av * dav))
+
+    eps = 1e-6
+    for name, base in (("q", q), ("k", k), ("v", v), ("pos_table", prm["pos_table"]),
+                       ("time_table", prm["time_table"])):
+        for fi in rng.choice(base.size, size=min(5, base.size), replace=False):
+            idx = np.unravel_index(fi, base.shape)
+            hi, lo = base.copy(), base.copy()
+            hi[idx] += eps
+            lo[idx] -= eps
+            args = {"q": q, "k": k, "v": v, "pp": prm}
+            if name in ("pos_table", "time_table"):
+                fd = (loss(q, k, v, {**prm, name: hi}) - loss(q, k, v, {**prm, name: lo})) / (2 * eps)
+            else:
+                a_hi, a_lo = dict(args), dict(args)
+                a_hi[name], a_lo[name] = hi, lo
+                fd = (loss(a_hi["q"], a_hi["k"], a_hi["v"], prm) - loss(a_lo["q"], a_lo["k"], a_lo["v"], prm)) / (2 * eps)
+            assert abs(g[name][idx] - fd) <= 1e-6 * max(1.0, abs(fd)), (name, idx)
