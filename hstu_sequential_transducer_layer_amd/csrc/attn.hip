@@ -342,6 +342,29 @@ __device__ __forceinline__ int classify_block(int j0, int64_t tmin, int64_t tmax
   const bool narrow = q.narrow && !__builtin_sub_overflow(tmin, sq.t0, &dmin) &&
                       !__builtin_sub_overflow(tmax, sq.t0, &dmax) && dmin > -kNear && dmin < kNear &&
                       dmax > -kNear && dmax < kNear;
+  const int jq = j0 + 4 * (int)((threadIdx.x >> 5) & 1);
+  if (full && pos_far && narrow) {
+    // The usual far block (wave-uniform test): modes 0 and 1 from 32-bit
+    // differences only (|t - t0| < 2^29 for every time involved, so the
+    // differences below are exact and span_ok holds); the same values as the
+    // general path below, which takes every other case.
+    const int32_t lo = q.rq - (int32_t)dmax, hi = q.rq - (int32_t)dmin;
+    if (__all((hi < (1 << 24) && lo > -(1 << 24)) || !q.qvalid)) {
+      const int bt_lo = time_bucket_small(lo, sq.NB, sq.sbits);
+      const int bt_hi = time_bucket_small(hi, sq.NB, sq.sbits);
+      if (__all(bt_hi == bt_lo || !q.qvalid)) {
+        x.c_lo = sq.time_s[bt_lo] + sq.cpos_far;
+        return 0;
+      }
+      if (__all(bt_hi <= bt_lo + 1 || !q.qvalid)) {
+        x.c_lo = sq.time_s[bt_lo] + sq.cpos_far;
+        x.c_hi = sq.time_s[bt_hi] + sq.cpos_far;
+        x.thr = hi - bucket_floor_small(max(bt_hi, 1), sq.sbits);
+        x.rel_s = rb + (jq - j0);
+        return 1;
+      }
+    }
+  }
   bool novf, span_ok;
   int64_t lo, hi;
   if (narrow) {  // |t - t0| < 2^29 for every time involved: 32-bit differences are exact
@@ -371,7 +394,6 @@ __device__ __forceinline__ int classify_block(int j0, int64_t tmin, int64_t tmax
   const bool fast = full && pos_far && __all(one || two || !q.qvalid);
   const float c_lo = sq.time_s[bt_lo] + sq.cpos_far;
   const bool hist_only = j0 + kAttnBN <= sq.nh;
-  const int jq = j0 + 4 * (int)((threadIdx.x >> 5) & 1);
   const int mode = __builtin_amdgcn_readfirstlane(!fast ? (all_small && hist_only ? 2 : 3)
                                                          : (__all(one || !q.qvalid) ? 0 : 1));
   float c_hi = c_lo;
