@@ -100,39 +100,45 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 // Asynchronous copy of one key block of a [rows, D] head-major tensor into a
-// swizzled LDS tile: every wave issues PER 16-byte-per-lane direct loads.  The
-// per-lane element offsets (relative to the block's first row) are fixed and
-// computed once.  In a block that runs past the sequence's end, rows past it
-// read the sequence's last row instead (finite values that the mask turns into
-// zero weight), so no other sequence's data is read.
+// swizzled LDS tile: every wave issues PER 16-byte-per-lane direct loads.
+// Load i of wave w fills the 64 / CPR rows starting at (i * NW + w) * 64 / CPR,
+// so a lane's rows in successive loads lie STRIDE rows apart, a multiple of
+// the swizzle period (16 rows): its source offset is one fixed value plus
+// i * STRIDE rows.  Each load is then a wave-uniform base (scalar registers)
+// plus that fixed per-lane offset.  In a block that runs past the sequence's
+// end, rows past it read the sequence's last row instead (finite values that
+// the mask turns into zero weight), so no other sequence's data is read.
 template <typename T, int D, int NW, int CPR, bool IS_K>
 struct TileCopy {
   static constexpr int V = Elem<T>::kVec;
   static constexpr int PER = 64 * CPR / (NW * 64);  // BN = 64 rows
+  static constexpr int STRIDE = NW * 64 / CPR;      // rows between a lane's loads
   static constexpr int LOG_D = D == 32 ? 5 : D == 64 ? 6 : 7;
   static_assert(D == 32 || D == 64 || D == 128, "head width");
-  int off[PER];
+  static_assert(PER == 1 || STRIDE % 16 == 0, "loads must share the swizzle");
+  int r0;    // this lane's row in load 0
+  int off0;  // its source offset (elements) in load 0
   __device__ __forceinline__ void init(int w, int lane) {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int slot = (w * PER + i) * 64 + lane;
-      const int r = slot / CPR, pc = slot % CPR;
-      off[i] = r * D + (pc ^ (IS_K ? k_swz<CPR>(r) : v_swz<CPR>(r))) * V;
-    }
+    const int slot = w * 64 + lane;
+    const int pc = slot % CPR;
+    r0 = slot / CPR;
+    off0 = r0 * D + (pc ^ (IS_K ? k_swz<CPR>(r0) : v_swz<CPR>(r0))) * V;
   }
   // g: the block's first row; rows: rows of the sequence from there (>= 1).
   __device__ __forceinline__ void issue(const T* __restrict__ g, int rows, T* lds, int w) const {
+    const uint32_t lane_bytes = (uint32_t)off0 * (uint32_t)sizeof(T);
     if (rows >= 64) {
 #pragma unroll
       for (int i = 0; i < PER; ++i)
-        __builtin_amdgcn_global_load_lds((glb_void*)(g + off[i]), (lds_void*)(lds + (w * PER + i) * 64 * V), 16,
-                                         0, 0);
+        __builtin_amdgcn_global_load_lds(
+            (glb_void*)(reinterpret_cast<const char*>(g + i * STRIDE * D) + lane_bytes),
+            (lds_void*)(lds + (i * NW + w) * 64 * V), 16, 0, 0);
     } else {
 #pragma unroll
       for (int i = 0; i < PER; ++i) {
-        const int r = off[i] >> LOG_D, rr = min(r, rows - 1);
-        __builtin_amdgcn_global_load_lds((glb_void*)(g + off[i] + (rr - r) * D),
-                                         (lds_void*)(lds + (w * PER + i) * 64 * V), 16, 0, 0);
+        const int r = r0 + i * STRIDE, rr = min(r, rows - 1);
+        __builtin_amdgcn_global_load_lds((glb_void*)(g + off0 + i * STRIDE * D + (rr - r) * D),
+                                         (lds_void*)(lds + (i * NW + w) * 64 * V), 16, 0, 0);
       }
     }
   }
@@ -543,7 +549,12 @@ __global__ __launch_bounds__(256, attn_min_blocks((DQK + DV) * (int)sizeof(T) + 
   // copies, so the wait that covers them covers it too).
   auto issue = [&](int blk, T* Kb, T* Vb, int32_t* rb, int32_t* yb, longlong2& tb) __attribute__((always_inline)) {
     const int j0 = block_start(blk);
-    tb = *reinterpret_cast<const longlong2*>(a.tstat + 2 * (k0 + j0));
+    // a wave-uniform address, read-only in this kernel: scalar loads
+    const __attribute__((address_space(4))) int64_t* t4 =
+        reinterpret_cast<const __attribute__((address_space(4))) int64_t*>(
+            reinterpret_cast<uintptr_t>(a.tstat + 2 * (k0 + j0)));
+    tb.x = t4[0];
+    tb.y = t4[1];
     kcopy.issue(kg + (int64_t)j0 * DQK, L - j0, Kb, w);
     vcopy.issue(vg + (int64_t)j0 * DV, L - j0, Vb, w);
     // the offsets and types arrays have kAttnBN rows of padding past the key
