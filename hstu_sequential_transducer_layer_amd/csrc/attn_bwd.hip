@@ -21,7 +21,8 @@
 //   query block that can see those keys.  S = Q K^T (Q rows from LDS, K in
 //   registers); DK = false: dV^T += dO^T a; DK = true: dA = dO V^T and
 //   dK^T += Q^T dS.  Two passes keep each pass's accumulators in registers.
-// Tiles in LDS are plain row-major rows padded by 16 bytes.
+// K/V (Q/dO) blocks are staged in LDS by direct global->LDS loads, double
+// buffered: block b + 1 is copied while block b is consumed.
 #include "common.h"
 #include "kernels.h"
 
@@ -41,37 +42,111 @@ struct BwdArgs {
   float* tab_part;    // [gridDim.x][P + NB]: per-workgroup bias-table gradients (dq kernel)
   const int2* tiles;
   const int32_t* counts;
+  const int64_t* tstat;  // per 64-row block's first row: its earliest, latest timestamp
   int64_t T;
   int H, P, NB, sbits, pos_stride, time_stride, norm_len, shared_pos, N1;
 };
 
-// Rows of 64 x D in LDS, row stride D + 16 bytes.
-template <typename T, int D>
-struct BTile {
-  static constexpr int V = Elem<T>::kVec, CPR = D / V, LD = D + V;
-};
+typedef __attribute__((address_space(3))) void bwd_lds_void;
+typedef __attribute__((address_space(1))) void bwd_glb_void;
 
-// 64 rows of D elements from src (row r at src + r * stride) into a padded
-// tile; rows at or past `avail` (>= 1) repeat row avail - 1.
-template <typename T, int D>
-__device__ __forceinline__ void bwd_copy(const T* __restrict__ src, int64_t stride, int avail, T* lds) {
-  typedef BTile<T, D> Bt;
-  for (int ch = threadIdx.x; ch < 64 * Bt::CPR; ch += 256) {
-    const int r = ch / Bt::CPR, c = ch - r * Bt::CPR;
-    const int rr = min(r, avail - 1);
-    st16(lds + r * Bt::LD + c * Bt::V, ld16(src + rr * stride + c * Bt::V));
+// Tiles in LDS: 64 rows of D elements, row-major without padding; chunk c
+// (one 16-byte vector of kVec elements) of row r is stored at chunk
+// c ^ bwd_swz(r).  The swizzle is chosen so that both access patterns are
+// free of bank conflicts (checked exhaustively on the host): 16 consecutive
+// rows read 16 bytes each at one logical chunk (row fragments), and four
+// consecutive rows read as two adjacent chunks each (the transposing reads of
+// column fragments).  bwd_swz(0) = 0 and bwd_swz depends on r % 16 only.
+template <int CPR>
+__device__ __forceinline__ int bwd_swz(int r) {
+  if constexpr (CPR >= 16) {
+    return ((r & 3) << 1) | ((r >> 2) & 1) | (r & 8);
+  } else if constexpr (CPR == 8) {
+    const int x = r >> 1;
+    return ((x & 1) << 1) | ((x >> 1) & 1) | (x & 4);
+  } else {
+    return (r >> 2) & 3;
   }
 }
 
-// A operand from tile rows: row r, elements e0 .. e0 + 7.
 template <typename T, int D>
-__device__ __forceinline__ typename Elem<T>::Frag bwd_row_frag(const T* lds, int r, int e0) {
+struct BTile {
+  static constexpr int V = Elem<T>::kVec, CPR = D / V;
+  static_assert(CPR >= 4 && CPR <= 16, "tile width");
+  // element offset of element e of row r
+  static __device__ __forceinline__ int at(int r, int e) { return r * D + (((e / V) ^ bwd_swz<CPR>(r)) * V) + e % V; }
+};
+
+// Asynchronous copy of 64 rows (row stride S elements in global memory) into a
+// swizzled tile by direct global->LDS loads: each of the four waves issues PER
+// 16-byte-per-lane loads; load i of wave w fills the 64 / CPR rows from
+// (4 i + w) * 64 / CPR, so a lane's rows lie STRIDE (a multiple of 16) rows
+// apart and share one swizzle.  Rows at or past `avail` (>= 1) repeat row
+// avail - 1.
+template <typename T, int D>
+struct BwdCopy {
+  static constexpr int V = Elem<T>::kVec, CPR = D / V, PER = CPR / 4, STRIDE = 256 / CPR;
+  static_assert(PER == 1 || STRIDE % 16 == 0, "a lane's loads must share the swizzle");
+  int r0;   // this lane's row in load 0
+  int col;  // element offset of the chunk it copies (source side)
+  __device__ __forceinline__ void init(int w, int lane) {
+    const int slot = w * 64 + lane;
+    r0 = slot / CPR;
+    col = ((slot % CPR) ^ bwd_swz<CPR>(r0)) * V;
+  }
+  __device__ __forceinline__ void issue(const T* __restrict__ g, int64_t S, int avail, T* lds, int w) const {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int rr = min(r0 + i * STRIDE, avail - 1);
+      __builtin_amdgcn_global_load_lds((bwd_glb_void*)(g + rr * S + col), (bwd_lds_void*)(lds + (4 * i + w) * 64 * V),
+                                       16, 0, 0);
+    }
+  }
+};
+
+// 64 int64 timestamps ts[min(j, avail - 1)], j = 0..63, into LDS by one wave
+// (two 4-byte-per-lane direct loads).
+__device__ __forceinline__ void bwd_copy_ts(const int64_t* __restrict__ ts, int avail, int64_t* lds, int lane) {
+#pragma unroll
+  for (int d = 0; d < 2; ++d) {
+    const int e = min(32 * d + (lane >> 1), avail - 1);
+    __builtin_amdgcn_global_load_lds((bwd_glb_void*)(reinterpret_cast<const int32_t*>(ts + e) + (lane & 1)),
+                                     (bwd_lds_void*)(lds + 32 * d), 4, 0, 0);
+  }
+}
+
+// The earliest and latest timestamp of the 64-row block whose first row is
+// `row` (the work list's per-block summary; a wave-uniform address, read-only
+// here: scalar loads).
+__device__ __forceinline__ void bwd_block_minmax(const int64_t* tstat, int64_t row, int64_t& mn, int64_t& mx) {
+  const __attribute__((address_space(4))) int64_t* t4 =
+      reinterpret_cast<const __attribute__((address_space(4))) int64_t*>(reinterpret_cast<uintptr_t>(tstat + 2 * row));
+  mn = t4[0];
+  mx = t4[1];
+}
+
+// Eight elements of one row in global memory, e0 .. e0 + 7.
+template <typename T>
+__device__ __forceinline__ typename Elem<T>::Frag bwd_global_frag(const T* p) {
   typedef typename Elem<T>::Frag Frag;
-  const T* p = lds + r * BTile<T, D>::LD + e0;
   if constexpr (Elem<T>::kVec == 8) {
     return *reinterpret_cast<const Frag*>(p);
   } else {
     const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
+    return Frag{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  }
+}
+
+// A operand from tile rows: row r, elements e0 .. e0 + 7 (e0 a multiple of 8).
+template <typename T, int D>
+__device__ __forceinline__ typename Elem<T>::Frag bwd_row_frag(const T* lds, int r, int e0) {
+  typedef typename Elem<T>::Frag Frag;
+  typedef BTile<T, D> Bt;
+  if constexpr (Elem<T>::kVec == 8) {
+    return *reinterpret_cast<const Frag*>(lds + Bt::at(r, e0));
+  } else {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(lds + Bt::at(r, e0));
+    const f32x4 b = *reinterpret_cast<const f32x4*>(lds + Bt::at(r, e0 + 4));
     return Frag{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
   }
 }
@@ -89,15 +164,15 @@ typedef __attribute__((address_space(3))) bwd_v4i16 bwd_lds_v4i16;
 // by element.
 template <typename T, int D>
 __device__ __forceinline__ typename Elem<T>::Frag bwd_col_frag(const T* lds, int kb, int nt, int lane) {
+  typedef BTile<T, D> Bt;
   typename Elem<T>::Frag x;
   const int half = lane >> 5;
   if constexpr (Elem<T>::kVec == 8) {
     const int a = lane & 15;
     const int row = kb + 4 * half + (a >> 2);
     const int col = 32 * nt + 16 * ((lane >> 4) & 1) + 4 * (a & 3);
-    const bwd_v4i16 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((bwd_lds_v4i16*)(lds + row * BTile<T, D>::LD + col));
-    const bwd_v4i16 x1 =
-        __builtin_amdgcn_ds_read_tr16_b64_v4i16((bwd_lds_v4i16*)(lds + (row + 8) * BTile<T, D>::LD + col));
+    const bwd_v4i16 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((bwd_lds_v4i16*)(lds + Bt::at(row, col)));
+    const bwd_v4i16 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((bwd_lds_v4i16*)(lds + Bt::at(row + 8, col)));
     const bf16* p0 = reinterpret_cast<const bf16*>(&x0);
     const bf16* p1 = reinterpret_cast<const bf16*>(&x1);
 #pragma unroll
@@ -108,21 +183,9 @@ __device__ __forceinline__ typename Elem<T>::Frag bwd_col_frag(const T* lds, int
   } else {
     const int f = 32 * nt + (lane & 31);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = lds[(kb + 8 * (e >> 2) + 4 * half + (e & 3)) * BTile<T, D>::LD + f];
+    for (int e = 0; e < 8; ++e) x[e] = lds[Bt::at(kb + 8 * (e >> 2) + 4 * half + (e & 3), f)];
   }
   return x;
-}
-
-// Min and max of 64 int64 values held one per lane (wave 0 of a block copy).
-__device__ __forceinline__ void bwd_minmax64(int64_t v, int64_t& mn, int64_t& mx) {
-  mn = v;
-  mx = v;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const int64_t a = __shfl_xor(mn, o, kWave), b = __shfl_xor(mx, o, kWave);
-    mn = a < mn ? a : mn;
-    mx = b > mx ? b : mx;
-  }
 }
 
 template <typename T>
@@ -140,10 +203,13 @@ __device__ __forceinline__ float bwd_sigmoid(float s) {
 template <typename T, int DQK, int DV>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
   typedef typename Elem<T>::Frag Frag;
-  __shared__ __attribute__((aligned(16))) T Ks[64 * BTile<T, DQK>::LD];
-  __shared__ __attribute__((aligned(16))) T Vs[64 * BTile<T, DV>::LD];
-  __shared__ int64_t tsk[64];
-  __shared__ int64_t kmm[2];  // the block's earliest and latest key timestamp
+  // two buffer sets (even / odd key blocks), each its own LDS objects
+  __shared__ __attribute__((aligned(16))) T Ks0[64 * DQK];
+  __shared__ __attribute__((aligned(16))) T Ks1[64 * DQK];
+  __shared__ __attribute__((aligned(16))) T Vs0[64 * DV];
+  __shared__ __attribute__((aligned(16))) T Vs1[64 * DV];
+  __shared__ __attribute__((aligned(16))) int64_t tsk0[64];
+  __shared__ __attribute__((aligned(16))) int64_t tsk1[64];
   // pos[P], time[NB], then one gradient histogram [P + NB] per wave (a
   // wave's updates land in program and lane order, so the sums are
   // reproducible; the four are added in wave order at the end)
@@ -184,12 +250,12 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
   for (int c = 0; c < DQK / 16; ++c) {
     qf[c] = Frag{};
-    if (qvalid) qf[c] = bwd_row_frag<T, DQK>(qrow - 0, 0, 16 * c + 8 * half);
+    if (qvalid) qf[c] = bwd_global_frag<T>(qrow + 16 * c + 8 * half);
   }
 #pragma unroll
   for (int c = 0; c < DV / 16; ++c) {
     df[c] = Frag{};
-    if (qvalid) df[c] = bwd_row_frag<T, DV>(drow, 0, 16 * c + 8 * half);
+    if (qvalid) df[c] = bwd_global_frag<T>(drow + 16 * c + 8 * half);
   }
   const int p_q = position(iq, nh, shared);
   const int64_t ts_q = qvalid ? a.ts[s0 + iq] : 0;
@@ -212,23 +278,24 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
   const int nblk_b = (b_lo < iend && jb0 < iend) ? (iend - jb0 + 63) / 64 : 0;
   const T* kg = reinterpret_cast<const T*>(a.k) + ((int64_t)h * a.T + s0) * DQK;
   const T* vg = reinterpret_cast<const T*>(a.v) + ((int64_t)h * a.T + s0) * DV;
-  for (int blk = 0; blk < nblk_a + nblk_b; ++blk) {
-    const int j0 = blk < nblk_a ? blk * 64 : jb0 + (blk - nblk_a) * 64;
-    __syncthreads();  // the previous block's reads are done
-    bwd_copy<T, DQK>(kg + (int64_t)j0 * DQK, DQK, L - j0, Ks);
-    bwd_copy<T, DV>(vg + (int64_t)j0 * DV, DV, L - j0, Vs);
-    if (tid < 64) {
-      const int64_t t = a.ts[s0 + min(j0 + tid, L - 1)];
-      tsk[tid] = t;
-      int64_t mn, mx;
-      bwd_minmax64(t, mn, mx);
-      if (tid == 0) {
-        kmm[0] = mn;
-        kmm[1] = mx;
-      }
-    }
-    __syncthreads();
-    if (r0 >= iend) continue;
+  const int nblk = nblk_a + nblk_b;
+  auto block_start = [&](int blk) __attribute__((always_inline)) {
+    return blk < nblk_a ? blk * 64 : jb0 + (blk - nblk_a) * 64;
+  };
+  BwdCopy<T, DQK> kcopy;
+  BwdCopy<T, DV> vcopy;
+  kcopy.init(w, lane);
+  vcopy.init(w, lane);
+  // K, V rows and key timestamps of block blk into one buffer set
+  auto issue = [&](int blk, T* Ks, T* Vs, int64_t* tsk) __attribute__((always_inline)) {
+    const int j0 = block_start(blk);
+    kcopy.issue(kg + (int64_t)j0 * DQK, DQK, L - j0, Ks, w);
+    vcopy.issue(vg + (int64_t)j0 * DV, DV, L - j0, Vs, w);
+    if (w == 0) bwd_copy_ts(a.ts + s0 + j0, L - j0, tsk, lane);
+  };
+  auto consume = [&](int blk, const T* Ks, const T* Vs, const int64_t* tsk) __attribute__((always_inline)) {
+    const int j0 = block_start(blk);
+    if (r0 >= iend) return;
     // A far block: every key a history key strictly before the wave's first
     // row and at least R positions from it (position bucket 2R, no mask);
     // with one time bucket per row over the block's time span, the bias is
@@ -237,8 +304,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
     int bt_row = 0;
     float b_row = 0.f;
     if (fast) {
-      const int lo = time_bucket(wrap_sub(ts_q, kmm[1]), NB, a.sbits);
-      const int hi = time_bucket(wrap_sub(ts_q, kmm[0]), NB, a.sbits);
+      int64_t kmin, kmax;
+      bwd_block_minmax(a.tstat, s0 + j0, kmin, kmax);
+      const int lo = time_bucket(wrap_sub(ts_q, kmax), NB, a.sbits);
+      const int hi = time_bucket(wrap_sub(ts_q, kmin), NB, a.sbits);
       fast = __all(lo == hi || !qvalid);
       bt_row = lo;
       b_row = pos_s[2 * R] + time_s[lo];
@@ -301,6 +370,23 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
           dq[n] = mma_k16(bwd_col_frag<T, DQK>(Ks, kh * 32 + 16 * c2, n, lane), pf, dq[n]);
       }
     }
+  };
+  if (nblk > 0) issue(0, Ks0, Vs0, tsk0);
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of block 0 have landed
+  __syncthreads();                // ... and every wave's, plus the tables and histograms
+  // Two blocks per trip so that each buffer set is named by a constant: the
+  // copies of block b + 1 run while block b is consumed; one barrier per block.
+  for (int blk = 0; blk < nblk; blk += 2) {
+    if (blk + 1 < nblk) issue(blk + 1, Ks1, Vs1, tsk1);
+    consume(blk, Ks0, Vs0, tsk0);
+    if (blk + 1 >= nblk) break;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (blk + 2 < nblk) issue(blk + 2, Ks0, Vs0, tsk0);
+    consume(blk + 1, Ks1, Vs1, tsk1);
+    if (blk + 2 >= nblk) break;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
   }
   if (qvalid) {
     float* dst = a.dact + (s0 + iq) * (int64_t)a.N1 + 2 * K2 + h * DQK;
@@ -325,10 +411,13 @@ template <typename T, int DQK, int DV, bool DK>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(BwdArgs a) {
   typedef typename Elem<T>::Frag Frag;
   constexpr int DACC = DK ? DQK : DV;  // width of this pass's gradient
-  __shared__ __attribute__((aligned(16))) T Qs[64 * BTile<T, DQK>::LD];
-  __shared__ __attribute__((aligned(16))) T Os[64 * BTile<T, DV>::LD];
-  __shared__ int64_t tsq[64];
-  __shared__ int64_t qmm[2];  // the block's earliest and latest query timestamp
+  // two buffer sets (even / odd query blocks), each its own LDS objects
+  __shared__ __attribute__((aligned(16))) T Qs0[64 * DQK];
+  __shared__ __attribute__((aligned(16))) T Qs1[64 * DQK];
+  __shared__ __attribute__((aligned(16))) T Os0[64 * DV];
+  __shared__ __attribute__((aligned(16))) T Os1[64 * DV];
+  __shared__ __attribute__((aligned(16))) int64_t tsq0[64];
+  __shared__ __attribute__((aligned(16))) int64_t tsq1[64];
   extern __shared__ float tabs[];  // pos[P], time[NB]
   const int H = a.H, h = blockIdx.x % H, item = blockIdx.x / H;
   if (item >= a.counts[0]) return;
@@ -359,13 +448,13 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(BwdArgs a) {
 #pragma unroll
   for (int c = 0; c < DQK / 16; ++c) {
     kf[c] = Frag{};
-    if (kvalid) kf[c] = bwd_row_frag<T, DQK>(krow, 0, 16 * c + 8 * half);
+    if (kvalid) kf[c] = bwd_global_frag<T>(krow + 16 * c + 8 * half);
   }
   if (DK) {
 #pragma unroll
     for (int c = 0; c < DV / 16; ++c) {
       vf[c] = Frag{};
-      if (kvalid) vf[c] = bwd_row_frag<T, DV>(vrow, 0, 16 * c + 8 * half);
+      if (kvalid) vf[c] = bwd_global_frag<T>(vrow + 16 * c + 8 * half);
     }
   }
   const int p_k = position(jk, nh, shared);
@@ -380,22 +469,21 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(BwdArgs a) {
   const int qend = j0t < nh ? L : jend;
   const T* qg = reinterpret_cast<const T*>(a.q) + ((int64_t)h * a.T + s0) * DQK;
   const T* og = reinterpret_cast<const T*>(a.dout) + s0 * (int64_t)K2 + h * DV;
-  for (int i0 = qb0; i0 < qend; i0 += 64) {
-    __syncthreads();
-    bwd_copy<T, DQK>(qg + (int64_t)i0 * DQK, DQK, L - i0, Qs);
-    bwd_copy<T, DV>(og + (int64_t)i0 * K2, K2, L - i0, Os);
-    if (tid < 64) {
-      const int64_t t = a.ts[s0 + min(i0 + tid, L - 1)];
-      tsq[tid] = t;
-      int64_t mn, mx;
-      bwd_minmax64(t, mn, mx);
-      if (tid == 0) {
-        qmm[0] = mn;
-        qmm[1] = mx;
-      }
-    }
-    __syncthreads();
-    if (kr0 >= jend) continue;
+  const int nblk = qend > qb0 ? (qend - qb0 + 63) / 64 : 0;
+  BwdCopy<T, DQK> qcopy;
+  BwdCopy<T, DV> ocopy;
+  qcopy.init(w, lane);
+  ocopy.init(w, lane);
+  // Q, dO rows and query timestamps of query block blk into one buffer set
+  auto issue = [&](int blk, T* Qs, T* Os, int64_t* tsq) __attribute__((always_inline)) {
+    const int i0 = qb0 + 64 * blk;
+    qcopy.issue(qg + (int64_t)i0 * DQK, DQK, L - i0, Qs, w);
+    ocopy.issue(og + (int64_t)i0 * K2, K2, L - i0, Os, w);
+    if (w == 0) bwd_copy_ts(a.ts + s0 + i0, L - i0, tsq, lane);
+  };
+  auto consume = [&](int blk, const T* Qs, const T* Os, const int64_t* tsq) __attribute__((always_inline)) {
+    const int i0 = qb0 + 64 * blk;
+    if (kr0 >= jend) return;
     // A far block (the dq kernel's test with queries and keys swapped): all
     // the wave's keys history keys strictly before the block's first query
     // and at least R positions from it; one time bucket per key.
@@ -403,8 +491,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(BwdArgs a) {
     bool fast = i0 + 63 < L && k_last < nh && i0 > k_last && position(i0, nh, shared) - k_last >= R;
     float b_key = 0.f;
     if (fast) {
-      const int lo = time_bucket(wrap_sub(qmm[0], ts_k), NB, a.sbits);
-      const int hi = time_bucket(wrap_sub(qmm[1], ts_k), NB, a.sbits);
+      int64_t qmin, qmax;
+      bwd_block_minmax(a.tstat, s0 + i0, qmin, qmax);
+      const int lo = time_bucket(wrap_sub(qmin, ts_k), NB, a.sbits);
+      const int hi = time_bucket(wrap_sub(qmax, ts_k), NB, a.sbits);
       fast = __all(lo == hi || !kvalid);
       b_key = pos_s[2 * R] + time_s[lo];
     }
@@ -449,6 +539,23 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(BwdArgs a) {
         }
       }
     }
+  };
+  if (nblk > 0) issue(0, Qs0, Os0, tsq0);
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of block 0 have landed
+  __syncthreads();                // ... and every wave's, plus the tables
+  // Two blocks per trip so that each buffer set is named by a constant: the
+  // copies of block b + 1 run while block b is consumed; one barrier per block.
+  for (int blk = 0; blk < nblk; blk += 2) {
+    if (blk + 1 < nblk) issue(blk + 1, Qs1, Os1, tsq1);
+    consume(blk, Qs0, Os0, tsq0);
+    if (blk + 1 >= nblk) break;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (blk + 2 < nblk) issue(blk + 2, Qs0, Os0, tsq0);
+    consume(blk + 1, Qs1, Os1, tsq1);
+    if (blk + 2 >= nblk) break;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
   }
   if (kvalid) {
     float* dst = a.dact + (s0 + jk) * (int64_t)a.N1 + (DK ? 2 * K2 + H * DQK + h * DQK : K2 + h * DV);
@@ -462,24 +569,50 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(BwdArgs a) {
 }
 
 // Bias-table gradients: column sums of the dq kernel's partial rows, per
-// head (rows item * H + h); a table with head stride 0 sums every head.
-__global__ __launch_bounds__(256) void table_grad_kernel(const float* __restrict__ part, int64_t items, int H, int P,
-                                                         int NB, int pos_shared, int time_shared,
-                                                         float* __restrict__ gpos, float* __restrict__ gtime) {
+// head (rows item * H + h); a table with head stride 0 sums every head (into
+// head 0's row).  One workgroup per 64 result columns; its 16 waves take
+// every 16th row each (four running sums apiece, so four loads are in
+// flight), then the 16 partial sums are added in wave order: a fixed order,
+// so the result is reproducible.
+constexpr int kTabGroups = 16;
+__global__ __launch_bounds__(64 * kTabGroups) void table_grad_kernel(const float* __restrict__ part, int64_t items,
+                                                                     int H, int P, int NB, int pos_shared,
+                                                                     int time_shared, float* __restrict__ gpos,
+                                                                     float* __restrict__ gtime) {
+  __shared__ float red[kTabGroups][64];
   const int W = P + NB;
-  const int c = blockIdx.x * 256 + threadIdx.x;  // column of the [H][P + NB] result
-  if (c >= H * W) return;
-  const int h = c / W, idx = c - h * W;
+  const int t = threadIdx.x, col = t & 63, g = t >> 6;
+  const int c = blockIdx.x * 64 + col;  // column of the [H][P + NB] result
+  const bool live = c < H * W;
+  const int h = live ? c / W : 0, idx = live ? c - h * W : 0;
   const bool is_pos = idx < P;
   const bool sh = is_pos ? pos_shared : time_shared;
-  if (sh && h > 0) return;  // head 0 sums all heads
-  float s = 0.f;
-  for (int hh = sh ? 0 : h; hh < (sh ? H : h + 1); ++hh)
-    for (int64_t it = 0; it < items; ++it) s += part[(it * H + hh) * W + idx];
+  // rows summed: every row (shared table, head 0) or rows it * H + h
+  const int64_t nrows = !live || (sh && h > 0) ? 0 : (sh ? items * H : items);
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  int64_t k = g;
+  for (; k + 3 * kTabGroups < nrows; k += 4 * kTabGroups) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t r = k + u * kTabGroups;
+      acc[u] += part[(sh ? r : r * H + h) * W + idx];
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < 3; ++u) {  // at most three rows left for this wave
+    const int64_t r = k + u * kTabGroups;
+    if (r < nrows) acc[u] += part[(sh ? r : r * H + h) * W + idx];
+  }
+  red[g][col] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  __syncthreads();
+  if (g != 0 || nrows == 0) return;
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < kTabGroups; ++i) sum += red[i][col];
   if (is_pos)
-    gpos[(sh ? 0 : h) * P + idx] = s;
+    gpos[(sh ? 0 : h) * P + idx] = sum;
   else
-    gtime[(sh ? 0 : h) * NB + idx - P] = s;
+    gtime[(sh ? 0 : h) * NB + idx - P] = sum;
 }
 
 template <typename T, int DQK, int DV>
@@ -510,6 +643,7 @@ hipError_t launch_attn_bwd(const hstu_desc& d, const int64_t* off, const int32_t
   a.tab_part = tab_part;
   a.tiles = sc.tiles;
   a.counts = sc.counts;
+  a.tstat = sc.tstat;
   a.T = T;
   a.H = d.num_heads;
   a.P = d.pos_buckets;
@@ -540,7 +674,7 @@ hipError_t launch_attn_bwd(const hstu_desc& d, const int64_t* off, const int32_t
 #undef HSTU_BWD_CASE
   if (e != hipSuccess) return e;
   const int W = d.pos_buckets + d.time_buckets;
-  hipLaunchKernelGGL(table_grad_kernel, dim3((unsigned)((d.num_heads * W + 255) / 256)), dim3(256), 0, s, tab_part,
+  hipLaunchKernelGGL(table_grad_kernel, dim3((unsigned)((d.num_heads * W + 63) / 64)), dim3(64 * kTabGroups), 0, s, tab_part,
                      items, (int)d.num_heads, (int)d.pos_buckets, (int)d.time_buckets,
                      tab.pos_head_stride == 0 ? 1 : 0, tab.time_head_stride == 0 ? 1 : 0, gpos, gtime);
   return hipGetLastError();
