@@ -7,7 +7,8 @@
 // Kernels:
 //   transpose_kernel      [R, C] -> [C, Rp] in the layer dtype, columns past R zero
 //   gemm_nt_f32_kernel    C = A B^T with fp32 output (128 x 128 tiles, MFMA)
-//   colsum_kernel         column sums, in two deterministic stages
+//   colsum_rows_kernel, colsum_chunks_kernel: column sums, in two
+//                         deterministic stages
 //   gate_bwd_kernel       one wave per row: dU, dL/dAV, and the per-row terms
 //                         of the LayerNorm_av parameter gradients
 //   silu_bwd_kernel       dpre = d(u|v|q|k) * SiLU'(pre)
@@ -18,20 +19,36 @@
 
 namespace hstu {
 
+// dst[c][r] = src[r][c] (zero for r >= R) for r < Rp, c < C, through a 64 x 64
+// LDS tile; 16-byte loads along the source rows and 16-byte stores along the
+// destination rows.  C, Rp multiples of 16 / sizeof(T).
 template <typename T>
 __global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ src, int64_t R, int64_t C, int64_t Rp,
                                                         T* __restrict__ dst) {
-  __shared__ T tile[64][65];
+  constexpr int V = 16 / (int)sizeof(T), VPR = 64 / V, PAD = 4 / (int)sizeof(T);
+  __shared__ T tile[64][64 + PAD];
   const int64_t r0 = (int64_t)blockIdx.x * 64, c0 = (int64_t)blockIdx.y * 64;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int i = ty; i < 64; i += 4) {
-    const int64_t r = r0 + i, c = c0 + tx;
-    tile[i][tx] = (r < R && c < C) ? src[r * C + c] : from_f32<T>(0.f);
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int k = 0; k < 64 * VPR / 256; ++k) {
+    const int idx = t + 256 * k, i = idx / VPR, j = idx % VPR;
+    const int64_t r = r0 + i, c = c0 + (int64_t)j * V;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (r < R && c < C) v = *reinterpret_cast<const uint4*>(src + r * C + c);
+    const T* e = reinterpret_cast<const T*>(&v);
+#pragma unroll
+    for (int q = 0; q < V; ++q) tile[i][j * V + q] = e[q];
   }
   __syncthreads();
-  for (int i = ty; i < 64; i += 4) {
-    const int64_t c = c0 + i, r = r0 + tx;
-    if (c < C && r < Rp) dst[c * Rp + r] = tile[tx][i];
+#pragma unroll
+  for (int k = 0; k < 64 * VPR / 256; ++k) {
+    const int idx = t + 256 * k, cc = idx / VPR, m = idx % VPR;
+    const int64_t c = c0 + cc, r = r0 + (int64_t)m * V;
+    uint4 v;
+    T* e = reinterpret_cast<T*>(&v);
+#pragma unroll
+    for (int q = 0; q < V; ++q) e[q] = tile[m * V + q][cc];
+    if (c < C && r < Rp) *reinterpret_cast<uint4*>(dst + c * Rp + r) = v;
   }
 }
 
@@ -70,16 +87,82 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_f32_kernel(const T* __restrict
   }
 }
 
-// dst[chunk][c] = sum of src rows [chunk * rows_per, (chunk + 1) * rows_per), c < C.
+// Column sums in two deterministic stages.
+// Stage 1: dst[chunk][c] = sum of src rows [chunk * kColRows, ...) for column
+// c; each lane owns four adjacent columns (one vector load per row) and keeps
+// four rows' loads in flight.  C is a multiple of 4.
+constexpr int kColRows = 128;
 template <typename TIn>
-__global__ __launch_bounds__(256) void colsum_kernel(const TIn* __restrict__ src, int64_t R, int64_t C,
-                                                     int64_t rows_per, float* __restrict__ dst) {
-  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+__global__ __launch_bounds__(256) void colsum_rows_kernel(const TIn* __restrict__ src, int64_t R, int64_t C,
+                                                          float* __restrict__ dst) {
+  const int64_t c = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (c >= C) return;
-  const int64_t r0 = (int64_t)blockIdx.y * rows_per, r1 = min(r0 + rows_per, R);
-  float s = 0.f;
-  for (int64_t r = r0; r < r1; ++r) s += to_f32(src[r * C + c]);
-  dst[blockIdx.y * C + c] = s;
+  const int64_t r0 = (int64_t)blockIdx.y * kColRows, r1 = min(r0 + kColRows, R);
+  float4 acc[4] = {};
+  auto load4 = [&](int64_t r) __attribute__((always_inline)) {
+    const TIn* p = src + r * C + c;
+    if constexpr (sizeof(TIn) == 4) {
+      return *reinterpret_cast<const float4*>(p);
+    } else {
+      const uint2 raw = *reinterpret_cast<const uint2*>(p);
+      const TIn* e = reinterpret_cast<const TIn*>(&raw);
+      return make_float4(to_f32(e[0]), to_f32(e[1]), to_f32(e[2]), to_f32(e[3]));
+    }
+  };
+  int64_t r = r0;
+  for (; r + 4 <= r1; r += 4) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float4 v = load4(r + u);
+      acc[u].x += v.x;
+      acc[u].y += v.y;
+      acc[u].z += v.z;
+      acc[u].w += v.w;
+    }
+  }
+  for (; r < r1; ++r) {  // at most three rows left
+    const float4 v = load4(r);
+    acc[0].x += v.x;
+    acc[0].y += v.y;
+    acc[0].z += v.z;
+    acc[0].w += v.w;
+  }
+  float4 t;
+  t.x = (acc[0].x + acc[1].x) + (acc[2].x + acc[3].x);
+  t.y = (acc[0].y + acc[1].y) + (acc[2].y + acc[3].y);
+  t.z = (acc[0].z + acc[1].z) + (acc[2].z + acc[3].z);
+  t.w = (acc[0].w + acc[1].w) + (acc[2].w + acc[3].w);
+  *reinterpret_cast<float4*>(dst + blockIdx.y * C + c) = t;
+}
+
+// Stage 2: dst[c] = sum over chunk < nchunks of part[chunk][c].  One
+// workgroup per 64 columns; its 16 waves take every 16th chunk, then the 16
+// partial sums are added in wave order.
+constexpr int kColGroups = 16;
+__global__ __launch_bounds__(64 * kColGroups) void colsum_chunks_kernel(const float* __restrict__ part,
+                                                                        int64_t nchunks, int64_t C,
+                                                                        float* __restrict__ dst) {
+  __shared__ float red[kColGroups][64];
+  const int t = threadIdx.x, col = t & 63, g = t >> 6;
+  const int64_t c = (int64_t)blockIdx.x * 64 + col;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  if (c < C) {
+    int64_t k = g;
+    for (; k + 3 * kColGroups < nchunks; k += 4 * kColGroups) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc[u] += part[(k + u * kColGroups) * C + c];
+    }
+#pragma unroll
+    for (int u = 0; u < 3; ++u)
+      if (k + u * kColGroups < nchunks) acc[u] += part[(k + u * kColGroups) * C + c];
+  }
+  red[g][col] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  __syncthreads();
+  if (g != 0 || c >= C) return;
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < kColGroups; ++i) sum += red[i][col];
+  dst[c] = sum;
 }
 
 // One wave per row.  Recomputes the LayerNorm of AV from the attention's
@@ -187,20 +270,19 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(const T* __restrict__ x, co
 
 template <typename T>
 static hipError_t colsum_t(const T* src, int64_t R, int64_t C, float* tmp, float* dst, hipStream_t s) {
-  const int64_t rows_per = 256, chunks = (R + rows_per - 1) / rows_per;
-  if (R == 0) {  // zero sums: one chunk of no rows
-    hipLaunchKernelGGL(colsum_kernel<float>, dim3((unsigned)((C + 255) / 256), 1), dim3(256), 0, s,
-                       (const float*)tmp, (int64_t)0, C, (int64_t)1, dst);
-    return hipGetLastError();
-  }
-  hipLaunchKernelGGL(colsum_kernel<T>, dim3((unsigned)((C + 255) / 256), (unsigned)chunks), dim3(256), 0, s, src, R, C,
-                     rows_per, tmp);
-  hipLaunchKernelGGL(colsum_kernel<float>, dim3((unsigned)((C + 255) / 256), 1), dim3(256), 0, s, (const float*)tmp,
-                     chunks, C, chunks, dst);
+  if (C % 4 != 0) return hipErrorInvalidValue;
+  const int64_t chunks = (R + kColRows - 1) / kColRows;
+  if (chunks > 0)
+    hipLaunchKernelGGL(colsum_rows_kernel<T>, dim3((unsigned)((C / 4 + 255) / 256), (unsigned)chunks), dim3(256), 0, s,
+                       src, R, C, tmp);
+  hipLaunchKernelGGL(colsum_chunks_kernel, dim3((unsigned)((C + 63) / 64)), dim3(64 * kColGroups), 0, s,
+                     (const float*)tmp, chunks, C, dst);
   return hipGetLastError();
 }
 
-size_t colsum_tmp_bytes(int64_t R, int64_t C) { return (size_t)((R + 255) / 256 + 1) * (size_t)C * sizeof(float); }
+size_t colsum_tmp_bytes(int64_t R, int64_t C) {
+  return (size_t)((R + kColRows - 1) / kColRows + 1) * (size_t)C * sizeof(float);
+}
 
 hipError_t launch_colsum(hstu_dtype dt_in, bool in_f32, const void* src, int64_t R, int64_t C, float* tmp, float* dst,
                          hipStream_t s) {
@@ -212,6 +294,8 @@ hipError_t launch_colsum(hstu_dtype dt_in, bool in_f32, const void* src, int64_t
 hipError_t launch_transpose(hstu_dtype dt, const void* src, int64_t R, int64_t C, int64_t Rp, void* dst,
                             hipStream_t s) {
   if (R == 0 && Rp == 0) return hipSuccess;
+  const int64_t vec = dt == HSTU_BF16 ? 8 : 4;
+  if (C % vec != 0 || Rp % vec != 0) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((Rp + 63) / 64), (unsigned)((C + 63) / 64)), block(256);
   if (dt == HSTU_BF16)
     hipLaunchKernelGGL(transpose_kernel<bf16>, grid, block, 0, s, (const bf16*)src, R, C, Rp, (bf16*)dst);
