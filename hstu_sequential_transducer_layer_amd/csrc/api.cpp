@@ -597,10 +597,9 @@ hstu_status hstu_layer_bwd(const hstu_desc* desc, const void* x, const int64_t* 
     return st;
   // f1 and SiLU: dpre = d(u|v|q|k) * SiLU'(x~ W1^T + b1); db1, dW1 = dpre^T x~, dx~ = dpre W1
   if ((st = device(hstu::launch_gemm_nt_f32(dt, xn, w->w1, F(L.pre), T, (int)N1, dm, nullptr, s), "gemm")) != HSTU_OK) return st;
-  if ((st = device(hstu::launch_silu_bwd(dt, F(L.pre), w->b1, dact, T, (int)N1, dact, base + L.dpre_t, s),
+  if ((st = device(hstu::launch_silu_bwd(dt, F(L.pre), w->b1, dact, T, (int)N1, base + L.dpre_t, ctmp, g->b1, s),
                    "silu backward launch")) != HSTU_OK)
     return st;
-  if ((st = colsum(true, dact, T, N1, g->b1)) != HSTU_OK) return st;
   if ((st = device(hstu::launch_transpose(dt, w->w1, N1, dm, N1, base + L.w1t, s), "transpose")) != HSTU_OK) return st;
   if ((st = device(hstu::launch_gemm_nt_f32(dt, base + L.dpre_t, base + L.w1t, F(L.dxn), T, dm, (int)N1, nullptr, s), "gemm")) !=
       HSTU_OK)

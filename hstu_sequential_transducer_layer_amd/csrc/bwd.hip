@@ -11,7 +11,7 @@
 //                         deterministic stages
 //   gate_bwd_kernel       one wave per row: dU, dL/dAV, and the per-row terms
 //                         of the LayerNorm_av parameter gradients
-//   silu_bwd_kernel       dpre = d(u|v|q|k) * SiLU'(pre)
+//   silu_bwd_kernel       dpre = d(u|v|q|k) * SiLU'(pre), with db1's row-chunk sums
 //   ln_bwd_kernel         one wave per row: dx through LayerNorm_in (+ dY)
 #include "common.h"
 #include "gemm.h"
@@ -206,19 +206,41 @@ __global__ __launch_bounds__(256) void gate_bwd_kernel(const float* __restrict__
   }
 }
 
-// dpre = dact * SiLU'(pre + b1), SiLU'(z) = s (1 + z (1 - s)), s = sigmoid(z);
-// written in fp32 and in the layer dtype.
+// dpre = dact * SiLU'(pre + b1), SiLU'(z) = s (1 + z (1 - s)), s = sigmoid(z),
+// written in the layer dtype, and db1's first stage: the column sums of dpre
+// (fp32) over rows [chunk * kColRows, ...) into part[chunk][c].  Each lane
+// owns four adjacent columns; n1 is a multiple of 4.
 template <typename T>
 __global__ __launch_bounds__(256) void silu_bwd_kernel(const float* __restrict__ pre, const T* __restrict__ b1,
-                                                       const float* __restrict__ dact, int64_t total, int n1,
-                                                       float* __restrict__ dpre, T* __restrict__ dpre_t) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= total) return;
-  const float z = pre[i] + to_f32(b1[i % n1]);
-  const float s = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z * -1.4426950408889634f));
-  const float d = dact[i] * s * (1.0f + z * (1.0f - s));
-  dpre[i] = d;
-  dpre_t[i] = from_f32<T>(d);
+                                                       const float* __restrict__ dact, int64_t R, int n1,
+                                                       T* __restrict__ dpre_t, float* __restrict__ part) {
+  const int64_t c = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (c >= n1) return;
+  const int64_t r0 = (int64_t)blockIdx.y * kColRows, r1 = min(r0 + kColRows, R);
+  float bias[4], acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) bias[q] = to_f32(b1[c + q]);
+  for (int64_t r = r0; r < r1; ++r) {
+    const float4 zp = *reinterpret_cast<const float4*>(pre + r * n1 + c);
+    const float4 g = *reinterpret_cast<const float4*>(dact + r * n1 + c);
+    const float zv[4] = {zp.x, zp.y, zp.z, zp.w}, gv[4] = {g.x, g.y, g.z, g.w};
+    T out[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float z = zv[q] + bias[q];
+      const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z * -1.4426950408889634f));
+      const float d = gv[q] * sg * (1.0f + z * (1.0f - sg));
+      acc[q] += d;
+      out[q] = from_f32<T>(d);
+    }
+    T* dst = dpre_t + r * n1 + c;
+    if constexpr (sizeof(T) == 2) {
+      *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(out);
+    } else {
+      *reinterpret_cast<float4*>(dst) = *reinterpret_cast<const float4*>(out);
+    }
+  }
+  *reinterpret_cast<float4*>(part + blockIdx.y * (int64_t)n1 + c) = make_float4(acc[0], acc[1], acc[2], acc[3]);
 }
 
 // One wave per row.  With the input LayerNorm: x^ = (x - mean) rstd,
@@ -362,16 +384,20 @@ hipError_t launch_gate_bwd(const hstu_desc& d, int64_t T, const hstu_weights& w,
 }
 
 hipError_t launch_silu_bwd(hstu_dtype dt, const float* pre, const void* b1, const float* dact, int64_t T, int n1,
-                           float* dpre, void* dpre_t, hipStream_t s) {
-  const int64_t total = T * n1;
-  if (total == 0) return hipSuccess;
-  const dim3 grid((unsigned)((total + 255) / 256)), block(256);
-  if (dt == HSTU_BF16)
-    hipLaunchKernelGGL(silu_bwd_kernel<bf16>, grid, block, 0, s, pre, (const bf16*)b1, dact, total, n1, dpre,
-                       (bf16*)dpre_t);
-  else
-    hipLaunchKernelGGL(silu_bwd_kernel<float>, grid, block, 0, s, pre, (const float*)b1, dact, total, n1, dpre,
-                       (float*)dpre_t);
+                           void* dpre_t, float* part, float* db1, hipStream_t s) {
+  if (n1 % 4 != 0) return hipErrorInvalidValue;
+  const int64_t chunks = (T + kColRows - 1) / kColRows;
+  if (chunks > 0) {
+    const dim3 grid((unsigned)((n1 / 4 + 255) / 256), (unsigned)chunks), block(256);
+    if (dt == HSTU_BF16)
+      hipLaunchKernelGGL(silu_bwd_kernel<bf16>, grid, block, 0, s, pre, (const bf16*)b1, dact, T, n1, (bf16*)dpre_t,
+                         part);
+    else
+      hipLaunchKernelGGL(silu_bwd_kernel<float>, grid, block, 0, s, pre, (const float*)b1, dact, T, n1,
+                         (float*)dpre_t, part);
+  }
+  hipLaunchKernelGGL(colsum_chunks_kernel, dim3((unsigned)((n1 + 63) / 64)), dim3(64 * kColGroups), 0, s,
+                     (const float*)part, chunks, (int64_t)n1, db1);
   return hipGetLastError();
 }
 
