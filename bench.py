@@ -367,6 +367,19 @@ def main():
         _, gout = _lib.layer_bwd(desc, x, off, ts, nc, dev["layers"][0], gdy, dx=gdx,
                                  grads=gout or None, workspace=gws)
     bwd_ms = timed(bwd, reps=5)
+    # A training step with saved activations: hstu_layer_fwd_train, then
+    # hstu_layer_bwd with HSTU_SAVED_FWD on the same workspace.
+    sdesc = _lib.make_desc(w.dims, _lib.HSTU_SAVED_FWD)
+    ty = torch.empty_like(x)
+
+    def train_step():
+        nonlocal gout
+        _lib.layer_fwd_train(desc, x, off, ts, nc, dev["layers"][0], workspace=gws, out=ty)
+        _, gout = _lib.layer_bwd(sdesc, x, off, ts, nc, dev["layers"][0], gdy, dx=gdx,
+                                 grads=gout or None, workspace=gws)
+    train_fwd_ms = timed(lambda: _lib.layer_fwd_train(desc, x, off, ts, nc, dev["layers"][0], workspace=gws,
+                                                      out=ty), reps=5)
+    train_ms = timed(train_step, reps=5)
     proj_ms = timed(lambda: _lib.proj_fwd(desc, x, dev["layers"][0], acts))
     zbuf = torch.empty_like(acts["u"])
     gate_ms = timed(lambda: _lib.gate_fwd(desc, dev["layers"][0], acts, z=zbuf), reps=20)
@@ -442,6 +455,13 @@ def main():
             "ms": bwd_ms,
             "tokens_per_s": T / (bwd_ms * 1e-3),
             "ratio_to_forward_layer": bwd_ms / (ms_step / len(w.layers)),
+            "saved_activations": {
+                "what": "hstu_layer_fwd_train then hstu_layer_bwd with HSTU_SAVED_FWD (no recompute)",
+                "fwd_train_ms": train_fwd_ms,
+                "bwd_ms": train_ms - train_fwd_ms,
+                "step_ms": train_ms,
+                "step_tokens_per_s": T / (train_ms * 1e-3),
+            },
         },
         "type_bias": {
             "what": "hstu_attn_fwd of layer 1 with a 2-type token-type term (interleaved content/action)",

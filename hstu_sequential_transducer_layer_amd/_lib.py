@@ -21,11 +21,12 @@ HSTU_OK, HSTU_ERR_INVALID_ARG, HSTU_ERR_UNSUPPORTED, HSTU_ERR_WORKSPACE, HSTU_ER
 HSTU_F32, HSTU_BF16 = 0, 1
 HSTU_INPUT_NORM, HSTU_RESIDUAL, HSTU_CAND_SHARED_POS, HSTU_VALIDATE = 1, 2, 4, 8
 HSTU_REUSE_PLAN = 1 << 4
+HSTU_SAVED_FWD = 1 << 5
 
 EXPORTS = [
     "hstu_workspace_size", "hstu_layer_fwd", "hstu_proj_workspace_size", "hstu_proj_fwd",
     "hstu_attn_workspace_size", "hstu_attn_fwd", "hstu_gate_fwd", "hstu_out_fwd",
-    "hstu_cand_workspace_size", "hstu_cand_fwd", "hstu_bwd_workspace_size", "hstu_layer_bwd",
+    "hstu_cand_workspace_size", "hstu_cand_fwd", "hstu_bwd_workspace_size", "hstu_layer_fwd_train", "hstu_layer_bwd",
     "hstu_attn_bwd_workspace_size", "hstu_attn_bwd",
     "hstu_sl_workspace_size", "hstu_sl_sample",
     "hstu_gather_rows", "hstu_debug_indices",
@@ -108,6 +109,8 @@ def load() -> ctypes.CDLL:
                                   P(HstuWeights), P(HstuBiasTables), vp, vp, sz, vp]
     lib.hstu_bwd_workspace_size.argtypes = [P(HstuDesc), i64, i32]
     lib.hstu_bwd_workspace_size.restype = sz
+    lib.hstu_layer_fwd_train.argtypes = [P(HstuDesc), vp, vp, i32, i64, vp, vp, P(HstuWeights),
+                                         P(HstuBiasTables), vp, vp, sz, vp]
     lib.hstu_layer_bwd.argtypes = [P(HstuDesc), vp, vp, i32, i64, vp, vp, P(HstuWeights), P(HstuBiasTables),
                                    vp, vp, P(HstuGrads), vp, sz, vp]
     lib.hstu_attn_bwd_workspace_size.argtypes = [P(HstuDesc), i64, i32]
@@ -120,7 +123,7 @@ def load() -> ctypes.CDLL:
     lib.hstu_gather_rows.argtypes = [vp, i64, i64, vp, vp, i64, vp, vp]
     lib.hstu_debug_indices.argtypes = [P(HstuDesc), vp, i32, i64, vp, vp, vp, i64, vp, vp]
     for f in ("hstu_layer_fwd", "hstu_proj_fwd", "hstu_attn_fwd", "hstu_gate_fwd", "hstu_out_fwd",
-              "hstu_cand_fwd", "hstu_layer_bwd", "hstu_attn_bwd", "hstu_sl_sample", "hstu_gather_rows", "hstu_debug_indices"):
+              "hstu_cand_fwd", "hstu_layer_fwd_train", "hstu_layer_bwd", "hstu_attn_bwd", "hstu_sl_sample", "hstu_gather_rows", "hstu_debug_indices"):
         getattr(lib, f).restype = ctypes.c_int
     lib.hstu_status_str.argtypes = [ctypes.c_int]
     lib.hstu_status_str.restype = ctypes.c_char_p
@@ -326,6 +329,22 @@ def cand_fwd(desc: HstuDesc, x_cand: torch.Tensor, cand_offsets: torch.Tensor,
 
 def bwd_workspace_size(desc: HstuDesc, T: int, B: int) -> int:
     return int(load().hstu_bwd_workspace_size(ctypes.byref(desc), T, B))
+
+
+def layer_fwd_train(desc: HstuDesc, x: torch.Tensor, seq_offsets: torch.Tensor, timestamps: torch.Tensor,
+                    num_candidates: Optional[torch.Tensor], prm: Dict[str, torch.Tensor],
+                    workspace: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """hstu_layer_fwd_train: the layer forward into a backward workspace (kept
+    for layer_bwd with HSTU_SAVED_FWD); returns `out`."""
+    lib = load()
+    T, B = x.shape[0], seq_offsets.shape[0] - 1
+    if out is None:
+        out = torch.empty_like(x)
+    w, t = make_weights(prm), make_tables(prm)
+    _check(lib.hstu_layer_fwd_train(ctypes.byref(desc), _ptr(x), _ptr(seq_offsets), B, T, _ptr(timestamps),
+                                    _ptr(num_candidates), ctypes.byref(w), ctypes.byref(t), _ptr(out),
+                                    _ptr(workspace), workspace.numel(), _stream()))
+    return out
 
 
 def layer_bwd(desc: HstuDesc, x: torch.Tensor, seq_offsets: torch.Tensor, timestamps: torch.Tensor,

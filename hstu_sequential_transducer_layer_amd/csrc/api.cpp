@@ -42,7 +42,7 @@ hstu_status check_desc(const hstu_desc* d) {
   if (d->dtype != HSTU_F32 && d->dtype != HSTU_BF16)
     return fail(HSTU_ERR_UNSUPPORTED, "unknown dtype %d", (int)d->dtype);
   if (d->flags & ~(uint32_t)(HSTU_INPUT_NORM | HSTU_RESIDUAL | HSTU_CAND_SHARED_POS | HSTU_VALIDATE |
-                             HSTU_REUSE_PLAN))
+                             HSTU_REUSE_PLAN | HSTU_SAVED_FWD))
     return fail(HSTU_ERR_INVALID_ARG, "unknown flag bits 0x%x", d->flags);
   if (d->d_model < 32 || d->d_model > 8192 || d->d_model % 32 != 0)
     return fail(HSTU_ERR_UNSUPPORTED, "d_model %d: must be a multiple of 32 in [32, 8192]", d->d_model);
@@ -514,6 +514,54 @@ size_t hstu_bwd_workspace_size(const hstu_desc* desc, int64_t T, int32_t B) {
   return bwd_layout(desc, T, B).total;
 }
 
+// The forward into a backward workspace: U, V, Q, K; AV and its statistics
+// (and the work list); Z in its own region (V stays); then f2 into out when
+// out is given.
+static hstu_status fwd_into_bwd_layout(const hstu_desc* desc, const void* x, const int64_t* off, int32_t B,
+                                       int64_t T, const int64_t* ts, const int32_t* nc, const hstu_weights* w,
+                                       const hstu_bias_tables* tables, const BwdLayout& L, char* base, void* out,
+                                       hipStream_t s) {
+  hstu_status st;
+  hstu_activations a;
+  a.u = base + L.f.u;
+  a.v = base + L.f.v;
+  a.q = base + L.f.q;
+  a.k = base + L.f.k;
+  a.av = base + L.f.av;
+  a.av_stats = (float*)(base + L.f.stats);
+  if ((st = run_proj(desc, x, T, w, &a, base + L.f.xn, s)) != HSTU_OK) return st;
+  if ((st = run_attn(desc, off, B, T, ts, nc, tables, &a, base + L.f.attn, s)) != HSTU_OK) return st;
+  void* z = base + L.z;
+  if ((st = device(hstu::launch_gate(*desc, T, *w, a.u, a.av, a.av_stats, z, s), "gate launch")) != HSTU_OK) return st;
+  if (out)
+    if ((st = device(hstu::launch_f2(*desc, x, T, *w, z, out, s), "f2 launch")) != HSTU_OK) return st;
+  return HSTU_OK;
+}
+
+hstu_status hstu_layer_fwd_train(const hstu_desc* desc, const void* x, const int64_t* off, int32_t B, int64_t T,
+                                 const int64_t* ts, const int32_t* nc, const hstu_weights* w,
+                                 const hstu_bias_tables* tables, void* out, void* ws, size_t ws_bytes,
+                                 hstu_stream_t stream) {
+  hstu_status st;
+  if ((st = check_bwd_desc(desc)) != HSTU_OK) return st;
+  if ((st = check_sizes(T, B)) != HSTU_OK) return st;
+  if (T == 0) return ok();
+  HSTU_REQ(x, 16, "x");
+  HSTU_REQ(out, 16, "out");
+  if ((st = check_meta(off, B, ts, nc)) != HSTU_OK) return st;
+  if ((st = check_proj_weights(desc, w)) != HSTU_OK) return st;
+  if ((st = check_out_weights(desc, w)) != HSTU_OK) return st;
+  if ((st = check_tables(desc, tables)) != HSTU_OK) return st;
+  const BwdLayout L = bwd_layout(desc, T, B);
+  if (!ws || ws_bytes < L.total || !aligned(ws, 256))
+    return fail(HSTU_ERR_WORKSPACE, "workspace: need %zu bytes (256-aligned), got %zu", L.total, ws_bytes);
+  hipStream_t s = (hipStream_t)stream;
+  if (desc->flags & HSTU_VALIDATE)
+    if ((st = validate_metadata(off, B, T, nc, s)) != HSTU_OK) return st;
+  if ((st = fwd_into_bwd_layout(desc, x, off, B, T, ts, nc, w, tables, L, (char*)ws, out, s)) != HSTU_OK) return st;
+  return ok();
+}
+
 hstu_status hstu_layer_bwd(const hstu_desc* desc, const void* x, const int64_t* off, int32_t B, int64_t T,
                            const int64_t* ts, const int32_t* nc, const hstu_weights* w,
                            const hstu_bias_tables* tables, const void* dy, void* dx, const hstu_grads* g,
@@ -566,11 +614,9 @@ hstu_status hstu_layer_bwd(const hstu_desc* desc, const void* x, const int64_t* 
   a.av_stats = F(L.f.stats);
   const bool norm = (desc->flags & HSTU_INPUT_NORM) != 0;
   const void* xn = norm ? (const void*)(base + L.f.xn) : x;
-  // forward recompute: U, V, Q, K; AV and its statistics (and the work list); Z
-  if ((st = run_proj(desc, x, T, w, &a, base + L.f.xn, s)) != HSTU_OK) return st;
-  if ((st = run_attn(desc, off, B, T, ts, nc, tables, &a, base + L.f.attn, s)) != HSTU_OK) return st;
   void* z = base + L.z;
-  if ((st = device(hstu::launch_gate(*desc, T, *w, a.u, a.av, a.av_stats, z, s), "gate launch")) != HSTU_OK) return st;
+  if (!(desc->flags & HSTU_SAVED_FWD))
+    if ((st = fwd_into_bwd_layout(desc, x, off, B, T, ts, nc, w, tables, L, base, nullptr, s)) != HSTU_OK) return st;
   // f2: dZ = dY W2, dW2 = dY^T Z, db2 = sum dY
   if ((st = device(hstu::launch_transpose(dt, w->w2, dm, K2, dm, base + L.w2t, s), "transpose")) != HSTU_OK) return st;
   if ((st = device(hstu::launch_gemm_nt_f32(dt, dy, base + L.w2t, F(L.dz), T, (int)K2, dm, nullptr, s), "gemm")) != HSTU_OK)

@@ -84,7 +84,9 @@ enum {
   HSTU_RESIDUAL = 1u << 1,        /* Y += x ([SRM] "Code")                           */
   HSTU_CAND_SHARED_POS = 1u << 2, /* candidates all take position n_b (M-FALCON)     */
   HSTU_VALIDATE = 1u << 3,        /* copy metadata to the host, check, synchronise   */
-  HSTU_REUSE_PLAN = 1u << 4       /* attention plan already in the workspace (below) */
+  HSTU_REUSE_PLAN = 1u << 4,      /* attention plan already in the workspace (below) */
+  HSTU_SAVED_FWD = 1u << 5        /* hstu_layer_bwd: forward activations already in the
+                                     workspace, from hstu_layer_fwd_train (below)     */
 };
 
 /* HSTU_REUSE_PLAN: the attention work list and the per-key-block timestamp
@@ -274,13 +276,28 @@ typedef struct {
  * Stochastic Length train this layer): given dy = dL/dy [T, d] (layer
  * dtype), writes dx = dL/dx [T, d] (layer dtype; may not alias dy or x) and
  * every parameter gradient, for the layer defined above.  The forward
- * activations are recomputed into the workspace (nothing is kept from a
- * forward call).  Supported: dqk = dv in {32, 64, 128} for bf16, {32, 64} for
+ * activations are recomputed into the workspace, unless desc->flags has
+ * HSTU_SAVED_FWD: then the caller asserts that hstu_layer_fwd_train ran just
+ * before with the same arguments and workspace (with other contents the
+ * gradients are wrong but every access stays in bounds).  Supported: dqk = dv in {32, 64, 128} for bf16, {32, 64} for
  * fp32, num_types = 0, pos_buckets + time_buckets <= 2048; else
  * HSTU_ERR_UNSUPPORTED.  Results are reproducible bit for bit.  Weight gradients come from
  * GEMMs over the token dimension in the layer dtype with fp32 accumulation.
  *   workspace >= hstu_bwd_workspace_size(desc, T, B) bytes, 256-aligned     */
 size_t hstu_bwd_workspace_size(const hstu_desc* desc, int64_t total_tokens, int32_t batch);
+
+/* The layer forward of a training step: the same computation and result as
+ * hstu_layer_fwd (bit for bit), run in a backward workspace whose forward part
+ * it leaves filled (x after the input LayerNorm, U, V, Q, K, AV and its
+ * statistics, the attention plan, and Z = LN(AV) * U), so that a following
+ * hstu_layer_bwd with HSTU_SAVED_FWD, on the same stream, with the same
+ * arguments and workspace, skips its forward recompute.  Limits as
+ * hstu_layer_bwd.  HSTU_SAVED_FWD in desc is ignored here.
+ *   workspace >= hstu_bwd_workspace_size(desc, T, B) bytes, 256-aligned     */
+hstu_status hstu_layer_fwd_train(const hstu_desc* desc, const void* x, const int64_t* seq_offsets, int32_t batch,
+                                 int64_t total_tokens, const int64_t* timestamps, const int32_t* num_candidates,
+                                 const hstu_weights* weights, const hstu_bias_tables* tables, void* out,
+                                 void* workspace, size_t workspace_bytes, hstu_stream_t stream);
 hstu_status hstu_layer_bwd(const hstu_desc* desc, const void* x, const int64_t* seq_offsets, int32_t batch,
                            int64_t total_tokens, const int64_t* timestamps, const int32_t* num_candidates,
                            const hstu_weights* weights, const hstu_bias_tables* tables, const void* dy,

@@ -28,7 +28,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 20
+    assert len(names) == 21
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.EXPORTS)
@@ -258,6 +258,24 @@ def test_bwd_entry_point_checks_arguments(lib):
     assert call(_desc(), ws=None) == _lib.HSTU_ERR_WORKSPACE
     assert lib.hstu_bwd_workspace_size(R(_desc()), 1000, 4) > lib.hstu_workspace_size(R(_desc()), 1000, 4)
     assert lib.hstu_bwd_workspace_size(R(_desc(dqk=64, dv=32)), 1000, 4) == 0
+
+
+def test_fwd_train_entry_point_checks_arguments(lib):
+    R = ctypes.byref
+    w = _lib.HstuWeights(*([FAKE] * 8))
+    t = _lib.HstuBiasTables(FAKE, FAKE, 129, 64)
+    call = lambda d, x=FAKE, out=FAKE, ws=FAKE, wb=1 << 40: lib.hstu_layer_fwd_train(
+        R(d), x, FAKE, 4, 1000, FAKE, None, R(w), R(t), out, ws, wb, None)
+    assert call(_desc(dqk=64, dv=128)) == _lib.HSTU_ERR_UNSUPPORTED          # the backward's limits
+    assert call(_desc(num_types=2)) == _lib.HSTU_ERR_UNSUPPORTED
+    assert call(_desc(), x=None) == _lib.HSTU_ERR_INVALID_ARG
+    assert call(_desc(), out=FAKE + 8) == _lib.HSTU_ERR_INVALID_ARG          # misaligned
+    assert call(_desc(), ws=None) == _lib.HSTU_ERR_WORKSPACE
+    need = lib.hstu_bwd_workspace_size(R(_desc()), 1000, 4)
+    assert call(_desc(), wb=need - 1) == _lib.HSTU_ERR_WORKSPACE             # a backward workspace
+    # the saved-forward flag is a known flag bit
+    flags = _lib.HSTU_INPUT_NORM | _lib.HSTU_RESIDUAL | _lib.HSTU_CAND_SHARED_POS | _lib.HSTU_SAVED_FWD
+    assert lib.hstu_bwd_workspace_size(R(_desc(flags=flags)), 1000, 4) == need
 
 
 def test_attn_bwd_entry_point_checks_arguments(lib):

@@ -193,3 +193,34 @@ def test_attention_stage_backward(case):
         say(f"  d{n}: err {e:.3e} (tol {tol:.0e})")
         assert e <= tol, n
     assert np.all(D[:, :K2] == 0)   # the u block is not written
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_saved_forward_matches_recompute(dtype):
+    """hstu_layer_fwd_train gives hstu_layer_fwd's output bit for bit, and
+    hstu_layer_bwd with HSTU_SAVED_FWD on its workspace gives the recomputing
+    backward's dx and gradients bit for bit (the same kernels on the same
+    inputs; only the recompute is skipped)."""
+    if dtype == "fp32":
+        w = edge_workload("fp32", seed=4)
+    else:
+        w = synth.make_workload("small_fp32", seed=5, lengths=[3, 127, 0, 200, 64],
+                                candidates=[0, 2, 0, 9, 64], dims=BF16_64, random_ln=True)
+    say(f"saved forward, {dtype}: lengths {w.lengths().tolist()}")
+    dev = layer.to_device(w)
+    desc = _lib.make_desc(w.dims)
+    saved = _lib.make_desc(w.dims, _lib.HSTU_SAVED_FWD)
+    prm = dev["layers"][0]
+    args = (dev["offsets"], dev["timestamps"], dev["num_candidates"], prm)
+    rng = np.random.default_rng(4)
+    dy = torch.from_numpy(rng.normal(0, 1, (w.T, w.dims.d_model)).astype(np.float32)).to(dev["x"].dtype).cuda()
+    y_ref = _lib.layer_fwd(desc, dev["x"], *args)
+    dx_ref, g_ref = _lib.layer_bwd(desc, dev["x"], *args, dy)
+    ws = _lib.alloc_workspace(_lib.bwd_workspace_size(desc, w.T, w.B), "cuda")
+    y = _lib.layer_fwd_train(desc, dev["x"], *args, workspace=ws)
+    dx, g = _lib.layer_bwd(saved, dev["x"], *args, dy, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_ref)
+    assert torch.equal(dx, dx_ref)
+    for k in g_ref:
+        assert torch.equal(g[k], g_ref[k]), k
