@@ -297,21 +297,42 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
     const int j0 = block_start(blk);
     if (r0 >= iend) return;
     // A far block: every key a history key strictly before the wave's first
-    // row and at least R positions from it (position bucket 2R, no mask);
-    // with one time bucket per row over the block's time span, the bias is
-    // one value per row (wave-uniform test).
-    bool fast = j0 + 63 < L && j0 + 63 < nh && j0 + 63 < r0 && position(r0, nh, shared) - (j0 + 63) >= R;
-    int bt_row = 0;
-    float b_row = 0.f;
-    if (fast) {
-      int64_t kmin, kmax;
+    // row and at least R positions from it (position bucket 2R, no mask).
+    // Per row the block's time differences lie in [ts_q - kmax, ts_q - kmin]
+    // (no overflow) and the bucket is monotone in dt: with one bucket at both
+    // ends the bias is one value per row (mode 0); with two adjacent ones a
+    // key takes the upper bucket exactly when ts_j <= ts_q - (first dt of
+    // that bucket) (mode 1).  Otherwise every pair is bucketed (mode 2).
+    // The mode is wave-uniform.
+    const bool far = j0 + 63 < L && j0 + 63 < nh && j0 + 63 < r0 && position(r0, nh, shared) - (j0 + 63) >= R;
+    int mode = 2, bt_lo = 0, bt_hi = 0;
+    float b_lo = 0.f, b_hi = 0.f;
+    int64_t tcut = 0;
+    if (far) {
+      int64_t kmin, kmax, dlo, dhi;
       bwd_block_minmax(a.tstat, s0 + j0, kmin, kmax);
-      const int lo = time_bucket(wrap_sub(ts_q, kmax), NB, a.sbits);
-      const int hi = time_bucket(wrap_sub(ts_q, kmin), NB, a.sbits);
-      fast = __all(lo == hi || !qvalid);
-      bt_row = lo;
-      b_row = pos_s[2 * R] + time_s[lo];
+      const bool ok = !__builtin_sub_overflow(ts_q, kmax, &dlo) && !__builtin_sub_overflow(ts_q, kmin, &dhi);
+      bt_lo = time_bucket(dlo, NB, a.sbits);
+      bt_hi = time_bucket(dhi, NB, a.sbits);
+      b_lo = pos_s[2 * R] + time_s[bt_lo];
+      if (__all((ok && bt_lo == bt_hi) || !qvalid)) {
+        mode = 0;
+      } else if (__all((ok && bt_hi <= bt_lo + 1) || !qvalid)) {
+        mode = 1;
+        b_hi = pos_s[2 * R] + time_s[bt_hi];
+        tcut = ts_q - bucket_floor(max(bt_hi, 1), a.sbits);  // >= kmin: no overflow
+      }
+      mode = __builtin_amdgcn_readfirstlane(mode);
     }
+    // time-bucket gradient runs: a lane's buckets only fall as its keys advance
+    auto add_run = [&](int bt, float v) __attribute__((always_inline)) {
+      if (bt != run_bt) {
+        if (run != 0.f) atomicAdd(&gtime[run_bt], run);
+        run_bt = bt;
+        run = 0.f;
+      }
+      run += v;
+    };
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
       f32x16 sc = f32x16{}, da = f32x16{};
@@ -320,22 +341,32 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int c = 0; c < DV / 16; ++c) da = mma_k16(bwd_row_frag<T, DV>(Vs, kh * 32 + l32, 16 * c + 8 * half), df[c], da);
       float ds[16];
-      if (fast) {
+      if (mode == 0) {
         float sum = 0.f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float s = sc[r] + b_row;
+          const float s = sc[r] + b_lo;
           const float sg = bwd_sigmoid(s);
           ds[r] = qvalid ? da[r] * sg * (1.0f + s * (1.0f - sg)) * inv_n : 0.f;
           sum += ds[r];
         }
         far_hi += sum;
-        if (bt_row != run_bt) {
-          if (run != 0.f) atomicAdd(&gtime[run_bt], run);
-          run_bt = bt_row;
-          run = 0.f;
+        add_run(bt_lo, sum);
+      } else if (mode == 1) {
+        float sum_lo = 0.f, sum_hi = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kl = kh * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          const bool up = tsk[kl] <= tcut;
+          const float s = sc[r] + (up ? b_hi : b_lo);
+          const float sg = bwd_sigmoid(s);
+          ds[r] = qvalid ? da[r] * sg * (1.0f + s * (1.0f - sg)) * inv_n : 0.f;
+          sum_hi += up ? ds[r] : 0.f;
+          sum_lo += up ? 0.f : ds[r];
         }
-        run += sum;
+        far_hi += sum_hi + sum_lo;
+        add_run(bt_hi, sum_hi);
+        add_run(bt_lo, sum_lo);
       } else
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -354,12 +385,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
             far_hi += g;
           else
             atomicAdd(&gpos[bp], g);
-          if (bt != run_bt) {
-            if (run != 0.f) atomicAdd(&gtime[run_bt], run);
-            run_bt = bt;
-            run = 0.f;
-          }
-          run += g;
+          add_run(bt, g);
         }
       }
 #pragma unroll
@@ -487,16 +513,29 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(BwdArgs a) {
     // A far block (the dq kernel's test with queries and keys swapped): all
     // the wave's keys history keys strictly before the block's first query
     // and at least R positions from it; one time bucket per key.
+    // Modes as in the dq kernel, per key: the block's differences lie in
+    // [qmin - ts_k, qmax - ts_k]; in mode 1 a query takes the upper bucket
+    // exactly when ts_i >= ts_k + (first dt of that bucket).
     const int k_last = min(kr0 + 31, jend - 1);
-    bool fast = i0 + 63 < L && k_last < nh && i0 > k_last && position(i0, nh, shared) - k_last >= R;
-    float b_key = 0.f;
-    if (fast) {
-      int64_t qmin, qmax;
+    const bool far = i0 + 63 < L && k_last < nh && i0 > k_last && position(i0, nh, shared) - k_last >= R;
+    int mode = 2;
+    float b_lo = 0.f, b_hi = 0.f;
+    int64_t tcut = 0;
+    if (far) {
+      int64_t qmin, qmax, dlo, dhi;
       bwd_block_minmax(a.tstat, s0 + i0, qmin, qmax);
-      const int lo = time_bucket(wrap_sub(qmin, ts_k), NB, a.sbits);
-      const int hi = time_bucket(wrap_sub(qmax, ts_k), NB, a.sbits);
-      fast = __all(lo == hi || !kvalid);
-      b_key = pos_s[2 * R] + time_s[lo];
+      const bool ok = !__builtin_sub_overflow(qmin, ts_k, &dlo) && !__builtin_sub_overflow(qmax, ts_k, &dhi);
+      const int lo = time_bucket(dlo, NB, a.sbits);
+      const int hi = time_bucket(dhi, NB, a.sbits);
+      b_lo = pos_s[2 * R] + time_s[lo];
+      if (__all((ok && lo == hi) || !kvalid)) {
+        mode = 0;
+      } else if (__all((ok && hi <= lo + 1) || !kvalid)) {
+        mode = 1;
+        b_hi = pos_s[2 * R] + time_s[hi];
+        tcut = ts_k + bucket_floor(max(hi, 1), a.sbits);  // <= qmax: no overflow
+      }
+      mode = __builtin_amdgcn_readfirstlane(mode);
     }
 #pragma unroll
     for (int qh = 0; qh < 2; ++qh) {
@@ -508,10 +547,19 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(BwdArgs a) {
         for (int c = 0; c < DV / 16; ++c) da = mma_k16(bwd_row_frag<T, DV>(Os, qh * 32 + l32, 16 * c + 8 * half), vf[c], da);
       }
       float g[16];
-      if (fast) {
+      if (mode == 0) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float s = sc[r] + b_key;
+          const float s = sc[r] + b_lo;
+          const float sg = bwd_sigmoid(s);
+          const float val = DK ? da[r] * sg * (1.0f + s * (1.0f - sg)) * inv_n : s * sg * inv_n;
+          g[r] = kvalid ? val : 0.f;
+        }
+      } else if (mode == 1) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int ql = qh * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          const float s = sc[r] + (tsq[ql] >= tcut ? b_hi : b_lo);
           const float sg = bwd_sigmoid(s);
           const float val = DK ? da[r] * sg * (1.0f + s * (1.0f - sg)) * inv_n : s * sg * inv_n;
           g[r] = kvalid ? val : 0.f;

@@ -94,6 +94,61 @@ def test_bwd_long_128_bf16():
     _check_grads(w, seed=4)
 
 
+FAR_FP32 = synth.LayerDims(64, 2, 32, 32, time_buckets=128, time_sub_bits=1, dtype="fp32")
+
+
+def _far_block_kinds(w):
+    """Count the backward kernels' far (32-row wave, 64-key block) pairs —
+    every key a history key at least R positions before the wave's first
+    row — by how many time buckets the wave's rows see over the block
+    (host-side count with the oracle's bucket function; the wave's rows are
+    positions r0 .. r0 + 31 of a sequence without candidates)."""
+    from oracle import hstu_oracle as O
+    d = w.dims
+    R = (d.pos_buckets - 1) // 2
+    kinds = {"one": 0, "two": 0, "more": 0}
+    for b in range(len(w.offsets) - 1):
+        s0, e = int(w.offsets[b]), int(w.offsets[b + 1])
+        t, L = w.timestamps[s0:e], e - s0
+        for r0 in range(0, L, 32):
+            tq = t[r0:min(r0 + 32, L)]
+            for j0 in range(0, L, 64):
+                if not (j0 + 63 < r0 and r0 - (j0 + 63) >= R):
+                    break
+                kb = t[j0:j0 + 64]
+                lo = O.time_bucket(tq - kb.max(), d.time_buckets, d.time_sub_bits)
+                hi = O.time_bucket(tq - kb.min(), d.time_buckets, d.time_sub_bits)
+                kinds["one" if np.all(lo == hi) else "two" if np.all(hi <= lo + 1) else "more"] += 1
+    return kinds
+
+
+def test_bwd_far_block_modes_fp32():
+    # long histories and two sub-buckets per octave: far blocks with one time
+    # bucket per row, with two adjacent ones (per-key split), and with more
+    w = synth.make_workload("small_fp32", seed=7, lengths=[640, 450], candidates=[0, 0], dims=FAR_FP32)
+    kinds = _far_block_kinds(w)
+    say(f"backward, far-block modes fp32: lengths {w.lengths().tolist()}, far blocks {kinds}")
+    assert kinds["one"] > 0 and kinds["two"] > 0
+    _check_grads(w, seed=8)
+
+
+def test_bwd_far_block_time_overflow_fp32():
+    # a far block whose time span overflows int64 differences: key 0 at the
+    # earliest representable time, the queries one second past the epoch, so
+    # the span's endpoints both give bucket 0 while the keys in between are
+    # 100+ seconds back; the per-pair path must take it (pairwise differences
+    # wrap as in the oracle)
+    w = synth.make_workload("small_fp32", seed=9, lengths=[300], candidates=[0], dims=FAR_FP32)
+    ts = np.zeros(w.T, np.int64)
+    ts[0] = np.iinfo(np.int64).min + 1
+    ts[1] = 5
+    ts[2:64] = -100 - np.arange(62)
+    ts[128:] = 1
+    w.timestamps = ts
+    say(f"backward, int64-overflowing far block fp32: lengths {w.lengths().tolist()}")
+    _check_grads(w, seed=10)
+
+
 def test_bwd_shared_tables_sum_heads():
     w = edge_workload("fp32", seed=5)
     dev = layer.to_device(w)
