@@ -215,16 +215,6 @@ __device__ __forceinline__ f32x8 to_frag<float>(const float* p) {
   return f;
 }
 
-// Log time bucket of dt for |dt| < 2^24, where (float)dt is exact: its bits
-// hold the exponent floor(log2 dt) + 127 followed by the mantissa, so
-// bits >> (23 - s) = ((k + 127) << s) | (the s bits below the leading one).
-// dt <= 0 gives a value below 1 (the bits of a negative float are negative as
-// int32), which the clamp sends to bucket 0.  Equal to time_bucket there.
-__device__ __forceinline__ int time_bucket_small(int dt, int nb, int s) {
-  const int b = (__float_as_int((float)dt) >> (23 - s)) + 1 - (127 << s);
-  return min(max(b, 0), nb - 1);
-}
-
 // bucket_floor for buckets reached by dt < 2^24 (k < 24), in 32 bits and
 // with selects only.
 __device__ __forceinline__ int bucket_floor_small(int b, int s) {

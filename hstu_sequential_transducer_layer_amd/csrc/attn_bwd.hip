@@ -23,6 +23,8 @@
 //   dK^T += Q^T dS.  Two passes keep each pass's accumulators in registers.
 // K/V (Q/dO) blocks are staged in LDS by direct global->LDS loads, double
 // buffered: block b + 1 is copied while block b is consumed.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -304,14 +306,17 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
     // key takes the upper bucket exactly when ts_j <= ts_q - (first dt of
     // that bucket) (mode 1).  Otherwise every pair is bucketed (mode 2).
     // The mode is wave-uniform.
+    // Mode 2 takes each pair's time difference from the low 32 bits of both
+    // timestamps when every row's range lies within +-2^24 (small).
     const bool far = j0 + 63 < L && j0 + 63 < nh && j0 + 63 < r0 && position(r0, nh, shared) - (j0 + 63) >= R;
     int mode = 2, bt_lo = 0, bt_hi = 0;
     float b_lo = 0.f, b_hi = 0.f;
-    int64_t tcut = 0;
+    int64_t tcut = 0, kmin, kmax, dlo, dhi;
+    bwd_block_minmax(a.tstat, s0 + j0, kmin, kmax);
+    const bool ok = !__builtin_sub_overflow(ts_q, kmax, &dlo) && !__builtin_sub_overflow(ts_q, kmin, &dhi);
+    const bool small = __builtin_amdgcn_readfirstlane(
+                           __all((ok && dlo > -(1 << 24) && dhi < (1 << 24)) || !qvalid) ? 1 : 0) != 0;
     if (far) {
-      int64_t kmin, kmax, dlo, dhi;
-      bwd_block_minmax(a.tstat, s0 + j0, kmin, kmax);
-      const bool ok = !__builtin_sub_overflow(ts_q, kmax, &dlo) && !__builtin_sub_overflow(ts_q, kmin, &dhi);
       bt_lo = time_bucket(dlo, NB, a.sbits);
       bt_hi = time_bucket(dhi, NB, a.sbits);
       b_lo = pos_s[2 * R] + time_s[bt_lo];
@@ -332,6 +337,32 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
         run = 0.f;
       }
       run += v;
+    };
+    // Mode 2: each pair's buckets, mask and table-gradient updates
+    auto pairs = [&](auto small_t, int kh, const f32x16& sc, const f32x16& da, float (&ds)[16])
+                     __attribute__((always_inline)) {
+      constexpr bool SMALL = decltype(small_t)::value;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kl = kh * 32 + 8 * (r >> 2) + 4 * half + (r & 3), j = j0 + kl;
+        const bool valid = qvalid && j < L && attends(iq, j, nh);
+        const int bp = pos_bucket(p_q, position(j, nh, shared), R);
+        const int bt = SMALL ? time_bucket_small((int)((uint32_t)ts_q - (uint32_t)tsk[kl]), NB, a.sbits)
+                             : time_bucket(wrap_sub(ts_q, tsk[kl]), NB, a.sbits);
+        const float s = sc[r] + pos_s[bp] + time_s[bt];
+        const float sg = bwd_sigmoid(s);
+        const float g = da[r] * sg * (1.0f + s * (1.0f - sg)) * inv_n;
+        ds[r] = valid ? g : 0.f;
+        if (valid) {
+          if (bp == 0)
+            far_lo += g;
+          else if (bp == 2 * R)
+            far_hi += g;
+          else
+            atomicAdd(&gpos[bp], g);
+          add_run(bt, g);
+        }
+      }
     };
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
@@ -367,26 +398,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
         far_hi += sum_hi + sum_lo;
         add_run(bt_hi, sum_hi);
         add_run(bt_lo, sum_lo);
-      } else
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kl = kh * 32 + 8 * (r >> 2) + 4 * half + (r & 3), j = j0 + kl;
-        const bool valid = qvalid && j < L && attends(iq, j, nh);
-        const int bp = pos_bucket(p_q, position(j, nh, shared), R);
-        const int bt = time_bucket(wrap_sub(ts_q, tsk[kl]), NB, a.sbits);
-        const float s = sc[r] + pos_s[bp] + time_s[bt];
-        const float sg = bwd_sigmoid(s);
-        const float g = da[r] * sg * (1.0f + s * (1.0f - sg)) * inv_n;
-        ds[r] = valid ? g : 0.f;
-        if (valid) {
-          if (bp == 0)
-            far_lo += g;
-          else if (bp == 2 * R)
-            far_hi += g;
-          else
-            atomicAdd(&gpos[bp], g);
-          add_run(bt, g);
-        }
+      } else if (small) {
+        pairs(std::true_type{}, kh, sc, da, ds);
+      } else {
+        pairs(std::false_type{}, kh, sc, da, ds);
       }
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2) {
@@ -520,11 +535,29 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(BwdArgs a) {
     const bool far = i0 + 63 < L && k_last < nh && i0 > k_last && position(i0, nh, shared) - k_last >= R;
     int mode = 2;
     float b_lo = 0.f, b_hi = 0.f;
-    int64_t tcut = 0;
+    int64_t tcut = 0, qmin, qmax, dlo, dhi;
+    bwd_block_minmax(a.tstat, s0 + i0, qmin, qmax);
+    const bool ok = !__builtin_sub_overflow(qmin, ts_k, &dlo) && !__builtin_sub_overflow(qmax, ts_k, &dhi);
+    const bool small = __builtin_amdgcn_readfirstlane(
+                           __all((ok && dlo > -(1 << 24) && dhi < (1 << 24)) || !kvalid) ? 1 : 0) != 0;
+    // Mode 2: each pair's buckets and mask (32-bit differences when small)
+    auto pairs = [&](auto small_t, int qh, const f32x16& sc, const f32x16& da, float (&g)[16])
+                     __attribute__((always_inline)) {
+      constexpr bool SMALL = decltype(small_t)::value;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int ql = qh * 32 + 8 * (r >> 2) + 4 * half + (r & 3), i = i0 + ql;
+        const bool valid = kvalid && i < L && attends(i, jk, nh);
+        const int bp = pos_bucket(position(i, nh, shared), p_k, R);
+        const int bt = SMALL ? time_bucket_small((int)((uint32_t)tsq[ql] - (uint32_t)ts_k), NB, a.sbits)
+                             : time_bucket(wrap_sub(tsq[ql], ts_k), NB, a.sbits);
+        const float s = sc[r] + pos_s[bp] + time_s[bt];
+        const float sg = bwd_sigmoid(s);
+        const float val = DK ? da[r] * sg * (1.0f + s * (1.0f - sg)) * inv_n : s * sg * inv_n;
+        g[r] = valid ? val : 0.f;
+      }
+    };
     if (far) {
-      int64_t qmin, qmax, dlo, dhi;
-      bwd_block_minmax(a.tstat, s0 + i0, qmin, qmax);
-      const bool ok = !__builtin_sub_overflow(qmin, ts_k, &dlo) && !__builtin_sub_overflow(qmax, ts_k, &dhi);
       const int lo = time_bucket(dlo, NB, a.sbits);
       const int hi = time_bucket(dhi, NB, a.sbits);
       b_lo = pos_s[2 * R] + time_s[lo];
@@ -564,17 +597,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(BwdArgs a) {
           const float val = DK ? da[r] * sg * (1.0f + s * (1.0f - sg)) * inv_n : s * sg * inv_n;
           g[r] = kvalid ? val : 0.f;
         }
-      } else
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int ql = qh * 32 + 8 * (r >> 2) + 4 * half + (r & 3), i = i0 + ql;
-        const bool valid = kvalid && i < L && attends(i, jk, nh);
-        const int bp = pos_bucket(position(i, nh, shared), p_k, R);
-        const int bt = time_bucket(wrap_sub(tsq[ql], ts_k), NB, a.sbits);
-        const float s = sc[r] + pos_s[bp] + time_s[bt];
-        const float sg = bwd_sigmoid(s);
-        const float val = DK ? da[r] * sg * (1.0f + s * (1.0f - sg)) * inv_n : s * sg * inv_n;
-        g[r] = valid ? val : 0.f;
+      } else if (small) {
+        pairs(std::true_type{}, qh, sc, da, g);
+      } else {
+        pairs(std::false_type{}, qh, sc, da, g);
       }
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2) {

@@ -156,6 +156,16 @@ __device__ __forceinline__ int time_bucket(int64_t dt, int nb, int s) {
   return dt > 0 ? b : 0;
 }
 
+// Log time bucket of dt for |dt| < 2^24, where (float)dt is exact: its bits
+// hold the exponent floor(log2 dt) + 127 followed by the mantissa, so
+// bits >> (23 - s) = ((k + 127) << s) | (the s bits below the leading one).
+// dt <= 0 gives a value below 1 (the bits of a negative float are negative as
+// int32), which the clamp sends to bucket 0.  Equal to time_bucket there.
+__device__ __forceinline__ int time_bucket_small(int dt, int nb, int s) {
+  const int b = (__float_as_int((float)dt) >> (23 - s)) + 1 - (127 << s);
+  return min(max(b, 0), nb - 1);
+}
+
 // Smallest dt >= 1 whose time bucket is >= b, for a bucket b >= 1 that some
 // dt in int64 reaches.  With c = b - 1 = (k << s) + sub: for k >= s every
 // sub-bucket exists and starts at 2^k + sub * 2^(k-s); for k < s the bits
