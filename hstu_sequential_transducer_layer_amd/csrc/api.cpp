@@ -457,7 +457,7 @@ hstu_status hstu_cand_fwd(const hstu_desc* desc, const void* x, const int64_t* c
 // Backward workspace: the forward's buffers, then the backward's.
 struct BwdLayout {
   Layout f;
-  size_t z, dz, dact, dav, gterm_av, bterm_av, tab_part, pre, dpre_t, w2t, dyt, zt, w1t, dpret, xnt, dxn, gterm_in,
+  size_t z, dz, dact, dav, gterm_av, bterm_av, tab_part, dpre_t, w2t, dyt, zt, w1t, dpret, xnt, dxn, gterm_in,
       ctmp, wsplit, total;
   int64_t Tp;
 };
@@ -482,7 +482,6 @@ static BwdLayout bwd_layout(const hstu_desc* d, int64_t T, int32_t B) {
   L.gterm_av = take((size_t)T * K2 * 4);
   L.bterm_av = take((size_t)T * K2 * 4);
   L.tab_part = take((size_t)hstu::attn_max_tiles(T, B) * d->num_heads * (d->pos_buckets + d->time_buckets) * 4);
-  L.pre = take((size_t)T * N1 * 4);
   L.dpre_t = take((size_t)T * N1 * e);
   L.w2t = take((size_t)K2 * dm * e);
   L.dyt = take((size_t)dm * L.Tp * e);
@@ -642,9 +641,8 @@ hstu_status hstu_layer_bwd(const hstu_desc* desc, const void* x, const int64_t* 
                    "attention backward launch")) != HSTU_OK)
     return st;
   // f1 and SiLU: dpre = d(u|v|q|k) * SiLU'(x~ W1^T + b1); db1, dW1 = dpre^T x~, dx~ = dpre W1
-  if ((st = device(hstu::launch_gemm_nt_f32(dt, xn, w->w1, F(L.pre), T, (int)N1, dm, nullptr, s), "gemm")) != HSTU_OK) return st;
-  if ((st = device(hstu::launch_silu_bwd(dt, F(L.pre), w->b1, dact, T, (int)N1, base + L.dpre_t, ctmp, g->b1, s),
-                   "silu backward launch")) != HSTU_OK)
+  if ((st = device(hstu::launch_gemm_silu_bwd(dt, xn, w->w1, w->b1, dact, T, (int)N1, dm, base + L.dpre_t, ctmp, g->b1, s),
+                   "pre-activation gemm and silu backward launch")) != HSTU_OK)
     return st;
   if ((st = device(hstu::launch_transpose(dt, w->w1, N1, dm, N1, base + L.w1t, s), "transpose")) != HSTU_OK) return st;
   if ((st = device(hstu::launch_gemm_nt_f32(dt, base + L.dpre_t, base + L.w1t, F(L.dxn), T, dm, (int)N1, nullptr, s), "gemm")) !=

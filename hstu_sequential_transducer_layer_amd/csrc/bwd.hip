@@ -11,7 +11,8 @@
 //                         deterministic stages
 //   gate_bwd_kernel       one wave per row: dU, dL/dAV, and the per-row terms
 //                         of the LayerNorm_av parameter gradients
-//   silu_bwd_kernel       dpre = d(u|v|q|k) * SiLU'(pre), with db1's row-chunk sums
+//   gemm_silu_bwd_kernel  pre = x~ W1^T on MFMA, kept in registers; dpre =
+//                         d(u|v|q|k) * SiLU'(pre + b1) and db1's row-chunk sums
 //   ln_bwd_kernel         one wave per row: dx through LayerNorm_in (+ dY)
 #include "common.h"
 #include "gemm.h"
@@ -206,41 +207,97 @@ __global__ __launch_bounds__(256) void gate_bwd_kernel(const float* __restrict__
   }
 }
 
-// dpre = dact * SiLU'(pre + b1), SiLU'(z) = s (1 + z (1 - s)), s = sigmoid(z),
-// written in the layer dtype, and db1's first stage: the column sums of dpre
-// (fp32) over rows [chunk * kColRows, ...) into part[chunk][c].  Each lane
-// owns four adjacent columns; n1 is a multiple of 4.
+// The pre-activation GEMM of f1 with the SiLU backward as its epilogue: the
+// 128 x 128 tile pre = A B^T (A = x~ [M, K], B = W1 [N, K]) never leaves the
+// chip.  z = pre + b1 goes through LDS, 64 rows at a time (rows padded to 136
+// floats, so the accumulator writes of a wave's two 4-row groups hit
+// different banks), and is read back along rows: each thread takes 8 columns
+// of one row per pass, loads dact with 16-byte loads and writes dpre =
+// dact * SiLU'(z) in the layer dtype.  The tile's 128 rows are one row chunk
+// of db1's column sums: a thread adds its rows in order, then the 16 row
+// groups are added in order into part[chunk][col].  N is a multiple of 8.
+constexpr int kSiluPad = 136;
 template <typename T>
-__global__ __launch_bounds__(256) void silu_bwd_kernel(const float* __restrict__ pre, const T* __restrict__ b1,
-                                                       const float* __restrict__ dact, int64_t R, int n1,
-                                                       T* __restrict__ dpre_t, float* __restrict__ part) {
-  const int64_t c = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
-  if (c >= n1) return;
-  const int64_t r0 = (int64_t)blockIdx.y * kColRows, r1 = min(r0 + kColRows, R);
-  float bias[4], acc[4] = {0.f, 0.f, 0.f, 0.f};
+__global__ __launch_bounds__(256, 2) void gemm_silu_bwd_kernel(const T* __restrict__ A, const T* __restrict__ Bm,
+                                                               const T* __restrict__ b1, const float* __restrict__ dact,
+                                                               int64_t M, int N, int K, T* __restrict__ dpre,
+                                                               float* __restrict__ part) {
+  typedef GemmTile<T> G;
+  static_assert(G::BM == kColRows && G::BM == 128 && G::BN == 128, "a tile row is one row chunk of the column sums");
+  __shared__ __attribute__((aligned(16))) T As[G::BM * G::LDK];
+  __shared__ __attribute__((aligned(16))) T Bs[G::BN * G::LDK];
+  __shared__ __attribute__((aligned(16))) float zs[64 * kSiluPad];
+  __shared__ float red[16][G::BN];
+  const int nrow = (int)((M + G::BM - 1) / G::BM), ncol = (N + G::BN - 1) / G::BN;
+  int tr, tc;
+  map_tile(blockIdx.x, nrow, ncol, tr, tc);
+  const int64_t row0 = (int64_t)tr * G::BM;
+  const int col0 = tc * G::BN;
+  RowLoader<T> al{A, row0, M, K, K};
+  f32x16 acc[2][2];
+  gemm_mainloop<T>(al, Bm, col0, N, K, As, Bs, acc, K);
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), wm = w >> 1, wn = w & 1;
+  float bias[2];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) bias[q] = to_f32(b1[c + q]);
-  for (int64_t r = r0; r < r1; ++r) {
-    const float4 zp = *reinterpret_cast<const float4*>(pre + r * n1 + c);
-    const float4 g = *reinterpret_cast<const float4*>(dact + r * n1 + c);
-    const float zv[4] = {zp.x, zp.y, zp.z, zp.w}, gv[4] = {g.x, g.y, g.z, g.w};
-    T out[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float z = zv[q] + bias[q];
-      const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z * -1.4426950408889634f));
-      const float d = gv[q] * sg * (1.0f + z * (1.0f - sg));
-      acc[q] += d;
-      out[q] = from_f32<T>(d);
-    }
-    T* dst = dpre_t + r * n1 + c;
-    if constexpr (sizeof(T) == 2) {
-      *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(out);
-    } else {
-      *reinterpret_cast<float4*>(dst) = *reinterpret_cast<const float4*>(out);
-    }
+  for (int nt = 0; nt < 2; ++nt) {
+    const int col = col0 + wn * 64 + nt * 32 + (lane & 31);
+    bias[nt] = col < N ? to_f32(b1[col]) : 0.f;
   }
-  *reinterpret_cast<float4*>(part + blockIdx.y * (int64_t)n1 + c) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  const int rr = tid >> 4, cg = tid & 15;  // read phase: row group, 8-column group
+  const int gcol = col0 + cg * 8;
+  float cs[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    if (wm == hf) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            zs[(acc_row(0, mt, lane, r)) * kSiluPad + wn * 64 + nt * 32 + (lane & 31)] = acc[mt][nt][r] + bias[nt];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int pss = 0; pss < 4; ++pss) {
+      const int lr = pss * 16 + rr;
+      const int64_t grow = row0 + hf * 64 + lr;
+      if (grow < M && gcol < N) {
+        const float4 z0 = *reinterpret_cast<const float4*>(zs + lr * kSiluPad + cg * 8);
+        const float4 z1 = *reinterpret_cast<const float4*>(zs + lr * kSiluPad + cg * 8 + 4);
+        const float* gp = dact + grow * N + gcol;
+        const float4 g0 = *reinterpret_cast<const float4*>(gp), g1 = *reinterpret_cast<const float4*>(gp + 4);
+        const float zv[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
+        const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+        T out[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const float z = zv[q];
+          const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z * -1.4426950408889634f));
+          const float d = gv[q] * sg * (1.0f + z * (1.0f - sg));
+          cs[q] += d;
+          out[q] = from_f32<T>(d);
+        }
+        T* dst = dpre + grow * N + gcol;
+        if constexpr (sizeof(T) == 2) {
+          *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(out);
+        } else {
+          *reinterpret_cast<float4*>(dst) = *reinterpret_cast<const float4*>(out);
+          *reinterpret_cast<float4*>(dst + 4) = *reinterpret_cast<const float4*>(out + 4);
+        }
+      }
+    }
+    __syncthreads();  // zs is rewritten by the next half
+  }
+#pragma unroll
+  for (int q = 0; q < 8; ++q) red[rr][cg * 8 + q] = cs[q];
+  __syncthreads();
+  if (tid < G::BN && col0 + tid < N) {
+    float sum = 0.f;
+#pragma unroll
+    for (int g = 0; g < 16; ++g) sum += red[g][tid];
+    part[(int64_t)tr * N + col0 + tid] = sum;
+  }
 }
 
 // One wave per row.  With the input LayerNorm: x^ = (x - mean) rstd,
@@ -383,18 +440,18 @@ hipError_t launch_gate_bwd(const hstu_desc& d, int64_t T, const hstu_weights& w,
   return hipGetLastError();
 }
 
-hipError_t launch_silu_bwd(hstu_dtype dt, const float* pre, const void* b1, const float* dact, int64_t T, int n1,
-                           void* dpre_t, float* part, float* db1, hipStream_t s) {
-  if (n1 % 4 != 0) return hipErrorInvalidValue;
+hipError_t launch_gemm_silu_bwd(hstu_dtype dt, const void* A, const void* w1, const void* b1, const float* dact,
+                                int64_t T, int n1, int K, void* dpre_t, float* part, float* db1, hipStream_t s) {
+  if (n1 % 8 != 0 || K % 8 != 0) return hipErrorInvalidValue;
   const int64_t chunks = (T + kColRows - 1) / kColRows;
   if (chunks > 0) {
-    const dim3 grid((unsigned)((n1 / 4 + 255) / 256), (unsigned)chunks), block(256);
+    const dim3 grid((unsigned)(chunks * ((n1 + 127) / 128)));
     if (dt == HSTU_BF16)
-      hipLaunchKernelGGL(silu_bwd_kernel<bf16>, grid, block, 0, s, pre, (const bf16*)b1, dact, T, n1, (bf16*)dpre_t,
-                         part);
+      hipLaunchKernelGGL(gemm_silu_bwd_kernel<bf16>, grid, dim3(256), 0, s, (const bf16*)A, (const bf16*)w1,
+                         (const bf16*)b1, dact, T, n1, K, (bf16*)dpre_t, part);
     else
-      hipLaunchKernelGGL(silu_bwd_kernel<float>, grid, block, 0, s, pre, (const float*)b1, dact, T, n1,
-                         (float*)dpre_t, part);
+      hipLaunchKernelGGL(gemm_silu_bwd_kernel<float>, grid, dim3(256), 0, s, (const float*)A, (const float*)w1,
+                         (const float*)b1, dact, T, n1, K, (float*)dpre_t, part);
   }
   hipLaunchKernelGGL(colsum_chunks_kernel, dim3((unsigned)((n1 + 63) / 64)), dim3(64 * kColGroups), 0, s,
                      (const float*)part, chunks, (int64_t)n1, db1);

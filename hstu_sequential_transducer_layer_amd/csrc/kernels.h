@@ -195,10 +195,11 @@ hipError_t launch_gemm_nt_f32(hstu_dtype dt, const void* A, const void* Bm, floa
 hipError_t launch_gate_bwd(const hstu_desc& d, int64_t T, const hstu_weights& w, const float* dz, const void* u,
                            const void* av, const float* stats, float* du, void* dav, float* gterm, float* bterm,
                            hipStream_t s);
-// dpre_t = dact * SiLU'(pre + b1) in the layer dtype; db1 = its column sums
-// (part: colsum_tmp_bytes(T, n1) of scratch).
-hipError_t launch_silu_bwd(hstu_dtype dt, const float* pre, const void* b1, const float* dact, int64_t T, int n1,
-                           void* dpre_t, float* part, float* db1, hipStream_t s);
+// pre = A W1^T (A [T, K], W1 [n1, K], K a multiple of 8), then dpre_t = dact *
+// SiLU'(pre + b1) in the layer dtype and db1 = its column sums (part:
+// colsum_tmp_bytes(T, n1) of scratch); pre itself is never stored.
+hipError_t launch_gemm_silu_bwd(hstu_dtype dt, const void* A, const void* w1, const void* b1, const float* dact,
+                                int64_t T, int n1, int K, void* dpre_t, float* part, float* db1, hipStream_t s);
 hipError_t launch_ln_bwd(const hstu_desc& d, const void* x, const float* dxn, const hstu_weights& w, const void* dy,
                          int64_t T, void* dx, float* gterm, hipStream_t s);
 
