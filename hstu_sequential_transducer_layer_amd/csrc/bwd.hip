@@ -20,6 +20,29 @@
 
 namespace hstu {
 
+// Eight consecutive elements (16-byte aligned) to and from fp32 registers:
+// one 16-byte access for bf16, two for fp32.
+__device__ __forceinline__ void load8(const float* p, float (&f)[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
+  f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+}
+__device__ __forceinline__ void load8(const bf16* p, float (&f)[8]) {
+  const uint4 raw = *reinterpret_cast<const uint4*>(p);
+  const bf16* e = reinterpret_cast<const bf16*>(&raw);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) f[q] = to_f32(e[q]);
+}
+__device__ __forceinline__ void store8(float* p, const float (&f)[8]) {
+  *reinterpret_cast<float4*>(p) = make_float4(f[0], f[1], f[2], f[3]);
+  *reinterpret_cast<float4*>(p + 4) = make_float4(f[4], f[5], f[6], f[7]);
+}
+__device__ __forceinline__ void store8(bf16* p, const float (&f)[8]) {
+  bf16 e[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) e[q] = from_f32<bf16>(f[q]);
+  *reinterpret_cast<uint4*>(p) = *reinterpret_cast<const uint4*>(e);
+}
+
 // dst[c][r] = src[r][c] (zero for r >= R) for r < Rp, c < C, through a 64 x 64
 // LDS tile; 16-byte loads along the source rows and 16-byte stores along the
 // destination rows.  C, Rp multiples of 16 / sizeof(T).
@@ -178,6 +201,8 @@ __global__ __launch_bounds__(256) void gate_bwd_kernel(const float* __restrict__
                                                        int64_t M, int H, int dv, float eps, int64_t n1,
                                                        float* __restrict__ du, T* __restrict__ dav,
                                                        float* __restrict__ gterm, float* __restrict__ bterm) {
+  // one wave per row; a lane takes 8 consecutive columns of one head per step
+  // (dv a multiple of 8)
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + wave_id();
   if (row >= M) return;
@@ -189,21 +214,43 @@ __global__ __launch_bounds__(256) void gate_bwd_kernel(const float* __restrict__
   const float rstd = rsqrtf(m2 / (float)K + eps);
   const int64_t o = row * K;
   float s1 = 0.f, s2 = 0.f;
-  for (int c = lane; c < K; c += kWave) {
-    const float nh = (to_f32(av[o + c]) + __shfl(dm, c / dv, kWave)) * rstd;
-    const float dnh = dz[o + c] * to_f32(u[o + c]) * to_f32(g[c]);
-    s1 += dnh;
-    s2 += dnh * nh;
+  float a8[8], z8[8], u8[8], g8[8];
+  for (int c = lane * 8; c < K; c += 8 * kWave) {
+    const float off = __shfl(dm, c / dv, kWave);
+    load8(av + o + c, a8);
+    load8(dz + o + c, z8);
+    load8(u + o + c, u8);
+    load8(g + c, g8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float nh = (a8[e] + off) * rstd;
+      const float dnh = z8[e] * u8[e] * g8[e];
+      s1 += dnh;
+      s2 += dnh * nh;
+    }
   }
   const float m1 = wave_sum(s1) / (float)K, mm = wave_sum(s2) / (float)K;
-  for (int c = lane; c < K; c += kWave) {
-    const float nh = (to_f32(av[o + c]) + __shfl(dm, c / dv, kWave)) * rstd;
-    const float gg = to_f32(g[c]);
-    const float dn = dz[o + c] * to_f32(u[o + c]);
-    du[row * n1 + c] = dz[o + c] * (nh * gg + to_f32(be[c]));
-    dav[o + c] = from_f32<T>(rstd * (dn * gg - m1 - nh * mm));
-    gterm[o + c] = dn * nh;
-    bterm[o + c] = dn;
+  for (int c = lane * 8; c < K; c += 8 * kWave) {
+    const float off = __shfl(dm, c / dv, kWave);
+    float b8[8], o_du[8], o_dav[8], o_g[8], o_b[8];
+    load8(av + o + c, a8);
+    load8(dz + o + c, z8);
+    load8(u + o + c, u8);
+    load8(g + c, g8);
+    load8(be + c, b8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float nh = (a8[e] + off) * rstd;
+      const float dn = z8[e] * u8[e];
+      o_du[e] = z8[e] * (nh * g8[e] + b8[e]);
+      o_dav[e] = rstd * (dn * g8[e] - m1 - nh * mm);
+      o_g[e] = dn * nh;
+      o_b[e] = dn;
+    }
+    store8(du + row * n1 + c, o_du);
+    store8(dav + o + c, o_dav);
+    store8(gterm + o + c, o_g);
+    store8(bterm + o + c, o_b);
   }
 }
 
@@ -308,42 +355,69 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(const T* __restrict__ x, co
                                                      const T* __restrict__ g, const T* __restrict__ dy, int64_t M,
                                                      int d, float eps, int norm, int residual, T* __restrict__ dx,
                                                      float* __restrict__ gterm) {
+  // one wave per row; a lane takes 8 consecutive columns per step (16-byte
+  // accesses for bf16), d a multiple of 8
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + wave_id();
   if (row >= M) return;
   const int64_t o = row * d;
   float mean = 0.f, rstd = 1.f, m1 = 0.f, mm = 0.f;
+  float xv[8], gv[8], dv8[8];
   if (norm) {
     float s = 0.f;
-    for (int c = lane; c < d; c += kWave) s += to_f32(x[o + c]);
+    for (int c = lane * 8; c < d; c += 8 * kWave) {
+      load8(x + o + c, xv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s += xv[e];
+    }
     mean = wave_sum(s) / (float)d;
     float v = 0.f;
-    for (int c = lane; c < d; c += kWave) {
-      const float t = to_f32(x[o + c]) - mean;
-      v += t * t;
+    for (int c = lane * 8; c < d; c += 8 * kWave) {
+      load8(x + o + c, xv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float t = xv[e] - mean;
+        v += t * t;
+      }
     }
     rstd = rsqrtf(wave_sum(v) / (float)d + eps);
     float s1 = 0.f, s2 = 0.f;
-    for (int c = lane; c < d; c += kWave) {
-      const float xh = (to_f32(x[o + c]) - mean) * rstd;
-      const float t = dxn[o + c] * to_f32(g[c]);
-      s1 += t;
-      s2 += t * xh;
+    for (int c = lane * 8; c < d; c += 8 * kWave) {
+      load8(x + o + c, xv);
+      load8(g + c, gv);
+      load8(dxn + o + c, dv8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float xh = (xv[e] - mean) * rstd;
+        const float t = dv8[e] * gv[e];
+        s1 += t;
+        s2 += t * xh;
+      }
     }
     m1 = wave_sum(s1) / (float)d;
     mm = wave_sum(s2) / (float)d;
   }
-  for (int c = lane; c < d; c += kWave) {
-    float r;
+  for (int c = lane * 8; c < d; c += 8 * kWave) {
+    float r[8], gt[8], yv[8];
+    load8(dxn + o + c, dv8);
     if (norm) {
-      const float xh = (to_f32(x[o + c]) - mean) * rstd;
-      r = rstd * (dxn[o + c] * to_f32(g[c]) - m1 - xh * mm);
-      gterm[o + c] = dxn[o + c] * xh;
-    } else {
-      r = dxn[o + c];
+      load8(x + o + c, xv);
+      load8(g + c, gv);
     }
-    if (residual) r += to_f32(dy[o + c]);
-    dx[o + c] = from_f32<T>(r);
+    if (residual) load8(dy + o + c, yv);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if (norm) {
+        const float xh = (xv[e] - mean) * rstd;
+        r[e] = rstd * (dv8[e] * gv[e] - m1 - xh * mm);
+        gt[e] = dv8[e] * xh;
+      } else {
+        r[e] = dv8[e];
+      }
+      if (residual) r[e] += yv[e];
+    }
+    if (norm) store8(gterm + o + c, gt);
+    store8(dx + o + c, r);
   }
 }
 
