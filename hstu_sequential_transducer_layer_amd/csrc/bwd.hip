@@ -11,7 +11,7 @@
 //                         deterministic stages
 //   gate_bwd_kernel       one wave per row: dU, dL/dAV, and the per-row terms
 //                         of the LayerNorm_av parameter gradients
-//   gemm_silu_bwd_kernel  pre = x~ W1^T on MFMA, kept in registers; dpre =
+//   gemm_silu_bwd_kernel  pre = x~ W1^T on MFMA, kept on chip (LDS); dpre =
 //                         d(u|v|q|k) * SiLU'(pre + b1) and db1's row-chunk sums
 //   ln_bwd_kernel         one wave per row: dx through LayerNorm_in (+ dY)
 #include "common.h"
