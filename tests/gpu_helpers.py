@@ -3,6 +3,7 @@ collect their taps as float64 NumPy arrays, and compare with the oracle."""
 
 from __future__ import annotations
 
+import dataclasses
 import sys
 
 import numpy as np
@@ -39,6 +40,10 @@ def gpu_taps(w: "synth.Workload", layer_idx: int = 0, x=None, flags_extra: int =
     y, z = _lib.out_fwd(desc, xin, prm, acts)
     y_layer = _lib.layer_fwd(desc, xin, dev["offsets"], dev["timestamps"],
                              dev["num_candidates"], prm)
+    # the f2 branch on its own: the same layer with the residual flag off
+    nores = dataclasses.replace(w.dims, residual=False)
+    branch = _lib.layer_fwd(_lib.make_desc(nores, flags_extra), xin, dev["offsets"], dev["timestamps"],
+                            dev["num_candidates"], prm)
     torch.cuda.synchronize()
     f = lambda t: t.float().cpu().numpy().astype(np.float64)
     H, dv = w.dims.num_heads, w.dims.dv
@@ -55,6 +60,7 @@ def gpu_taps(w: "synth.Workload", layer_idx: int = 0, x=None, flags_extra: int =
         "z": f(z) if z is not None else None,
         "y": f(y),
         "y_layer": f(y_layer),
+        "branch": f(branch),
         "y_layer_raw": y_layer,
         "y_raw": y,
     }

@@ -26,7 +26,7 @@ def _weight_rounding_error(kind, flags, scale):
     exact = O.attention(q, k, v, w.offsets, w.timestamps, w.num_candidates, prm, w.dims)
     real = O.silu
     try:
-        O.silu = lambda z: r(real(z) * scale) / scale
+        O.silu = lambda z, *a: r(real(z) * scale) / scale
         rounded = O.attention(q, k, v, w.offsets, w.timestamps, w.num_candidates, prm, w.dims)
     finally:
         O.silu = real

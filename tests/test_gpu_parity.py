@@ -21,7 +21,8 @@ from hstu_sequential_transducer_layer_amd import _lib, layer, synth
 from oracle import hstu_oracle as O
 
 from edge_workloads import EDGE_DIMS, bucket_edge_workload, edge_workload as _edge_workload
-from gpu_helpers import check, gpu_taps, say
+from gpu_helpers import BF16_AV_TOL, check, gpu_taps, say
+import bf16_envelope as E
 
 pytestmark = pytest.mark.gpu
 
@@ -31,16 +32,21 @@ def _rows_of(w, seqs):
         if len(seqs) else np.zeros(0, np.int64)
 
 
-def _compare_layer(w, seqs=None, layer_idx=0):
+def _compare_layer(w, seqs=None, layer_idx=0, env_key=None):
     """GPU layer on the whole batch vs oracle on sequences `seqs` (all if None).
 
-    Checked: u, v, q, k end to end; av against the oracle attention fed the
-    GPU's own q, k, v; z and y against the oracle gate/projection fed the
-    GPU's own av and u (each stage isolated, so a stage is judged on its own
-    arithmetic); and y end to end against the float64 oracle (the layer's
-    output, unit scale).  The end-to-end av and z deviations are printed: at
-    this init scale av is a strongly cancelling sum, so bf16 storage of q, k, v
-    alone moves it by a few percent (shown by the isolated check's input)."""
+    Stage by stage: u, v, q, k end to end; av against the oracle attention fed
+    the GPU's own q, k, v; z and y against the oracle gate/projection fed the
+    GPU's own av and u (each stage judged on its own arithmetic).
+
+    End to end against the float64 oracle: y (unit scale), and the taps where
+    an error cannot hide: LayerNorm(AV) (unit variance by construction), z,
+    and the f2 branch (the layer run with the residual flag off, so that
+    neither x nor the output's rounding at x's scale masks it).  fp32 layers
+    hold these to the fp32 tolerance; bf16 layers to the committed bf16
+    envelope of the case (tests/golden/bf16_envelope.json: how far the
+    oracle itself moves when u, v, q, k, the pointwise weights, z and the
+    output are rounded to bf16 inside it) plus 2e-2."""
     g = gpu_taps(w, layer_idx)
     np.testing.assert_array_equal(g["y"], g["y_layer"])   # same kernels, same bits
     sub = w if seqs is None else w.sub_batch(seqs)
@@ -54,15 +60,27 @@ def _compare_layer(w, seqs=None, layer_idx=0):
         errs[t] = check(t, g[t][rows], ref[t], dt)
     av_iso = O.attention(g["q"][rows], g["k"][rows], g["v"][rows], sub.offsets, sub.timestamps,
                          sub.num_candidates, prm, w.dims)
-    from gpu_helpers import BF16_AV_TOL
     errs["av"] = check("av (stage)", g["av"][rows], av_iso, dt, tol=BF16_AV_TOL if dt == "bf16" else None)
     out_iso = O.gate_and_project(g["av"][rows], g["u"][rows], sub.x, prm, w.dims)
     errs["z"] = check("z (stage)", g["z"][rows], out_iso["z"], dt)
     errs["y_stage"] = check("y (stage)", g["y"][rows], out_iso["y"], dt, unit=True)
     errs["y"] = check("y (end to end)", g["y"][rows], ref["y"], dt, unit=True)
-    for t in ("av", "z"):
-        from gpu_helpers import err_fp32
-        say(f"  {t} end to end (info): {err_fp32(g[t][rows], ref[t]):.3e}")
+    # end to end on the taps that bite
+    ln_gpu = O.layer_norm(g["av"][rows], prm["ln_av_g"], prm["ln_av_b"], w.dims.ln_eps)
+    branch_ref = ref["y"] - np.asarray(sub.x, np.float64) if w.dims.residual else ref["y"]
+    got = {"ln_av": ln_gpu, "z": g["z"][rows], "branch": g["branch"][rows]}
+    want = {"ln_av": ref["ln_av"], "z": ref["z"], "branch": branch_ref}
+    for t in E.TAPS:
+        if dt == "bf16":
+            assert env_key is not None, "a bf16 case needs its committed envelope"
+            env = E.load_envelopes()[env_key][t]
+            e = E.unit_err(got[t], want[t])
+            say(f"  {t} end to end: err {e:.3e} (envelope {env:.3e} + {E.MARGIN:.0e})")
+            assert np.all(np.isfinite(got[t])), t
+            assert e <= env + E.MARGIN, f"{t}: end-to-end error {e:.3e} > envelope {env:.3e} + {E.MARGIN}"
+            errs[t + "_e2e"] = e
+        else:
+            errs[t + "_e2e"] = check(f"{t} (end to end)", got[t], want[t], dt)
     return errs
 
 
@@ -80,59 +98,62 @@ def test_small_fp32_random_layernorm():
 def test_zipf_bf16_full():
     w = synth.make_workload("zipf_bf16")
     say(f"zipf_bf16 (bf16, B=32, T={w.T}, d=256, 4x64/64), oracle on all rows")
-    _compare_layer(w)
+    _compare_layer(w, env_key="zipf_bf16")
 
 
 def test_ranking_candidates_full_size():
-    w = synth.make_workload("ranking_cand")
-    L = w.lengths()
-    seqs = [int(np.argmin(L)), int(np.argmax(L))]
+    w, seqs = E.load_full_size_case("ranking_cand")     # shortest and longest
     say(f"ranking_cand (bf16, B=16, T={w.T}, 512 candidates each), oracle on sequences {seqs}")
-    _compare_layer(w, seqs)
+    _compare_layer(w, seqs, env_key="ranking_cand")
 
 
 def test_stochastic_length_full_size():
-    w = synth.make_workload("sl_train")
-    L = w.lengths()
-    long_ = [int(b) for b in np.nonzero(L == L.max())[0][:1]]
-    short = [int(b) for b in np.nonzero(L == L.min())[0][:2]]
-    say(f"sl_train (bf16, B=64, T={w.T}, 8x128/128), oracle on sequences {long_ + short}")
-    _compare_layer(w, long_ + short)
+    w, seqs = E.load_full_size_case("sl_train")         # one longest, two shortest
+    say(f"sl_train (bf16, B=64, T={w.T}, 8x128/128), oracle on sequences {seqs}")
+    _compare_layer(w, seqs, env_key="sl_train")
 
 
 def test_len4k_full_size():
-    w = synth.make_workload("len4k")
-    say(f"len4k (bf16, B=16 x 4096, 8x128/128), oracle on sequence 5")
-    _compare_layer(w, [5])
+    w, seqs = E.load_full_size_case("len4k")
+    say(f"len4k (bf16, B=16 x 4096, 8x128/128), oracle on sequence {seqs}")
+    _compare_layer(w, seqs, env_key="len4k")
 
 
 def test_stack8_first_layer_full_size():
-    w = synth.make_workload("stack8_long", n_layers=1)
-    seqs = [int(np.argmin(w.lengths()))]
-    say(f"stack8_long layer 1 (bf16, B=8, T={w.T}, d=1024, 128 time buckets), oracle on {seqs}")
-    _compare_layer(w, seqs)
+    w, seqs = E.load_full_size_case("stack8_long_layer1")   # shortest and longest
+    say(f"stack8_long layer 1 (bf16, B=8, T={w.T}, d=1024, 128 time buckets), oracle on {seqs} "
+        f"({w.lengths()[seqs].tolist()} rows)")
+    _compare_layer(w, seqs, env_key="stack8_long_layer1")
 
 
 def test_stack8_full_stack():
-    """8 layers on the GPU (full batch).  Checked on the shortest sequence:
-    every layer against the oracle layer applied to the GPU's own bf16 input of
-    that layer (2e-2, unit scale), and the final output against the float64
-    oracle stack within the conditioning envelope (see below)."""
+    """8 layers on the GPU (full batch).
+
+    Shortest sequence: every layer against the oracle layer applied to the
+    GPU's own bf16 input of that layer (2e-2, unit scale), and the final
+    output against the float64 oracle stack within the conditioning envelope
+    (see below).  Longest sequence: every layer against the oracle layer on
+    the GPU's own input of that layer, on 384 of its rows (its first 64, its
+    last 128 and 192 drawn at random; the oracle projects every row, since
+    each sampled row's attention needs all earlier keys)."""
     w = synth.make_workload("stack8_long")
-    s = int(np.argmin(w.lengths()))
-    rows = _rows_of(w, [s])
+    L = w.lengths()
+    s, sl = int(np.argmin(L)), int(np.argmax(L))
+    rows, rows_l = _rows_of(w, [s]), _rows_of(w, [sl])
     say(f"stack8_long, 8 layers (bf16, B=8, T={w.T}), oracle on sequence {s} "
-        f"({w.lengths()[s]} rows)")
+        f"({L[s]} rows) and on sampled rows of sequence {sl} ({L[sl]} rows)")
     dev = layer.to_device(w)
     stack = layer.HSTUStack(w.dims, dev["layers"])
     y = stack.forward(dev["x"], dev["offsets"], dev["timestamps"], dev["num_candidates"])
     # layer by layer through the same entry point
     desc = _lib.make_desc(w.dims)
     h = dev["x"]
-    outs = []
+    outs, outs_l = [], []
     for prm in dev["layers"]:
         h = _lib.layer_fwd(desc, h, dev["offsets"], dev["timestamps"], None, prm)
-        outs.append(h.float().cpu().numpy().astype(np.float64)[rows])
+        hn = h.float().cpu().numpy().astype(np.float64)
+        outs.append(hn[rows])
+        outs_l.append(hn[rows_l])
     torch.cuda.synchronize()
     got = y.float().cpu().numpy().astype(np.float64)[rows]
     np.testing.assert_array_equal(got, outs[-1])
@@ -142,6 +163,18 @@ def test_stack8_full_stack():
         ref_n = O.layer_forward(prev, sub.offsets, sub.timestamps, None, prm, w.dims)["y"]
         check(f"layer {n + 1} (own input)", outs[n], ref_n, "bf16", unit=True)
         prev = outs[n]
+    # the longest sequence, sampled rows of every layer
+    sub_l = w.sub_batch([sl])
+    n_l = int(L[sl])
+    rng = np.random.default_rng(1)
+    pick = np.unique(np.concatenate([np.arange(64), np.arange(n_l - 128, n_l),
+                                     rng.choice(np.arange(64, n_l - 128), 192, replace=False)]))
+    prev = sub_l.x.astype(np.float64)
+    for n, prm in enumerate(sub_l.layers):
+        ref_n = O.layer_forward(prev, sub_l.offsets, sub_l.timestamps, None, prm, w.dims, rows=pick)["y"]
+        check(f"longest sequence, layer {n + 1} (own input, {len(pick)} rows)", outs_l[n][pick], ref_n,
+              "bf16", unit=True)
+        prev = outs_l[n]
     # End to end.  The 8-layer map is ill-conditioned at this init: rounding the
     # exact layers' outputs to bf16 (the stack's interface dtype) already moves
     # the float64 result by several percent.  The GPU must be no further from
@@ -170,7 +203,8 @@ def test_stack8_full_stack():
 def test_edge_cases(kind, flags):
     w = _edge_workload(kind, **flags)
     say(f"edge {kind} {flags}: lengths {w.lengths().tolist()}")
-    _compare_layer(w)
+    key = E.edge_key(kind, E.flag_name_of(flags)) if w.dims.dtype == "bf16" else None
+    _compare_layer(w, env_key=key)
 
 
 @pytest.mark.parametrize("sub_bits,pos_buckets", [(0, 9), (1, 9), (2, 129)])
