@@ -41,8 +41,11 @@ struct BwdArgs {
   const void* v;      // [H, T, DV]
   const void* dout;   // [T, H * DV]: dL/dAV
   float* dact;        // [T, N1]: dv at column K2 + h DV, dq at 2 K2 + h DQK, dk at 2 K2 + H DQK + h DQK
-  float* tab_part;    // [gridDim.x][P + NB]: per-workgroup bias-table gradients (dq kernel)
+  float* tab_part;    // [gridDim.x][P + NB]: per-workgroup bias-table gradients (dq kernel),
+                      // row (tbase[b] + query tile) * H + h: fixed by the batch, not by
+                      // where the item sits in the work list
   const int2* tiles;
+  const int32_t* tbase;  // first query tile of each sequence
   const int32_t* counts;
   const int64_t* tstat;  // per 64-row block's first row: its earliest, latest timestamp
   int64_t T;
@@ -221,8 +224,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
   float* pos_s = tabs;
   float* time_s = tabs + P;
   const int tid = threadIdx.x;
-  float* part = a.tab_part + (int64_t)blockIdx.x * (P + NB);
-  if (item >= a.counts[0]) {  // whole workgroup: an empty partial row
+  if (item >= a.counts[0]) {  // whole workgroup: an empty partial row (rows past the items')
+    float* part = a.tab_part + (int64_t)blockIdx.x * (P + NB);
     for (int i = tid; i < P + NB; i += 256) part[i] = 0.f;
     return;
   }
@@ -234,6 +237,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
   float* gpos = tabs + (P + NB) * (1 + wave_id());
   float* gtime = gpos + P;
   const int2 tl = a.tiles[item];
+  // The item's partial row is its stable index (sequence's first tile + its
+  // query tile), so the column sums of table_grad_kernel add the same rows in
+  // the same order whatever order the work list holds the items in.
+  float* part = a.tab_part + ((int64_t)(a.tbase[tl.x] + tl.y) * H + h) * (P + NB);
   const SeqInfo si = seq_info(a.off, a.ncand, tl.x, a.T);
   const int L = si.len, nh = si.nhist;
   const int64_t s0 = si.start;
@@ -716,6 +723,7 @@ hipError_t launch_attn_bwd(const hstu_desc& d, const int64_t* off, const int32_t
   a.dact = dact;
   a.tab_part = tab_part;
   a.tiles = sc.tiles;
+  a.tbase = sc.tbase;
   a.counts = sc.counts;
   a.tstat = sc.tstat;
   a.T = T;

@@ -4,8 +4,8 @@
 //    row held in registers, fp32 statistics, biased variance.
 //  * build_tiles: the attention work list for jagged batches — one item per
 //    (sequence, 128-row query tile), ordered by decreasing work so the longest
-//    items start first (the pages' "sparsity-aware kernels for variable-length
-//    sequences", "Efficiency tricks" paragraph of the same page), plus the
+//    items start first (kernels that skip the padding of variable-length
+//    sequences: "Efficiency tricks" paragraph of the same page), plus the
 //    list of all 64-key blocks;
 //  * block_ts: per 64-key block, the earliest and latest timestamp and each
 //    key's offset from the earliest — head- and query-independent facts that

@@ -168,11 +168,18 @@ def test_bwd_shared_tables_sum_heads():
     assert err_fp32(g["time"].cpu().numpy(), ref["time_table"].sum(0)) <= 1e-3
 
 
-def test_bwd_deterministic_bitwise():
-    w = synth.make_workload("zipf_bf16", batch=4)
+@pytest.mark.parametrize("name,batch", [("zipf_bf16", 4), ("zipf_bf16", None), ("sl_train", 16)])
+def test_bwd_deterministic_bitwise(name, batch):
+    """Two runs give the same bits.  The full zipf_bf16 batch (32 sequences,
+    over 100 work items of equal cost across sequences, which the work-list
+    builder may place in any order) and 16 stochastic-length sequences (many
+    items of equal cost) check that the bias-table gradients do not depend
+    on the work list's order."""
+    w = synth.make_workload(name, batch=batch, n_layers=1)
     dy = np.random.default_rng(6).normal(0, 1, (w.T, w.dims.d_model))
     a, _ = _gpu_bwd(w, dy)
     b, _ = _gpu_bwd(w, dy)
+    say(f"determinism {name} batch={w.B}: T={w.T}")
     for k in a:
         np.testing.assert_array_equal(a[k], b[k], err_msg=k)
 

@@ -74,25 +74,42 @@ def test_oracle_matches_brute(case):
 
 # ------------------------------------------------------- the page's sketch
 def _sketch_dense_torch(x, prm, H, eps):
-    """Dense equal-length layer in torch float64, written from the "Code" section's
-    description: LN_in -> f1 -> SiLU -> chunk(u, v, q, k) -> heads -> q k^T + rab
-    -> SiLU -> tril (diagonal kept) -> /n -> A V -> merge heads -> LN_av -> * u
-    -> f2 -> + x.  rab[h, i, j] is the dense per-head table."""
-    xb = torch.from_numpy(x)                              # [B, n, d]
-    Bn, n, d = xb.shape
-    t = lambda k: torch.from_numpy(np.asarray(prm[k], np.float64))
-    y0 = F.layer_norm(xb, (d,), t("ln_in_g"), t("ln_in_b"), eps)
-    proj = F.silu(F.linear(y0, t("w1"), t("b1")))
-    u, v, q, k = proj.chunk(4, dim=-1)
-    dh = u.shape[-1] // H
-    heads = lambda a: a.reshape(Bn, n, H, dh).permute(0, 2, 1, 3)
-    q, k, v = heads(q), heads(k), heads(v)
-    scores = torch.matmul(q, k.transpose(-1, -2).contiguous()) + t("rab")[None]
-    keep = torch.ones(n, n, dtype=torch.bool).tril()
-    a = torch.where(keep, F.silu(scores), torch.zeros(())) / n
-    av = torch.matmul(a, v).permute(0, 2, 1, 3).reshape(Bn, n, H * dh)
-    g = F.layer_norm(av, (H * dh,), t("ln_av_g"), t("ln_av_b"), eps) * u
-    return (xb + F.linear(g, t("w2"), t("b2"))).numpy()
+    """Dense equal-length layer in torch float64, written from the three layer
+    equations of page "4.4 Scaling Recommendation Models", section "Generative
+    Recommenders and HSTU": U, V, Q, K are the four equal blocks of
+    SiLU(f1(X)); each head's output is SiLU(Q K^T + rab) V under the causal
+    mask, divided by the constant n; Y = f2(LayerNorm(AV) * U).  From section
+    "Code" it takes the LayerNorm before f1 and the residual.  Sequences and
+    heads are explicit loops, the mask is M_ij = [j <= i] built on index
+    grids, SiLU is z * sigmoid(z) and both LayerNorms are written out.
+    rab[h, i, j] is a dense per-head table."""
+    X = torch.from_numpy(x)                                   # [B, n, d]
+    nb, n, d = X.shape
+    par = lambda key: torch.from_numpy(np.asarray(prm[key], np.float64))
+
+    def norm(a, g, b):
+        mu = a.mean(-1, keepdim=True)
+        var = ((a - mu) ** 2).mean(-1, keepdim=True)
+        return (a - mu) / torch.sqrt(var + eps) * g + b
+
+    Xn = norm(X, par("ln_in_g"), par("ln_in_b"))
+    pre = torch.einsum("bnd,ed->bne", Xn, par("w1")) + par("b1")
+    act = pre * torch.sigmoid(pre)
+    width = act.shape[-1] // 4
+    U, V, Q, K = (act[..., c * width:(c + 1) * width] for c in range(4))
+    dh = width // H
+    ii = torch.arange(n)[:, None]
+    jj = torch.arange(n)[None, :]
+    M = (jj <= ii).to(torch.float64)
+    AV = torch.zeros(nb, n, width, dtype=torch.float64)
+    for b in range(nb):
+        for h in range(H):
+            cols = slice(h * dh, (h + 1) * dh)
+            S = torch.einsum("ie,je->ij", Q[b][:, cols], K[b][:, cols]) + par("rab")[h]
+            A = M * (S * torch.sigmoid(S)) / n
+            AV[b, :, cols] = torch.einsum("ij,je->ie", A, V[b][:, cols])
+    Z = norm(AV, par("ln_av_g"), par("ln_av_b")) * U
+    return (X + torch.einsum("bne,de->bnd", Z, par("w2")) + par("b2")).numpy()
 
 
 def _sketch_case(seed=0, B=3, n=23, d=16, H=2, P=9):
@@ -148,6 +165,28 @@ def test_round_to_bf16_matches_torch():
     a = np.concatenate([a, np.float32([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 0.0, 1e30])])
     want = torch.from_numpy(a).to(torch.bfloat16).to(torch.float64).numpy()
     np.testing.assert_array_equal(O.round_to_bf16(a.astype(np.float64)), want)
+
+
+def test_stack_forward_applies_the_layers_in_order():
+    """stack_forward over two layers is layer 2 applied to layer 1's output;
+    with io_dtype="bf16" each layer's output is rounded to bf16 (the torch-
+    pinned round_to_bf16 above) before the next layer reads it."""
+    w = synth.make_workload("zipf_bf16", batch=3, n_layers=2, lengths=[5, 0, 9], seed=2,
+                            random_ln=True)
+    args = (w.offsets, w.timestamps, None)
+    l1 = O.layer_forward(w.x, *args, w.layers[0], w.dims)["y"]
+    two = O.layer_forward(l1, *args, w.layers[1], w.dims)["y"]
+    np.testing.assert_array_equal(O.stack_forward(w.x, *args, w.layers, w.dims), two)
+    l1b = O.round_to_bf16(l1)
+    twob = O.round_to_bf16(O.layer_forward(l1b, *args, w.layers[1], w.dims)["y"])
+    got = O.stack_forward(w.x, *args, w.layers, w.dims, io_dtype="bf16")
+    np.testing.assert_array_equal(got, twob)
+    # the bf16 interface really rounds: the two stacks differ, and every
+    # element of the bf16 stack is a bf16 value
+    assert np.abs(got - two).max() > 0
+    np.testing.assert_array_equal(torch.from_numpy(got).to(torch.bfloat16).double().numpy(), got)
+    # an empty layer list is the identity
+    np.testing.assert_array_equal(O.stack_forward(w.x, *args, [], w.dims), w.x.astype(np.float64))
 
 
 def _zero_qk(prm, dims):
@@ -350,9 +389,9 @@ MUTANTS = {
     "pos_bias_sign_flipped": ("pos_bucket",
                               lambda dp, P: np.clip(-np.asarray(dp), -(P - 1) // 2, (P - 1) // 2)
                               + (P - 1) // 2),
-    "silu_is_sigmoid": ("silu", lambda z: 1.0 / (1.0 + np.exp(-np.asarray(z, np.float64)))),
+    "silu_is_sigmoid": ("silu", lambda z, *a: 1.0 / (1.0 + np.exp(-np.asarray(z, np.float64)))),
     "layernorm_without_centering": ("layer_norm",
-                                    lambda a, g, b, eps: np.asarray(a) / np.sqrt(
+                                    lambda a, g, b, eps, *_: np.asarray(a) / np.sqrt(
                                         (np.asarray(a) ** 2).mean(-1, keepdims=True) + eps)
                                     * g + b),
 }
@@ -368,8 +407,8 @@ def test_planted_mistake_is_caught(name, monkeypatch):
 def test_planted_split_order_is_caught(monkeypatch):
     real = O.project
 
-    def swapped(x, prm, cfg):
-        u, v, q, k = real(x, prm, cfg)
+    def swapped(x, prm, cfg, **kw):
+        u, v, q, k = real(x, prm, cfg, **kw)
         return u, q.reshape(v.shape), v.reshape(q.shape), k   # V and Q swapped
     monkeypatch.setattr(O, "project", swapped)
     assert not _sketch_pin_holds()
