@@ -75,36 +75,155 @@ def load_traffic(workload: str):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(w, budget_s: float = 20.0):
-    """The oracle as it stands, on a bounded sample: one layer over whole
-    sequences (shortest first) until the budget is spent; reported in the
-    metric's unit (tokens through all layers of the step per second)."""
+# ------------------------------------------------------------ CPU baseline
+# The float64 oracle is the parity reference; for timing, the same oracle
+# functions run in float32 and are spread over worker processes (spawned:
+# fresh interpreters that load NumPy and the oracle only, one BLAS thread
+# each).  Inputs, parameters and results live in shared memory.  The work
+# units: 1024-row blocks for the two GEMM stages, (sequence, 1024-row query
+# block) for the attention, all heads of a unit together so that its bias
+# indices are formed once.
+_CPU = {}
+
+
+def _shm_put(arr, registry, name):
+    from multiprocessing import shared_memory
+    arr = np.ascontiguousarray(arr)
+    shm = shared_memory.SharedMemory(create=True, size=max(arr.nbytes, 1))
+    view = np.ndarray(arr.shape, arr.dtype, buffer=shm.buf)
+    view[...] = arr
+    registry[name] = (shm.name, arr.shape, arr.dtype.str)
+    return shm, view
+
+
+def _shm_get(spec):
+    from multiprocessing import shared_memory
+    shm = shared_memory.SharedMemory(name=spec[0])
+    _CPU.setdefault("_keep", []).append(shm)
+    return np.ndarray(spec[1], np.dtype(spec[2]), buffer=shm.buf)
+
+
+def _cpu_init(registry, cfg):
+    from threadpoolctl import threadpool_limits
+    _CPU["_limits"] = threadpool_limits(1)
+    _CPU["cfg"] = cfg
+    _CPU["arr"] = {k: _shm_get(v) for k, v in registry.items()}
+
+
+def _cpu_ready(_):
+    return os.getpid()
+
+
+def _cpu_task(task):
     from oracle import hstu_oracle as O
+    kind, layer_i, a, b = task[:4]
+    A, cfg = _CPU["arr"], _CPU["cfg"]
+    prm = {k[len(f"p{layer_i}_"):]: v for k, v in A.items() if k.startswith(f"p{layer_i}_")}
+    f32 = np.float32
+    H, dqk, dv = cfg.num_heads, cfg.dqk, cfg.dv
+    if kind == "proj":            # rows [a, b)
+        u, v, q, k = O.project(A["h"][a:b], prm, cfg, dtype=f32)
+        A["u"][a:b] = u
+        A["v"][a:b] = v
+        A["q"][a:b] = q
+        A["k"][a:b] = k
+    elif kind == "attn":          # sequence rows [a, b), local query rows task[4]
+        r0, r1 = task[4]
+        off = np.array([0, b - a], np.int64)
+        nc = A["nc"][task[5]:task[5] + 1] if "nc" in A else None
+        av = O.attention(A["q"][a:b], A["k"][a:b], A["v"][a:b], off, A["ts"][a:b], nc, prm, cfg,
+                         rows=np.arange(r0, r1), dtype=f32)
+        A["av"][a + r0:a + r1] = av
+    else:                         # "out": rows [a, b)
+        out = O.gate_and_project(A["av"][a:b], A["u"][a:b], A["h"][a:b], prm, cfg, dtype=f32)
+        A["y"][a:b] = out["y"]
+    return b - a
+
+
+def cpu_model() -> str:
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = 1
-    order = np.argsort(w.lengths())
-    done_rows, t_used, seqs = 0, 0.0, []
-    for b in order:
-        if t_used > budget_s * 0.5 and seqs:
-            break
-        sub = w.sub_batch([int(b)])
-        t0 = time.perf_counter()
-        O.layer_forward(sub.x, sub.offsets, sub.timestamps, sub.num_candidates, sub.layers[0],
-                        w.dims)
-        t_used += time.perf_counter() - t0
-        done_rows += sub.T
-        seqs.append(int(b))
-        if t_used > budget_s:
-            break
-    n_layers = len(w.layers)
-    value = done_rows / t_used / n_layers
-    return {"value": value, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"float64 NumPy oracle, layer 1 of {n_layers} over sequence(s) {seqs} "
-                      f"({done_rows} tokens) in {t_used:.1f} s; value = tokens / time / "
-                      f"{n_layers} layers"}
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, budget_s: float = 30.0, max_workers: int = 16):
+    """The oracle's functions in float32 over the whole batch, layer after
+    layer of the stack until every layer has run or the budget is spent; the
+    value is tokens through the stack per second (measured, or, if the
+    budget stopped the stack early, the measured per-layer time times the
+    number of layers, which the sample text then says)."""
+    import multiprocessing as mp
+    workers = max(1, min(len(os.sched_getaffinity(0)), max_workers))
+    cfg = w.dims
+    T, H, dqk, dv = w.T, cfg.num_heads, cfg.dqk, cfg.dv
+    reg, keep = {}, []
+    f32 = np.float32
+    try:
+        def put(name, arr):
+            shm, view = _shm_put(arr, reg, name)
+            keep.append(shm)
+            return view
+        h = put("h", w.x.astype(f32))
+        put("u", np.zeros((T, H * dv), f32))
+        put("v", np.zeros((T, H, dv), f32))
+        put("q", np.zeros((T, H, dqk), f32))
+        put("k", np.zeros((T, H, dqk), f32))
+        put("av", np.zeros((T, H * dv), f32))
+        y = put("y", np.zeros((T, cfg.d_model), f32))
+        put("ts", w.timestamps)
+        if w.num_candidates is not None:
+            put("nc", np.asarray(w.num_candidates, np.int32))
+        for li, prm in enumerate(w.layers):
+            for k, v in prm.items():
+                put(f"p{li}_{k}", np.asarray(v, f32))
+        blocks = [(r, min(r + 1024, T)) for r in range(0, T, 1024)]
+        attn_units = []
+        for b in range(w.B):
+            s0, s1 = int(w.offsets[b]), int(w.offsets[b + 1])
+            for r in range(0, s1 - s0, 1024):
+                attn_units.append((s0, s1, (r, min(r + 1024, s1 - s0)), b))
+        # longest units first, so the pool's tail is short
+        attn_units.sort(key=lambda u: -(u[2][1] ** 2 - u[2][0] ** 2))
+        ctx = mp.get_context("spawn")
+        with ctx.Pool(workers, initializer=_cpu_init, initargs=(reg, cfg)) as pool:
+            pool.map(_cpu_ready, range(workers * 4))      # every worker up and attached
+            t_layers = []
+            for li in range(len(w.layers)):
+                t0 = time.perf_counter()
+                pool.map(_cpu_task, [("proj", li, a, b) for a, b in blocks])
+                pool.map(_cpu_task, [("attn", li, s0, s1, rr, bi) for s0, s1, rr, bi in attn_units],
+                         chunksize=1)
+                pool.map(_cpu_task, [("out", li, a, b) for a, b in blocks])
+                t_layers.append(time.perf_counter() - t0)
+                h[...] = y                                 # the next layer's input
+                if sum(t_layers) > budget_s and li + 1 < len(w.layers):
+                    break
+        done = len(t_layers)
+        n_layers = len(w.layers)
+        t_used = sum(t_layers)
+        value = T / (t_used / done * n_layers)
+        ran = (f"all {n_layers} layers" if done == n_layers else
+               f"layers 1-{done} of {n_layers} (the budget of {budget_s:.0f} s was spent; value = "
+               f"tokens / (mean layer time x {n_layers}))")
+        return {"value": value, "unit": "tokens/s", "cores": workers, "kind": "oracle",
+                "precision": "float32 (the float64 mode is the parity reference)",
+                "cpu_model": cpu_model(),
+                "affinity_cores": len(os.sched_getaffinity(0)),
+                "sample": f"the oracle's project / attention / gate_and_project in float32 over the whole "
+                          f"batch ({w.B} sequences, {T} tokens, lengths {int(w.lengths().min())}.."
+                          f"{int(w.lengths().max())}), {ran}, in {t_used:.1f} s on {workers} worker "
+                          f"processes with one BLAS thread each (1024-row blocks for the GEMMs, "
+                          f"(sequence, 1024-row query block) units for the attention)",
+                "layer_seconds": t_layers}
+    finally:
+        for shm in keep:
+            shm.close()
+            shm.unlink()
 
 
 def cand_inference(torch, _lib, layer, synth, per_seq: int = 128, reps: int = 20):
@@ -274,7 +393,7 @@ def main():
     ap.add_argument("--no-cand", action="store_true", help="skip the cached-candidate measurement")
     ap.add_argument("--cand-only", action="store_true",
                     help="run only the cached-candidate measurement and print its JSON object")
-    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--cpu-budget", type=float, default=30.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-MiB device buffer 4 times (a plain copy kernel of "
                          "known size, to scale profiler byte counters) and exit")

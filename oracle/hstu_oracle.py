@@ -117,9 +117,9 @@ def wrap_sub_i64(a, b):
 
 
 # -------------------------------------------------------------- float parts
-def silu(z: np.ndarray) -> np.ndarray:
+def silu(z: np.ndarray, dtype=np.float64) -> np.ndarray:
     """z * sigmoid(z), evaluated so that neither branch overflows."""
-    z = np.asarray(z, np.float64)
+    z = np.asarray(z, dtype)
     out = np.empty_like(z)
     p = z >= 0
     out[p] = z[p] / (1.0 + np.exp(-z[p]))
@@ -128,31 +128,32 @@ def silu(z: np.ndarray) -> np.ndarray:
     return out
 
 
-def layer_norm(a: np.ndarray, gamma, beta, eps: float) -> np.ndarray:
+def layer_norm(a: np.ndarray, gamma, beta, eps: float, dtype=np.float64) -> np.ndarray:
     """LayerNorm over the last axis, biased variance, affine gamma/beta."""
-    a = np.asarray(a, np.float64)
+    a = np.asarray(a, dtype)
     mu = a.mean(axis=-1, keepdims=True)
     var = ((a - mu) ** 2).mean(axis=-1, keepdims=True)
-    return (a - mu) / np.sqrt(var + eps) * np.asarray(gamma, np.float64) \
-        + np.asarray(beta, np.float64)
+    return (a - mu) / np.sqrt(var + eps) * np.asarray(gamma, dtype) \
+        + np.asarray(beta, dtype)
 
 
-def _f64(a):
-    return np.asarray(a, np.float64)
+def _f64(a, dtype=np.float64):
+    return np.asarray(a, dtype)
 
 
 # ------------------------------------------------------------------- layer
-def project(x, prm, cfg):
+def project(x, prm, cfg, dtype=np.float64):
     """Steps 1-2: optional input LayerNorm, f1, SiLU, split into U, V, Q, K.
 
     Returns u [T, H*dv], v [T, H, dv], q [T, H, dqk], k [T, H, dqk].
     Head h owns the contiguous columns h*dh .. h*dh+dh-1 of each block.
+    ``dtype``: float64 for parity; float32 only times the same steps.
     """
-    x = _f64(x)
+    x = _f64(x, dtype)
     T = x.shape[0]
     H, dqk, dv = cfg.num_heads, cfg.dqk, cfg.dv
-    xin = layer_norm(x, prm["ln_in_g"], prm["ln_in_b"], cfg.ln_eps) if cfg.input_norm else x
-    act = silu(xin @ _f64(prm["w1"]).T + _f64(prm["b1"]))
+    xin = layer_norm(x, prm["ln_in_g"], prm["ln_in_b"], cfg.ln_eps, dtype) if cfg.input_norm else x
+    act = silu(xin @ _f64(prm["w1"], dtype).T + _f64(prm["b1"], dtype), dtype)
     c0, c1, c2 = H * dv, 2 * H * dv, 2 * H * dv + H * dqk
     u = act[:, :c0]
     v = act[:, c0:c1].reshape(T, H, dv)
@@ -162,30 +163,32 @@ def project(x, prm, cfg):
 
 
 def attention(q, k, v, offsets, timestamps, num_candidates, prm, cfg, rows=None,
-              row_chunk: int = 256, token_types=None):
+              row_chunk: int = 256, token_types=None, dtype=np.float64):
     """Step 3: AV_i^h = (1/N_b) sum_{j: M_ij} SiLU(q_i.k_j + rab_ij^h) v_j^h.
 
     Returns AV [len(rows), H*dv] for the requested flat rows (all rows when
     ``rows`` is None).  Query rows are processed a chunk at a time only to
     bound memory; each row's sum is one matrix product over keys 0..i.
     With cfg.num_types > 0, rab gains type_table[h, type_i, type_j]
-    (token_types: one type per flat row).
+    (token_types: one type per flat row).  ``dtype``: float64 for parity;
+    float32 only times the same steps.
     """
     typed = getattr(cfg, "num_types", 0) > 0
     if typed:
         ty_all = np.asarray(token_types, I64)
-        wy = _f64(prm["type_table"])
+        wy = _f64(prm["type_table"], dtype)
     T, H, dqk = q.shape
     dv = v.shape[2]
     off = np.asarray(offsets, I64)
     ts_all = np.asarray(timestamps, I64)
     B = len(off) - 1
-    wp = _f64(prm["pos_table"])
-    wt = _f64(prm["time_table"])
+    q, k, v = _f64(q, dtype), _f64(k, dtype), _f64(v, dtype)
+    wp = _f64(prm["pos_table"], dtype)
+    wt = _f64(prm["time_table"], dtype)
     if rows is None:
         rows = np.arange(T, dtype=I64)
     rows = np.asarray(rows, I64)
-    out = np.zeros((len(rows), H, dv))
+    out = np.zeros((len(rows), H, dv), dtype)
     rb, _ = token_index(off, T)
     row_seq = rb[rows]
     for b in range(B):
@@ -215,12 +218,13 @@ def attention(q, k, v, offsets, timestamps, num_candidates, prm, cfg, rows=None,
                 S = q[s0 + ii, h] @ k[s0:s0 + kend, h].T + wp[h][bp] + wt[h][bt]
                 if typed:
                     S = S + type_bias(wy[h], ty_all[s0 + ii][:, None], ty_all[s0 + jj][None, :])
-                A = np.where(M, silu(S), 0.0) / N
+                A = np.where(M, silu(S, dtype), dtype(0.0)) / dtype(N)
                 out[idx, h] = A @ v[s0:s0 + kend, h]
     return out.reshape(len(rows), H * dv)
 
 
-def layer_forward(x, offsets, timestamps, num_candidates, prm, cfg, rows=None, token_types=None):
+def layer_forward(x, offsets, timestamps, num_candidates, prm, cfg, rows=None, token_types=None,
+                  dtype=np.float64):
     """One HSTU layer.  Returns a dict of taps:
 
     u, v, q, k   projections for all rows;
@@ -228,26 +232,27 @@ def layer_forward(x, offsets, timestamps, num_candidates, prm, cfg, rows=None, t
     ln_av        LayerNorm(av) over the H*dv axis;
     z            ln_av * u;
     y            f2(z) (+ x when cfg.residual) for ``rows``.
+    ``dtype``: float64 for parity; float32 only times the same steps.
     """
-    x = _f64(x)
+    x = _f64(x, dtype)
     T = x.shape[0]
-    u, v, q, k = project(x, prm, cfg)
+    u, v, q, k = project(x, prm, cfg, dtype=dtype)
     sel = np.arange(T, dtype=I64) if rows is None else np.asarray(rows, I64)
     av = attention(q, k, v, offsets, timestamps, num_candidates, prm, cfg, rows=sel,
-                   token_types=token_types)
-    out = gate_and_project(av, u[sel], x[sel], prm, cfg)
+                   token_types=token_types, dtype=dtype)
+    out = gate_and_project(av, u[sel], x[sel], prm, cfg, dtype=dtype)
     return {"u": u, "v": v, "q": q, "k": k, "av": av, "ln_av": out["ln_av"], "z": out["z"],
             "y": out["y"], "rows": sel}
 
 
-def gate_and_project(av, u, x, prm, cfg):
+def gate_and_project(av, u, x, prm, cfg, dtype=np.float64):
     """Steps 4-5: Z = LayerNorm(AV) * U over the merged heads, Y = Z W2^T + b2
     (+ x when cfg.residual).  Rows of av, u and x correspond one to one."""
-    ln_av = layer_norm(_f64(av), prm["ln_av_g"], prm["ln_av_b"], cfg.ln_eps)
-    z = ln_av * _f64(u)
-    y = z @ _f64(prm["w2"]).T + _f64(prm["b2"])
+    ln_av = layer_norm(_f64(av, dtype), prm["ln_av_g"], prm["ln_av_b"], cfg.ln_eps, dtype)
+    z = ln_av * _f64(u, dtype)
+    y = z @ _f64(prm["w2"], dtype).T + _f64(prm["b2"], dtype)
     if cfg.residual:
-        y = y + _f64(x)
+        y = y + _f64(x, dtype)
     return {"ln_av": ln_av, "z": z, "y": y}
 
 
