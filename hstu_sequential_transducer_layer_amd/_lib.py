@@ -30,8 +30,9 @@ EXPORTS = [
     "hstu_attn_bwd_workspace_size", "hstu_attn_bwd",
     "hstu_sl_workspace_size", "hstu_sl_sample",
     "hstu_gather_rows", "hstu_debug_indices",
-    "hstu_status_str", "hstu_last_error",
+    "hstu_status_str", "hstu_last_error", "hstu_layer_fwd_noalloc",
 ]
+NOALLOC_SCRATCH_BYTES = 256 << 20
 
 
 class HstuDesc(ctypes.Structure):
@@ -96,6 +97,8 @@ def load() -> ctypes.CDLL:
     lib.hstu_attn_workspace_size.restype = sz
     lib.hstu_layer_fwd.argtypes = [P(HstuDesc), vp, vp, i32, i64, vp, vp, P(HstuWeights),
                                    P(HstuBiasTables), vp, vp, sz, vp]
+    lib.hstu_layer_fwd_noalloc.argtypes = [P(HstuDesc), vp, vp, i32, i64, vp, vp, P(HstuWeights),
+                                           P(HstuBiasTables), vp, vp]
     lib.hstu_proj_fwd.argtypes = [P(HstuDesc), vp, i64, P(HstuWeights), P(HstuActivations),
                                   vp, sz, vp]
     lib.hstu_attn_fwd.argtypes = [P(HstuDesc), vp, i32, i64, vp, vp, P(HstuBiasTables),
@@ -123,7 +126,8 @@ def load() -> ctypes.CDLL:
     lib.hstu_gather_rows.argtypes = [vp, i64, i64, vp, vp, i64, vp, vp]
     lib.hstu_debug_indices.argtypes = [P(HstuDesc), vp, i32, i64, vp, vp, vp, i64, vp, vp]
     for f in ("hstu_layer_fwd", "hstu_proj_fwd", "hstu_attn_fwd", "hstu_gate_fwd", "hstu_out_fwd",
-              "hstu_cand_fwd", "hstu_layer_fwd_train", "hstu_layer_bwd", "hstu_attn_bwd", "hstu_sl_sample", "hstu_gather_rows", "hstu_debug_indices"):
+              "hstu_cand_fwd", "hstu_layer_fwd_train", "hstu_layer_bwd", "hstu_attn_bwd", "hstu_sl_sample",
+              "hstu_gather_rows", "hstu_debug_indices", "hstu_layer_fwd_noalloc"):
         getattr(lib, f).restype = ctypes.c_int
     lib.hstu_status_str.argtypes = [ctypes.c_int]
     lib.hstu_status_str.restype = ctypes.c_char_p
@@ -213,6 +217,23 @@ def layer_fwd(desc: HstuDesc, x: torch.Tensor, seq_offsets: torch.Tensor,
                               _ptr(timestamps), _ptr(num_candidates), ctypes.byref(w),
                               ctypes.byref(t), _ptr(out), _ptr(workspace), workspace.numel(),
                               _stream()))
+    return out
+
+
+def layer_fwd_noalloc(desc: HstuDesc, x: torch.Tensor, seq_offsets: torch.Tensor,
+                      timestamps: torch.Tensor, num_candidates: Optional[torch.Tensor],
+                      prm: Dict[str, torch.Tensor], out: torch.Tensor,
+                      weights: Optional[HstuWeights] = None,
+                      tables: Optional[HstuBiasTables] = None) -> torch.Tensor:
+    """hstu_layer_fwd_noalloc on torch's current stream (the library's own
+    per-GPU scratch, no workspace); writes and returns `out` ([T, d])."""
+    lib = load()
+    T, B = x.shape[0], seq_offsets.shape[0] - 1
+    w = weights if weights is not None else make_weights(prm)
+    t = tables if tables is not None else make_tables(prm)
+    _check(lib.hstu_layer_fwd_noalloc(ctypes.byref(desc), _ptr(x), _ptr(seq_offsets), B, T,
+                                      _ptr(timestamps), _ptr(num_candidates), ctypes.byref(w),
+                                      ctypes.byref(t), _ptr(out), _stream()))
     return out
 
 

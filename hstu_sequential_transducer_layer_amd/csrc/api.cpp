@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 #include <utility>
 #include <vector>
@@ -345,20 +346,29 @@ hstu_status hstu_out_fwd(const hstu_desc* desc, const void* x, int64_t T, const 
   return ok();
 }
 
-hstu_status hstu_layer_fwd(const hstu_desc* desc, const void* x, const int64_t* off, int32_t B,
-                           int64_t T, const int64_t* ts, const int32_t* nc, const hstu_weights* w,
-                           const hstu_bias_tables* tables, void* out, void* ws, size_t ws_bytes,
-                           hstu_stream_t stream) {
+// Host-side checks of hstu_layer_fwd's arguments (no device access).
+static hstu_status check_layer_args(const hstu_desc* desc, const void* x, const int64_t* off, int32_t B, int64_t T,
+                                    const int64_t* ts, const int32_t* nc, const hstu_weights* w,
+                                    const hstu_bias_tables* tables, const void* out) {
   hstu_status st;
   if ((st = check_desc(desc)) != HSTU_OK) return st;
   if ((st = check_sizes(T, B)) != HSTU_OK) return st;
-  if (T == 0) return ok();
+  if (T == 0) return HSTU_OK;
   HSTU_REQ(x, 16, "x");
   HSTU_REQ(out, 16, "out");
   if ((st = check_meta(off, B, ts, nc)) != HSTU_OK) return st;
   if ((st = check_proj_weights(desc, w)) != HSTU_OK) return st;
   if ((st = check_out_weights(desc, w)) != HSTU_OK) return st;
-  if ((st = check_tables(desc, tables)) != HSTU_OK) return st;
+  return check_tables(desc, tables);
+}
+
+hstu_status hstu_layer_fwd(const hstu_desc* desc, const void* x, const int64_t* off, int32_t B,
+                           int64_t T, const int64_t* ts, const int32_t* nc, const hstu_weights* w,
+                           const hstu_bias_tables* tables, void* out, void* ws, size_t ws_bytes,
+                           hstu_stream_t stream) {
+  hstu_status st;
+  if ((st = check_layer_args(desc, x, off, B, T, ts, nc, w, tables, out)) != HSTU_OK) return st;
+  if (T == 0) return ok();
   const Layout L = layout(desc, T, B, T, false);
   if (!ws || ws_bytes < L.total || !aligned(ws, 256))
     return fail(HSTU_ERR_WORKSPACE, "workspace: need %zu bytes (256-aligned), got %zu", L.total, ws_bytes);
@@ -382,6 +392,49 @@ hstu_status hstu_layer_fwd(const hstu_desc* desc, const void* x, const int64_t* 
     return st;
   if ((st = device(hstu::launch_f2(*desc, x, T, *w, z, out, s), "f2 launch")) != HSTU_OK) return st;
   return ok();
+}
+
+// The no-allocation entry point's scratch: one array per GPU (each device
+// holds its own copy of a __device__ variable), looked up once per device.
+// In host code `scratch` names a host-side stand-in, never the device memory:
+// only the addresses from hipGetSymbolAddress are passed to kernels.
+static __device__ __align__(256) unsigned char scratch[HSTU_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+static hstu_status device_scratch(void** ptr) {
+  int dev = -1;
+  hstu_status st = device(hipGetDevice(&dev), "hipGetDevice");
+  if (st != HSTU_OK) return st;
+  if (dev < 0 || dev >= kMaxDevices) return fail(HSTU_ERR_UNSUPPORTED, "device %d >= %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if ((st = device(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)")) != HSTU_OK)
+      return st;
+    if (!p || !aligned(p, 256)) return fail(HSTU_ERR_DEVICE, "scratch array address %p not 256-aligned", p);
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return HSTU_OK;
+}
+
+hstu_status hstu_layer_fwd_noalloc(const hstu_desc* desc, const void* x, const int64_t* off, int32_t B,
+                                   int64_t T, const int64_t* ts, const int32_t* nc, const hstu_weights* w,
+                                   const hstu_bias_tables* tables, void* out, hstu_stream_t stream) {
+  hstu_status st;
+  if ((st = check_layer_args(desc, x, off, B, T, ts, nc, w, tables, out)) != HSTU_OK) return st;
+  if (desc->flags & HSTU_VALIDATE)
+    return fail(HSTU_ERR_INVALID_ARG, "HSTU_VALIDATE copies to the host and synchronises: not available here");
+  if (T == 0) return ok();
+  const size_t need = layout(desc, T, B, T, false).total;
+  if (need > HSTU_NOALLOC_SCRATCH_BYTES)
+    return fail(HSTU_ERR_WORKSPACE, "%lld tokens in %d sequences need %zu bytes of scratch; the limit is %zu",
+                (long long)T, B, need, (size_t)HSTU_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if ((st = device_scratch(&ws)) != HSTU_OK) return st;
+  return hstu_layer_fwd(desc, x, off, B, T, ts, nc, w, tables, out, ws, HSTU_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 size_t hstu_cand_workspace_size(const hstu_desc* desc, int64_t Tc, int64_t Th, int32_t B) {

@@ -176,6 +176,25 @@ hstu_status hstu_layer_fwd(const hstu_desc* desc, const void* x, const int64_t* 
                            const hstu_bias_tables* tables, void* out, void* workspace,
                            size_t workspace_bytes, hstu_stream_t stream);
 
+/* hstu_layer_fwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same kernels on the same arguments, with the workspace taken from a
+ * library-owned device array of HSTU_NOALLOC_SCRATCH_BYTES per GPU instead of
+ * a caller buffer.  The array is found once per device, on the first call with
+ * that device current, and is held until the process ends.  Calls with
+ * hstu_workspace_size(desc, T, B) above the limit return HSTU_ERR_WORKSPACE;
+ * HSTU_VALIDATE (which copies to the host and synchronises) is rejected with
+ * HSTU_ERR_INVALID_ARG.  Nothing is allocated.  All calls on one GPU share
+ * that GPU's array: calls whose work overlaps on one GPU (two streams, two
+ * threads) race and give wrong results; calls enqueued one after another on
+ * one stream are safe.  HSTU_REUSE_PLAN reuses the plan of the previous call
+ * on the same GPU.                                                          */
+#define HSTU_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+hstu_status hstu_layer_fwd_noalloc(const hstu_desc* desc, const void* x, const int64_t* seq_offsets,
+                                   int32_t batch, int64_t total_tokens, const int64_t* timestamps,
+                                   const int32_t* num_candidates, const hstu_weights* weights,
+                                   const hstu_bias_tables* tables, void* out, hstu_stream_t stream);
+
 /* Stage 1 ([SRM] first equation and the "Code" LayerNorm before f1): input
  * LayerNorm, f1, SiLU, split into acts->u, v, q, k.  Needs
  * hstu_proj_workspace_size() bytes of workspace (the normalised x).          */

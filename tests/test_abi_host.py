@@ -28,7 +28,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 21
+    assert len(names) == 22
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.EXPORTS)
@@ -289,3 +289,25 @@ def test_attn_bwd_entry_point_checks_arguments(lib):
     assert call(_desc(), acts=_lib.HstuActivations(FAKE, FAKE, None, FAKE, FAKE, FAKE)) == _lib.HSTU_ERR_INVALID_ARG
     assert call(_desc(), ws=None) == _lib.HSTU_ERR_WORKSPACE
     assert lib.hstu_attn_bwd_workspace_size(R(_desc()), 1000, 4) >= lib.hstu_attn_workspace_size(R(_desc()), 1000, 4)
+
+
+def _call_noalloc(lib, desc, T=1000, B=4, x=FAKE, off=FAKE, ts=FAKE, nc=None, out=FAKE):
+    w = _lib.HstuWeights(*([FAKE] * 8))
+    t = _lib.HstuBiasTables(FAKE, FAKE, 129, 64)
+    return lib.hstu_layer_fwd_noalloc(ctypes.byref(desc), x, off, B, T, ts, nc, ctypes.byref(w),
+                                      ctypes.byref(t), out, None)
+
+
+def test_noalloc_rejects_before_touching_a_device(lib):
+    """hstu_layer_fwd_noalloc: argument checks, HSTU_VALIDATE, and inputs whose
+    workspace exceeds the library's scratch array are refused on the host."""
+    d = _desc()
+    need = lib.hstu_workspace_size(ctypes.byref(d), 200000, 4)
+    assert need > _lib.NOALLOC_SCRATCH_BYTES
+    assert _call_noalloc(lib, d, T=200000) == _lib.HSTU_ERR_WORKSPACE
+    assert str(_lib.NOALLOC_SCRATCH_BYTES) in lib.hstu_last_error().decode()
+    assert _call_noalloc(lib, _desc(flags=_lib.HSTU_VALIDATE)) == _lib.HSTU_ERR_INVALID_ARG
+    assert _call_noalloc(lib, d, x=None) == _lib.HSTU_ERR_INVALID_ARG
+    assert _call_noalloc(lib, d, off=FAKE + 4) == _lib.HSTU_ERR_INVALID_ARG
+    assert _call_noalloc(lib, _desc(dqk=48)) == _lib.HSTU_ERR_UNSUPPORTED
+    assert _call_noalloc(lib, d, T=0) == _lib.HSTU_OK
