@@ -382,6 +382,75 @@ def sl_repack(torch, _lib, reps: int = 20):
     }
 
 
+def config_measure(torch, _lib, layer, synth, name: str, reps: int = 20):
+    """One workload's layer forward and its stages: tokens/s of the whole
+    layer (hstu_layer_fwd, every kernel of the step), the attention kernel
+    alone (plan built once and reused; events on its launch stream) against
+    the MFMA peak of the layer's dtype, and the LayerNorm/gate kernel against
+    the HBM peak.  For the 8-layer workload the layer is its first."""
+    w = synth.make_workload(name, n_layers=1)
+    dev = layer.to_device(w)
+    x, off, ts, nc = dev["x"], dev["offsets"], dev["timestamps"], dev["num_candidates"]
+    prm = dev["layers"][0]
+    desc = _lib.make_desc(w.dims)
+    reuse = _lib.make_desc(w.dims, _lib.HSTU_REUSE_PLAN)
+    T, B = w.T, w.B
+    stream = torch.cuda.current_stream()
+    ws = _lib.alloc_workspace(_lib.workspace_size(desc, T, B), x.device)
+    out = torch.empty_like(x)
+    wts, tab = _lib.make_weights(prm), _lib.make_tables(prm)
+
+    def timed(fn, n=reps):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(n):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    layer_ms = timed(lambda: _lib.layer_fwd(desc, x, off, ts, nc, prm, out=out, workspace=ws, weights=wts,
+                                            tables=tab))
+    acts = _lib.proj_fwd(desc, x, prm)
+    aws = _lib.alloc_workspace(_lib.attn_workspace_size(desc, T, B), x.device)
+    _lib.attn_fwd(desc, off, ts, nc, prm, acts, workspace=aws)
+    attn_ms = timed(lambda: _lib.attn_fwd(reuse, off, ts, nc, prm, acts, workspace=aws))
+    zbuf = torch.empty_like(acts["u"])
+    gate_ms = timed(lambda: _lib.gate_fwd(desc, prm, acts, z=zbuf))
+    proj_ms = timed(lambda: _lib.proj_fwd(desc, x, prm, acts))
+    out_ms = timed(lambda: _lib.out_fwd(desc, x, prm, acts, out=out, z=zbuf))
+    dm, H, dqk, dv = w.dims.d_model, w.dims.num_heads, w.dims.dqk, w.dims.dv
+    pairs = attended_pairs(w.lengths(), w.num_candidates)
+    attn_flop = 2.0 * (dqk + dv) * H * pairs
+    bf16 = w.dims.dtype == "bf16"
+    peak = PEAK_BF16_TFLOPS if bf16 else PEAK_FP32_MFMA_TFLOPS
+    e = 2 if bf16 else 4
+    gate_bytes = T * (3 * H * dv * e + 8 * H) + 2 * H * dv * e
+    attn_tflops = attn_flop / (attn_ms * 1e-3) / 1e12
+    return {
+        "workload": f"{name}: {synth.WORKLOADS[name].description}" + (" (layer 1 of 8)" if name == "stack8_long" else ""),
+        "tokens": T,
+        "sequences": B,
+        "seq_len": f"{int(w.lengths().min())}..{int(w.lengths().max())}",
+        "layer_ms": layer_ms,
+        "tokens_per_s": T / (layer_ms * 1e-3),
+        "stages_ms": {"proj": proj_ms, "attn": attn_ms, "out (gate + f2)": out_ms},
+        "attention": {"kernel": "attn_kernel", "bound": "mfma", "achieved": attn_tflops, "peak": peak,
+                      "unit": "TFLOP/s", "frac": attn_tflops / peak, "launch_ms": attn_ms,
+                      "flop_per_launch": attn_flop, "pairs_per_launch": pairs,
+                      "mfma_dtype": "bf16" if bf16 else "fp32"},
+        "gate": {"kernel": "gate_kernel", "bound": "hbm", "achieved": gate_bytes / (gate_ms * 1e-3) / 1e9,
+                 "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                 "frac": gate_bytes / (gate_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "launch_ms": gate_ms,
+                 "bytes_per_launch": gate_bytes},
+    }
+
+
+CONFIGS = ["small_fp32", "zipf_bf16", "ranking_cand", "sl_train", "len4k", "stack8_long"]
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -394,6 +463,9 @@ def main():
     ap.add_argument("--cand-only", action="store_true",
                     help="run only the cached-candidate measurement and print its JSON object")
     ap.add_argument("--cpu-budget", type=float, default=30.0)
+    ap.add_argument("--minimal", action="store_true",
+                    help="only the step and its attention / gate timings (for profiler runs)")
+    ap.add_argument("--no-configs", action="store_true", help="skip the per-workload measurements")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-MiB device buffer 4 times (a plain copy kernel of "
                          "known size, to scale profiler byte counters) and exit")
@@ -470,45 +542,47 @@ def main():
         e.record(stream)
         torch.cuda.synchronize()
         return s.elapsed_time(e) / reps
-    # The same launch with the token-type term: two types, the history
-    # interleaving content (0) and action (1) tokens, a random [H, 2, 2] table.
-    rng = np.random.default_rng(7)
-    types = np.concatenate([np.arange(L) % 2 for L in w.lengths()]).astype(np.uint8)
-    tdims = dataclasses.replace(w.dims, num_types=2)
-    tdesc = _lib.make_desc(tdims)
-    tdesc_reuse = _lib.make_desc(tdims, _lib.HSTU_REUSE_PLAN)
-    tprm = dict(dev["layers"][0])
-    tprm["type_table"] = torch.from_numpy(synth.round_bf16(
-        rng.normal(0.0, 0.02, (w.dims.num_heads, 2, 2)))).to(x.dtype).cuda()
-    ttypes = torch.from_numpy(types).cuda()
-    tws = _lib.alloc_workspace(_lib.attn_workspace_size(tdesc, T, B), x.device)
-    _lib.attn_fwd(tdesc, off, ts, nc, tprm, acts, workspace=tws, token_types=ttypes)  # plan with the key types
-    typed_ms = timed(lambda: _lib.attn_fwd(tdesc_reuse, off, ts, nc, tprm, acts, workspace=tws, token_types=ttypes),
-                     reps=args.attn_reps)
-    # The layer backward (forward recompute + all gradients) of layer 1.
-    gdy = torch.randn(x.shape, generator=torch.Generator(device="cuda").manual_seed(5), device="cuda").to(x.dtype)
-    gdx = torch.empty_like(x)
-    gws = _lib.alloc_workspace(_lib.bwd_workspace_size(desc, T, B), "cuda")
-    gout = {}
+    typed_ms = bwd_ms = train_fwd_ms = train_ms = None
+    if not args.minimal:
+        # The same launch with the token-type term: two types, the history
+        # interleaving content (0) and action (1) tokens, a random [H, 2, 2] table.
+        rng = np.random.default_rng(7)
+        types = np.concatenate([np.arange(L) % 2 for L in w.lengths()]).astype(np.uint8)
+        tdims = dataclasses.replace(w.dims, num_types=2)
+        tdesc = _lib.make_desc(tdims)
+        tdesc_reuse = _lib.make_desc(tdims, _lib.HSTU_REUSE_PLAN)
+        tprm = dict(dev["layers"][0])
+        tprm["type_table"] = torch.from_numpy(synth.round_bf16(
+            rng.normal(0.0, 0.02, (w.dims.num_heads, 2, 2)))).to(x.dtype).cuda()
+        ttypes = torch.from_numpy(types).cuda()
+        tws = _lib.alloc_workspace(_lib.attn_workspace_size(tdesc, T, B), x.device)
+        _lib.attn_fwd(tdesc, off, ts, nc, tprm, acts, workspace=tws, token_types=ttypes)  # plan with the key types
+        typed_ms = timed(lambda: _lib.attn_fwd(tdesc_reuse, off, ts, nc, tprm, acts, workspace=tws, token_types=ttypes),
+                         reps=args.attn_reps)
+        # The layer backward (forward recompute + all gradients) of layer 1.
+        gdy = torch.randn(x.shape, generator=torch.Generator(device="cuda").manual_seed(5), device="cuda").to(x.dtype)
+        gdx = torch.empty_like(x)
+        gws = _lib.alloc_workspace(_lib.bwd_workspace_size(desc, T, B), "cuda")
+        gout = {}
 
-    def bwd():
-        nonlocal gout
-        _, gout = _lib.layer_bwd(desc, x, off, ts, nc, dev["layers"][0], gdy, dx=gdx,
-                                 grads=gout or None, workspace=gws)
-    bwd_ms = timed(bwd, reps=5)
-    # A training step with saved activations: hstu_layer_fwd_train, then
-    # hstu_layer_bwd with HSTU_SAVED_FWD on the same workspace.
-    sdesc = _lib.make_desc(w.dims, _lib.HSTU_SAVED_FWD)
-    ty = torch.empty_like(x)
+        def bwd():
+            nonlocal gout
+            _, gout = _lib.layer_bwd(desc, x, off, ts, nc, dev["layers"][0], gdy, dx=gdx,
+                                     grads=gout or None, workspace=gws)
+        bwd_ms = timed(bwd, reps=5)
+        # A training step with saved activations: hstu_layer_fwd_train, then
+        # hstu_layer_bwd with HSTU_SAVED_FWD on the same workspace.
+        sdesc = _lib.make_desc(w.dims, _lib.HSTU_SAVED_FWD)
+        ty = torch.empty_like(x)
 
-    def train_step():
-        nonlocal gout
-        _lib.layer_fwd_train(desc, x, off, ts, nc, dev["layers"][0], workspace=gws, out=ty)
-        _, gout = _lib.layer_bwd(sdesc, x, off, ts, nc, dev["layers"][0], gdy, dx=gdx,
-                                 grads=gout or None, workspace=gws)
-    train_fwd_ms = timed(lambda: _lib.layer_fwd_train(desc, x, off, ts, nc, dev["layers"][0], workspace=gws,
-                                                      out=ty), reps=5)
-    train_ms = timed(train_step, reps=5)
+        def train_step():
+            nonlocal gout
+            _lib.layer_fwd_train(desc, x, off, ts, nc, dev["layers"][0], workspace=gws, out=ty)
+            _, gout = _lib.layer_bwd(sdesc, x, off, ts, nc, dev["layers"][0], gdy, dx=gdx,
+                                     grads=gout or None, workspace=gws)
+        train_fwd_ms = timed(lambda: _lib.layer_fwd_train(desc, x, off, ts, nc, dev["layers"][0], workspace=gws,
+                                                          out=ty), reps=5)
+        train_ms = timed(train_step, reps=5)
     proj_ms = timed(lambda: _lib.proj_fwd(desc, x, dev["layers"][0], acts))
     zbuf = torch.empty_like(acts["u"])
     gate_ms = timed(lambda: _lib.gate_fwd(desc, dev["layers"][0], acts, z=zbuf), reps=20)
@@ -579,31 +653,36 @@ def main():
             "f2_tflops_excl_gate": f2_flop / (max(out_ms - gate_ms, 1e-6) * 1e-3) / 1e12,
         },
         "layer_tokens_per_s": T * len(w.layers) / (ms_step * 1e-3),
-        "backward": {
-            "what": "hstu_layer_bwd of layer 1: forward recompute, then dx and every parameter gradient",
-            "ms": bwd_ms,
-            "tokens_per_s": T / (bwd_ms * 1e-3),
-            "ratio_to_forward_layer": bwd_ms / (ms_step / len(w.layers)),
-            "saved_activations": {
-                "what": "hstu_layer_fwd_train then hstu_layer_bwd with HSTU_SAVED_FWD (no recompute)",
-                "fwd_train_ms": train_fwd_ms,
-                "bwd_ms": train_ms - train_fwd_ms,
-                "step_ms": train_ms,
-                "step_tokens_per_s": T / (train_ms * 1e-3),
-            },
-        },
-        "type_bias": {
-            "what": "hstu_attn_fwd of layer 1 with a 2-type token-type term (interleaved content/action)",
-            "launch_ms": typed_ms,
-            "untyped_launch_ms": attn_ms,
-            "overhead": typed_ms / attn_ms - 1.0,
-            "tflops": attn_flop / (typed_ms * 1e-3) / 1e12,
-        },
     }
-    if not args.no_cand:
+    if not args.minimal:
+        rec.update({
+            "backward": {
+                "what": "hstu_layer_bwd of layer 1: forward recompute, then dx and every parameter gradient",
+                "ms": bwd_ms,
+                "tokens_per_s": T / (bwd_ms * 1e-3),
+                "ratio_to_forward_layer": bwd_ms / (ms_step / len(w.layers)),
+                "saved_activations": {
+                    "what": "hstu_layer_fwd_train then hstu_layer_bwd with HSTU_SAVED_FWD (no recompute)",
+                    "fwd_train_ms": train_fwd_ms,
+                    "bwd_ms": train_ms - train_fwd_ms,
+                    "step_ms": train_ms,
+                    "step_tokens_per_s": T / (train_ms * 1e-3),
+                },
+            },
+            "type_bias": {
+                "what": "hstu_attn_fwd of layer 1 with a 2-type token-type term (interleaved content/action)",
+                "launch_ms": typed_ms,
+                "untyped_launch_ms": attn_ms,
+                "overhead": typed_ms / attn_ms - 1.0,
+                "tflops": attn_flop / (typed_ms * 1e-3) / 1e12,
+            },
+        })
+    if not args.no_cand and not args.minimal:
         rec["cand_inference"] = cand_inference(torch, _lib, layer, synth)
         rec["stochastic_length"] = sl_repack(torch, _lib)
-    if not args.no_cpu:
+    if not args.no_configs and not args.minimal:
+        rec["configs"] = {n: config_measure(torch, _lib, layer, synth, n) for n in CONFIGS}
+    if not args.no_cpu and not args.minimal:
         rec["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
     print(json.dumps(rec), flush=True)
 
