@@ -29,7 +29,7 @@ EXPORTS = [
     "hstu_cand_workspace_size", "hstu_cand_fwd", "hstu_bwd_workspace_size", "hstu_layer_fwd_train", "hstu_layer_bwd",
     "hstu_attn_bwd_workspace_size", "hstu_attn_bwd",
     "hstu_sl_workspace_size", "hstu_sl_sample",
-    "hstu_gather_rows", "hstu_debug_indices",
+    "hstu_gather_rows", "hstu_debug_indices", "hstu_debug_attn_bias",
     "hstu_status_str", "hstu_last_error", "hstu_layer_fwd_noalloc",
 ]
 NOALLOC_SCRATCH_BYTES = 256 << 20
@@ -125,9 +125,11 @@ def load() -> ctypes.CDLL:
     lib.hstu_sl_sample.argtypes = [vp, i32, i64, i32, ctypes.c_float, vp, vp, vp, vp, vp, sz, vp]
     lib.hstu_gather_rows.argtypes = [vp, i64, i64, vp, vp, i64, vp, vp]
     lib.hstu_debug_indices.argtypes = [P(HstuDesc), vp, i32, i64, vp, vp, vp, i64, vp, vp]
+    lib.hstu_debug_attn_bias.argtypes = [P(HstuDesc), vp, i32, i64, vp, vp, P(HstuBiasTables), vp, i32, i32, vp,
+                                         vp, sz, vp]
     for f in ("hstu_layer_fwd", "hstu_proj_fwd", "hstu_attn_fwd", "hstu_gate_fwd", "hstu_out_fwd",
               "hstu_cand_fwd", "hstu_layer_fwd_train", "hstu_layer_bwd", "hstu_attn_bwd", "hstu_sl_sample",
-              "hstu_gather_rows", "hstu_debug_indices", "hstu_layer_fwd_noalloc"):
+              "hstu_gather_rows", "hstu_debug_indices", "hstu_debug_attn_bias", "hstu_layer_fwd_noalloc"):
         getattr(lib, f).restype = ctypes.c_int
     lib.hstu_status_str.argtypes = [ctypes.c_int]
     lib.hstu_status_str.restype = ctypes.c_char_p
@@ -180,6 +182,9 @@ def make_tables(prm: Dict[str, torch.Tensor], token_types: Optional[torch.Tensor
     has a "type_table" ([H, NT, NT], or [NT, NT] shared across heads)."""
     pos, tim = prm["pos_table"], prm["time_table"]
     typ = prm.get("type_table")
+    for name, t in (("pos_table", pos), ("time_table", tim), ("type_table", typ)):
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous (rows of the table one after another)")
     tstride = 0
     if typ is not None and typ.dim() == 3:
         tstride = typ.shape[1] * typ.shape[2]
@@ -458,4 +463,22 @@ def debug_indices(desc: HstuDesc, seq_offsets, timestamps, num_candidates, pairs
     out = torch.empty(n, 6, dtype=torch.int64, device=pairs.device)
     _check(lib.hstu_debug_indices(ctypes.byref(desc), _ptr(seq_offsets), B, T, _ptr(timestamps),
                                   _ptr(num_candidates), _ptr(pairs), n, _ptr(out), _stream()))
+    return out
+
+
+def debug_attn_bias(desc: HstuDesc, seq_offsets, timestamps, num_candidates, prm, slot: torch.Tensor,
+                    n_slots: int, max_len: int, fill: float = float("inf")):
+    """hstu_debug_attn_bias: the attention kernel's per-pair biases (times
+    -log2 e; NaN where masked) of the rows with slot[row] >= 0, as a float32
+    [H, n_slots, max_len] tensor first filled with `fill` (entries the kernel
+    does not visit keep it)."""
+    lib = load()
+    T, B = timestamps.shape[0], seq_offsets.shape[0] - 1
+    need = attn_workspace_size(desc, T, B)
+    ws = alloc_workspace(need, timestamps.device)
+    out = torch.full((desc.num_heads, n_slots, max_len), fill, dtype=torch.float32, device=timestamps.device)
+    t = make_tables(prm)
+    _check(lib.hstu_debug_attn_bias(ctypes.byref(desc), _ptr(seq_offsets), B, T, _ptr(timestamps),
+                                    _ptr(num_candidates), ctypes.byref(t), _ptr(slot), n_slots, max_len,
+                                    _ptr(out), _ptr(ws), ws.numel(), _stream()))
     return out

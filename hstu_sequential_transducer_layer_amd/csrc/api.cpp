@@ -833,4 +833,33 @@ hstu_status hstu_debug_indices(const hstu_desc* desc, const int64_t* off, int32_
   return ok();
 }
 
+hstu_status hstu_debug_attn_bias(const hstu_desc* desc, const int64_t* off, int32_t B, int64_t T,
+                                 const int64_t* ts, const int32_t* nc, const hstu_bias_tables* tables,
+                                 const int32_t* slot, int32_t n_slots, int32_t max_len, float* out, void* ws,
+                                 size_t ws_bytes, hstu_stream_t stream) {
+  hstu_status st;
+  if ((st = check_desc(desc)) != HSTU_OK) return st;
+  if ((st = check_sizes(T, B)) != HSTU_OK) return st;
+  if (desc->num_types > 0) return fail(HSTU_ERR_UNSUPPORTED, "bias inspection: token types not supported");
+  if (n_slots < 0 || max_len < 0)
+    return fail(HSTU_ERR_INVALID_ARG, "n_slots %d and max_len %d must be >= 0", n_slots, max_len);
+  if (T == 0 || n_slots == 0 || max_len == 0) return ok();
+  if ((st = check_meta(off, B, ts, nc)) != HSTU_OK) return st;
+  if ((st = check_tables(desc, tables)) != HSTU_OK) return st;
+  HSTU_REQ(slot, 4, "slot");
+  HSTU_REQ(out, 4, "out");
+  const size_t need = attn_ws(T, B);
+  if (!ws || ws_bytes < need || !aligned(ws, 256))
+    return fail(HSTU_ERR_WORKSPACE, "workspace: need %zu bytes (256-aligned), got %zu", need, ws_bytes);
+  hipStream_t s = (hipStream_t)stream;
+  if (desc->flags & HSTU_VALIDATE)
+    if ((st = validate_metadata(off, B, T, nc, s)) != HSTU_OK) return st;
+  const hstu::AttnScratch sc = hstu::attn_scratch(ws, T, B);
+  const hstu::AttnRows rows{off, nc, ts, T, off, ts, T, nullptr, B, false, {}};
+  if ((st = device(hstu::launch_attn_prep(rows, hstu::kAttnBM, sc, s), "attention prep launch")) != HSTU_OK)
+    return st;
+  return device(hstu::launch_attn_dump(*desc, rows, *tables, slot, n_slots, max_len, out, sc, s),
+                "bias inspection launch");
+}
+
 }  // extern "C"

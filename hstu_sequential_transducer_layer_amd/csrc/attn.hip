@@ -86,6 +86,9 @@ struct AttnArgs {
   const int32_t* counts;   // [0]: work items
   const int32_t* rel;      // per key row: offset from its key block's earliest timestamp
   const int64_t* tstat;    // per key block's first row: earliest, latest timestamp
+  float* dump;             // inspection: [H][dump_slots][dump_len] biases
+  const int32_t* dump_slot;  // inspection: per query row its slot, or -1
+  int dump_slots, dump_len;
   int64_t T, TK;           // query rows, key rows
   int H, P, NB, sbits, pos_stride, time_stride, norm_len, shared_pos;
 };
@@ -255,38 +258,72 @@ struct ElemCtx {
 //           in 32 bits (|dt| < 2^24 over the block) and position(j) = j.
 //   MODE 3: any block: the same from the 64-bit timestamps, with shared
 //           candidate positions and the candidate mask.
+// The bias (times -log2 e) of the pair (query iq, key jq + c) in weight mode
+// MODE, and whether the pair is attended; rel is the key's time offset from
+// its block's earliest timestamp (modes 1 and 2).
+template <int MODE>
+__device__ __forceinline__ float elem_bias(const ElemCtx& x, int c, int32_t rel, bool& att) {
+  att = true;
+  if (MODE == 0) return x.c_lo;
+  if (MODE == 1) return rel <= x.thr ? x.c_hi : x.c_lo;
+  if (MODE == 2) {
+    const int bt = time_bucket_small((int)((uint32_t)x.hi32 - (uint32_t)rel), x.NB, x.sbits);
+    const int d = min(max(x.pq0 - c, -x.R), x.R);  // p(i) - p(j), clamped
+    att = c <= x.iq0;                              // j <= i
+    return x.time_s[bt] + x.pos_s[x.R + d];
+  }
+  const int j = x.jq + c;
+  att = attends(x.iq, j, x.nh);
+  return x.time_s[time_bucket(wrap_sub(x.ts_q, x.ts[min(j, x.L - 1)]), x.NB, x.sbits)] +
+         x.pos_s[pos_bucket(x.p_q, position(j, x.nh, x.shared), x.R)];
+}
+
+// The time offsets of keys kb + 8 g + 0..3 (modes 1 and 2; zeros otherwise).
+template <int MODE>
+__device__ __forceinline__ void elem_rel4(const ElemCtx& x, int kb, int g, int32_t (&rel)[4]) {
+  if (MODE == 1 || MODE == 2) {
+    const int4 rv = *reinterpret_cast<const int4*>(x.rel_s + kb + 8 * g);
+    rel[0] = rv.x; rel[1] = rv.y; rel[2] = rv.z; rel[3] = rv.w;
+  } else {
+    rel[0] = rel[1] = rel[2] = rel[3] = 0;
+  }
+}
+
 template <int MODE>
 __device__ __forceinline__ void elems(const f32x16& s, float (&p)[16], int kb, const ElemCtx& x) {
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     int32_t rel[4];
-    if (MODE == 1 || MODE == 2) {
-      const int4 rv = *reinterpret_cast<const int4*>(x.rel_s + kb + 8 * g);
-      rel[0] = rv.x; rel[1] = rv.y; rel[2] = rv.z; rel[3] = rv.w;
-    }
+    elem_rel4<MODE>(x, kb, g, rel);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int r = 4 * g + e, c = kb + 8 * g + e;
-      float v;
-      if (MODE == 0) {
-        v = silu_neglog2e(s[r], x.c_lo);
-      } else if (MODE == 1) {
-        v = silu_neglog2e(s[r], rel[e] <= x.thr ? x.c_hi : x.c_lo);
-      } else if (MODE == 2) {
-        const int bt = time_bucket_small((int)((uint32_t)x.hi32 - (uint32_t)rel[e]), x.NB, x.sbits);
-        const int d = min(max(x.pq0 - c, -x.R), x.R);  // p(i) - p(j), clamped
-        v = silu_neglog2e(s[r], x.time_s[bt] + x.pos_s[x.R + d]);
-        v = c <= x.iq0 ? v : 0.f;                     // j <= i
-      } else {
-        const int j = x.jq + c;
-        const int bt = time_bucket(wrap_sub(x.ts_q, x.ts[min(j, x.L - 1)]), x.NB, x.sbits);
-        const float b = x.time_s[bt] + x.pos_s[pos_bucket(x.p_q, position(j, x.nh, x.shared), x.R)];
-        v = silu_neglog2e(s[r], b);
-        v = attends(x.iq, j, x.nh) ? v : 0.f;
-      }
-      p[r] = v;
+      bool att;
+      const float b = elem_bias<MODE>(x, c, rel[e], att);
+      const float v = silu_neglog2e(s[r], b);
+      p[r] = att ? v : 0.f;
     }
   }
+}
+
+// Inspection: the biases of this lane's row for both 32-key halves of the
+// block, written at dst[j] for keys j < L (NaN where the pair is masked).
+template <int MODE>
+__device__ __forceinline__ void dump_block(const ElemCtx& x, float* dst, int L) {
+#pragma unroll
+  for (int kb = 0; kb < 64; kb += 32)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      int32_t rel[4];
+      elem_rel4<MODE>(x, kb, g, rel);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int c = kb + 8 * g + e, j = x.jq + c;
+        bool att;
+        const float b = elem_bias<MODE>(x, c, rel[e], att);
+        if (j < L) dst[j] = att ? b : __builtin_nanf("");
+      }
+    }
 }
 
 // Facts about this lane's query row and its wave that the per-block
@@ -348,6 +385,7 @@ __device__ __forceinline__ int classify_block(int j0, int64_t tmin, int64_t tmax
     if (__all((hi < (1 << 24) && lo > -(1 << 24)) || !q.qvalid)) {
       const int bt_lo = time_bucket_small(lo, sq.NB, sq.sbits);
       const int bt_hi = time_bucket_small(hi, sq.NB, sq.sbits);
+      x.jq = jq;  // (read only by the inspection dump in these modes)
       if (__all(bt_hi == bt_lo || !q.qvalid)) {
         x.c_lo = sq.time_s[bt_lo] + sq.cpos_far;
         return 0;
@@ -473,7 +511,10 @@ constexpr int attn_min_blocks(int row_bytes) { return row_bytes <= 256 ? 3 : 2; 
 // one more k16 MFMA step per 32-key half: the keys' one-hot types times each
 // query row's table row (exact: one-hot entries, table values in the layer
 // dtype, fp32 accumulation).
-template <typename T, int DQK, int DV, bool CACHED, bool TYPED>
+// DUMP (inspection): the same block enumeration, classification and per-pair
+// bias selection, but no copies of K and V and no matrix products: each
+// selected query row writes the bias of every pair it visits (dump_block).
+template <typename T, int DQK, int DV, bool CACHED, bool TYPED, bool DUMP = false>
 __global__ __launch_bounds__(256, attn_min_blocks((DQK + DV) * (int)sizeof(T) + (TYPED ? 64 : 0))) void attn_kernel(
     AttnArgs a) {
   typedef AttnCfg<T, DQK, DV> C;
@@ -545,8 +586,10 @@ __global__ __launch_bounds__(256, attn_min_blocks((DQK + DV) * (int)sizeof(T) + 
             reinterpret_cast<uintptr_t>(a.tstat + 2 * (k0 + j0)));
     tb.x = t4[0];
     tb.y = t4[1];
-    kcopy.issue(kg + (int64_t)j0 * DQK, L - j0, Kb, w);
-    vcopy.issue(vg + (int64_t)j0 * DV, L - j0, Vb, w);
+    if (!DUMP) {
+      kcopy.issue(kg + (int64_t)j0 * DQK, L - j0, Kb, w);
+      vcopy.issue(vg + (int64_t)j0 * DV, L - j0, Vb, w);
+    }
     // the offsets and types arrays have kAttnBN rows of padding past the key
     // rows, so these never read outside them; entries of rows past the
     // sequence are never used
@@ -580,7 +623,7 @@ __global__ __launch_bounds__(256, attn_min_blocks((DQK + DV) * (int)sizeof(T) + 
   Frag qf[DQK / 16];
 #pragma unroll
   for (int c = 0; c < DQK / 16; ++c) {
-    if (qvalid) {
+    if (qvalid && !DUMP) {
       qf[c] = *reinterpret_cast<const Frag*>(qbase + 16 * c + 8 * half);
     } else {
       qf[c] = Frag{};
@@ -623,12 +666,31 @@ __global__ __launch_bounds__(256, attn_min_blocks((DQK + DV) * (int)sizeof(T) + 
   const QueryRow qr = CACHED ? QueryRow{nh - 1, nh - 1, nh - 1, p_q, pmin_q, qvalid, ts_q, rq, q_narrow}
                              : QueryRow{r0, rlast, iq, p_q, pmin_q, qvalid, ts_q, rq, q_narrow};
   const SeqCtx sq{L, nh, R, a.NB, a.sbits, shared, cpos_far, pos_s, time_s, a.kts + k0, t0};
+  float* dump_dst = nullptr;  // inspection: this row's bias row, keys [0, dump_len)
+  if (DUMP && qvalid) {
+    const int slot = a.dump_slot[s0 + iq];
+    if (slot >= 0 && slot < a.dump_slots)
+      dump_dst = a.dump + ((int64_t)h * a.dump_slots + slot) * a.dump_len;
+  }
   auto consume = [&](int blk, const T* Kb, const T* Vb, const int32_t* rb, const int32_t* yb, int64_t tmin,
                      int64_t tmax) __attribute__((always_inline)) {
     const int j0 = block_start(blk);
     if (!wave_rows || !block_active(j0, qr, sq)) return;
     ElemCtx x;
     const int mode = classify_block(j0, tmin, tmax, qr, sq, rb, x);
+    if constexpr (DUMP) {
+      if (dump_dst) {
+        if (mode == 0)
+          dump_block<0>(x, dump_dst, min(L, a.dump_len));
+        else if (mode == 1)
+          dump_block<1>(x, dump_dst, min(L, a.dump_len));
+        else if (mode == 2)
+          dump_block<2>(x, dump_dst, min(L, a.dump_len));
+        else
+          dump_block<3>(x, dump_dst, min(L, a.dump_len));
+      }
+      return;
+    }
     // Per 32-key half: S^T (K fragments straight from LDS), then this half's
     // V fragments are read while its weights are computed, then P.V.
 #pragma unroll
@@ -694,7 +756,7 @@ __global__ __launch_bounds__(256, attn_min_blocks((DQK + DV) * (int)sizeof(T) + 
     tmax0 = uniform64(tb0.y);
   }
 
-  if (r0 >= iend) return;
+  if (DUMP || r0 >= iend) return;
   if (CACHED && qvalid && chunk == 0) {
     // The candidate's own key: distance 0 (bucket R), time difference 0
     // (bucket 0).  q.k over this lane's half of dqk, then across the halves.
@@ -772,11 +834,10 @@ static hipError_t launch_dims_f32(const AttnArgs& a, bool cached, int dqk, int d
   return hipErrorInvalidValue;
 }
 
-static hipError_t launch_attn_impl(const hstu_desc& d, const AttnRows& r, const hstu_bias_tables& tab,
-                                   const void* q, const void* k, const void* v, const void* qk, const void* qv,
-                                   float* part, void* av, float* stats, const AttnScratch& sc, hipStream_t s) {
-  if (r.Tq == 0) return hipSuccess;
-  AttnArgs a;
+static AttnArgs attn_args(const hstu_desc& d, const AttnRows& r, const hstu_bias_tables& tab, const void* q,
+                          const void* k, const void* v, const void* qk, const void* qv, float* part, void* av,
+                          float* stats, const AttnScratch& sc) {
+  AttnArgs a{};
   a.part = part;
   a.nsplit = sc.nsplit;
   a.NT = r.types.nt;
@@ -813,6 +874,14 @@ static hipError_t launch_attn_impl(const hstu_desc& d, const AttnRows& r, const 
   a.time_stride = tab.time_head_stride;
   a.norm_len = d.norm_len;
   a.shared_pos = (d.flags & HSTU_CAND_SHARED_POS) ? 1 : 0;
+  return a;
+}
+
+static hipError_t launch_attn_impl(const hstu_desc& d, const AttnRows& r, const hstu_bias_tables& tab,
+                                   const void* q, const void* k, const void* v, const void* qk, const void* qv,
+                                   float* part, void* av, float* stats, const AttnScratch& sc, hipStream_t s) {
+  if (r.Tq == 0) return hipSuccess;
+  const AttnArgs a = attn_args(d, r, tab, q, k, v, qk, qv, part, av, stats, sc);
   const int64_t grid = attn_max_items(r.Tq, r.B, r.cached) * d.num_heads;
   if (d.dtype == HSTU_BF16) return launch_dims<bf16>(a, r.cached, d.dqk, d.dv, grid, s);
   return launch_dims_f32(a, r.cached, d.dqk, d.dv, grid, s);
@@ -823,6 +892,25 @@ hipError_t launch_attn(const hstu_desc& d, const AttnRows& r, const hstu_bias_ta
                        const AttnScratch& sc, hipStream_t s) {
   if (r.cached) return hipErrorInvalidValue;  // needs the partial buffer: launch_attn_cached
   return launch_attn_impl(d, r, tab, q, k, v, qk, qv, nullptr, av, stats, sc, s);
+}
+
+hipError_t launch_attn_dump(const hstu_desc& d, const AttnRows& r, const hstu_bias_tables& tab,
+                            const int32_t* slot, int nslots, int len, float* out, const AttnScratch& sc,
+                            hipStream_t s) {
+  if (r.cached || r.types.nt > 0) return hipErrorInvalidValue;
+  if (r.Tq == 0 || nslots == 0 || len == 0) return hipSuccess;
+  AttnArgs a = attn_args(d, r, tab, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, sc);
+  a.dump = out;
+  a.dump_slot = slot;
+  a.dump_slots = nslots;
+  a.dump_len = len;
+  const size_t shmem = (size_t)(a.P + a.NB) * sizeof(float);
+  const dim3 g((unsigned)(attn_max_items(r.Tq, r.B, false) * d.num_heads)), b(kAttnBM / 32 * kWave);
+  if (d.dtype == HSTU_BF16)
+    hipLaunchKernelGGL((attn_kernel<bf16, 32, 32, false, false, true>), g, b, shmem, s, a);
+  else
+    hipLaunchKernelGGL((attn_kernel<float, 32, 32, false, false, true>), g, b, shmem, s, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_attn_cached(const hstu_desc& d, const AttnRows& r, const hstu_bias_tables& tab,

@@ -154,6 +154,11 @@ hipError_t launch_attn(const hstu_desc& d, const AttnRows& rows, const hstu_bias
 hipError_t launch_attn_cached(const hstu_desc& d, const AttnRows& rows, const hstu_bias_tables& tab,
                               const void* q, const void* k, const void* v, const void* qk, const void* qv,
                               float* part, const AttnScratch& sc, hipStream_t s);
+// Inspection: the attention kernel's per-pair biases (times -log2 e) for the
+// query rows with slot[row] in [0, nslots): out[h][slot][j], j < len.
+hipError_t launch_attn_dump(const hstu_desc& d, const AttnRows& rows, const hstu_bias_tables& tab,
+                            const int32_t* slot, int nslots, int len, float* out, const AttnScratch& sc,
+                            hipStream_t s);
 
 // --- out.hip: z = LN_av(av) * u, then out = z W2^T + b2 (+ x).
 hipError_t launch_gate(const hstu_desc& d, int64_t T, const hstu_weights& w, const void* u,

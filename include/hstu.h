@@ -378,6 +378,28 @@ hstu_status hstu_debug_indices(const hstu_desc* desc, const int64_t* seq_offsets
                                const int32_t* num_candidates, const int64_t* pairs,
                                int64_t n_pairs, int64_t* out, hstu_stream_t stream);
 
+/* The attention kernel's own bias, for inspection ([SRM] second equation and
+ * the bullets under it: the relative-position and time-bucket bias added to
+ * q.k per head; [FRC] 7.1.4 Innovation 1).  Runs the
+ * forward attention kernel's block enumeration, its per-(wave, key block)
+ * weight-mode classification and its per-pair bias selection -- the code the
+ * forward runs -- without the matrix products, and for every query row r
+ * with 0 <= slot[r] < n_slots writes, for each key j < min(L_b, max_len) of
+ * r's sequence that the kernel visits:
+ *   out[(h * n_slots + slot[r]) * max_len + j]
+ *     = -log2(e) * (pos[h][bp(i, j)] + time[h][bt(i, j)])   (float32, as the
+ *       kernel holds it: each table entry widened to fp32 and scaled, then added)
+ * or NaN where the pair is masked.  Entries the kernel does not visit (key
+ * blocks it skips as wholly masked for a wave's rows) are left as they were.
+ *   slot [T] int32 (device), out [H * n_slots * max_len] float32 (device)
+ *   workspace >= hstu_attn_workspace_size(desc, T, B) bytes, 256-aligned
+ * Token types are not supported (num_types must be 0).                     */
+hstu_status hstu_debug_attn_bias(const hstu_desc* desc, const int64_t* seq_offsets, int32_t batch,
+                                 int64_t total_tokens, const int64_t* timestamps,
+                                 const int32_t* num_candidates, const hstu_bias_tables* tables,
+                                 const int32_t* slot, int32_t n_slots, int32_t max_len, float* out,
+                                 void* workspace, size_t workspace_bytes, hstu_stream_t stream);
+
 const char* hstu_status_str(hstu_status status);
 const char* hstu_last_error(void);
 

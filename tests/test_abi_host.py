@@ -28,7 +28,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 22
+    assert len(names) == 23
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.EXPORTS)
@@ -289,6 +289,21 @@ def test_attn_bwd_entry_point_checks_arguments(lib):
     assert call(_desc(), acts=_lib.HstuActivations(FAKE, FAKE, None, FAKE, FAKE, FAKE)) == _lib.HSTU_ERR_INVALID_ARG
     assert call(_desc(), ws=None) == _lib.HSTU_ERR_WORKSPACE
     assert lib.hstu_attn_bwd_workspace_size(R(_desc()), 1000, 4) >= lib.hstu_attn_workspace_size(R(_desc()), 1000, 4)
+
+
+def test_debug_attn_bias_checks_arguments(lib):
+    R = ctypes.byref
+    t = _lib.HstuBiasTables(FAKE, FAKE, 129, 64)
+    call = lambda d, n_slots=4, max_len=100, slot=FAKE, out=FAKE, ws=FAKE, T=1000: lib.hstu_debug_attn_bias(
+        R(d), FAKE, 4, T, FAKE, None, R(t), slot, n_slots, max_len, out, ws, 1 << 40, None)
+    assert call(_desc(num_types=2)) == _lib.HSTU_ERR_UNSUPPORTED
+    assert call(_desc(), n_slots=-1) == _lib.HSTU_ERR_INVALID_ARG
+    assert call(_desc(), max_len=-1) == _lib.HSTU_ERR_INVALID_ARG
+    assert call(_desc(), slot=None) == _lib.HSTU_ERR_INVALID_ARG
+    assert call(_desc(), out=FAKE + 2) == _lib.HSTU_ERR_INVALID_ARG
+    assert call(_desc(), ws=None) == _lib.HSTU_ERR_WORKSPACE
+    assert call(_desc(), n_slots=0, slot=None, out=None, ws=None) == _lib.HSTU_OK
+    assert call(_desc(), T=0) == _lib.HSTU_OK
 
 
 def _call_noalloc(lib, desc, T=1000, B=4, x=FAKE, off=FAKE, ts=FAKE, nc=None, out=FAKE):
