@@ -16,6 +16,7 @@
 //   ln_bwd_kernel         one wave per row: dx through LayerNorm_in (+ dY)
 #include "common.h"
 #include "gemm.h"
+#include "gemm2.h"
 #include "kernels.h"
 
 namespace hstu {
@@ -467,6 +468,49 @@ __global__ __launch_bounds__(256) void split_sum_kernel(const float* __restrict_
   dst[i] = v;
 }
 
+// The same product on the forward's 256 x 256 core (bf16, every K chunk a
+// multiple of 64): operands copied straight into LDS, fp32 results stored from
+// the accumulators (32 consecutive columns per row and store instruction).
+// Split s covers k in [s * kc, min((s + 1) * kc, K)) and writes C + s * M * N;
+// within a split the k16 steps run in ascending order, as in
+// gemm_nt_f32_kernel.
+__global__ __launch_bounds__(512, 2) void gemm_nt_f32_big_kernel(const bf16* __restrict__ A,
+                                                                 const bf16* __restrict__ Bm, float* __restrict__ C,
+                                                                 int64_t M, int N, int K, int kc) {
+  __shared__ __attribute__((aligned(16))) bf16 As0[G2::STAGE];
+  __shared__ __attribute__((aligned(16))) bf16 As1[G2::STAGE];
+  __shared__ __attribute__((aligned(16))) bf16 Bs0[G2::STAGE];
+  __shared__ __attribute__((aligned(16))) bf16 Bs1[G2::STAGE];
+  const int nrow = (int)((M + G2::BM - 1) / G2::BM), ncol = (N + G2::BN - 1) / G2::BN;
+  const int tiles = nrow * ncol, split = blockIdx.x / tiles;
+  int tr, tc;
+  map_tile(blockIdx.x - split * tiles, nrow, ncol, tr, tc);
+  const int64_t row0 = (int64_t)tr * G2::BM;
+  const int col0 = tc * G2::BN;
+  const int k0 = split * kc, kn = min(kc, K - k0);
+  C += (int64_t)split * M * N;
+  const int lane = threadIdx.x & 63, w = wave_id(), wm = w >> 1, wn = w & 1;
+  G2RowsA ap;
+  ap.c.init(A + k0, row0, M, K, w, lane);
+  ap.w = w;
+  G2Copy bc;
+  bc.init(Bm + k0, col0, N, K, w, lane);
+  f32x16 acc[2][4];
+  g2_mainloop<true>(ap, bc, kn, As0, As1, Bs0, Bs1, acc);
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    const int col = col0 + wn * 128 + nt * 32 + (lane & 31);
+    if (col >= N) continue;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = row0 + g2_row(wm, mt, lane, r);
+        if (row < M) C[row * N + col] = acc[mt][nt][r];
+      }
+  }
+}
+
 int gemm_splits(int64_t M, int N, int K) {
   const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
   int S = 1;
@@ -474,9 +518,35 @@ int gemm_splits(int64_t M, int N, int K) {
   return S;
 }
 
+// Splits for the 256 x 256 kernel: enough (sequence of k chunks, tile) work
+// items to give every compute unit one, chunks of at least 1024.
+static int gemm_splits_big(int64_t M, int N, int K) {
+  const int64_t tiles = ((M + G2::BM - 1) / G2::BM) * ((N + G2::BN - 1) / G2::BN);
+  int S = 1;
+  while (S < kGemmMaxSplit && tiles * S < 256 && (int64_t)K / (2 * S) >= 1024) S *= 2;
+  return S;
+}
+
 hipError_t launch_gemm_nt_f32(hstu_dtype dt, const void* A, const void* Bm, float* C, int64_t M, int N, int K,
                               float* split_buf, hipStream_t s) {
   if (M == 0 || N == 0) return hipSuccess;
+  if (dt == HSTU_BF16 && K % G2::BK == 0) {
+    const int64_t tiles = ((M + G2::BM - 1) / G2::BM) * ((N + G2::BN - 1) / G2::BN);
+    const int S = split_buf ? gemm_splits_big(M, N, K) : 1;
+    if (tiles * S >= 256) {
+      const int kc = (int)((((int64_t)K + S - 1) / S + G2::BK - 1) / G2::BK * G2::BK);
+      const int nsp = (int)((K + kc - 1) / kc);
+      float* out = nsp > 1 ? split_buf : C;
+      hipLaunchKernelGGL(gemm_nt_f32_big_kernel, dim3((unsigned)(tiles * nsp)), dim3(G2::NT), 0, s, (const bf16*)A,
+                         (const bf16*)Bm, out, M, N, K, kc);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess || nsp == 1) return e;
+      const int64_t n = M * (int64_t)N;
+      hipLaunchKernelGGL(split_sum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, (const float*)split_buf,
+                         n, nsp, C);
+      return hipGetLastError();
+    }
+  }
   const int64_t nr = (M + 127) / 128, nc = (N + 127) / 128;
   const int S = split_buf ? gemm_splits(M, N, K) : 1;
   const int bk = dt == HSTU_BF16 ? 64 : 32;
