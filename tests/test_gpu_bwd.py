@@ -211,6 +211,34 @@ def test_bwd_ranking_full_size():
         assert e <= tol, k
 
 
+def test_bwd_stack8_full_size():
+    """The 8-layer workload's first layer (bf16, B=8, L in [4096, 8192], d=1024,
+    8 x 128/128) at full size, where the fp32-output GEMMs and the
+    pre-activation GEMM run on the 256 x 256 kernels (dZ and dx~ over 43,864
+    rows; dW1 split over K): dx rows of the shortest sequence from the full
+    batch, and every gradient of that sequence run alone (dW1 again split over
+    K on the 256 x 256 kernel), against the oracle run on that sequence."""
+    w = synth.make_workload("stack8_long", n_layers=1)
+    s = int(np.argmin(w.lengths()))
+    rng = np.random.default_rng(12)
+    dy = rng.normal(0, 1, (w.T, w.dims.d_model))
+    got, dy_used = _gpu_bwd(w, dy)
+    sub = w.sub_batch([s])
+    rows = np.arange(w.offsets[s], w.offsets[s + 1])
+    say(f"backward, stack8_long layer 1 full batch (T={w.T}); oracle on sequence {s} ({len(rows)} rows)")
+    ref = G.layer_grads(sub.x, sub.offsets, sub.timestamps, sub.num_candidates, sub.layers[0], w.dims,
+                        dy_used[rows])
+    e = err_bf16(got["x"][rows], ref["x"])
+    say(f"  dx (full batch, sequence {s}): err {e:.3e} (tol 5e-02)")
+    assert e <= 5e-2
+    got1, _ = _gpu_bwd(sub, dy_used[rows])
+    for k, rk in NAMES.items():
+        tol = 1e-1 if k in ("pos", "time") else 5e-2
+        e = err_bf16(got1[k], ref[rk])
+        say(f"  d{k} (sequence {s} alone): err {e:.3e} (tol {tol:.0e})")
+        assert e <= tol, k
+
+
 @pytest.mark.parametrize("case", ["edge_fp32", "edge_bf16_64", "zipf_bf16", "sl_128_bf16"])
 def test_attention_stage_backward(case):
     """hstu_attn_bwd fed the GPU's own q, k, v and a bf16 dL/dAV, against the
