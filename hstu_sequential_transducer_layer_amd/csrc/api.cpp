@@ -532,8 +532,9 @@ static BwdLayout bwd_layout(const hstu_desc* d, int64_t T, int32_t B) {
   L.dz = take((size_t)T * K2 * 4);
   L.dact = take((size_t)T * N1 * 4);
   L.dav = take((size_t)T * K2 * e);
-  L.gterm_av = take((size_t)T * K2 * 4);
-  L.bterm_av = take((size_t)T * K2 * 4);
+  const int64_t rchunks = (T + 31) / 32;  // the LayerNorm backward kernels' 32-row partial sums
+  L.gterm_av = take((size_t)rchunks * K2 * 4);
+  L.bterm_av = take((size_t)rchunks * K2 * 4);
   L.tab_part = take((size_t)hstu::attn_max_tiles(T, B) * d->num_heads * (d->pos_buckets + d->time_buckets) * 4);
   L.dpre_t = take((size_t)T * N1 * e);
   L.w2t = take((size_t)K2 * dm * e);
@@ -543,7 +544,7 @@ static BwdLayout bwd_layout(const hstu_desc* d, int64_t T, int32_t B) {
   L.dpret = take((size_t)N1 * L.Tp * e);
   L.xnt = take((size_t)dm * L.Tp * e);
   L.dxn = take((size_t)T * dm * 4);
-  L.gterm_in = take((size_t)T * dm * 4);
+  L.gterm_in = take((size_t)2 * rchunks * dm * 4);
   const int64_t cmax = N1 > dm ? (N1 > K2 ? N1 : K2) : (dm > K2 ? dm : K2);
   L.ctmp = take(hstu::colsum_tmp_bytes(T, cmax));
   L.wsplit = take((size_t)hstu::kGemmMaxSplit * (size_t)(N1 > K2 ? N1 : K2) * dm * 4);
@@ -558,6 +559,8 @@ static hstu_status check_bwd_desc(const hstu_desc* d) {
   if (d->dqk != d->dv) return fail(HSTU_ERR_UNSUPPORTED, "the backward pass needs dqk == dv");
   if (d->pos_buckets + d->time_buckets > 2048)
     return fail(HSTU_ERR_UNSUPPORTED, "the backward pass needs pos_buckets + time_buckets <= 2048");
+  if (d->d_model > 2048 || d->num_heads * d->dv > 2048)
+    return fail(HSTU_ERR_UNSUPPORTED, "the backward pass needs d_model <= 2048 and num_heads * dv <= 2048");
   return HSTU_OK;
 }
 
@@ -682,11 +685,9 @@ hstu_status hstu_layer_bwd(const hstu_desc* desc, const void* x, const int64_t* 
   // gate and LayerNorm over the merged heads
   float* dact = F(L.dact);
   if ((st = device(hstu::launch_gate_bwd(*desc, T, *w, F(L.dz), a.u, a.av, a.av_stats, dact, base + L.dav,
-                                         F(L.gterm_av), F(L.bterm_av), s),
+                                         F(L.gterm_av), F(L.bterm_av), g->ln_av_g, g->ln_av_b, s),
                    "gate backward launch")) != HSTU_OK)
     return st;
-  if ((st = colsum(true, F(L.gterm_av), T, K2, g->ln_av_g)) != HSTU_OK) return st;
-  if ((st = colsum(true, F(L.bterm_av), T, K2, g->ln_av_b)) != HSTU_OK) return st;
   // attention: dV, dQ, dK into dact; the bias tables
   const hstu::AttnScratch sc = hstu::attn_scratch(base + L.f.attn, T, B);
   if ((st = device(hstu::launch_attn_bwd(*desc, off, nc, B, T, ts, *tables, a.q, a.k, a.v, base + L.dav, dact,
@@ -708,11 +709,12 @@ hstu_status hstu_layer_bwd(const hstu_desc* desc, const void* x, const int64_t* 
       HSTU_OK)
     return st;
   // input LayerNorm and the residual
-  if ((st = device(hstu::launch_ln_bwd(*desc, x, F(L.dxn), *w, dy, T, dx, F(L.gterm_in), s), "ln backward launch")) !=
-      HSTU_OK)
+  // the two sets of partial rows (ceil(T / 32) x d_model each) share one region
+  float* gp_in = F(L.gterm_in);
+  float* bp_in = gp_in + ((T + 31) / 32) * (int64_t)dm;
+  if ((st = device(hstu::launch_ln_bwd(*desc, x, F(L.dxn), *w, dy, T, dx, gp_in, bp_in, g->ln_in_g, g->ln_in_b, s),
+                   "ln backward launch")) != HSTU_OK)
     return st;
-  if ((st = colsum(true, F(L.gterm_in), norm ? T : 0, dm, g->ln_in_g)) != HSTU_OK) return st;
-  if ((st = colsum(true, F(L.dxn), norm ? T : 0, dm, g->ln_in_b)) != HSTU_OK) return st;
   return ok();
 }
 

@@ -190,69 +190,113 @@ __global__ __launch_bounds__(64 * kColGroups) void colsum_chunks_kernel(const fl
   dst[c] = sum;
 }
 
+// Rows of the LayerNorm backward kernels: eight consecutive rows per wave, 32
+// per workgroup.  The per-row terms of the LayerNorm parameters' gradients
+// are summed over a workgroup's rows in a fixed order (each wave over its
+// rows in order, then the four waves in order) into one partial row per
+// workgroup, which colsum_chunks_kernel then sums over the workgroups; so
+// the [T, columns] term arrays are never written.  Columns (H * dv, d_model):
+// a multiple of 8, at most kBwdRowCols.
+constexpr int kRowsPerWave = 8, kChunkRows = 4 * kRowsPerWave, kBwdRowCols = 2048;
+
+// The partial rows of the two terms accumulated by each wave (lane: columns
+// lane * 8 + 512 j .. + 7): written to LDS, then added in wave order.
+__device__ __forceinline__ void chunk_partials(const float (&ga)[kBwdRowCols / 512][8],
+                                               const float (&ba)[kBwdRowCols / 512][8], int K, float* red,
+                                               float* __restrict__ gpart, float* __restrict__ bpart) {
+  const int lane = threadIdx.x & 63, w = wave_id();
+#pragma unroll
+  for (int j = 0; j < kBwdRowCols / 512; ++j) {
+    const int c = lane * 8 + 512 * j;
+    if (c < K) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        red[w * K + c + e] = ga[j][e];
+        red[(4 + w) * K + c + e] = ba[j][e];
+      }
+    }
+  }
+  __syncthreads();
+  const int64_t o = (int64_t)blockIdx.x * K;
+  for (int c = threadIdx.x; c < K; c += 256) {
+    gpart[o + c] = ((red[c] + red[K + c]) + red[2 * K + c]) + red[3 * K + c];
+    bpart[o + c] = ((red[4 * K + c] + red[5 * K + c]) + red[6 * K + c]) + red[7 * K + c];
+  }
+}
+
 // One wave per row.  Recomputes the LayerNorm of AV from the attention's
 // per-head statistics (the forward gate's merge), then
 //   n^ = (AV - mean) * rstd,  dn = dZ * U,  dn^ = dn * g
 //   dU = dZ * (n^ g + b),  dAV = rstd (dn^ - mean(dn^) - n^ mean(dn^ n^))
-// and the per-row terms dn * n^ and dn of dg and db.
+// and the workgroup's partial sums of dn * n^ and dn (the terms of dg and db).
 template <typename T>
 __global__ __launch_bounds__(256) void gate_bwd_kernel(const float* __restrict__ dz, const T* __restrict__ u,
                                                        const T* __restrict__ av, const float* __restrict__ stats,
                                                        const T* __restrict__ g, const T* __restrict__ be,
                                                        int64_t M, int H, int dv, float eps, int64_t n1,
                                                        float* __restrict__ du, T* __restrict__ dav,
-                                                       float* __restrict__ gterm, float* __restrict__ bterm) {
-  // one wave per row; a lane takes 8 consecutive columns of one head per step
-  // (dv a multiple of 8)
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + wave_id();
-  if (row >= M) return;
+                                                       float* __restrict__ gpart, float* __restrict__ bpart) {
+  // a lane takes 8 consecutive columns of one head per step (dv a multiple of 8)
+  extern __shared__ float red[];  // [2][4 waves][K]
+  constexpr int NC = kBwdRowCols / 512;
+  const int lane = threadIdx.x & 63, w = wave_id();
   const int K = H * dv;
-  const float2 st = lane < H ? reinterpret_cast<const float2*>(stats)[row * H + lane] : make_float2(0.f, 0.f);
-  const float mean = wave_sum(st.x) / (float)H;
-  const float dm = st.x - mean;
-  const float m2 = wave_sum(lane < H ? st.y + (float)dv * dm * dm : 0.f);
-  const float rstd = rsqrtf(m2 / (float)K + eps);
-  const int64_t o = row * K;
-  float s1 = 0.f, s2 = 0.f;
-  float a8[8], z8[8], u8[8], g8[8];
-  for (int c = lane * 8; c < K; c += 8 * kWave) {
-    const float off = __shfl(dm, c / dv, kWave);
-    load8(av + o + c, a8);
-    load8(dz + o + c, z8);
-    load8(u + o + c, u8);
-    load8(g + c, g8);
+  float ga[NC][8], ba[NC][8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float nh = (a8[e] + off) * rstd;
-      const float dnh = z8[e] * u8[e] * g8[e];
-      s1 += dnh;
-      s2 += dnh * nh;
+  for (int j = 0; j < NC; ++j)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ga[j][e] = ba[j][e] = 0.f;
+  for (int i = 0; i < kRowsPerWave; ++i) {
+    const int64_t row = (int64_t)blockIdx.x * kChunkRows + w * kRowsPerWave + i;
+    if (row >= M) break;  // wave-uniform
+    const float2 st = lane < H ? reinterpret_cast<const float2*>(stats)[row * H + lane] : make_float2(0.f, 0.f);
+    const float mean = wave_sum(st.x) / (float)H;
+    const float dm = st.x - mean;
+    const float m2 = wave_sum(lane < H ? st.y + (float)dv * dm * dm : 0.f);
+    const float rstd = rsqrtf(m2 / (float)K + eps);
+    const int64_t o = row * K;
+    float s1 = 0.f, s2 = 0.f;
+    float a8[8], z8[8], u8[8], g8[8];
+    for (int c = lane * 8; c < K; c += 8 * kWave) {
+      const float off = __shfl(dm, c / dv, kWave);
+      load8(av + o + c, a8);
+      load8(dz + o + c, z8);
+      load8(u + o + c, u8);
+      load8(g + c, g8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float nh = (a8[e] + off) * rstd;
+        const float dnh = z8[e] * u8[e] * g8[e];
+        s1 += dnh;
+        s2 += dnh * nh;
+      }
+    }
+    const float m1 = wave_sum(s1) / (float)K, mm = wave_sum(s2) / (float)K;
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      const int c = lane * 8 + 512 * j;
+      if (c >= K) break;
+      const float off = __shfl(dm, c / dv, kWave);
+      float b8[8], o_du[8], o_dav[8];
+      load8(av + o + c, a8);
+      load8(dz + o + c, z8);
+      load8(u + o + c, u8);
+      load8(g + c, g8);
+      load8(be + c, b8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float nh = (a8[e] + off) * rstd;
+        const float dn = z8[e] * u8[e];
+        o_du[e] = z8[e] * (nh * g8[e] + b8[e]);
+        o_dav[e] = rstd * (dn * g8[e] - m1 - nh * mm);
+        ga[j][e] += dn * nh;
+        ba[j][e] += dn;
+      }
+      store8(du + row * n1 + c, o_du);
+      store8(dav + o + c, o_dav);
     }
   }
-  const float m1 = wave_sum(s1) / (float)K, mm = wave_sum(s2) / (float)K;
-  for (int c = lane * 8; c < K; c += 8 * kWave) {
-    const float off = __shfl(dm, c / dv, kWave);
-    float b8[8], o_du[8], o_dav[8], o_g[8], o_b[8];
-    load8(av + o + c, a8);
-    load8(dz + o + c, z8);
-    load8(u + o + c, u8);
-    load8(g + c, g8);
-    load8(be + c, b8);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float nh = (a8[e] + off) * rstd;
-      const float dn = z8[e] * u8[e];
-      o_du[e] = z8[e] * (nh * g8[e] + b8[e]);
-      o_dav[e] = rstd * (dn * g8[e] - m1 - nh * mm);
-      o_g[e] = dn * nh;
-      o_b[e] = dn;
-    }
-    store8(du + row * n1 + c, o_du);
-    store8(dav + o + c, o_dav);
-    store8(gterm + o + c, o_g);
-    store8(bterm + o + c, o_b);
-  }
+  chunk_partials(ga, ba, K, red, gpart, bpart);
 }
 
 // The pre-activation GEMM of f1 with the SiLU backward as its epilogue: the
@@ -447,78 +491,93 @@ __global__ __launch_bounds__(512, 2) void gemm_silu_bwd_big_kernel(const bf16* _
   }
 }
 
-// One wave per row.  With the input LayerNorm: x^ = (x - mean) rstd,
+// One wave per row (eight consecutive rows per wave, as above).  With the
+// input LayerNorm: x^ = (x - mean) rstd,
 // dx = rstd (dxn g - mean(dxn g) - x^ mean(dxn g x^)); else dx = dxn.  Plus dY
-// for the residual.  gterm = dxn * x^ (per-row term of the gain's gradient).
+// for the residual.  With the LayerNorm, the workgroup's partial sums of
+// dxn * x^ and dxn (the terms of its gain's and offset's gradients).
 template <typename T>
 __global__ __launch_bounds__(256) void ln_bwd_kernel(const T* __restrict__ x, const float* __restrict__ dxn,
                                                      const T* __restrict__ g, const T* __restrict__ dy, int64_t M,
                                                      int d, float eps, int norm, int residual, T* __restrict__ dx,
-                                                     float* __restrict__ gterm) {
-  // one wave per row; a lane takes 8 consecutive columns per step (16-byte
-  // accesses for bf16), d a multiple of 8
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + wave_id();
-  if (row >= M) return;
-  const int64_t o = row * d;
-  float mean = 0.f, rstd = 1.f, m1 = 0.f, mm = 0.f;
-  float xv[8], gv[8], dv8[8];
-  if (norm) {
-    float s = 0.f;
-    for (int c = lane * 8; c < d; c += 8 * kWave) {
-      load8(x + o + c, xv);
+                                                     float* __restrict__ gpart, float* __restrict__ bpart) {
+  // a lane takes 8 consecutive columns per step (16-byte accesses for bf16),
+  // d a multiple of 8
+  extern __shared__ float red[];  // [2][4 waves][d]
+  constexpr int NC = kBwdRowCols / 512;
+  const int lane = threadIdx.x & 63, w = wave_id();
+  float ga[NC][8], ba[NC][8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s += xv[e];
-    }
-    mean = wave_sum(s) / (float)d;
-    float v = 0.f;
-    for (int c = lane * 8; c < d; c += 8 * kWave) {
-      load8(x + o + c, xv);
+  for (int j = 0; j < NC; ++j)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float t = xv[e] - mean;
-        v += t * t;
-      }
-    }
-    rstd = rsqrtf(wave_sum(v) / (float)d + eps);
-    float s1 = 0.f, s2 = 0.f;
-    for (int c = lane * 8; c < d; c += 8 * kWave) {
-      load8(x + o + c, xv);
-      load8(g + c, gv);
-      load8(dxn + o + c, dv8);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float xh = (xv[e] - mean) * rstd;
-        const float t = dv8[e] * gv[e];
-        s1 += t;
-        s2 += t * xh;
-      }
-    }
-    m1 = wave_sum(s1) / (float)d;
-    mm = wave_sum(s2) / (float)d;
-  }
-  for (int c = lane * 8; c < d; c += 8 * kWave) {
-    float r[8], gt[8], yv[8];
-    load8(dxn + o + c, dv8);
+    for (int e = 0; e < 8; ++e) ga[j][e] = ba[j][e] = 0.f;
+  for (int i = 0; i < kRowsPerWave; ++i) {
+    const int64_t row = (int64_t)blockIdx.x * kChunkRows + w * kRowsPerWave + i;
+    if (row >= M) break;  // wave-uniform
+    const int64_t o = row * d;
+    float mean = 0.f, rstd = 1.f, m1 = 0.f, mm = 0.f;
+    float xv[8], gv[8], dv8[8];
     if (norm) {
-      load8(x + o + c, xv);
-      load8(g + c, gv);
-    }
-    if (residual) load8(dy + o + c, yv);
+      float sx = 0.f;
+      for (int c = lane * 8; c < d; c += 8 * kWave) {
+        load8(x + o + c, xv);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      if (norm) {
-        const float xh = (xv[e] - mean) * rstd;
-        r[e] = rstd * (dv8[e] * gv[e] - m1 - xh * mm);
-        gt[e] = dv8[e] * xh;
-      } else {
-        r[e] = dv8[e];
+        for (int e = 0; e < 8; ++e) sx += xv[e];
       }
-      if (residual) r[e] += yv[e];
+      mean = wave_sum(sx) / (float)d;
+      float v = 0.f;
+      for (int c = lane * 8; c < d; c += 8 * kWave) {
+        load8(x + o + c, xv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float t = xv[e] - mean;
+          v += t * t;
+        }
+      }
+      rstd = rsqrtf(wave_sum(v) / (float)d + eps);
+      float s1 = 0.f, s2 = 0.f;
+      for (int c = lane * 8; c < d; c += 8 * kWave) {
+        load8(x + o + c, xv);
+        load8(g + c, gv);
+        load8(dxn + o + c, dv8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float xh = (xv[e] - mean) * rstd;
+          const float t = dv8[e] * gv[e];
+          s1 += t;
+          s2 += t * xh;
+        }
+      }
+      m1 = wave_sum(s1) / (float)d;
+      mm = wave_sum(s2) / (float)d;
     }
-    if (norm) store8(gterm + o + c, gt);
-    store8(dx + o + c, r);
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      const int c = lane * 8 + 512 * j;
+      if (c >= d) break;
+      float r[8], yv[8];
+      load8(dxn + o + c, dv8);
+      if (norm) {
+        load8(x + o + c, xv);
+        load8(g + c, gv);
+      }
+      if (residual) load8(dy + o + c, yv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (norm) {
+          const float xh = (xv[e] - mean) * rstd;
+          r[e] = rstd * (dv8[e] * gv[e] - m1 - xh * mm);
+          ga[j][e] += dv8[e] * xh;
+          ba[j][e] += dv8[e];
+        } else {
+          r[e] = dv8[e];
+        }
+        if (residual) r[e] += yv[e];
+      }
+      store8(dx + o + c, r);
+    }
   }
+  chunk_partials(ga, ba, d, red, gpart, bpart);
 }
 
 template <typename T>
@@ -667,19 +726,27 @@ hipError_t launch_gemm_nt_f32(hstu_dtype dt, const void* A, const void* Bm, floa
 }
 
 hipError_t launch_gate_bwd(const hstu_desc& d, int64_t T, const hstu_weights& w, const float* dz, const void* u,
-                           const void* av, const float* stats, float* du, void* dav, float* gterm, float* bterm,
-                           hipStream_t s) {
-  if (T == 0) return hipSuccess;
+                           const void* av, const float* stats, float* du, void* dav, float* gpart, float* bpart,
+                           float* dg, float* db, hipStream_t s) {
+  const int K = d.num_heads * d.dv;
+  if (K % 8 != 0 || K > kBwdRowCols) return hipErrorInvalidValue;
   const int64_t n1 = 2 * (int64_t)d.num_heads * (d.dqk + d.dv);
-  const dim3 grid((unsigned)((T + 3) / 4)), block(256);
-  if (d.dtype == HSTU_BF16)
-    hipLaunchKernelGGL(gate_bwd_kernel<bf16>, grid, block, 0, s, dz, (const bf16*)u, (const bf16*)av, stats,
-                       (const bf16*)w.ln_av_g, (const bf16*)w.ln_av_b, T, d.num_heads, d.dv, d.ln_eps, n1, du,
-                       (bf16*)dav, gterm, bterm);
-  else
-    hipLaunchKernelGGL(gate_bwd_kernel<float>, grid, block, 0, s, dz, (const float*)u, (const float*)av, stats,
-                       (const float*)w.ln_av_g, (const float*)w.ln_av_b, T, d.num_heads, d.dv, d.ln_eps, n1, du,
-                       (float*)dav, gterm, bterm);
+  const int64_t chunks = (T + kChunkRows - 1) / kChunkRows;
+  if (chunks > 0) {
+    const dim3 grid((unsigned)chunks), block(256);
+    const size_t shmem = (size_t)8 * K * sizeof(float);
+    if (d.dtype == HSTU_BF16)
+      hipLaunchKernelGGL(gate_bwd_kernel<bf16>, grid, block, shmem, s, dz, (const bf16*)u, (const bf16*)av, stats,
+                         (const bf16*)w.ln_av_g, (const bf16*)w.ln_av_b, T, d.num_heads, d.dv, d.ln_eps, n1, du,
+                         (bf16*)dav, gpart, bpart);
+    else
+      hipLaunchKernelGGL(gate_bwd_kernel<float>, grid, block, shmem, s, dz, (const float*)u, (const float*)av, stats,
+                         (const float*)w.ln_av_g, (const float*)w.ln_av_b, T, d.num_heads, d.dv, d.ln_eps, n1, du,
+                         (float*)dav, gpart, bpart);
+  }
+  const dim3 cg((unsigned)((K + 63) / 64)), cb(64 * kColGroups);
+  hipLaunchKernelGGL(colsum_chunks_kernel, cg, cb, 0, s, (const float*)gpart, chunks, (int64_t)K, dg);
+  hipLaunchKernelGGL(colsum_chunks_kernel, cg, cb, 0, s, (const float*)bpart, chunks, (int64_t)K, db);
   return hipGetLastError();
 }
 
@@ -711,16 +778,25 @@ hipError_t launch_gemm_silu_bwd(hstu_dtype dt, const void* A, const void* w1, co
 }
 
 hipError_t launch_ln_bwd(const hstu_desc& d, const void* x, const float* dxn, const hstu_weights& w, const void* dy,
-                         int64_t T, void* dx, float* gterm, hipStream_t s) {
-  if (T == 0) return hipSuccess;
+                         int64_t T, void* dx, float* gpart, float* bpart, float* dg, float* db, hipStream_t s) {
+  const int dm = d.d_model;
+  if (dm % 8 != 0 || dm > kBwdRowCols) return hipErrorInvalidValue;
   const int norm = (d.flags & HSTU_INPUT_NORM) ? 1 : 0, res = (d.flags & HSTU_RESIDUAL) ? 1 : 0;
-  const dim3 grid((unsigned)((T + 3) / 4)), block(256);
-  if (d.dtype == HSTU_BF16)
-    hipLaunchKernelGGL(ln_bwd_kernel<bf16>, grid, block, 0, s, (const bf16*)x, dxn, (const bf16*)w.ln_in_g,
-                       (const bf16*)dy, T, d.d_model, d.ln_eps, norm, res, (bf16*)dx, gterm);
-  else
-    hipLaunchKernelGGL(ln_bwd_kernel<float>, grid, block, 0, s, (const float*)x, dxn, (const float*)w.ln_in_g,
-                       (const float*)dy, T, d.d_model, d.ln_eps, norm, res, (float*)dx, gterm);
+  const int64_t chunks = (T + kChunkRows - 1) / kChunkRows;
+  if (chunks > 0) {
+    const dim3 grid((unsigned)chunks), block(256);
+    const size_t shmem = (size_t)8 * dm * sizeof(float);
+    if (d.dtype == HSTU_BF16)
+      hipLaunchKernelGGL(ln_bwd_kernel<bf16>, grid, block, shmem, s, (const bf16*)x, dxn, (const bf16*)w.ln_in_g,
+                         (const bf16*)dy, T, dm, d.ln_eps, norm, res, (bf16*)dx, gpart, bpart);
+    else
+      hipLaunchKernelGGL(ln_bwd_kernel<float>, grid, block, shmem, s, (const float*)x, dxn, (const float*)w.ln_in_g,
+                         (const float*)dy, T, dm, d.ln_eps, norm, res, (float*)dx, gpart, bpart);
+  }
+  // without the input LayerNorm its parameters get zero gradients
+  const dim3 cg((unsigned)((dm + 63) / 64)), cb(64 * kColGroups);
+  hipLaunchKernelGGL(colsum_chunks_kernel, cg, cb, 0, s, (const float*)gpart, norm ? chunks : 0, (int64_t)dm, dg);
+  hipLaunchKernelGGL(colsum_chunks_kernel, cg, cb, 0, s, (const float*)bpart, norm ? chunks : 0, (int64_t)dm, db);
   return hipGetLastError();
 }
 

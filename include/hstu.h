@@ -299,8 +299,8 @@ typedef struct {
  * HSTU_SAVED_FWD: then the caller asserts that hstu_layer_fwd_train ran just
  * before with the same arguments and workspace (with other contents the
  * gradients are wrong but every access stays in bounds).  Supported: dqk = dv in {32, 64, 128} for bf16, {32, 64} for
- * fp32, num_types = 0, pos_buckets + time_buckets <= 2048; else
- * HSTU_ERR_UNSUPPORTED.  Results are reproducible bit for bit.  Weight gradients come from
+ * fp32, num_types = 0, pos_buckets + time_buckets <= 2048, d_model <= 2048
+ * and num_heads * dv <= 2048; else HSTU_ERR_UNSUPPORTED.  Results are reproducible bit for bit.  Weight gradients come from
  * GEMMs over the token dimension in the layer dtype with fp32 accumulation.
  *   workspace >= hstu_bwd_workspace_size(desc, T, B) bytes, 256-aligned     */
 size_t hstu_bwd_workspace_size(const hstu_desc* desc, int64_t total_tokens, int32_t batch);
