@@ -538,11 +538,14 @@ static BwdLayout bwd_layout(const hstu_desc* d, int64_t T, int32_t B) {
   L.tab_part = take((size_t)hstu::attn_max_tiles(T, B) * d->num_heads * (d->pos_buckets + d->time_buckets) * 4);
   L.dpre_t = take((size_t)T * N1 * e);
   L.w2t = take((size_t)K2 * dm * e);
-  L.dyt = take((size_t)dm * L.Tp * e);
-  L.zt = take((size_t)K2 * L.Tp * e);
+  // transposed copies for the weight gradients: fp32 layers only (bf16 layers
+  // read the token-major operands directly)
+  const bool tcopies = d->dtype != HSTU_BF16;
+  L.dyt = take(tcopies ? (size_t)dm * L.Tp * e : 0);
+  L.zt = take(tcopies ? (size_t)K2 * L.Tp * e : 0);
   L.w1t = take((size_t)dm * N1 * e);
-  L.dpret = take((size_t)N1 * L.Tp * e);
-  L.xnt = take((size_t)dm * L.Tp * e);
+  L.dpret = take(tcopies ? (size_t)N1 * L.Tp * e : 0);
+  L.xnt = take(tcopies ? (size_t)dm * L.Tp * e : 0);
   L.dxn = take((size_t)T * dm * 4);
   L.gterm_in = take((size_t)2 * rchunks * dm * 4);
   const int64_t cmax = N1 > dm ? (N1 > K2 ? N1 : K2) : (dm > K2 ? dm : K2);
@@ -676,11 +679,19 @@ hstu_status hstu_layer_bwd(const hstu_desc* desc, const void* x, const int64_t* 
   if ((st = device(hstu::launch_transpose(dt, w->w2, dm, K2, dm, base + L.w2t, s), "transpose")) != HSTU_OK) return st;
   if ((st = device(hstu::launch_gemm_nt_f32(dt, dy, base + L.w2t, F(L.dz), T, (int)K2, dm, nullptr, s), "gemm")) != HSTU_OK)
     return st;
-  if ((st = device(hstu::launch_transpose(dt, dy, T, dm, L.Tp, base + L.dyt, s), "transpose")) != HSTU_OK) return st;
-  if ((st = device(hstu::launch_transpose(dt, z, T, K2, L.Tp, base + L.zt, s), "transpose")) != HSTU_OK) return st;
-  if ((st = device(hstu::launch_gemm_nt_f32(dt, base + L.dyt, base + L.zt, g->w2, dm, (int)K2, (int)L.Tp, F(L.wsplit), s), "gemm")) !=
-      HSTU_OK)
-    return st;
+  const int64_t split_cap = (int64_t)hstu::kGemmMaxSplit * (N1 > K2 ? N1 : K2) * dm;  // L.wsplit, floats
+  if (dt == HSTU_BF16) {
+    if ((st = device(hstu::launch_gemm_tn_f32(dy, z, g->w2, dm, (int)K2, T, F(L.wsplit), split_cap, s), "gemm")) !=
+        HSTU_OK)
+      return st;
+  } else {
+    if ((st = device(hstu::launch_transpose(dt, dy, T, dm, L.Tp, base + L.dyt, s), "transpose")) != HSTU_OK) return st;
+    if ((st = device(hstu::launch_transpose(dt, z, T, K2, L.Tp, base + L.zt, s), "transpose")) != HSTU_OK) return st;
+    if ((st = device(hstu::launch_gemm_nt_f32(dt, base + L.dyt, base + L.zt, g->w2, dm, (int)K2, (int)L.Tp,
+                                              F(L.wsplit), s),
+                     "gemm")) != HSTU_OK)
+      return st;
+  }
   if ((st = colsum(false, dy, T, dm, g->b2)) != HSTU_OK) return st;
   // gate and LayerNorm over the merged heads
   float* dact = F(L.dact);
@@ -702,12 +713,20 @@ hstu_status hstu_layer_bwd(const hstu_desc* desc, const void* x, const int64_t* 
   if ((st = device(hstu::launch_gemm_nt_f32(dt, base + L.dpre_t, base + L.w1t, F(L.dxn), T, dm, (int)N1, nullptr, s), "gemm")) !=
       HSTU_OK)
     return st;
-  if ((st = device(hstu::launch_transpose(dt, base + L.dpre_t, T, N1, L.Tp, base + L.dpret, s), "transpose")) != HSTU_OK)
-    return st;
-  if ((st = device(hstu::launch_transpose(dt, xn, T, dm, L.Tp, base + L.xnt, s), "transpose")) != HSTU_OK) return st;
-  if ((st = device(hstu::launch_gemm_nt_f32(dt, base + L.dpret, base + L.xnt, g->w1, N1, dm, (int)L.Tp, F(L.wsplit), s), "gemm")) !=
-      HSTU_OK)
-    return st;
+  if (dt == HSTU_BF16) {
+    if ((st = device(hstu::launch_gemm_tn_f32(base + L.dpre_t, xn, g->w1, (int)N1, dm, T, F(L.wsplit), split_cap, s),
+                     "gemm")) != HSTU_OK)
+      return st;
+  } else {
+    if ((st = device(hstu::launch_transpose(dt, base + L.dpre_t, T, N1, L.Tp, base + L.dpret, s), "transpose")) !=
+        HSTU_OK)
+      return st;
+    if ((st = device(hstu::launch_transpose(dt, xn, T, dm, L.Tp, base + L.xnt, s), "transpose")) != HSTU_OK) return st;
+    if ((st = device(hstu::launch_gemm_nt_f32(dt, base + L.dpret, base + L.xnt, g->w1, N1, dm, (int)L.Tp,
+                                              F(L.wsplit), s),
+                     "gemm")) != HSTU_OK)
+      return st;
+  }
   // input LayerNorm and the residual
   // the two sets of partial rows (ceil(T / 32) x d_model each) share one region
   float* gp_in = F(L.gterm_in);

@@ -669,6 +669,174 @@ __global__ __launch_bounds__(512, 2) void gemm_nt_f32_big_kernel(const bf16* __r
   }
 }
 
+// Weight gradients C[M, N] = A^T B over the token dimension with both
+// operands read in their own row-major layout, A [K, M] and B [K, N] (K = the
+// token count): no transposed copies.  Tiles 256 x 256 x 64 on the forward's
+// wave layout.  A 64-row slice of each operand (64 tokens x 256 columns, 512
+// bytes per row) is copied straight into LDS with 16-byte chunk c of row r at
+// c ^ 4 (r & 3), and the MFMA fragments are read with transposing LDS reads
+// (ds_read_b64_tr_b16): lane l gets column 32 t + l % 32 at the eight k
+// values kb + 4 (l / 32) + {0..3} and kb + 8 + 4 (l / 32) + {0..3}, the same
+// k order for both operands, so every product pairs equal k.  Rows past K are
+// clamped on load and zeroed in LDS before use; columns past M (N) clamp to the
+// last full chunk and are never stored.  Split s covers rows
+// [s * kc, min((s + 1) * kc, K)) and writes C + s * M * N.
+typedef short tn_v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) tn_v4i16 tn_lds_v4i16;
+struct TnCopy {
+  static constexpr int PER = 4;  // 64 rows x 32 chunks / 512 threads
+  int r[PER], cofs[PER];         // tile row and element column of each load
+  __device__ __forceinline__ void init(int col0, int M, int w, int lane) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int slot = (w * PER + i) * 64 + lane;
+      r[i] = slot >> 5;
+      const int lc = (slot & 31) ^ (4 * (r[i] & 3));
+      cofs[i] = min(col0 + lc * 8, M - 8);
+    }
+  }
+  __device__ __forceinline__ void issue(const bf16* g, int64_t ld, int64_t k0, int64_t K, bf16* lds, int w) const {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int64_t t = min(k0 + r[i], K - 1);
+      __builtin_amdgcn_global_load_lds((g2_glb_void*)(g + t * ld + cofs[i]),
+                                       (g2_lds_void*)(lds + (w * PER + i) * 64 * 8), 16, 0, 0);
+    }
+  }
+};
+__device__ __forceinline__ bf16x8 tn_frag(const bf16* lds, int kb, int t, int lane) {
+  const int a = lane & 15;
+  const int row = kb + 4 * (lane >> 5) + (a >> 2);
+  const int col = 32 * t + 16 * ((lane >> 4) & 1) + 4 * (a & 3);
+  const int c = col >> 3, off = col & 7;
+  const tn_v4i16 x0 =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((tn_lds_v4i16*)(lds + row * 256 + ((c ^ (4 * (row & 3))) << 3) + off));
+  const tn_v4i16 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (tn_lds_v4i16*)(lds + (row + 8) * 256 + ((c ^ (4 * ((row + 8) & 3))) << 3) + off));
+  bf16x8 f;
+  const bf16* p0 = reinterpret_cast<const bf16*>(&x0);
+  const bf16* p1 = reinterpret_cast<const bf16*>(&x1);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f[e] = p0[e];
+    f[4 + e] = p1[e];
+  }
+  return f;
+}
+
+__global__ __launch_bounds__(512, 2) void gemm_tn_f32_kernel(const bf16* __restrict__ A, const bf16* __restrict__ B,
+                                                             float* __restrict__ C, int M, int N, int64_t K,
+                                                             int64_t kc) {
+  __shared__ __attribute__((aligned(16))) bf16 As0[64 * 256];
+  __shared__ __attribute__((aligned(16))) bf16 As1[64 * 256];
+  __shared__ __attribute__((aligned(16))) bf16 Bs0[64 * 256];
+  __shared__ __attribute__((aligned(16))) bf16 Bs1[64 * 256];
+  const int nrow = (M + 255) / 256, ncol = (N + 255) / 256;
+  const int tiles = nrow * ncol, split = blockIdx.x / tiles;
+  int tr, tc;
+  map_tile(blockIdx.x - split * tiles, nrow, ncol, tr, tc);
+  const int row0 = tr * 256, col0 = tc * 256;
+  const int64_t kbeg = split * kc, kend = min(kbeg + kc, K);
+  const int nk = (int)((kend - kbeg + 63) / 64);
+  C += (int64_t)split * M * N;
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), wm = w >> 1, wn = w & 1;
+  TnCopy ac, bc;
+  ac.init(row0, M, w, lane);
+  bc.init(col0, N, w, lane);
+  f32x16 acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+  // rows of the slice at k0 past kend read zero: clear them in this
+  // thread's A chunks (its own copies, landed), before the barrier
+  auto clear_tail = [&](int64_t k0, bf16* As) __attribute__((always_inline)) {
+    if (k0 + 64 <= kend) return;  // workgroup-uniform
+#pragma unroll
+    for (int i = 0; i < TnCopy::PER; ++i)
+      if (k0 + ac.r[i] >= kend)
+        *reinterpret_cast<uint4*>(As + ((w * TnCopy::PER + i) * 64 + lane) * 8) = make_uint4(0, 0, 0, 0);
+  };
+  auto mma = [&](const bf16* As, const bf16* Bs) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      bf16x8 af[2], bfr[4];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) af[mt] = tn_frag(As, 16 * kk, wm * 2 + mt, lane);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) bfr[nt] = tn_frag(Bs, 16 * kk, wn * 4 + nt, lane);
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = mma_k16(af[mt], bfr[nt], acc[mt][nt]);
+    }
+  };
+  // two slices per trip, each buffer a distinct LDS object; one barrier per slice
+  if (nk > 0) {
+    ac.issue(A, M, kbeg, K, As0, w);
+    bc.issue(B, N, kbeg, K, Bs0, w);
+  }
+  int ks = 0;
+  for (; ks + 2 <= nk; ks += 2) {
+    const int64_t k0 = kbeg + (int64_t)ks * 64;
+    __builtin_amdgcn_s_waitcnt(0);
+    clear_tail(k0, As0);
+    __syncthreads();
+    ac.issue(A, M, k0 + 64, K, As1, w);
+    bc.issue(B, N, k0 + 64, K, Bs1, w);
+    mma(As0, Bs0);
+    __builtin_amdgcn_s_waitcnt(0);
+    clear_tail(k0 + 64, As1);
+    __syncthreads();
+    if (ks + 2 < nk) {
+      ac.issue(A, M, k0 + 128, K, As0, w);
+      bc.issue(B, N, k0 + 128, K, Bs0, w);
+    }
+    mma(As1, Bs1);
+  }
+  if (ks < nk) {  // odd slice count: the last slice is in buffer 0
+    __builtin_amdgcn_s_waitcnt(0);
+    clear_tail(kbeg + (int64_t)ks * 64, As0);
+    __syncthreads();
+    mma(As0, Bs0);
+  }
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    const int col = col0 + wn * 128 + nt * 32 + (lane & 31);
+    if (col >= N) continue;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = row0 + g2_row(wm, mt, lane, r);
+        if (row < M) C[(int64_t)row * N + col] = acc[mt][nt][r];
+      }
+  }
+}
+
+hipError_t launch_gemm_tn_f32(const void* A, const void* B, float* C, int M, int N, int64_t K, float* split_buf,
+                              int64_t split_cap, hipStream_t s) {
+  if (M == 0 || N == 0) return hipSuccess;
+  if (M % 8 != 0 || N % 8 != 0 || M < 8 || N < 8) return hipErrorInvalidValue;
+  const int64_t tiles = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
+  // k splits: until the tiles give every compute unit one, chunks of at
+  // least 1024 rows, and the partial products fit split_cap floats
+  int S = 1;
+  while (split_buf && S < 16 && tiles * S < 256 && K / (2 * S) >= 1024 && (int64_t)2 * S * M * N <= split_cap)
+    S *= 2;
+  const int64_t kc = ((K + S - 1) / S + 63) / 64 * 64;
+  const int nsp = K > 0 ? (int)((K + kc - 1) / kc) : 1;
+  float* out = nsp > 1 ? split_buf : C;
+  hipLaunchKernelGGL(gemm_tn_f32_kernel, dim3((unsigned)(tiles * nsp)), dim3(512), 0, s, (const bf16*)A,
+                     (const bf16*)B, out, M, N, K, kc);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || nsp == 1) return e;
+  const int64_t n = (int64_t)M * N;
+  hipLaunchKernelGGL(split_sum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, (const float*)split_buf, n,
+                     nsp, C);
+  return hipGetLastError();
+}
+
 int gemm_splits(int64_t M, int N, int K) {
   const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
   int S = 1;

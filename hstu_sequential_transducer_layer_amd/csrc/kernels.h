@@ -184,6 +184,12 @@ hipError_t launch_attn_bwd(const hstu_desc& d, const int64_t* off, const int32_t
                            const int64_t* ts, const hstu_bias_tables& tab, const void* q, const void* k,
                            const void* v, const void* dout, float* dact, float* tab_part, float* gpos,
                            float* gtime, const AttnScratch& sc, hipStream_t s);
+// C [M, N] = A^T B (fp32) over K rows of the row-major bf16 A [K, M] and
+// B [K, N] (M, N multiples of 8): weight gradients over the token dimension
+// without transposed copies; split over K into split_buf (split_cap floats)
+// when the tiles alone would leave compute units idle.
+hipError_t launch_gemm_tn_f32(const void* A, const void* B, float* C, int M, int N, int64_t K, float* split_buf,
+                              int64_t split_cap, hipStream_t s);
 
 // --- bwd.hip
 size_t colsum_tmp_bytes(int64_t R, int64_t C);
