@@ -258,6 +258,11 @@ def test_bwd_entry_point_checks_arguments(lib):
     assert call(_desc(), ws=None) == _lib.HSTU_ERR_WORKSPACE
     assert lib.hstu_bwd_workspace_size(R(_desc()), 1000, 4) > lib.hstu_workspace_size(R(_desc()), 1000, 4)
     assert lib.hstu_bwd_workspace_size(R(_desc(dqk=64, dv=32)), 1000, 4) == 0
+    # the LayerNorm backward kernels' per-workgroup column sums cover 2048 columns
+    assert call(_desc(d_model=4096)) == _lib.HSTU_ERR_UNSUPPORTED
+    assert call(_desc(num_heads=32, dqk=128, dv=128)) == _lib.HSTU_ERR_UNSUPPORTED
+    assert lib.hstu_bwd_workspace_size(R(_desc(d_model=4096)), 1000, 4) == 0
+    assert lib.hstu_bwd_workspace_size(R(_desc(d_model=2048, num_heads=16)), 1000, 4) > 0
 
 
 def test_fwd_train_entry_point_checks_arguments(lib):
