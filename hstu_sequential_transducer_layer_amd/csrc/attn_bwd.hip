@@ -82,13 +82,33 @@ struct BTile {
   static __device__ __forceinline__ int at(int r, int e) { return r * D + (((e / V) ^ bwd_swz<CPR>(r)) * V) + e % V; }
 };
 
+// The merged dK/dV kernel's bf16 tiles (16 x 16 MFMA fragments) read them in
+// two other patterns: 16 consecutive rows at one logical chunk (row
+// fragments), and eight consecutive rows at two adjacent chunks per 32 lanes
+// (transposing reads).  With 64 four-byte banks both are free of conflicts
+// when, over any 16 rows, the rows that share a bank window get distinct
+// physical chunks and, over any aligned 8 rows, kv_swz(r) >> 1 takes distinct
+// values (checked exhaustively on the host).  Depends on r % 16 only.
+template <int CPR>
+__device__ __forceinline__ int kv_swz(int r) {
+  constexpr int SH = CPR >= 16 ? 0 : (CPR == 8 ? 1 : 2);
+  return (((r & 7) >> SH) << 1) | ((r >> 3) & 1);
+}
+
+template <int D>
+struct KvTile {
+  static constexpr int CPR = D / 8;
+  static_assert(CPR >= 4 && CPR <= 16, "tile width");
+  static __device__ __forceinline__ int at(int r, int e) { return r * D + (((e >> 3) ^ kv_swz<CPR>(r)) << 3) + (e & 7); }
+};
+
 // Asynchronous copy of 64 rows (row stride S elements in global memory) into a
 // swizzled tile by direct global->LDS loads: each of the four waves issues PER
 // 16-byte-per-lane loads; load i of wave w fills the 64 / CPR rows from
 // (4 i + w) * 64 / CPR, so a lane's rows lie STRIDE (a multiple of 16) rows
 // apart and share one swizzle.  Rows at or past `avail` (>= 1) repeat row
-// avail - 1.
-template <typename T, int D>
+// avail - 1.  KV selects kv_swz (KvTile) in place of bwd_swz (BTile).
+template <typename T, int D, bool KV = false>
 struct BwdCopy {
   static constexpr int V = Elem<T>::kVec, CPR = D / V, PER = CPR / 4, STRIDE = 256 / CPR;
   static_assert(PER == 1 || STRIDE % 16 == 0, "a lane's loads must share the swizzle");
@@ -97,7 +117,7 @@ struct BwdCopy {
   __device__ __forceinline__ void init(int w, int lane) {
     const int slot = w * 64 + lane;
     r0 = slot / CPR;
-    col = ((slot % CPR) ^ bwd_swz<CPR>(r0)) * V;
+    col = ((slot % CPR) ^ (KV ? kv_swz<CPR>(r0) : bwd_swz<CPR>(r0))) * V;
   }
   __device__ __forceinline__ void issue(const T* __restrict__ g, int64_t S, int avail, T* lds, int w) const {
 #pragma unroll
@@ -193,6 +213,54 @@ __device__ __forceinline__ typename Elem<T>::Frag bwd_col_frag(const T* lds, int
   return x;
 }
 
+// Runs use(c, read(c)) for c = 0 .. N - 1 with the reads issued DEPTH
+// steps ahead of their use, so that LDS latency overlaps the MFMAs.  The
+// scheduling barriers keep the compiler from sinking each read back to its
+// use, which it otherwise does to save registers.
+template <int N, int DEPTH, typename Read, typename Use>
+__device__ __forceinline__ void bwd_piped(Read read, Use use) {
+  decltype(read(0)) buf[DEPTH];
+#pragma unroll
+  for (int c = 0; c < DEPTH && c < N; ++c) buf[c] = read(c);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int c = 0; c < N; ++c) {
+    const auto x = buf[c % DEPTH];
+    use(c, x);
+    if (c + DEPTH < N) buf[c % DEPTH] = read(c + DEPTH);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// An operand fragment of one tile row at precomputed element offsets: one
+// 16-byte read for bf16, two for fp32 (offs[0], offs[1]).
+template <typename T>
+__device__ __forceinline__ typename Elem<T>::Frag bwd_frag_at(const T* base, const int* offs) {
+  typedef typename Elem<T>::Frag Frag;
+  if constexpr (Elem<T>::kVec == 8) {
+    return *reinterpret_cast<const Frag*>(base + offs[0]);
+  } else {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(base + offs[0]);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(base + offs[1]);
+    return Frag{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  }
+}
+
+// bwd_col_frag for bf16 at precomputed offsets of its two transposing reads.
+__device__ __forceinline__ bf16x8 bwd_tr_frag(const bf16* base, const int* offs) {
+  const bwd_v4i16 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((bwd_lds_v4i16*)(base + offs[0]));
+  const bwd_v4i16 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((bwd_lds_v4i16*)(base + offs[1]));
+  const bf16* p0 = reinterpret_cast<const bf16*>(&x0);
+  const bf16* p1 = reinterpret_cast<const bf16*>(&x1);
+  bf16x8 x;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    x[e] = p0[e];
+    x[4 + e] = p1[e];
+  }
+  return x;
+}
+
 template <typename T>
 __device__ __forceinline__ typename Elem<T>::Frag bwd_frag(const float* p) {
   typename Elem<T>::Frag f;
@@ -208,13 +276,11 @@ __device__ __forceinline__ float bwd_sigmoid(float s) {
 template <typename T, int DQK, int DV>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
   typedef typename Elem<T>::Frag Frag;
-  // two buffer sets (even / odd key blocks), each its own LDS objects
-  __shared__ __attribute__((aligned(16))) T Ks0[64 * DQK];
-  __shared__ __attribute__((aligned(16))) T Ks1[64 * DQK];
-  __shared__ __attribute__((aligned(16))) T Vs0[64 * DV];
-  __shared__ __attribute__((aligned(16))) T Vs1[64 * DV];
-  __shared__ __attribute__((aligned(16))) int64_t tsk0[64];
-  __shared__ __attribute__((aligned(16))) int64_t tsk1[64];
+  // two buffer sets (even / odd key blocks) of a K and a V tile, all in one
+  // array so that each LDS read is a per-lane offset plus a constant
+  constexpr int TK = 64 * DQK, SET = 64 * (DQK + DV);
+  __shared__ __attribute__((aligned(16))) T tiles[2 * SET];
+  __shared__ __attribute__((aligned(16))) int64_t tsks[2][64];
   // pos[P], time[NB], then one gradient histogram [P + NB] per wave (a
   // wave's updates land in program and lane order, so the sums are
   // reproducible; the four are added in wave order at the end)
@@ -295,14 +361,40 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
   BwdCopy<T, DV> vcopy;
   kcopy.init(w, lane);
   vcopy.init(w, lane);
+  // Per-lane LDS offsets of the fragment reads for the tile's rows 0..31
+  // (row l32) and, for bf16, of dQ's transposing reads at key rows 0..15:
+  // rows further by a multiple of 16 add a constant, the swizzle depending on
+  // the row modulo 16 only.
+  constexpr int RW = Elem<T>::kVec == 8 ? 1 : 2;
+  int rk[DQK / 16][RW], rv[DV / 16][RW], ck[DQK / 32][2];
+#pragma unroll
+  for (int c = 0; c < DQK / 16; ++c)
+#pragma unroll
+    for (int u = 0; u < RW; ++u) rk[c][u] = BTile<T, DQK>::at(l32, 16 * c + 8 * half + 4 * u);
+#pragma unroll
+  for (int c = 0; c < DV / 16; ++c)
+#pragma unroll
+    for (int u = 0; u < RW; ++u) rv[c][u] = BTile<T, DV>::at(l32, 16 * c + 8 * half + 4 * u);
+#pragma unroll
+  for (int n = 0; n < DQK / 32; ++n) {
+    const int a4 = lane & 15, row = 4 * half + (a4 >> 2), col = 32 * n + 16 * ((lane >> 4) & 1) + 4 * (a4 & 3);
+    ck[n][0] = BTile<T, DQK>::at(row, col);
+    ck[n][1] = BTile<T, DQK>::at(row + 8, col);
+  }
   // K, V rows and key timestamps of block blk into one buffer set
-  auto issue = [&](int blk, T* Ks, T* Vs, int64_t* tsk) __attribute__((always_inline)) {
+  auto issue = [&](int blk, int set) __attribute__((always_inline)) {
+    T* Ks = tiles + set * SET;
+    T* Vs = Ks + TK;
+    int64_t* tsk = tsks[set];
     const int j0 = block_start(blk);
     kcopy.issue(kg + (int64_t)j0 * DQK, DQK, L - j0, Ks, w);
     vcopy.issue(vg + (int64_t)j0 * DV, DV, L - j0, Vs, w);
     if (w == 0) bwd_copy_ts(a.ts + s0 + j0, L - j0, tsk, lane);
   };
-  auto consume = [&](int blk, const T* Ks, const T* Vs, const int64_t* tsk) __attribute__((always_inline)) {
+  auto consume = [&](int blk, int set) __attribute__((always_inline)) {
+    const T* Ks = tiles + set * SET;
+    const T* Vs = Ks + TK;
+    const int64_t* tsk = tsks[set];
     const int j0 = block_start(blk);
     if (r0 >= iend) return;
     // A far block: every key a history key strictly before the wave's first
@@ -374,10 +466,18 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
       f32x16 sc = f32x16{}, da = f32x16{};
-#pragma unroll
-      for (int c = 0; c < DQK / 16; ++c) sc = mma_k16(bwd_row_frag<T, DQK>(Ks, kh * 32 + l32, 16 * c + 8 * half), qf[c], sc);
-#pragma unroll
-      for (int c = 0; c < DV / 16; ++c) da = mma_k16(bwd_row_frag<T, DV>(Vs, kh * 32 + l32, 16 * c + 8 * half), df[c], da);
+      // S^T then dA^T: K rows, then V rows, read four steps ahead
+      constexpr int NK = DQK / 16, NV = DV / 16;
+      bwd_piped<NK + NV, 4>(
+          [&](int c) __attribute__((always_inline)) {
+            return c < NK ? bwd_frag_at<T>(Ks + kh * 32 * DQK, rk[c]) : bwd_frag_at<T>(Vs + kh * 32 * DV, rv[c - NK]);
+          },
+          [&](int c, const Frag& x) __attribute__((always_inline)) {
+            if (c < NK)
+              sc = mma_k16(x, qf[c], sc);
+            else
+              da = mma_k16(x, df[c - NK], da);
+          });
       float ds[16];
       if (mode == 0) {
         float sum = 0.f;
@@ -410,28 +510,35 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
       } else {
         pairs(std::false_type{}, kh, sc, da, ds);
       }
-#pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) {
-        const Frag pf = bwd_frag<T>(ds + 8 * c2);
-#pragma unroll
-        for (int n = 0; n < DQK / 32; ++n)
-          dq[n] = mma_k16(bwd_col_frag<T, DQK>(Ks, kh * 32 + 16 * c2, n, lane), pf, dq[n]);
-      }
+      // dQ^T += K^T dS^T over the two 16-key halves, K^T read two steps ahead
+      constexpr int NQ = DQK / 32;
+      const Frag pf0 = bwd_frag<T>(ds), pf1 = bwd_frag<T>(ds + 8);
+      bwd_piped<2 * NQ, 2>(
+          [&](int c) __attribute__((always_inline)) {
+            const int c2 = c / NQ, n = c % NQ;
+            if constexpr (Elem<T>::kVec == 8)
+              return bwd_tr_frag(Ks + (kh * 32 + 16 * c2) * DQK, ck[n]);
+            else
+              return bwd_col_frag<T, DQK>(Ks, kh * 32 + 16 * c2, n, lane);
+          },
+          [&](int c, const Frag& x) __attribute__((always_inline)) {
+            dq[c % NQ] = mma_k16(x, c < NQ ? pf0 : pf1, dq[c % NQ]);
+          });
     }
   };
-  if (nblk > 0) issue(0, Ks0, Vs0, tsk0);
+  if (nblk > 0) issue(0, 0);
   __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of block 0 have landed
   __syncthreads();                // ... and every wave's, plus the tables and histograms
   // Two blocks per trip so that each buffer set is named by a constant: the
   // copies of block b + 1 run while block b is consumed; one barrier per block.
   for (int blk = 0; blk < nblk; blk += 2) {
-    if (blk + 1 < nblk) issue(blk + 1, Ks1, Vs1, tsk1);
-    consume(blk, Ks0, Vs0, tsk0);
+    if (blk + 1 < nblk) issue(blk + 1, 1);
+    consume(blk, 0);
     if (blk + 1 >= nblk) break;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (blk + 2 < nblk) issue(blk + 2, Ks0, Vs0, tsk0);
-    consume(blk + 1, Ks1, Vs1, tsk1);
+    if (blk + 2 < nblk) issue(blk + 2, 0);
+    consume(blk + 1, 1);
     if (blk + 2 >= nblk) break;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -649,6 +756,279 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(BwdArgs a) {
   }
 }
 
+// One 16 x 16 x 32 bf16 MFMA step.  Lane l holds A row l % 16 and B column
+// l % 16 at k values 8 (l / 16) .. + 7, and C column l % 16 at rows
+// 4 (l / 16) .. + 3.
+__device__ __forceinline__ f32x4 mma16(const bf16x8& x, const bf16x8& y, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, y, c, 0, 0, 0);
+}
+
+// A operand of a 16 x 16 x 32 step from tile columns: A row m = feature
+// 16 ft + m (m = lane % 16); k value e = tile row kb + 4 (lane / 16) + e for
+// e < 4 and kb + 16 + 4 (lane / 16) + e - 4 above, the order in which a lane
+// holds the accumulator rows of two consecutive 16-row tiles.  Two
+// transposing 8-byte reads: within each 16-lane group, lane a addresses row
+// kb + 4 (lane / 16) + a / 4, columns 16 ft + 4 (a % 4) .. + 3, and receives
+// column 16 ft + a of the group's four rows (then the same 16 rows further).
+// kv_col_off is the lane's element offset for kb = 0; kb, a multiple of 16,
+// adds kb D (the swizzle depends on the row modulo 16), so one offset register
+// per ft serves every row block and, with the tiles in one array, every tile.
+template <int D>
+__device__ __forceinline__ int kv_col_off(int lane, int ft) {
+  const int a = lane & 15;
+  return KvTile<D>::at(4 * (lane >> 4) + (a >> 2), 16 * ft + 4 * (a & 3));
+}
+template <int D>
+__device__ __forceinline__ bf16x8 kv_col_frag(const bf16* p) {
+  const bwd_v4i16 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((bwd_lds_v4i16*)p);
+  const bwd_v4i16 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((bwd_lds_v4i16*)(p + 16 * D));
+  const bf16* p0 = reinterpret_cast<const bf16*>(&x0);
+  const bf16* p1 = reinterpret_cast<const bf16*>(&x1);
+  bf16x8 x;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    x[e] = p0[e];
+    x[4 + e] = p1[e];
+  }
+  return x;
+}
+
+// attn_bwd_kv16_kernel (bf16): dK and dV in one pass.  Work item (sequence,
+// 64-key half of a 128-key tile, head); each of the four waves owns 16 keys
+// and keeps both gradients in registers on 16 x 16 x 32 MFMA tiles (half the
+// accumulator registers per key of 32 x 32 tiles), so S = Q K^T, dA = dO V^T
+// and the weights are formed once per (key, query block) rather than once per
+// gradient.  Per query block of 64 rows: four 16-query tiles of S and dA (Q,
+// dO rows from LDS, K, V in registers), then dV^T += dO^T a and
+// dK^T += Q^T dS with a and dS fed from the accumulators as the B operand.
+template <int DQK, int DV>
+__global__ __launch_bounds__(256, 2) void attn_bwd_kv16_kernel(BwdArgs a) {
+  typedef bf16 T;
+  // two buffer sets (even / odd query blocks) of a Q and a dO tile, all in
+  // one array so that each LDS read is a per-lane offset plus a constant
+  constexpr int TQ = 64 * DQK, SET = 64 * (DQK + DV);
+  __shared__ __attribute__((aligned(16))) T tiles[2 * SET];
+  __shared__ __attribute__((aligned(16))) int64_t tsqs[2][64];
+  extern __shared__ float tabs[];  // pos[P], time[NB]
+  const int H = a.H, h = blockIdx.x % H, unit = blockIdx.x / H, item = unit >> 1;
+  if (item >= a.counts[0]) return;
+  const int2 tl = a.tiles[item];
+  const SeqInfo si = seq_info(a.off, a.ncand, tl.x, a.T);
+  const int L = si.len, nh = si.nhist;
+  const int j0t = tl.y * 128 + 64 * (unit & 1);
+  if (j0t >= L) return;  // the tile's second half lies past the sequence
+  const int P = a.P, NB = a.NB;
+  float* pos_s = tabs;
+  float* time_s = tabs + P;
+  const int tid = threadIdx.x;
+  // the tables times -log2(e): the weight step works on x = -log2(e) S
+  for (int i = tid; i < P; i += 256)
+    pos_s[i] = kNegLog2e * to_f32(reinterpret_cast<const T*>(a.pos_tab)[(int64_t)h * a.pos_stride + i]);
+  for (int i = tid; i < NB; i += 256)
+    time_s[i] = kNegLog2e * to_f32(reinterpret_cast<const T*>(a.time_tab)[(int64_t)h * a.time_stride + i]);
+  const int64_t s0 = si.start;
+  const int jend = min(j0t + 64, L);
+  const int lane = tid & 63, w = wave_id(), g = lane >> 4, l16 = lane & 15;
+  const int kr0 = j0t + 16 * w, jk = kr0 + l16;
+  const bool kvalid = jk < jend;
+  const float inv_n = 1.0f / (float)(a.norm_len > 0 ? a.norm_len : L);
+  const int R = (P - 1) / 2;
+  const bool shared = a.shared_pos != 0;
+  const int K2 = H * DV;
+
+  bf16x8 kf[DQK / 32], vf[DV / 32];
+  const T* krow = reinterpret_cast<const T*>(a.k) + ((int64_t)h * a.T + s0 + jk) * DQK;
+  const T* vrow = reinterpret_cast<const T*>(a.v) + ((int64_t)h * a.T + s0 + jk) * DV;
+#pragma unroll
+  for (int c = 0; c < DQK / 32; ++c) {
+    kf[c] = bf16x8{};
+    if (kvalid) kf[c] = bwd_global_frag<T>(krow + 32 * c + 8 * g);
+  }
+#pragma unroll
+  for (int c = 0; c < DV / 32; ++c) {
+    vf[c] = bf16x8{};
+    if (kvalid) vf[c] = bwd_global_frag<T>(vrow + 32 * c + 8 * g);
+  }
+  const int p_k = position(jk, nh, shared);
+  const int64_t ts_k = kvalid ? a.ts[s0 + jk] : 0;
+  f32x4 dk[DQK / 16], dv[DV / 16];
+#pragma unroll
+  for (int n = 0; n < DQK / 16; ++n) dk[n] = f32x4{};
+#pragma unroll
+  for (int n = 0; n < DV / 16; ++n) dv[n] = f32x4{};
+
+  // query blocks: history keys are seen by every later row (candidates
+  // included); candidate keys only by their own row
+  const int qend = j0t < nh ? L : jend;
+  const T* qg = reinterpret_cast<const T*>(a.q) + ((int64_t)h * a.T + s0) * DQK;
+  const T* og = reinterpret_cast<const T*>(a.dout) + s0 * (int64_t)K2 + h * DV;
+  const int nblk = (qend - j0t + 63) / 64;
+  BwdCopy<T, DQK, true> qcopy;
+  BwdCopy<T, DV, true> ocopy;
+  qcopy.init(w, lane);
+  ocopy.init(w, lane);
+  int roq[DQK / 32], rov[DV / 32], coq[DQK / 16], cov[DV / 16];  // per-lane LDS offsets
+#pragma unroll
+  for (int c = 0; c < DQK / 32; ++c) roq[c] = KvTile<DQK>::at(l16, 32 * c + 8 * g);
+#pragma unroll
+  for (int c = 0; c < DV / 32; ++c) rov[c] = KvTile<DV>::at(l16, 32 * c + 8 * g);
+#pragma unroll
+  for (int ft = 0; ft < DQK / 16; ++ft) coq[ft] = kv_col_off<DQK>(lane, ft);
+#pragma unroll
+  for (int ft = 0; ft < DV / 16; ++ft) cov[ft] = kv_col_off<DV>(lane, ft);
+  auto issue = [&](int blk, int set) __attribute__((always_inline)) {
+    T* Qs = tiles + set * SET;
+    T* Os = Qs + TQ;
+    int64_t* tsq = tsqs[set];
+    const int i0 = j0t + 64 * blk;
+    qcopy.issue(qg + (int64_t)i0 * DQK, DQK, L - i0, Qs, w);
+    ocopy.issue(og + (int64_t)i0 * K2, K2, L - i0, Os, w);
+    if (w == 0) bwd_copy_ts(a.ts + s0 + i0, L - i0, tsq, lane);
+  };
+  auto consume = [&](int blk, int set) __attribute__((always_inline)) {
+    const T* Qs = tiles + set * SET;
+    const T* Os = Qs + TQ;
+    const int64_t* tsq = tsqs[set];
+    const int i0 = j0t + 64 * blk;
+    if (kr0 >= jend) return;
+    // Weight modes per (wave, query block) as in attn_bwd_dkv_kernel, over
+    // the wave's 16 keys.
+    const int k_last = min(kr0 + 15, jend - 1);
+    const bool far = i0 + 63 < L && k_last < nh && i0 > k_last && position(i0, nh, shared) - k_last >= R;
+    int mode = 2;
+    float b_lo = 0.f, b_hi = 0.f;
+    int64_t tcut = 0, qmin, qmax, dlo, dhi;
+    bwd_block_minmax(a.tstat, s0 + i0, qmin, qmax);
+    const bool ok = !__builtin_sub_overflow(qmin, ts_k, &dlo) && !__builtin_sub_overflow(qmax, ts_k, &dhi);
+    const bool small = __builtin_amdgcn_readfirstlane(
+                           __all((ok && dlo > -(1 << 24) && dhi < (1 << 24)) || !kvalid) ? 1 : 0) != 0;
+    if (far) {
+      const int lo = time_bucket(dlo, NB, a.sbits);
+      const int hi = time_bucket(dhi, NB, a.sbits);
+      b_lo = pos_s[2 * R] + time_s[lo];
+      if (__all((ok && lo == hi) || !kvalid)) {
+        mode = 0;
+      } else if (__all((ok && hi <= lo + 1) || !kvalid)) {
+        mode = 1;
+        b_hi = pos_s[2 * R] + time_s[hi];
+        tcut = ts_k + bucket_floor(max(hi, 1), a.sbits);  // <= qmax: no overflow
+      }
+      mode = __builtin_amdgcn_readfirstlane(mode);
+    }
+    // S and dA over the block's four 16-query tiles; element e = 4 qt + r of
+    // a lane is query i0 + 16 qt + 4 g + r, key jk
+    f32x4 sc[4], da[4];
+#pragma unroll
+    for (int qt = 0; qt < 4; ++qt) sc[qt] = da[qt] = f32x4{};
+    // step t: S (t < 4 NK) or dA, query tile t % 4, k chunk (t / 4) % NK;
+    // consecutive steps use different accumulators
+    constexpr int NK = DQK / 32, NV = DV / 32;
+    bwd_piped<4 * (NK + NV), 4>(
+        [&](int t) __attribute__((always_inline)) {
+          const int qt = t % 4, c = (t / 4) % (t < 4 * NK ? NK : NV);
+          return t < 4 * NK ? *reinterpret_cast<const bf16x8*>(Qs + 16 * qt * DQK + roq[c])
+                            : *reinterpret_cast<const bf16x8*>(Os + 16 * qt * DV + rov[c]);
+        },
+        [&](int t, const bf16x8& x) __attribute__((always_inline)) {
+          const int qt = t % 4;
+          if (t < 4 * NK)
+            sc[qt] = mma16(x, kf[(t / 4) % NK], sc[qt]);
+          else
+            da[qt] = mma16(x, vf[(t / 4 - NK) % NV], da[qt]);
+        });
+    // Weight step on x = -log2(e) S_ij (a masked pair gets x = 1e30):
+    //   sg = sigmoid(S) = 1 / (1 + 2^x),  t = x sg = -log2(e) SiLU(S),
+    //   SiLU'(S) = sg + SiLU(S) (1 - sg) = t u + sg with u = ln2 (sg - 1).
+    // The B operands hold t and dA SiLU'(S); the constant factors -ln2 / N_b
+    // and 1 / N_b are applied to the accumulators once, at the end.  A masked
+    // pair gives 2^x = inf, sg = 0, t = 0 and SiLU' = 0.  Keys past the tile
+    // need no mask: their K and V rows are zero and their accumulator columns
+    // are never stored.
+    float pa[16], pd[16];
+    auto put = [&](int e, float x) __attribute__((always_inline)) {
+      const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x));
+      const float t = x * sg;
+      pa[e] = t;
+      pd[e] = da[e >> 2][e & 3] * __builtin_fmaf(t, __builtin_fmaf(sg, -kNegLn2, kNegLn2), sg);
+    };
+    // mode 2: each pair's buckets and mask (32-bit differences when small)
+    auto pairs = [&](auto small_t) __attribute__((always_inline)) {
+      constexpr bool SMALL = decltype(small_t)::value;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int ql = 16 * (e >> 2) + 4 * g + (e & 3), i = i0 + ql;
+        const bool valid = kvalid && i < L && attends(i, jk, nh);
+        const int bp = pos_bucket(position(i, nh, shared), p_k, R);
+        const int bt = SMALL ? time_bucket_small((int)((uint32_t)tsq[ql] - (uint32_t)ts_k), NB, a.sbits)
+                             : time_bucket(wrap_sub(tsq[ql], ts_k), NB, a.sbits);
+        const float x = __builtin_fmaf(sc[e >> 2][e & 3], kNegLog2e, pos_s[bp] + time_s[bt]);
+        put(e, valid ? x : 1e30f);
+      }
+    };
+    if (mode == 0) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) put(e, __builtin_fmaf(sc[e >> 2][e & 3], kNegLog2e, b_lo));
+    } else if (mode == 1) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int ql = 16 * (e >> 2) + 4 * g + (e & 3);
+        put(e, __builtin_fmaf(sc[e >> 2][e & 3], kNegLog2e, tsq[ql] >= tcut ? b_hi : b_lo));
+      }
+    } else if (small) {
+      pairs(std::true_type{});
+    } else {
+      pairs(std::false_type{});
+    }
+    // dV^T += dO^T a and dK^T += Q^T dS, one 32-query half at a time: a
+    // lane's elements 8 c .. 8 c + 7 are that half's k values in kv_col_frag's
+    // order
+    const bf16x8 fa0 = bwd_frag<T>(pa), fa1 = bwd_frag<T>(pa + 8);
+    const bf16x8 fd0 = bwd_frag<T>(pd), fd1 = bwd_frag<T>(pd + 8);
+    // step t: half c = t / (FV + FQ); dV tile ft, then dK tile ft
+    constexpr int FV = DV / 16, FQ = DQK / 16;
+    bwd_piped<2 * (FV + FQ), 4>(
+        [&](int t) __attribute__((always_inline)) {
+          const int c = t / (FV + FQ), u = t % (FV + FQ);
+          return u < FV ? kv_col_frag<DV>(Os + 32 * c * DV + cov[u]) : kv_col_frag<DQK>(Qs + 32 * c * DQK + coq[u - FV]);
+        },
+        [&](int t, const bf16x8& x) __attribute__((always_inline)) {
+          const int c = t / (FV + FQ), u = t % (FV + FQ);
+          if (u < FV)
+            dv[u] = mma16(x, c ? fa1 : fa0, dv[u]);
+          else
+            dk[u - FV] = mma16(x, c ? fd1 : fd0, dk[u - FV]);
+        });
+  };
+  issue(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of block 0 have landed
+  __syncthreads();                // ... and every wave's, plus the tables
+  for (int blk = 0; blk < nblk; blk += 2) {
+    if (blk + 1 < nblk) issue(blk + 1, 1);
+    consume(blk, 0);
+    if (blk + 1 >= nblk) break;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (blk + 2 < nblk) issue(blk + 2, 0);
+    consume(blk + 1, 1);
+    if (blk + 2 >= nblk) break;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+  if (kvalid) {
+    float* dvd = a.dact + (s0 + jk) * (int64_t)a.N1 + K2 + h * DV + 4 * g;
+    float* dkd = a.dact + (s0 + jk) * (int64_t)a.N1 + 2 * K2 + H * DQK + h * DQK + 4 * g;
+    const float fv = kNegLn2 * inv_n;
+#pragma unroll
+    for (int ft = 0; ft < DV / 16; ++ft)
+      *reinterpret_cast<float4*>(dvd + 16 * ft) =
+          make_float4(fv * dv[ft][0], fv * dv[ft][1], fv * dv[ft][2], fv * dv[ft][3]);
+#pragma unroll
+    for (int ft = 0; ft < DQK / 16; ++ft)
+      *reinterpret_cast<float4*>(dkd + 16 * ft) =
+          make_float4(inv_n * dk[ft][0], inv_n * dk[ft][1], inv_n * dk[ft][2], inv_n * dk[ft][3]);
+  }
+}
+
 // Bias-table gradients: column sums of the dq kernel's partial rows, per
 // head (rows item * H + h); a table with head stride 0 sums every head (into
 // head 0's row).  One workgroup per 64 result columns; its 16 waves take
@@ -700,8 +1080,13 @@ template <typename T, int DQK, int DV>
 static hipError_t bwd_dims(const BwdArgs& a, int64_t grid, hipStream_t s) {
   const size_t sh_dq = (size_t)5 * (a.P + a.NB) * sizeof(float), sh_kv = (size_t)(a.P + a.NB) * sizeof(float);
   hipLaunchKernelGGL((attn_bwd_dq_kernel<T, DQK, DV>), dim3((unsigned)grid), dim3(256), sh_dq, s, a);
-  hipLaunchKernelGGL((attn_bwd_dkv_kernel<T, DQK, DV, false>), dim3((unsigned)grid), dim3(256), sh_kv, s, a);
-  hipLaunchKernelGGL((attn_bwd_dkv_kernel<T, DQK, DV, true>), dim3((unsigned)grid), dim3(256), sh_kv, s, a);
+  if constexpr (std::is_same<T, bf16>::value) {
+    // two 64-key halves per work item
+    hipLaunchKernelGGL((attn_bwd_kv16_kernel<DQK, DV>), dim3((unsigned)(2 * grid)), dim3(256), sh_kv, s, a);
+  } else {
+    hipLaunchKernelGGL((attn_bwd_dkv_kernel<T, DQK, DV, false>), dim3((unsigned)grid), dim3(256), sh_kv, s, a);
+    hipLaunchKernelGGL((attn_bwd_dkv_kernel<T, DQK, DV, true>), dim3((unsigned)grid), dim3(256), sh_kv, s, a);
+  }
   return hipGetLastError();
 }
 
