@@ -213,6 +213,23 @@ __device__ __forceinline__ typename Elem<T>::Frag bwd_col_frag(const T* lds, int
   return x;
 }
 
+// Sixteen int64 timestamps from LDS: four groups of four consecutive
+// entries, group q at p + q * STRIDE (p 16-byte aligned), read with eight
+// 16-byte loads that are all issued before any result is used.
+template <int STRIDE>
+__device__ __forceinline__ void bwd_ts16(const int64_t* p, int64_t (&t)[16]) {
+  typedef long long bwd_i64x2 __attribute__((ext_vector_type(2)));
+  bwd_i64x2 v[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) v[k] = *reinterpret_cast<const bwd_i64x2*>(p + (k >> 1) * STRIDE + 2 * (k & 1));
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    t[2 * k] = v[k][0];
+    t[2 * k + 1] = v[k][1];
+  }
+}
+
 // Runs use(c, read(c)) for c = 0 .. N - 1 with the reads issued DEPTH
 // steps ahead of their use, so that LDS latency overlaps the MFMAs.  The
 // scheduling barriers keep the compiler from sinking each read back to its
@@ -441,13 +458,15 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
     auto pairs = [&](auto small_t, int kh, const f32x16& sc, const f32x16& da, float (&ds)[16])
                      __attribute__((always_inline)) {
       constexpr bool SMALL = decltype(small_t)::value;
+      int64_t tk[16];
+      bwd_ts16<8>(tsk + kh * 32 + 4 * half, tk);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int kl = kh * 32 + 8 * (r >> 2) + 4 * half + (r & 3), j = j0 + kl;
         const bool valid = qvalid && j < L && attends(iq, j, nh);
         const int bp = pos_bucket(p_q, position(j, nh, shared), R);
-        const int bt = SMALL ? time_bucket_small((int)((uint32_t)ts_q - (uint32_t)tsk[kl]), NB, a.sbits)
-                             : time_bucket(wrap_sub(ts_q, tsk[kl]), NB, a.sbits);
+        const int bt = SMALL ? time_bucket_small((int)((uint32_t)ts_q - (uint32_t)tk[r]), NB, a.sbits)
+                             : time_bucket(wrap_sub(ts_q, tk[r]), NB, a.sbits);
         const float s = sc[r] + pos_s[bp] + time_s[bt];
         const float sg = bwd_sigmoid(s);
         const float g = da[r] * sg * (1.0f + s * (1.0f - sg)) * inv_n;
@@ -492,10 +511,11 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
         add_run(bt_lo, sum);
       } else if (mode == 1) {
         float sum_lo = 0.f, sum_hi = 0.f;
+        int64_t tk[16];  // element r: key kh * 32 + 8 (r / 4) + 4 half + r % 4
+        bwd_ts16<8>(tsk + kh * 32 + 4 * half, tk);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int kl = kh * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          const bool up = tsk[kl] <= tcut;
+          const bool up = tk[r] <= tcut;
           const float s = sc[r] + (up ? b_hi : b_lo);
           const float sg = bwd_sigmoid(s);
           ds[r] = qvalid ? da[r] * sg * (1.0f + s * (1.0f - sg)) * inv_n : 0.f;
@@ -954,13 +974,15 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kv16_kernel(BwdArgs a) {
     // mode 2: each pair's buckets and mask (32-bit differences when small)
     auto pairs = [&](auto small_t) __attribute__((always_inline)) {
       constexpr bool SMALL = decltype(small_t)::value;
+      int64_t tq[16];
+      bwd_ts16<16>(tsq + 4 * g, tq);
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int ql = 16 * (e >> 2) + 4 * g + (e & 3), i = i0 + ql;
         const bool valid = kvalid && i < L && attends(i, jk, nh);
         const int bp = pos_bucket(position(i, nh, shared), p_k, R);
-        const int bt = SMALL ? time_bucket_small((int)((uint32_t)tsq[ql] - (uint32_t)ts_k), NB, a.sbits)
-                             : time_bucket(wrap_sub(tsq[ql], ts_k), NB, a.sbits);
+        const int bt = SMALL ? time_bucket_small((int)((uint32_t)tq[e] - (uint32_t)ts_k), NB, a.sbits)
+                             : time_bucket(wrap_sub(tq[e], ts_k), NB, a.sbits);
         const float x = __builtin_fmaf(sc[e >> 2][e & 3], kNegLog2e, pos_s[bp] + time_s[bt]);
         put(e, valid ? x : 1e30f);
       }
@@ -969,11 +991,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kv16_kernel(BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) put(e, __builtin_fmaf(sc[e >> 2][e & 3], kNegLog2e, b_lo));
     } else if (mode == 1) {
+      int64_t tq[16];  // element e: query 16 (e / 4) + 4 g + e % 4
+      bwd_ts16<16>(tsq + 4 * g, tq);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int ql = 16 * (e >> 2) + 4 * g + (e & 3);
-        put(e, __builtin_fmaf(sc[e >> 2][e & 3], kNegLog2e, tsq[ql] >= tcut ? b_hi : b_lo));
-      }
+      for (int e = 0; e < 16; ++e) put(e, __builtin_fmaf(sc[e >> 2][e & 3], kNegLog2e, tq[e] >= tcut ? b_hi : b_lo));
     } else if (small) {
       pairs(std::true_type{});
     } else {
