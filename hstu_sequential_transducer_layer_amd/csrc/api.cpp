@@ -250,7 +250,7 @@ size_t hstu_attn_workspace_size(const hstu_desc* desc, int64_t T, int32_t B) {
 }
 
 static hstu_status run_proj(const hstu_desc* d, const void* x, int64_t T, const hstu_weights* w,
-                            const hstu_activations* a, void* xn, hipStream_t s) {
+                            const hstu_activations* a, void* xn, hipStream_t s, void* pre = nullptr) {
   const void* src = x;
   if (d->flags & HSTU_INPUT_NORM) {
     hstu_status st = device(hstu::launch_ln_in(d->dtype, x, w->ln_in_g, w->ln_in_b, xn, T,
@@ -258,7 +258,7 @@ static hstu_status run_proj(const hstu_desc* d, const void* x, int64_t T, const 
     if (st != HSTU_OK) return st;
     src = xn;
   }
-  return device(hstu::launch_proj(*d, src, T, w->w1, w->b1, a->u, a->v, a->q, a->k, s), "proj launch");
+  return device(hstu::launch_proj(*d, src, T, w->w1, w->b1, a->u, a->v, a->q, a->k, pre, s), "proj launch");
 }
 
 static hstu_status run_attn(const hstu_desc* d, const int64_t* off, int32_t B, int64_t T,
@@ -510,7 +510,7 @@ hstu_status hstu_cand_fwd(const hstu_desc* desc, const void* x, const int64_t* c
 // Backward workspace: the forward's buffers, then the backward's.
 struct BwdLayout {
   Layout f;
-  size_t z, dz, dact, dav, gterm_av, bterm_av, tab_part, dpre_t, w2t, dyt, zt, w1t, dpret, xnt, dxn, gterm_in,
+  size_t pre, z, dz, dact, dav, gterm_av, bterm_av, tab_part, dpre_t, w2t, dyt, zt, w1t, dpret, xnt, dxn, gterm_in,
       ctmp, wsplit, total;
   int64_t Tp;
 };
@@ -528,6 +528,7 @@ static BwdLayout bwd_layout(const hstu_desc* d, int64_t T, int32_t B) {
     o += align256(bytes);
     return at;
   };
+  L.pre = take((size_t)T * N1 * e);
   L.z = take((size_t)T * K2 * e);
   L.dz = take((size_t)T * K2 * 4);
   L.dact = take((size_t)T * N1 * 4);
@@ -572,9 +573,9 @@ size_t hstu_bwd_workspace_size(const hstu_desc* desc, int64_t T, int32_t B) {
   return bwd_layout(desc, T, B).total;
 }
 
-// The forward into a backward workspace: U, V, Q, K; AV and its statistics
-// (and the work list); Z in its own region (V stays); then f2 into out when
-// out is given.
+// The forward into a backward workspace: U, V, Q, K and the pre-activation
+// x~ W1^T + b1; AV and its statistics (and the work list); Z in its own
+// region (V stays); then f2 into out when out is given.
 static hstu_status fwd_into_bwd_layout(const hstu_desc* desc, const void* x, const int64_t* off, int32_t B,
                                        int64_t T, const int64_t* ts, const int32_t* nc, const hstu_weights* w,
                                        const hstu_bias_tables* tables, const BwdLayout& L, char* base, void* out,
@@ -587,7 +588,7 @@ static hstu_status fwd_into_bwd_layout(const hstu_desc* desc, const void* x, con
   a.k = base + L.f.k;
   a.av = base + L.f.av;
   a.av_stats = (float*)(base + L.f.stats);
-  if ((st = run_proj(desc, x, T, w, &a, base + L.f.xn, s)) != HSTU_OK) return st;
+  if ((st = run_proj(desc, x, T, w, &a, base + L.f.xn, s, base + L.pre)) != HSTU_OK) return st;
   if ((st = run_attn(desc, off, B, T, ts, nc, tables, &a, base + L.f.attn, s)) != HSTU_OK) return st;
   void* z = base + L.z;
   if ((st = device(hstu::launch_gate(*desc, T, *w, a.u, a.av, a.av_stats, z, s), "gate launch")) != HSTU_OK) return st;
@@ -705,9 +706,10 @@ hstu_status hstu_layer_bwd(const hstu_desc* desc, const void* x, const int64_t* 
                                          F(L.tab_part), g->pos, g->time, sc, s),
                    "attention backward launch")) != HSTU_OK)
     return st;
-  // f1 and SiLU: dpre = d(u|v|q|k) * SiLU'(x~ W1^T + b1); db1, dW1 = dpre^T x~, dx~ = dpre W1
-  if ((st = device(hstu::launch_gemm_silu_bwd(dt, xn, w->w1, w->b1, dact, T, (int)N1, dm, base + L.dpre_t, ctmp, g->b1, s),
-                   "pre-activation gemm and silu backward launch")) != HSTU_OK)
+  // f1 and SiLU: dpre = d(u|v|q|k) * SiLU'(x~ W1^T + b1) from the saved
+  // pre-activation; db1, dW1 = dpre^T x~, dx~ = dpre W1
+  if ((st = device(hstu::launch_silu_bwd(dt, dact, base + L.pre, T, (int)N1, base + L.dpre_t, ctmp, g->b1, s),
+                   "silu backward launch")) != HSTU_OK)
     return st;
   if ((st = device(hstu::launch_transpose(dt, w->w1, N1, dm, N1, base + L.w1t, s), "transpose")) != HSTU_OK) return st;
   if ((st = device(hstu::launch_gemm_nt_f32(dt, base + L.dpre_t, base + L.w1t, F(L.dxn), T, dm, (int)N1, nullptr, s), "gemm")) !=

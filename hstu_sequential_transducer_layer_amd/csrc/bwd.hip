@@ -299,68 +299,45 @@ __global__ __launch_bounds__(256) void gate_bwd_kernel(const float* __restrict__
   chunk_partials(ga, ba, K, red, gpart, bpart);
 }
 
-// The pre-activation GEMM of f1 with the SiLU backward as its epilogue: the
-// 128 x 128 tile pre = A B^T (A = x~ [M, K], B = W1 [N, K]) never leaves the
-// chip.  z = pre + b1 goes through LDS, 64 rows at a time (rows padded to 136
-// floats, so the accumulator writes of a wave's two 4-row groups hit
-// different banks), and is read back along rows: each thread takes 8 columns
-// of one row per pass, loads dact with 16-byte loads and writes dpre =
-// dact * SiLU'(z) in the layer dtype.  The tile's 128 rows are one row chunk
-// of db1's column sums: a thread adds its rows in order, then the 16 row
-// groups are added in order into part[chunk][col].  N is a multiple of 8.
-constexpr int kSiluPad = 136;
+// The SiLU backward of f1 from the forward's saved pre-activation z:
+// dpre = dact * SiLU'(z) in the layer dtype, with db1's column sums.  A
+// workgroup takes kColRows rows and 512 columns; each thread 8 consecutive
+// columns (16-byte accesses for bf16) of 32 rows, in order, four row groups
+// per workgroup.  The row groups' column sums are added in order into
+// part[chunk][col], which colsum_chunks_kernel then sums over the chunks.
+// N is a multiple of 8.
 template <typename T>
-__global__ __launch_bounds__(256, 2) void gemm_silu_bwd_kernel(const T* __restrict__ A, const T* __restrict__ Bm,
-                                                               const T* __restrict__ b1, const float* __restrict__ dact,
-                                                               int64_t M, int N, int K, T* __restrict__ dpre,
-                                                               float* __restrict__ part) {
-  typedef GemmTile<T> G;
-  static_assert(G::BM == kColRows && G::BM == 128 && G::BN == 128, "a tile row is one row chunk of the column sums");
-  __shared__ __attribute__((aligned(16))) T As[G::BM * G::LDK];
-  __shared__ __attribute__((aligned(16))) T Bs[G::BN * G::LDK];
-  __shared__ __attribute__((aligned(16))) float zs[64 * kSiluPad];
-  __shared__ float red[16][G::BN];
-  const int nrow = (int)((M + G::BM - 1) / G::BM), ncol = (N + G::BN - 1) / G::BN;
-  int tr, tc;
-  map_tile(blockIdx.x, nrow, ncol, tr, tc);
-  const int64_t row0 = (int64_t)tr * G::BM;
-  const int col0 = tc * G::BN;
-  RowLoader<T> al{A, row0, M, K, K};
-  f32x16 acc[2][2];
-  gemm_mainloop<T>(al, Bm, col0, N, K, As, Bs, acc, K);
-  const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), wm = w >> 1, wn = w & 1;
-  float bias[2];
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int col = col0 + wn * 64 + nt * 32 + (lane & 31);
-    bias[nt] = col < N ? to_f32(b1[col]) : 0.f;
-  }
-  const int rr = tid >> 4, cg = tid & 15;  // read phase: row group, 8-column group
-  const int gcol = col0 + cg * 8;
+__global__ __launch_bounds__(256) void silu_bwd_kernel(const float* __restrict__ dact, const T* __restrict__ pre,
+                                                       int64_t M, int N, T* __restrict__ dpre,
+                                                       float* __restrict__ part) {
+  static_assert(kColRows == 128, "four row groups of 32 rows");
+  __shared__ float red[4][512];
+  const int ncb = (N + 511) / 512;
+  const int64_t chunk = blockIdx.x / ncb;
+  const int cg = threadIdx.x & 63, rg = threadIdx.x >> 6;
+  const int col = (int)(blockIdx.x % ncb) * 512 + 8 * cg;
+  const int64_t r0 = chunk * kColRows + 32 * rg;
   float cs[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int hf = 0; hf < 2; ++hf) {
-    if (wm == hf) {
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            zs[(acc_row(0, mt, lane, r)) * kSiluPad + wn * 64 + nt * 32 + (lane & 31)] = acc[mt][nt][r] + bias[nt];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int pss = 0; pss < 4; ++pss) {
-      const int lr = pss * 16 + rr;
-      const int64_t grow = row0 + hf * 64 + lr;
-      if (grow < M && gcol < N) {
-        const float4 z0 = *reinterpret_cast<const float4*>(zs + lr * kSiluPad + cg * 8);
-        const float4 z1 = *reinterpret_cast<const float4*>(zs + lr * kSiluPad + cg * 8 + 4);
-        const float* gp = dact + grow * N + gcol;
+  if (col < N) {
+#pragma unroll 4
+    for (int i = 0; i < 32; ++i) {
+      const int64_t row = r0 + i;
+      if (row < M) {
+        const float* gp = dact + row * N + col;
         const float4 g0 = *reinterpret_cast<const float4*>(gp), g1 = *reinterpret_cast<const float4*>(gp + 4);
-        const float zv[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
         const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+        float zv[8];
+        if constexpr (sizeof(T) == 2) {
+          const uint4 zr = *reinterpret_cast<const uint4*>(pre + row * N + col);
+          const T* z8 = reinterpret_cast<const T*>(&zr);
+#pragma unroll
+          for (int q = 0; q < 8; ++q) zv[q] = to_f32(z8[q]);
+        } else {
+          const float4 z0 = *reinterpret_cast<const float4*>(pre + row * N + col);
+          const float4 z1 = *reinterpret_cast<const float4*>(pre + row * N + col + 4);
+          zv[0] = z0.x, zv[1] = z0.y, zv[2] = z0.z, zv[3] = z0.w;
+          zv[4] = z1.x, zv[5] = z1.y, zv[6] = z1.z, zv[7] = z1.w;
+        }
         T out[8];
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
@@ -370,7 +347,7 @@ __global__ __launch_bounds__(256, 2) void gemm_silu_bwd_kernel(const T* __restri
           cs[q] += d;
           out[q] = from_f32<T>(d);
         }
-        T* dst = dpre + grow * N + gcol;
+        T* dst = dpre + row * N + col;
         if constexpr (sizeof(T) == 2) {
           *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(out);
         } else {
@@ -379,115 +356,13 @@ __global__ __launch_bounds__(256, 2) void gemm_silu_bwd_kernel(const T* __restri
         }
       }
     }
-    __syncthreads();  // zs is rewritten by the next half
   }
 #pragma unroll
-  for (int q = 0; q < 8; ++q) red[rr][cg * 8 + q] = cs[q];
+  for (int q = 0; q < 8; ++q) red[rg][8 * cg + q] = cs[q];
   __syncthreads();
-  if (tid < G::BN && col0 + tid < N) {
-    float sum = 0.f;
-#pragma unroll
-    for (int g = 0; g < 16; ++g) sum += red[g][tid];
-    part[(int64_t)tr * N + col0 + tid] = sum;
-  }
-}
-
-// The same on the 256 x 256 core (bf16, K a multiple of 64).  z goes through
-// the four freed operand stages, 128 rows at a time: stage b holds 32 rows x
-// 256 fp32 columns, row r at r * 256 with 16-byte chunk c at
-// c ^ ((r >> 2) & 1) * 4 (so a wave's two 4-row groups hit different banks);
-// wave tile (wm, mt) goes to stage (wm & 1) * 2 + mt in pass wm >> 1.  Each
-// thread then takes 8 columns of one row per step, as above, and the column
-// partials are per 256-row tile (part[tile row][N]).
-__global__ __launch_bounds__(512, 2) void gemm_silu_bwd_big_kernel(const bf16* __restrict__ A,
-                                                                   const bf16* __restrict__ Bm,
-                                                                   const bf16* __restrict__ b1,
-                                                                   const float* __restrict__ dact, int64_t M, int N,
-                                                                   int K, bf16* __restrict__ dpre,
-                                                                   float* __restrict__ part) {
-  __shared__ __attribute__((aligned(16))) bf16 As0[G2::STAGE];
-  __shared__ __attribute__((aligned(16))) bf16 As1[G2::STAGE];
-  __shared__ __attribute__((aligned(16))) bf16 Bs0[G2::STAGE];
-  __shared__ __attribute__((aligned(16))) bf16 Bs1[G2::STAGE];
-  __shared__ float red[16][G2::BN];
-  const int nrow = (int)((M + G2::BM - 1) / G2::BM), ncol = (N + G2::BN - 1) / G2::BN;
-  int tr, tc;
-  map_tile(blockIdx.x, nrow, ncol, tr, tc);
-  const int64_t row0 = (int64_t)tr * G2::BM;
-  const int col0 = tc * G2::BN;
-  const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), wm = w >> 1, wn = w & 1;
-  G2RowsA ap;
-  ap.c.init(A, row0, M, K, w, lane);
-  ap.w = w;
-  G2Copy bc;
-  bc.init(Bm, col0, N, K, w, lane);
-  f32x16 acc[2][4];
-  g2_mainloop<true>(ap, bc, K, As0, As1, Bs0, Bs1, acc);
-  __syncthreads();  // every wave is past its last operand read
-  auto stage = [&](int b) __attribute__((always_inline)) {
-    return reinterpret_cast<float*>(b == 0 ? As0 : b == 1 ? As1 : b == 2 ? Bs0 : Bs1);
-  };
-  float bias[4];
-#pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    const int col = col0 + wn * 128 + nt * 32 + (lane & 31);
-    bias[nt] = col < N ? (float)b1[col] : 0.f;
-  }
-  const int rr = tid >> 5, cg = tid & 31;  // read phase: row group, 8-column group
-  const int gcol = col0 + cg * 8;
-  float cs[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-    if ((wm >> 1) == pass) {
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        float* const zb = stage((wm & 1) * 2 + mt);
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-          const int col = wn * 128 + nt * 32 + (lane & 31);
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int rl = g2_out_row(0, lane, r);
-            zb[rl * 256 + ((((col >> 2) ^ (((rl >> 2) & 1) << 2))) << 2) + (col & 3)] = acc[mt][nt][r] + bias[nt];
-          }
-        }
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int lr = i * 16 + rr, rl = lr & 31, sw = ((rl >> 2) & 1) << 2;
-      const int64_t grow = row0 + pass * 128 + lr;
-      if (grow < M && gcol < N) {
-        const float* zr = stage(lr >> 5) + rl * 256;
-        const float4 z0 = *reinterpret_cast<const float4*>(zr + (((2 * cg) ^ sw) << 2));
-        const float4 z1 = *reinterpret_cast<const float4*>(zr + (((2 * cg + 1) ^ sw) << 2));
-        const float* gp = dact + grow * N + gcol;
-        const float4 g0 = *reinterpret_cast<const float4*>(gp), g1 = *reinterpret_cast<const float4*>(gp + 4);
-        const float zv[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
-        const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-        bf16 out[8];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const float z = zv[q];
-          const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z * -1.4426950408889634f));
-          const float d = gv[q] * sg * (1.0f + z * (1.0f - sg));
-          cs[q] += d;
-          out[q] = (bf16)d;
-        }
-        *reinterpret_cast<uint4*>(dpre + grow * N + gcol) = *reinterpret_cast<const uint4*>(out);
-      }
-    }
-    __syncthreads();  // the stages are rewritten by the next pass
-  }
-#pragma unroll
-  for (int q = 0; q < 8; ++q) red[rr][cg * 8 + q] = cs[q];
-  __syncthreads();
-  if (tid < G2::BN && col0 + tid < N) {
-    float sum = 0.f;
-#pragma unroll
-    for (int g = 0; g < 16; ++g) sum += red[g][tid];
-    part[(int64_t)tr * N + col0 + tid] = sum;
+  for (int c = threadIdx.x; c < 512; c += 256) {
+    const int gc = (int)(blockIdx.x % ncb) * 512 + c;
+    if (gc < N) part[chunk * N + gc] = ((red[0][c] + red[1][c]) + red[2][c]) + red[3][c];
   }
 }
 
@@ -918,27 +793,18 @@ hipError_t launch_gate_bwd(const hstu_desc& d, int64_t T, const hstu_weights& w,
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_silu_bwd(hstu_dtype dt, const void* A, const void* w1, const void* b1, const float* dact,
-                                int64_t T, int n1, int K, void* dpre_t, float* part, float* db1, hipStream_t s) {
-  if (n1 % 8 != 0 || K % 8 != 0) return hipErrorInvalidValue;
-  const int64_t big_tiles = ((T + G2::BM - 1) / G2::BM) * ((n1 + G2::BN - 1) / G2::BN);
-  if (dt == HSTU_BF16 && K % G2::BK == 0 && big_tiles >= kG2MinTiles) {
-    const int64_t rows = (T + G2::BM - 1) / G2::BM;
-    hipLaunchKernelGGL(gemm_silu_bwd_big_kernel, dim3((unsigned)big_tiles), dim3(G2::NT), 0, s, (const bf16*)A,
-                       (const bf16*)w1, (const bf16*)b1, dact, T, n1, K, (bf16*)dpre_t, part);
-    hipLaunchKernelGGL(colsum_chunks_kernel, dim3((unsigned)((n1 + 63) / 64)), dim3(64 * kColGroups), 0, s,
-                       (const float*)part, rows, (int64_t)n1, db1);
-    return hipGetLastError();
-  }
+hipError_t launch_silu_bwd(hstu_dtype dt, const float* dact, const void* pre, int64_t T, int n1, void* dpre,
+                           float* part, float* db1, hipStream_t s) {
+  if (n1 % 8 != 0) return hipErrorInvalidValue;
   const int64_t chunks = (T + kColRows - 1) / kColRows;
   if (chunks > 0) {
-    const dim3 grid((unsigned)(chunks * ((n1 + 127) / 128)));
+    const dim3 grid((unsigned)(chunks * ((n1 + 511) / 512)));
     if (dt == HSTU_BF16)
-      hipLaunchKernelGGL(gemm_silu_bwd_kernel<bf16>, grid, dim3(256), 0, s, (const bf16*)A, (const bf16*)w1,
-                         (const bf16*)b1, dact, T, n1, K, (bf16*)dpre_t, part);
+      hipLaunchKernelGGL(silu_bwd_kernel<bf16>, grid, dim3(256), 0, s, dact, (const bf16*)pre, T, n1, (bf16*)dpre,
+                         part);
     else
-      hipLaunchKernelGGL(gemm_silu_bwd_kernel<float>, grid, dim3(256), 0, s, (const float*)A, (const float*)w1,
-                         (const float*)b1, dact, T, n1, K, (float*)dpre_t, part);
+      hipLaunchKernelGGL(silu_bwd_kernel<float>, grid, dim3(256), 0, s, dact, (const float*)pre, T, n1,
+                         (float*)dpre, part);
   }
   hipLaunchKernelGGL(colsum_chunks_kernel, dim3((unsigned)((n1 + 63) / 64)), dim3(64 * kColGroups), 0, s,
                      (const float*)part, chunks, (int64_t)n1, db1);

@@ -139,9 +139,11 @@ hipError_t launch_ln_in(hstu_dtype dt, const void* x, const void* g, const void*
 // time-stamp summary (tstat, rel) that the attention kernel reads per block.
 hipError_t launch_attn_prep(const AttnRows& rows, int bm, const AttnScratch& sc, hipStream_t s);
 
-// --- proj.hip: u|v|q|k = SiLU(xn W1^T + b1), scattered to the stage layouts.
+// --- proj.hip: u|v|q|k = SiLU(xn W1^T + b1), scattered to the stage layouts;
+// when pre is not null also the pre-activation xn W1^T + b1 itself, [T, N1]
+// row-major in the layer dtype (the backward's SiLU derivative reads it).
 hipError_t launch_proj(const hstu_desc& d, const void* xn, int64_t T, const void* w1,
-                       const void* b1, void* u, void* v, void* q, void* k, hipStream_t s);
+                       const void* b1, void* u, void* v, void* q, void* k, void* pre, hipStream_t s);
 
 // --- attn.hip: av, stats of the query rows.  k, v: the key rows' tensors (in
 // a cached pass the history cache; q, qk, qv are then the candidates' own
@@ -208,11 +210,11 @@ hipError_t launch_gemm_nt_f32(hstu_dtype dt, const void* A, const void* Bm, floa
 hipError_t launch_gate_bwd(const hstu_desc& d, int64_t T, const hstu_weights& w, const float* dz, const void* u,
                            const void* av, const float* stats, float* du, void* dav, float* gpart, float* bpart,
                            float* dg, float* db, hipStream_t s);
-// pre = A W1^T (A [T, K], W1 [n1, K], K a multiple of 8), then dpre_t = dact *
-// SiLU'(pre + b1) in the layer dtype and db1 = its column sums (part:
-// colsum_tmp_bytes(T, n1) of scratch); pre itself is never stored.
-hipError_t launch_gemm_silu_bwd(hstu_dtype dt, const void* A, const void* w1, const void* b1, const float* dact,
-                                int64_t T, int n1, int K, void* dpre_t, float* part, float* db1, hipStream_t s);
+// dpre = dact * SiLU'(pre) in the layer dtype, pre the forward's saved
+// pre-activation [T, n1] (n1 a multiple of 8), and db1 = the column sums of
+// dpre (part: colsum_tmp_bytes(T, n1) of scratch).
+hipError_t launch_silu_bwd(hstu_dtype dt, const float* dact, const void* pre, int64_t T, int n1, void* dpre,
+                           float* part, float* db1, hipStream_t s);
 // gpart, bpart: ceil(T / 32) x d_model partial rows of the LayerNorm_in gain
 // and offset gradients, summed into dg, db (zero without HSTU_INPUT_NORM).
 hipError_t launch_ln_bwd(const hstu_desc& d, const void* x, const float* dxn, const hstu_weights& w, const void* dy,

@@ -302,13 +302,16 @@ typedef struct {
  * fp32, num_types = 0, pos_buckets + time_buckets <= 2048, d_model <= 2048
  * and num_heads * dv <= 2048; else HSTU_ERR_UNSUPPORTED.  Results are reproducible bit for bit.  Weight gradients come from
  * GEMMs over the token dimension in the layer dtype with fp32 accumulation.
+ * The SiLU derivative of f1 is taken at the forward's pre-activation
+ * x W1^T + b1 as stored in the workspace, in the layer dtype.
  *   workspace >= hstu_bwd_workspace_size(desc, T, B) bytes, 256-aligned     */
 size_t hstu_bwd_workspace_size(const hstu_desc* desc, int64_t total_tokens, int32_t batch);
 
 /* The layer forward of a training step: the same computation and result as
  * hstu_layer_fwd (bit for bit), run in a backward workspace whose forward part
- * it leaves filled (x after the input LayerNorm, U, V, Q, K, AV and its
- * statistics, the attention plan, and Z = LN(AV) * U), so that a following
+ * it leaves filled (x after the input LayerNorm, U, V, Q, K, the
+ * pre-activation x W1^T + b1, AV and its statistics, the attention plan, and
+ * Z = LN(AV) * U), so that a following
  * hstu_layer_bwd with HSTU_SAVED_FWD, on the same stream, with the same
  * arguments and workspace, skips its forward recompute.  Limits as
  * hstu_layer_bwd.  HSTU_SAVED_FWD in desc is ignored here.
