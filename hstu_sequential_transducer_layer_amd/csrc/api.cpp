@@ -510,7 +510,7 @@ hstu_status hstu_cand_fwd(const hstu_desc* desc, const void* x, const int64_t* c
 // Backward workspace: the forward's buffers, then the backward's.
 struct BwdLayout {
   Layout f;
-  size_t pre, z, dz, dact, dav, gterm_av, bterm_av, tab_part, dpre_t, w2t, dyt, zt, w1t, dpret, xnt, dxn, gterm_in,
+  size_t pre, z, dz, dav, gterm_av, bterm_av, tab_part, dpre_t, w2t, dyt, zt, w1t, dpret, xnt, dxn, gterm_in,
       ctmp, wsplit, total;
   int64_t Tp;
 };
@@ -531,7 +531,6 @@ static BwdLayout bwd_layout(const hstu_desc* d, int64_t T, int32_t B) {
   L.pre = take((size_t)T * N1 * e);
   L.z = take((size_t)T * K2 * e);
   L.dz = take((size_t)T * K2 * 4);
-  L.dact = take((size_t)T * N1 * 4);
   L.dav = take((size_t)T * K2 * e);
   const int64_t rchunks = (T + 31) / 32;  // the LayerNorm backward kernels' 32-row partial sums
   L.gterm_av = take((size_t)rchunks * K2 * 4);
@@ -694,23 +693,22 @@ hstu_status hstu_layer_bwd(const hstu_desc* desc, const void* x, const int64_t* 
       return st;
   }
   if ((st = colsum(false, dy, T, dm, g->b2)) != HSTU_OK) return st;
-  // gate and LayerNorm over the merged heads
-  float* dact = F(L.dact);
-  if ((st = device(hstu::launch_gate_bwd(*desc, T, *w, F(L.dz), a.u, a.av, a.av_stats, dact, base + L.dav,
-                                         F(L.gterm_av), F(L.bterm_av), g->ln_av_g, g->ln_av_b, s),
+  // Each of dU, dV, dQ, dK goes out as its pre-activation gradient:
+  // dpre = d(u|v|q|k) * SiLU'(x~ W1^T + b1), from the saved pre-activation.
+  // Gate and LayerNorm over the merged heads (dU, dL/dAV):
+  void* dpre = base + L.dpre_t;
+  if ((st = device(hstu::launch_gate_bwd(*desc, T, *w, F(L.dz), a.u, a.av, a.av_stats, base + L.pre, dpre,
+                                         base + L.dav, F(L.gterm_av), F(L.bterm_av), g->ln_av_g, g->ln_av_b, s),
                    "gate backward launch")) != HSTU_OK)
     return st;
-  // attention: dV, dQ, dK into dact; the bias tables
+  // attention: dV, dQ, dK; the bias tables
   const hstu::AttnScratch sc = hstu::attn_scratch(base + L.f.attn, T, B);
-  if ((st = device(hstu::launch_attn_bwd(*desc, off, nc, B, T, ts, *tables, a.q, a.k, a.v, base + L.dav, dact,
-                                         F(L.tab_part), g->pos, g->time, sc, s),
+  if ((st = device(hstu::launch_attn_bwd(*desc, off, nc, B, T, ts, *tables, a.q, a.k, a.v, base + L.dav, nullptr,
+                                         base + L.pre, dpre, F(L.tab_part), g->pos, g->time, sc, s),
                    "attention backward launch")) != HSTU_OK)
     return st;
-  // f1 and SiLU: dpre = d(u|v|q|k) * SiLU'(x~ W1^T + b1) from the saved
-  // pre-activation; db1, dW1 = dpre^T x~, dx~ = dpre W1
-  if ((st = device(hstu::launch_silu_bwd(dt, dact, base + L.pre, T, (int)N1, base + L.dpre_t, ctmp, g->b1, s),
-                   "silu backward launch")) != HSTU_OK)
-    return st;
+  // f1: db1 = column sums of dpre, dW1 = dpre^T x~, dx~ = dpre W1
+  if ((st = colsum(false, dpre, T, N1, g->b1)) != HSTU_OK) return st;
   if ((st = device(hstu::launch_transpose(dt, w->w1, N1, dm, N1, base + L.w1t, s), "transpose")) != HSTU_OK) return st;
   if ((st = device(hstu::launch_gemm_nt_f32(dt, base + L.dpre_t, base + L.w1t, F(L.dxn), T, dm, (int)N1, nullptr, s), "gemm")) !=
       HSTU_OK)
@@ -782,7 +780,7 @@ hstu_status hstu_attn_bwd(const hstu_desc* desc, const int64_t* off, int32_t B, 
       return st;
   }
   return device(hstu::launch_attn_bwd(*desc, off, nc, B, T, ts, *tables, acts->q, acts->k, acts->v, dav, dqkv,
-                                      (float*)((char*)ws + part_off), dpos, dtime, sc, s),
+                                      nullptr, nullptr, (float*)((char*)ws + part_off), dpos, dtime, sc, s),
                 "attention backward launch");
 }
 

@@ -21,6 +21,10 @@
 //   query block that can see those keys.  S = Q K^T (Q rows from LDS, K in
 //   registers); DK = false: dV^T += dO^T a; DK = true: dA = dO V^T and
 //   dK^T += Q^T dS.  Two passes keep each pass's accumulators in registers.
+// attn_bwd_kv16_kernel (bf16): dK and dV in one pass (described there).
+// PRE kernels write each gradient times SiLU'(pre), the forward's saved
+// pre-activation, straight into the layer backward's dpre; the others write
+// the raw gradients in fp32.
 // K/V (Q/dO) blocks are staged in LDS by direct global->LDS loads, double
 // buffered: block b + 1 is copied while block b is consumed.
 #include <type_traits>
@@ -41,6 +45,8 @@ struct BwdArgs {
   const void* v;      // [H, T, DV]
   const void* dout;   // [T, H * DV]: dL/dAV
   float* dact;        // [T, N1]: dv at column K2 + h DV, dq at 2 K2 + h DQK, dk at 2 K2 + H DQK + h DQK
+  const void* pre;    // PRE kernels: the saved pre-activation [T, N1] (layer dtype) ...
+  void* dpre;         // ... and the gradients times SiLU'(pre) in its layout, in place of dact
   float* tab_part;    // [gridDim.x][P + NB]: per-workgroup bias-table gradients (dq kernel),
                       // row (tbase[b] + query tile) * H + h: fixed by the batch, not by
                       // where the item sits in the work list
@@ -290,7 +296,31 @@ __device__ __forceinline__ float bwd_sigmoid(float s) {
   return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(s * -1.4426950408889634f));
 }
 
-template <typename T, int DQK, int DV>
+// Four gradient values of one token at flat index idx (row * N1 + column,
+// column a multiple of 4) of the [T, N1] output: raw fp32 into dact, or (PRE)
+// times SiLU'(pre) into dpre in the layer dtype.
+template <typename T, bool PRE>
+__device__ __forceinline__ void bwd_out4(const BwdArgs& a, int64_t idx, float x0, float x1, float x2, float x3) {
+  if constexpr (PRE) {
+    const T* p = reinterpret_cast<const T*>(a.pre) + idx;
+    T* d = reinterpret_cast<T*>(a.dpre) + idx;
+    if constexpr (sizeof(T) == 2) {
+      const uint2 raw = *reinterpret_cast<const uint2*>(p);
+      const T* z = reinterpret_cast<const T*>(&raw);
+      T o[4] = {from_f32<T>(x0 * silu_grad(to_f32(z[0]))), from_f32<T>(x1 * silu_grad(to_f32(z[1]))),
+                from_f32<T>(x2 * silu_grad(to_f32(z[2]))), from_f32<T>(x3 * silu_grad(to_f32(z[3])))};
+      *reinterpret_cast<uint2*>(d) = *reinterpret_cast<const uint2*>(o);
+    } else {
+      const float4 z = *reinterpret_cast<const float4*>(p);
+      *reinterpret_cast<float4*>(d) =
+          make_float4(x0 * silu_grad(z.x), x1 * silu_grad(z.y), x2 * silu_grad(z.z), x3 * silu_grad(z.w));
+    }
+  } else {
+    *reinterpret_cast<float4*>(a.dact + idx) = make_float4(x0, x1, x2, x3);
+  }
+}
+
+template <typename T, int DQK, int DV, bool PRE>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
   typedef typename Elem<T>::Frag Frag;
   // two buffer sets (even / odd key blocks) of a K and a V tile, all in one
@@ -564,13 +594,13 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
     __syncthreads();
   }
   if (qvalid) {
-    float* dst = a.dact + (s0 + iq) * (int64_t)a.N1 + 2 * K2 + h * DQK;
+    const int64_t dst = (s0 + iq) * (int64_t)a.N1 + 2 * K2 + h * DQK + 4 * half;
 #pragma unroll
     for (int n = 0; n < DQK / 32; ++n)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4)
-        *reinterpret_cast<float4*>(dst + 32 * n + 8 * g4 + 4 * half) =
-            make_float4(dq[n][4 * g4], dq[n][4 * g4 + 1], dq[n][4 * g4 + 2], dq[n][4 * g4 + 3]);
+        bwd_out4<T, PRE>(a, dst + 32 * n + 8 * g4, dq[n][4 * g4], dq[n][4 * g4 + 1], dq[n][4 * g4 + 2],
+                         dq[n][4 * g4 + 3]);
   }
   if (run != 0.f) atomicAdd(&gtime[run_bt], run);
   if (far_lo != 0.f) atomicAdd(&gpos[0], far_lo);
@@ -582,7 +612,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
   }
 }
 
-template <typename T, int DQK, int DV, bool DK>
+template <typename T, int DQK, int DV, bool DK, bool PRE>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(BwdArgs a) {
   typedef typename Elem<T>::Frag Frag;
   constexpr int DACC = DK ? DQK : DV;  // width of this pass's gradient
@@ -766,13 +796,14 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(BwdArgs a) {
     __syncthreads();
   }
   if (kvalid) {
-    float* dst = a.dact + (s0 + jk) * (int64_t)a.N1 + (DK ? 2 * K2 + H * DQK + h * DQK : K2 + h * DV);
+    const int64_t dst =
+        (s0 + jk) * (int64_t)a.N1 + (DK ? 2 * K2 + H * DQK + h * DQK : K2 + h * DV) + 4 * half;
 #pragma unroll
     for (int n = 0; n < DACC / 32; ++n)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4)
-        *reinterpret_cast<float4*>(dst + 32 * n + 8 * g4 + 4 * half) =
-            make_float4(acc[n][4 * g4], acc[n][4 * g4 + 1], acc[n][4 * g4 + 2], acc[n][4 * g4 + 3]);
+        bwd_out4<T, PRE>(a, dst + 32 * n + 8 * g4, acc[n][4 * g4], acc[n][4 * g4 + 1], acc[n][4 * g4 + 2],
+                         acc[n][4 * g4 + 3]);
   }
 }
 
@@ -821,7 +852,7 @@ __device__ __forceinline__ bf16x8 kv_col_frag(const bf16* p) {
 // gradient.  Per query block of 64 rows: four 16-query tiles of S and dA (Q,
 // dO rows from LDS, K, V in registers), then dV^T += dO^T a and
 // dK^T += Q^T dS with a and dS fed from the accumulators as the B operand.
-template <int DQK, int DV>
+template <int DQK, int DV, bool PRE>
 __global__ __launch_bounds__(256, 2) void attn_bwd_kv16_kernel(BwdArgs a) {
   typedef bf16 T;
   // two buffer sets (even / odd query blocks) of a Q and a dO tile, all in
@@ -1036,17 +1067,15 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kv16_kernel(BwdArgs a) {
     __syncthreads();
   }
   if (kvalid) {
-    float* dvd = a.dact + (s0 + jk) * (int64_t)a.N1 + K2 + h * DV + 4 * g;
-    float* dkd = a.dact + (s0 + jk) * (int64_t)a.N1 + 2 * K2 + H * DQK + h * DQK + 4 * g;
+    const int64_t dvd = (s0 + jk) * (int64_t)a.N1 + K2 + h * DV + 4 * g;
+    const int64_t dkd = (s0 + jk) * (int64_t)a.N1 + 2 * K2 + H * DQK + h * DQK + 4 * g;
     const float fv = kNegLn2 * inv_n;
 #pragma unroll
     for (int ft = 0; ft < DV / 16; ++ft)
-      *reinterpret_cast<float4*>(dvd + 16 * ft) =
-          make_float4(fv * dv[ft][0], fv * dv[ft][1], fv * dv[ft][2], fv * dv[ft][3]);
+      bwd_out4<T, PRE>(a, dvd + 16 * ft, fv * dv[ft][0], fv * dv[ft][1], fv * dv[ft][2], fv * dv[ft][3]);
 #pragma unroll
     for (int ft = 0; ft < DQK / 16; ++ft)
-      *reinterpret_cast<float4*>(dkd + 16 * ft) =
-          make_float4(inv_n * dk[ft][0], inv_n * dk[ft][1], inv_n * dk[ft][2], inv_n * dk[ft][3]);
+      bwd_out4<T, PRE>(a, dkd + 16 * ft, inv_n * dk[ft][0], inv_n * dk[ft][1], inv_n * dk[ft][2], inv_n * dk[ft][3]);
   }
 }
 
@@ -1097,24 +1126,29 @@ __global__ __launch_bounds__(64 * kTabGroups) void table_grad_kernel(const float
     gtime[(sh ? 0 : h) * NB + idx - P] = sum;
 }
 
-template <typename T, int DQK, int DV>
-static hipError_t bwd_dims(const BwdArgs& a, int64_t grid, hipStream_t s) {
+template <typename T, int DQK, int DV, bool PRE>
+static hipError_t bwd_dims_pre(const BwdArgs& a, int64_t grid, hipStream_t s) {
   const size_t sh_dq = (size_t)5 * (a.P + a.NB) * sizeof(float), sh_kv = (size_t)(a.P + a.NB) * sizeof(float);
-  hipLaunchKernelGGL((attn_bwd_dq_kernel<T, DQK, DV>), dim3((unsigned)grid), dim3(256), sh_dq, s, a);
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<T, DQK, DV, PRE>), dim3((unsigned)grid), dim3(256), sh_dq, s, a);
   if constexpr (std::is_same<T, bf16>::value) {
     // two 64-key halves per work item
-    hipLaunchKernelGGL((attn_bwd_kv16_kernel<DQK, DV>), dim3((unsigned)(2 * grid)), dim3(256), sh_kv, s, a);
+    hipLaunchKernelGGL((attn_bwd_kv16_kernel<DQK, DV, PRE>), dim3((unsigned)(2 * grid)), dim3(256), sh_kv, s, a);
   } else {
-    hipLaunchKernelGGL((attn_bwd_dkv_kernel<T, DQK, DV, false>), dim3((unsigned)grid), dim3(256), sh_kv, s, a);
-    hipLaunchKernelGGL((attn_bwd_dkv_kernel<T, DQK, DV, true>), dim3((unsigned)grid), dim3(256), sh_kv, s, a);
+    hipLaunchKernelGGL((attn_bwd_dkv_kernel<T, DQK, DV, false, PRE>), dim3((unsigned)grid), dim3(256), sh_kv, s, a);
+    hipLaunchKernelGGL((attn_bwd_dkv_kernel<T, DQK, DV, true, PRE>), dim3((unsigned)grid), dim3(256), sh_kv, s, a);
   }
   return hipGetLastError();
 }
 
+template <typename T, int DQK, int DV>
+static hipError_t bwd_dims(const BwdArgs& a, int64_t grid, hipStream_t s) {
+  return a.pre ? bwd_dims_pre<T, DQK, DV, true>(a, grid, s) : bwd_dims_pre<T, DQK, DV, false>(a, grid, s);
+}
+
 hipError_t launch_attn_bwd(const hstu_desc& d, const int64_t* off, const int32_t* ncand, int32_t B, int64_t T,
                            const int64_t* ts, const hstu_bias_tables& tab, const void* q, const void* k,
-                           const void* v, const void* dout, float* dact, float* tab_part, float* gpos,
-                           float* gtime, const AttnScratch& sc, hipStream_t s) {
+                           const void* v, const void* dout, float* dact, const void* pre, void* dpre,
+                           float* tab_part, float* gpos, float* gtime, const AttnScratch& sc, hipStream_t s) {
   if (T == 0) return hipSuccess;
   BwdArgs a;
   a.off = off;
@@ -1127,6 +1161,8 @@ hipError_t launch_attn_bwd(const hstu_desc& d, const int64_t* off, const int32_t
   a.v = v;
   a.dout = dout;
   a.dact = dact;
+  a.pre = pre;
+  a.dpre = dpre;
   a.tab_part = tab_part;
   a.tiles = sc.tiles;
   a.tbase = sc.tbase;

@@ -234,8 +234,9 @@ __global__ __launch_bounds__(256) void gate_bwd_kernel(const float* __restrict__
                                                        const T* __restrict__ av, const float* __restrict__ stats,
                                                        const T* __restrict__ g, const T* __restrict__ be,
                                                        int64_t M, int H, int dv, float eps, int64_t n1,
-                                                       float* __restrict__ du, T* __restrict__ dav,
-                                                       float* __restrict__ gpart, float* __restrict__ bpart) {
+                                                       const T* __restrict__ pre, T* __restrict__ dpre,
+                                                       T* __restrict__ dav, float* __restrict__ gpart,
+                                                       float* __restrict__ bpart) {
   // a lane takes 8 consecutive columns of one head per step (dv a multiple of 8)
   extern __shared__ float red[];  // [2][4 waves][K]
   constexpr int NC = kBwdRowCols / 512;
@@ -277,94 +278,29 @@ __global__ __launch_bounds__(256) void gate_bwd_kernel(const float* __restrict__
       const int c = lane * 8 + 512 * j;
       if (c >= K) break;
       const float off = __shfl(dm, c / dv, kWave);
-      float b8[8], o_du[8], o_dav[8];
+      float b8[8], p8[8], o_du[8], o_dav[8];
       load8(av + o + c, a8);
       load8(dz + o + c, z8);
       load8(u + o + c, u8);
       load8(g + c, g8);
       load8(be + c, b8);
+      load8(pre + row * n1 + c, p8);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float nh = (a8[e] + off) * rstd;
         const float dn = z8[e] * u8[e];
-        o_du[e] = z8[e] * (nh * g8[e] + b8[e]);
+        o_du[e] = z8[e] * (nh * g8[e] + b8[e]) * silu_grad(p8[e]);
         o_dav[e] = rstd * (dn * g8[e] - m1 - nh * mm);
         ga[j][e] += dn * nh;
         ba[j][e] += dn;
       }
-      store8(du + row * n1 + c, o_du);
+      store8(dpre + row * n1 + c, o_du);
       store8(dav + o + c, o_dav);
     }
   }
   chunk_partials(ga, ba, K, red, gpart, bpart);
 }
 
-// The SiLU backward of f1 from the forward's saved pre-activation z:
-// dpre = dact * SiLU'(z) in the layer dtype, with db1's column sums.  A
-// workgroup takes kColRows rows and 512 columns; each thread 8 consecutive
-// columns (16-byte accesses for bf16) of 32 rows, in order, four row groups
-// per workgroup.  The row groups' column sums are added in order into
-// part[chunk][col], which colsum_chunks_kernel then sums over the chunks.
-// N is a multiple of 8.
-template <typename T>
-__global__ __launch_bounds__(256) void silu_bwd_kernel(const float* __restrict__ dact, const T* __restrict__ pre,
-                                                       int64_t M, int N, T* __restrict__ dpre,
-                                                       float* __restrict__ part) {
-  static_assert(kColRows == 128, "four row groups of 32 rows");
-  __shared__ float red[4][512];
-  const int ncb = (N + 511) / 512;
-  const int64_t chunk = blockIdx.x / ncb;
-  const int cg = threadIdx.x & 63, rg = threadIdx.x >> 6;
-  const int col = (int)(blockIdx.x % ncb) * 512 + 8 * cg;
-  const int64_t r0 = chunk * kColRows + 32 * rg;
-  float cs[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  if (col < N) {
-#pragma unroll 4
-    for (int i = 0; i < 32; ++i) {
-      const int64_t row = r0 + i;
-      if (row < M) {
-        const float* gp = dact + row * N + col;
-        const float4 g0 = *reinterpret_cast<const float4*>(gp), g1 = *reinterpret_cast<const float4*>(gp + 4);
-        const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-        float zv[8];
-        if constexpr (sizeof(T) == 2) {
-          const uint4 zr = *reinterpret_cast<const uint4*>(pre + row * N + col);
-          const T* z8 = reinterpret_cast<const T*>(&zr);
-#pragma unroll
-          for (int q = 0; q < 8; ++q) zv[q] = to_f32(z8[q]);
-        } else {
-          const float4 z0 = *reinterpret_cast<const float4*>(pre + row * N + col);
-          const float4 z1 = *reinterpret_cast<const float4*>(pre + row * N + col + 4);
-          zv[0] = z0.x, zv[1] = z0.y, zv[2] = z0.z, zv[3] = z0.w;
-          zv[4] = z1.x, zv[5] = z1.y, zv[6] = z1.z, zv[7] = z1.w;
-        }
-        T out[8];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const float z = zv[q];
-          const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z * -1.4426950408889634f));
-          const float d = gv[q] * sg * (1.0f + z * (1.0f - sg));
-          cs[q] += d;
-          out[q] = from_f32<T>(d);
-        }
-        T* dst = dpre + row * N + col;
-        if constexpr (sizeof(T) == 2) {
-          *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(out);
-        } else {
-          *reinterpret_cast<float4*>(dst) = *reinterpret_cast<const float4*>(out);
-          *reinterpret_cast<float4*>(dst + 4) = *reinterpret_cast<const float4*>(out + 4);
-        }
-      }
-    }
-  }
-#pragma unroll
-  for (int q = 0; q < 8; ++q) red[rg][8 * cg + q] = cs[q];
-  __syncthreads();
-  for (int c = threadIdx.x; c < 512; c += 256) {
-    const int gc = (int)(blockIdx.x % ncb) * 512 + c;
-    if (gc < N) part[chunk * N + gc] = ((red[0][c] + red[1][c]) + red[2][c]) + red[3][c];
-  }
-}
 
 // One wave per row (eight consecutive rows per wave, as above).  With the
 // input LayerNorm: x^ = (x - mean) rstd,
@@ -769,8 +705,8 @@ hipError_t launch_gemm_nt_f32(hstu_dtype dt, const void* A, const void* Bm, floa
 }
 
 hipError_t launch_gate_bwd(const hstu_desc& d, int64_t T, const hstu_weights& w, const float* dz, const void* u,
-                           const void* av, const float* stats, float* du, void* dav, float* gpart, float* bpart,
-                           float* dg, float* db, hipStream_t s) {
+                           const void* av, const float* stats, const void* pre, void* dpre, void* dav, float* gpart,
+                           float* bpart, float* dg, float* db, hipStream_t s) {
   const int K = d.num_heads * d.dv;
   if (K % 8 != 0 || K > kBwdRowCols) return hipErrorInvalidValue;
   const int64_t n1 = 2 * (int64_t)d.num_heads * (d.dqk + d.dv);
@@ -780,12 +716,12 @@ hipError_t launch_gate_bwd(const hstu_desc& d, int64_t T, const hstu_weights& w,
     const size_t shmem = (size_t)8 * K * sizeof(float);
     if (d.dtype == HSTU_BF16)
       hipLaunchKernelGGL(gate_bwd_kernel<bf16>, grid, block, shmem, s, dz, (const bf16*)u, (const bf16*)av, stats,
-                         (const bf16*)w.ln_av_g, (const bf16*)w.ln_av_b, T, d.num_heads, d.dv, d.ln_eps, n1, du,
-                         (bf16*)dav, gpart, bpart);
+                         (const bf16*)w.ln_av_g, (const bf16*)w.ln_av_b, T, d.num_heads, d.dv, d.ln_eps, n1,
+                         (const bf16*)pre, (bf16*)dpre, (bf16*)dav, gpart, bpart);
     else
       hipLaunchKernelGGL(gate_bwd_kernel<float>, grid, block, shmem, s, dz, (const float*)u, (const float*)av, stats,
-                         (const float*)w.ln_av_g, (const float*)w.ln_av_b, T, d.num_heads, d.dv, d.ln_eps, n1, du,
-                         (float*)dav, gpart, bpart);
+                         (const float*)w.ln_av_g, (const float*)w.ln_av_b, T, d.num_heads, d.dv, d.ln_eps, n1,
+                         (const float*)pre, (float*)dpre, (float*)dav, gpart, bpart);
   }
   const dim3 cg((unsigned)((K + 63) / 64)), cb(64 * kColGroups);
   hipLaunchKernelGGL(colsum_chunks_kernel, cg, cb, 0, s, (const float*)gpart, chunks, (int64_t)K, dg);
@@ -793,23 +729,6 @@ hipError_t launch_gate_bwd(const hstu_desc& d, int64_t T, const hstu_weights& w,
   return hipGetLastError();
 }
 
-hipError_t launch_silu_bwd(hstu_dtype dt, const float* dact, const void* pre, int64_t T, int n1, void* dpre,
-                           float* part, float* db1, hipStream_t s) {
-  if (n1 % 8 != 0) return hipErrorInvalidValue;
-  const int64_t chunks = (T + kColRows - 1) / kColRows;
-  if (chunks > 0) {
-    const dim3 grid((unsigned)(chunks * ((n1 + 511) / 512)));
-    if (dt == HSTU_BF16)
-      hipLaunchKernelGGL(silu_bwd_kernel<bf16>, grid, dim3(256), 0, s, dact, (const bf16*)pre, T, n1, (bf16*)dpre,
-                         part);
-    else
-      hipLaunchKernelGGL(silu_bwd_kernel<float>, grid, dim3(256), 0, s, dact, (const float*)pre, T, n1,
-                         (float*)dpre, part);
-  }
-  hipLaunchKernelGGL(colsum_chunks_kernel, dim3((unsigned)((n1 + 63) / 64)), dim3(64 * kColGroups), 0, s,
-                     (const float*)part, chunks, (int64_t)n1, db1);
-  return hipGetLastError();
-}
 
 hipError_t launch_ln_bwd(const hstu_desc& d, const void* x, const float* dxn, const hstu_weights& w, const void* dy,
                          int64_t T, void* dx, float* gpart, float* bpart, float* dg, float* db, hipStream_t s) {

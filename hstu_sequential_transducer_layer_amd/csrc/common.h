@@ -105,6 +105,12 @@ __device__ __forceinline__ float silu(float z) {
   return z * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
+// SiLU'(z) = sigmoid(z) (1 + z (1 - sigmoid(z))).
+__device__ __forceinline__ float silu_grad(float z) {
+  const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z * -1.4426950408889634f));
+  return sg * (1.0f + z * (1.0f - sg));
+}
+
 // -log2(e) * SiLU(s + b), given bn = -log2(e) * b: z' = -log2(e) (s + b) in one
 // fused multiply-add, then z' / (1 + 2^z').  Callers fold the constant
 // -ln(2) = 1 / -log2(e) into a later scale.

@@ -182,10 +182,13 @@ hipError_t launch_gather_rows(const void* src, int64_t src_rows, int64_t row_byt
 
 // --- attn_bwd.hip: dq, dv, dk into dact (fp32 [T, N1], columns of the
 // u|v|q|k split) and the bias-table gradients (tab_part: [max items * H][P + NB]).
+// With pre (the forward's saved pre-activation [T, N1], layer dtype) the
+// gradients go out times SiLU'(pre) into dpre (same layout and dtype) instead
+// of into dact.
 hipError_t launch_attn_bwd(const hstu_desc& d, const int64_t* off, const int32_t* ncand, int32_t B, int64_t T,
                            const int64_t* ts, const hstu_bias_tables& tab, const void* q, const void* k,
-                           const void* v, const void* dout, float* dact, float* tab_part, float* gpos,
-                           float* gtime, const AttnScratch& sc, hipStream_t s);
+                           const void* v, const void* dout, float* dact, const void* pre, void* dpre,
+                           float* tab_part, float* gpos, float* gtime, const AttnScratch& sc, hipStream_t s);
 // C [M, N] = A^T B (fp32) over K rows of the row-major bf16 A [K, M] and
 // B [K, N] (M, N multiples of 8): weight gradients over the token dimension
 // without transposed copies; split over K into split_buf (split_cap floats)
@@ -207,14 +210,12 @@ hipError_t launch_gemm_nt_f32(hstu_dtype dt, const void* A, const void* Bm, floa
                               float* split_buf, hipStream_t s);
 // gpart, bpart: ceil(T / 32) x H*dv partial rows of the LayerNorm_av gain and
 // offset gradients, summed into dg, db.
+// dU goes out as its pre-activation gradient dU * SiLU'(pre) into the u
+// columns of dpre [T, N1] (layer dtype), pre the forward's saved
+// pre-activation.
 hipError_t launch_gate_bwd(const hstu_desc& d, int64_t T, const hstu_weights& w, const float* dz, const void* u,
-                           const void* av, const float* stats, float* du, void* dav, float* gpart, float* bpart,
-                           float* dg, float* db, hipStream_t s);
-// dpre = dact * SiLU'(pre) in the layer dtype, pre the forward's saved
-// pre-activation [T, n1] (n1 a multiple of 8), and db1 = the column sums of
-// dpre (part: colsum_tmp_bytes(T, n1) of scratch).
-hipError_t launch_silu_bwd(hstu_dtype dt, const float* dact, const void* pre, int64_t T, int n1, void* dpre,
-                           float* part, float* db1, hipStream_t s);
+                           const void* av, const float* stats, const void* pre, void* dpre, void* dav, float* gpart,
+                           float* bpart, float* dg, float* db, hipStream_t s);
 // gpart, bpart: ceil(T / 32) x d_model partial rows of the LayerNorm_in gain
 // and offset gradients, summed into dg, db (zero without HSTU_INPUT_NORM).
 hipError_t launch_ln_bwd(const hstu_desc& d, const void* x, const float* dxn, const hstu_weights& w, const void* dy,
