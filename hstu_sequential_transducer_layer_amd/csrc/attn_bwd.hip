@@ -342,10 +342,11 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
     for (int i = tid; i < P + NB; i += 256) part[i] = 0.f;
     return;
   }
+  // the tables times -log2(e): the weight step works on x = -log2(e) S
   for (int i = tid; i < P; i += 256)
-    pos_s[i] = to_f32(reinterpret_cast<const T*>(a.pos_tab)[(int64_t)h * a.pos_stride + i]);
+    pos_s[i] = kNegLog2e * to_f32(reinterpret_cast<const T*>(a.pos_tab)[(int64_t)h * a.pos_stride + i]);
   for (int i = tid; i < NB; i += 256)
-    time_s[i] = to_f32(reinterpret_cast<const T*>(a.time_tab)[(int64_t)h * a.time_stride + i]);
+    time_s[i] = kNegLog2e * to_f32(reinterpret_cast<const T*>(a.time_tab)[(int64_t)h * a.time_stride + i]);
   for (int i = tid; i < 4 * (P + NB); i += 256) tabs[P + NB + i] = 0.f;
   float* gpos = tabs + (P + NB) * (1 + wave_id());
   float* gtime = gpos + P;
@@ -475,6 +476,15 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
       }
       mode = __builtin_amdgcn_readfirstlane(mode);
     }
+    // dS_ij N_b = dA_ij SiLU'(S_ij) from x = -log2(e) S_ij: sg = 1 / (1 + 2^x),
+    // SiLU'(S) = sg + S sg (1 - sg) = (x sg) ln2 (sg - 1) + sg; a masked pair
+    // gets x = 1e30 (sg = 0, dS = 0).  1 / N_b is applied to dQ and to the
+    // table-gradient row at the end.  The dQ columns of rows past the tile
+    // are never stored, so only their table-gradient sums are masked.
+    auto dsv = [](float d, float x) __attribute__((always_inline)) {
+      const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x));
+      return d * __builtin_fmaf(x * sg, __builtin_fmaf(sg, -kNegLn2, kNegLn2), sg);
+    };
     // time-bucket gradient runs: a lane's buckets only fall as its keys advance
     auto add_run = [&](int bt, float v) __attribute__((always_inline)) {
       if (bt != run_bt) {
@@ -497,10 +507,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
         const int bp = pos_bucket(p_q, position(j, nh, shared), R);
         const int bt = SMALL ? time_bucket_small((int)((uint32_t)ts_q - (uint32_t)tk[r]), NB, a.sbits)
                              : time_bucket(wrap_sub(ts_q, tk[r]), NB, a.sbits);
-        const float s = sc[r] + pos_s[bp] + time_s[bt];
-        const float sg = bwd_sigmoid(s);
-        const float g = da[r] * sg * (1.0f + s * (1.0f - sg)) * inv_n;
-        ds[r] = valid ? g : 0.f;
+        const float g = dsv(da[r], valid ? __builtin_fmaf(sc[r], kNegLog2e, pos_s[bp] + time_s[bt]) : 1e30f);
+        ds[r] = g;
         if (valid) {
           if (bp == 0)
             far_lo += g;
@@ -532,11 +540,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
         float sum = 0.f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float s = sc[r] + b_lo;
-          const float sg = bwd_sigmoid(s);
-          ds[r] = qvalid ? da[r] * sg * (1.0f + s * (1.0f - sg)) * inv_n : 0.f;
+          ds[r] = dsv(da[r], __builtin_fmaf(sc[r], kNegLog2e, b_lo));
           sum += ds[r];
         }
+        sum = qvalid ? sum : 0.f;
         far_hi += sum;
         add_run(bt_lo, sum);
       } else if (mode == 1) {
@@ -546,12 +553,12 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const bool up = tk[r] <= tcut;
-          const float s = sc[r] + (up ? b_hi : b_lo);
-          const float sg = bwd_sigmoid(s);
-          ds[r] = qvalid ? da[r] * sg * (1.0f + s * (1.0f - sg)) * inv_n : 0.f;
+          ds[r] = dsv(da[r], __builtin_fmaf(sc[r], kNegLog2e, up ? b_hi : b_lo));
           sum_hi += up ? ds[r] : 0.f;
           sum_lo += up ? 0.f : ds[r];
         }
+        sum_hi = qvalid ? sum_hi : 0.f;
+        sum_lo = qvalid ? sum_lo : 0.f;
         far_hi += sum_hi + sum_lo;
         add_run(bt_hi, sum_hi);
         add_run(bt_lo, sum_lo);
@@ -599,8 +606,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
     for (int n = 0; n < DQK / 32; ++n)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4)
-        bwd_out4<T, PRE>(a, dst + 32 * n + 8 * g4, dq[n][4 * g4], dq[n][4 * g4 + 1], dq[n][4 * g4 + 2],
-                         dq[n][4 * g4 + 3]);
+        bwd_out4<T, PRE>(a, dst + 32 * n + 8 * g4, inv_n * dq[n][4 * g4], inv_n * dq[n][4 * g4 + 1],
+                         inv_n * dq[n][4 * g4 + 2], inv_n * dq[n][4 * g4 + 3]);
   }
   if (run != 0.f) atomicAdd(&gtime[run_bt], run);
   if (far_lo != 0.f) atomicAdd(&gpos[0], far_lo);
@@ -608,7 +615,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
   __syncthreads();  // every LDS histogram update is done
   for (int i = tid; i < P + NB; i += 256) {
     const float* hw = tabs + (P + NB) + i;
-    part[i] = ((hw[0] + hw[P + NB]) + hw[2 * (P + NB)]) + hw[3 * (P + NB)];
+    part[i] = inv_n * (((hw[0] + hw[P + NB]) + hw[2 * (P + NB)]) + hw[3 * (P + NB)]);
   }
 }
 
