@@ -14,6 +14,8 @@
 //   gemm_silu_bwd_kernel  pre = x~ W1^T on MFMA, kept on chip (LDS); dpre =
 //                         d(u|v|q|k) * SiLU'(pre + b1) and db1's row-chunk sums
 //   ln_bwd_kernel         one wave per row: dx through LayerNorm_in (+ dY)
+#include <type_traits>
+
 #include "common.h"
 #include "gemm.h"
 #include "gemm2.h"
@@ -197,16 +199,29 @@ __global__ __launch_bounds__(64 * kColGroups) void colsum_chunks_kernel(const fl
 // workgroup, which colsum_chunks_kernel then sums over the workgroups; so
 // the [T, columns] term arrays are never written.  Columns (H * dv, d_model):
 // a multiple of 8, at most kBwdRowCols.
+// NC = ceil(columns / 512) chunks of 8 columns per lane: the per-lane
+// accumulators of the parameters' gradients are sized for the layer's width.
 constexpr int kRowsPerWave = 8, kChunkRows = 4 * kRowsPerWave, kBwdRowCols = 2048;
+
+// Runs f(std::integral_constant<int, NC>) for the chunk count of K columns.
+template <typename F>
+static void with_chunks(int K, F f) {
+  if (K <= 512)
+    f(std::integral_constant<int, 1>{});
+  else if (K <= 1024)
+    f(std::integral_constant<int, 2>{});
+  else
+    f(std::integral_constant<int, 4>{});
+}
 
 // The partial rows of the two terms accumulated by each wave (lane: columns
 // lane * 8 + 512 j .. + 7): written to LDS, then added in wave order.
-__device__ __forceinline__ void chunk_partials(const float (&ga)[kBwdRowCols / 512][8],
-                                               const float (&ba)[kBwdRowCols / 512][8], int K, float* red,
+template <int NC>
+__device__ __forceinline__ void chunk_partials(const float (&ga)[NC][8], const float (&ba)[NC][8], int K, float* red,
                                                float* __restrict__ gpart, float* __restrict__ bpart) {
   const int lane = threadIdx.x & 63, w = wave_id();
 #pragma unroll
-  for (int j = 0; j < kBwdRowCols / 512; ++j) {
+  for (int j = 0; j < NC; ++j) {
     const int c = lane * 8 + 512 * j;
     if (c < K) {
 #pragma unroll
@@ -229,7 +244,7 @@ __device__ __forceinline__ void chunk_partials(const float (&ga)[kBwdRowCols / 5
 //   n^ = (AV - mean) * rstd,  dn = dZ * U,  dn^ = dn * g
 //   dU = dZ * (n^ g + b),  dAV = rstd (dn^ - mean(dn^) - n^ mean(dn^ n^))
 // and the workgroup's partial sums of dn * n^ and dn (the terms of dg and db).
-template <typename T>
+template <typename T, int NC>
 __global__ __launch_bounds__(256) void gate_bwd_kernel(const float* __restrict__ dz, const T* __restrict__ u,
                                                        const T* __restrict__ av, const float* __restrict__ stats,
                                                        const T* __restrict__ g, const T* __restrict__ be,
@@ -239,7 +254,6 @@ __global__ __launch_bounds__(256) void gate_bwd_kernel(const float* __restrict__
                                                        float* __restrict__ bpart) {
   // a lane takes 8 consecutive columns of one head per step (dv a multiple of 8)
   extern __shared__ float red[];  // [2][4 waves][K]
-  constexpr int NC = kBwdRowCols / 512;
   const int lane = threadIdx.x & 63, w = wave_id();
   const int K = H * dv;
   float ga[NC][8], ba[NC][8];
@@ -307,7 +321,7 @@ __global__ __launch_bounds__(256) void gate_bwd_kernel(const float* __restrict__
 // dx = rstd (dxn g - mean(dxn g) - x^ mean(dxn g x^)); else dx = dxn.  Plus dY
 // for the residual.  With the LayerNorm, the workgroup's partial sums of
 // dxn * x^ and dxn (the terms of its gain's and offset's gradients).
-template <typename T>
+template <typename T, int NC>
 __global__ __launch_bounds__(256) void ln_bwd_kernel(const T* __restrict__ x, const float* __restrict__ dxn,
                                                      const T* __restrict__ g, const T* __restrict__ dy, int64_t M,
                                                      int d, float eps, int norm, int residual, T* __restrict__ dx,
@@ -315,7 +329,6 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(const T* __restrict__ x, co
   // a lane takes 8 consecutive columns per step (16-byte accesses for bf16),
   // d a multiple of 8
   extern __shared__ float red[];  // [2][4 waves][d]
-  constexpr int NC = kBwdRowCols / 512;
   const int lane = threadIdx.x & 63, w = wave_id();
   float ga[NC][8], ba[NC][8];
 #pragma unroll
@@ -714,14 +727,17 @@ hipError_t launch_gate_bwd(const hstu_desc& d, int64_t T, const hstu_weights& w,
   if (chunks > 0) {
     const dim3 grid((unsigned)chunks), block(256);
     const size_t shmem = (size_t)8 * K * sizeof(float);
-    if (d.dtype == HSTU_BF16)
-      hipLaunchKernelGGL(gate_bwd_kernel<bf16>, grid, block, shmem, s, dz, (const bf16*)u, (const bf16*)av, stats,
-                         (const bf16*)w.ln_av_g, (const bf16*)w.ln_av_b, T, d.num_heads, d.dv, d.ln_eps, n1,
-                         (const bf16*)pre, (bf16*)dpre, (bf16*)dav, gpart, bpart);
-    else
-      hipLaunchKernelGGL(gate_bwd_kernel<float>, grid, block, shmem, s, dz, (const float*)u, (const float*)av, stats,
-                         (const float*)w.ln_av_g, (const float*)w.ln_av_b, T, d.num_heads, d.dv, d.ln_eps, n1,
-                         (const float*)pre, (float*)dpre, (float*)dav, gpart, bpart);
+    with_chunks(K, [&](auto nc) {
+      constexpr int NC = decltype(nc)::value;
+      if (d.dtype == HSTU_BF16)
+        hipLaunchKernelGGL((gate_bwd_kernel<bf16, NC>), grid, block, shmem, s, dz, (const bf16*)u, (const bf16*)av,
+                           stats, (const bf16*)w.ln_av_g, (const bf16*)w.ln_av_b, T, d.num_heads, d.dv, d.ln_eps, n1,
+                           (const bf16*)pre, (bf16*)dpre, (bf16*)dav, gpart, bpart);
+      else
+        hipLaunchKernelGGL((gate_bwd_kernel<float, NC>), grid, block, shmem, s, dz, (const float*)u, (const float*)av,
+                           stats, (const float*)w.ln_av_g, (const float*)w.ln_av_b, T, d.num_heads, d.dv, d.ln_eps,
+                           n1, (const float*)pre, (float*)dpre, (float*)dav, gpart, bpart);
+    });
   }
   const dim3 cg((unsigned)((K + 63) / 64)), cb(64 * kColGroups);
   hipLaunchKernelGGL(colsum_chunks_kernel, cg, cb, 0, s, (const float*)gpart, chunks, (int64_t)K, dg);
@@ -739,12 +755,17 @@ hipError_t launch_ln_bwd(const hstu_desc& d, const void* x, const float* dxn, co
   if (chunks > 0) {
     const dim3 grid((unsigned)chunks), block(256);
     const size_t shmem = (size_t)8 * dm * sizeof(float);
-    if (d.dtype == HSTU_BF16)
-      hipLaunchKernelGGL(ln_bwd_kernel<bf16>, grid, block, shmem, s, (const bf16*)x, dxn, (const bf16*)w.ln_in_g,
-                         (const bf16*)dy, T, dm, d.ln_eps, norm, res, (bf16*)dx, gpart, bpart);
-    else
-      hipLaunchKernelGGL(ln_bwd_kernel<float>, grid, block, shmem, s, (const float*)x, dxn, (const float*)w.ln_in_g,
-                         (const float*)dy, T, dm, d.ln_eps, norm, res, (float*)dx, gpart, bpart);
+    with_chunks(dm, [&](auto nc) {
+      constexpr int NC = decltype(nc)::value;
+      if (d.dtype == HSTU_BF16)
+        hipLaunchKernelGGL((ln_bwd_kernel<bf16, NC>), grid, block, shmem, s, (const bf16*)x, dxn,
+                           (const bf16*)w.ln_in_g, (const bf16*)dy, T, dm, d.ln_eps, norm, res, (bf16*)dx, gpart,
+                           bpart);
+      else
+        hipLaunchKernelGGL((ln_bwd_kernel<float, NC>), grid, block, shmem, s, (const float*)x, dxn,
+                           (const float*)w.ln_in_g, (const float*)dy, T, dm, d.ln_eps, norm, res, (float*)dx, gpart,
+                           bpart);
+    });
   }
   // without the input LayerNorm its parameters get zero gradients
   const dim3 cg((unsigned)((dm + 63) / 64)), cb(64 * kColGroups);
