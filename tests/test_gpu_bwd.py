@@ -13,6 +13,8 @@ so they cancel heavily: rounding only dL/dAV to bf16 inside the float64
 oracle already moves the position table's gradient by 3.5e-2 of its rms on
 the 8 x 128/128 case (shown on the CPU), hence 1e-1 for those two in bf16."""
 
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -95,6 +97,9 @@ def test_bwd_long_128_bf16():
 
 
 FAR_FP32 = synth.LayerDims(64, 2, 32, 32, time_buckets=128, time_sub_bits=1, dtype="fp32")
+# the same in bf16: the bf16 kernels (the merged dK/dV pass on 16 x 16 tiles)
+# at head width 32
+FAR_BF16 = dataclasses.replace(FAR_FP32, dtype="bf16")
 
 
 def _far_block_kinds(w):
@@ -122,30 +127,41 @@ def _far_block_kinds(w):
     return kinds
 
 
-def test_bwd_far_block_modes_fp32():
+def _far_modes_workload(dims):
     # long histories and two sub-buckets per octave: far blocks with one time
     # bucket per row, with two adjacent ones (per-key split), and with more
-    w = synth.make_workload("small_fp32", seed=7, lengths=[640, 450], candidates=[0, 0], dims=FAR_FP32)
-    kinds = _far_block_kinds(w)
-    say(f"backward, far-block modes fp32: lengths {w.lengths().tolist()}, far blocks {kinds}")
-    assert kinds["one"] > 0 and kinds["two"] > 0
-    _check_grads(w, seed=8)
+    return synth.make_workload("small_fp32", seed=7, lengths=[640, 450], candidates=[0, 0], dims=dims)
 
 
-def test_bwd_far_block_time_overflow_fp32():
+def _time_overflow_workload(dims):
     # a far block whose time span overflows int64 differences: key 0 at the
     # earliest representable time, the queries one second past the epoch, so
     # the span's endpoints both give bucket 0 while the keys in between are
     # 100+ seconds back; the per-pair path must take it (pairwise differences
     # wrap as in the oracle)
-    w = synth.make_workload("small_fp32", seed=9, lengths=[300], candidates=[0], dims=FAR_FP32)
+    w = synth.make_workload("small_fp32", seed=9, lengths=[300], candidates=[0], dims=dims)
     ts = np.zeros(w.T, np.int64)
     ts[0] = np.iinfo(np.int64).min + 1
     ts[1] = 5
     ts[2:64] = -100 - np.arange(62)
     ts[128:] = 1
     w.timestamps = ts
-    say(f"backward, int64-overflowing far block fp32: lengths {w.lengths().tolist()}")
+    return w
+
+
+@pytest.mark.parametrize("dims", [FAR_FP32, FAR_BF16], ids=["fp32", "bf16"])
+def test_bwd_far_block_modes(dims):
+    w = _far_modes_workload(dims)
+    kinds = _far_block_kinds(w)
+    say(f"backward, far-block modes {dims.dtype}: lengths {w.lengths().tolist()}, far blocks {kinds}")
+    assert kinds["one"] > 0 and kinds["two"] > 0
+    _check_grads(w, seed=8)
+
+
+@pytest.mark.parametrize("dims", [FAR_FP32, FAR_BF16], ids=["fp32", "bf16"])
+def test_bwd_far_block_time_overflow(dims):
+    w = _time_overflow_workload(dims)
+    say(f"backward, int64-overflowing far block {dims.dtype}: lengths {w.lengths().tolist()}")
     _check_grads(w, seed=10)
 
 
@@ -239,7 +255,8 @@ def test_bwd_stack8_full_size():
         assert e <= tol, k
 
 
-@pytest.mark.parametrize("case", ["edge_fp32", "edge_bf16_64", "zipf_bf16", "sl_128_bf16"])
+@pytest.mark.parametrize("case", ["edge_fp32", "edge_bf16_64", "zipf_bf16", "sl_128_bf16", "far_modes_bf16_32",
+                                  "time_overflow_bf16_32"])
 def test_attention_stage_backward(case):
     """hstu_attn_bwd fed the GPU's own q, k, v and a bf16 dL/dAV, against the
     float64 autograd of the attention alone fed the same values: the stage's
@@ -257,6 +274,10 @@ def test_attention_stage_backward(case):
                                 candidates=[0, 1, 0, 5, 129, 0, 70, 64, 2], dims=BF16_64, random_ln=True)
     elif case == "zipf_bf16":
         w = synth.make_workload("zipf_bf16", batch=6)
+    elif case == "far_modes_bf16_32":
+        w = _far_modes_workload(FAR_BF16)
+    elif case == "time_overflow_bf16_32":
+        w = _time_overflow_workload(FAR_BF16)
     else:
         w = synth.make_workload("sl_train", batch=2, lengths=[700, 300], dims=synth.WORKLOADS["sl_train"].dims)
     dev = layer.to_device(w)
