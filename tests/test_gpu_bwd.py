@@ -89,6 +89,23 @@ def test_bwd_zipf_bf16_subset():
     _check_grads(w, seed=3)
 
 
+# The widest layers the backward accepts: H * dv = 2048 (the gate's LayerNorm
+# backward at its widest row) and d_model = 2048 (the input LayerNorm's).
+# fp32 (head widths up to 64) checks the same paths at 1e-3.
+WIDE = {"heads_2048_bf16": synth.LayerDims(64, 16, 128, 128, pos_buckets=33, time_buckets=32, dtype="bf16"),
+        "model_2048_bf16": synth.LayerDims(2048, 2, 32, 32, pos_buckets=33, time_buckets=32, dtype="bf16"),
+        "heads_2048_fp32": synth.LayerDims(64, 32, 64, 64, pos_buckets=33, time_buckets=32, dtype="fp32"),
+        "model_2048_fp32": synth.LayerDims(2048, 2, 32, 32, pos_buckets=33, time_buckets=32, dtype="fp32")}
+
+
+@pytest.mark.parametrize("name", sorted(WIDE))
+def test_bwd_widest_rows(name):
+    w = synth.make_workload("small_fp32", seed=11, lengths=[150, 0, 97], candidates=[0, 0, 5], dims=WIDE[name],
+                            random_ln=True)
+    say(f"backward, {name}: lengths {w.lengths().tolist()}")
+    _check_grads(w, seed=12)
+
+
 def test_bwd_long_128_bf16():
     dims = synth.WORKLOADS["sl_train"].dims
     w = synth.make_workload("sl_train", batch=2, lengths=[700, 300], dims=dims)
