@@ -894,18 +894,22 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kv16_kernel(BwdArgs a) {
   const bool shared = a.shared_pos != 0;
   const int K2 = H * DV;
 
+  // S and dA contract over the head dimension in the chunk order kv_chunk:
+  // k-step c takes 16-byte chunk c + (D / 32) g for lane group g, which keeps
+  // the 16-row reads of Q and dO free of bank conflicts (adjacent chunks per
+  // group conflict two-way under kv_swz, measured); K and V use the same order
   bf16x8 kf[DQK / 32], vf[DV / 32];
   const T* krow = reinterpret_cast<const T*>(a.k) + ((int64_t)h * a.T + s0 + jk) * DQK;
   const T* vrow = reinterpret_cast<const T*>(a.v) + ((int64_t)h * a.T + s0 + jk) * DV;
 #pragma unroll
   for (int c = 0; c < DQK / 32; ++c) {
     kf[c] = bf16x8{};
-    if (kvalid) kf[c] = bwd_global_frag<T>(krow + 32 * c + 8 * g);
+    if (kvalid) kf[c] = bwd_global_frag<T>(krow + 8 * (c + (DQK / 32) * g));
   }
 #pragma unroll
   for (int c = 0; c < DV / 32; ++c) {
     vf[c] = bf16x8{};
-    if (kvalid) vf[c] = bwd_global_frag<T>(vrow + 32 * c + 8 * g);
+    if (kvalid) vf[c] = bwd_global_frag<T>(vrow + 8 * (c + (DV / 32) * g));
   }
   const int p_k = position(jk, nh, shared);
   const int64_t ts_k = kvalid ? a.ts[s0 + jk] : 0;
@@ -927,9 +931,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kv16_kernel(BwdArgs a) {
   ocopy.init(w, lane);
   int roq[DQK / 32], rov[DV / 32], coq[DQK / 16], cov[DV / 16];  // per-lane LDS offsets
 #pragma unroll
-  for (int c = 0; c < DQK / 32; ++c) roq[c] = KvTile<DQK>::at(l16, 32 * c + 8 * g);
+  for (int c = 0; c < DQK / 32; ++c) roq[c] = KvTile<DQK>::at(l16, 8 * (c + (DQK / 32) * g));
 #pragma unroll
-  for (int c = 0; c < DV / 32; ++c) rov[c] = KvTile<DV>::at(l16, 32 * c + 8 * g);
+  for (int c = 0; c < DV / 32; ++c) rov[c] = KvTile<DV>::at(l16, 8 * (c + (DV / 32) * g));
 #pragma unroll
   for (int ft = 0; ft < DQK / 16; ++ft) coq[ft] = kv_col_off<DQK>(lane, ft);
 #pragma unroll
