@@ -242,7 +242,7 @@ struct ElemCtx {
   int64_t ts_q;
   const float* pos_s;
   const float* time_s;
-  const int32_t* rel_s;  // the block's key offsets, from key jq
+  int rel_off;           // MODES 1, 2: jq - j0, the index of key jq in the block's offsets
   const int64_t* ts;     // MODE 3: the sequence's timestamps (global)
 };
 
@@ -278,11 +278,15 @@ __device__ __forceinline__ float elem_bias(const ElemCtx& x, int c, int32_t rel,
          x.pos_s[pos_bucket(x.p_q, position(j, x.nh, x.shared), x.R)];
 }
 
-// The time offsets of keys kb + 8 g + 0..3 (modes 1 and 2; zeros otherwise).
+// The time offsets of keys kb + 8 g + 0..3 (modes 1 and 2; zeros otherwise)
+// out of the block's offsets rb in LDS.  rb is passed down from the LDS
+// array itself, never through a merged or stored pointer: the compiler can
+// then tell these reads from a global->LDS copy in flight into the other
+// buffer, and does not wait for that copy before them.
 template <int MODE>
-__device__ __forceinline__ void elem_rel4(const ElemCtx& x, int kb, int g, int32_t (&rel)[4]) {
+__device__ __forceinline__ void elem_rel4(const ElemCtx& x, const int32_t* rb, int kb, int g, int32_t (&rel)[4]) {
   if (MODE == 1 || MODE == 2) {
-    const int4 rv = *reinterpret_cast<const int4*>(x.rel_s + kb + 8 * g);
+    const int4 rv = *reinterpret_cast<const int4*>(rb + x.rel_off + kb + 8 * g);
     rel[0] = rv.x; rel[1] = rv.y; rel[2] = rv.z; rel[3] = rv.w;
   } else {
     rel[0] = rel[1] = rel[2] = rel[3] = 0;
@@ -290,11 +294,12 @@ __device__ __forceinline__ void elem_rel4(const ElemCtx& x, int kb, int g, int32
 }
 
 template <int MODE>
-__device__ __forceinline__ void elems(const f32x16& s, float (&p)[16], int kb, const ElemCtx& x) {
+__device__ __forceinline__ void elems(const f32x16& s, float (&p)[16], int kb, const ElemCtx& x,
+                                      const int32_t* rb) {
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     int32_t rel[4];
-    elem_rel4<MODE>(x, kb, g, rel);
+    elem_rel4<MODE>(x, rb, kb, g, rel);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int r = 4 * g + e, c = kb + 8 * g + e;
@@ -309,13 +314,13 @@ __device__ __forceinline__ void elems(const f32x16& s, float (&p)[16], int kb, c
 // Inspection: the biases of this lane's row for both 32-key halves of the
 // block, written at dst[j] for keys j < L (NaN where the pair is masked).
 template <int MODE>
-__device__ __forceinline__ void dump_block(const ElemCtx& x, float* dst, int L) {
+__device__ __forceinline__ void dump_block(const ElemCtx& x, const int32_t* rb, float* dst, int L) {
 #pragma unroll
   for (int kb = 0; kb < 64; kb += 32)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       int32_t rel[4];
-      elem_rel4<MODE>(x, kb, g, rel);
+      elem_rel4<MODE>(x, rb, kb, g, rel);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int c = kb + 8 * g + e, j = x.jq + c;
@@ -366,7 +371,7 @@ __device__ __forceinline__ bool block_active(int j0, const QueryRow& q, const Se
 // overflow-checked 64-bit ones.  The mode-1 threshold and second bias are
 // only formed when mode 1 is chosen.
 __device__ __forceinline__ int classify_block(int j0, int64_t tmin, int64_t tmax, const QueryRow& q,
-                                              const SeqCtx& sq, const int32_t* rb, ElemCtx& x) {
+                                              const SeqCtx& sq, ElemCtx& x) {
   const bool full = (j0 + kAttnBN - 1 <= q.r0) && (j0 + kAttnBN <= sq.nh);
   const int pmax_k = position(min(j0 + kAttnBN - 1, sq.L - 1), sq.nh, sq.shared);
   const bool pos_far = q.pmin_q - pmax_k >= sq.R;  // clamped position bias is constant
@@ -394,7 +399,7 @@ __device__ __forceinline__ int classify_block(int j0, int64_t tmin, int64_t tmax
         x.c_lo = sq.time_s[bt_lo] + sq.cpos_far;
         x.c_hi = sq.time_s[bt_hi] + sq.cpos_far;
         x.thr = hi - bucket_floor_small(max(bt_hi, 1), sq.sbits);
-        x.rel_s = rb + (jq - j0);
+        x.rel_off = jq - j0;
         return 1;
       }
     }
@@ -442,20 +447,21 @@ __device__ __forceinline__ int classify_block(int j0, int64_t tmin, int64_t tmax
     }
   }
   x = ElemCtx{jq, q.iq, sq.nh, q.p_q, sq.R, sq.NB, sq.sbits, sq.L, sq.shared, c_lo, c_hi, thr, (int32_t)hi,
-              q.p_q - jq, q.iq - jq, q.ts_q, sq.pos_s, sq.time_s, rb + (jq - j0), sq.ts};
+              q.p_q - jq, q.iq - jq, q.ts_q, sq.pos_s, sq.time_s, jq - j0, sq.ts};
   return mode;
 }
 
 // Weights of 32-key half kh in the wave's mode.
-__device__ __forceinline__ void half_weights(int mode, const f32x16& sc, float (&p)[16], int kh, const ElemCtx& x) {
+__device__ __forceinline__ void half_weights(int mode, const f32x16& sc, float (&p)[16], int kh, const ElemCtx& x,
+                                             const int32_t* rb) {
   if (mode == 0)
-    elems<0>(sc, p, 32 * kh, x);
+    elems<0>(sc, p, 32 * kh, x, rb);
   else if (mode == 1)
-    elems<1>(sc, p, 32 * kh, x);
+    elems<1>(sc, p, 32 * kh, x, rb);
   else if (mode == 2)
-    elems<2>(sc, p, 32 * kh, x);
+    elems<2>(sc, p, 32 * kh, x, rb);
   else
-    elems<3>(sc, p, 32 * kh, x);
+    elems<3>(sc, p, 32 * kh, x, rb);
 }
 
 // Epilogue of one wave: scale by 1/N_b, per-(row, head) mean and M2 over dv,
@@ -525,8 +531,10 @@ __global__ __launch_bounds__(256, attn_min_blocks((DQK + DV) * (int)sizeof(T) + 
   __shared__ __attribute__((aligned(16))) T Ks1[C::BN * DQK];
   __shared__ __attribute__((aligned(16))) T Vs0[C::BN * DV];
   __shared__ __attribute__((aligned(16))) T Vs1[C::BN * DV];
-  __shared__ __attribute__((aligned(16))) int32_t rel_s[2][C::BN];
-  __shared__ __attribute__((aligned(16))) int32_t kty_s[2][TYPED ? C::BN : 1];
+  __shared__ __attribute__((aligned(16))) int32_t rel_s0[C::BN];
+  __shared__ __attribute__((aligned(16))) int32_t rel_s1[C::BN];
+  __shared__ __attribute__((aligned(16))) int32_t kty_s0[TYPED ? C::BN : 1];
+  __shared__ __attribute__((aligned(16))) int32_t kty_s1[TYPED ? C::BN : 1];
   extern __shared__ float tabs[];  // [P] position, [NB] time, [NT * NT] type table of head h
   float* pos_s = tabs;
   float* time_s = tabs + a.P;
@@ -601,7 +609,7 @@ __global__ __launch_bounds__(256, attn_min_blocks((DQK + DV) * (int)sizeof(T) + 
 
   // Issue the first block's copies before anything else.
   longlong2 tb0 = {0, 0}, tb1 = {0, 0};
-  if (nblk > 0) issue(0, Ks0, Vs0, rel_s[0], kty_s[0], tb0);
+  if (nblk > 0) issue(0, Ks0, Vs0, rel_s0, kty_s0, tb0);
 
   // Bias tables of head h, as fp32 times -log2(e), into LDS (the weights take
   // s * -log2(e) + bias in one fused multiply-add; the type table stays
@@ -677,17 +685,17 @@ __global__ __launch_bounds__(256, attn_min_blocks((DQK + DV) * (int)sizeof(T) + 
     const int j0 = block_start(blk);
     if (!wave_rows || !block_active(j0, qr, sq)) return;
     ElemCtx x;
-    const int mode = classify_block(j0, tmin, tmax, qr, sq, rb, x);
+    const int mode = classify_block(j0, tmin, tmax, qr, sq, x);
     if constexpr (DUMP) {
       if (dump_dst) {
         if (mode == 0)
-          dump_block<0>(x, dump_dst, min(L, a.dump_len));
+          dump_block<0>(x, rb, dump_dst, min(L, a.dump_len));
         else if (mode == 1)
-          dump_block<1>(x, dump_dst, min(L, a.dump_len));
+          dump_block<1>(x, rb, dump_dst, min(L, a.dump_len));
         else if (mode == 2)
-          dump_block<2>(x, dump_dst, min(L, a.dump_len));
+          dump_block<2>(x, rb, dump_dst, min(L, a.dump_len));
         else
-          dump_block<3>(x, dump_dst, min(L, a.dump_len));
+          dump_block<3>(x, rb, dump_dst, min(L, a.dump_len));
       }
       return;
     }
@@ -720,7 +728,7 @@ __global__ __launch_bounds__(256, attn_min_blocks((DQK + DV) * (int)sizeof(T) + 
 #pragma unroll
         for (int n = 0; n < DV / 32; ++n) vf[c2][n] = v_frag<T, DV>(Vb, kh * 32 + 16 * c2, n, lane);
       float p[16];
-      half_weights(mode, sc, p, kh, x);
+      half_weights(mode, sc, p, kh, x, rb);
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2) {
@@ -740,15 +748,15 @@ __global__ __launch_bounds__(256, attn_min_blocks((DQK + DV) * (int)sizeof(T) + 
   // completed (after the wait that precedes each barrier).
   int64_t tmin0 = uniform64(tb0.x), tmax0 = uniform64(tb0.y), tmin1 = 0, tmax1 = 0;
   for (int blk = 0; blk < nblk; blk += 2) {
-    if (blk + 1 < nblk) issue(blk + 1, Ks1, Vs1, rel_s[1], kty_s[1], tb1);
-    consume(blk, Ks0, Vs0, rel_s[0], kty_s[0], tmin0, tmax0);
+    if (blk + 1 < nblk) issue(blk + 1, Ks1, Vs1, rel_s1, kty_s1, tb1);
+    consume(blk, Ks0, Vs0, rel_s0, kty_s0, tmin0, tmax0);
     if (blk + 1 >= nblk) break;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     tmin1 = uniform64(tb1.x);
     tmax1 = uniform64(tb1.y);
-    if (blk + 2 < nblk) issue(blk + 2, Ks0, Vs0, rel_s[0], kty_s[0], tb0);
-    consume(blk + 1, Ks1, Vs1, rel_s[1], kty_s[1], tmin1, tmax1);
+    if (blk + 2 < nblk) issue(blk + 2, Ks0, Vs0, rel_s0, kty_s0, tb0);
+    consume(blk + 1, Ks1, Vs1, rel_s1, kty_s1, tmin1, tmax1);
     if (blk + 2 >= nblk) break;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
