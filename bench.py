@@ -684,6 +684,8 @@ def main():
         rec["configs"] = {n: config_measure(torch, _lib, layer, synth, n) for n in CONFIGS}
     if not args.no_cpu and not args.minimal:
         rec["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+        # same workload and unit: the GPU's tokens/s over the oracle's
+        rec["cpu_baseline"]["gpu_over_cpu"] = rec["value"] / rec["cpu_baseline"]["value"]
     print(json.dumps(rec), flush=True)
 
 
