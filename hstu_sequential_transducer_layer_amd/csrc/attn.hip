@@ -234,6 +234,7 @@ __device__ __forceinline__ int bucket_floor_small(int b, int s) {
 struct ElemCtx {
   int jq;        // j0 + 4 * (lane / 32): key index of c = 0
   int iq, nh, p_q, R, NB, sbits, L;
+  SmallBucket bk;
   bool shared;
   float c_lo, c_hi;
   int32_t thr;   // MODE 1: keys with offset <= thr take c_hi
@@ -267,7 +268,7 @@ __device__ __forceinline__ float elem_bias(const ElemCtx& x, int c, int32_t rel,
   if (MODE == 0) return x.c_lo;
   if (MODE == 1) return rel <= x.thr ? x.c_hi : x.c_lo;
   if (MODE == 2) {
-    const int bt = time_bucket_small((int)((uint32_t)x.hi32 - (uint32_t)rel), x.NB, x.sbits);
+    const int bt = time_bucket_med3((int)((uint32_t)x.hi32 - (uint32_t)rel), x.bk);
     const int d = min(max(x.pq0 - c, -x.R), x.R);  // p(i) - p(j), clamped
     att = c <= x.iq0;                              // j <= i
     return x.time_s[bt] + x.pos_s[x.R + d];
@@ -339,11 +340,13 @@ struct QueryRow {
   int64_t ts_q;
   int32_t rq;   // ts_q - t0 when every row of the wave is within 2^29 of t0 (narrow)
   bool narrow;  // wave-uniform
+  uint64_t idle;  // lanes without a query row (they take no part in the wave's tests)
 };
 
 // Per-(workgroup) constants of the classification.
 struct SeqCtx {
   int L, nh, R, NB, sbits;
+  SmallBucket bk;  // the small-range bucket's clamp bounds and shift
   bool shared;
   float cpos_far;  // bias of every pair at relative distance >= R
   const float* pos_s;
@@ -387,15 +390,15 @@ __device__ __forceinline__ int classify_block(int j0, int64_t tmin, int64_t tmax
     // differences below are exact and span_ok holds); the same values as the
     // general path below, which takes every other case.
     const int32_t lo = q.rq - (int32_t)dmax, hi = q.rq - (int32_t)dmin;
-    if (__all((hi < (1 << 24) && lo > -(1 << 24)) || !q.qvalid)) {
-      const int bt_lo = time_bucket_small(lo, sq.NB, sq.sbits);
-      const int bt_hi = time_bucket_small(hi, sq.NB, sq.sbits);
+    if (all_lanes((ballot(hi < (1 << 24)) & ballot(lo > -(1 << 24))) | q.idle)) {
+      const int bt_lo = time_bucket_med3(lo, sq.bk);
+      const int bt_hi = time_bucket_med3(hi, sq.bk);
       x.jq = jq;  // (read only by the inspection dump in these modes)
-      if (__all(bt_hi == bt_lo || !q.qvalid)) {
+      if (all_lanes(ballot(bt_hi == bt_lo) | q.idle)) {
         x.c_lo = sq.time_s[bt_lo] + sq.cpos_far;
         return 0;
       }
-      if (__all(bt_hi <= bt_lo + 1 || !q.qvalid)) {
+      if (all_lanes(ballot(bt_hi <= bt_lo + 1) | q.idle)) {
         x.c_lo = sq.time_s[bt_lo] + sq.cpos_far;
         x.c_hi = sq.time_s[bt_hi] + sq.cpos_far;
         x.thr = hi - bucket_floor_small(max(bt_hi, 1), sq.sbits);
@@ -417,11 +420,11 @@ __device__ __forceinline__ int classify_block(int j0, int64_t tmin, int64_t tmax
     novf = !__builtin_sub_overflow(q.ts_q, tmax, &lo) && !__builtin_sub_overflow(q.ts_q, tmin, &hi);
   }
   const bool small = novf && hi < (1 << 24) && lo > -(1 << 24);
-  const bool all_small = __builtin_amdgcn_readfirstlane(__all(small || !q.qvalid) ? 1 : 0) != 0;
+  const bool all_small = all_lanes(ballot(small) | q.idle);
   int bt_lo, bt_hi;
   if (all_small) {
-    bt_lo = time_bucket_small((int)lo, sq.NB, sq.sbits);
-    bt_hi = time_bucket_small((int)hi, sq.NB, sq.sbits);
+    bt_lo = time_bucket_med3((int)lo, sq.bk);
+    bt_hi = time_bucket_med3((int)hi, sq.bk);
   } else {
     bt_lo = time_bucket(lo, sq.NB, sq.sbits);
     bt_hi = time_bucket(hi, sq.NB, sq.sbits);
@@ -430,11 +433,11 @@ __device__ __forceinline__ int classify_block(int j0, int64_t tmin, int64_t tmax
   const bool two = novf && span_ok && bt_hi == bt_lo + 1;
   // Fast modes: no mask, constant position bias, and per row at most two
   // time buckets (decided for the whole wave).
-  const bool fast = full && pos_far && __all(one || two || !q.qvalid);
+  const bool fast = full && pos_far && all_lanes(ballot(one) | ballot(two) | q.idle);
   const float c_lo = sq.time_s[bt_lo] + sq.cpos_far;
   const bool hist_only = j0 + kAttnBN <= sq.nh;
   const int mode = __builtin_amdgcn_readfirstlane(!fast ? (all_small && hist_only ? 2 : 3)
-                                                         : (__all(one || !q.qvalid) ? 0 : 1));
+                                                         : (all_lanes(ballot(one) | q.idle) ? 0 : 1));
   float c_hi = c_lo;
   int32_t thr = 0;
   if (mode == 1) {
@@ -446,7 +449,7 @@ __device__ __forceinline__ int classify_block(int j0, int64_t tmin, int64_t tmax
       thr = tt > INT32_MAX ? INT32_MAX : (int32_t)tt;
     }
   }
-  x = ElemCtx{jq, q.iq, sq.nh, q.p_q, sq.R, sq.NB, sq.sbits, sq.L, sq.shared, c_lo, c_hi, thr, (int32_t)hi,
+  x = ElemCtx{jq, q.iq, sq.nh, q.p_q, sq.R, sq.NB, sq.sbits, sq.L, sq.bk, sq.shared, c_lo, c_hi, thr, (int32_t)hi,
               q.p_q - jq, q.iq - jq, q.ts_q, sq.pos_s, sq.time_s, jq - j0, sq.ts};
   return mode;
 }
@@ -671,9 +674,10 @@ __global__ __launch_bounds__(256, attn_min_blocks((DQK + DV) * (int)sizeof(T) + 
   const bool q_near = !qvalid || (!__builtin_sub_overflow(ts_q, t0, &dq) && dq > -kNear && dq < kNear);
   const bool q_narrow = __builtin_amdgcn_readfirstlane(__all(q_near) ? 1 : 0) != 0;
   const int32_t rq = qvalid && q_near ? (int32_t)dq : 0;
-  const QueryRow qr = CACHED ? QueryRow{nh - 1, nh - 1, nh - 1, p_q, pmin_q, qvalid, ts_q, rq, q_narrow}
-                             : QueryRow{r0, rlast, iq, p_q, pmin_q, qvalid, ts_q, rq, q_narrow};
-  const SeqCtx sq{L, nh, R, a.NB, a.sbits, shared, cpos_far, pos_s, time_s, a.kts + k0, t0};
+  const uint64_t idle = ballot(!qvalid);
+  const QueryRow qr = CACHED ? QueryRow{nh - 1, nh - 1, nh - 1, p_q, pmin_q, qvalid, ts_q, rq, q_narrow, idle}
+                             : QueryRow{r0, rlast, iq, p_q, pmin_q, qvalid, ts_q, rq, q_narrow, idle};
+  const SeqCtx sq{L, nh, R, a.NB, a.sbits, small_bucket(a.NB, a.sbits), shared, cpos_far, pos_s, time_s, a.kts + k0, t0};
   float* dump_dst = nullptr;  // inspection: this row's bias row, keys [0, dump_len)
   if (DUMP && qvalid) {
     const int slot = a.dump_slot[s0 + iq];

@@ -121,6 +121,13 @@ __device__ __forceinline__ float silu_neglog2e(float s, float bn) {
   return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z));
 }
 
+// Lane masks of the wave in scalar registers.  A comparison's ballot is the
+// mask the comparison itself writes, so testing "every lane that counts"
+// as ballot(cmp) | (mask of lanes that do not count) == exec costs no
+// vector instruction beyond the comparison.
+__device__ __forceinline__ uint64_t ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
+__device__ __forceinline__ bool all_lanes(uint64_t m) { return m == __builtin_amdgcn_read_exec(); }
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
@@ -170,6 +177,24 @@ __device__ __forceinline__ int time_bucket(int64_t dt, int nb, int s) {
 __device__ __forceinline__ int time_bucket_small(int dt, int nb, int s) {
   const int b = (__float_as_int((float)dt) >> (23 - s)) + 1 - (127 << s);
   return min(max(b, 0), nb - 1);
+}
+
+// The same bucket with the clamp done by one float median instead of an
+// integer max and min: lo and hi are the smallest floats whose bits give
+// bucket 0 and bucket nb - 1 (hi capped at 2^24, above every dt of this
+// path), so clamping float(dt) to [lo, hi] clamps the bucket to [0, nb - 1].
+// Checked equal to time_bucket_small on the host for s in [0, 4].
+struct SmallBucket {
+  float lo, hi;
+  int sh, add;
+};
+__device__ __forceinline__ SmallBucket small_bucket(int nb, int s) {
+  const int top = (nb - 2 + (127 << s)) << (23 - s);  // bits of the first float of bucket nb - 1
+  return SmallBucket{__int_as_float(((127 << s) - 1) << (23 - s)),
+                     __int_as_float(min(top, __float_as_int(16777216.0f))), 23 - s, 1 - (127 << s)};
+}
+__device__ __forceinline__ int time_bucket_med3(int dt, const SmallBucket& k) {
+  return (__float_as_int(__builtin_amdgcn_fmed3f((float)dt, k.lo, k.hi)) >> k.sh) + k.add;
 }
 
 // Smallest dt >= 1 whose time bucket is >= b, for a bucket b >= 1 that some
