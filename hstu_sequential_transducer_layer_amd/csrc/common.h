@@ -183,7 +183,8 @@ __device__ __forceinline__ int time_bucket_small(int dt, int nb, int s) {
 // integer max and min: lo and hi are the smallest floats whose bits give
 // bucket 0 and bucket nb - 1 (hi capped at 2^24, above every dt of this
 // path), so clamping float(dt) to [lo, hi] clamps the bucket to [0, nb - 1].
-// Checked equal to time_bucket_small on the host for s in [0, 4].
+// tests/test_bucket_clamp_host.py restates the formula and checks it against
+// the oracle's bucket for every sub-bucket count the library accepts.
 struct SmallBucket {
   float lo, hi;
   int sh, add;
