@@ -34,6 +34,10 @@
 
 namespace hstu {
 
+// Entries of padding on each side of the position-bias table in LDS (edge
+// values repeated): mode 2 reads p(i) - j in [-94, R + 94) without a clamp.
+constexpr int kPosPad = 96;
+
 template <typename T, int DQK, int DV>
 struct AttnCfg {
   static constexpr int BM = kAttnBM, BN = kAttnBN, NW = BM / 32;
@@ -238,8 +242,10 @@ struct ElemCtx {
   bool shared;
   float c_lo, c_hi;
   int32_t thr;   // MODE 1: keys with offset <= thr take c_hi
-  int32_t hi32;  // MODE 2: t_i - (block's earliest timestamp)
+  int32_t hi32;  // MODES 2, 4: t_i - (block's earliest timestamp)
   int pq0, iq0;  // MODE 2: p(i) - jq and i - jq
+  const float* posb;  // MODE 2: &pos_s[R + p(i) - jq - 63]; key jq + c reads posb[63 - c]
+  float cpos_far;     // MODE 4: the position bias of every pair
   int64_t ts_q;
   const float* pos_s;
   const float* time_s;
@@ -254,11 +260,18 @@ struct ElemCtx {
 //           position bias both constant over the block).
 //   MODE 1: every pair attended, bias c_hi for keys whose offset from the
 //           block's earliest timestamp is <= thr, else c_lo.
-//   MODE 2: a block of history keys only: time bucket, relative-position
-//           bucket and causal mask per pair, with t_i - t_j = hi32 - offset_j
-//           in 32 bits (|dt| < 2^24 over the block) and position(j) = j.
+//   MODE 2: a block of history keys only, near the wave's rows: time
+//           bucket, relative-position bias and causal mask per pair, with
+//           t_i - t_j = hi32 - offset_j in 32 bits (|dt| < 2^24 over the
+//           block) and position(j) = j.  Here p(i) - j lies in [-94, R + 94)
+//           (the block is active for the wave and not R positions away), so
+//           the position bias is read without a clamp from the table padded
+//           with its edge values, at a per-lane base plus a constant offset.
 //   MODE 3: any block: the same from the 64-bit timestamps, with shared
 //           candidate positions and the candidate mask.
+//   MODE 4: a full block of history keys at least R positions from every
+//           row whose rows span three or more time buckets: time bucket per
+//           pair as in mode 2, constant position bias, no mask.
 // The bias (times -log2 e) of the pair (query iq, key jq + c) in weight mode
 // MODE, and whether the pair is attended; rel is the key's time offset from
 // its block's earliest timestamp (modes 1 and 2).
@@ -269,24 +282,24 @@ __device__ __forceinline__ float elem_bias(const ElemCtx& x, int c, int32_t rel,
   if (MODE == 1) return rel <= x.thr ? x.c_hi : x.c_lo;
   if (MODE == 2) {
     const int bt = time_bucket_med3((int)((uint32_t)x.hi32 - (uint32_t)rel), x.bk);
-    const int d = min(max(x.pq0 - c, -x.R), x.R);  // p(i) - p(j), clamped
-    att = c <= x.iq0;                              // j <= i
-    return x.time_s[bt] + x.pos_s[x.R + d];
+    att = c <= x.iq0;  // j <= i
+    return x.time_s[bt] + x.posb[63 - c];
   }
+  if (MODE == 4) return x.time_s[time_bucket_med3((int)((uint32_t)x.hi32 - (uint32_t)rel), x.bk)] + x.cpos_far;
   const int j = x.jq + c;
   att = attends(x.iq, j, x.nh);
   return x.time_s[time_bucket(wrap_sub(x.ts_q, x.ts[min(j, x.L - 1)]), x.NB, x.sbits)] +
          x.pos_s[pos_bucket(x.p_q, position(j, x.nh, x.shared), x.R)];
 }
 
-// The time offsets of keys kb + 8 g + 0..3 (modes 1 and 2; zeros otherwise)
+// The time offsets of keys kb + 8 g + 0..3 (modes 1, 2 and 4; zeros otherwise)
 // out of the block's offsets rb in LDS.  rb is passed down from the LDS
 // array itself, never through a merged or stored pointer: the compiler can
 // then tell these reads from a global->LDS copy in flight into the other
 // buffer, and does not wait for that copy before them.
 template <int MODE>
 __device__ __forceinline__ void elem_rel4(const ElemCtx& x, const int32_t* rb, int kb, int g, int32_t (&rel)[4]) {
-  if (MODE == 1 || MODE == 2) {
+  if (MODE == 1 || MODE == 2 || MODE == 4) {
     const int4 rv = *reinterpret_cast<const int4*>(rb + x.rel_off + kb + 8 * g);
     rel[0] = rv.x; rel[1] = rv.y; rel[2] = rv.z; rel[3] = rv.w;
   } else {
@@ -436,8 +449,8 @@ __device__ __forceinline__ int classify_block(int j0, int64_t tmin, int64_t tmax
   const bool fast = full && pos_far && all_lanes(ballot(one) | ballot(two) | q.idle);
   const float c_lo = sq.time_s[bt_lo] + sq.cpos_far;
   const bool hist_only = j0 + kAttnBN <= sq.nh;
-  const int mode = __builtin_amdgcn_readfirstlane(!fast ? (all_small && hist_only ? 2 : 3)
-                                                         : (all_lanes(ballot(one) | q.idle) ? 0 : 1));
+  const int mode = __builtin_amdgcn_readfirstlane(
+      !fast ? (all_small && hist_only ? (full && pos_far ? 4 : 2) : 3) : (all_lanes(ballot(one) | q.idle) ? 0 : 1));
   float c_hi = c_lo;
   int32_t thr = 0;
   if (mode == 1) {
@@ -450,7 +463,8 @@ __device__ __forceinline__ int classify_block(int j0, int64_t tmin, int64_t tmax
     }
   }
   x = ElemCtx{jq, q.iq, sq.nh, q.p_q, sq.R, sq.NB, sq.sbits, sq.L, sq.bk, sq.shared, c_lo, c_hi, thr, (int32_t)hi,
-              q.p_q - jq, q.iq - jq, q.ts_q, sq.pos_s, sq.time_s, jq - j0, sq.ts};
+              q.p_q - jq, q.iq - jq, sq.pos_s + sq.R + (q.p_q - jq) - 63, sq.cpos_far, q.ts_q, sq.pos_s,
+              sq.time_s, jq - j0, sq.ts};
   return mode;
 }
 
@@ -463,6 +477,8 @@ __device__ __forceinline__ void half_weights(int mode, const f32x16& sc, float (
     elems<1>(sc, p, 32 * kh, x, rb);
   else if (mode == 2)
     elems<2>(sc, p, 32 * kh, x, rb);
+  else if (mode == 4)
+    elems<4>(sc, p, 32 * kh, x, rb);
   else
     elems<3>(sc, p, 32 * kh, x, rb);
 }
@@ -539,9 +555,9 @@ __global__ __launch_bounds__(256, attn_min_blocks((DQK + DV) * (int)sizeof(T) + 
   __shared__ __attribute__((aligned(16))) int32_t kty_s0[TYPED ? C::BN : 1];
   __shared__ __attribute__((aligned(16))) int32_t kty_s1[TYPED ? C::BN : 1];
   extern __shared__ float tabs[];  // [P] position, [NB] time, [NT * NT] type table of head h
-  float* pos_s = tabs;
-  float* time_s = tabs + a.P;
-  float* type_s = tabs + a.P + a.NB;
+  float* pos_s = tabs + kPosPad;  // entries -kPosPad .. P + kPosPad - 1, the edge values repeated
+  float* time_s = tabs + a.P + 2 * kPosPad;
+  float* type_s = time_s + a.NB;
 
   const int H = a.H;
   const int h = blockIdx.x % H;
@@ -617,8 +633,9 @@ __global__ __launch_bounds__(256, attn_min_blocks((DQK + DV) * (int)sizeof(T) + 
   // Bias tables of head h, as fp32 times -log2(e), into LDS (the weights take
   // s * -log2(e) + bias in one fused multiply-add; the type table stays
   // unscaled: its term is added to the score on the matrix cores).
-  for (int i = tid; i < a.P; i += C::NT)
-    pos_s[i] = kNegLog2e * to_f32(reinterpret_cast<const T*>(a.pos_tab)[(int64_t)h * a.pos_stride + i]);
+  for (int i = tid; i < a.P + 2 * kPosPad; i += C::NT)
+    tabs[i] = kNegLog2e * to_f32(reinterpret_cast<const T*>(a.pos_tab)[(int64_t)h * a.pos_stride +
+                                                                       min(max(i - kPosPad, 0), a.P - 1)]);
   for (int i = tid; i < a.NB; i += C::NT)
     time_s[i] = kNegLog2e * to_f32(reinterpret_cast<const T*>(a.time_tab)[(int64_t)h * a.time_stride + i]);
   if (TYPED)
@@ -698,6 +715,8 @@ __global__ __launch_bounds__(256, attn_min_blocks((DQK + DV) * (int)sizeof(T) + 
           dump_block<1>(x, rb, dump_dst, min(L, a.dump_len));
         else if (mode == 2)
           dump_block<2>(x, rb, dump_dst, min(L, a.dump_len));
+        else if (mode == 4)
+          dump_block<4>(x, rb, dump_dst, min(L, a.dump_len));
         else
           dump_block<3>(x, rb, dump_dst, min(L, a.dump_len));
       }
@@ -807,7 +826,7 @@ __global__ __launch_bounds__(256, attn_min_blocks((DQK + DV) * (int)sizeof(T) + 
 template <typename T, int DQK, int DV>
 static hipError_t launch_t(const AttnArgs& a, bool cached, int64_t grid, hipStream_t s) {
   const bool typed = a.NT > 0;
-  const size_t shmem = (size_t)(a.P + a.NB + (typed ? a.NT * a.NT : 0)) * sizeof(float);
+  const size_t shmem = (size_t)(a.P + 2 * kPosPad + a.NB + (typed ? a.NT * a.NT : 0)) * sizeof(float);
   const dim3 g((unsigned)grid), b(AttnCfg<T, DQK, DV>::NT);
   if (cached && typed)
     hipLaunchKernelGGL((attn_kernel<T, DQK, DV, true, true>), g, b, shmem, s, a);
@@ -916,7 +935,7 @@ hipError_t launch_attn_dump(const hstu_desc& d, const AttnRows& r, const hstu_bi
   a.dump_slot = slot;
   a.dump_slots = nslots;
   a.dump_len = len;
-  const size_t shmem = (size_t)(a.P + a.NB) * sizeof(float);
+  const size_t shmem = (size_t)(a.P + 2 * kPosPad + a.NB) * sizeof(float);
   const dim3 g((unsigned)(attn_max_items(r.Tq, r.B, false) * d.num_heads)), b(kAttnBM / 32 * kWave);
   if (d.dtype == HSTU_BF16)
     hipLaunchKernelGGL((attn_kernel<bf16, 32, 32, false, false, true>), g, b, shmem, s, a);
