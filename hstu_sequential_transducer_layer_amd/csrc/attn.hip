@@ -382,27 +382,33 @@ __device__ __forceinline__ bool block_active(int j0, const QueryRow& q, const Se
 // threshold on the key's time offset, covers the whole row.
 //
 // When the block's and the wave's timestamps all lie within 2^29 of the
-// reference t0 (the usual case; a wave-uniform test on scalars), the row's
-// range comes from 32-bit differences of times relative to t0; otherwise from
-// overflow-checked 64-bit ones.  The mode-1 threshold and second bias are
+// reference t0 (the usual case; a wave-uniform test on scalars, differences
+// modulo 2^64), the row's range comes from 32-bit differences of times
+// relative to t0; otherwise from overflow-checked 64-bit ones.  The mode-1 threshold and second bias are
 // only formed when mode 1 is chosen.
 __device__ __forceinline__ int classify_block(int j0, int64_t tmin, int64_t tmax, const QueryRow& q,
                                               const SeqCtx& sq, ElemCtx& x) {
   const bool full = (j0 + kAttnBN - 1 <= q.r0) && (j0 + kAttnBN <= sq.nh);
   const int pmax_k = position(min(j0 + kAttnBN - 1, sq.L - 1), sq.nh, sq.shared);
   const bool pos_far = q.pmin_q - pmax_k >= sq.R;  // clamped position bias is constant
-  constexpr int64_t kNear = (int64_t)1 << 29;
-  int64_t dmin = 0, dmax = 0;
-  const bool narrow = q.narrow && !__builtin_sub_overflow(tmin, sq.t0, &dmin) &&
-                      !__builtin_sub_overflow(tmax, sq.t0, &dmax) && dmin > -kNear && dmin < kNear &&
-                      dmax > -kNear && dmax < kNear;
+  // The block's earliest and latest times relative to t0, modulo 2^64 as
+  // every time difference of the method is: when both offsets lie within
+  // 2^29 of zero (and the wave's rows' do), the difference of any two of the
+  // times involved is the difference of their 32-bit offsets, exactly.  The
+  // test runs on 32-bit halves, in scalar instructions.
+  constexpr uint32_t kNear = 1u << 29;
+  const uint64_t emin = (uint64_t)tmin - (uint64_t)sq.t0 + kNear;
+  const uint64_t emax = (uint64_t)tmax - (uint64_t)sq.t0 + kNear;
+  const bool narrow = q.narrow && (uint32_t)(emin >> 32) == 0u && (uint32_t)emin < 2 * kNear &&
+                      (uint32_t)(emax >> 32) == 0u && (uint32_t)emax < 2 * kNear;
+  const int32_t dmin = (int32_t)((uint32_t)emin - kNear), dmax = (int32_t)((uint32_t)emax - kNear);
   const int jq = j0 + 4 * (int)((threadIdx.x >> 5) & 1);
   if (full && pos_far && narrow) {
     // The usual far block (wave-uniform test): modes 0 and 1 from 32-bit
     // differences only (|t - t0| < 2^29 for every time involved, so the
     // differences below are exact and span_ok holds); the same values as the
     // general path below, which takes every other case.
-    const int32_t lo = q.rq - (int32_t)dmax, hi = q.rq - (int32_t)dmin;
+    const int32_t lo = q.rq - dmax, hi = q.rq - dmin;
     if (all_lanes((ballot(hi < (1 << 24)) & ballot(lo > -(1 << 24))) | q.idle)) {
       const int bt_lo = time_bucket_med3(lo, sq.bk);
       const int bt_hi = time_bucket_med3(hi, sq.bk);
@@ -425,8 +431,8 @@ __device__ __forceinline__ int classify_block(int j0, int64_t tmin, int64_t tmax
   if (narrow) {  // |t - t0| < 2^29 for every time involved: 32-bit differences are exact
     novf = true;
     span_ok = true;
-    lo = q.rq - (int32_t)dmax;
-    hi = q.rq - (int32_t)dmin;
+    lo = q.rq - dmax;
+    hi = q.rq - dmin;
   } else {
     int64_t span;
     span_ok = !__builtin_sub_overflow(tmax, tmin, &span) && span <= INT32_MAX;
