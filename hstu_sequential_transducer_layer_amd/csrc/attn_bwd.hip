@@ -364,6 +364,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
   const int lane = tid & 63, w = wave_id(), l32 = lane & 31, half = lane >> 5;
   const int r0 = i0 + 32 * w, iq = r0 + l32;
   const bool qvalid = iq < iend;
+  // lanes without a row (they take no part in the wave's tests), and the
+  // small-range bucket's bounds
+  const uint64_t idle = ballot(!qvalid);
+  const SmallBucket bk = small_bucket(a.NB, a.sbits);
   const float inv_n = 1.0f / (float)(a.norm_len > 0 ? a.norm_len : L);
   const int R = (P - 1) / 2;
   const bool shared = a.shared_pos != 0;
@@ -463,15 +467,15 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
     int64_t tcut = 0, kmin, kmax, dlo, dhi;
     bwd_block_minmax(a.tstat, s0 + j0, kmin, kmax);
     const bool ok = !__builtin_sub_overflow(ts_q, kmax, &dlo) && !__builtin_sub_overflow(ts_q, kmin, &dhi);
-    const bool small = __builtin_amdgcn_readfirstlane(
-                           __all((ok && dlo > -(1 << 24) && dhi < (1 << 24)) || !qvalid) ? 1 : 0) != 0;
+    const uint64_t okm = ballot(ok);
+    const bool small = all_lanes((okm & ballot(dlo > -(1 << 24)) & ballot(dhi < (1 << 24))) | idle);
     if (far) {
-      bt_lo = time_bucket(dlo, NB, a.sbits);
-      bt_hi = time_bucket(dhi, NB, a.sbits);
+      bt_lo = small ? time_bucket_med3((int)dlo, bk) : time_bucket(dlo, NB, a.sbits);
+      bt_hi = small ? time_bucket_med3((int)dhi, bk) : time_bucket(dhi, NB, a.sbits);
       b_lo = pos_s[2 * R] + time_s[bt_lo];
-      if (__all((ok && bt_lo == bt_hi) || !qvalid)) {
+      if (all_lanes((okm & ballot(bt_lo == bt_hi)) | idle)) {
         mode = 0;
-      } else if (__all((ok && bt_hi <= bt_lo + 1) || !qvalid)) {
+      } else if (all_lanes((okm & ballot(bt_hi <= bt_lo + 1)) | idle)) {
         mode = 1;
         b_hi = pos_s[2 * R] + time_s[bt_hi];
         tcut = ts_q - bucket_floor(max(bt_hi, 1), a.sbits);  // >= kmin: no overflow
@@ -507,7 +511,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdArgs a) {
         const int kl = kh * 32 + 8 * (r >> 2) + 4 * half + (r & 3), j = j0 + kl;
         const bool valid = qvalid && j < L && attends(iq, j, nh);
         const int bp = pos_bucket(p_q, position(j, nh, shared), R);
-        const int bt = SMALL ? time_bucket_small((int)((uint32_t)ts_q - (uint32_t)tk[r]), NB, a.sbits)
+        const int bt = SMALL ? time_bucket_med3((int)((uint32_t)ts_q - (uint32_t)tk[r]), bk)
                              : time_bucket(wrap_sub(ts_q, tk[r]), NB, a.sbits);
         const float g = dsv(da[r], valid ? __builtin_fmaf(sc[r], kNegLog2e, pos_s[bp] + time_s[bt]) : 1e30f);
         ds[r] = g;
@@ -651,6 +655,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(BwdArgs a) {
   const int lane = tid & 63, w = wave_id(), l32 = lane & 31, half = lane >> 5;
   const int kr0 = j0t + 32 * w, jk = kr0 + l32;
   const bool kvalid = jk < jend;
+  // lanes without a row (they take no part in the wave's tests), and the
+  // small-range bucket's bounds
+  const uint64_t idle = ballot(!kvalid);
+  const SmallBucket bk = small_bucket(a.NB, a.sbits);
   const float inv_n = 1.0f / (float)(a.norm_len > 0 ? a.norm_len : L);
   const int R = (P - 1) / 2;
   const bool shared = a.shared_pos != 0;
@@ -711,8 +719,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(BwdArgs a) {
     int64_t tcut = 0, qmin, qmax, dlo, dhi;
     bwd_block_minmax(a.tstat, s0 + i0, qmin, qmax);
     const bool ok = !__builtin_sub_overflow(qmin, ts_k, &dlo) && !__builtin_sub_overflow(qmax, ts_k, &dhi);
-    const bool small = __builtin_amdgcn_readfirstlane(
-                           __all((ok && dlo > -(1 << 24) && dhi < (1 << 24)) || !kvalid) ? 1 : 0) != 0;
+    const uint64_t okm = ballot(ok);
+    const bool small = all_lanes((okm & ballot(dlo > -(1 << 24)) & ballot(dhi < (1 << 24))) | idle);
     // Mode 2: each pair's buckets and mask (32-bit differences when small)
     auto pairs = [&](auto small_t, int qh, const f32x16& sc, const f32x16& da, float (&g)[16])
                      __attribute__((always_inline)) {
@@ -722,7 +730,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(BwdArgs a) {
         const int ql = qh * 32 + 8 * (r >> 2) + 4 * half + (r & 3), i = i0 + ql;
         const bool valid = kvalid && i < L && attends(i, jk, nh);
         const int bp = pos_bucket(position(i, nh, shared), p_k, R);
-        const int bt = SMALL ? time_bucket_small((int)((uint32_t)tsq[ql] - (uint32_t)ts_k), NB, a.sbits)
+        const int bt = SMALL ? time_bucket_med3((int)((uint32_t)tsq[ql] - (uint32_t)ts_k), bk)
                              : time_bucket(wrap_sub(tsq[ql], ts_k), NB, a.sbits);
         const float s = sc[r] + pos_s[bp] + time_s[bt];
         const float sg = bwd_sigmoid(s);
@@ -731,12 +739,12 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(BwdArgs a) {
       }
     };
     if (far) {
-      const int lo = time_bucket(dlo, NB, a.sbits);
-      const int hi = time_bucket(dhi, NB, a.sbits);
+      const int lo = small ? time_bucket_med3((int)dlo, bk) : time_bucket(dlo, NB, a.sbits);
+      const int hi = small ? time_bucket_med3((int)dhi, bk) : time_bucket(dhi, NB, a.sbits);
       b_lo = pos_s[2 * R] + time_s[lo];
-      if (__all((ok && lo == hi) || !kvalid)) {
+      if (all_lanes((okm & ballot(lo == hi)) | idle)) {
         mode = 0;
-      } else if (__all((ok && hi <= lo + 1) || !kvalid)) {
+      } else if (all_lanes((okm & ballot(hi <= lo + 1)) | idle)) {
         mode = 1;
         b_hi = pos_s[2 * R] + time_s[hi];
         tcut = ts_k + bucket_floor(max(hi, 1), a.sbits);  // <= qmax: no overflow
@@ -891,6 +899,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kv16_kernel(BwdArgs a) {
   const int lane = tid & 63, w = wave_id(), g = lane >> 4, l16 = lane & 15;
   const int kr0 = j0t + 16 * w, jk = kr0 + l16;
   const bool kvalid = jk < jend;
+  // lanes without a row (they take no part in the wave's tests), and the
+  // small-range bucket's bounds
+  const uint64_t idle = ballot(!kvalid);
+  const SmallBucket bk = small_bucket(a.NB, a.sbits);
   const float inv_n = 1.0f / (float)(a.norm_len > 0 ? a.norm_len : L);
   const int R = (P - 1) / 2;
   const bool shared = a.shared_pos != 0;
@@ -964,15 +976,15 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kv16_kernel(BwdArgs a) {
     int64_t tcut = 0, qmin, qmax, dlo, dhi;
     bwd_block_minmax(a.tstat, s0 + i0, qmin, qmax);
     const bool ok = !__builtin_sub_overflow(qmin, ts_k, &dlo) && !__builtin_sub_overflow(qmax, ts_k, &dhi);
-    const bool small = __builtin_amdgcn_readfirstlane(
-                           __all((ok && dlo > -(1 << 24) && dhi < (1 << 24)) || !kvalid) ? 1 : 0) != 0;
+    const uint64_t okm = ballot(ok);
+    const bool small = all_lanes((okm & ballot(dlo > -(1 << 24)) & ballot(dhi < (1 << 24))) | idle);
     if (far) {
-      const int lo = time_bucket(dlo, NB, a.sbits);
-      const int hi = time_bucket(dhi, NB, a.sbits);
+      const int lo = small ? time_bucket_med3((int)dlo, bk) : time_bucket(dlo, NB, a.sbits);
+      const int hi = small ? time_bucket_med3((int)dhi, bk) : time_bucket(dhi, NB, a.sbits);
       b_lo = pos_s[2 * R] + time_s[lo];
-      if (__all((ok && lo == hi) || !kvalid)) {
+      if (all_lanes((okm & ballot(lo == hi)) | idle)) {
         mode = 0;
-      } else if (__all((ok && hi <= lo + 1) || !kvalid)) {
+      } else if (all_lanes((okm & ballot(hi <= lo + 1)) | idle)) {
         mode = 1;
         b_hi = pos_s[2 * R] + time_s[hi];
         tcut = ts_k + bucket_floor(max(hi, 1), a.sbits);  // <= qmax: no overflow
@@ -1025,7 +1037,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kv16_kernel(BwdArgs a) {
         const int ql = 16 * (e >> 2) + 4 * g + (e & 3), i = i0 + ql;
         const bool valid = kvalid && i < L && attends(i, jk, nh);
         const int bp = pos_bucket(position(i, nh, shared), p_k, R);
-        const int bt = SMALL ? time_bucket_small((int)((uint32_t)tq[e] - (uint32_t)ts_k), NB, a.sbits)
+        const int bt = SMALL ? time_bucket_med3((int)((uint32_t)tq[e] - (uint32_t)ts_k), bk)
                              : time_bucket(wrap_sub(tq[e], ts_k), NB, a.sbits);
         const float x = __builtin_fmaf(sc[e >> 2][e & 3], kNegLog2e, pos_s[bp] + time_s[bt]);
         put(e, valid ? x : 1e30f);
